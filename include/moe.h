@@ -1,0 +1,237 @@
+/*
+ * moe.h -- C ABI of libmoe, the forward pass of a Mixture-of-Experts FFN layer
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The layer (Vector Institute, "Mixture-of-Experts: From sparse routing to
+ * multimodal deployment", router paragraphs and Eq. (moe-output); "Fine-Tuning
+ * Mixture of Experts (MoE) Models: Router Optimization Techniques", What Is It?):
+ *
+ *   y[t] = sum over the k experts e selected for token t of  g_e(t) * FFN_e(x[t])
+ *          (+ FFN_shared(x[t]) when a shared expert is configured)
+ *
+ * computed as five stages, each a call below, all enqueued on one HIP stream:
+ *   moe_route       router logits, scores, top-k, gates, counts, balance statistics
+ *   moe_permute     expert histogram, exclusive scan, stable expert-contiguous gather
+ *   moe_grouped_ffn every expert's FFN as one grouped GEMM over variable-size segments
+ *   moe_shared_ffn  the always-on shared SwiGLU expert (dense)
+ *   moe_combine     gate-weighted sum back to token order (+ shared output)
+ * and moe_forward, which chains them.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory:    every pointer argument is caller-owned DEVICE memory of the current
+ *            HIP device (except `shape`, which is host memory). The library never
+ *            allocates, frees or synchronises and keeps no state between calls;
+ *            scratch comes only from the caller's workspace `ws` of `ws_bytes`
+ *            bytes, sized by moe_workspace_bytes().
+ * Layout:    row-major everywhere. Weights use the Linear [out, in] layout, so
+ *            both operands of every product are contiguous along the reduced
+ *            dimension. Expert weights are stacked along a leading expert axis.
+ *            bf16 tensors hold IEEE bfloat16 bit patterns (uint16_t storage).
+ * dtype:     `dtype` (MOE_F32 or MOE_BF16) is the type of x, expert weights and
+ *            biases, x_perm, y_perm, y_shared and y. The router weights, the
+ *            selection bias, logits, gates and statistics are always fp32
+ *            ("Mixture of Experts" tutorial, Selective precision; "Fine-tuning and
+ *            serving MoE models", the router softmax runs in FP32).
+ * Alignment: every device pointer must be 16-byte aligned.
+ * Streams:   `stream` is a hipStream_t passed as moe_stream_t; NULL is the null
+ *            stream. Every call only enqueues work, so results are ready when the
+ *            stream reaches that point. Calls are graph-capturable (no host
+ *            synchronisation, no device-to-host reads).
+ * Aliasing:  outputs must not overlap inputs or each other.
+ * Errors:    every call returns MOE_OK (0) or a negative moe_status. All argument
+ *            checks run on the host before any HIP call; a rejected call enqueues
+ *            nothing. MOE_ERR_HIP reports a failed launch. T = 0 is a successful
+ *            no-op. Non-finite inputs are outside the contract (not checked).
+ * Threads:   re-entrant; concurrent calls on different streams with different
+ *            workspaces are independent.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1, /* null required pointer, bad enum, inconsistent sizes, misalignment */
+    MOE_ERR_UNSUPPORTED = -2, /* valid request this build does not implement (e.g. d_model % 64) */
+    MOE_ERR_WORKSPACE = -3,   /* ws_bytes below moe_workspace_bytes() for the call */
+    MOE_ERR_HIP = -4          /* a kernel launch failed (hipGetLastError) */
+} moe_status;
+
+/* dtype */
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
+/* act: expert FFN form */
+enum {
+    MOE_GELU_MLP = 0, /* Linear(d->F, bias) + exact erf GELU + Linear(F->d, bias)
+                         ("Fine-tuning and serving MoE models", How an MoE layer actually works) */
+    MOE_SWIGLU = 1    /* (SiLU(x Wg^T) * (x Wu^T)) Wd^T, no biases
+                         ("Router Optimization Techniques", What Is It?: W_gate, W_up, W_down) */
+};
+/* score: router scoring */
+enum {
+    MOE_SOFTMAX = 0, /* softmax over the E logits; selection on the logit (+ bias) */
+    MOE_SIGMOID = 1  /* per-expert sigmoid; selection on sigmoid + bias; gates = s / sum_selected s */
+};
+/* stage argument of moe_workspace_bytes */
+enum {
+    MOE_STAGE_ROUTE = 0,
+    MOE_STAGE_PERMUTE = 1,
+    MOE_STAGE_FFN = 2,
+    MOE_STAGE_SHARED = 3,
+    MOE_STAGE_FORWARD = 4
+};
+
+/* Layer description (host memory). Limits: T >= 0; 1 <= E <= 1024; 1 <= k <= min(E, 32);
+ * T*k <= 2^31-1; bf16: d_model, d_ff, d_ff_shared multiples of 64; f32: multiples of 4;
+ * MOE_SIGMOID requires renorm = 1. Violations give MOE_ERR_INVALID_ARG or
+ * MOE_ERR_UNSUPPORTED (multiples). */
+typedef struct {
+    int64_t T;           /* tokens */
+    int32_t d_model;     /* hidden size d */
+    int32_t d_ff;        /* routed expert intermediate size F */
+    int32_t E;           /* routed experts */
+    int32_t k;           /* experts per token */
+    int32_t dtype;       /* MOE_F32 | MOE_BF16 */
+    int32_t act;         /* MOE_GELU_MLP | MOE_SWIGLU */
+    int32_t score;       /* MOE_SOFTMAX | MOE_SIGMOID */
+    int32_t renorm;      /* 1: gates renormalised over the selected k; 0: raw softmax probabilities */
+    int32_t d_ff_shared; /* shared SwiGLU expert intermediate size; 0 = no shared expert */
+} moe_shape;
+
+typedef void* moe_stream_t; /* a hipStream_t */
+
+/* Scratch bytes a call needs. stage: MOE_STAGE_*. Writes the size to *bytes.
+ * Returns MOE_ERR_INVALID_ARG for an invalid shape or stage, else MOE_OK. */
+int moe_workspace_bytes(const moe_shape* shape, int stage, size_t* bytes);
+
+/* moe_route -- the router: logits, scores, per-token top-k, gates, counts, statistics.
+ *
+ * Defined by: Vector Institute post, router score W_r x and softmax, top-k, gate
+ * renormalisation paragraph; "Router Optimization Techniques", What Is It? (h(x) = x W_g,
+ * TopK, Softmax(TopK(h))), How It Works 1 (f_i, P_i, L_aux), How It Works 2 (bias used only
+ * to pick the top-k, gates from the unbiased scores); "Fine-tuning and serving MoE models",
+ * load_balancing_loss and the utilisation tally.
+ *
+ *   x        [T, d_model]  dtype          token activations
+ *   w_router [E, d_model]  fp32           router weights (no router bias)
+ *   sel_bias [E]           fp32 or NULL   selection-only bias: enters the top-k key, never a gate
+ *   logits   [T, E]        fp32 or NULL   out: l[t,e] = sum_i x[t,i] w_router[e,i]
+ *   topk_idx [T, k]        int32          out: selected experts, slot order = descending key,
+ *                                         equal keys -> lower expert index first
+ *   topk_w   [T, k]        fp32           out: gates of the selected experts, same slot order
+ *   counts   [E]           int32          out: assignments per expert (sums to T*k)
+ *   stats    [2E + 2]      fp32 or NULL   out: f[0..E) = counts/T, P[E..2E) = mean over tokens of
+ *                                         the softmax probability (sigmoid: s / sum_e s),
+ *                                         stats[2E] = aux = E * sum_e f_e P_e (alpha not applied),
+ *                                         stats[2E+1] = mean token entropy -sum_e p ln p (nats)
+ * Key: softmax -> logit (+ sel_bias); sigmoid -> sigmoid(logit) + sel_bias.
+ * Gates: softmax & renorm -> softmax over the selected logits; softmax & !renorm -> full-softmax
+ * probability; sigmoid -> selected sigmoid scores over their sum.
+ * All reductions are deterministic (fixed order, no float atomics): repeated calls give
+ * identical bits. Workspace: MOE_STAGE_ROUTE. */
+int moe_route(const moe_shape* shape, const void* x, const float* w_router, const float* sel_bias,
+              float* logits, int32_t* topk_idx, float* topk_w, int32_t* counts, float* stats,
+              void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* moe_permute -- expert-contiguous, stable order of the T*k assignments.
+ *
+ * Defined by: "Fine-tuning and serving MoE models", the loop over experts (nonzero(idx == e)
+ * gathers each expert's tokens in ascending token order); "Router Optimization Techniques",
+ * What Most Articles Miss 2 (all assigned tokens packed into one contiguous workspace).
+ *
+ *   topk_idx     [T, k]        int32  in: experts per token (each in [0, E); a token's k experts
+ *                                     distinct, as moe_route produces; other values: undefined)
+ *   x            [T, d_model]  dtype  in: token activations
+ *   offsets      [E + 1]       int32  out: exclusive prefix sum of the expert histogram;
+ *                                     offsets[E] = T*k
+ *   sorted_token [T*k]         int32  out: row p of x_perm holds token sorted_token[p]
+ *   inv_pos      [T*k]         int32  out: assignment (t, j) sits at row inv_pos[t*k + j]
+ *   x_perm       [T*k, d_model] dtype out: x_perm[p] = x[sorted_token[p]]
+ * Within an expert's segment rows are ordered by ascending t*k + j. Integer outputs are exact
+ * and deterministic. Workspace: MOE_STAGE_PERMUTE. */
+int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, int32_t* offsets,
+                int32_t* sorted_token, int32_t* inv_pos, void* x_perm, void* ws, size_t ws_bytes,
+                moe_stream_t stream);
+
+/* moe_grouped_ffn -- every expert's FFN on its contiguous rows, as one grouped GEMM pair.
+ *
+ * Defined by: "Router Optimization Techniques", What Is It? (expert = SwiGLU FFN with W_gate,
+ * W_up, W_down) and Production Deployment 1 / What Most Articles Miss 2 (one grouped-GEMM launch
+ * instead of one kernel per expert); "Fine-tuning and serving MoE models", the expert
+ * Linear + GELU + Linear and grouped GEMM in one launch.
+ *
+ *   e_begin, e_end  experts [e_begin, e_end) are computed (0 <= e_begin <= e_end <= E); only rows
+ *                   [offsets[e_begin], offsets[e_end]) of y_perm are written (the share of one
+ *                   expert-parallel rank)
+ *   x_perm  [T*k, d_model]      dtype  in: rows grouped by expert (moe_permute)
+ *   offsets [E + 1]             int32  in: segment starts (device memory; never read by the host)
+ *   w_in    [E, n_in, d_model]  dtype  in: GELU: n_in = d_ff (W1); SwiGLU: n_in = 2*d_ff,
+ *                                      rows [0, d_ff) = W_gate, rows [d_ff, 2 d_ff) = W_up
+ *   b_in    [E, d_ff]           dtype or NULL  GELU only (must be NULL for SwiGLU)
+ *   w_out   [E, d_model, d_ff]  dtype  in: W2 / W_down
+ *   b_out   [E, d_model]        dtype or NULL  GELU only
+ *   y_perm  [T*k, d_model]      dtype  out: FFN_e(x_perm[p]) for each row p of expert e
+ * Accumulation is fp32; bf16 layers round the intermediate activation once to bf16 (RNE) and
+ * the output once. Empty experts cost nothing: the tile schedule is built on the device from
+ * offsets. Workspace: MOE_STAGE_FFN. */
+int moe_grouped_ffn(const moe_shape* shape, int32_t e_begin, int32_t e_end, const void* x_perm,
+                    const int32_t* offsets, const void* w_in, const void* b_in, const void* w_out,
+                    const void* b_out, void* y_perm, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* moe_shared_ffn -- the always-on shared SwiGLU expert on every token (gate 1).
+ *
+ * Defined by: Vector Institute post, shared experts that run for every token (DeepSeekMoE);
+ * "Router Optimization Techniques", lesson 2 (1 shared + 256 routed experts).
+ *
+ *   x        [T, d_model]             dtype  in
+ *   ws_in    [2*d_ff_shared, d_model] dtype  in: rows [0, Fs) gate, [Fs, 2 Fs) up
+ *   ws_out   [d_model, d_ff_shared]   dtype  in
+ *   y_shared [T, d_model]             dtype  out
+ * Requires shape->d_ff_shared > 0. Workspace: MOE_STAGE_SHARED. */
+int moe_shared_ffn(const moe_shape* shape, const void* x, const void* ws_in, const void* ws_out,
+                   void* y_shared, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* moe_combine -- gate-weighted sum of each token's k expert outputs, back in token order.
+ *
+ * Defined by: Vector Institute post, Eq. (moe-output); "Router Optimization Techniques",
+ * MoE Layer Output = sum_{i in TopK} P_i(x) E_i(x); "Fine-tuning and serving MoE models",
+ * index_add of gate-scaled expert outputs.
+ *
+ *   y_perm   [T*k, d_model] dtype        in
+ *   inv_pos  [T*k]          int32        in: moe_permute's inverse permutation
+ *   topk_w   [T, k]         fp32         in: gates
+ *   y_shared [T, d_model]   dtype or NULL in: shared-expert output, added with gate 1
+ *   y        [T, d_model]   dtype        out: y[t] = sum_j topk_w[t,j] y_perm[inv_pos[t*k+j]]
+ *                                        (+ y_shared[t]), fp32 accumulation in slot order
+ *                                        j = 0..k-1, shared last, one final rounding
+ * Needs no workspace. */
+int moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* inv_pos, const float* topk_w,
+                const void* y_shared, void* y, moe_stream_t stream);
+
+/* moe_forward -- route, permute, grouped FFN, shared expert and combine on one stream.
+ *
+ * Same definitions as the stage calls. Inputs as in moe_route / moe_grouped_ffn /
+ * moe_shared_ffn (ws_in and ws_out required iff d_ff_shared > 0). y [T, d_model] dtype is the
+ * layer output. The optional outputs topk_idx_out [T,k] int32, topk_w_out [T,k] fp32,
+ * counts_out [E] int32 and stats_out [2E+2] fp32 receive the routing results when non-NULL.
+ * Workspace: MOE_STAGE_FORWARD. */
+int moe_forward(const moe_shape* shape, const void* x, const float* w_router, const float* sel_bias,
+                const void* w_in, const void* b_in, const void* w_out, const void* b_out,
+                const void* ws_in, const void* ws_out, void* y, int32_t* topk_idx_out,
+                float* topk_w_out, int32_t* counts_out, float* stats_out, void* ws, size_t ws_bytes,
+                moe_stream_t stream);
+
+/* Human-readable name of a moe_status value (static string; never NULL). */
+const char* moe_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,369 @@
+// moe_grouped_ffn / moe_shared_ffn kernels: all experts' FFN products as one grouped GEMM launch
+// per projection ("Router Optimization Techniques", Production Deployment 1 and What Most Articles
+// Miss 2: one grouped-GEMM kernel over a contiguous token workspace instead of one kernel per
+// expert). The expert FFNs are SwiGLU ((SiLU(x Wg^T) * x Wu^T) Wd^T; same page, What Is It?) or
+// Linear + GELU + Linear with biases ("Fine-tuning and serving MoE models").
+//
+// Tile schedule: ffn_schedule turns the device-side expert offsets into a prefix sum of per-
+// expert row-tile counts. The GEMM grid is an upper bound; a block decodes its linear id into
+// (row tile, column tile), finds its expert by binary search over the prefix sum and exits if it
+// is past the end, so empty experts own no tile and a ragged last tile is masked, not padded.
+//
+// bf16 path: v_mfma_f32_32x32x16_bf16, 256 threads (2 x 2 waves), BM x BN x 64 tiles staged
+// through LDS with double buffering; both operands are K-contiguous and 16-byte chunks are XOR-
+// swizzled by row so the 128-bit LDS reads of a 32-row MFMA operand hit distinct banks. The
+// SwiGLU epilogue gets gate and up columns of the same output in the same lane (the B tile holds
+// BN/2 gate rows then the matching BN/2 up rows) and writes SiLU(g)*u rounded once to bf16.
+#include "moe_common.h"
+#include "moe_kernels.h"
+#include "../../include/moe.h"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
+__device__ __forceinline__ float gelu_f(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+
+struct TileCoord {
+    int64_t row0, row_end;  // rows [row0, min(row0 + BM, row_end)) of A and C
+    int e;                  // weight group
+    int n0;                 // first output column
+    bool valid;
+};
+
+// Decode the block's linear id into a tile. Row tiles are visited in groups of GM sharing a
+// sweep over the column tiles, so blocks running together reuse the same A rows and B panels.
+template <int BM, int BNO, int GM>
+__device__ __forceinline__ TileCoord decode_tile(const int32_t* __restrict__ offsets,
+                                                 const int32_t* __restrict__ tile_start, int e_begin,
+                                                 int n_groups, int64_t dense_rows, int n_out) {
+    TileCoord tc;
+    const int n_tiles_n = (n_out + BNO - 1) / BNO;
+    const int64_t m_tiles = offsets ? (int64_t)tile_start[n_groups] : (dense_rows + BM - 1) / BM;
+    const int64_t lin = blockIdx.x;
+    tc.valid = lin < m_tiles * n_tiles_n;
+    if (!tc.valid) return tc;
+    const int64_t grp = lin / ((int64_t)GM * n_tiles_n);
+    const int64_t first_m = grp * GM;
+    const int64_t gsz = m_tiles - first_m < GM ? m_tiles - first_m : GM;
+    const int64_t rem = lin - grp * GM * n_tiles_n;
+    const int64_t mt = first_m + rem % gsz;
+    tc.n0 = (int)(rem / gsz) * BNO;
+    if (offsets) {
+        int lo = 0, hi = n_groups - 1;  // largest g with tile_start[g] <= mt
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (tile_start[mid] <= mt) lo = mid;
+            else hi = mid - 1;
+        }
+        tc.e = e_begin + lo;
+        tc.row0 = offsets[tc.e] + (mt - tile_start[lo]) * BM;
+        tc.row_end = offsets[tc.e + 1];
+    } else {
+        tc.e = 0;
+        tc.row0 = mt * BM;
+        tc.row_end = dense_rows;
+    }
+    return tc;
+}
+
+}  // namespace
+
+// One block per group: tile_start[g] = sum_{g' < g} ceil(rows_{g'} / bm).
+__global__ __launch_bounds__(1024) void ffn_schedule_kernel(const int32_t* __restrict__ offsets, int e_begin,
+                                                            int n_groups, int bm, int32_t* __restrict__ tile_start) {
+    __shared__ int s_wave[17];
+    const int g = threadIdx.x;
+    int n = 0;
+    if (g < n_groups) {
+        const int rows = offsets[e_begin + g + 1] - offsets[e_begin + g];
+        n = (rows + bm - 1) / bm;
+    }
+    int total;
+    const int start = block1024_excl_scan(n, s_wave, &total);
+    if (g < n_groups) tile_start[g] = start;
+    if (g == 0) tile_start[n_groups] = total;
+}
+
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
+                                                        const uint16_t* __restrict__ B,
+                                                        const uint16_t* __restrict__ bias,
+                                                        uint16_t* __restrict__ C,
+                                                        const int32_t* __restrict__ offsets,
+                                                        const int32_t* __restrict__ tile_start, int e_begin,
+                                                        int n_groups, int64_t dense_rows, int n_out, int K) {
+    constexpr int BK = 64;
+    constexpr bool GATED = EPI == EPI_SWIGLU;
+    constexpr int WTM = BM / WM;
+    constexpr int TM = WTM / 32;
+    constexpr int BNO = GATED ? BN / 2 : BN;  // output columns per block
+    constexpr int WTNO = BNO / WN;            // output columns per wave
+    constexpr int TNO = WTNO / 32;
+    constexpr int TN = GATED ? 2 * TNO : TNO;  // B sub-tiles per wave
+    constexpr int ACH = BM * 8 / 256;          // 16-byte A chunks per thread per stage
+    constexpr int BCH = BN * 8 / 256;
+    static_assert(WM * WN == 4 && TM >= 1 && TNO >= 1 && ACH >= 1 && BCH >= 1, "tile shape");
+
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][(BM + BN) * BK];
+
+    const TileCoord tc = decode_tile<BM, BNO, 8>(offsets, tile_start, e_begin, n_groups, dense_rows, n_out);
+    if (!tc.valid) return;
+
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int wm = wave % WM, wn = wave / WM;
+    const int64_t last_row = tc.row_end - 1;
+    const int64_t n_b_rows = GATED ? 2 * (int64_t)n_out : n_out;
+    const uint16_t* Bg = B + (int64_t)tc.e * n_b_rows * K;
+
+    const uint16_t* a_src[ACH];
+    int a_dst[ACH];
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+        const int q = tid + i * 256, r = q >> 3, c = q & 7;
+        const int64_t gr = tc.row0 + r <= last_row ? tc.row0 + r : last_row;
+        a_src[i] = A + gr * K + c * 8;
+        a_dst[i] = r * BK + ((c ^ (r & 7)) << 3);
+    }
+    const uint16_t* b_src[BCH];
+    int b_dst[BCH];
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) {
+        const int q = tid + i * 256, r = q >> 3, c = q & 7;
+        int64_t br;
+        if (GATED) {
+            const int rr = r < BN / 2 ? r : r - BN / 2;
+            const int col = tc.n0 + rr < n_out ? tc.n0 + rr : n_out - 1;
+            br = r < BN / 2 ? col : (int64_t)n_out + col;
+        } else {
+            br = tc.n0 + r < n_out ? tc.n0 + r : n_out - 1;
+        }
+        b_src[i] = Bg + br * K + c * 8;
+        b_dst[i] = BM * BK + r * BK + ((c ^ (r & 7)) << 3);
+    }
+
+    floatx16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    u32x4 ra[ACH], rb[BCH];
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) ra[i] = ld16(a_src[i]);
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) rb[i] = ld16(b_src[i]);
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) st16(&lds[0][a_dst[i]], ra[i]);
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) st16(&lds[0][b_dst[i]], rb[i]);
+    __syncthreads();
+
+    // LDS rows of this lane's operands
+    int a_row[TM], b_row[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a_row[i] = wm * WTM + i * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int jj = j < TNO ? j : j - TNO;
+        b_row[j] = BM + (GATED && j >= TNO ? BN / 2 : 0) + wn * WTNO + jj * 32 + (lane & 31);
+    }
+    const int khalf = lane >> 5;
+
+    const int nk = K / BK;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            const int koff = (kt + 1) * BK;
+#pragma unroll
+            for (int i = 0; i < ACH; ++i) ra[i] = ld16(a_src[i] + koff);
+#pragma unroll
+            for (int i = 0; i < BCH; ++i) rb[i] = ld16(b_src[i] + koff);
+        }
+        const uint16_t* L = lds[cur];
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            const int c = kk * 2 + khalf;
+            bf16x8 af[TM], bfr[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                af[i] = *reinterpret_cast<const bf16x8*>(L + a_row[i] * BK + ((c ^ (a_row[i] & 7)) << 3));
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                bfr[j] = *reinterpret_cast<const bf16x8*>(L + b_row[j] * BK + ((c ^ (b_row[j] & 7)) << 3));
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        if (more) {
+#pragma unroll
+            for (int i = 0; i < ACH; ++i) st16(&lds[cur ^ 1][a_dst[i]], ra[i]);
+#pragma unroll
+            for (int i = 0; i < BCH; ++i) st16(&lds[cur ^ 1][b_dst[i]], rb[i]);
+        }
+        __syncthreads();
+    }
+
+    // Epilogue. 32x32 accumulator: lane holds column lane%32 and rows 8*(v/4) + 4*(lane/32) + v%4.
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TNO; ++j) {
+            const int col = tc.n0 + wn * WTNO + j * 32 + (lane & 31);
+            if (col >= n_out) continue;
+            float bcol = 0.f;
+            if (EPI != EPI_SWIGLU && bias != nullptr) bcol = bf16_to_f32(bias[(int64_t)tc.e * n_out + col]);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = tc.row0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
+                if (row >= tc.row_end) continue;
+                float out;
+                if (EPI == EPI_SWIGLU) out = silu_f(acc[i][j][v]) * acc[i][j + TNO][v];
+                else if (EPI == EPI_GELU_BIAS) out = gelu_f(acc[i][j][v] + bcol);
+                else out = acc[i][j][v] + bcol;
+                C[row * n_out + col] = f32_to_bf16(out);
+            }
+        }
+    }
+}
+
+// fp32 path (SIMT, 64 x 64 output tile, 4 x 4 per thread, sequential fp32 FMA over K).
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ B,
+                                                       const float* __restrict__ bias, float* __restrict__ C,
+                                                       const int32_t* __restrict__ offsets,
+                                                       const int32_t* __restrict__ tile_start, int e_begin,
+                                                       int n_groups, int64_t dense_rows, int n_out, int K) {
+    constexpr int BM = 64, BNO = 64, BK = 16;
+    constexpr bool GATED = EPI == EPI_SWIGLU;
+    constexpr int NB = GATED ? 2 : 1;
+    __shared__ float As[BK][BM + 4];
+    __shared__ float Bs[NB][BK][BNO + 4];
+    const TileCoord tc = decode_tile<BM, BNO, 8>(offsets, tile_start, e_begin, n_groups, dense_rows, n_out);
+    if (!tc.valid) return;
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const int64_t last_row = tc.row_end - 1;
+    const int64_t n_b_rows = GATED ? 2 * (int64_t)n_out : n_out;
+    const float* Bg = B + (int64_t)tc.e * n_b_rows * K;
+    const int lr = tid >> 2, lk = (tid & 3) * 4;  // loader: row (0..63), k quad
+    const int64_t arow = tc.row0 + lr <= last_row ? tc.row0 + lr : last_row;
+    const int bcol = tc.n0 + lr < n_out ? tc.n0 + lr : n_out - 1;
+    float acc[NB][4][4] = {};
+    for (int k0 = 0; k0 < K; k0 += BK) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int kk = k0 + lk + q;
+            As[lk + q][lr] = kk < K ? A[arow * K + kk] : 0.f;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                Bs[nb][lk + q][lr] = kk < K ? Bg[((int64_t)nb * n_out + bcol) * K + kk] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < BK; ++kk) {
+            float a[4], b[NB][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) b[nb][j] = Bs[nb][kk][tx * 4 + j];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[nb][i][j] = fmaf(a[i], b[nb][j], acc[nb][i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t row = tc.row0 + ty * 4 + i;
+        if (row >= tc.row_end) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int col = tc.n0 + tx * 4 + j;
+            if (col >= n_out) continue;
+            float out;
+            if (EPI == EPI_SWIGLU) {
+                out = silu_f(acc[0][i][j]) * acc[NB - 1][i][j];
+            } else {
+                const float bc = bias != nullptr ? bias[(int64_t)tc.e * n_out + col] : 0.f;
+                out = EPI == EPI_GELU_BIAS ? gelu_f(acc[0][i][j] + bc) : acc[0][i][j] + bc;
+            }
+            C[row * n_out + col] = out;
+        }
+    }
+}
+
+GemmPlan plan_gemm(int dtype, int64_t rows_per_group_hint, int n_out, int K) {
+    (void)rows_per_group_hint;
+    (void)n_out;
+    (void)K;
+    GemmPlan p;
+    p.bm = dtype == MOE_BF16 ? 128 : 64;
+    return p;
+}
+
+void launch_ffn_schedule(const int32_t* offsets, int e_begin, int n_groups, int bm, int32_t* tile_start,
+                         hipStream_t s) {
+    ffn_schedule_kernel<<<1, 1024, 0, s>>>(offsets, e_begin, n_groups, bm, tile_start);
+}
+
+template <int BM, int BN, int WM, int WN>
+static void launch_bf16_tiles(int epi, const void* A, const void* B, const void* bias, void* C,
+                              const int32_t* offsets, const int32_t* tile_start, int e_begin, int n_groups,
+                              int64_t max_rows, int64_t dense_rows, int n_out, int K, hipStream_t s) {
+    const int bno = epi == EPI_SWIGLU ? BN / 2 : BN;
+    const int64_t m_tiles = offsets ? (max_rows + BM - 1) / BM + n_groups : (dense_rows + BM - 1) / BM;
+    const int64_t n_tiles = (n_out + bno - 1) / bno;
+    const unsigned grid = (unsigned)(m_tiles * n_tiles);
+    const auto a = static_cast<const uint16_t*>(A);
+    const auto b = static_cast<const uint16_t*>(B);
+    const auto bi = static_cast<const uint16_t*>(bias);
+    auto c = static_cast<uint16_t*>(C);
+    if (epi == EPI_SWIGLU)
+        gemm_bf16_kernel<BM, BN, WM, WN, EPI_SWIGLU><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, tile_start, e_begin,
+                                                                         n_groups, dense_rows, n_out, K);
+    else if (epi == EPI_GELU_BIAS)
+        gemm_bf16_kernel<BM, BN, WM, WN, EPI_GELU_BIAS><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, tile_start,
+                                                                            e_begin, n_groups, dense_rows, n_out, K);
+    else
+        gemm_bf16_kernel<BM, BN, WM, WN, EPI_BIAS><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, tile_start, e_begin,
+                                                                       n_groups, dense_rows, n_out, K);
+}
+
+void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* B, const void* bias, void* C,
+                         const int32_t* offsets, const int32_t* tile_start, int e_begin, int n_groups,
+                         int64_t max_rows, int64_t dense_rows, int n_out, int K, hipStream_t s) {
+    if (dtype == MOE_BF16) {
+        (void)bm;
+        launch_bf16_tiles<128, 128, 2, 2>(epi, A, B, bias, C, offsets, tile_start, e_begin, n_groups, max_rows,
+                                          dense_rows, n_out, K, s);
+        return;
+    }
+    const int64_t m_tiles = offsets ? (max_rows + 63) / 64 + n_groups : (dense_rows + 63) / 64;
+    const unsigned grid = (unsigned)(m_tiles * ((n_out + 63) / 64));
+    const auto a = static_cast<const float*>(A);
+    const auto b = static_cast<const float*>(B);
+    const auto bi = static_cast<const float*>(bias);
+    auto c = static_cast<float*>(C);
+    if (epi == EPI_SWIGLU)
+        gemm_f32_kernel<EPI_SWIGLU><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, tile_start, e_begin, n_groups,
+                                                         dense_rows, n_out, K);
+    else if (epi == EPI_GELU_BIAS)
+        gemm_f32_kernel<EPI_GELU_BIAS><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, tile_start, e_begin, n_groups,
+                                                            dense_rows, n_out, K);
+    else
+        gemm_f32_kernel<EPI_BIAS><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, tile_start, e_begin, n_groups,
+                                                       dense_rows, n_out, K);
+}
+
+}  // namespace moe

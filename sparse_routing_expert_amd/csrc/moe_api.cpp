@@ -1,0 +1,341 @@
+// libmoe C ABI (include/moe.h): argument validation, workspace planning and stage launches.
+// Every check runs before the first HIP call, so a rejected call enqueues nothing and the
+// validation paths run on hosts without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+#include "../../include/moe.h"
+#include "moe_kernels.h"
+
+namespace {
+
+using moe::kPermTile;
+using moe::kRouteTokensPerBlock;
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int check_shape(const moe_shape* s) {
+    if (s == nullptr) return MOE_ERR_INVALID_ARG;
+    if (s->T < 0 || s->E < 1 || s->E > 1024 || s->k < 1 || s->k > s->E || s->k > 32) return MOE_ERR_INVALID_ARG;
+    if (s->d_model <= 0 || s->d_ff <= 0 || s->d_ff_shared < 0) return MOE_ERR_INVALID_ARG;
+    if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+    if (s->act != MOE_GELU_MLP && s->act != MOE_SWIGLU) return MOE_ERR_INVALID_ARG;
+    if (s->score != MOE_SOFTMAX && s->score != MOE_SIGMOID) return MOE_ERR_INVALID_ARG;
+    if (s->renorm != 0 && s->renorm != 1) return MOE_ERR_INVALID_ARG;
+    if (s->T * (int64_t)s->k > (int64_t)INT32_MAX) return MOE_ERR_INVALID_ARG;
+    if (s->score == MOE_SIGMOID && s->renorm != 1) return MOE_ERR_UNSUPPORTED;
+    const int mult = s->dtype == MOE_BF16 ? 64 : 4;
+    if (s->d_model % mult || s->d_ff % mult || s->d_ff_shared % mult) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+inline int elem_bytes(const moe_shape* s) { return s->dtype == MOE_BF16 ? 2 : 4; }
+
+// ---- workspace layouts (each region 256-byte aligned) ----------------------------------------
+struct Carver {
+    size_t off = 0;
+    size_t take(size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    }
+};
+
+struct RouteWs {
+    size_t logits, blk_counts, blk_P, blk_H, bytes;
+    int nblk;
+};
+RouteWs route_ws(const moe_shape* s) {
+    RouteWs w;
+    Carver c;
+    w.nblk = (int)cdiv(s->T, kRouteTokensPerBlock);
+    w.logits = c.take((size_t)s->T * s->E * 4);
+    w.blk_counts = c.take((size_t)w.nblk * s->E * 4);
+    w.blk_P = c.take((size_t)w.nblk * s->E * 4);
+    w.blk_H = c.take((size_t)w.nblk * 4);
+    w.bytes = c.off;
+    return w;
+}
+
+struct PermWs {
+    size_t tile_counts, tile_base, bytes;
+    int ntiles;
+};
+PermWs perm_ws(const moe_shape* s) {
+    PermWs w;
+    Carver c;
+    w.ntiles = (int)cdiv(s->T * s->k, kPermTile);
+    w.tile_counts = c.take((size_t)w.ntiles * s->E * 4);
+    w.tile_base = c.take((size_t)w.ntiles * s->E * 4);
+    w.bytes = c.off;
+    return w;
+}
+
+struct FfnWs {
+    size_t sched1, sched2, h, bytes;
+};
+FfnWs ffn_ws(const moe_shape* s) {
+    FfnWs w;
+    Carver c;
+    w.sched1 = c.take((size_t)(s->E + 1) * 4);
+    w.sched2 = c.take((size_t)(s->E + 1) * 4);
+    w.h = c.take((size_t)s->T * s->k * s->d_ff * elem_bytes(s));
+    w.bytes = c.off;
+    return w;
+}
+
+struct SharedWs {
+    size_t hs, bytes;
+};
+SharedWs shared_ws(const moe_shape* s) {
+    SharedWs w;
+    Carver c;
+    w.hs = c.take((size_t)s->T * s->d_ff_shared * elem_bytes(s));
+    w.bytes = c.off;
+    return w;
+}
+
+struct FwdWs {
+    size_t topk_idx, topk_w, counts, stats, offsets, sorted_token, inv_pos, x_perm, y_perm, ys, scratch, bytes;
+};
+FwdWs fwd_ws(const moe_shape* s) {
+    FwdWs w;
+    Carver c;
+    const size_t A = (size_t)s->T * s->k, eb = elem_bytes(s);
+    w.topk_idx = c.take(A * 4);
+    w.topk_w = c.take(A * 4);
+    w.counts = c.take((size_t)s->E * 4);
+    w.stats = c.take((size_t)(2 * s->E + 2) * 4);
+    w.offsets = c.take((size_t)(s->E + 1) * 4);
+    w.sorted_token = c.take(A * 4);
+    w.inv_pos = c.take(A * 4);
+    w.x_perm = c.take(A * s->d_model * eb);
+    w.y_perm = c.take(A * s->d_model * eb);
+    w.ys = c.take(s->d_ff_shared ? (size_t)s->T * s->d_model * eb : 0);
+    size_t scratch = route_ws(s).bytes;  // the stages run one after another on one stream
+    if (perm_ws(s).bytes > scratch) scratch = perm_ws(s).bytes;
+    if (ffn_ws(s).bytes > scratch) scratch = ffn_ws(s).bytes;
+    if (s->d_ff_shared && shared_ws(s).bytes > scratch) scratch = shared_ws(s).bytes;
+    w.scratch = c.take(scratch);
+    w.bytes = c.off;
+    return w;
+}
+
+template <typename T>
+inline T* at(void* ws, size_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+inline int launched() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// ---- stage bodies (arguments already validated) ------------------------------------------------
+void do_route(const moe_shape* s, const void* x, const float* w_router, const float* sel_bias, float* logits,
+              int32_t* topk_idx, float* topk_w, int32_t* counts, float* stats, void* ws, hipStream_t st) {
+    const RouteWs w = route_ws(s);
+    float* lg = logits ? logits : at<float>(ws, w.logits);
+    moe::launch_route_logits(s->dtype, x, w_router, lg, s->T, s->d_model, s->E, st);
+    moe::launch_route_select(lg, sel_bias, s->T, s->E, s->k, s->score, s->renorm, topk_idx, topk_w,
+                             at<int32_t>(ws, w.blk_counts), at<float>(ws, w.blk_P), at<float>(ws, w.blk_H), st);
+    moe::launch_route_finalize(at<int32_t>(ws, w.blk_counts), at<float>(ws, w.blk_P), at<float>(ws, w.blk_H),
+                               w.nblk, s->T, s->E, counts, stats, st);
+}
+
+void do_permute(const moe_shape* s, const int32_t* topk_idx, const void* x, int32_t* offsets,
+                int32_t* sorted_token, int32_t* inv_pos, void* x_perm, void* ws, hipStream_t st) {
+    const PermWs w = perm_ws(s);
+    const int64_t A = s->T * s->k;
+    moe::launch_perm_count(topk_idx, A, s->E, at<int32_t>(ws, w.tile_counts), st);
+    moe::launch_perm_scan(at<int32_t>(ws, w.tile_counts), w.ntiles, A, s->E, at<int32_t>(ws, w.tile_base), offsets,
+                          st);
+    moe::launch_perm_rank(topk_idx, at<int32_t>(ws, w.tile_base), A, s->E, s->k, inv_pos, sorted_token, st);
+    moe::launch_perm_scatter(x, inv_pos, s->T, s->d_model, s->k, elem_bytes(s), x_perm, st);
+}
+
+void do_ffn(const moe_shape* s, int e_begin, int e_end, const void* x_perm, const int32_t* offsets,
+            const void* w_in, const void* b_in, const void* w_out, const void* b_out, void* y_perm, void* ws,
+            hipStream_t st) {
+    const FfnWs w = ffn_ws(s);
+    const int n_groups = e_end - e_begin;
+    const int64_t A = s->T * s->k;
+    const int64_t hint = A / (s->E > 0 ? s->E : 1);
+    const bool swiglu = s->act == MOE_SWIGLU;
+    const moe::GemmPlan p1 = moe::plan_gemm(s->dtype, hint, s->d_ff, s->d_model);
+    const moe::GemmPlan p2 = moe::plan_gemm(s->dtype, hint, s->d_model, s->d_ff);
+    int32_t* ts1 = at<int32_t>(ws, w.sched1);
+    int32_t* ts2 = at<int32_t>(ws, w.sched2);
+    moe::launch_ffn_schedule(offsets, e_begin, n_groups, p1.bm, ts1, st);
+    if (p2.bm != p1.bm) moe::launch_ffn_schedule(offsets, e_begin, n_groups, p2.bm, ts2, st);
+    else ts2 = ts1;
+    void* h = at<void>(ws, w.h);
+    moe::launch_grouped_gemm(s->dtype, swiglu ? moe::EPI_SWIGLU : moe::EPI_GELU_BIAS, p1.bm, x_perm, w_in, b_in, h,
+                             offsets, ts1, e_begin, n_groups, A, 0, s->d_ff, s->d_model, st);
+    moe::launch_grouped_gemm(s->dtype, moe::EPI_BIAS, p2.bm, h, w_out, b_out, y_perm, offsets, ts2, e_begin,
+                             n_groups, A, 0, s->d_model, s->d_ff, st);
+}
+
+void do_shared(const moe_shape* s, const void* x, const void* ws_in, const void* ws_out, void* y_shared, void* ws,
+               hipStream_t st) {
+    const SharedWs w = shared_ws(s);
+    void* hs = at<void>(ws, w.hs);
+    const moe::GemmPlan p1 = moe::plan_gemm(s->dtype, s->T, s->d_ff_shared, s->d_model);
+    const moe::GemmPlan p2 = moe::plan_gemm(s->dtype, s->T, s->d_model, s->d_ff_shared);
+    moe::launch_grouped_gemm(s->dtype, moe::EPI_SWIGLU, p1.bm, x, ws_in, nullptr, hs, nullptr, nullptr, 0, 1, s->T,
+                             s->T, s->d_ff_shared, s->d_model, st);
+    moe::launch_grouped_gemm(s->dtype, moe::EPI_BIAS, p2.bm, hs, ws_out, nullptr, y_shared, nullptr, nullptr, 0, 1,
+                             s->T, s->T, s->d_model, s->d_ff_shared, st);
+}
+
+#define MOE_REQUIRE(cond)                       \
+    do {                                        \
+        if (!(cond)) return MOE_ERR_INVALID_ARG; \
+    } while (0)
+
+inline bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
+inline bool ok_opt(const void* p) { return p == nullptr || aligned16(p); }
+
+}  // namespace
+
+extern "C" {
+
+int moe_workspace_bytes(const moe_shape* shape, int stage, size_t* bytes) {
+    const int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+    switch (stage) {
+        case MOE_STAGE_ROUTE: *bytes = route_ws(shape).bytes; break;
+        case MOE_STAGE_PERMUTE: *bytes = perm_ws(shape).bytes; break;
+        case MOE_STAGE_FFN: *bytes = ffn_ws(shape).bytes; break;
+        case MOE_STAGE_SHARED: *bytes = shared_ws(shape).bytes; break;
+        case MOE_STAGE_FORWARD: *bytes = fwd_ws(shape).bytes; break;
+        default: return MOE_ERR_INVALID_ARG;
+    }
+    return MOE_OK;
+}
+
+int moe_route(const moe_shape* shape, const void* x, const float* w_router, const float* sel_bias, float* logits,
+              int32_t* topk_idx, float* topk_w, int32_t* counts, float* stats, void* ws, size_t ws_bytes,
+              moe_stream_t stream) {
+    const int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    MOE_REQUIRE(ok_ptr(x) && ok_ptr(w_router) && ok_ptr(topk_idx) && ok_ptr(topk_w) && ok_ptr(counts));
+    MOE_REQUIRE(ok_opt(sel_bias) && ok_opt(logits) && ok_opt(stats) && ok_opt(ws));
+    if (ws_bytes < route_ws(shape).bytes || (ws == nullptr && route_ws(shape).bytes > 0)) return MOE_ERR_WORKSPACE;
+    if (shape->T == 0) return MOE_OK;
+    (void)hipGetLastError();
+    do_route(shape, x, w_router, sel_bias, logits, topk_idx, topk_w, counts, stats, ws,
+             static_cast<hipStream_t>(stream));
+    return launched();
+}
+
+int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, int32_t* offsets,
+                int32_t* sorted_token, int32_t* inv_pos, void* x_perm, void* ws, size_t ws_bytes,
+                moe_stream_t stream) {
+    const int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    MOE_REQUIRE(ok_ptr(topk_idx) && ok_ptr(x) && ok_ptr(offsets) && ok_ptr(sorted_token) && ok_ptr(inv_pos) &&
+                ok_ptr(x_perm) && ok_opt(ws));
+    if (ws_bytes < perm_ws(shape).bytes || (ws == nullptr && perm_ws(shape).bytes > 0)) return MOE_ERR_WORKSPACE;
+    if (shape->T == 0) return MOE_OK;
+    (void)hipGetLastError();
+    do_permute(shape, topk_idx, x, offsets, sorted_token, inv_pos, x_perm, ws, static_cast<hipStream_t>(stream));
+    return launched();
+}
+
+int moe_grouped_ffn(const moe_shape* shape, int32_t e_begin, int32_t e_end, const void* x_perm,
+                    const int32_t* offsets, const void* w_in, const void* b_in, const void* w_out, const void* b_out,
+                    void* y_perm, void* ws, size_t ws_bytes, moe_stream_t stream) {
+    const int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    MOE_REQUIRE(e_begin >= 0 && e_begin <= e_end && e_end <= shape->E);
+    MOE_REQUIRE(ok_ptr(x_perm) && ok_ptr(offsets) && ok_ptr(w_in) && ok_ptr(w_out) && ok_ptr(y_perm) && ok_opt(ws));
+    MOE_REQUIRE(ok_opt(b_in) && ok_opt(b_out));
+    if (shape->act == MOE_SWIGLU && (b_in != nullptr || b_out != nullptr)) return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < ffn_ws(shape).bytes || ws == nullptr) return MOE_ERR_WORKSPACE;
+    if (shape->T == 0 || e_begin == e_end) return MOE_OK;
+    (void)hipGetLastError();
+    do_ffn(shape, e_begin, e_end, x_perm, offsets, w_in, b_in, w_out, b_out, y_perm, ws,
+           static_cast<hipStream_t>(stream));
+    return launched();
+}
+
+int moe_shared_ffn(const moe_shape* shape, const void* x, const void* ws_in, const void* ws_out, void* y_shared,
+                   void* ws, size_t ws_bytes, moe_stream_t stream) {
+    const int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    if (shape->d_ff_shared == 0) return MOE_ERR_INVALID_ARG;
+    MOE_REQUIRE(ok_ptr(x) && ok_ptr(ws_in) && ok_ptr(ws_out) && ok_ptr(y_shared) && ok_opt(ws));
+    if (ws_bytes < shared_ws(shape).bytes || (ws == nullptr && shared_ws(shape).bytes > 0)) return MOE_ERR_WORKSPACE;
+    if (shape->T == 0) return MOE_OK;
+    (void)hipGetLastError();
+    do_shared(shape, x, ws_in, ws_out, y_shared, ws, static_cast<hipStream_t>(stream));
+    return launched();
+}
+
+int moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* inv_pos, const float* topk_w,
+                const void* y_shared, void* y, moe_stream_t stream) {
+    const int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    MOE_REQUIRE(ok_ptr(y_perm) && ok_ptr(inv_pos) && ok_ptr(topk_w) && ok_opt(y_shared) && ok_ptr(y));
+    if (shape->T == 0) return MOE_OK;
+    (void)hipGetLastError();
+    moe::launch_combine(shape->dtype, y_perm, inv_pos, topk_w, y_shared, y, shape->T, shape->d_model, shape->k,
+                        static_cast<hipStream_t>(stream));
+    return launched();
+}
+
+int moe_forward(const moe_shape* shape, const void* x, const float* w_router, const float* sel_bias,
+                const void* w_in, const void* b_in, const void* w_out, const void* b_out, const void* ws_in,
+                const void* ws_out, void* y, int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
+                float* stats_out, void* ws, size_t ws_bytes, moe_stream_t stream) {
+    const int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    MOE_REQUIRE(ok_ptr(x) && ok_ptr(w_router) && ok_opt(sel_bias) && ok_ptr(w_in) && ok_ptr(w_out) && ok_ptr(y));
+    MOE_REQUIRE(ok_opt(b_in) && ok_opt(b_out) && ok_opt(topk_idx_out) && ok_opt(topk_w_out) &&
+                ok_opt(counts_out) && ok_opt(stats_out) && ok_opt(ws));
+    if (shape->act == MOE_SWIGLU && (b_in != nullptr || b_out != nullptr)) return MOE_ERR_INVALID_ARG;
+    if (shape->d_ff_shared > 0) MOE_REQUIRE(ok_ptr(ws_in) && ok_ptr(ws_out));
+    else MOE_REQUIRE(ws_in == nullptr && ws_out == nullptr);
+    const FwdWs w = fwd_ws(shape);
+    if (ws_bytes < w.bytes || ws == nullptr) return MOE_ERR_WORKSPACE;
+    if (shape->T == 0) return MOE_OK;
+    (void)hipGetLastError();
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, w.topk_idx);
+    float* gw = topk_w_out ? topk_w_out : at<float>(ws, w.topk_w);
+    int32_t* cnt = counts_out ? counts_out : at<int32_t>(ws, w.counts);
+    float* sts = stats_out ? stats_out : at<float>(ws, w.stats);
+    void* scratch = at<void>(ws, w.scratch);
+    int32_t* offsets = at<int32_t>(ws, w.offsets);
+    int32_t* inv_pos = at<int32_t>(ws, w.inv_pos);
+    do_route(shape, x, w_router, sel_bias, nullptr, idx, gw, cnt, sts, scratch, st);
+    do_permute(shape, idx, x, offsets, at<int32_t>(ws, w.sorted_token), inv_pos, at<void>(ws, w.x_perm), scratch,
+               st);
+    do_ffn(shape, 0, shape->E, at<void>(ws, w.x_perm), offsets, w_in, b_in, w_out, b_out, at<void>(ws, w.y_perm),
+           scratch, st);
+    void* ys = nullptr;
+    if (shape->d_ff_shared > 0) {
+        ys = at<void>(ws, w.ys);
+        do_shared(shape, x, ws_in, ws_out, ys, scratch, st);
+    }
+    moe::launch_combine(shape->dtype, at<void>(ws, w.y_perm), inv_pos, gw, ys, y, shape->T, shape->d_model, shape->k,
+                        st);
+    return launched();
+}
+
+const char* moe_status_str(int status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+        default: return "MOE_ERR_UNKNOWN";
+    }
+}
+
+}  // extern "C"

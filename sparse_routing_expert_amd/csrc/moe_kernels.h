@@ -1,0 +1,55 @@
+// Host-side launchers of the libmoe kernels (internal; the public ABI is include/moe.h).
+// Every launcher only enqueues work on `stream`; argument checks happen in moe_api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- route ------------------------------------------------------------------------------
+constexpr int kRouteTokensPerBlock = 64;  // tokens per select block (4 waves x 16 tokens)
+
+void launch_route_logits(int dtype, const void* x, const float* w_router, float* logits, int64_t T, int d,
+                         int E, hipStream_t s);
+void launch_route_select(const float* logits, const float* sel_bias, int64_t T, int E, int k, int score,
+                         int renorm, int32_t* topk_idx, float* topk_w, int32_t* blk_counts, float* blk_P,
+                         float* blk_H, hipStream_t s);
+void launch_route_finalize(const int32_t* blk_counts, const float* blk_P, const float* blk_H, int nblk,
+                           int64_t T, int E, int32_t* counts, float* stats, hipStream_t s);
+
+// ---- permute ----------------------------------------------------------------------------
+constexpr int kPermTile = 1024;  // assignments per histogram / rank tile
+
+void launch_perm_count(const int32_t* topk_idx, int64_t A, int E, int32_t* tile_counts, hipStream_t s);
+void launch_perm_scan(const int32_t* tile_counts, int ntiles, int64_t A, int E, int32_t* tile_base,
+                      int32_t* offsets, hipStream_t s);
+void launch_perm_rank(const int32_t* topk_idx, const int32_t* tile_base, int64_t A, int E, int k,
+                      int32_t* inv_pos, int32_t* sorted_token, hipStream_t s);
+void launch_perm_scatter(const void* x, const int32_t* inv_pos, int64_t T, int d, int k, int elem_bytes,
+                         void* x_perm, hipStream_t s);
+
+// ---- grouped FFN ------------------------------------------------------------------------
+enum Epilogue { EPI_SWIGLU = 0, EPI_GELU_BIAS = 1, EPI_BIAS = 2 };
+
+struct GemmPlan {
+    int bm;  // rows per tile
+};
+GemmPlan plan_gemm(int dtype, int64_t rows_per_group_hint, int n_out, int K);
+
+// Tile schedule: tile_start[g] = sum over groups g' < g of ceil(rows_g' / bm), g = 0..n_groups.
+void launch_ffn_schedule(const int32_t* offsets, int e_begin, int n_groups, int bm, int32_t* tile_start,
+                         hipStream_t s);
+
+// C[rows, n_out] = epi(A[rows, K] * B_e^T) over groups (offsets != NULL) or one dense group of
+// `dense_rows` rows (offsets == NULL). B is [E][n_b_rows][K] (n_b_rows = 2*n_out for SwiGLU).
+void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* B, const void* bias,
+                         void* C, const int32_t* offsets, const int32_t* tile_start, int e_begin,
+                         int n_groups, int64_t max_rows, int64_t dense_rows, int n_out, int K, hipStream_t s);
+
+// ---- combine ----------------------------------------------------------------------------
+void launch_combine(int dtype, const void* y_perm, const int32_t* inv_pos, const float* topk_w,
+                    const void* y_shared, void* y, int64_t T, int d, int k, hipStream_t s);
+
+}  // namespace moe

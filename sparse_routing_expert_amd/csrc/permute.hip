@@ -1,0 +1,147 @@
+// moe_permute kernels: expert histogram, exclusive scan, stable ranking and the row scatter that
+// packs every expert's tokens into one contiguous buffer ("Router Optimization Techniques",
+// What Most Articles Miss 2), each expert's rows in ascending token order -- the order of the
+// per-expert nonzero() in "Fine-tuning and serving MoE models", How an MoE layer actually works.
+//
+// Assignments a = t*k + j are cut into tiles of kPermTile. perm_count builds one LDS-atomic
+// histogram per tile (integer atomics: exact and order-independent); perm_scan turns the
+// [tile][expert] counts into expert offsets and per-tile bases; perm_rank ranks every
+// assignment inside its tile with wave ballots (stable, no atomics); perm_scatter reads each token
+// row once and writes its k copies with 128-bit stores.
+#include "moe_common.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void perm_count_kernel(const int32_t* __restrict__ idx, int64_t A, int E,
+                                                         int32_t* __restrict__ tile_counts) {
+    __shared__ int h[1024];
+    for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
+    __syncthreads();
+    const int64_t a0 = (int64_t)blockIdx.x * kPermTile;
+#pragma unroll
+    for (int it = 0; it < kPermTile / 256; ++it) {
+        const int64_t a = a0 + it * 256 + threadIdx.x;
+        if (a < A) atomicAdd(&h[idx[a]], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) tile_counts[(int64_t)blockIdx.x * E + e] = h[e];
+}
+
+// One block of 1024 threads; thread e owns expert e (E <= 1024).
+__global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restrict__ tile_counts, int ntiles,
+                                                         int E, int32_t* __restrict__ tile_base,
+                                                         int32_t* __restrict__ offsets) {
+    __shared__ int s_wave[17];
+    const int e = threadIdx.x;
+    int tot = 0;
+    if (e < E)
+        for (int tile = 0; tile < ntiles; ++tile) tot += tile_counts[(int64_t)tile * E + e];
+    int total;
+    const int start = block1024_excl_scan(tot, s_wave, &total);
+    if (e < E) {
+        offsets[e] = start;
+        int run = start;
+        for (int tile = 0; tile < ntiles; ++tile) {
+            tile_base[(int64_t)tile * E + e] = run;
+            run += tile_counts[(int64_t)tile * E + e];
+        }
+    }
+    if (e == 0) offsets[E] = total;
+}
+
+// Stable rank of each assignment within its tile. The tile is processed as 16 chunks of 64
+// consecutive assignments (chunk c = iteration * 4 + wave). Inside a chunk, lanes holding the
+// same expert are found by intersecting ballots over the bits of the expert id; the lane's rank
+// among them is the popcount below it. Chunk counts go to LDS, so
+// position = tile_base[e] + sum of counts of e in earlier chunks + rank.
+__global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restrict__ idx,
+                                                        const int32_t* __restrict__ tile_base, int64_t A,
+                                                        int E, int k, int nbits, int32_t* __restrict__ inv_pos,
+                                                        int32_t* __restrict__ sorted_token) {
+    constexpr int ITERS = kPermTile / 256;
+    constexpr int CHUNKS = kPermTile / 64;
+    extern __shared__ int cnt[];  // [CHUNKS][E]
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < CHUNKS * E; i += 256) cnt[i] = 0;
+    __syncthreads();
+    const int64_t a0 = (int64_t)blockIdx.x * kPermTile;
+    const uint64_t below = (1ull << lane) - 1ull;
+    int rank[ITERS], ev[ITERS];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+        const int64_t a = a0 + it * 256 + threadIdx.x;
+        const bool valid = a < A;
+        const int e = valid ? idx[a] : E;  // E never equals a real expert id
+        uint64_t m = ~0ull;
+        for (int b = 0; b < nbits; ++b) {
+            const int bit = (e >> b) & 1;
+            const uint64_t bb = __ballot(bit);
+            m &= bit ? bb : ~bb;
+        }
+        const int rk = __popcll(m & below);
+        if (valid && rk == 0) cnt[(it * 4 + wave) * E + e] = __popcll(m);
+        rank[it] = rk;
+        ev[it] = e;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+        const int64_t a = a0 + it * 256 + threadIdx.x;
+        if (a >= A) continue;
+        const int e = ev[it];
+        const int c = it * 4 + wave;
+        int pos = tile_base[(int64_t)blockIdx.x * E + e] + rank[it];
+        for (int c2 = 0; c2 < c; ++c2) pos += cnt[c2 * E + e];
+        inv_pos[a] = pos;
+        sorted_token[pos] = (int32_t)(a / k);
+    }
+}
+
+// One wave per token: read the row once, store it at its k destinations (16-byte vectors).
+__global__ __launch_bounds__(256) void perm_scatter_kernel(const uint8_t* __restrict__ x,
+                                                           const int32_t* __restrict__ inv_pos, int64_t T,
+                                                           int row_bytes, int k, uint8_t* __restrict__ x_perm) {
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    const int mypos = lane < k ? inv_pos[t * k + lane] : 0;
+    const int nchunks = row_bytes / 16;
+    const uint8_t* src = x + t * row_bytes;
+    for (int c = lane; c < nchunks; c += 64) {
+        const u32x4 v = ld16(src + (int64_t)c * 16);
+        for (int j = 0; j < k; ++j) {
+            const int p = __builtin_amdgcn_readlane(mypos, j);
+            st16(x_perm + (int64_t)p * row_bytes + (int64_t)c * 16, v);
+        }
+    }
+}
+
+void launch_perm_count(const int32_t* topk_idx, int64_t A, int E, int32_t* tile_counts, hipStream_t s) {
+    const unsigned ntiles = (unsigned)((A + kPermTile - 1) / kPermTile);
+    perm_count_kernel<<<ntiles, 256, 0, s>>>(topk_idx, A, E, tile_counts);
+}
+
+void launch_perm_scan(const int32_t* tile_counts, int ntiles, int64_t A, int E, int32_t* tile_base,
+                      int32_t* offsets, hipStream_t s) {
+    (void)A;
+    perm_scan_kernel<<<1, 1024, 0, s>>>(tile_counts, ntiles, E, tile_base, offsets);
+}
+
+void launch_perm_rank(const int32_t* topk_idx, const int32_t* tile_base, int64_t A, int E, int k,
+                      int32_t* inv_pos, int32_t* sorted_token, hipStream_t s) {
+    const unsigned ntiles = (unsigned)((A + kPermTile - 1) / kPermTile);
+    int nbits = 0;
+    while ((1 << nbits) <= E) ++nbits;  // ids 0..E (E = padding sentinel) fit in nbits bits
+    const size_t lds = (size_t)(kPermTile / 64) * E * sizeof(int);
+    perm_rank_kernel<<<ntiles, 256, lds, s>>>(topk_idx, tile_base, A, E, k, nbits, inv_pos, sorted_token);
+}
+
+void launch_perm_scatter(const void* x, const int32_t* inv_pos, int64_t T, int d, int k, int elem_bytes,
+                         void* x_perm, hipStream_t s) {
+    const unsigned nblk = (unsigned)((T + 3) / 4);
+    perm_scatter_kernel<<<nblk, 256, 0, s>>>(static_cast<const uint8_t*>(x), inv_pos, T, d * elem_bytes, k,
+                                             static_cast<uint8_t*>(x_perm));
+}
+
+}  // namespace moe

@@ -1,0 +1,187 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/moe.h declares, and rejects
+invalid calls on the host before any HIP call (so nothing here touches a GPU; every call below
+is one the library must refuse, or a T = 0 no-op)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_routing_expert_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # 16-byte aligned address; never dereferenced because every call is rejected first
+MISALIGNED = FAKE + 4
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libmoe.so is not built (run `python -m sparse_routing_expert_amd.build`)")
+    return L.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = header_functions()
+    assert declared == sorted(L.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert L.status_name(0) == "MOE_OK"
+    assert L.status_name(-3) == "MOE_ERR_WORKSPACE"
+    assert L.status_name(123) == "MOE_ERR_UNKNOWN"
+
+
+def good_shape(**kw):
+    args = dict(T=128, d_model=256, d_ff=128, E=8, k=2, dtype="bf16", act="swiglu", score="softmax", renorm=True)
+    args.update(kw)
+    return L.make_shape(**args)
+
+
+def ws_bytes(shape, stage):
+    out = ctypes.c_size_t(0)
+    rc = L.lib().moe_workspace_bytes(ctypes.byref(shape), stage, ctypes.byref(out))
+    return rc, out.value
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(T=-1), L.MOE_ERR_INVALID_ARG),
+    (dict(E=0), L.MOE_ERR_INVALID_ARG),
+    (dict(E=1025), L.MOE_ERR_INVALID_ARG),
+    (dict(k=0), L.MOE_ERR_INVALID_ARG),
+    (dict(k=9), L.MOE_ERR_INVALID_ARG),  # k > E
+    (dict(E=64, k=33), L.MOE_ERR_INVALID_ARG),
+    (dict(d_model=0), L.MOE_ERR_INVALID_ARG),
+    (dict(d_model=96), L.MOE_ERR_UNSUPPORTED),  # bf16 needs multiples of 64
+    (dict(d_ff=100), L.MOE_ERR_UNSUPPORTED),
+    (dict(dtype="f32", d_model=6), L.MOE_ERR_UNSUPPORTED),
+    (dict(score="sigmoid", renorm=False), L.MOE_ERR_UNSUPPORTED),
+    (dict(T=2**31, k=2), L.MOE_ERR_INVALID_ARG),  # T*k overflows int32
+])
+def test_shape_validation(lib, kw, want):
+    rc, _ = ws_bytes(good_shape(**kw), L.MOE_STAGE_FORWARD)
+    assert rc == want
+
+
+def test_bad_enums_and_stage(lib):
+    s = good_shape()
+    s.dtype = 7
+    assert ws_bytes(s, 0)[0] == L.MOE_ERR_INVALID_ARG
+    s = good_shape()
+    s.act = 5
+    assert ws_bytes(s, 0)[0] == L.MOE_ERR_INVALID_ARG
+    s = good_shape()
+    s.score = 2
+    assert ws_bytes(s, 0)[0] == L.MOE_ERR_INVALID_ARG
+    s = good_shape()
+    s.renorm = 3
+    assert ws_bytes(s, 0)[0] == L.MOE_ERR_INVALID_ARG
+    assert ws_bytes(good_shape(), 9)[0] == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_workspace_bytes(None, 0, None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_workspace_sizes_monotone(lib):
+    small = [ws_bytes(good_shape(T=64), st)[1] for st in range(5)]
+    big = [ws_bytes(good_shape(T=4096), st)[1] for st in range(5)]
+    assert all(b >= a for a, b in zip(small, big))
+    assert big[L.MOE_STAGE_FFN] >= 4096 * 2 * 128 * 2  # h = [T*k, d_ff] bf16
+    rc, n = ws_bytes(good_shape(d_ff_shared=0), L.MOE_STAGE_SHARED)
+    assert rc == 0 and n == 0
+
+
+def test_route_rejections(lib):
+    s = good_shape()
+    r = lib.moe_route
+    n = ws_bytes(s, L.MOE_STAGE_ROUTE)[1]
+    args = [ctypes.byref(s), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE, n, None]
+    for i in (1, 2, 5, 6, 7):  # required pointers
+        bad = list(args)
+        bad[i] = None
+        assert r(*bad) == L.MOE_ERR_INVALID_ARG
+        bad[i] = MISALIGNED
+        assert r(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(args)
+    bad[10] = n - 1
+    assert r(*bad) == L.MOE_ERR_WORKSPACE
+    bad = list(args)
+    bad[3] = MISALIGNED  # optional pointer, misaligned
+    assert r(*bad) == L.MOE_ERR_INVALID_ARG
+    # T = 0 is a successful no-op (no launch)
+    s0 = good_shape(T=0)
+    assert r(ctypes.byref(s0), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE, n, None) == L.MOE_OK
+
+
+def test_permute_combine_rejections(lib):
+    s = good_shape()
+    n = ws_bytes(s, L.MOE_STAGE_PERMUTE)[1]
+    p = lib.moe_permute
+    good = [ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n, None]
+    for i in range(1, 7):
+        bad = list(good)
+        bad[i] = None
+        assert p(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(good)
+    bad[8] = 0
+    assert p(*bad) == L.MOE_ERR_WORKSPACE
+    c = lib.moe_combine
+    assert c(ctypes.byref(s), None, FAKE, FAKE, None, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert c(ctypes.byref(s), FAKE, FAKE, FAKE, MISALIGNED, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert c(ctypes.byref(good_shape(T=0)), FAKE, FAKE, FAKE, None, FAKE, None) == L.MOE_OK
+
+
+def test_ffn_rejections(lib):
+    s = good_shape()
+    n = ws_bytes(s, L.MOE_STAGE_FFN)[1]
+    f = lib.moe_grouped_ffn
+    good = [ctypes.byref(s), 0, 8, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, n, None]
+    for eb, ee in ((-1, 8), (3, 2), (0, 9)):
+        bad = list(good)
+        bad[1], bad[2] = eb, ee
+        assert f(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(good)
+    bad[6] = FAKE  # bias given to a SwiGLU layer
+    assert f(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(good)
+    bad[11] = n - 256
+    assert f(*bad) == L.MOE_ERR_WORKSPACE
+    bad = list(good)
+    bad[1], bad[2] = 4, 4  # empty expert range: no-op
+    assert f(*bad) == L.MOE_OK
+    sh = lib.moe_shared_ffn
+    assert sh(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == L.MOE_ERR_INVALID_ARG  # no shared
+
+
+def test_forward_rejections(lib):
+    s = good_shape(d_ff_shared=128)
+    n = ws_bytes(s, L.MOE_STAGE_FORWARD)[1]
+    fw = lib.moe_forward
+    good = [ctypes.byref(s), FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, None, None, None, None,
+            FAKE, n, None]
+    bad = list(good)
+    bad[8] = None  # shared weights missing
+    assert fw(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(good)
+    bad[16] = n - 1
+    assert fw(*bad) == L.MOE_ERR_WORKSPACE
+    bad = list(good)
+    bad[15] = None
+    assert fw(*bad) == L.MOE_ERR_WORKSPACE
+    s2 = good_shape()
+    n2 = ws_bytes(s2, L.MOE_STAGE_FORWARD)[1]
+    assert fw(ctypes.byref(s2), FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, None, None, None,
+              None, FAKE, n2, None) == L.MOE_ERR_INVALID_ARG  # shared weights without a shared expert
+
+
+def test_binding_raises_on_missing_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(L, "_lib", None)
+    with pytest.raises(L.MoeLibraryMissing):
+        L.lib()

@@ -1,0 +1,144 @@
+"""HIP library vs the float64 oracle through the C ABI, at sizes the oracle finishes in seconds
+(several tiles, ragged tails) and on the edge cases: T = 1, E = 1 with k = 1, k = E, all-tied
+logits (lower-index rule, empty experts, one expert taking every token), expert sub-ranges, no
+renormalisation, fp32 and bf16, GELU with biases and SwiGLU, sigmoid scoring with a selection
+bias and a shared expert."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_ref as R
+from sparse_routing_expert_amd import inputs as I
+from sparse_routing_expert_amd.layer import MoeLayer
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+TINY = I.CONFIGS["tiny_fp32"]
+CASES = {
+    "tiny_fp32": TINY,
+    "tiny_fp32_T37": TINY.with_sizes(T=37),
+    "f32_swiglu_sigmoid_shared": TINY.with_sizes(act="swiglu", score="sigmoid", router="biased", E=6, k=3, T=100,
+                                                 Fs=64),
+    "bf16_gelu_bias": TINY.with_sizes(dtype="bf16", T=300, d=128, F=192, E=6, k=2),
+    "small_mini": I.mini("small_bf16", T=1000, d=256, F=320),
+    "small_norenorm": I.mini("small_bf16", T=300, d=128, F=128, renorm=False),
+    "mixtral_mini": I.mini("mixtral_prefill", T=700, d=512, F=448),
+    "mixtral_decode_mini": I.mini("mixtral_prefill", T=64, d=512, F=448),
+    "qwen_mini": I.mini("qwen3_30b_a3b", T=2000, d=256, F=192),
+    "deepseek_mini": I.mini("deepseek_v3", T=500, d=448, F=128, Fs=192),
+    "E1_k1": I.mini("small_bf16", T=300, d=128, F=128, E=1, k=1),
+    "k_eq_E": I.mini("small_bf16", T=257, d=128, F=64, E=4, k=4),
+    "T1": I.mini("deepseek_v3", T=1, d=128, F=64, Fs=64),
+}
+
+
+def poison(L):
+    for name in ("logits", "topk_w", "stats", "x_perm", "y_perm", "y", "y_shared"):
+        t = getattr(L, name)
+        if t is not None:
+            t.fill_(float("nan"))
+    for name in ("topk_idx", "counts", "offsets", "sorted_token", "inv_pos"):
+        getattr(L, name).fill_(-7)
+
+
+def make(cfg, zero_router=False):
+    torch.manual_seed(0)
+    tens = I.gen_layer(cfg, device="cuda")
+    if zero_router:
+        tens["w_r"].zero_()
+    L = MoeLayer(cfg, tens)
+    poison(L)
+    return L
+
+
+def full_check(name, cfg, L):
+    print(f"[parity] {name}: T={cfg.T} d={cfg.d} F={cfg.F} E={cfg.E} k={cfg.k} {cfg.dtype} {cfg.act} "
+          f"{cfg.score}", flush=True)
+    t = L.t
+    ref = R.route(t["x"], t["w_r"], cfg.k, cfg.score, cfg.renorm, t["sel_bias"])
+    L.route()
+    torch.cuda.synchronize()
+    n_amb = P.check_route(cfg, L, ref)
+    L.permute()
+    torch.cuda.synchronize()
+    off, st, inv = P.check_permute(cfg, L, None)
+    x_perm64 = P.np64(t["x"])[st]
+    L.ffn()
+    torch.cuda.synchronize()
+    ffn_err = P.check_ffn(cfg, L, off, x_perm64)
+    if cfg.Fs:
+        L.shared()
+        torch.cuda.synchronize()
+        ys_ref = R.shared_ffn(P.np64(t["x"]), P.np64(t["ws_in"]), P.np64(t["ws_out"]))
+        P.check_layer(cfg, L.y_shared, ys_ref)
+    L.combine()
+    torch.cuda.synchronize()
+    y_stages = L.y.clone()
+    lay = P.oracle_layer_on_gpu_routing(cfg, L)
+    err = P.check_layer(cfg, y_stages, lay.y)
+    # moe_forward = the same kernels in the same order: bitwise equal, and deterministic
+    idx_stage, gw_stage = L.topk_idx.clone(), L.topk_w.clone()
+    y_fwd = torch.full_like(L.y, float("nan"))
+    L.forward(out=y_fwd)
+    torch.cuda.synchronize()
+    assert torch.equal(y_fwd.view(torch.uint8), y_stages.view(torch.uint8)), "forward != stages"
+    assert torch.equal(L.topk_idx, idx_stage) and torch.equal(L.topk_w, gw_stage)
+    y_fwd2 = torch.full_like(L.y, float("nan"))
+    L.forward(out=y_fwd2)
+    torch.cuda.synchronize()
+    assert torch.equal(y_fwd2.view(torch.uint8), y_fwd.view(torch.uint8)), "forward not deterministic"
+    print(f"[parity] {name}: ok ambiguous={n_amb} ffn_err={ffn_err:.2e} layer_err={err:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_layer_parity(name):
+    cfg = CASES[name]
+    full_check(name, cfg, make(cfg))
+
+
+@pytest.mark.parametrize("k,E", [(2, 8), (1, 8), (8, 128), (8, 256)])
+def test_all_logits_tied(k, E):
+    """W_r = 0: every key ties, so every token takes experts 0..k-1 (lower index wins); the other
+    experts are empty and, with k = 1, one expert takes every token."""
+    cfg = I.mini("small_bf16", T=333, d=128, F=64, E=E, k=k)
+    L = make(cfg, zero_router=True)
+    full_check(f"tied_k{k}_E{E}", cfg, L)
+    idx = L.topk_idx.cpu().numpy()
+    assert (idx == np.arange(k)[None, :]).all()
+    counts = L.counts.cpu().numpy()
+    assert (counts[:k] == cfg.T).all() and (counts[k:] == 0).all()
+
+
+def test_expert_subrange():
+    """moe_grouped_ffn(e_begin, e_end) writes exactly rows [offsets[e_begin], offsets[e_end])."""
+    cfg = I.mini("mixtral_prefill", T=400, d=256, F=192)
+    L = make(cfg)
+    L.route()
+    L.permute()
+    torch.cuda.synchronize()
+    off = L.offsets.cpu().numpy()
+    x_perm64 = P.np64(L.x_perm)
+    for e0, e1 in ((2, 5), (0, 1), (7, 8), (3, 3)):
+        L.y_perm.fill_(float("nan"))
+        L.ffn(e0, e1)
+        torch.cuda.synchronize()
+        y = L.y_perm.float().cpu().numpy()
+        inside = np.zeros(y.shape[0], bool)
+        inside[off[e0]:off[e1]] = True
+        assert np.isnan(y[~inside]).all(), (e0, e1)
+        assert np.isfinite(y[inside]).all(), (e0, e1)
+        P.check_ffn(cfg, L, off, x_perm64, (e0, e1))
+
+
+def test_route_without_optional_outputs():
+    cfg = I.mini("deepseek_v3", T=200, d=128, F=64, Fs=64)
+    L = make(cfg)
+    L.route(with_logits=True, with_stats=True)
+    torch.cuda.synchronize()
+    idx1, gw1, c1 = L.topk_idx.clone(), L.topk_w.clone(), L.counts.clone()
+    poison(L)
+    L.route(with_logits=False, with_stats=False)
+    torch.cuda.synchronize()
+    assert torch.equal(L.topk_idx, idx1) and torch.equal(L.topk_w, gw1) and torch.equal(L.counts, c1)
+    assert torch.isnan(L.stats).all() and torch.isnan(L.logits).all()  # untouched
