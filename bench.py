@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE-FFN layer forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+
+A step is one moe_forward call (route, permute, grouped expert FFN, shared expert if any, combine)
+over one batch of seeded synthetic tokens already resident in HBM. Default workload: the
+Mixtral-8x7B-shaped prefill layer (T=8192, d_model=4096, d_ff=14336, E=8, top-2, bf16 SwiGLU,
+fp32 router). Prints ONE JSON line with the throughput, the roofline of the dominant kernel
+(the gate/up grouped GEMM, timed with HIP events on the stream it runs on), per-stage timings
+and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+FP32_PEAK_TFLOPS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="mixtral_prefill")
+    ap.add_argument("--stage-reps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0: automatic)")
+    return ap.parse_args()
+
+
+def stage_bytes_flops(cfg):
+    """Algorithmic bytes / flops per stage call (each input read once, each output written once)."""
+    T, d, F, E, k = cfg.T, cfg.d, cfg.F, cfg.E, cfg.k
+    A, b = T * k, cfg.elem_bytes
+    gemm1_n = 2 * F if cfg.act == "swiglu" else F
+    out = {
+        # x, router weights, top-k indices + gates, counts (logits not requested in the forward)
+        "route": dict(bytes=T * d * b + E * d * 4 + A * 8 + E * 4),
+        # top-k indices, x once, x_perm, sorted_token + inv_pos, offsets
+        "permute": dict(bytes=A * 4 + T * d * b + A * d * b + 2 * A * 4 + (E + 1) * 4),
+        "expert_up": dict(flops=2.0 * A * d * gemm1_n),
+        "expert_down": dict(flops=2.0 * A * F * d),
+        # y_perm, gates + positions, y (+ shared output)
+        "combine": dict(bytes=A * d * b + A * 8 + T * d * b + (T * d * b if cfg.Fs else 0)),
+    }
+    if cfg.Fs:
+        out["shared"] = dict(flops=2.0 * T * d * 2 * cfg.Fs + 2.0 * T * cfg.Fs * d)
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not part of "
+                                   "this build (see the sharding notes in DESIGN.md)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_routing_expert_amd import inputs as I
+    from sparse_routing_expert_amd.layer import MoeLayer
+
+    cfg = I.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    tens = I.gen_layer(cfg, device=dev)
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    L = MoeLayer(cfg, tens, device=dev)
+    stream = torch.cuda.current_stream()
+
+    # ---- the timed region: K forward steps ----------------------------------------------------
+    for _ in range(args.warmup):
+        L.forward()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        L.forward()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_per_step = wall * 1e3 / args.steps
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+    value = cfg.T / (ms_per_step / 1e3)
+
+    # ---- per-stage timings (HIP events on the launch stream, caches flushed before each) ------
+    flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+    L.route()
+    L.permute()
+    torch.cuda.synchronize()
+    stage_calls = [("route", lambda: L.route(with_logits=False)), ("permute", L.permute), ("expert_up", L.up),
+                   ("expert_down", L.down)]
+    if cfg.Fs:
+        stage_calls.append(("shared", L.shared))
+    stage_calls.append(("combine", L.combine))
+    times = {name: [] for name, _ in stage_calls}
+    for _ in range(args.stage_reps):
+        for name, fn in stage_calls:
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            times[name].append(a.elapsed_time(b))
+    del flush
+    work = stage_bytes_flops(cfg)
+    peak_tf = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_PEAK_TFLOPS
+    stages = {}
+    for name, ts in times.items():
+        ms = float(np.median(ts))
+        ent = {"ms": round(ms, 5), "ms_min": round(float(np.min(ts)), 5)}
+        w = work[name]
+        if "bytes" in w:
+            gbs = w["bytes"] / (ms * 1e-3) / 1e9
+            ent.update({"GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": w["bytes"]})
+        else:
+            tf = w["flops"] / (ms * 1e-3) / 1e12
+            ent.update({"TFLOP/s": round(tf, 1), "frac_mfma": round(tf / peak_tf, 4), "flops": w["flops"]})
+        stages[name] = ent
+    up = stages["expert_up"]
+    ffn_ms = stages["expert_up"]["ms"] + stages["expert_down"]["ms"]
+    ffn_tf = (work["expert_up"]["flops"] + work["expert_down"]["flops"]) / (ffn_ms * 1e-3) / 1e12
+    roofline = {"kernel": "gemm_bf16_kernel (expert_up: gate/up grouped GEMM + SwiGLU)" if cfg.dtype == "bf16"
+                else "gemm_f32_kernel (expert_up)",
+                "bound": "mfma" if cfg.dtype == "bf16" else "alu", "achieved": up["TFLOP/s"], "peak": peak_tf,
+                "unit": "TFLOP/s", "frac": round(up["TFLOP/s"] / peak_tf, 4), "traffic": None,
+                "algorithmic_flops_per_launch": work["expert_up"]["flops"], "avg_launch_ms": up["ms"]}
+
+    # ---- CPU oracle on a bounded sample of the same workload ----------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, L, args.cpu_tokens)
+
+    out = {
+        "metric": "routed tokens/sec per MoE layer fwd; grouped-GEMM % MFMA peak; route GB/s",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; random-init weights of the layer's shape)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "d_ff": cfg.F, "E": cfg.E, "k": cfg.k,
+                   "act": cfg.act, "score": cfg.score, "d_ff_shared": cfg.Fs, "router": cfg.router},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages": stages,
+        "grouped_ffn": {"ms": round(ffn_ms, 4), "TFLOP/s": round(ffn_tf, 1), "frac_mfma": round(ffn_tf / peak_tf, 4)},
+        "route_GB/s": stages["route"]["GB/s"],
+        "assignments_per_s": round(value * cfg.k, 1),
+        "event_ms_per_step": round(ev_ms, 4),
+        "input_gen_s": round(gen_s, 2),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, L, n_tokens: int):
+    """The float64 oracle, as it stands, on the first n tokens of the same layer (host cores)."""
+    import numpy as np
+
+    from oracle import moe_ref as R
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        cores = 1
+    if n_tokens <= 0:  # about 10-30 s of CPU work on a many-core host
+        per_tok = 6.0 * cfg.k * cfg.d * cfg.F + 2.0 * cfg.E * cfg.d + (6.0 * cfg.d * cfg.Fs if cfg.Fs else 0)
+        n_tokens = int(max(16, min(cfg.T, 4e11 / per_tok)))
+    n_tokens = min(n_tokens, cfg.T)
+    t = L.t
+    x = t["x"][:n_tokens]
+    get = R.stacked_experts(t["w_in"], t["b_in"], t["w_out"], t["b_out"])
+    t0 = time.perf_counter()
+    res = R.layer_forward(x, t["w_r"], get, cfg.k, cfg.act, cfg.score, cfg.renorm, t["sel_bias"], t["ws_in"],
+                          t["ws_out"])
+    dt = time.perf_counter() - t0
+    assert np.isfinite(res.y).all()
+    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n_tokens} of {cfg.T} tokens of the same layer, full oracle forward (route, permute, "
+                      f"per-expert fp64 loop incl. converting each used expert's bf16 weights, combine)",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

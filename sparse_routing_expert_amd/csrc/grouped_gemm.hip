@@ -4,10 +4,11 @@
 // expert). The expert FFNs are SwiGLU ((SiLU(x Wg^T) * x Wu^T) Wd^T; same page, What Is It?) or
 // Linear + GELU + Linear with biases ("Fine-tuning and serving MoE models").
 //
-// Tile schedule: ffn_schedule turns the device-side expert offsets into a prefix sum of per-
-// expert row-tile counts. The GEMM grid is an upper bound; a block decodes its linear id into
-// (row tile, column tile), finds its expert by binary search over the prefix sum and exits if it
-// is past the end, so empty experts own no tile and a ragged last tile is masked, not padded.
+// Tile schedule: every block turns the device-side expert offsets into a prefix sum of per-expert
+// row-tile counts in LDS (the host never reads the offsets, so no synchronisation). The grid is an
+// upper bound; a block decodes its linear id into (row tile, column tile), finds its expert by
+// binary search over the prefix sum and exits if it is past the end, so empty experts own no tile
+// and a ragged last tile is masked, not padded. Each projection is exactly one kernel launch.
 //
 // bf16 path: v_mfma_f32_32x32x16_bf16, 256 threads (2 x 2 waves), BM x BN x 64 tiles staged
 // through LDS with double buffering; both operands are K-contiguous and 16-byte chunks are XOR-
@@ -32,15 +33,52 @@ struct TileCoord {
     bool valid;
 };
 
+// Tile schedule of a grouped launch, built by every block from the device-side offsets (the host
+// never reads them): s_ts[g] = sum over groups g' < g of ceil(rows_g' / BM), s_ts[n_groups] = total.
+// Needs a block of 256 threads; each thread owns up to 4 consecutive groups (n_groups <= 1024).
+template <int BM>
+__device__ __forceinline__ void build_schedule(const int32_t* __restrict__ offsets, int e_begin, int n_groups,
+                                               int* s_ts, int* s_wave) {
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    int n[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int g = tid * 4 + i;
+        n[i] = 0;
+        if (g < n_groups) {
+            const int rows = offsets[e_begin + g + 1] - offsets[e_begin + g];
+            n[i] = (rows + BM - 1) / BM;
+        }
+        sum += n[i];
+    }
+    int inc = sum;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int v = __shfl_up(inc, o, kWave);
+        if (lane >= o) inc += v;
+    }
+    if (lane == kWave - 1) s_wave[wave] = inc;
+    __syncthreads();
+    int base = inc - sum;
+    for (int w = 0; w < wave; ++w) base += s_wave[w];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int g = tid * 4 + i;
+        if (g < n_groups) s_ts[g] = base;
+        base += n[i];
+    }
+    if (tid == 255) s_ts[n_groups] = base;  // thread 255 holds the last prefix
+    __syncthreads();
+}
+
 // Decode the block's linear id into a tile. Row tiles are visited in groups of GM sharing a
 // sweep over the column tiles, so blocks running together reuse the same A rows and B panels.
 template <int BM, int BNO, int GM>
-__device__ __forceinline__ TileCoord decode_tile(const int32_t* __restrict__ offsets,
-                                                 const int32_t* __restrict__ tile_start, int e_begin,
-                                                 int n_groups, int64_t dense_rows, int n_out) {
+__device__ __forceinline__ TileCoord decode_tile(const int32_t* __restrict__ offsets, const int* s_ts,
+                                                 int e_begin, int n_groups, int64_t dense_rows, int n_out) {
     TileCoord tc;
     const int n_tiles_n = (n_out + BNO - 1) / BNO;
-    const int64_t m_tiles = offsets ? (int64_t)tile_start[n_groups] : (dense_rows + BM - 1) / BM;
+    const int64_t m_tiles = offsets ? (int64_t)s_ts[n_groups] : (dense_rows + BM - 1) / BM;
     const int64_t lin = blockIdx.x;
     tc.valid = lin < m_tiles * n_tiles_n;
     if (!tc.valid) return tc;
@@ -51,14 +89,14 @@ __device__ __forceinline__ TileCoord decode_tile(const int32_t* __restrict__ off
     const int64_t mt = first_m + rem % gsz;
     tc.n0 = (int)(rem / gsz) * BNO;
     if (offsets) {
-        int lo = 0, hi = n_groups - 1;  // largest g with tile_start[g] <= mt
+        int lo = 0, hi = n_groups - 1;  // largest g with s_ts[g] <= mt
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (tile_start[mid] <= mt) lo = mid;
+            if (s_ts[mid] <= mt) lo = mid;
             else hi = mid - 1;
         }
         tc.e = e_begin + lo;
-        tc.row0 = offsets[tc.e] + (mt - tile_start[lo]) * BM;
+        tc.row0 = offsets[tc.e] + (mt - s_ts[lo]) * BM;
         tc.row_end = offsets[tc.e + 1];
     } else {
         tc.e = 0;
@@ -70,29 +108,12 @@ __device__ __forceinline__ TileCoord decode_tile(const int32_t* __restrict__ off
 
 }  // namespace
 
-// One block per group: tile_start[g] = sum_{g' < g} ceil(rows_{g'} / bm).
-__global__ __launch_bounds__(1024) void ffn_schedule_kernel(const int32_t* __restrict__ offsets, int e_begin,
-                                                            int n_groups, int bm, int32_t* __restrict__ tile_start) {
-    __shared__ int s_wave[17];
-    const int g = threadIdx.x;
-    int n = 0;
-    if (g < n_groups) {
-        const int rows = offsets[e_begin + g + 1] - offsets[e_begin + g];
-        n = (rows + bm - 1) / bm;
-    }
-    int total;
-    const int start = block1024_excl_scan(n, s_wave, &total);
-    if (g < n_groups) tile_start[g] = start;
-    if (g == 0) tile_start[n_groups] = total;
-}
-
 template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                         const uint16_t* __restrict__ B,
                                                         const uint16_t* __restrict__ bias,
                                                         uint16_t* __restrict__ C,
-                                                        const int32_t* __restrict__ offsets,
-                                                        const int32_t* __restrict__ tile_start, int e_begin,
+                                                        const int32_t* __restrict__ offsets, int e_begin,
                                                         int n_groups, int64_t dense_rows, int n_out, int K) {
     constexpr int BK = 64;
     constexpr bool GATED = EPI == EPI_SWIGLU;
@@ -107,8 +128,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
     static_assert(WM * WN == 4 && TM >= 1 && TNO >= 1 && ACH >= 1 && BCH >= 1, "tile shape");
 
     __shared__ __attribute__((aligned(16))) uint16_t lds[2][(BM + BN) * BK];
+    __shared__ int s_ts[1025];
+    __shared__ int s_wave[4];
 
-    const TileCoord tc = decode_tile<BM, BNO, 8>(offsets, tile_start, e_begin, n_groups, dense_rows, n_out);
+    if (offsets) build_schedule<BM>(offsets, e_begin, n_groups, s_ts, s_wave);
+    const TileCoord tc = decode_tile<BM, BNO, 8>(offsets, s_ts, e_begin, n_groups, dense_rows, n_out);
     if (!tc.valid) return;
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -237,15 +261,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ B,
                                                        const float* __restrict__ bias, float* __restrict__ C,
-                                                       const int32_t* __restrict__ offsets,
-                                                       const int32_t* __restrict__ tile_start, int e_begin,
+                                                       const int32_t* __restrict__ offsets, int e_begin,
                                                        int n_groups, int64_t dense_rows, int n_out, int K) {
     constexpr int BM = 64, BNO = 64, BK = 16;
     constexpr bool GATED = EPI == EPI_SWIGLU;
     constexpr int NB = GATED ? 2 : 1;
     __shared__ float As[BK][BM + 4];
     __shared__ float Bs[NB][BK][BNO + 4];
-    const TileCoord tc = decode_tile<BM, BNO, 8>(offsets, tile_start, e_begin, n_groups, dense_rows, n_out);
+    __shared__ int s_ts[1025];
+    __shared__ int s_wave[4];
+    if (offsets) build_schedule<BM>(offsets, e_begin, n_groups, s_ts, s_wave);
+    const TileCoord tc = decode_tile<BM, BNO, 8>(offsets, s_ts, e_begin, n_groups, dense_rows, n_out);
     if (!tc.valid) return;
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
     const int64_t last_row = tc.row_end - 1;
@@ -312,15 +338,9 @@ GemmPlan plan_gemm(int dtype, int64_t rows_per_group_hint, int n_out, int K) {
     return p;
 }
 
-void launch_ffn_schedule(const int32_t* offsets, int e_begin, int n_groups, int bm, int32_t* tile_start,
-                         hipStream_t s) {
-    ffn_schedule_kernel<<<1, 1024, 0, s>>>(offsets, e_begin, n_groups, bm, tile_start);
-}
-
 template <int BM, int BN, int WM, int WN>
 static void launch_bf16_tiles(int epi, const void* A, const void* B, const void* bias, void* C,
-                              const int32_t* offsets, const int32_t* tile_start, int e_begin, int n_groups,
-                              int64_t max_rows, int64_t dense_rows, int n_out, int K, hipStream_t s) {
+                              const int32_t* offsets, int e_begin, int n_groups, int64_t max_rows, int64_t dense_rows, int n_out, int K, hipStream_t s) {
     const int bno = epi == EPI_SWIGLU ? BN / 2 : BN;
     const int64_t m_tiles = offsets ? (max_rows + BM - 1) / BM + n_groups : (dense_rows + BM - 1) / BM;
     const int64_t n_tiles = (n_out + bno - 1) / bno;
@@ -330,23 +350,23 @@ static void launch_bf16_tiles(int epi, const void* A, const void* B, const void*
     const auto bi = static_cast<const uint16_t*>(bias);
     auto c = static_cast<uint16_t*>(C);
     if (epi == EPI_SWIGLU)
-        gemm_bf16_kernel<BM, BN, WM, WN, EPI_SWIGLU><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, tile_start, e_begin,
+        gemm_bf16_kernel<BM, BN, WM, WN, EPI_SWIGLU><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin,
                                                                          n_groups, dense_rows, n_out, K);
     else if (epi == EPI_GELU_BIAS)
-        gemm_bf16_kernel<BM, BN, WM, WN, EPI_GELU_BIAS><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, tile_start,
+        gemm_bf16_kernel<BM, BN, WM, WN, EPI_GELU_BIAS><<<grid, 256, 0, s>>>(a, b, bi, c, offsets,
                                                                             e_begin, n_groups, dense_rows, n_out, K);
     else
-        gemm_bf16_kernel<BM, BN, WM, WN, EPI_BIAS><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, tile_start, e_begin,
+        gemm_bf16_kernel<BM, BN, WM, WN, EPI_BIAS><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin,
                                                                        n_groups, dense_rows, n_out, K);
 }
 
 void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* B, const void* bias, void* C,
-                         const int32_t* offsets, const int32_t* tile_start, int e_begin, int n_groups,
-                         int64_t max_rows, int64_t dense_rows, int n_out, int K, hipStream_t s) {
+                         const int32_t* offsets, int e_begin, int n_groups, int64_t max_rows,
+                         int64_t dense_rows, int n_out, int K, hipStream_t s) {
     if (dtype == MOE_BF16) {
         (void)bm;
-        launch_bf16_tiles<128, 128, 2, 2>(epi, A, B, bias, C, offsets, tile_start, e_begin, n_groups, max_rows,
-                                          dense_rows, n_out, K, s);
+        launch_bf16_tiles<128, 128, 2, 2>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows,
+                                          n_out, K, s);
         return;
     }
     const int64_t m_tiles = offsets ? (max_rows + 63) / 64 + n_groups : (dense_rows + 63) / 64;
@@ -356,13 +376,13 @@ void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* 
     const auto bi = static_cast<const float*>(bias);
     auto c = static_cast<float*>(C);
     if (epi == EPI_SWIGLU)
-        gemm_f32_kernel<EPI_SWIGLU><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, tile_start, e_begin, n_groups,
+        gemm_f32_kernel<EPI_SWIGLU><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
                                                          dense_rows, n_out, K);
     else if (epi == EPI_GELU_BIAS)
-        gemm_f32_kernel<EPI_GELU_BIAS><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, tile_start, e_begin, n_groups,
+        gemm_f32_kernel<EPI_GELU_BIAS><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
                                                             dense_rows, n_out, K);
     else
-        gemm_f32_kernel<EPI_BIAS><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, tile_start, e_begin, n_groups,
+        gemm_f32_kernel<EPI_BIAS><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
                                                        dense_rows, n_out, K);
 }
 

@@ -77,13 +77,11 @@ PermWs perm_ws(const moe_shape* s) {
 }
 
 struct FfnWs {
-    size_t sched1, sched2, h, bytes;
+    size_t h, bytes;
 };
 FfnWs ffn_ws(const moe_shape* s) {
     FfnWs w;
     Carver c;
-    w.sched1 = c.take((size_t)(s->E + 1) * 4);
-    w.sched2 = c.take((size_t)(s->E + 1) * 4);
     w.h = c.take((size_t)s->T * s->k * s->d_ff * elem_bytes(s));
     w.bytes = c.off;
     return w;
@@ -156,26 +154,28 @@ void do_permute(const moe_shape* s, const int32_t* topk_idx, const void* x, int3
     moe::launch_perm_scatter(x, inv_pos, s->T, s->d_model, s->k, elem_bytes(s), x_perm, st);
 }
 
+void do_up(const moe_shape* s, int e_begin, int e_end, const void* x_perm, const int32_t* offsets,
+           const void* w_in, const void* b_in, void* h, hipStream_t st) {
+    const int64_t A = s->T * s->k;
+    const moe::GemmPlan p = moe::plan_gemm(s->dtype, A / s->E, s->d_ff, s->d_model);
+    moe::launch_grouped_gemm(s->dtype, s->act == MOE_SWIGLU ? moe::EPI_SWIGLU : moe::EPI_GELU_BIAS, p.bm, x_perm,
+                             w_in, b_in, h, offsets, e_begin, e_end - e_begin, A, 0, s->d_ff, s->d_model, st);
+}
+
+void do_down(const moe_shape* s, int e_begin, int e_end, const void* h, const int32_t* offsets, const void* w_out,
+             const void* b_out, void* y_perm, hipStream_t st) {
+    const int64_t A = s->T * s->k;
+    const moe::GemmPlan p = moe::plan_gemm(s->dtype, A / s->E, s->d_model, s->d_ff);
+    moe::launch_grouped_gemm(s->dtype, moe::EPI_BIAS, p.bm, h, w_out, b_out, y_perm, offsets, e_begin,
+                             e_end - e_begin, A, 0, s->d_model, s->d_ff, st);
+}
+
 void do_ffn(const moe_shape* s, int e_begin, int e_end, const void* x_perm, const int32_t* offsets,
             const void* w_in, const void* b_in, const void* w_out, const void* b_out, void* y_perm, void* ws,
             hipStream_t st) {
-    const FfnWs w = ffn_ws(s);
-    const int n_groups = e_end - e_begin;
-    const int64_t A = s->T * s->k;
-    const int64_t hint = A / (s->E > 0 ? s->E : 1);
-    const bool swiglu = s->act == MOE_SWIGLU;
-    const moe::GemmPlan p1 = moe::plan_gemm(s->dtype, hint, s->d_ff, s->d_model);
-    const moe::GemmPlan p2 = moe::plan_gemm(s->dtype, hint, s->d_model, s->d_ff);
-    int32_t* ts1 = at<int32_t>(ws, w.sched1);
-    int32_t* ts2 = at<int32_t>(ws, w.sched2);
-    moe::launch_ffn_schedule(offsets, e_begin, n_groups, p1.bm, ts1, st);
-    if (p2.bm != p1.bm) moe::launch_ffn_schedule(offsets, e_begin, n_groups, p2.bm, ts2, st);
-    else ts2 = ts1;
-    void* h = at<void>(ws, w.h);
-    moe::launch_grouped_gemm(s->dtype, swiglu ? moe::EPI_SWIGLU : moe::EPI_GELU_BIAS, p1.bm, x_perm, w_in, b_in, h,
-                             offsets, ts1, e_begin, n_groups, A, 0, s->d_ff, s->d_model, st);
-    moe::launch_grouped_gemm(s->dtype, moe::EPI_BIAS, p2.bm, h, w_out, b_out, y_perm, offsets, ts2, e_begin,
-                             n_groups, A, 0, s->d_model, s->d_ff, st);
+    void* h = at<void>(ws, ffn_ws(s).h);
+    do_up(s, e_begin, e_end, x_perm, offsets, w_in, b_in, h, st);
+    do_down(s, e_begin, e_end, h, offsets, w_out, b_out, y_perm, st);
 }
 
 void do_shared(const moe_shape* s, const void* x, const void* ws_in, const void* ws_out, void* y_shared, void* ws,
@@ -184,10 +184,10 @@ void do_shared(const moe_shape* s, const void* x, const void* ws_in, const void*
     void* hs = at<void>(ws, w.hs);
     const moe::GemmPlan p1 = moe::plan_gemm(s->dtype, s->T, s->d_ff_shared, s->d_model);
     const moe::GemmPlan p2 = moe::plan_gemm(s->dtype, s->T, s->d_model, s->d_ff_shared);
-    moe::launch_grouped_gemm(s->dtype, moe::EPI_SWIGLU, p1.bm, x, ws_in, nullptr, hs, nullptr, nullptr, 0, 1, s->T,
-                             s->T, s->d_ff_shared, s->d_model, st);
-    moe::launch_grouped_gemm(s->dtype, moe::EPI_BIAS, p2.bm, hs, ws_out, nullptr, y_shared, nullptr, nullptr, 0, 1,
-                             s->T, s->T, s->d_model, s->d_ff_shared, st);
+    moe::launch_grouped_gemm(s->dtype, moe::EPI_SWIGLU, p1.bm, x, ws_in, nullptr, hs, nullptr, 0, 1, s->T, s->T,
+                             s->d_ff_shared, s->d_model, st);
+    moe::launch_grouped_gemm(s->dtype, moe::EPI_BIAS, p2.bm, hs, ws_out, nullptr, y_shared, nullptr, 0, 1, s->T, s->T,
+                             s->d_model, s->d_ff_shared, st);
 }
 
 #define MOE_REQUIRE(cond)                       \
@@ -260,6 +260,32 @@ int moe_grouped_ffn(const moe_shape* shape, int32_t e_begin, int32_t e_end, cons
     (void)hipGetLastError();
     do_ffn(shape, e_begin, e_end, x_perm, offsets, w_in, b_in, w_out, b_out, y_perm, ws,
            static_cast<hipStream_t>(stream));
+    return launched();
+}
+
+int moe_expert_up(const moe_shape* shape, int32_t e_begin, int32_t e_end, const void* x_perm, const int32_t* offsets,
+                  const void* w_in, const void* b_in, void* h, moe_stream_t stream) {
+    const int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    MOE_REQUIRE(e_begin >= 0 && e_begin <= e_end && e_end <= shape->E);
+    MOE_REQUIRE(ok_ptr(x_perm) && ok_ptr(offsets) && ok_ptr(w_in) && ok_opt(b_in) && ok_ptr(h));
+    if (shape->act == MOE_SWIGLU && b_in != nullptr) return MOE_ERR_INVALID_ARG;
+    if (shape->T == 0 || e_begin == e_end) return MOE_OK;
+    (void)hipGetLastError();
+    do_up(shape, e_begin, e_end, x_perm, offsets, w_in, b_in, h, static_cast<hipStream_t>(stream));
+    return launched();
+}
+
+int moe_expert_down(const moe_shape* shape, int32_t e_begin, int32_t e_end, const void* h, const int32_t* offsets,
+                    const void* w_out, const void* b_out, void* y_perm, moe_stream_t stream) {
+    const int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    MOE_REQUIRE(e_begin >= 0 && e_begin <= e_end && e_end <= shape->E);
+    MOE_REQUIRE(ok_ptr(h) && ok_ptr(offsets) && ok_ptr(w_out) && ok_opt(b_out) && ok_ptr(y_perm));
+    if (shape->act == MOE_SWIGLU && b_out != nullptr) return MOE_ERR_INVALID_ARG;
+    if (shape->T == 0 || e_begin == e_end) return MOE_OK;
+    (void)hipGetLastError();
+    do_down(shape, e_begin, e_end, h, offsets, w_out, b_out, y_perm, static_cast<hipStream_t>(stream));
     return launched();
 }
 

@@ -38,15 +38,12 @@ struct GemmPlan {
 };
 GemmPlan plan_gemm(int dtype, int64_t rows_per_group_hint, int n_out, int K);
 
-// Tile schedule: tile_start[g] = sum over groups g' < g of ceil(rows_g' / bm), g = 0..n_groups.
-void launch_ffn_schedule(const int32_t* offsets, int e_begin, int n_groups, int bm, int32_t* tile_start,
-                         hipStream_t s);
-
-// C[rows, n_out] = epi(A[rows, K] * B_e^T) over groups (offsets != NULL) or one dense group of
-// `dense_rows` rows (offsets == NULL). B is [E][n_b_rows][K] (n_b_rows = 2*n_out for SwiGLU).
+// C[rows, n_out] = epi(A[rows, K] * B_e^T) over groups e_begin.. (offsets != NULL; the kernel builds
+// its tile schedule from the device-side offsets) or one dense group of `dense_rows` rows
+// (offsets == NULL). B is [E][n_b_rows][K] (n_b_rows = 2*n_out for SwiGLU). One kernel launch.
 void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* B, const void* bias,
-                         void* C, const int32_t* offsets, const int32_t* tile_start, int e_begin,
-                         int n_groups, int64_t max_rows, int64_t dense_rows, int n_out, int K, hipStream_t s);
+                         void* C, const int32_t* offsets, int e_begin, int n_groups, int64_t max_rows,
+                         int64_t dense_rows, int n_out, int K, hipStream_t s);
 
 // ---- combine ----------------------------------------------------------------------------
 void launch_combine(int dtype, const void* y_perm, const int32_t* inv_pos, const float* topk_w,

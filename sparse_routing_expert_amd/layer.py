@@ -39,6 +39,7 @@ class MoeLayer:
         self.y_perm = torch.empty((A, d), dtype=dt, device=dev)
         self.y_shared = torch.empty((T_, d), dtype=dt, device=dev) if cfg.Fs else None
         self.y = torch.empty((T_, d), dtype=dt, device=dev)
+        self.h = torch.empty((A, cfg.F), dtype=dt, device=dev)
         self._ws = {}
 
     def ws(self, stage: int) -> torch.Tensor:
@@ -63,6 +64,16 @@ class MoeLayer:
         L.moe_grouped_ffn(self.shape, e_begin, self.cfg.E if e_end is None else e_end,
                           self.x_perm if x_perm is None else x_perm, self.offsets if offsets is None else offsets,
                           t["w_in"], t["b_in"], t["w_out"], t["b_out"], self.y_perm, self.ws(L.MOE_STAGE_FFN))
+
+    def up(self, e_begin=0, e_end=None):
+        t = self.t
+        L.moe_expert_up(self.shape, e_begin, self.cfg.E if e_end is None else e_end, self.x_perm, self.offsets,
+                        t["w_in"], t["b_in"], self.h)
+
+    def down(self, e_begin=0, e_end=None):
+        t = self.t
+        L.moe_expert_down(self.shape, e_begin, self.cfg.E if e_end is None else e_end, self.h, self.offsets,
+                          t["w_out"], t["b_out"], self.y_perm)
 
     def shared(self):
         t = self.t

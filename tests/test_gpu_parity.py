@@ -142,3 +142,19 @@ def test_route_without_optional_outputs():
     torch.cuda.synchronize()
     assert torch.equal(L.topk_idx, idx1) and torch.equal(L.topk_w, gw1) and torch.equal(L.counts, c1)
     assert torch.isnan(L.stats).all() and torch.isnan(L.logits).all()  # untouched
+
+
+def test_up_down_equal_grouped_ffn():
+    """The two one-launch projections reproduce moe_grouped_ffn bit for bit."""
+    cfg = I.mini("qwen3_30b_a3b", T=600, d=256, F=192)
+    L = make(cfg)
+    L.route()
+    L.permute()
+    L.ffn()
+    torch.cuda.synchronize()
+    y1 = L.y_perm.clone()
+    L.y_perm.fill_(float("nan"))
+    L.up()
+    L.down()
+    torch.cuda.synchronize()
+    assert torch.equal(L.y_perm.view(torch.int16), y1.view(torch.int16))
