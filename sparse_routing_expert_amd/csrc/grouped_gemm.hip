@@ -1,20 +1,29 @@
-// moe_grouped_ffn / moe_shared_ffn kernels: all experts' FFN products as one grouped GEMM launch
-// per projection ("Router Optimization Techniques", Production Deployment 1 and What Most Articles
-// Miss 2: one grouped-GEMM kernel over a contiguous token workspace instead of one kernel per
-// expert). The expert FFNs are SwiGLU ((SiLU(x Wg^T) * x Wu^T) Wd^T; same page, What Is It?) or
-// Linear + GELU + Linear with biases ("Fine-tuning and serving MoE models").
+// moe_expert_up / moe_expert_down / moe_shared_ffn kernels: all experts' FFN products as one grouped
+// GEMM launch per projection ("Router Optimization Techniques", Production Deployment 1 and What
+// Most Articles Miss 2: one grouped-GEMM kernel over a contiguous token workspace instead of one
+// kernel per expert). The expert FFNs are SwiGLU ((SiLU(x Wg^T) * x Wu^T) Wd^T; same page, What Is
+// It?) or Linear + GELU + Linear with biases ("Fine-tuning and serving MoE models").
 //
 // Tile schedule: every block turns the device-side expert offsets into a prefix sum of per-expert
-// row-tile counts in LDS (the host never reads the offsets, so no synchronisation). The grid is an
-// upper bound; a block decodes its linear id into (row tile, column tile), finds its expert by
-// binary search over the prefix sum and exits if it is past the end, so empty experts own no tile
-// and a ragged last tile is masked, not padded. Each projection is exactly one kernel launch.
+// row-tile counts in LDS (the host never reads the offsets, so there is no synchronisation). The
+// grid is an upper bound; a block decodes its id into (expert, row tile, column tile) and exits
+// when it is past the end, so empty experts own no tile and a ragged last tile is masked, not
+// padded. Blocks are dealt round-robin to the 8 XCDs (block i runs on XCD i % 8), so the decode
+// hands each XCD a contiguous chunk of an expert-major tile sequence in which groups of GM row
+// tiles sweep the column panels: the row tiles that share a weight panel run on the same XCD and
+// read it through that XCD's L2 once.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16, 256 threads (2 x 2 waves), BM x BN x 64 tiles staged
-// through LDS with double buffering; both operands are K-contiguous and 16-byte chunks are XOR-
-// swizzled by row so the 128-bit LDS reads of a 32-row MFMA operand hit distinct banks. The
-// SwiGLU epilogue gets gate and up columns of the same output in the same lane (the B tile holds
-// BN/2 gate rows then the matching BN/2 up rows) and writes SiLU(g)*u rounded once to bf16.
+// bf16 path (one kernel per projection): 256 threads = 2 x 2 waves, a BM x BN output tile (SwiGLU:
+// BN/2 gate columns and the matching BN/2 up columns, so a lane holds gate and up of the same
+// output element), v_mfma_f32_32x32x16_bf16 with fp32 accumulators. Operands stream into an NS-
+// stage LDS ring (K slices of 32) with buffer_load ... lds (global -> LDS without registers),
+// issued NS-1 stages ahead; buffer descriptors bound each tile's rows, so rows past an expert's end
+// or columns past n_out read as zero and nothing is clamped. LDS rows are 64 bytes; their four
+// 16-byte chunks are XOR-swizzled by (row >> 2) & 3, which measured conflict-free for the 128-bit
+// operand reads on gfx950 (16 lanes per LDS cycle, 64 banks). The steady-state loop is straight-
+// line with its issue order pinned: MFMAs of one 16-wide K half interleaved with the LDS reads of
+// the next half, then after the stage barrier the next stage's first-half reads and the DMA of
+// stage +NS-1. Waits on the DMA are explicit (vmcnt), because the compiler cannot see it.
 #include "moe_common.h"
 #include "moe_kernels.h"
 #include "../../include/moe.h"
@@ -22,6 +31,8 @@
 namespace moe {
 
 namespace {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 __device__ __forceinline__ float gelu_f(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
@@ -33,9 +44,8 @@ struct TileCoord {
     bool valid;
 };
 
-// Tile schedule of a grouped launch, built by every block from the device-side offsets (the host
-// never reads them): s_ts[g] = sum over groups g' < g of ceil(rows_g' / BM), s_ts[n_groups] = total.
-// Needs a block of 256 threads; each thread owns up to 4 consecutive groups (n_groups <= 1024).
+// s_ts[g] = sum over groups g' < g of ceil(rows_g' / BM); s_ts[n_groups] = total (n_groups <= 1024).
+// Needs a block of 256 threads; each thread owns up to 4 consecutive groups.
 template <int BM>
 __device__ __forceinline__ void build_schedule(const int32_t* __restrict__ offsets, int e_begin, int n_groups,
                                                int* s_ts, int* s_wave) {
@@ -67,36 +77,47 @@ __device__ __forceinline__ void build_schedule(const int32_t* __restrict__ offse
         if (g < n_groups) s_ts[g] = base;
         base += n[i];
     }
-    if (tid == 255) s_ts[n_groups] = base;  // thread 255 holds the last prefix
+    if (tid == 255) s_ts[n_groups] = base;
     __syncthreads();
 }
 
-// Decode the block's linear id into a tile. Row tiles are visited in groups of GM sharing a
-// sweep over the column tiles, so blocks running together reuse the same A rows and B panels.
+// Block id -> tile: XCD-contiguous chunks of an expert-major sequence; inside an expert, groups of
+// GM row tiles sweep the column tiles (row tile fastest).
 template <int BM, int BNO, int GM>
 __device__ __forceinline__ TileCoord decode_tile(const int32_t* __restrict__ offsets, const int* s_ts,
                                                  int e_begin, int n_groups, int64_t dense_rows, int n_out) {
     TileCoord tc;
     const int n_tiles_n = (n_out + BNO - 1) / BNO;
     const int64_t m_tiles = offsets ? (int64_t)s_ts[n_groups] : (dense_rows + BM - 1) / BM;
-    const int64_t lin = blockIdx.x;
-    tc.valid = lin < m_tiles * n_tiles_n;
+    const int64_t R = m_tiles * n_tiles_n;
+    const int64_t per = (R + 7) / 8;
+    const int64_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int64_t lin = xcd * per + slot;
+    tc.valid = slot < per && lin < R;
     if (!tc.valid) return tc;
-    const int64_t grp = lin / ((int64_t)GM * n_tiles_n);
-    const int64_t first_m = grp * GM;
-    const int64_t gsz = m_tiles - first_m < GM ? m_tiles - first_m : GM;
-    const int64_t rem = lin - grp * GM * n_tiles_n;
-    const int64_t mt = first_m + rem % gsz;
-    tc.n0 = (int)(rem / gsz) * BNO;
+    int g = 0;
+    int64_t g_mt = m_tiles, local = lin;
     if (offsets) {
-        int lo = 0, hi = n_groups - 1;  // largest g with s_ts[g] <= mt
+        const int64_t key = lin / n_tiles_n;  // group g owns [s_ts[g] * NT, s_ts[g + 1] * NT)
+        int lo = 0, hi = n_groups - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (s_ts[mid] <= mt) lo = mid;
+            if (s_ts[mid] <= key) lo = mid;
             else hi = mid - 1;
         }
-        tc.e = e_begin + lo;
-        tc.row0 = offsets[tc.e] + (mt - s_ts[lo]) * BM;
+        g = lo;
+        g_mt = s_ts[g + 1] - s_ts[g];
+        local = lin - (int64_t)s_ts[g] * n_tiles_n;
+    }
+    const int64_t grp = local / ((int64_t)GM * n_tiles_n);
+    const int64_t first_m = grp * GM;
+    const int64_t gsz = g_mt - first_m < GM ? g_mt - first_m : GM;
+    const int64_t rem = local - grp * GM * n_tiles_n;
+    const int64_t mt = first_m + rem % gsz;  // row tile within the group
+    tc.n0 = (int)(rem / gsz) * BNO;
+    if (offsets) {
+        tc.e = e_begin + g;
+        tc.row0 = offsets[tc.e] + mt * BM;
         tc.row_end = offsets[tc.e + 1];
     } else {
         tc.e = 0;
@@ -106,66 +127,114 @@ __device__ __forceinline__ TileCoord decode_tile(const int32_t* __restrict__ off
     return tc;
 }
 
+// Raw buffer resource (gfx9 layout): base, stride 0, byte range; word 3 = 0x00020000.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t b = (uint64_t)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from the buffer (byte offset voff + soff) into LDS at m0 + 16 * lane. Written as
+// inline asm so the compiler's conservative wait-before-every-LDS-read for LDS DMA does not apply;
+// the waits are placed explicitly with wait_vm. No register is written by the instruction.
+__device__ __forceinline__ void dma16(uint32_t m0, int voff, i32x4 rsrc, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// wait until at most n stages of NQ DMA instructions each are in flight (0 <= n <= 6)
+template <int NQ>
+__device__ __forceinline__ void wait_stages(int n) {
+    if (n <= 0) wait_vm<0>();
+    else if (n == 1) wait_vm<NQ>();
+    else if (n == 2) wait_vm<2 * NQ>();
+    else if (n == 3) wait_vm<3 * NQ>();
+    else if (n == 4) wait_vm<4 * NQ>();
+    else if (n == 5) wait_vm<5 * NQ>();
+    else wait_vm<6 * NQ>();
+}
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+
 }  // namespace
 
-template <int BM, int BN, int WM, int WN, int EPI>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
-                                                        const uint16_t* __restrict__ B,
-                                                        const uint16_t* __restrict__ bias,
-                                                        uint16_t* __restrict__ C,
-                                                        const int32_t* __restrict__ offsets, int e_begin,
-                                                        int n_groups, int64_t dense_rows, int n_out, int K) {
-    constexpr int BK = 64;
+template <int BM, int BN, int EPI, int NS, int GM>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
+                                                           const uint16_t* __restrict__ B,
+                                                           const uint16_t* __restrict__ bias,
+                                                           uint16_t* __restrict__ C,
+                                                           const int32_t* __restrict__ offsets, int e_begin,
+                                                           int n_groups, int64_t dense_rows, int n_out, int K) {
+    constexpr int BK = 32, WM = 2, WN = 2;
     constexpr bool GATED = EPI == EPI_SWIGLU;
-    constexpr int WTM = BM / WM;
-    constexpr int TM = WTM / 32;
-    constexpr int BNO = GATED ? BN / 2 : BN;  // output columns per block
-    constexpr int WTNO = BNO / WN;            // output columns per wave
-    constexpr int TNO = WTNO / 32;
-    constexpr int TN = GATED ? 2 * TNO : TNO;  // B sub-tiles per wave
-    constexpr int ACH = BM * 8 / 256;          // 16-byte A chunks per thread per stage
-    constexpr int BCH = BN * 8 / 256;
-    static_assert(WM * WN == 4 && TM >= 1 && TNO >= 1 && ACH >= 1 && BCH >= 1, "tile shape");
+    constexpr int WTM = BM / WM, TM = WTM / 32;
+    constexpr int BNO = GATED ? BN / 2 : BN, WTNO = BNO / WN, TNO = WTNO / 32, TN = GATED ? 2 * TNO : TNO;
+    constexpr int ROWS = BM + BN;           // 64-byte LDS rows per stage
+    constexpr int STAGE_ELEMS = ROWS * BK;  // bf16 elements per stage
+    constexpr int STAGE_BYTES = STAGE_ELEMS * 2;
+    constexpr int NQ = ROWS / 64;  // 1 KB DMA instructions per wave per stage
+    static_assert(TM >= 1 && TNO >= 1 && BM % 64 == 0 && BN % 128 == 0 && NS >= 4 && NS <= 8, "tile shape");
+    constexpr int STEPS_A = TM * TN > TM + TN ? TM * TN : TM + TN;
+    constexpr int STEPS_B = TM * TN > TM + TN + NQ ? TM * TN : TM + TN + NQ;
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][(BM + BN) * BK];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE_ELEMS];
     __shared__ int s_ts[1025];
     __shared__ int s_wave[4];
 
     if (offsets) build_schedule<BM>(offsets, e_begin, n_groups, s_ts, s_wave);
-    const TileCoord tc = decode_tile<BM, BNO, 8>(offsets, s_ts, e_begin, n_groups, dense_rows, n_out);
+    const TileCoord tc = decode_tile<BM, BNO, GM>(offsets, s_ts, e_begin, n_groups, dense_rows, n_out);
     if (!tc.valid) return;
 
-    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM, wn = wave / WM;
-    const int64_t last_row = tc.row_end - 1;
     const int64_t n_b_rows = GATED ? 2 * (int64_t)n_out : n_out;
     const uint16_t* Bg = B + (int64_t)tc.e * n_b_rows * K;
+    const int64_t a_rows = tc.row_end - tc.row0 < BM ? tc.row_end - tc.row0 : BM;
+    const int bn_part = GATED ? BN / 2 : BN;
+    const int bcols = n_out - tc.n0 < bn_part ? n_out - tc.n0 : bn_part;
+    const i32x4 ra = make_rsrc(A + tc.row0 * K, (uint32_t)(a_rows * K * 2));
+    const i32x4 rb0 = make_rsrc(Bg + (int64_t)tc.n0 * K, (uint32_t)((int64_t)bcols * K * 2));
+    const i32x4 rb1 = make_rsrc(Bg + (int64_t)(GATED ? n_out + tc.n0 : tc.n0) * K, (uint32_t)((int64_t)bcols * K * 2));
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)lds;
 
-    const uint16_t* a_src[ACH];
-    int a_dst[ACH];
+    // DMA q of this wave covers LDS rows [(q * 4 + wave) * 16, +16) of a stage; lane -> (row, chunk)
+    int voff[NQ];
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-        const int q = tid + i * 256, r = q >> 3, c = q & 7;
-        const int64_t gr = tc.row0 + r <= last_row ? tc.row0 + r : last_row;
-        a_src[i] = A + gr * K + c * 8;
-        a_dst[i] = r * BK + ((c ^ (r & 7)) << 3);
+    for (int q = 0; q < NQ; ++q) {
+        const int R = (q * 4 + wave) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ swz(R);
+        int row;
+        if (q < BM / 64) row = R;
+        else if (!GATED || q < (BM + BN / 2) / 64) row = R - BM;
+        else row = R - BM - BN / 2;
+        voff[q] = row * K * 2 + c * 16;
     }
-    const uint16_t* b_src[BCH];
-    int b_dst[BCH];
+    // operand rows of this lane
+    int a_off[TM], a_sw[TM], b_off[TN], b_sw[TN];
 #pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-        const int q = tid + i * 256, r = q >> 3, c = q & 7;
-        int64_t br;
-        if (GATED) {
-            const int rr = r < BN / 2 ? r : r - BN / 2;
-            const int col = tc.n0 + rr < n_out ? tc.n0 + rr : n_out - 1;
-            br = r < BN / 2 ? col : (int64_t)n_out + col;
-        } else {
-            br = tc.n0 + r < n_out ? tc.n0 + r : n_out - 1;
-        }
-        b_src[i] = Bg + br * K + c * 8;
-        b_dst[i] = BM * BK + r * BK + ((c ^ (r & 7)) << 3);
+    for (int i = 0; i < TM; ++i) {
+        const int r = wm * WTM + i * 32 + (lane & 31);
+        a_off[i] = r * BK;
+        a_sw[i] = swz(r);
     }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int jj = j < TNO ? j : j - TNO;
+        const int r = BM + (GATED && j >= TNO ? BN / 2 : 0) + wn * WTNO + jj * 32 + (lane & 31);
+        b_off[j] = r * BK;
+        b_sw[j] = swz(r);
+    }
+    const int khalf = lane >> 5;
 
     floatx16 acc[TM][TN];
 #pragma unroll
@@ -174,65 +243,97 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
         for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    bf16x8 fa[2][TM], fb[2][TN];
 
-    u32x4 ra[ACH], rb[BCH];
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) ra[i] = ld16(a_src[i]);
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) rb[i] = ld16(b_src[i]);
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) st16(&lds[0][a_dst[i]], ra[i]);
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) st16(&lds[0][b_dst[i]], rb[i]);
-    __syncthreads();
-
-    // LDS rows of this lane's operands
-    int a_row[TM], b_row[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) a_row[i] = wm * WTM + i * 32 + (lane & 31);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int jj = j < TNO ? j : j - TNO;
-        b_row[j] = BM + (GATED && j >= TNO ? BN / 2 : 0) + wn * WTNO + jj * 32 + (lane & 31);
+#define MOE_ISSUE(kt_)                                                                                    \
+    {                                                                                                     \
+        const int kt__ = (kt_);                                                                           \
+        const uint32_t sbase = lds_base + (kt__ % NS) * STAGE_BYTES + wave * 1024;                        \
+        const int soff = __builtin_amdgcn_readfirstlane(kt__ * BK * 2);                                   \
+        _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                                  \
+            const i32x4 rs = q < BM / 64 ? ra : ((!GATED || q < (BM + BN / 2) / 64) ? rb0 : rb1);         \
+            dma16(sbase + q * 4096, voff[q], rs, soff);                                                   \
+        }                                                                                                 \
     }
-    const int khalf = lane >> 5;
+#define MOE_FREAD(slot_, kk, f)                                                                           \
+    {                                                                                                     \
+        const uint16_t* L_ = lds + (slot_) * STAGE_ELEMS;                                                 \
+        const int c_ = (kk) * 2 + khalf;                                                                  \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i) fa[f][i] =                                          \
+            *reinterpret_cast<const bf16x8*>(L_ + a_off[i] + ((c_ ^ a_sw[i]) << 3));                      \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j) fb[f][j] =                                          \
+            *reinterpret_cast<const bf16x8*>(L_ + b_off[j] + ((c_ ^ b_sw[j]) << 3));                      \
+    }
+#define MOE_MMA(f)                                                                                        \
+    _Pragma("unroll") for (int i = 0; i < TM; ++i) _Pragma("unroll") for (int j = 0; j < TN; ++j)         \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][i], fb[f][j], acc[i][j], 0, 0, 0);
 
     const int nk = K / BK;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            const int koff = (kt + 1) * BK;
 #pragma unroll
-            for (int i = 0; i < ACH; ++i) ra[i] = ld16(a_src[i] + koff);
+    for (int p = 0; p < NS - 1; ++p)
+        if (p < nk) MOE_ISSUE(p);
+    wait_stages<NQ>((nk < NS - 1 ? nk : NS - 1) - 1);
+    lds_barrier();
+    MOE_FREAD(0, 0, 0);
+    int kt = 0;
+    for (; kt + NS - 1 < nk; ++kt) {
+        // phase A: MFMAs on the first K half of stage kt, reads of its second half
+        {
+            const uint16_t* L1 = lds + (kt % NS) * STAGE_ELEMS;
+            const int c1 = 2 + khalf;
 #pragma unroll
-            for (int i = 0; i < BCH; ++i) rb[i] = ld16(b_src[i] + koff);
+            for (int t = 0; t < STEPS_A; ++t) {
+                if (t < TM * TN)
+                    acc[t / TN][t % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][t / TN], fb[0][t % TN],
+                                                                                  acc[t / TN][t % TN], 0, 0, 0);
+                if (t < TM) fa[1][t] = *reinterpret_cast<const bf16x8*>(L1 + a_off[t] + ((c1 ^ a_sw[t]) << 3));
+                else if (t < TM + TN)
+                    fb[1][t - TM] =
+                        *reinterpret_cast<const bf16x8*>(L1 + b_off[t - TM] + ((c1 ^ b_sw[t - TM]) << 3));
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        const uint16_t* L = lds[cur];
+        // stage kt+1 has landed for every wave, and stage kt-1's slot is free for stage kt+NS-1
+        wait_vm<(NS - 3) * NQ>();
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        // phase B: MFMAs on the second half; reads of stage kt+1's first half; DMA of stage kt+NS-1
+        {
+            const int ktn = kt + NS - 1;
+            const uint32_t sbase = lds_base + (ktn % NS) * STAGE_BYTES + wave * 1024;
+            const int soff = __builtin_amdgcn_readfirstlane(ktn * BK * 2);
+            const uint16_t* L0 = lds + ((kt + 1) % NS) * STAGE_ELEMS;
+            const int c0 = khalf;
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int c = kk * 2 + khalf;
-            bf16x8 af[TM], bfr[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(L + a_row[i] * BK + ((c ^ (a_row[i] & 7)) << 3));
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8*>(L + b_row[j] * BK + ((c ^ (b_row[j] & 7)) << 3));
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            for (int t = 0; t < STEPS_B; ++t) {
+                if (t < TM * TN)
+                    acc[t / TN][t % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][t / TN], fb[1][t % TN],
+                                                                                  acc[t / TN][t % TN], 0, 0, 0);
+                if (t < TM) {
+                    fa[0][t] = *reinterpret_cast<const bf16x8*>(L0 + a_off[t] + ((c0 ^ a_sw[t]) << 3));
+                } else if (t < TM + TN) {
+                    fb[0][t - TM] =
+                        *reinterpret_cast<const bf16x8*>(L0 + b_off[t - TM] + ((c0 ^ b_sw[t - TM]) << 3));
+                } else if (t - TM - TN < NQ) {
+                    const int q = t - TM - TN;
+                    const i32x4 rs = q < BM / 64 ? ra : ((!GATED || q < (BM + BN / 2) / 64) ? rb0 : rb1);
+                    dma16(sbase + q * 4096, voff[q], rs, soff);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        if (more) {
-#pragma unroll
-            for (int i = 0; i < ACH; ++i) st16(&lds[cur ^ 1][a_dst[i]], ra[i]);
-#pragma unroll
-            for (int i = 0; i < BCH; ++i) st16(&lds[cur ^ 1][b_dst[i]], rb[i]);
-        }
-        __syncthreads();
     }
+    for (; kt < nk; ++kt) {  // the last NS - 1 stages (already in flight)
+        MOE_FREAD(kt % NS, 1, 1);
+        MOE_MMA(0);
+        if (kt + 1 < nk) wait_stages<NQ>(nk - kt - 2);
+        lds_barrier();
+        if (kt + 1 < nk) MOE_FREAD((kt + 1) % NS, 0, 0);
+        MOE_MMA(1);
+    }
+#undef MOE_ISSUE
+#undef MOE_FREAD
+#undef MOE_MMA
 
     // Epilogue. 32x32 accumulator: lane holds column lane%32 and rows 8*(v/4) + 4*(lane/32) + v%4.
 #pragma unroll
@@ -334,56 +435,57 @@ GemmPlan plan_gemm(int dtype, int64_t rows_per_group_hint, int n_out, int K) {
     (void)n_out;
     (void)K;
     GemmPlan p;
-    p.bm = dtype == MOE_BF16 ? 128 : 64;
+    p.bm = dtype == MOE_BF16 ? 256 : 64;
     return p;
 }
 
-template <int BM, int BN, int WM, int WN>
-static void launch_bf16_tiles(int epi, const void* A, const void* B, const void* bias, void* C,
-                              const int32_t* offsets, int e_begin, int n_groups, int64_t max_rows, int64_t dense_rows, int n_out, int K, hipStream_t s) {
+template <int BM, int BN, int NS, int GM>
+void launch_bf16_tiles(int epi, const void* A, const void* B, const void* bias, void* C, const int32_t* offsets,
+                       int e_begin, int n_groups, int64_t max_rows, int64_t dense_rows, int n_out, int K,
+                       hipStream_t s) {
     const int bno = epi == EPI_SWIGLU ? BN / 2 : BN;
     const int64_t m_tiles = offsets ? (max_rows + BM - 1) / BM + n_groups : (dense_rows + BM - 1) / BM;
     const int64_t n_tiles = (n_out + bno - 1) / bno;
-    const unsigned grid = (unsigned)(m_tiles * n_tiles);
+    const int64_t tiles = m_tiles * n_tiles;
+    const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);  // whole XCD rounds
     const auto a = static_cast<const uint16_t*>(A);
     const auto b = static_cast<const uint16_t*>(B);
     const auto bi = static_cast<const uint16_t*>(bias);
     auto c = static_cast<uint16_t*>(C);
     if (epi == EPI_SWIGLU)
-        gemm_bf16_kernel<BM, BN, WM, WN, EPI_SWIGLU><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin,
-                                                                         n_groups, dense_rows, n_out, K);
+        gemm_bf16_kernel<BM, BN, EPI_SWIGLU, NS, GM><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
+                                                                         dense_rows, n_out, K);
     else if (epi == EPI_GELU_BIAS)
-        gemm_bf16_kernel<BM, BN, WM, WN, EPI_GELU_BIAS><<<grid, 256, 0, s>>>(a, b, bi, c, offsets,
-                                                                            e_begin, n_groups, dense_rows, n_out, K);
+        gemm_bf16_kernel<BM, BN, EPI_GELU_BIAS, NS, GM><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin,
+                                                                            n_groups, dense_rows, n_out, K);
     else
-        gemm_bf16_kernel<BM, BN, WM, WN, EPI_BIAS><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin,
-                                                                       n_groups, dense_rows, n_out, K);
+        gemm_bf16_kernel<BM, BN, EPI_BIAS, NS, GM><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
+                                                                       dense_rows, n_out, K);
 }
 
 void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* B, const void* bias, void* C,
-                         const int32_t* offsets, int e_begin, int n_groups, int64_t max_rows,
-                         int64_t dense_rows, int n_out, int K, hipStream_t s) {
+                         const int32_t* offsets, int e_begin, int n_groups, int64_t max_rows, int64_t dense_rows,
+                         int n_out, int K, hipStream_t s) {
     if (dtype == MOE_BF16) {
         (void)bm;
-        launch_bf16_tiles<128, 128, 2, 2>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows,
-                                          n_out, K, s);
+        launch_bf16_tiles<256, 256, 4, 8>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows, n_out,
+                                          K, s);
         return;
     }
     const int64_t m_tiles = offsets ? (max_rows + 63) / 64 + n_groups : (dense_rows + 63) / 64;
-    const unsigned grid = (unsigned)(m_tiles * ((n_out + 63) / 64));
+    const int64_t tiles = m_tiles * ((n_out + 63) / 64);
+    const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
     const auto a = static_cast<const float*>(A);
     const auto b = static_cast<const float*>(B);
     const auto bi = static_cast<const float*>(bias);
     auto c = static_cast<float*>(C);
     if (epi == EPI_SWIGLU)
-        gemm_f32_kernel<EPI_SWIGLU><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
-                                                         dense_rows, n_out, K);
+        gemm_f32_kernel<EPI_SWIGLU><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out, K);
     else if (epi == EPI_GELU_BIAS)
-        gemm_f32_kernel<EPI_GELU_BIAS><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
-                                                            dense_rows, n_out, K);
+        gemm_f32_kernel<EPI_GELU_BIAS><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out,
+                                                            K);
     else
-        gemm_f32_kernel<EPI_BIAS><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
-                                                       dense_rows, n_out, K);
+        gemm_f32_kernel<EPI_BIAS><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out, K);
 }
 
 }  // namespace moe
