@@ -189,7 +189,7 @@ def cpu_baseline(cfg, L, n_tokens: int):
         cores = 1
     if n_tokens <= 0:  # about 10-30 s of CPU work on a many-core host
         per_tok = 6.0 * cfg.k * cfg.d * cfg.F + 2.0 * cfg.E * cfg.d + (6.0 * cfg.d * cfg.Fs if cfg.Fs else 0)
-        n_tokens = int(max(16, min(cfg.T, 4e11 / per_tok)))
+        n_tokens = int(max(16, min(cfg.T, 3e12 / per_tok)))
     n_tokens = min(n_tokens, cfg.T)
     t = L.t
     x = t["x"][:n_tokens]

@@ -22,8 +22,10 @@
 // 16-byte chunks are XOR-swizzled by (row >> 2) & 3, which measured conflict-free for the 128-bit
 // operand reads on gfx950 (16 lanes per LDS cycle, 64 banks). The steady-state loop is straight-
 // line with its issue order pinned: MFMAs of one 16-wide K half interleaved with the LDS reads of
-// the next half, then after the stage barrier the next stage's first-half reads and the DMA of
-// stage +NS-1. Waits on the DMA are explicit (vmcnt), because the compiler cannot see it.
+// the next half and, evenly spaced (one every four MFMAs), half of a future stage's DMA. Each CU
+// moves about 64 bytes per clock from L1/L2, so a stage's operands need roughly half the MFMA time;
+// bunched loads would stall the waves' in-order issue, MFMAs included. Waits on the DMA are
+// explicit (vmcnt), because the compiler cannot see it.
 #include "moe_common.h"
 #include "moe_kernels.h"
 #include "../../include/moe.h"
@@ -182,17 +184,25 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
     constexpr int STAGE_ELEMS = ROWS * BK;  // bf16 elements per stage
     constexpr int STAGE_BYTES = STAGE_ELEMS * 2;
     constexpr int NQ = ROWS / 64;  // 1 KB DMA instructions per wave per stage
-    static_assert(TM >= 1 && TNO >= 1 && BM % 64 == 0 && BN % 128 == 0 && NS >= 4 && NS <= 8, "tile shape");
+    static_assert(TM >= 1 && TNO >= 1 && BM % 64 == 0 && BN % 128 == 0 && NS >= 4 && NS <= 9, "tile shape");
+    // one phase = max(MFMAs, fragment reads) pinned steps; a wave's DMAs go out every SP steps
     constexpr int STEPS_A = TM * TN > TM + TN ? TM * TN : TM + TN;
-    constexpr int STEPS_B = TM * TN > TM + TN + NQ ? TM * TN : TM + TN + NQ;
+    constexpr int STEPS_B = STEPS_A;
+    constexpr int SP = STEPS_A / (NQ - NQ / 2) > 0 ? STEPS_A / (NQ - NQ / 2) : 1;
+    constexpr int SP0 = SP > 1 ? 1 : 0;
+    static_assert(SP * (NQ - NQ / 2) <= STEPS_A, "DMA slots");
 
+    // The tile-schedule scratch (1029 ints) lives at the start of the LDS ring: it is dead once the
+    // tile is decoded, and the barrier below orders its last read before the first DMA write.
+    static_assert(NS * STAGE_BYTES >= 1029 * 4 && NS * STAGE_BYTES <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE_ELEMS];
-    __shared__ int s_ts[1025];
-    __shared__ int s_wave[4];
+    int* s_ts = reinterpret_cast<int*>(lds);
+    int* s_wave = s_ts + 1025;
 
     if (offsets) build_schedule<BM>(offsets, e_begin, n_groups, s_ts, s_wave);
     const TileCoord tc = decode_tile<BM, BNO, GM>(offsets, s_ts, e_begin, n_groups, dense_rows, n_out);
-    if (!tc.valid) return;
+    if (!tc.valid) return;  // uniform per block
+    __syncthreads();
 
     const int tid = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -245,15 +255,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
     bf16x8 fa[2][TM], fb[2][TN];
 
-#define MOE_ISSUE(kt_)                                                                                    \
+#define MOE_RSRC(q) ((q) < BM / 64 ? ra : ((!GATED || (q) < (BM + BN / 2) / 64) ? rb0 : rb1))
+#define MOE_ISSUE(kt_, q0, q1)                                                                            \
     {                                                                                                     \
         const int kt__ = (kt_);                                                                           \
         const uint32_t sbase = lds_base + (kt__ % NS) * STAGE_BYTES + wave * 1024;                        \
         const int soff = __builtin_amdgcn_readfirstlane(kt__ * BK * 2);                                   \
-        _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                                  \
-            const i32x4 rs = q < BM / 64 ? ra : ((!GATED || q < (BM + BN / 2) / 64) ? rb0 : rb1);         \
-            dma16(sbase + q * 4096, voff[q], rs, soff);                                                   \
-        }                                                                                                 \
+        _Pragma("unroll") for (int q = 0; q < NQ; ++q) if (q >= (q0) && q < (q1))                          \
+            dma16(sbase + q * 4096, voff[q], MOE_RSRC(q), soff);                                          \
     }
 #define MOE_FREAD(slot_, kk, f)                                                                           \
     {                                                                                                     \
@@ -269,27 +278,45 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][i], fb[f][j], acc[i][j], 0, 0, 0);
 
     const int nk = K / BK;
+    // DMA schedule: a stage's first NH instructions go out in phase B of one iteration and the rest in
+    // phase A of the next, one every two MFMAs, so no wave bursts the vector-memory queue.
+    constexpr int NH = NQ / 2;
+    const bool split = nk >= NS;
+    if (split) {
 #pragma unroll
-    for (int p = 0; p < NS - 1; ++p)
-        if (p < nk) MOE_ISSUE(p);
-    wait_stages<NQ>((nk < NS - 1 ? nk : NS - 1) - 1);
+        for (int p = 0; p < NS - 2; ++p) MOE_ISSUE(p, 0, NQ);
+        MOE_ISSUE(NS - 2, 0, NH);
+        wait_vm<(NS - 3) * NQ + NH>();
+    } else {
+        for (int p = 0; p < nk; ++p) MOE_ISSUE(p, 0, NQ);
+        wait_stages<NQ>(nk - 1);
+    }
     lds_barrier();
     MOE_FREAD(0, 0, 0);
     int kt = 0;
     for (; kt + NS - 1 < nk; ++kt) {
-        // phase A: MFMAs on the first K half of stage kt, reads of its second half
+        // phase A: MFMAs on the first K half of stage kt, reads of its second half, rest of stage kt+NS-2
         {
             const uint16_t* L1 = lds + (kt % NS) * STAGE_ELEMS;
             const int c1 = 2 + khalf;
+            const int kd = kt + NS - 2;
+            const uint32_t sbase = lds_base + (kd % NS) * STAGE_BYTES + wave * 1024;
+            const int soff = __builtin_amdgcn_readfirstlane(kd * BK * 2);
 #pragma unroll
             for (int t = 0; t < STEPS_A; ++t) {
                 if (t < TM * TN)
                     acc[t / TN][t % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][t / TN], fb[0][t % TN],
                                                                                   acc[t / TN][t % TN], 0, 0, 0);
-                if (t < TM) fa[1][t] = *reinterpret_cast<const bf16x8*>(L1 + a_off[t] + ((c1 ^ a_sw[t]) << 3));
-                else if (t < TM + TN)
+                if (t < TM) {
+                    fa[1][t] = *reinterpret_cast<const bf16x8*>(L1 + a_off[t] + ((c1 ^ a_sw[t]) << 3));
+                } else if (t < TM + TN) {
                     fb[1][t - TM] =
                         *reinterpret_cast<const bf16x8*>(L1 + b_off[t - TM] + ((c1 ^ b_sw[t - TM]) << 3));
+                }
+                if (t % SP == SP0 && NH + t / SP < NQ) {
+                    const int q = NH + t / SP;
+                    dma16(sbase + q * 4096, voff[q], MOE_RSRC(q), soff);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -297,11 +324,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
         wait_vm<(NS - 3) * NQ>();
         lds_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        // phase B: MFMAs on the second half; reads of stage kt+1's first half; DMA of stage kt+NS-1
+        // phase B: MFMAs on the second half; reads of stage kt+1's first half; first half of stage kt+NS-1
         {
-            const int ktn = kt + NS - 1;
-            const uint32_t sbase = lds_base + (ktn % NS) * STAGE_BYTES + wave * 1024;
-            const int soff = __builtin_amdgcn_readfirstlane(ktn * BK * 2);
+            const int kd = kt + NS - 1;
+            const uint32_t sbase = lds_base + (kd % NS) * STAGE_BYTES + wave * 1024;
+            const int soff = __builtin_amdgcn_readfirstlane(kd * BK * 2);
             const uint16_t* L0 = lds + ((kt + 1) % NS) * STAGE_ELEMS;
             const int c0 = khalf;
 #pragma unroll
@@ -314,16 +341,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
                 } else if (t < TM + TN) {
                     fb[0][t - TM] =
                         *reinterpret_cast<const bf16x8*>(L0 + b_off[t - TM] + ((c0 ^ b_sw[t - TM]) << 3));
-                } else if (t - TM - TN < NQ) {
-                    const int q = t - TM - TN;
-                    const i32x4 rs = q < BM / 64 ? ra : ((!GATED || q < (BM + BN / 2) / 64) ? rb0 : rb1);
-                    dma16(sbase + q * 4096, voff[q], rs, soff);
+                }
+                if (t % SP == SP0 && t / SP < NH) {
+                    const int q = t / SP;
+                    dma16(sbase + q * 4096, voff[q], MOE_RSRC(q), soff);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
-    for (; kt < nk; ++kt) {  // the last NS - 1 stages (already in flight)
+    if (split) MOE_ISSUE(nk - 1, NH, NQ);  // rest of the last stage
+    for (; kt < nk; ++kt) {  // the last NS - 1 stages (all issued)
         MOE_FREAD(kt % NS, 1, 1);
         MOE_MMA(0);
         if (kt + 1 < nk) wait_stages<NQ>(nk - kt - 2);
@@ -332,6 +360,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
         MOE_MMA(1);
     }
 #undef MOE_ISSUE
+#undef MOE_RSRC
 #undef MOE_FREAD
 #undef MOE_MMA
 
@@ -356,6 +385,252 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
             }
         }
     }
+}
+
+// Register-staged variant of the same tile (the one the library dispatches): operands come to
+// VGPRs with buffer loads two stages ahead (two staging sets) and each stage is written to a
+// 2-slot LDS ring with ds_write_b128. Needs less LDS than the DMA ring and leaves the waits to the
+// compiler. Same fragment layout, swizzle and epilogue as gemm_bf16_kernel; the pinned schedule
+// spreads a wave's 8 buffer loads and 8 LDS writes per stage evenly over the 32 MFMAs.
+template <int BM, int BN, int EPI, int GM>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_rs_kernel(const uint16_t* __restrict__ A,
+                                                              const uint16_t* __restrict__ B,
+                                                              const uint16_t* __restrict__ bias,
+                                                              uint16_t* __restrict__ C,
+                                                              const int32_t* __restrict__ offsets, int e_begin,
+                                                              int n_groups, int64_t dense_rows, int n_out, int K) {
+    constexpr int BK = 32, WM = 2, WN = 2, NSL = 2;
+    constexpr bool GATED = EPI == EPI_SWIGLU;
+    constexpr int WTM = BM / WM, TM = WTM / 32;
+    constexpr int BNO = GATED ? BN / 2 : BN, WTNO = BNO / WN, TNO = WTNO / 32, TN = GATED ? 2 * TNO : TNO;
+    constexpr int ROWS = BM + BN;
+    constexpr int STAGE_ELEMS = ROWS * BK;
+    constexpr int NQ = ROWS / 64;  // 16-byte chunks per thread per stage
+    static_assert(TM >= 1 && TNO >= 1 && BM % 64 == 0 && BN % 128 == 0, "tile shape");
+    constexpr int STEPS = TM * TN > 2 * NQ ? TM * TN : 2 * NQ;  // writes every other step of phase A
+    constexpr int RNH = NQ / 2;                                  // loads per phase (first half in A)
+    constexpr int RSP = STEPS / RNH;
+    static_assert(RSP >= 2 && 2 * (RNH - 1) <= RSP * (RNH - 1) + 1 && STEPS >= TM + TN, "RS slots");
+    static_assert(NSL * STAGE_ELEMS * 2 >= 1029 * 4, "schedule scratch");
+
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[NSL * STAGE_ELEMS];
+    int* s_ts = reinterpret_cast<int*>(lds);
+    int* s_wave = s_ts + 1025;
+    if (offsets) build_schedule<BM>(offsets, e_begin, n_groups, s_ts, s_wave);
+    const TileCoord tc = decode_tile<BM, BNO, GM>(offsets, s_ts, e_begin, n_groups, dense_rows, n_out);
+    if (!tc.valid) return;
+    __syncthreads();
+
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % WM, wn = wave / WM;
+    const int64_t n_b_rows = GATED ? 2 * (int64_t)n_out : n_out;
+    const uint16_t* Bg = B + (int64_t)tc.e * n_b_rows * K;
+    const int64_t a_rows = tc.row_end - tc.row0 < BM ? tc.row_end - tc.row0 : BM;
+    const int bn_part = GATED ? BN / 2 : BN;
+    const int bcols = n_out - tc.n0 < bn_part ? n_out - tc.n0 : bn_part;
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(A + tc.row0 * K), (short)0, (int)(a_rows * K * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb0 = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Bg + (int64_t)tc.n0 * K), (short)0, (int)((int64_t)bcols * K * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb1 = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Bg + (int64_t)(GATED ? n_out + tc.n0 : tc.n0) * K), (short)0, (int)((int64_t)bcols * K * 2),
+        0x00020000);
+
+    // chunk q of this thread: LDS rows [(q * 4 + wave) * 16, +16), lane -> (row, 16-byte chunk)
+    int voff[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int R = (q * 4 + wave) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ swz(R);
+        int row;
+        if (q < BM / 64) row = R;
+        else if (!GATED || q < (BM + BN / 2) / 64) row = R - BM;
+        else row = R - BM - BN / 2;
+        voff[q] = row * K * 2 + c * 16;
+    }
+    const int wofs = wave * 512 + lane * 8;  // element offset of this lane's 16 bytes in chunk q = 0
+    int a_off[TM], a_sw[TM], b_off[TN], b_sw[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int r = wm * WTM + i * 32 + (lane & 31);
+        a_off[i] = r * BK;
+        a_sw[i] = swz(r);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int jj = j < TNO ? j : j - TNO;
+        const int r = BM + (GATED && j >= TNO ? BN / 2 : 0) + wn * WTNO + jj * 32 + (lane & 31);
+        b_off[j] = r * BK;
+        b_sw[j] = swz(r);
+    }
+    const int khalf = lane >> 5;
+    floatx16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    bf16x8 fa[2][TM], fb[2][TN];
+    u32x4 stg[2][NQ];
+
+#define RS_RSRC(q) ((q) < BM / 64 ? ra : ((!GATED || (q) < (BM + BN / 2) / 64) ? rb0 : rb1))
+#define RS_LOAD1(set, q, stage)                                                                           \
+    stg[set][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(RS_RSRC(q), voff[q],    \
+                                                                                  (stage) * BK * 2, 0));
+#define RS_WRITE1(set, q, slot)                                                                           \
+    *reinterpret_cast<u32x4*>(lds + (slot) * STAGE_ELEMS + (q) * 2048 + wofs) = stg[set][q];
+#define RS_READ(slot, kk, f)                                                                              \
+    {                                                                                                     \
+        const uint16_t* L_ = lds + (slot) * STAGE_ELEMS;                                                  \
+        const int c_ = (kk) * 2 + khalf;                                                                  \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i) fa[f][i] =                                          \
+            *reinterpret_cast<const bf16x8*>(L_ + a_off[i] + ((c_ ^ a_sw[i]) << 3));                      \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j) fb[f][j] =                                          \
+            *reinterpret_cast<const bf16x8*>(L_ + b_off[j] + ((c_ ^ b_sw[j]) << 3));                      \
+    }
+    // One iteration kt: phase A = MFMAs on (kt, first K half), reads of (kt, second half), LDS write
+    // of stage kt+1 from staging set SET; barrier; phase B = MFMAs on (kt, second half), reads of
+    // (kt+1, first half), loads of stage kt+3 into SET. SET = (kt + 1) & 1 is a constant per copy.
+#define RS_STEP(kt_, SET, DO_W, DO_L)                                                                     \
+    {                                                                                                     \
+        const int ktv = (kt_);                                                                            \
+        const uint16_t* L1 = lds + (ktv & 1) * STAGE_ELEMS;                                               \
+        const int c1 = 2 + khalf;                                                                         \
+        const int wslot = (ktv + 1) & 1;                                                                  \
+        _Pragma("unroll") for (int t = 0; t < STEPS; ++t) {                                               \
+            if (t < TM * TN)                                                                              \
+                acc[t / TN][t % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][t / TN], fb[0][t % TN], \
+                                                                              acc[t / TN][t % TN], 0, 0, 0); \
+            if (t < TM) fa[1][t] = *reinterpret_cast<const bf16x8*>(L1 + a_off[t] + ((c1 ^ a_sw[t]) << 3)); \
+            else if (t < TM + TN)                                                                         \
+                fb[1][t - TM] = *reinterpret_cast<const bf16x8*>(L1 + b_off[t - TM] + ((c1 ^ b_sw[t - TM]) << 3)); \
+            if (t % 2 == 0 && t / 2 < NQ) {                                                               \
+                if (DO_W) { RS_WRITE1(SET, t / 2, wslot) }                                                \
+            }                                                                                             \
+            if (t % RSP == 1 && t / RSP < RNH) {                                                          \
+                if (DO_L) { RS_LOAD1(SET, t / RSP, ktv + 3) }                                             \
+            }                                                                                             \
+            __builtin_amdgcn_sched_barrier(0);                                                            \
+        }                                                                                                 \
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                                 \
+        __builtin_amdgcn_sched_barrier(0);                                                                \
+        const uint16_t* L0 = lds + wslot * STAGE_ELEMS;                                                   \
+        const int c0 = khalf;                                                                             \
+        const int nstage = ktv + 3;                                                                       \
+        _Pragma("unroll") for (int t = 0; t < STEPS; ++t) {                                               \
+            if (t < TM * TN)                                                                              \
+                acc[t / TN][t % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][t / TN], fb[1][t % TN], \
+                                                                              acc[t / TN][t % TN], 0, 0, 0); \
+            if (t < TM) {                                                                                 \
+                if (DO_W) fa[0][t] = *reinterpret_cast<const bf16x8*>(L0 + a_off[t] + ((c0 ^ a_sw[t]) << 3)); \
+            } else if (t < TM + TN) {                                                                     \
+                if (DO_W)                                                                                 \
+                    fb[0][t - TM] =                                                                       \
+                        *reinterpret_cast<const bf16x8*>(L0 + b_off[t - TM] + ((c0 ^ b_sw[t - TM]) << 3)); \
+            }                                                                                             \
+            if (t % RSP == 1 && RNH + t / RSP < NQ) {                                                     \
+                if (DO_L) { RS_LOAD1(SET, RNH + t / RSP, nstage) }                                        \
+            }                                                                                             \
+            __builtin_amdgcn_sched_barrier(0);                                                            \
+        }                                                                                                 \
+    }
+
+    const int nk = K / BK;
+    // prologue: stage 0 -> set 0 -> slot 0; stage 1 -> set 1; stage 2 -> set 0
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) RS_LOAD1(0, q, 0)
+    if (nk > 1) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) RS_LOAD1(1, q, 1)
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) RS_WRITE1(0, q, 0)
+    if (nk > 2) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) RS_LOAD1(0, q, 2)
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    RS_READ(0, 0, 0)
+    int kt = 0;
+    for (; kt + 4 < nk; kt += 2) {
+        RS_STEP(kt, 1, true, true)
+        RS_STEP(kt + 1, 0, true, true)
+    }
+    // tail (kt is even here; at most four iterations): plain order, static staging sets
+#define RS_TAIL(j, SET)                                                                                   \
+    if (kt + (j) < nk) {                                                                                  \
+        const int ktv = kt + (j);                                                                         \
+        const bool w = ktv + 1 < nk, l = ktv + 3 < nk;                                                    \
+        RS_READ(ktv & 1, 1, 1)                                                                            \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i) _Pragma("unroll") for (int jj = 0; jj < TN; ++jj)  \
+            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][i], fb[0][jj], acc[i][jj], 0, 0, 0); \
+        if (w) {                                                                                          \
+            _Pragma("unroll") for (int q = 0; q < NQ; ++q) { RS_WRITE1(SET, q, (ktv + 1) & 1) }           \
+        }                                                                                                 \
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                                 \
+        if (w) RS_READ((ktv + 1) & 1, 0, 0)                                                               \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i) _Pragma("unroll") for (int jj = 0; jj < TN; ++jj)  \
+            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][jj], acc[i][jj], 0, 0, 0); \
+        if (l) {                                                                                          \
+            _Pragma("unroll") for (int q = 0; q < NQ; ++q) { RS_LOAD1(SET, q, ktv + 3) }                  \
+        }                                                                                                 \
+    }
+    RS_TAIL(0, 1)
+    RS_TAIL(1, 0)
+    RS_TAIL(2, 1)
+    RS_TAIL(3, 0)
+#undef RS_TAIL
+#undef RS_RSRC
+#undef RS_LOAD1
+#undef RS_WRITE1
+#undef RS_READ
+#undef RS_STEP
+
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TNO; ++j) {
+            const int col = tc.n0 + wn * WTNO + j * 32 + (lane & 31);
+            if (col >= n_out) continue;
+            float bcol = 0.f;
+            if (EPI != EPI_SWIGLU && bias != nullptr) bcol = bf16_to_f32(bias[(int64_t)tc.e * n_out + col]);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = tc.row0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
+                if (row >= tc.row_end) continue;
+                float out;
+                if (EPI == EPI_SWIGLU) out = silu_f(acc[i][j][v]) * acc[i][j + TNO][v];
+                else if (EPI == EPI_GELU_BIAS) out = gelu_f(acc[i][j][v] + bcol);
+                else out = acc[i][j][v] + bcol;
+                C[row * n_out + col] = f32_to_bf16(out);
+            }
+        }
+    }
+}
+
+template <int BM, int BN, int GM>
+void launch_bf16_rs_tiles(int epi, const void* A, const void* B, const void* bias, void* C, const int32_t* offsets,
+                          int e_begin, int n_groups, int64_t max_rows, int64_t dense_rows, int n_out, int K,
+                          hipStream_t s) {
+    const int bno = epi == EPI_SWIGLU ? BN / 2 : BN;
+    const int64_t m_tiles = offsets ? (max_rows + BM - 1) / BM + n_groups : (dense_rows + BM - 1) / BM;
+    const int64_t tiles = m_tiles * ((n_out + bno - 1) / bno);
+    const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
+    const auto a = static_cast<const uint16_t*>(A);
+    const auto b = static_cast<const uint16_t*>(B);
+    const auto bi = static_cast<const uint16_t*>(bias);
+    auto c = static_cast<uint16_t*>(C);
+    if (epi == EPI_SWIGLU)
+        gemm_bf16_rs_kernel<BM, BN, EPI_SWIGLU, GM><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
+                                                                        dense_rows, n_out, K);
+    else if (epi == EPI_GELU_BIAS)
+        gemm_bf16_rs_kernel<BM, BN, EPI_GELU_BIAS, GM><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
+                                                                           dense_rows, n_out, K);
+    else
+        gemm_bf16_rs_kernel<BM, BN, EPI_BIAS, GM><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
+                                                                      dense_rows, n_out, K);
 }
 
 // fp32 path (SIMT, 64 x 64 output tile, 4 x 4 per thread, sequential fp32 FMA over K).
@@ -468,7 +743,7 @@ void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* 
                          int n_out, int K, hipStream_t s) {
     if (dtype == MOE_BF16) {
         (void)bm;
-        launch_bf16_tiles<256, 256, 4, 8>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows, n_out,
+        launch_bf16_rs_tiles<256, 256, 8>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows, n_out,
                                           K, s);
         return;
     }
