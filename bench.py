@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--stage-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0: automatic)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run two plain 1 GiB device copies (calibration for the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -120,6 +122,13 @@ def main():
             b.synchronize()
             times[name].append(a.elapsed_time(b))
     del flush
+    if args.copy_probe:  # a plain copy of known size: FETCH_SIZE and WRITE_SIZE should each read 1 GiB
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(3)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     work = stage_bytes_flops(cfg)
     peak_tf = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_PEAK_TFLOPS
     stages = {}
@@ -137,10 +146,11 @@ def main():
     up = stages["expert_up"]
     ffn_ms = stages["expert_up"]["ms"] + stages["expert_down"]["ms"]
     ffn_tf = (work["expert_up"]["flops"] + work["expert_down"]["flops"]) / (ffn_ms * 1e-3) / 1e12
-    roofline = {"kernel": "gemm_bf16_kernel (expert_up: gate/up grouped GEMM + SwiGLU)" if cfg.dtype == "bf16"
-                else "gemm_f32_kernel (expert_up)",
+    roofline = {"kernel": "gemm_bf16_persistent_kernel (expert_up: gate/up grouped GEMM + SwiGLU)"
+                if cfg.dtype == "bf16" else "gemm_f32_kernel (expert_up)",
                 "bound": "mfma" if cfg.dtype == "bf16" else "alu", "achieved": up["TFLOP/s"], "peak": peak_tf,
-                "unit": "TFLOP/s", "frac": round(up["TFLOP/s"] / peak_tf, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(up["TFLOP/s"] / peak_tf, 4),
+                "traffic": measured_traffic(cfg.name) if cfg.dtype == "bf16" else None,
                 "algorithmic_flops_per_launch": work["expert_up"]["flops"], "avg_launch_ms": up["ms"]}
 
     # ---- CPU oracle on a bounded sample of the same workload ----------------------------------
@@ -175,6 +185,34 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+COPY_PROBE_BYTES = 1 << 30
+GEMM_SOURCE = os.path.join(ROOT, "sparse_routing_expert_amd", "csrc", "grouped_gemm.hip")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per gate/up GEMM launch from the committed counter summary, or None.
+
+    The summary (profiles/traffic_expert_up_<workload>.md) records FETCH_SIZE + WRITE_SIZE of the
+    kernel, each scaled by the same counter's reading for a plain 1 GiB copy, together with the
+    SHA-256 of the GEMM source it was taken on. A changed kernel source makes the figure stale: None.
+    """
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"traffic_expert_up_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if line.startswith("- `") and "`: " in line:
+            key, val = line[3:].split("`: ", 1)
+            fields[key] = val.strip().strip("`")
+    with open(GEMM_SOURCE, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if fields.get("kernel_source_sha256") != sha or "hbm_bytes_per_launch" not in fields:
+        return None
+    return int(fields["hbm_bytes_per_launch"])
+
+
 def cpu_baseline(cfg, L, n_tokens: int):
     """The float64 oracle, as it stands, on the first n tokens of the same layer (host cores)."""
     import numpy as np
@@ -189,7 +227,7 @@ def cpu_baseline(cfg, L, n_tokens: int):
         cores = 1
     if n_tokens <= 0:  # about 10-30 s of CPU work on a many-core host
         per_tok = 6.0 * cfg.k * cfg.d * cfg.F + 2.0 * cfg.E * cfg.d + (6.0 * cfg.d * cfg.Fs if cfg.Fs else 0)
-        n_tokens = int(max(16, min(cfg.T, 3e12 / per_tok)))
+        n_tokens = int(max(16, min(cfg.T, 1e13 / per_tok)))
     n_tokens = min(n_tokens, cfg.T)
     t = L.t
     x = t["x"][:n_tokens]

@@ -47,15 +47,17 @@ struct TileCoord {
 };
 
 // s_ts[g] = sum over groups g' < g of ceil(rows_g' / BM); s_ts[n_groups] = total (n_groups <= 1024).
-// Needs a block of 256 threads; each thread owns up to 4 consecutive groups.
-template <int BM>
+// Needs a block of NT threads (256 or 512); each thread owns up to 1024 / NT consecutive groups.
+template <int BM, int NT>
 __device__ __forceinline__ void build_schedule(const int32_t* __restrict__ offsets, int e_begin, int n_groups,
                                                int* s_ts, int* s_wave) {
+    constexpr int GPT = 1024 / NT;
+    static_assert(NT * GPT == 1024 && NT % 64 == 0, "schedule block");
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    int n[4], sum = 0;
+    int n[GPT], sum = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int g = tid * 4 + i;
+    for (int i = 0; i < GPT; ++i) {
+        const int g = tid * GPT + i;
         n[i] = 0;
         if (g < n_groups) {
             const int rows = offsets[e_begin + g + 1] - offsets[e_begin + g];
@@ -74,12 +76,12 @@ __device__ __forceinline__ void build_schedule(const int32_t* __restrict__ offse
     int base = inc - sum;
     for (int w = 0; w < wave; ++w) base += s_wave[w];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int g = tid * 4 + i;
+    for (int i = 0; i < GPT; ++i) {
+        const int g = tid * GPT + i;
         if (g < n_groups) s_ts[g] = base;
         base += n[i];
     }
-    if (tid == 255) s_ts[n_groups] = base;
+    if (tid == NT - 1) s_ts[n_groups] = base;
     __syncthreads();
 }
 
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
     int* s_ts = reinterpret_cast<int*>(lds);
     int* s_wave = s_ts + 1025;
 
-    if (offsets) build_schedule<BM>(offsets, e_begin, n_groups, s_ts, s_wave);
+    if (offsets) build_schedule<BM, 256>(offsets, e_begin, n_groups, s_ts, s_wave);
     const TileCoord tc = decode_tile<BM, BNO, GM>(offsets, s_ts, e_begin, n_groups, dense_rows, n_out);
     if (!tc.valid) return;  // uniform per block
     __syncthreads();
@@ -387,7 +389,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
     }
 }
 
-// Register-staged variant of the same tile (the one the library dispatches): operands come to
+// Register-staged variant of the same tile: operands come to
 // VGPRs with buffer loads two stages ahead (two staging sets) and each stage is written to a
 // 2-slot LDS ring with ds_write_b128. Needs less LDS than the DMA ring and leaves the waits to the
 // compiler. Same fragment layout, swizzle and epilogue as gemm_bf16_kernel; the pinned schedule
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_rs_kernel(const uint16_t* __
     __shared__ __attribute__((aligned(1024))) uint16_t lds[NSL * STAGE_ELEMS];
     int* s_ts = reinterpret_cast<int*>(lds);
     int* s_wave = s_ts + 1025;
-    if (offsets) build_schedule<BM>(offsets, e_begin, n_groups, s_ts, s_wave);
+    if (offsets) build_schedule<BM, 256>(offsets, e_begin, n_groups, s_ts, s_wave);
     const TileCoord tc = decode_tile<BM, BNO, GM>(offsets, s_ts, e_begin, n_groups, dense_rows, n_out);
     if (!tc.valid) return;
     __syncthreads();
@@ -633,6 +635,527 @@ void launch_bf16_rs_tiles(int epi, const void* A, const void* B, const void* bia
                                                                       dense_rows, n_out, K);
 }
 
+// Eight-wave ping-pong variant of the 256 x 256 tile (two waves per SIMD). Waves 0-3 (group 0) and
+// 4-7 (group 1) each own half of the output rows; a wave computes a 64 x 128 sub-tile (SwiGLU:
+// 64 gate + 64 up columns). Every wave alternates a memory cluster (the LDS fragment reads of one
+// 32-wide K stage, its group's half of the stage D ahead as buffer_load ... lds, and the waits) and
+// a compute cluster (16 MFMAs on those fragments), with a block barrier after each. Group 1 starts
+// one barrier late, so on every SIMD one wave issues MFMAs back to back while the other issues its
+// memory operations: a stalled load no longer holds up the matrix core. Group 0 loads the A rows of
+// each stage and group 1 the B rows. The ring has D + 1 stages; a slot is refilled only after both
+// groups' reads of it have returned (lgkmcnt(0) before every barrier that ends a memory cluster).
+// Per output element the K order is the same as gemm_bf16_kernel's, so results are bitwise equal.
+template <int EPI, int GM, int D>
+__global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(const uint16_t* __restrict__ A,
+                                                              const uint16_t* __restrict__ B,
+                                                              const uint16_t* __restrict__ bias,
+                                                              uint16_t* __restrict__ C,
+                                                              const int32_t* __restrict__ offsets, int e_begin,
+                                                              int n_groups, int64_t dense_rows, int n_out, int K) {
+    constexpr int BM = 256, BN = 256, BK = 32, NS = D + 1;
+    constexpr bool GATED = EPI == EPI_SWIGLU;
+    constexpr int TM = 2;  // 64 rows per wave
+    constexpr int BNO = GATED ? BN / 2 : BN, WTNO = BNO / 2, TNO = WTNO / 32, TN = GATED ? 2 * TNO : TNO;
+    constexpr int STAGE_ELEMS = (BM + BN) * BK;  // 512 rows of 64 bytes
+    constexpr int STAGE_BYTES = STAGE_ELEMS * 2;
+    constexpr int NQ = 4;  // DMA instructions per wave per stage (a group moves 256 rows = 16 KB)
+    static_assert(TN == 4 && D >= 2 && D <= 6, "tile shape");
+    static_assert(NS * STAGE_BYTES >= 1029 * 4 && NS * STAGE_BYTES <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE_ELEMS];
+    int* s_ts = reinterpret_cast<int*>(lds);
+    int* s_wave = s_ts + 1025;
+
+    if (offsets) build_schedule<BM, 512>(offsets, e_begin, n_groups, s_ts, s_wave);
+    const TileCoord tc = decode_tile<BM, BNO, GM>(offsets, s_ts, e_begin, n_groups, dense_rows, n_out);
+    if (!tc.valid) return;  // uniform per block
+    __syncthreads();
+
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, wig = wave & 3;
+    const int wm = wig & 1, wn = wig >> 1;
+    const int64_t n_b_rows = GATED ? 2 * (int64_t)n_out : n_out;
+    const uint16_t* Bg = B + (int64_t)tc.e * n_b_rows * K;
+    const int64_t a_rows = tc.row_end - tc.row0 < BM ? tc.row_end - tc.row0 : BM;
+    const int bn_part = GATED ? BN / 2 : BN;
+    const int bcols = n_out - tc.n0 < bn_part ? n_out - tc.n0 : bn_part;
+    const i32x4 ra = make_rsrc(A + tc.row0 * K, (uint32_t)(a_rows * K * 2));
+    const i32x4 rb0 = make_rsrc(Bg + (int64_t)tc.n0 * K, (uint32_t)((int64_t)bcols * K * 2));
+    const i32x4 rb1 = make_rsrc(Bg + (int64_t)(GATED ? n_out + tc.n0 : tc.n0) * K, (uint32_t)((int64_t)bcols * K * 2));
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)lds;
+
+    // DMA q of this wave: LDS rows grp * 256 + (q * 4 + wig) * 16 + [0, 16); lane -> (row, chunk)
+    int voff[NQ];
+    i32x4 rs[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int Rl = (q * 4 + wig) * 16 + (lane >> 2);  // row within the group's 256
+        const int R = grp * 256 + Rl;
+        const int c = (lane & 3) ^ swz(R);
+        int row;
+        if (grp == 0) {
+            row = Rl;
+            rs[q] = ra;
+        } else if (GATED && q >= 2) {
+            row = Rl - 128;
+            rs[q] = rb1;
+        } else {
+            row = Rl;
+            rs[q] = rb0;
+        }
+        voff[q] = row * K * 2 + c * 16;
+    }
+    int a_off[TM], a_sw[TM], b_off[TN], b_sw[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int r = grp * 128 + wm * 64 + i * 32 + (lane & 31);
+        a_off[i] = r * BK;
+        a_sw[i] = swz(r);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int jj = j < TNO ? j : j - TNO;
+        const int r = BM + (GATED && j >= TNO ? BN / 2 : 0) + wn * WTNO + jj * 32 + (lane & 31);
+        b_off[j] = r * BK;
+        b_sw[j] = swz(r);
+    }
+    const int khalf = lane >> 5;
+
+    floatx16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    bf16x8 fa[2][TM], fb[2][TN];
+
+#define PP_ISSUE(st_)                                                                                     \
+    {                                                                                                     \
+        const int st__ = (st_);                                                                           \
+        const uint32_t sbase = lds_base + (st__ % NS) * STAGE_BYTES + grp * 16384 + wig * 1024;           \
+        const int soff = __builtin_amdgcn_readfirstlane(st__ * BK * 2);                                   \
+        _Pragma("unroll") for (int q = 0; q < NQ; ++q) dma16(sbase + q * 4096, voff[q], rs[q], soff);     \
+    }
+#define PP_READ(st_)                                                                                      \
+    {                                                                                                     \
+        const uint16_t* L_ = lds + ((st_) % NS) * STAGE_ELEMS;                                            \
+        _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                                \
+            const int c_ = kk * 2 + khalf;                                                                \
+            _Pragma("unroll") for (int i = 0; i < TM; ++i) fa[kk][i] =                                     \
+                *reinterpret_cast<const bf16x8*>(L_ + a_off[i] + ((c_ ^ a_sw[i]) << 3));                  \
+            _Pragma("unroll") for (int j = 0; j < TN; ++j) fb[kk][j] =                                     \
+                *reinterpret_cast<const bf16x8*>(L_ + b_off[j] + ((c_ ^ b_sw[j]) << 3));                  \
+        }                                                                                                 \
+    }
+#define PP_MMA                                                                                            \
+    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) _Pragma("unroll") for (int i = 0; i < TM; ++i)       \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                    \
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
+#define PP_END_MEM                                                                                        \
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                                    \
+    lds_barrier();                                                                                        \
+    __builtin_amdgcn_sched_barrier(0);
+
+    const int nk = K / BK;
+    const int npro = nk < D ? nk : D;
+    for (int p = 0; p < npro; ++p) PP_ISSUE(p)
+    wait_stages<NQ>(npro - 1);  // stage 0 of this wave has landed
+    lds_barrier();
+    if (grp == 1) lds_barrier();  // group 1 runs one cluster behind group 0
+    __builtin_amdgcn_sched_barrier(0);
+    int st = 0;
+    for (; st + D < nk; ++st) {
+        PP_READ(st)
+        PP_ISSUE(st + D)
+        wait_vm<(D - 1) * NQ>();  // stage st + 1 of this wave has landed
+        PP_END_MEM
+        PP_MMA
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (; st < nk; ++st) {
+        PP_READ(st)
+        wait_stages<NQ>(nk - st - 2);
+        PP_END_MEM
+        PP_MMA
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (grp == 0) lds_barrier();
+#undef PP_ISSUE
+#undef PP_READ
+#undef PP_MMA
+#undef PP_END_MEM
+
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TNO; ++j) {
+            const int col = tc.n0 + wn * WTNO + j * 32 + (lane & 31);
+            if (col >= n_out) continue;
+            float bcol = 0.f;
+            if (EPI != EPI_SWIGLU && bias != nullptr) bcol = bf16_to_f32(bias[(int64_t)tc.e * n_out + col]);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = tc.row0 + grp * 128 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
+                if (row >= tc.row_end) continue;
+                float out;
+                if (EPI == EPI_SWIGLU) out = silu_f(acc[i][j][v]) * acc[i][j + TNO][v];
+                else if (EPI == EPI_GELU_BIAS) out = gelu_f(acc[i][j][v] + bcol);
+                else out = acc[i][j][v] + bcol;
+                C[row * n_out + col] = f32_to_bf16(out);
+            }
+        }
+    }
+}
+
+template <int GM, int D>
+void launch_bf16_pp_tiles(int epi, const void* A, const void* B, const void* bias, void* C, const int32_t* offsets,
+                          int e_begin, int n_groups, int64_t max_rows, int64_t dense_rows, int n_out, int K,
+                          hipStream_t s) {
+    const int bno = epi == EPI_SWIGLU ? 128 : 256;
+    const int64_t m_tiles = offsets ? (max_rows + 255) / 256 + n_groups : (dense_rows + 255) / 256;
+    const int64_t tiles = m_tiles * ((n_out + bno - 1) / bno);
+    const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
+    const auto a = static_cast<const uint16_t*>(A);
+    const auto b = static_cast<const uint16_t*>(B);
+    const auto bi = static_cast<const uint16_t*>(bias);
+    auto c = static_cast<uint16_t*>(C);
+    if (epi == EPI_SWIGLU)
+        gemm_bf16_pp_kernel<EPI_SWIGLU, GM, D><<<grid, 512, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
+                                                                   dense_rows, n_out, K);
+    else if (epi == EPI_GELU_BIAS)
+        gemm_bf16_pp_kernel<EPI_GELU_BIAS, GM, D><<<grid, 512, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
+                                                                      dense_rows, n_out, K);
+    else
+        gemm_bf16_pp_kernel<EPI_BIAS, GM, D><<<grid, 512, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
+                                                                 dense_rows, n_out, K);
+}
+
+
+// Compute units of the current device (cached per device; 256 on MI355X).
+int device_cu_count() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// Persistent form of the eight-wave ping-pong tile: one block per CU walks its share of the tile
+// sequence, so the tile schedule and the expert offsets are read into LDS once per block, and the
+// LDS ring runs on across tile boundaries (the next tile's first stages arrive while the current
+// tile's last stages are multiplied). Blocks are dealt to XCDs round-robin; the 32 blocks of an XCD
+// take 32 consecutive tiles of that XCD's chunk at a time (GM row tiles x 32/GM column tiles of one
+// expert), so they share weight panels and token tiles through the XCD's L2 while running in step.
+//
+// The MFMA operands are the weight fragment first and the token fragment second, so an accumulator
+// holds a (feature x token) block: a lane owns one token and, per group of 4 registers, 4
+// consecutive output features, written with one 8-byte store. Stores and LDS-DMA loads share the
+// vector-memory counter and may complete out of order, so the memory cluster after a tile's stores
+// waits for the counter to drain before it issues new loads.
+template <int EPI, int GM, int D>
+__global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ C, const int32_t* __restrict__ offsets, int e_begin, int n_groups, int64_t dense_rows,
+    int n_out, int K) {
+    constexpr int BM = 256, BN = 256, BK = 32, NS = D + 1;
+    constexpr bool GATED = EPI == EPI_SWIGLU;
+    constexpr int TM = 2;  // 64 tokens per wave
+    constexpr int BNO = GATED ? BN / 2 : BN, WTNO = BNO / 2, TNO = WTNO / 32, TN = GATED ? 2 * TNO : TNO;
+    constexpr int STAGE_ELEMS = (BM + BN) * BK;  // 512 rows of 64 bytes
+    constexpr int STAGE_BYTES = STAGE_ELEMS * 2;
+    constexpr int NQ = 4;  // DMA instructions per wave per stage (a group moves 256 rows = 16 KB)
+    static_assert(TN == 4 && D >= 2 && D <= 5, "tile shape");
+    static_assert(NS * STAGE_BYTES + 2 * 1025 * 4 + 8 * 4 <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE_ELEMS];
+    __shared__ int s_ts[1025];   // row-tile prefix sums per group
+    __shared__ int s_off[1025];  // offsets[e_begin .. e_begin + n_groups]
+    __shared__ int s_wave[8];
+
+    const int tid = threadIdx.x, lane = lane_id();
+    if (offsets) {
+        for (int g = tid; g <= n_groups; g += 512) s_off[g] = offsets[e_begin + g];
+        build_schedule<BM, 512>(offsets, e_begin, n_groups, s_ts, s_wave);  // ends with a barrier
+    }
+    // Tile counts fit 32 bits: rows <= T * k <= 2^31 - 1 and at most 2^31 / 128 column tiles.
+    const uint32_t n_tiles_n = (uint32_t)((n_out + BNO - 1) / BNO);
+    const uint32_t m_tiles = offsets ? (uint32_t)s_ts[n_groups] : (uint32_t)((dense_rows + BM - 1) / BM);
+    const uint32_t R = m_tiles * n_tiles_n;
+    const uint32_t per = (R + 7) / 8;
+    const uint32_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
+    const uint32_t first = xcd * per + slot;
+    const uint32_t chunk_end = (xcd + 1) * per < R ? (xcd + 1) * per : R;
+    if (first >= chunk_end) return;  // uniform per block
+    const int ntile = (int)((chunk_end - 1 - first) / nslots + 1);
+
+    // lin -> tile; inside an expert, groups of GM row tiles sweep the column tiles (row tile fastest)
+    auto decode = [&](uint32_t lin, int64_t& row0, int64_t& row_end, int& e, int& n0) {
+        int g = 0;
+        uint32_t g_mt = m_tiles, local = lin;
+        if (offsets) {
+            const uint32_t key = lin / n_tiles_n;
+            int lo = 0, hi = n_groups - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if ((uint32_t)s_ts[mid] <= key) lo = mid;
+                else hi = mid - 1;
+            }
+            g = lo;
+            g_mt = (uint32_t)(s_ts[g + 1] - s_ts[g]);
+            local = lin - (uint32_t)s_ts[g] * n_tiles_n;
+        }
+        const uint32_t grp_ = local / (GM * n_tiles_n);
+        const uint32_t first_m = grp_ * GM;
+        const uint32_t gsz = g_mt - first_m < GM ? g_mt - first_m : GM;
+        const uint32_t rem = local - grp_ * GM * n_tiles_n;
+        const uint32_t col = rem / gsz;
+        const uint32_t mt = first_m + (rem - col * gsz);
+        n0 = (int)col * BNO;
+        if (offsets) {
+            e = e_begin + g;
+            row0 = s_off[g] + (int64_t)mt * BM;
+            row_end = s_off[g + 1];
+        } else {
+            e = 0;
+            row0 = (int64_t)mt * BM;
+            row_end = dense_rows;
+        }
+    };
+
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, wig = wave & 3;
+    const int wm = wig & 1, wn = wig >> 1;
+    const int64_t n_b_rows = GATED ? 2 * (int64_t)n_out : n_out;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)lds;
+
+    // DMA q of this wave: LDS rows grp * 256 + (q * 4 + wig) * 16 + [0, 16); lane -> (row, chunk).
+    // Row offsets are relative to the tile's buffer descriptors, so they hold for every tile.
+    int voff[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int Rl = (q * 4 + wig) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ swz(grp * 256 + Rl);
+        const int row = (grp == 1 && GATED && q >= 2) ? Rl - 128 : Rl;
+        voff[q] = row * K * 2 + c * 16;
+    }
+    // buffer descriptors of the tile whose stages are being loaded
+    i32x4 rs[NQ];
+    auto set_dma_tile = [&](uint32_t lin) {
+        int64_t row0, row_end;
+        int e, n0;
+        decode(lin, row0, row_end, e, n0);
+        if (grp == 0) {
+            const int64_t a_rows = row_end - row0 < BM ? row_end - row0 : BM;
+            const i32x4 ra = make_rsrc(A + row0 * K, (uint32_t)(a_rows * K * 2));
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) rs[q] = ra;
+        } else {
+            const uint16_t* Bg = B + (int64_t)e * n_b_rows * K;
+            const int bn_part = GATED ? BN / 2 : BN;
+            const int bcols = n_out - n0 < bn_part ? n_out - n0 : bn_part;
+            const i32x4 rb0 = make_rsrc(Bg + (int64_t)n0 * K, (uint32_t)((int64_t)bcols * K * 2));
+            const i32x4 rb1 =
+                make_rsrc(Bg + (int64_t)(GATED ? n_out + n0 : n0) * K, (uint32_t)((int64_t)bcols * K * 2));
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) rs[q] = (GATED && q >= 2) ? rb1 : rb0;
+        }
+    };
+
+    int a_off[TM], a_sw[TM], b_off[TN], b_sw[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int r = grp * 128 + wm * 64 + i * 32 + (lane & 31);
+        a_off[i] = r * BK;
+        a_sw[i] = swz(r);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int jj = j < TNO ? j : j - TNO;
+        const int r = BM + (GATED && j >= TNO ? BN / 2 : 0) + wn * WTNO + jj * 32 + (lane & 31);
+        b_off[j] = r * BK;
+        b_sw[j] = swz(r);
+    }
+    const int khalf = lane >> 5;
+
+    floatx16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    bf16x8 fa[2][TM], fb[2][TN];
+
+    // stage counters are kept incrementally (no division in the loop): slot in the ring, K slice in
+    // the tile
+#define PS_ISSUE(slot_, ks_)                                                                              \
+    {                                                                                                     \
+        const uint32_t sbase = lds_base + (slot_) * STAGE_BYTES + grp * 16384 + wig * 1024;               \
+        const int soff = (ks_) * (BK * 2);                                                                \
+        _Pragma("unroll") for (int q = 0; q < NQ; ++q) dma16(sbase + q * 4096, voff[q], rs[q], soff);     \
+    }
+#define PS_READ(slot_)                                                                                    \
+    {                                                                                                     \
+        const uint16_t* L_ = lds + (slot_) * STAGE_ELEMS;                                                 \
+        _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                                \
+            const int c_ = kk * 2 + khalf;                                                                \
+            _Pragma("unroll") for (int i = 0; i < TM; ++i) fa[kk][i] =                                     \
+                *reinterpret_cast<const bf16x8*>(L_ + a_off[i] + ((c_ ^ a_sw[i]) << 3));                  \
+            _Pragma("unroll") for (int j = 0; j < TN; ++j) fb[kk][j] =                                     \
+                *reinterpret_cast<const bf16x8*>(L_ + b_off[j] + ((c_ ^ b_sw[j]) << 3));                  \
+        }                                                                                                 \
+    }
+#define PS_MMA                                                                                            \
+    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) _Pragma("unroll") for (int i = 0; i < TM; ++i)       \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                    \
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk][j], fa[kk][i], acc[i][j], 0, 0, 0);
+
+    const int nk = K / BK;
+    const int G = ntile * nk;  // stages of all this block's tiles
+    const int npro = G < D ? G : D;
+    uint32_t dma_lin = first;  // tile whose stages are being issued
+    set_dma_tile(dma_lin);
+    int w_slot = 0, w_ks = 0;  // ring slot and K slice of the next stage to issue
+    for (int p = 0; p < npro; ++p) {
+        if (p > 0 && w_ks == 0) {
+            dma_lin += nslots;
+            set_dma_tile(dma_lin);
+        }
+        PS_ISSUE(w_slot, w_ks)
+        w_slot = w_slot + 1 == NS ? 0 : w_slot + 1;
+        w_ks = w_ks + 1 == nk ? 0 : w_ks + 1;
+    }
+    wait_stages<NQ>(npro - 1);  // stage 0 of this wave has landed
+    lds_barrier();
+    if (grp == 1) lds_barrier();  // group 1 runs one cluster behind group 0
+    __builtin_amdgcn_sched_barrier(0);
+
+    uint32_t cmp_lin = first;  // tile being multiplied
+    bool drain = false;        // stores of the previous tile may be in flight
+    int r_slot = 0, r_ks = 0;  // ring slot and K slice of stage g
+    for (int g = 0; g < G; ++g) {
+        // memory cluster: fragments of stage g, loads of stage g + D
+        PS_READ(r_slot)
+        if (drain) {
+            wait_vm<0>();
+            drain = false;
+        }
+        if (g + D < G) {
+            if (w_ks == 0) {
+                dma_lin += nslots;
+                set_dma_tile(dma_lin);
+            }
+            PS_ISSUE(w_slot, w_ks)
+            w_slot = w_slot + 1 == NS ? 0 : w_slot + 1;
+            w_ks = w_ks + 1 == nk ? 0 : w_ks + 1;
+            wait_vm<(D - 1) * NQ>();  // stage g + 1 of this wave has landed
+        } else {
+            wait_stages<NQ>(G - g - 2);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        // compute cluster
+        PS_MMA
+        __builtin_amdgcn_sched_barrier(0);
+        const bool tile_end = r_ks == nk - 1;
+        r_slot = r_slot + 1 == NS ? 0 : r_slot + 1;
+        r_ks = tile_end ? 0 : r_ks + 1;
+        if (tile_end) {  // last stage of a tile: epilogue of this wave's 64 x 64 (or 64 x 128) block
+            int64_t row0, row_end;
+            int e, n0;
+            decode(cmp_lin, row0, row_end, e, n0);
+            cmp_lin += nslots;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int64_t row = row0 + grp * 128 + wm * 64 + i * 32 + (lane & 31);
+#pragma unroll
+                for (int j = 0; j < TNO; ++j) {
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int f0 = n0 + wn * WTNO + j * 32 + 8 * q4 + 4 * khalf;
+                        float o[4];
+                        if (EPI == EPI_SWIGLU) {
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) {
+                                const float z = acc[i][j][4 * q4 + c];
+                                o[c] = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) * acc[i][j + TNO][4 * q4 + c];
+                            }
+                        } else {
+                            float bc[4] = {0.f, 0.f, 0.f, 0.f};
+                            if (bias != nullptr && f0 < n_out) {
+                                const uint2 bb = *reinterpret_cast<const uint2*>(bias + (int64_t)e * n_out + f0);
+                                bc[0] = __uint_as_float(bb.x << 16);
+                                bc[1] = __uint_as_float(bb.x & 0xffff0000u);
+                                bc[2] = __uint_as_float(bb.y << 16);
+                                bc[3] = __uint_as_float(bb.y & 0xffff0000u);
+                            }
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) {
+                                const float z = acc[i][j][4 * q4 + c] + bc[c];
+                                o[c] = EPI == EPI_GELU_BIAS ? gelu_f(z) : z;
+                            }
+                        }
+                        if (row < row_end && f0 < n_out) {
+                            uint2 pk;
+                            pk.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+                            pk.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+                            *reinterpret_cast<uint2*>(C + row * n_out + f0) = pk;
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+            drain = true;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (grp == 0) lds_barrier();
+#undef PS_ISSUE
+#undef PS_READ
+#undef PS_MMA
+}
+
+template <int GM, int D>
+void launch_bf16_persistent(int epi, const void* A, const void* B, const void* bias, void* C,
+                            const int32_t* offsets, int e_begin, int n_groups, int64_t max_rows, int64_t dense_rows,
+                            int n_out, int K, hipStream_t s) {
+    const int bno = epi == EPI_SWIGLU ? 128 : 256;
+    const int64_t m_tiles = offsets ? (max_rows + 255) / 256 + n_groups : (dense_rows + 255) / 256;
+    const int64_t tiles = m_tiles * ((n_out + bno - 1) / bno);
+    const int64_t cap = (int64_t)(device_cu_count() / 8) * 8;
+    const int64_t want = ((tiles + 7) / 8) * 8;
+    const unsigned grid = (unsigned)(want < cap ? want : cap);
+    const auto a = static_cast<const uint16_t*>(A);
+    const auto b = static_cast<const uint16_t*>(B);
+    const auto bi = static_cast<const uint16_t*>(bias);
+    auto c = static_cast<uint16_t*>(C);
+    if (epi == EPI_SWIGLU)
+        gemm_bf16_persistent_kernel<EPI_SWIGLU, GM, D><<<grid, 512, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
+                                                                           dense_rows, n_out, K);
+    else if (epi == EPI_GELU_BIAS)
+        gemm_bf16_persistent_kernel<EPI_GELU_BIAS, GM, D><<<grid, 512, 0, s>>>(a, b, bi, c, offsets, e_begin,
+                                                                              n_groups, dense_rows, n_out, K);
+    else
+        gemm_bf16_persistent_kernel<EPI_BIAS, GM, D><<<grid, 512, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
+                                                                         dense_rows, n_out, K);
+}
+
 // fp32 path (SIMT, 64 x 64 output tile, 4 x 4 per thread, sequential fp32 FMA over K).
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ B,
@@ -646,7 +1169,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
     __shared__ float Bs[NB][BK][BNO + 4];
     __shared__ int s_ts[1025];
     __shared__ int s_wave[4];
-    if (offsets) build_schedule<BM>(offsets, e_begin, n_groups, s_ts, s_wave);
+    if (offsets) build_schedule<BM, 256>(offsets, e_begin, n_groups, s_ts, s_wave);
     const TileCoord tc = decode_tile<BM, BNO, 8>(offsets, s_ts, e_begin, n_groups, dense_rows, n_out);
     if (!tc.valid) return;
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
@@ -743,8 +1266,8 @@ void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* 
                          int n_out, int K, hipStream_t s) {
     if (dtype == MOE_BF16) {
         (void)bm;
-        launch_bf16_rs_tiles<256, 256, 8>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows, n_out,
-                                          K, s);
+        launch_bf16_persistent<8, 3>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows, n_out, K,
+                                     s);
         return;
     }
     const int64_t m_tiles = offsets ? (max_rows + 63) / 64 + n_groups : (dense_rows + 63) / 64;
