@@ -47,17 +47,21 @@ struct Carver {
 };
 
 struct RouteWs {
-    size_t logits, blk_counts, blk_P, blk_H, bytes;
-    int nblk;
+    size_t logits, wsplit, blk_counts, blk_P, blk_H, fp, ticket, bytes;
+    int nblk, Epad;
 };
 RouteWs route_ws(const moe_shape* s) {
     RouteWs w;
     Carver c;
     w.nblk = (int)cdiv(s->T, kRouteTokensPerBlock);
+    w.Epad = (int)cdiv(s->E, 16) * 16;
     w.logits = c.take((size_t)s->T * s->E * 4);
+    w.wsplit = c.take(s->dtype == MOE_BF16 ? (size_t)3 * w.Epad * s->d_model * 2 : 0);
     w.blk_counts = c.take((size_t)w.nblk * s->E * 4);
     w.blk_P = c.take((size_t)w.nblk * s->E * 4);
     w.blk_H = c.take((size_t)w.nblk * 4);
+    w.fp = c.take((size_t)s->E * 8);
+    w.ticket = c.take(4);
     w.bytes = c.off;
     return w;
 }
@@ -99,7 +103,7 @@ SharedWs shared_ws(const moe_shape* s) {
 }
 
 struct FwdWs {
-    size_t topk_idx, topk_w, counts, stats, offsets, sorted_token, inv_pos, x_perm, y_perm, ys, scratch, bytes;
+    size_t topk_idx, topk_w, counts, offsets, sorted_token, inv_pos, x_perm, y_perm, ys, scratch, bytes;
 };
 FwdWs fwd_ws(const moe_shape* s) {
     FwdWs w;
@@ -108,7 +112,6 @@ FwdWs fwd_ws(const moe_shape* s) {
     w.topk_idx = c.take(A * 4);
     w.topk_w = c.take(A * 4);
     w.counts = c.take((size_t)s->E * 4);
-    w.stats = c.take((size_t)(2 * s->E + 2) * 4);
     w.offsets = c.take((size_t)(s->E + 1) * 4);
     w.sorted_token = c.take(A * 4);
     w.inv_pos = c.take(A * 4);
@@ -136,11 +139,17 @@ void do_route(const moe_shape* s, const void* x, const float* w_router, const fl
               int32_t* topk_idx, float* topk_w, int32_t* counts, float* stats, void* ws, hipStream_t st) {
     const RouteWs w = route_ws(s);
     float* lg = logits ? logits : at<float>(ws, w.logits);
-    moe::launch_route_logits(s->dtype, x, w_router, lg, s->T, s->d_model, s->E, st);
-    moe::launch_route_select(lg, sel_bias, s->T, s->E, s->k, s->score, s->renorm, topk_idx, topk_w,
-                             at<int32_t>(ws, w.blk_counts), at<float>(ws, w.blk_P), at<float>(ws, w.blk_H), st);
-    moe::launch_route_finalize(at<int32_t>(ws, w.blk_counts), at<float>(ws, w.blk_P), at<float>(ws, w.blk_H),
-                               w.nblk, s->T, s->E, counts, stats, st);
+    uint16_t* wsplit = s->dtype == MOE_BF16 ? at<uint16_t>(ws, w.wsplit) : nullptr;
+    int32_t* ticket = at<int32_t>(ws, w.ticket);
+    int32_t* blk_counts = at<int32_t>(ws, w.blk_counts);
+    float* blk_P = stats ? at<float>(ws, w.blk_P) : nullptr;
+    float* blk_H = stats ? at<float>(ws, w.blk_H) : nullptr;
+    moe::launch_route_prep(w_router, s->E, w.Epad, s->d_model, wsplit, ticket, st);
+    moe::launch_route_logits(s->dtype, x, w_router, wsplit, w.Epad, lg, s->T, s->d_model, s->E, st);
+    moe::launch_route_select(lg, sel_bias, s->T, s->E, s->k, s->score, s->renorm, topk_idx, topk_w, blk_counts, blk_P,
+                             blk_H, st);
+    moe::launch_route_finalize(blk_counts, blk_P, blk_H, w.nblk, s->T, s->E, counts, at<double>(ws, w.fp), ticket,
+                               stats, st);
 }
 
 void do_permute(const moe_shape* s, const int32_t* topk_idx, const void* x, int32_t* offsets,
@@ -334,11 +343,10 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router, co
     int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, w.topk_idx);
     float* gw = topk_w_out ? topk_w_out : at<float>(ws, w.topk_w);
     int32_t* cnt = counts_out ? counts_out : at<int32_t>(ws, w.counts);
-    float* sts = stats_out ? stats_out : at<float>(ws, w.stats);
     void* scratch = at<void>(ws, w.scratch);
     int32_t* offsets = at<int32_t>(ws, w.offsets);
     int32_t* inv_pos = at<int32_t>(ws, w.inv_pos);
-    do_route(shape, x, w_router, sel_bias, nullptr, idx, gw, cnt, sts, scratch, st);
+    do_route(shape, x, w_router, sel_bias, nullptr, idx, gw, cnt, stats_out, scratch, st);
     do_permute(shape, idx, x, offsets, at<int32_t>(ws, w.sorted_token), inv_pos, at<void>(ws, w.x_perm), scratch,
                st);
     do_ffn(shape, 0, shape->E, at<void>(ws, w.x_perm), offsets, w_in, b_in, w_out, b_out, at<void>(ws, w.y_perm),

@@ -9,15 +9,21 @@
 namespace moe {
 
 // ---- route ------------------------------------------------------------------------------
-constexpr int kRouteTokensPerBlock = 64;  // tokens per select block (4 waves x 16 tokens)
+constexpr int kRouteTokensPerBlock = 16;  // tokens per select block (4 waves x 4 tokens)
 
-void launch_route_logits(int dtype, const void* x, const float* w_router, float* logits, int64_t T, int d,
-                         int E, hipStream_t s);
+// bf16 layers: split the fp32 router into hi/mid/lo bf16 rows [3][Epad][d] (rows >= E zero);
+// every layer: zero the statistics ticket.
+void launch_route_prep(const float* w_router, int E, int Epad, int d, uint16_t* wsplit, int32_t* ticket,
+                       hipStream_t s);
+void launch_route_logits(int dtype, const void* x, const float* w_router, const uint16_t* wsplit, int Epad,
+                         float* logits, int64_t T, int d, int E, hipStream_t s);
 void launch_route_select(const float* logits, const float* sel_bias, int64_t T, int E, int k, int score,
                          int renorm, int32_t* topk_idx, float* topk_w, int32_t* blk_counts, float* blk_P,
                          float* blk_H, hipStream_t s);
-void launch_route_finalize(const int32_t* blk_counts, const float* blk_P, const float* blk_H, int nblk,
-                           int64_t T, int E, int32_t* counts, float* stats, hipStream_t s);
+// counts[E] always; stats (f, P, aux, entropy) when stats != NULL
+void launch_route_finalize(const int32_t* blk_counts, const float* blk_P, const float* blk_H, int nblk, int64_t T,
+                           int E, int32_t* counts, double* fp_scratch, int32_t* ticket, float* stats,
+                           hipStream_t s);
 
 // ---- permute ----------------------------------------------------------------------------
 constexpr int kPermTile = 1024;  // assignments per histogram / rank tile

@@ -98,21 +98,28 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restric
     }
 }
 
-// One wave per token: read the row once, store it at its k destinations (16-byte vectors).
+// One wave per token: read the row once, store it at its k destinations (16-byte vectors, up to
+// 8 per lane loaded before any store so a row is one memory round trip).
 __global__ __launch_bounds__(256) void perm_scatter_kernel(const uint8_t* __restrict__ x,
                                                            const int32_t* __restrict__ inv_pos, int64_t T,
                                                            int row_bytes, int k, uint8_t* __restrict__ x_perm) {
+    constexpr int U = 8;
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int64_t t = (int64_t)blockIdx.x * 4 + wave;
     if (t >= T) return;
     const int mypos = lane < k ? inv_pos[t * k + lane] : 0;
     const int nchunks = row_bytes / 16;
     const uint8_t* src = x + t * row_bytes;
-    for (int c = lane; c < nchunks; c += 64) {
-        const u32x4 v = ld16(src + (int64_t)c * 16);
+    for (int c0 = lane; c0 < nchunks; c0 += 64 * U) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (c0 + 64 * u < nchunks) v[u] = ld16(src + (int64_t)(c0 + 64 * u) * 16);
         for (int j = 0; j < k; ++j) {
-            const int p = __builtin_amdgcn_readlane(mypos, j);
-            st16(x_perm + (int64_t)p * row_bytes + (int64_t)c * 16, v);
+            uint8_t* dst = x_perm + (int64_t)__builtin_amdgcn_readlane(mypos, j) * row_bytes;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (c0 + 64 * u < nchunks) st16(dst + (int64_t)(c0 + 64 * u) * 16, v[u]);
         }
     }
 }

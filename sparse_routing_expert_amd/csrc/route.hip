@@ -14,19 +14,6 @@ namespace moe {
 
 namespace {
 
-__device__ __forceinline__ void split3(const float* w, bf16x8& hi, bf16x8& mid, bf16x8& lo) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        __bf16 h = (__bf16)w[j];
-        float r1 = w[j] - (float)h;
-        __bf16 m = (__bf16)r1;
-        float r2 = r1 - (float)m;
-        hi[j] = h;
-        mid[j] = m;
-        lo[j] = (__bf16)r2;
-    }
-}
-
 // Order-preserving 64-bit key: larger float first, then the LOWER expert index (its complement
 // sits in the low word), so one unsigned max gives the (key desc, index asc) total order.
 __device__ __forceinline__ uint64_t pack_key(float v, int e) {
@@ -40,75 +27,135 @@ __device__ __forceinline__ float sigmoidf_(float l) { return 1.0f / (1.0f + expf
 
 }  // namespace
 
-// logits[T, E] = x[T, d] (bf16) . w[E, d]^T (fp32), one wave per 16 tokens x 16 experts
-// (v_mfma_f32_16x16x32_bf16). Any assignment of the reduced index k to lanes is valid as long
-// as both operands use the same one, so each lane reads 32 contiguous bf16 of its token row and
-// the matching 32 fp32 of its expert row per 128-wide step: 64-byte contiguous loads.
-template <int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void route_logits_bf16_kernel(const uint16_t* __restrict__ x,
-                                                                       const float* __restrict__ w,
-                                                                       float* __restrict__ logits, int64_t T,
-                                                                       int d, int E) {
-    const int lane = lane_id();
-    const int wave = threadIdx.x >> 6;
-    const int64_t t0 = ((int64_t)blockIdx.x * WAVES + wave) * 16;
-    if (t0 >= T) return;  // no barriers in this kernel
+// Split of the fp32 router into three bf16 terms, once per call: w = hi + mid + lo with each term
+// the bf16 rounding of what the previous ones leave, which carries the 24-bit significand. Rows
+// E..Epad-1 are zero. The same launch zeroes the ticket route_finalize counts its blocks with.
+__global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict__ w, int E, int Epad, int d,
+                                                         uint16_t* __restrict__ wsplit, int32_t* __restrict__ ticket) {
+    const int64_t n = (int64_t)Epad * d;
+    const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0;
+    if (wsplit == nullptr || i4 >= n) return;
+    const int64_t row = i4 / d;
+    floatx4 v = {0.f, 0.f, 0.f, 0.f};
+    if (row < E) v = *reinterpret_cast<const floatx4*>(w + i4);
+    uint16_t hi[4], mid[4], lo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const __bf16 h = (__bf16)v[j];
+        const float r1 = v[j] - (float)h;
+        const __bf16 m = (__bf16)r1;
+        const float r2 = r1 - (float)m;
+        const __bf16 l = (__bf16)r2;
+        hi[j] = __builtin_bit_cast(uint16_t, h);
+        mid[j] = __builtin_bit_cast(uint16_t, m);
+        lo[j] = __builtin_bit_cast(uint16_t, l);
+    }
+    uint2 ph, pm, pl;
+    ph.x = hi[0] | ((uint32_t)hi[1] << 16);
+    ph.y = hi[2] | ((uint32_t)hi[3] << 16);
+    pm.x = mid[0] | ((uint32_t)mid[1] << 16);
+    pm.y = mid[2] | ((uint32_t)mid[3] << 16);
+    pl.x = lo[0] | ((uint32_t)lo[1] << 16);
+    pl.y = lo[2] | ((uint32_t)lo[3] << 16);
+    *reinterpret_cast<uint2*>(wsplit + i4) = ph;
+    *reinterpret_cast<uint2*>(wsplit + n + i4) = pm;
+    *reinterpret_cast<uint2*>(wsplit + 2 * n + i4) = pl;
+}
+
+// logits[T, E] = x[T, d] (bf16) . w[E, d]^T with the split router (v_mfma_f32_16x16x32_bf16, three
+// products per K step). A block owns 16*TT tokens x 16 experts; its four waves take a quarter of d
+// each (TT token tiles per wave share each router load) and their partial tiles are summed in LDS
+// in a fixed order. Any assignment of the reduced index k to lanes is valid as long as both
+// operands use the same one, so each lane reads 64 contiguous bytes of its token row and of its
+// expert row per 128-wide step; the next step's loads are issued before the current products.
+template <int TT>
+__global__ __launch_bounds__(256) void route_logits_bf16_kernel(const uint16_t* __restrict__ x,
+                                                                const uint16_t* __restrict__ wsplit, int Epad,
+                                                                float* __restrict__ logits, int64_t T, int d,
+                                                                int E) {
+    __shared__ floatx4 s_part[4][TT][64];
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int64_t t0 = (int64_t)blockIdx.x * 16 * TT;
     const int e0 = blockIdx.y * 16;
     const int r = lane & 15, g = lane >> 4;
-    const int64_t t = t0 + r < T ? t0 + r : T - 1;
-    const int e = e0 + r;
-    const bool e_ok = e < E;
-    const uint16_t* xr = x + t * d;
-    const float* wr = w + (int64_t)(e_ok ? e : E - 1) * d;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    int kb = 0;
-    for (; kb + 128 <= d; kb += 128) {
-        const int base = kb + g * 32;
-        u32x4 xv[4];
-        floatx4 wv[8];
+    const uint16_t* xr[TT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xv[i] = ld16(xr + base + i * 8);
+    for (int tt = 0; tt < TT; ++tt) {
+        const int64_t t = t0 + tt * 16 + r;
+        xr[tt] = x + (t < T ? t : T - 1) * d;
+    }
+    const bool w_ok = e0 + r < E;  // rows E..Epad-1 are zero: not loaded
+    const int64_t n = (int64_t)Epad * d;
+    const uint16_t* wh = wsplit + (int64_t)(e0 + r) * d;
+    const int nc = d / 32;  // 32-wide K chunks, split over the four waves
+    const int kb0 = (wave * nc / 4) * 32, kb1 = ((wave + 1) * nc / 4) * 32;
+    floatx4 acc[TT];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) wv[i] = *reinterpret_cast<const floatx4*>(wr + base + i * 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float wf[8] = {wv[2 * i][0], wv[2 * i][1], wv[2 * i][2], wv[2 * i][3],
-                           wv[2 * i + 1][0], wv[2 * i + 1][1], wv[2 * i + 1][2], wv[2 * i + 1][3]};
-            if (!e_ok) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) wf[j] = 0.f;
-            }
-            bf16x8 hi, mid, lo;
-            split3(wf, hi, mid, lo);
-            const bf16x8 a = __builtin_bit_cast(bf16x8, xv[i]);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, hi, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, mid, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, lo, acc, 0, 0, 0);
+    for (int tt = 0; tt < TT; ++tt) acc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    u32x4 xv[2][TT][4], wv[2][3][4];
+#define RL_LOAD(b_, kb_)                                                                                  \
+    {                                                                                                     \
+        const int base = (kb_) + g * 32;                                                                  \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                   \
+            _Pragma("unroll") for (int tt = 0; tt < TT; ++tt) xv[b_][tt][i] = ld16(xr[tt] + base + i * 8); \
+            _Pragma("unroll") for (int p = 0; p < 3; ++p) wv[b_][p][i] =                                   \
+                w_ok ? ld16(wh + p * n + base + i * 8) : zero;                                            \
+        }                                                                                                 \
+    }
+#define RL_MMA(b_)                                                                                        \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) _Pragma("unroll") for (int tt = 0; tt < TT; ++tt)      \
+        _Pragma("unroll") for (int p = 0; p < 3; ++p) acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(   \
+            __builtin_bit_cast(bf16x8, xv[b_][tt][i]), __builtin_bit_cast(bf16x8, wv[b_][p][i]), acc[tt], 0, 0, 0);
+    int kb = kb0;
+    const int nsteps = (kb1 - kb0) / 128;
+    if (nsteps > 0) {
+        RL_LOAD(0, kb)
+        int st = 0;
+        for (; st + 2 <= nsteps; st += 2) {
+            if (st + 1 < nsteps) RL_LOAD(1, kb + 128)
+            RL_MMA(0)
+            if (st + 2 < nsteps) RL_LOAD(0, kb + 256)
+            RL_MMA(1)
+            kb += 256;
+        }
+        if (st < nsteps) {
+            RL_MMA(0)
+            kb += 128;
         }
     }
-    for (; kb < d; kb += 32) {  // d is a multiple of 64: at most one 64-wide tail (two steps)
+#undef RL_LOAD
+#undef RL_MMA
+    for (; kb < kb1; kb += 32) {  // 32-wide tail of the wave's range
         const int base = kb + g * 8;
-        const u32x4 xv = ld16(xr + base);
-        const floatx4 w0 = *reinterpret_cast<const floatx4*>(wr + base);
-        const floatx4 w1 = *reinterpret_cast<const floatx4*>(wr + base + 4);
-        float wf[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-        if (!e_ok) {
+        u32x4 w3[3];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) wf[j] = 0.f;
+        for (int p = 0; p < 3; ++p) w3[p] = w_ok ? ld16(wh + p * n + base) : zero;
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(xr[tt] + base));
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+                acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, w3[p]), acc[tt], 0, 0, 0);
         }
-        bf16x8 hi, mid, lo;
-        split3(wf, hi, mid, lo);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, xv);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, hi, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, mid, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, lo, acc, 0, 0, 0);
     }
-    // 16x16 accumulator: lane holds column (expert) lane%16, rows (tokens) 4*(lane/16) + v.
-    if (e_ok) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t tt = t0 + 4 * g + v;
-            if (tt < T) logits[tt * E + e] = acc[v];
+    for (int tt = 0; tt < TT; ++tt) s_part[wave][tt][lane] = acc[tt];
+    __syncthreads();
+    if (wave != 0) return;
+    // 16x16 accumulator: lane holds column (expert) lane%16, rows (tokens) 4*(lane/16) + v.
+    const int e = e0 + r;
+    if (e < E) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            const floatx4 p0 = s_part[0][tt][lane], p1 = s_part[1][tt][lane], p2 = s_part[2][tt][lane],
+                          p3 = s_part[3][tt][lane];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t tk = t0 + tt * 16 + 4 * g + v;
+                if (tk < T) logits[tk * E + e] = ((p0[v] + p1[v]) + p2[v]) + p3[v];
+            }
         }
     }
 }
@@ -135,9 +182,11 @@ __global__ __launch_bounds__(256) void route_logits_f32_kernel(const float* __re
     logits[i] = acc;
 }
 
-// Per token (one wave): scores, balance-statistic partials, top-k by k rounds of a wave-wide
-// max over packed keys, gates. Each block (4 waves x 16 tokens) writes its expert histogram, its
-// per-expert probability sums and its entropy sum; route_finalize reduces them in a fixed order.
+// Per token (one wave handles kSelTokensPerWave tokens, their logits loaded up front): scores,
+// balance-statistic partials, top-k by k rounds of a wave-wide max over packed keys, gates. Each
+// block writes its expert histogram, its per-expert probability sums and its entropy sum;
+// route_finalize reduces them.
+constexpr int kSelTokensPerWave = kRouteTokensPerBlock / 4;
 template <int EPL>
 __global__ __launch_bounds__(256) void route_select_kernel(const float* __restrict__ logits,
                                                            const float* __restrict__ sel_bias, int64_t T,
@@ -163,17 +212,24 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
     }
     float hacc = 0.f;
 
-    const int64_t tb = (int64_t)blockIdx.x * kRouteTokensPerBlock + wave * 16;
-    for (int q = 0; q < 16; ++q) {
+    const int64_t tb = (int64_t)blockIdx.x * kRouteTokensPerBlock + wave * kSelTokensPerWave;
+    float lall[kSelTokensPerWave][EPL];
+#pragma unroll
+    for (int q = 0; q < kSelTokensPerWave; ++q)
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane + 64 * i;
+            lall[q][i] = (tb + q < T && e < E) ? logits[(tb + q) * E + e] : -INFINITY;
+        }
+#pragma unroll
+    for (int q = 0; q < kSelTokensPerWave; ++q) {
         const int64_t t = tb + q;
         if (t >= T) break;
-        const float* lt = logits + t * E;
         float l[EPL];
         float lmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
-            const int e = lane + 64 * i;
-            l[i] = e < E ? lt[e] : -INFINITY;
+            l[i] = lall[q][i];
             lmax = fmaxf(lmax, l[i]);
         }
         const float m = wave_max(lmax);
@@ -201,19 +257,28 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
             key[i] = e < E ? pack_key(kv, e) : 0ull;
         }
         int sel_e = 0;
+        float sel_l = -INFINITY;
         for (int j = 0; j < k; ++j) {
             uint64_t best = 0ull;
 #pragma unroll
             for (int i = 0; i < EPL; ++i) best = key[i] > best ? key[i] : best;
             best = wave_max_u64(best);
             const int e = key_index(best);
+            float le = -INFINITY;  // unbiased logit of the winner, from the lane that holds it
 #pragma unroll
             for (int i = 0; i < EPL; ++i)
-                if (e == lane + 64 * i) key[i] = 0ull;
-            if (lane == j) sel_e = e;
+                if (e == lane + 64 * i) {
+                    key[i] = 0ull;
+                    le = l[i];
+                }
+            le = wave_max(le);
+            if (lane == j) {
+                sel_e = e;
+                sel_l = le;
+            }
         }
         // gates from the unbiased logits of the selection (lane j holds slot j)
-        const float lv = lane < k ? lt[sel_e] : -INFINITY;
+        const float lv = lane < k ? sel_l : -INFINITY;
         float gate;
         if (softmax) {
             if (renorm) {
@@ -224,8 +289,8 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
                 gate = expf(lv - m) * invZ;
             }
         } else {
-            const float s = lane < k ? sigmoidf_(lv) : 0.f;
-            gate = s / wave_sum(s);
+            const float sg = lane < k ? sigmoidf_(lv) : 0.f;
+            gate = sg / wave_sum(sg);
         }
         if (lane < k) {
             topk_idx[t * k + lane] = sel_e;
@@ -243,52 +308,90 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += 256) {
         blk_counts[(int64_t)blockIdx.x * E + e] = s_cnt[e];
-        blk_P[(int64_t)blockIdx.x * E + e] = ((s_P[0][e] + s_P[1][e]) + s_P[2][e]) + s_P[3][e];
+        if (blk_P != nullptr) blk_P[(int64_t)blockIdx.x * E + e] = ((s_P[0][e] + s_P[1][e]) + s_P[2][e]) + s_P[3][e];
     }
-    if (threadIdx.x == 0) blk_H[blockIdx.x] = ((s_H[0] + s_H[1]) + s_H[2]) + s_H[3];
+    if (threadIdx.x == 0 && blk_H != nullptr) blk_H[blockIdx.x] = ((s_H[0] + s_H[1]) + s_H[2]) + s_H[3];
 }
 
-// Fixed-order reduction of the per-block partials: counts, f = counts/T, P = mean p,
-// aux = E * sum f P, mean entropy.
+// Expert counts and balance statistics from the per-block partials, in fixed-order sums (float64
+// for the statistics): block e < E reduces expert e (count; with stats, f = counts/T and P = mean
+// p), block E the entropy; the last block to finish (ticket) forms aux = E * sum_e f_e P_e over the
+// per-expert products in expert order.
 __global__ __launch_bounds__(256) void route_finalize_kernel(const int32_t* __restrict__ blk_counts,
                                                              const float* __restrict__ blk_P,
                                                              const float* __restrict__ blk_H, int nblk,
                                                              int64_t T, int E, int32_t* __restrict__ counts,
+                                                             double* __restrict__ fp_scratch,
+                                                             int32_t* __restrict__ ticket,
                                                              float* __restrict__ stats) {
-    __shared__ double s_fp[1024];
+    __shared__ double s_sum[256];
+    __shared__ int s_cnt[256];
+    __shared__ bool s_last;
+    const int tid = threadIdx.x;
+    const int e = blockIdx.x;
     const double invT = 1.0 / (double)T;
-    for (int e = threadIdx.x; e < E; e += 256) {
-        int64_t c = 0;
-        double P = 0.0;
-        for (int b = 0; b < nblk; ++b) {
-            c += blk_counts[(int64_t)b * E + e];
-            P += (double)blk_P[(int64_t)b * E + e];
+    double acc = 0.0;
+    int cnt = 0;
+    if (e < E) {
+        for (int b = tid; b < nblk; b += 256) {
+            cnt += blk_counts[(int64_t)b * E + e];
+            if (stats) acc += (double)blk_P[(int64_t)b * E + e];
         }
-        counts[e] = (int32_t)c;
-        const double f = (double)c * invT, Pm = P * invT;
-        s_fp[e] = f * Pm;
-        if (stats) {
+    } else if (stats) {
+        for (int b = tid; b < nblk; b += 256) acc += (double)blk_H[b];
+    }
+    s_sum[tid] = acc;
+    s_cnt[tid] = cnt;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (tid < o) {
+            s_sum[tid] += s_sum[tid + o];
+            s_cnt[tid] += s_cnt[tid + o];
+        }
+        __syncthreads();
+    }
+    if (tid == 0 && e < E) counts[e] = s_cnt[0];
+    if (stats == nullptr) return;
+    if (tid == 0) {
+        if (e < E) {
+            const double f = (double)s_cnt[0] * invT, Pm = s_sum[0] * invT;
             stats[e] = (float)f;
             stats[E + e] = (float)Pm;
+            fp_scratch[e] = f * Pm;
+        } else {
+            stats[2 * E + 1] = (float)(s_sum[0] * invT);
         }
+        __threadfence();
+        s_last = atomicAdd(ticket, 1) == (int)gridDim.x - 1;
     }
     __syncthreads();
-    if (threadIdx.x == 0 && stats) {
-        double aux = 0.0, H = 0.0;
-        for (int e = 0; e < E; ++e) aux += s_fp[e];
-        for (int b = 0; b < nblk; ++b) H += (double)blk_H[b];
-        stats[2 * E] = (float)(E * aux);
-        stats[2 * E + 1] = (float)(H * invT);
+    if (!s_last) return;
+    __threadfence();
+    if (tid == 0) {
+        double aux = 0.0;
+        for (int i = 0; i < E; ++i) aux += __builtin_nontemporal_load(fp_scratch + i);
+        stats[2 * E] = (float)((double)E * aux);
     }
 }
 
-void launch_route_logits(int dtype, const void* x, const float* w_router, float* logits, int64_t T, int d,
-                         int E, hipStream_t s) {
+void launch_route_prep(const float* w_router, int E, int Epad, int d, uint16_t* wsplit, int32_t* ticket,
+                       hipStream_t s) {
+    const int64_t n = wsplit ? (int64_t)Epad * d : 0;
+    const unsigned grid = (unsigned)(n > 0 ? (n / 4 + 255) / 256 : 1);
+    route_prep_kernel<<<grid, 256, 0, s>>>(w_router, E, Epad, d, wsplit, ticket);
+}
+
+void launch_route_logits(int dtype, const void* x, const float* w_router, const uint16_t* wsplit, int Epad,
+                         float* logits, int64_t T, int d, int E, hipStream_t s) {
     if (dtype == MOE_BF16) {
-        constexpr int W = 4;
-        dim3 grid((unsigned)((T + 16 * W - 1) / (16 * W)), (unsigned)((E + 15) / 16));
-        route_logits_bf16_kernel<W><<<grid, 64 * W, 0, s>>>(static_cast<const uint16_t*>(x), w_router, logits,
-                                                            T, d, E);
+        const auto xb = static_cast<const uint16_t*>(x);
+        if (T >= 32 * 256) {  // two token tiles per wave still leave a block per CU
+            dim3 grid((unsigned)((T + 31) / 32), (unsigned)(Epad / 16));
+            route_logits_bf16_kernel<2><<<grid, 256, 0, s>>>(xb, wsplit, Epad, logits, T, d, E);
+        } else {
+            dim3 grid((unsigned)((T + 15) / 16), (unsigned)(Epad / 16));
+            route_logits_bf16_kernel<1><<<grid, 256, 0, s>>>(xb, wsplit, Epad, logits, T, d, E);
+        }
     } else {
         const int64_t n = T * E;
         route_logits_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(static_cast<const float*>(x),
@@ -311,9 +414,11 @@ void launch_route_select(const float* logits, const float* sel_bias, int64_t T, 
 #undef MOE_SELECT
 }
 
-void launch_route_finalize(const int32_t* blk_counts, const float* blk_P, const float* blk_H, int nblk,
-                           int64_t T, int E, int32_t* counts, float* stats, hipStream_t s) {
-    route_finalize_kernel<<<1, 256, 0, s>>>(blk_counts, blk_P, blk_H, nblk, T, E, counts, stats);
+void launch_route_finalize(const int32_t* blk_counts, const float* blk_P, const float* blk_H, int nblk, int64_t T,
+                           int E, int32_t* counts, double* fp_scratch, int32_t* ticket, float* stats,
+                           hipStream_t s) {
+    route_finalize_kernel<<<(unsigned)(stats ? E + 1 : E), 256, 0, s>>>(blk_counts, blk_P, blk_H, nblk, T, E,
+                                                                         counts, fp_scratch, ticket, stats);
 }
 
 }  // namespace moe
