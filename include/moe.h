@@ -13,7 +13,7 @@
  *   moe_route       router logits, scores, top-k, gates, counts, balance statistics
  *   moe_permute     expert histogram, exclusive scan, stable expert-contiguous gather
  *   moe_grouped_ffn every expert's FFN as one grouped GEMM over variable-size segments
- *                   (= moe_expert_up then moe_expert_down, one launch each)
+ *                   (= moe_expert_up then moe_expert_down)
  *   moe_shared_ffn  the always-on shared SwiGLU expert (dense)
  *   moe_combine     gate-weighted sum back to token order (+ shared output)
  * and moe_forward, which chains them.
@@ -85,7 +85,8 @@ enum {
     MOE_STAGE_PERMUTE = 1,
     MOE_STAGE_FFN = 2,
     MOE_STAGE_SHARED = 3,
-    MOE_STAGE_FORWARD = 4
+    MOE_STAGE_FORWARD = 4,
+    MOE_STAGE_EXPERT = 5 /* moe_expert_up / moe_expert_down */
 };
 
 /* Layer description (host memory). Limits: T >= 0; 1 <= E <= 1024; 1 <= k <= min(E, 32);
@@ -185,25 +186,28 @@ int moe_grouped_ffn(const moe_shape* shape, int32_t e_begin, int32_t e_end, cons
                     const int32_t* offsets, const void* w_in, const void* b_in, const void* w_out,
                     const void* b_out, void* y_perm, void* ws, size_t ws_bytes, moe_stream_t stream);
 
-/* moe_expert_up -- the first projection and activation of every expert (one kernel launch).
+/* moe_expert_up -- the first projection and activation of every expert (one grouped-GEMM launch,
+ * plus a short second launch when the last round of tiles is split along K).
  *
  * The first half of moe_grouped_ffn, exposed on its own (same definitions and arguments):
  *   h [T*k, d_ff] dtype  out: GELU: gelu(x_perm[p] W1_e^T + b1_e); SwiGLU: SiLU(x_perm[p] Wg_e^T) *
  *                        (x_perm[p] Wu_e^T), for each row p of an expert e in [e_begin, e_end);
  *                        other rows untouched. bf16 layers round h once to bf16.
- * Needs no workspace. */
+ * Workspace: MOE_STAGE_EXPERT (bf16 layers: fp32 partial tiles of the split last round, summed in a
+ * fixed order, so results are deterministic; fp32 layers need none). */
 int moe_expert_up(const moe_shape* shape, int32_t e_begin, int32_t e_end, const void* x_perm,
-                  const int32_t* offsets, const void* w_in, const void* b_in, void* h, moe_stream_t stream);
+                  const int32_t* offsets, const void* w_in, const void* b_in, void* h, void* ws,
+                  size_t ws_bytes, moe_stream_t stream);
 
-/* moe_expert_down -- the second projection of every expert (one kernel launch).
+/* moe_expert_down -- the second projection of every expert (launches as moe_expert_up).
  *
  * The second half of moe_grouped_ffn (same definitions and arguments):
  *   h      [T*k, d_ff]    dtype  in: moe_expert_up's output
  *   y_perm [T*k, d_model] dtype  out: h[p] W2_e^T (+ b2_e) for each row p of an expert in range.
- * Needs no workspace. */
+ * Workspace: MOE_STAGE_EXPERT (as for moe_expert_up). */
 int moe_expert_down(const moe_shape* shape, int32_t e_begin, int32_t e_end, const void* h,
-                    const int32_t* offsets, const void* w_out, const void* b_out, void* y_perm,
-                    moe_stream_t stream);
+                    const int32_t* offsets, const void* w_out, const void* b_out, void* y_perm, void* ws,
+                    size_t ws_bytes, moe_stream_t stream);
 
 /* moe_shared_ffn -- the always-on shared SwiGLU expert on every token (gate 1).
  *

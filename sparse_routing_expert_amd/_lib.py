@@ -19,7 +19,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 MOE_GELU_MLP, MOE_SWIGLU = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
-MOE_STAGE_ROUTE, MOE_STAGE_PERMUTE, MOE_STAGE_FFN, MOE_STAGE_SHARED, MOE_STAGE_FORWARD = range(5)
+MOE_STAGE_ROUTE, MOE_STAGE_PERMUTE, MOE_STAGE_FFN, MOE_STAGE_SHARED, MOE_STAGE_FORWARD, MOE_STAGE_EXPERT = range(6)
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -46,9 +46,9 @@ _SIGS = {
     "moe_grouped_ffn": (ctypes.c_int, [ctypes.POINTER(moe_shape), ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P,
                                        _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_expert_up": (ctypes.c_int, [ctypes.POINTER(moe_shape), ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P,
-                                     _P]),
+                                     _P, ctypes.c_size_t, _P]),
     "moe_expert_down": (ctypes.c_int, [ctypes.POINTER(moe_shape), ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P,
-                                       _P]),
+                                       _P, ctypes.c_size_t, _P]),
     "moe_shared_ffn": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_combine": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P]),
     "moe_forward": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -149,15 +149,16 @@ def moe_grouped_ffn(shape, e_begin, e_end, x_perm, offsets, w_in, b_in, w_out, b
                                                     _ptr(y_perm), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
-def moe_expert_up(shape, e_begin, e_end, x_perm, offsets, w_in, b_in, h, stream=None) -> None:
+def moe_expert_up(shape, e_begin, e_end, x_perm, offsets, w_in, b_in, h, ws, stream=None) -> None:
     _check("moe_expert_up", lib().moe_expert_up(ctypes.byref(shape), int(e_begin), int(e_end), _ptr(x_perm),
-                                                _ptr(offsets), _ptr(w_in), _ptr(b_in), _ptr(h), _stream(stream)))
+                                                _ptr(offsets), _ptr(w_in), _ptr(b_in), _ptr(h), _ptr(ws), _nbytes(ws),
+                                                _stream(stream)))
 
 
-def moe_expert_down(shape, e_begin, e_end, h, offsets, w_out, b_out, y_perm, stream=None) -> None:
+def moe_expert_down(shape, e_begin, e_end, h, offsets, w_out, b_out, y_perm, ws, stream=None) -> None:
     _check("moe_expert_down", lib().moe_expert_down(ctypes.byref(shape), int(e_begin), int(e_end), _ptr(h),
-                                                    _ptr(offsets), _ptr(w_out), _ptr(b_out), _ptr(y_perm),
-                                                    _stream(stream)))
+                                                    _ptr(offsets), _ptr(w_out), _ptr(b_out), _ptr(y_perm), _ptr(ws),
+                                                    _nbytes(ws), _stream(stream)))
 
 
 def moe_shared_ffn(shape, x, ws_in, ws_out, y_shared, ws, stream=None) -> None:

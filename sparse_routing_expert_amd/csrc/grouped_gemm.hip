@@ -849,58 +849,22 @@ int device_cu_count() {
     return cache[dev];
 }
 
-// Persistent form of the eight-wave ping-pong tile: one block per CU walks its share of the tile
-// sequence, so the tile schedule and the expert offsets are read into LDS once per block, and the
-// LDS ring runs on across tile boundaries (the next tile's first stages arrive while the current
-// tile's last stages are multiplied). Blocks are dealt to XCDs round-robin; the 32 blocks of an XCD
-// take 32 consecutive tiles of that XCD's chunk at a time (GM row tiles x 32/GM column tiles of one
-// expert), so they share weight panels and token tiles through the XCD's L2 while running in step.
-//
-// The MFMA operands are the weight fragment first and the token fragment second, so an accumulator
-// holds a (feature x token) block: a lane owns one token and, per group of 4 registers, 4
-// consecutive output features, written with one 8-byte store. Stores and LDS-DMA loads share the
-// vector-memory counter and may complete out of order, so the memory cluster after a tile's stores
-// waits for the counter to drain before it issues new loads.
-template <int EPI, int GM, int D>
-__global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ C, const int32_t* __restrict__ offsets, int e_begin, int n_groups, int64_t dense_rows,
-    int n_out, int K) {
-    constexpr int BM = 256, BN = 256, BK = 32, NS = D + 1;
-    constexpr bool GATED = EPI == EPI_SWIGLU;
-    constexpr int TM = 2;  // 64 tokens per wave
-    constexpr int BNO = GATED ? BN / 2 : BN, WTNO = BNO / 2, TNO = WTNO / 32, TN = GATED ? 2 * TNO : TNO;
-    constexpr int STAGE_ELEMS = (BM + BN) * BK;  // 512 rows of 64 bytes
-    constexpr int STAGE_BYTES = STAGE_ELEMS * 2;
-    constexpr int NQ = 4;  // DMA instructions per wave per stage (a group moves 256 rows = 16 KB)
-    static_assert(TN == 4 && D >= 2 && D <= 5, "tile shape");
-    static_assert(NS * STAGE_BYTES + 2 * 1025 * 4 + 8 * 4 <= 160 * 1024, "LDS budget");
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE_ELEMS];
-    __shared__ int s_ts[1025];   // row-tile prefix sums per group
-    __shared__ int s_off[1025];  // offsets[e_begin .. e_begin + n_groups]
-    __shared__ int s_wave[8];
-
-    const int tid = threadIdx.x, lane = lane_id();
-    if (offsets) {
-        for (int g = tid; g <= n_groups; g += 512) s_off[g] = offsets[e_begin + g];
-        build_schedule<BM, 512>(offsets, e_begin, n_groups, s_ts, s_wave);  // ends with a barrier
-    }
-    // Tile counts fit 32 bits: rows <= T * k <= 2^31 - 1 and at most 2^31 / 128 column tiles.
-    const uint32_t n_tiles_n = (uint32_t)((n_out + BNO - 1) / BNO);
-    const uint32_t m_tiles = offsets ? (uint32_t)s_ts[n_groups] : (uint32_t)((dense_rows + BM - 1) / BM);
-    const uint32_t R = m_tiles * n_tiles_n;
-    const uint32_t per = (R + 7) / 8;
-    const uint32_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
-    const uint32_t first = xcd * per + slot;
-    const uint32_t chunk_end = (xcd + 1) * per < R ? (xcd + 1) * per : R;
-    if (first >= chunk_end) return;  // uniform per block
-    const int ntile = (int)((chunk_end - 1 - first) / nslots + 1);
+// Tile schedule of the persistent GEMM and its tail fixup: the expert-major tile order, each
+// XCD's contiguous chunk of it, and how that chunk is dealt to the XCD's blocks.
+template <int BM, int BNO, int GM>
+struct TileSched {
+    const int* s_ts;   // LDS: row-tile prefix sums per group (grouped)
+    const int* s_off;  // LDS: offsets[e_begin .. e_begin + n_groups] (grouped)
+    bool grouped;
+    int e_begin, n_groups;
+    int64_t dense_rows;
+    uint32_t n_tiles_n, m_tiles, R;
 
     // lin -> tile; inside an expert, groups of GM row tiles sweep the column tiles (row tile fastest)
-    auto decode = [&](uint32_t lin, int64_t& row0, int64_t& row_end, int& e, int& n0) {
+    __device__ __forceinline__ void decode(uint32_t lin, int64_t& row0, int64_t& row_end, int& e, int& n0) const {
         int g = 0;
         uint32_t g_mt = m_tiles, local = lin;
-        if (offsets) {
+        if (grouped) {
             const uint32_t key = lin / n_tiles_n;
             int lo = 0, hi = n_groups - 1;
             while (lo < hi) {
@@ -919,7 +883,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
         const uint32_t col = rem / gsz;
         const uint32_t mt = first_m + (rem - col * gsz);
         n0 = (int)col * BNO;
-        if (offsets) {
+        if (grouped) {
             e = e_begin + g;
             row0 = s_off[g] + (int64_t)mt * BM;
             row_end = s_off[g + 1];
@@ -928,7 +892,191 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
             row0 = (int64_t)mt * BM;
             row_end = dense_rows;
         }
-    };
+    }
+};
+
+// Split of one XCD's chunk over its nslots blocks: every block takes nwhole whole tiles; the rem
+// tiles left over are cut along K into S slices each (S >= 2, rem * S <= nslots) when a partial
+// buffer is given, so the last round keeps every CU busy; otherwise the first rem blocks take one
+// more whole tile.
+struct XcdPlan {
+    uint32_t chunk0, nwhole, rem, S;
+};
+__device__ __forceinline__ XcdPlan xcd_plan(uint32_t R, uint32_t xcd, uint32_t nslots, int nk, bool split) {
+    const uint32_t per = (R + 7) / 8;
+    const uint32_t c0 = xcd * per;
+    const uint32_t c1 = (xcd + 1) * per < R ? (xcd + 1) * per : R;
+    const uint32_t C = c1 > c0 ? c1 - c0 : 0;
+    XcdPlan p;
+    p.chunk0 = c0;
+    p.nwhole = C / nslots;
+    p.rem = C - p.nwhole * nslots;
+    p.S = 1;
+    if (split && p.rem > 0) {
+        uint32_t S = nslots / p.rem;
+        if (S > (uint32_t)nk) S = (uint32_t)nk;
+        p.S = S >= 2 ? S : 1;
+    }
+    return p;
+}
+
+// Build the schedule in LDS (512 threads) and fill a TileSched.
+template <int BM, int BNO, int GM>
+__device__ __forceinline__ TileSched<BM, BNO, GM> setup_sched(const int32_t* __restrict__ offsets, int e_begin,
+                                                              int n_groups, int64_t dense_rows, int n_out,
+                                                              int* s_ts, int* s_off, int* s_wave) {
+    if (offsets) {
+        for (int g = threadIdx.x; g <= n_groups; g += 512) s_off[g] = offsets[e_begin + g];
+        build_schedule<BM, 512>(offsets, e_begin, n_groups, s_ts, s_wave);  // ends with a barrier
+    }
+    TileSched<BM, BNO, GM> ts;
+    ts.s_ts = s_ts;
+    ts.s_off = s_off;
+    ts.grouped = offsets != nullptr;
+    ts.e_begin = e_begin;
+    ts.n_groups = n_groups;
+    ts.dense_rows = dense_rows;
+    // Tile counts fit 32 bits: rows <= T * k <= 2^31 - 1 and at most 2^31 / 128 column tiles.
+    ts.n_tiles_n = (uint32_t)((n_out + BNO - 1) / BNO);
+    ts.m_tiles = offsets ? (uint32_t)s_ts[n_groups] : (uint32_t)((dense_rows + BM - 1) / BM);
+    ts.R = ts.m_tiles * ts.n_tiles_n;
+    return ts;
+}
+
+// Epilogue of one wave's block of a tile: acc[i][j] holds (feature x token) 32 x 32 blocks; a lane
+// owns token i*32 + lane%32 of the wave's 64 and, per group of 4 registers, 4 consecutive features.
+template <int EPI, int TM, int TN>
+__device__ __forceinline__ void store_tile(const floatx16 (&acc)[TM][TN], int64_t row0, int64_t row_end, int e,
+                                           int n0, int grp, int wm, int wn, int lane,
+                                           uint16_t* __restrict__ C, const uint16_t* __restrict__ bias,
+                                           int n_out) {
+    constexpr bool GATED = EPI == EPI_SWIGLU;
+    constexpr int TNO = GATED ? TN / 2 : TN, WTNO = TNO * 32;
+    const int khalf = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int64_t row = row0 + grp * 128 + wm * 64 + i * 32 + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < TNO; ++j) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int f0 = n0 + wn * WTNO + j * 32 + 8 * q4 + 4 * khalf;
+                float o[4];
+                if (GATED) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const float z = acc[i][j][4 * q4 + c];
+                        o[c] = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) * acc[i][j + TNO][4 * q4 + c];
+                    }
+                } else {
+                    float bc[4] = {0.f, 0.f, 0.f, 0.f};
+                    if (bias != nullptr && f0 < n_out) {
+                        const uint2 bb = *reinterpret_cast<const uint2*>(bias + (int64_t)e * n_out + f0);
+                        bc[0] = __uint_as_float(bb.x << 16);
+                        bc[1] = __uint_as_float(bb.x & 0xffff0000u);
+                        bc[2] = __uint_as_float(bb.y << 16);
+                        bc[3] = __uint_as_float(bb.y & 0xffff0000u);
+                    }
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const float z = acc[i][j][4 * q4 + c] + bc[c];
+                        o[c] = EPI == EPI_GELU_BIAS ? gelu_f(z) : z;
+                    }
+                }
+                if (row < row_end && f0 < n_out) {
+                    uint2 pk;
+                    pk.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+                    pk.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+                    *reinterpret_cast<uint2*>(C + row * n_out + f0) = pk;
+                }
+            }
+        }
+    }
+}
+
+// Partial buffer: a header, then the fp32 accumulators of each tile slice as
+// [slot][wave][i][j][v / 4][lane] float4 (each store and load moves 1 KB per wave instruction).
+// Header: per XCD {rem, S} of its split last round, and per tail tile {row0, row_end, e, n0}.
+constexpr int kPartialFloats = 256 * 256;  // one 256 x 256 tile
+constexpr int kMaxSlotsPerXcd = 64;        // nslots <= 64 (512 blocks)
+struct TailTile {
+    int64_t row0, row_end;
+    int32_t e, n0;
+};
+struct TailHeader {
+    int32_t rem[8], S[8];
+    TailTile tile[8][kMaxSlotsPerXcd];
+};
+constexpr size_t kTailHeaderBytes = (sizeof(TailHeader) + 255) / 256 * 256;
+template <int TM, int TN>
+__device__ __forceinline__ floatx4* partial_at(float* partials, uint32_t pslot, int wave) {
+    float* slots = partials + kTailHeaderBytes / sizeof(float);
+    return reinterpret_cast<floatx4*>(slots + (size_t)pslot * kPartialFloats) + (size_t)wave * (TM * TN * 4 * 64);
+}
+
+// Persistent form of the eight-wave ping-pong tile: one block per CU walks its share of the tile
+// sequence, so the tile schedule and the expert offsets are read into LDS once per block, and the
+// LDS ring runs on across tile boundaries (the next tile's first stages arrive while the current
+// tile's last stages are multiplied). Blocks are dealt to XCDs round-robin; the 32 blocks of an XCD
+// take 32 consecutive tiles of that XCD's chunk at a time (GM row tiles x 32/GM column tiles of one
+// expert), so they share weight panels and token tiles through the XCD's L2 while running in step.
+// When the chunk does not divide into whole rounds, the tiles of the last round are cut along K
+// and spread over all the XCD's blocks (see xcd_plan); those slices leave fp32 partial tiles that
+// gemm_bf16_tail_kernel sums in slice order, so the result does not depend on timing.
+//
+// The MFMA operands are the weight fragment first and the token fragment second, so an accumulator
+// holds a (feature x token) block: a lane owns one token and, per group of 4 registers, 4
+// consecutive output features, written with one 8-byte store. Stores and LDS-DMA loads share the
+// vector-memory counter and may complete out of order, so the memory cluster after a tile's stores
+// waits for the counter to drain before it issues new loads.
+template <int EPI, int GM, int D>
+__global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ C, const int32_t* __restrict__ offsets, int e_begin, int n_groups, int64_t dense_rows,
+    int n_out, int K, float* __restrict__ partials) {
+    constexpr int BM = 256, BN = 256, BK = 32, NS = D + 1;
+    constexpr bool GATED = EPI == EPI_SWIGLU;
+    constexpr int TM = 2;  // 64 tokens per wave
+    constexpr int BNO = GATED ? BN / 2 : BN, WTNO = BNO / 2, TNO = WTNO / 32, TN = GATED ? 2 * TNO : TNO;
+    constexpr int STAGE_ELEMS = (BM + BN) * BK;  // 512 rows of 64 bytes
+    constexpr int STAGE_BYTES = STAGE_ELEMS * 2;
+    constexpr int NQ = 4;  // DMA instructions per wave per stage (a group moves 256 rows = 16 KB)
+    static_assert(TN == 4 && D >= 2 && D <= 5, "tile shape");
+    static_assert(NS * STAGE_BYTES + 2 * 1025 * 4 + 8 * 4 <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE_ELEMS];
+    __shared__ int s_ts[1025];
+    __shared__ int s_off[1025];
+    __shared__ int s_wave[8];
+
+    const int tid = threadIdx.x, lane = lane_id();
+    const TileSched<BM, BNO, GM> ts =
+        setup_sched<BM, BNO, GM>(offsets, e_begin, n_groups, dense_rows, n_out, s_ts, s_off, s_wave);
+    const int nk = K / BK;
+    const uint32_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
+    const XcdPlan plan = xcd_plan(ts.R, xcd, nslots, nk, partials != nullptr);
+    // this block's units: nw whole tiles, then at most one K slice of a tail tile
+    const uint32_t nw = plan.nwhole + ((plan.S == 1 && slot < plan.rem) ? 1u : 0u);
+    const bool has_slice = plan.S >= 2 && slot < plan.rem * plan.S;
+    const uint32_t slice_lin = plan.chunk0 + plan.nwhole * nslots + (has_slice ? slot / plan.S : 0);
+    const int slice_part = has_slice ? (int)(slot % plan.S) : 0;
+    const int slice_kb = slice_part * nk / (int)plan.S, slice_ke = (slice_part + 1) * nk / (int)plan.S;
+    const int nunits = (int)nw + (has_slice ? 1 : 0);
+    if (partials != nullptr && tid == 0) {
+        TailHeader* hdr = reinterpret_cast<TailHeader*>(partials);
+        if (slot == 0) {
+            hdr->rem[xcd] = (int32_t)plan.rem;
+            hdr->S[xcd] = (int32_t)plan.S;
+        }
+        if (has_slice && slice_part == 0) {
+            TailTile tt;
+            ts.decode(slice_lin, tt.row0, tt.row_end, tt.e, tt.n0);
+            hdr->tile[xcd][slot / plan.S] = tt;
+        }
+    }
+    if (nunits == 0) return;  // uniform per block
+    auto unit_lin = [&](int u) { return u < (int)nw ? plan.chunk0 + slot + (uint32_t)u * nslots : slice_lin; };
+    auto unit_kb = [&](int u) { return u < (int)nw ? 0 : slice_kb; };
+    auto unit_ke = [&](int u) { return u < (int)nw ? nk : slice_ke; };
 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = wave >> 2, wig = wave & 3;
@@ -951,7 +1099,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
     auto set_dma_tile = [&](uint32_t lin) {
         int64_t row0, row_end;
         int e, n0;
-        decode(lin, row0, row_end, e, n0);
+        ts.decode(lin, row0, row_end, e, n0);
         if (grp == 0) {
             const int64_t a_rows = row_end - row0 < BM ? row_end - row0 : BM;
             const i32x4 ra = make_rsrc(A + row0 * K, (uint32_t)(a_rows * K * 2));
@@ -994,8 +1142,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
     bf16x8 fa[2][TM], fb[2][TN];
 
-    // stage counters are kept incrementally (no division in the loop): slot in the ring, K slice in
-    // the tile
+    // stage counters are kept incrementally (no division in the loop): slot in the ring, K slice
+    // in the unit
 #define PS_ISSUE(slot_, ks_)                                                                              \
     {                                                                                                     \
         const uint32_t sbase = lds_base + (slot_) * STAGE_BYTES + grp * 16384 + wig * 1024;               \
@@ -1018,29 +1166,32 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
         _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                    \
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk][j], fa[kk][i], acc[i][j], 0, 0, 0);
 
-    const int nk = K / BK;
-    const int G = ntile * nk;  // stages of all this block's tiles
+    int G = (int)nw * nk + (has_slice ? slice_ke - slice_kb : 0);  // stages of all this block's units
     const int npro = G < D ? G : D;
-    uint32_t dma_lin = first;  // tile whose stages are being issued
-    set_dma_tile(dma_lin);
-    int w_slot = 0, w_ks = 0;  // ring slot and K slice of the next stage to issue
-    for (int p = 0; p < npro; ++p) {
-        if (p > 0 && w_ks == 0) {
-            dma_lin += nslots;
-            set_dma_tile(dma_lin);
-        }
-        PS_ISSUE(w_slot, w_ks)
+    int dma_u = 0;  // unit whose stages are being issued
+    set_dma_tile(unit_lin(0));
+    int w_slot = 0, w_ks = unit_kb(0), w_ke = unit_ke(0);
+    auto dma_advance = [&]() {
         w_slot = w_slot + 1 == NS ? 0 : w_slot + 1;
-        w_ks = w_ks + 1 == nk ? 0 : w_ks + 1;
+        if (++w_ks == w_ke && dma_u + 1 < nunits) {
+            ++dma_u;
+            set_dma_tile(unit_lin(dma_u));
+            w_ks = unit_kb(dma_u);
+            w_ke = unit_ke(dma_u);
+        }
+    };
+    for (int p = 0; p < npro; ++p) {
+        PS_ISSUE(w_slot, w_ks)
+        dma_advance();
     }
     wait_stages<NQ>(npro - 1);  // stage 0 of this wave has landed
     lds_barrier();
     if (grp == 1) lds_barrier();  // group 1 runs one cluster behind group 0
     __builtin_amdgcn_sched_barrier(0);
 
-    uint32_t cmp_lin = first;  // tile being multiplied
-    bool drain = false;        // stores of the previous tile may be in flight
-    int r_slot = 0, r_ks = 0;  // ring slot and K slice of stage g
+    int cmp_u = 0;        // unit being multiplied
+    bool drain = false;   // stores of the previous unit may be in flight
+    int r_slot = 0, r_ks = unit_kb(0), r_ke = unit_ke(0);
     for (int g = 0; g < G; ++g) {
         // memory cluster: fragments of stage g, loads of stage g + D
         PS_READ(r_slot)
@@ -1049,13 +1200,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
             drain = false;
         }
         if (g + D < G) {
-            if (w_ks == 0) {
-                dma_lin += nslots;
-                set_dma_tile(dma_lin);
-            }
             PS_ISSUE(w_slot, w_ks)
-            w_slot = w_slot + 1 == NS ? 0 : w_slot + 1;
-            w_ks = w_ks + 1 == nk ? 0 : w_ks + 1;
+            dma_advance();
             wait_vm<(D - 1) * NQ>();  // stage g + 1 of this wave has landed
         } else {
             wait_stages<NQ>(G - g - 2);
@@ -1066,52 +1212,24 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
         // compute cluster
         PS_MMA
         __builtin_amdgcn_sched_barrier(0);
-        const bool tile_end = r_ks == nk - 1;
         r_slot = r_slot + 1 == NS ? 0 : r_slot + 1;
-        r_ks = tile_end ? 0 : r_ks + 1;
-        if (tile_end) {  // last stage of a tile: epilogue of this wave's 64 x 64 (or 64 x 128) block
-            int64_t row0, row_end;
-            int e, n0;
-            decode(cmp_lin, row0, row_end, e, n0);
-            cmp_lin += nslots;
+        if (++r_ks == r_ke) {  // last stage of a unit: store it
+            if (cmp_u < (int)nw) {
+                int64_t row0, row_end;
+                int e, n0;
+                ts.decode(unit_lin(cmp_u), row0, row_end, e, n0);
+                store_tile<EPI, TM, TN>(acc, row0, row_end, e, n0, grp, wm, wn, lane, C, bias, n_out);
+            } else {
+                floatx4* dst = partial_at<TM, TN>(partials, xcd * nslots + slot, wave);
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int64_t row = row0 + grp * 128 + wm * 64 + i * 32 + (lane & 31);
+                for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TNO; ++j) {
+                    for (int j = 0; j < TN; ++j)
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const int f0 = n0 + wn * WTNO + j * 32 + 8 * q4 + 4 * khalf;
-                        float o[4];
-                        if (EPI == EPI_SWIGLU) {
-#pragma unroll
-                            for (int c = 0; c < 4; ++c) {
-                                const float z = acc[i][j][4 * q4 + c];
-                                o[c] = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) * acc[i][j + TNO][4 * q4 + c];
-                            }
-                        } else {
-                            float bc[4] = {0.f, 0.f, 0.f, 0.f};
-                            if (bias != nullptr && f0 < n_out) {
-                                const uint2 bb = *reinterpret_cast<const uint2*>(bias + (int64_t)e * n_out + f0);
-                                bc[0] = __uint_as_float(bb.x << 16);
-                                bc[1] = __uint_as_float(bb.x & 0xffff0000u);
-                                bc[2] = __uint_as_float(bb.y << 16);
-                                bc[3] = __uint_as_float(bb.y & 0xffff0000u);
-                            }
-#pragma unroll
-                            for (int c = 0; c < 4; ++c) {
-                                const float z = acc[i][j][4 * q4 + c] + bc[c];
-                                o[c] = EPI == EPI_GELU_BIAS ? gelu_f(z) : z;
-                            }
-                        }
-                        if (row < row_end && f0 < n_out) {
-                            uint2 pk;
-                            pk.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
-                            pk.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
-                            *reinterpret_cast<uint2*>(C + row * n_out + f0) = pk;
-                        }
-                    }
-                }
+                        for (int v4 = 0; v4 < 4; ++v4)
+                            dst[((i * TN + j) * 4 + v4) * 64 + lane] =
+                                floatx4{acc[i][j][4 * v4], acc[i][j][4 * v4 + 1], acc[i][j][4 * v4 + 2],
+                                        acc[i][j][4 * v4 + 3]};
             }
 #pragma unroll
             for (int i = 0; i < TM; ++i)
@@ -1120,6 +1238,11 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
 #pragma unroll
                     for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
             drain = true;
+            if (cmp_u + 1 < nunits) {
+                ++cmp_u;
+                r_ks = unit_kb(cmp_u);
+                r_ke = unit_ke(cmp_u);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         lds_barrier();
@@ -1131,29 +1254,102 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
 #undef PS_MMA
 }
 
+// Tail of gemm_bf16_persistent_kernel: sums the S fp32 partial tiles of each split tail tile in
+// slice order and applies the epilogue. One thread per group of 4 consecutive output features of
+// one token (gate and up together for SwiGLU); block b covers XCD b % 8, tail tile (b / 8) / CH and
+// chunk (b / 8) % CH of that tile's groups. Tile coordinates come from the header the GEMM wrote.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_bf16_tail_kernel(const float* __restrict__ partials,
+                                                             const uint16_t* __restrict__ bias,
+                                                             uint16_t* __restrict__ C, int n_out) {
+    constexpr bool GATED = EPI == EPI_SWIGLU;
+    constexpr int TM = 2, TN = 4, TNO = GATED ? 2 : 4, WTNO = TNO * 32;
+    constexpr int NGROUPS = 8 * TM * TNO * 4 * 64;  // (wave, i, j, v4, lane) per tile
+    constexpr int CH = NGROUPS / 256;
+    const TailHeader* hdr = reinterpret_cast<const TailHeader*>(partials);
+    const int xcd = blockIdx.x & 7;
+    const int t = (blockIdx.x >> 3) / CH, ch = (blockIdx.x >> 3) % CH;
+    const int S = hdr->S[xcd];
+    if (S < 2 || t >= hdr->rem[xcd]) return;
+    const TailTile tt = hdr->tile[xcd][t];
+    const int gid = ch * 256 + threadIdx.x;  // group id: lane fastest, then v4, j, i, wave
+    const int lane = gid & 63, v4 = (gid >> 6) & 3;
+    const int j = (gid >> 8) % TNO, i = ((gid >> 8) / TNO) % TM, wave = (gid >> 8) / (TNO * TM);
+    const int grp = wave >> 2, wig = wave & 3, wm = wig & 1, wn = wig >> 1;
+    const int nslots = gridDim.x / (8 * CH);
+    floatx4 z = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+    for (int sidx = 0; sidx < S; ++sidx) {
+        const floatx4* src = partial_at<TM, TN>(const_cast<float*>(partials), xcd * nslots + t * S + sidx, wave);
+        z += src[((i * TN + j) * 4 + v4) * 64 + lane];
+        if (GATED) u += src[((i * TN + j + TNO) * 4 + v4) * 64 + lane];
+    }
+    const int64_t row = tt.row0 + grp * 128 + wm * 64 + i * 32 + (lane & 31);
+    const int f0 = tt.n0 + wn * WTNO + j * 32 + 8 * v4 + 4 * (lane >> 5);
+    if (row >= tt.row_end || f0 >= n_out) return;
+    float o[4];
+    if (GATED) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o[c] = z[c] * __builtin_amdgcn_rcpf(1.0f + __expf(-z[c])) * u[c];
+    } else {
+        float bc[4] = {0.f, 0.f, 0.f, 0.f};
+        if (bias != nullptr) {
+            const uint2 bb = *reinterpret_cast<const uint2*>(bias + (int64_t)tt.e * n_out + f0);
+            bc[0] = __uint_as_float(bb.x << 16);
+            bc[1] = __uint_as_float(bb.x & 0xffff0000u);
+            bc[2] = __uint_as_float(bb.y << 16);
+            bc[3] = __uint_as_float(bb.y & 0xffff0000u);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o[c] = EPI == EPI_GELU_BIAS ? gelu_f(z[c] + bc[c]) : z[c] + bc[c];
+    }
+    uint2 pk;
+    pk.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+    pk.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+    *reinterpret_cast<uint2*>(C + row * n_out + f0) = pk;
+}
+
+// Blocks of the persistent GEMM: the CU count in whole XCD rounds, at most 8 * kMaxSlotsPerXcd.
+int persistent_grid_cap() {
+    const int cap = (device_cu_count() / 8) * 8;
+    return cap < 8 * kMaxSlotsPerXcd ? cap : 8 * kMaxSlotsPerXcd;
+}
+
+// Bytes of the partial buffer the bf16 grouped GEMM may use (header + one 256 x 256 fp32 tile per
+// block).
+size_t gemm_partials_bytes(int dtype) {
+    if (dtype != MOE_BF16) return 0;
+    return kTailHeaderBytes + (size_t)persistent_grid_cap() * kPartialFloats * sizeof(float);
+}
+
 template <int GM, int D>
 void launch_bf16_persistent(int epi, const void* A, const void* B, const void* bias, void* C,
                             const int32_t* offsets, int e_begin, int n_groups, int64_t max_rows, int64_t dense_rows,
-                            int n_out, int K, hipStream_t s) {
+                            int n_out, int K, float* partials, hipStream_t s) {
     const int bno = epi == EPI_SWIGLU ? 128 : 256;
     const int64_t m_tiles = offsets ? (max_rows + 255) / 256 + n_groups : (dense_rows + 255) / 256;
     const int64_t tiles = m_tiles * ((n_out + bno - 1) / bno);
-    const int64_t cap = (int64_t)(device_cu_count() / 8) * 8;
+    const int64_t cap = persistent_grid_cap();
     const int64_t want = ((tiles + 7) / 8) * 8;
     const unsigned grid = (unsigned)(want < cap ? want : cap);
+    // a dense product whose tiles fill whole rounds needs no tail pass
+    if (!offsets && tiles % grid == 0) partials = nullptr;
     const auto a = static_cast<const uint16_t*>(A);
     const auto b = static_cast<const uint16_t*>(B);
     const auto bi = static_cast<const uint16_t*>(bias);
     auto c = static_cast<uint16_t*>(C);
-    if (epi == EPI_SWIGLU)
-        gemm_bf16_persistent_kernel<EPI_SWIGLU, GM, D><<<grid, 512, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
-                                                                           dense_rows, n_out, K);
-    else if (epi == EPI_GELU_BIAS)
-        gemm_bf16_persistent_kernel<EPI_GELU_BIAS, GM, D><<<grid, 512, 0, s>>>(a, b, bi, c, offsets, e_begin,
-                                                                              n_groups, dense_rows, n_out, K);
-    else
-        gemm_bf16_persistent_kernel<EPI_BIAS, GM, D><<<grid, 512, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
-                                                                         dense_rows, n_out, K);
+#define MOE_PERSIST(EPI_)                                                                                 \
+    {                                                                                                     \
+        gemm_bf16_persistent_kernel<EPI_, GM, D><<<grid, 512, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups, \
+                                                                     dense_rows, n_out, K, partials);     \
+        if (partials) {                                                                                   \
+            constexpr int CH_ = 8 * 2 * (EPI_ == EPI_SWIGLU ? 2 : 4) * 4 * 64 / 256;                          \
+            gemm_bf16_tail_kernel<EPI_><<<grid * CH_, 256, 0, s>>>(partials, bi, c, n_out);               \
+        }                                                                                                 \
+    }
+    if (epi == EPI_SWIGLU) MOE_PERSIST(EPI_SWIGLU)
+    else if (epi == EPI_GELU_BIAS) MOE_PERSIST(EPI_GELU_BIAS)
+    else MOE_PERSIST(EPI_BIAS)
+#undef MOE_PERSIST
 }
 
 // fp32 path (SIMT, 64 x 64 output tile, 4 x 4 per thread, sequential fp32 FMA over K).
@@ -1263,11 +1459,11 @@ void launch_bf16_tiles(int epi, const void* A, const void* B, const void* bias, 
 
 void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* B, const void* bias, void* C,
                          const int32_t* offsets, int e_begin, int n_groups, int64_t max_rows, int64_t dense_rows,
-                         int n_out, int K, hipStream_t s) {
+                         int n_out, int K, float* partials, hipStream_t s) {
     if (dtype == MOE_BF16) {
         (void)bm;
         launch_bf16_persistent<8, 3>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows, n_out, K,
-                                     s);
+                                     partials, s);
         return;
     }
     const int64_t m_tiles = offsets ? (max_rows + 63) / 64 + n_groups : (dense_rows + 63) / 64;

@@ -80,24 +80,38 @@ PermWs perm_ws(const moe_shape* s) {
     return w;
 }
 
+// fp32 partial tiles of the grouped GEMM's split last round (bf16 layers only)
+struct ExpertWs {
+    size_t partials, bytes;
+};
+ExpertWs expert_ws(const moe_shape* s) {
+    ExpertWs w;
+    Carver c;
+    w.partials = c.take(moe::gemm_partials_bytes(s->dtype));
+    w.bytes = c.off;
+    return w;
+}
+
 struct FfnWs {
-    size_t h, bytes;
+    size_t h, partials, bytes;
 };
 FfnWs ffn_ws(const moe_shape* s) {
     FfnWs w;
     Carver c;
     w.h = c.take((size_t)s->T * s->k * s->d_ff * elem_bytes(s));
+    w.partials = c.take(moe::gemm_partials_bytes(s->dtype));
     w.bytes = c.off;
     return w;
 }
 
 struct SharedWs {
-    size_t hs, bytes;
+    size_t hs, partials, bytes;
 };
 SharedWs shared_ws(const moe_shape* s) {
     SharedWs w;
     Carver c;
     w.hs = c.take((size_t)s->T * s->d_ff_shared * elem_bytes(s));
+    w.partials = c.take(s->d_ff_shared ? moe::gemm_partials_bytes(s->dtype) : 0);
     w.bytes = c.off;
     return w;
 }
@@ -163,40 +177,48 @@ void do_permute(const moe_shape* s, const int32_t* topk_idx, const void* x, int3
     moe::launch_perm_scatter(x, inv_pos, s->T, s->d_model, s->k, elem_bytes(s), x_perm, st);
 }
 
+inline float* partials_of(void* ws, size_t off, const moe_shape* s) {
+    return s->dtype == MOE_BF16 ? at<float>(ws, off) : nullptr;
+}
+
 void do_up(const moe_shape* s, int e_begin, int e_end, const void* x_perm, const int32_t* offsets,
-           const void* w_in, const void* b_in, void* h, hipStream_t st) {
+           const void* w_in, const void* b_in, void* h, float* partials, hipStream_t st) {
     const int64_t A = s->T * s->k;
     const moe::GemmPlan p = moe::plan_gemm(s->dtype, A / s->E, s->d_ff, s->d_model);
     moe::launch_grouped_gemm(s->dtype, s->act == MOE_SWIGLU ? moe::EPI_SWIGLU : moe::EPI_GELU_BIAS, p.bm, x_perm,
-                             w_in, b_in, h, offsets, e_begin, e_end - e_begin, A, 0, s->d_ff, s->d_model, st);
+                             w_in, b_in, h, offsets, e_begin, e_end - e_begin, A, 0, s->d_ff, s->d_model, partials,
+                             st);
 }
 
 void do_down(const moe_shape* s, int e_begin, int e_end, const void* h, const int32_t* offsets, const void* w_out,
-             const void* b_out, void* y_perm, hipStream_t st) {
+             const void* b_out, void* y_perm, float* partials, hipStream_t st) {
     const int64_t A = s->T * s->k;
     const moe::GemmPlan p = moe::plan_gemm(s->dtype, A / s->E, s->d_model, s->d_ff);
     moe::launch_grouped_gemm(s->dtype, moe::EPI_BIAS, p.bm, h, w_out, b_out, y_perm, offsets, e_begin,
-                             e_end - e_begin, A, 0, s->d_model, s->d_ff, st);
+                             e_end - e_begin, A, 0, s->d_model, s->d_ff, partials, st);
 }
 
 void do_ffn(const moe_shape* s, int e_begin, int e_end, const void* x_perm, const int32_t* offsets,
             const void* w_in, const void* b_in, const void* w_out, const void* b_out, void* y_perm, void* ws,
             hipStream_t st) {
-    void* h = at<void>(ws, ffn_ws(s).h);
-    do_up(s, e_begin, e_end, x_perm, offsets, w_in, b_in, h, st);
-    do_down(s, e_begin, e_end, h, offsets, w_out, b_out, y_perm, st);
+    const FfnWs w = ffn_ws(s);
+    void* h = at<void>(ws, w.h);
+    float* partials = partials_of(ws, w.partials, s);
+    do_up(s, e_begin, e_end, x_perm, offsets, w_in, b_in, h, partials, st);
+    do_down(s, e_begin, e_end, h, offsets, w_out, b_out, y_perm, partials, st);
 }
 
 void do_shared(const moe_shape* s, const void* x, const void* ws_in, const void* ws_out, void* y_shared, void* ws,
                hipStream_t st) {
     const SharedWs w = shared_ws(s);
     void* hs = at<void>(ws, w.hs);
+    float* partials = partials_of(ws, w.partials, s);
     const moe::GemmPlan p1 = moe::plan_gemm(s->dtype, s->T, s->d_ff_shared, s->d_model);
     const moe::GemmPlan p2 = moe::plan_gemm(s->dtype, s->T, s->d_model, s->d_ff_shared);
     moe::launch_grouped_gemm(s->dtype, moe::EPI_SWIGLU, p1.bm, x, ws_in, nullptr, hs, nullptr, 0, 1, s->T, s->T,
-                             s->d_ff_shared, s->d_model, st);
+                             s->d_ff_shared, s->d_model, partials, st);
     moe::launch_grouped_gemm(s->dtype, moe::EPI_BIAS, p2.bm, hs, ws_out, nullptr, y_shared, nullptr, 0, 1, s->T, s->T,
-                             s->d_model, s->d_ff_shared, st);
+                             s->d_model, s->d_ff_shared, partials, st);
 }
 
 #define MOE_REQUIRE(cond)                       \
@@ -221,6 +243,7 @@ int moe_workspace_bytes(const moe_shape* shape, int stage, size_t* bytes) {
         case MOE_STAGE_FFN: *bytes = ffn_ws(shape).bytes; break;
         case MOE_STAGE_SHARED: *bytes = shared_ws(shape).bytes; break;
         case MOE_STAGE_FORWARD: *bytes = fwd_ws(shape).bytes; break;
+        case MOE_STAGE_EXPERT: *bytes = expert_ws(shape).bytes; break;
         default: return MOE_ERR_INVALID_ARG;
     }
     return MOE_OK;
@@ -273,28 +296,35 @@ int moe_grouped_ffn(const moe_shape* shape, int32_t e_begin, int32_t e_end, cons
 }
 
 int moe_expert_up(const moe_shape* shape, int32_t e_begin, int32_t e_end, const void* x_perm, const int32_t* offsets,
-                  const void* w_in, const void* b_in, void* h, moe_stream_t stream) {
+                  const void* w_in, const void* b_in, void* h, void* ws, size_t ws_bytes, moe_stream_t stream) {
     const int rc = check_shape(shape);
     if (rc != MOE_OK) return rc;
     MOE_REQUIRE(e_begin >= 0 && e_begin <= e_end && e_end <= shape->E);
-    MOE_REQUIRE(ok_ptr(x_perm) && ok_ptr(offsets) && ok_ptr(w_in) && ok_opt(b_in) && ok_ptr(h));
+    MOE_REQUIRE(ok_ptr(x_perm) && ok_ptr(offsets) && ok_ptr(w_in) && ok_opt(b_in) && ok_ptr(h) && ok_opt(ws));
     if (shape->act == MOE_SWIGLU && b_in != nullptr) return MOE_ERR_INVALID_ARG;
+    const ExpertWs w = expert_ws(shape);
+    if (ws_bytes < w.bytes || (ws == nullptr && w.bytes > 0)) return MOE_ERR_WORKSPACE;
     if (shape->T == 0 || e_begin == e_end) return MOE_OK;
     (void)hipGetLastError();
-    do_up(shape, e_begin, e_end, x_perm, offsets, w_in, b_in, h, static_cast<hipStream_t>(stream));
+    do_up(shape, e_begin, e_end, x_perm, offsets, w_in, b_in, h, partials_of(ws, w.partials, shape),
+          static_cast<hipStream_t>(stream));
     return launched();
 }
 
 int moe_expert_down(const moe_shape* shape, int32_t e_begin, int32_t e_end, const void* h, const int32_t* offsets,
-                    const void* w_out, const void* b_out, void* y_perm, moe_stream_t stream) {
+                    const void* w_out, const void* b_out, void* y_perm, void* ws, size_t ws_bytes,
+                    moe_stream_t stream) {
     const int rc = check_shape(shape);
     if (rc != MOE_OK) return rc;
     MOE_REQUIRE(e_begin >= 0 && e_begin <= e_end && e_end <= shape->E);
-    MOE_REQUIRE(ok_ptr(h) && ok_ptr(offsets) && ok_ptr(w_out) && ok_opt(b_out) && ok_ptr(y_perm));
+    MOE_REQUIRE(ok_ptr(h) && ok_ptr(offsets) && ok_ptr(w_out) && ok_opt(b_out) && ok_ptr(y_perm) && ok_opt(ws));
     if (shape->act == MOE_SWIGLU && b_out != nullptr) return MOE_ERR_INVALID_ARG;
+    const ExpertWs w = expert_ws(shape);
+    if (ws_bytes < w.bytes || (ws == nullptr && w.bytes > 0)) return MOE_ERR_WORKSPACE;
     if (shape->T == 0 || e_begin == e_end) return MOE_OK;
     (void)hipGetLastError();
-    do_down(shape, e_begin, e_end, h, offsets, w_out, b_out, y_perm, static_cast<hipStream_t>(stream));
+    do_down(shape, e_begin, e_end, h, offsets, w_out, b_out, y_perm, partials_of(ws, w.partials, shape),
+            static_cast<hipStream_t>(stream));
     return launched();
 }
 

@@ -47,9 +47,12 @@ GemmPlan plan_gemm(int dtype, int64_t rows_per_group_hint, int n_out, int K);
 // C[rows, n_out] = epi(A[rows, K] * B_e^T) over groups e_begin.. (offsets != NULL; the kernel builds
 // its tile schedule from the device-side offsets) or one dense group of `dense_rows` rows
 // (offsets == NULL). B is [E][n_b_rows][K] (n_b_rows = 2*n_out for SwiGLU). One kernel launch.
+// partials: fp32 scratch of gemm_partials_bytes(dtype) bytes (or NULL) in which the bf16 kernel
+// splits the last, incomplete round of tiles along K; summed in a fixed order by a second launch.
 void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* B, const void* bias,
                          void* C, const int32_t* offsets, int e_begin, int n_groups, int64_t max_rows,
-                         int64_t dense_rows, int n_out, int K, hipStream_t s);
+                         int64_t dense_rows, int n_out, int K, float* partials, hipStream_t s);
+size_t gemm_partials_bytes(int dtype);
 
 // ---- combine ----------------------------------------------------------------------------
 void launch_combine(int dtype, const void* y_perm, const int32_t* inv_pos, const float* topk_w,

@@ -68,12 +68,12 @@ class MoeLayer:
     def up(self, e_begin=0, e_end=None):
         t = self.t
         L.moe_expert_up(self.shape, e_begin, self.cfg.E if e_end is None else e_end, self.x_perm, self.offsets,
-                        t["w_in"], t["b_in"], self.h)
+                        t["w_in"], t["b_in"], self.h, self.ws(L.MOE_STAGE_EXPERT))
 
     def down(self, e_begin=0, e_end=None):
         t = self.t
         L.moe_expert_down(self.shape, e_begin, self.cfg.E if e_end is None else e_end, self.h, self.offsets,
-                          t["w_out"], t["b_out"], self.y_perm)
+                          t["w_out"], t["b_out"], self.y_perm, self.ws(L.MOE_STAGE_EXPERT))
 
     def shared(self):
         t = self.t

@@ -89,11 +89,17 @@ def test_bad_enums_and_stage(lib):
 
 
 def test_workspace_sizes_monotone(lib):
-    small = [ws_bytes(good_shape(T=64), st)[1] for st in range(5)]
-    big = [ws_bytes(good_shape(T=4096), st)[1] for st in range(5)]
+    small = [ws_bytes(good_shape(T=64), st)[1] for st in range(6)]
+    big = [ws_bytes(good_shape(T=4096), st)[1] for st in range(6)]
     assert all(b >= a for a, b in zip(small, big))
     assert big[L.MOE_STAGE_FFN] >= 4096 * 2 * 128 * 2  # h = [T*k, d_ff] bf16
     rc, n = ws_bytes(good_shape(d_ff_shared=0), L.MOE_STAGE_SHARED)
+    assert rc == 0 and n == 0
+    # bf16 grouped GEMMs keep one fp32 256 x 256 partial tile per block (at least 8 blocks)
+    rc, n = ws_bytes(good_shape(), L.MOE_STAGE_EXPERT)
+    assert rc == 0 and n >= 8 * 256 * 256 * 4
+    assert ws_bytes(good_shape(), L.MOE_STAGE_FFN)[1] >= n
+    rc, n = ws_bytes(good_shape(dtype="f32"), L.MOE_STAGE_EXPERT)
     assert rc == 0 and n == 0
 
 
@@ -155,6 +161,25 @@ def test_ffn_rejections(lib):
     bad = list(good)
     bad[1], bad[2] = 4, 4  # empty expert range: no-op
     assert f(*bad) == L.MOE_OK
+    # the two one-projection entry points: range, bias and workspace checks come before any launch
+    ne = ws_bytes(s, L.MOE_STAGE_EXPERT)[1]
+    for fn in (lib.moe_expert_up, lib.moe_expert_down):
+        good = [ctypes.byref(s), 0, 8, FAKE, FAKE, FAKE, None, FAKE, FAKE, ne, None]
+        bad = list(good)
+        bad[1], bad[2] = 0, 9
+        assert fn(*bad) == L.MOE_ERR_INVALID_ARG
+        bad = list(good)
+        bad[6] = FAKE  # bias given to a SwiGLU layer
+        assert fn(*bad) == L.MOE_ERR_INVALID_ARG
+        bad = list(good)
+        bad[9] = ne - 256
+        assert fn(*bad) == L.MOE_ERR_WORKSPACE
+        bad = list(good)
+        bad[8], bad[9] = None, 0
+        assert fn(*bad) == L.MOE_ERR_WORKSPACE
+        bad = list(good)
+        bad[1], bad[2] = 4, 4  # empty expert range: no-op
+        assert fn(*bad) == L.MOE_OK
     sh = lib.moe_shared_ffn
     assert sh(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == L.MOE_ERR_INVALID_ARG  # no shared
 

@@ -2,7 +2,7 @@
 (several tiles, ragged tails) and on the edge cases: T = 1, E = 1 with k = 1, k = E, all-tied
 logits (lower-index rule, empty experts, one expert taking every token), expert sub-ranges, no
 renormalisation, fp32 and bf16, GELU with biases and SwiGLU, sigmoid scoring with a selection
-bias and a shared expert."""
+bias and a shared expert, and GEMMs whose last round of tiles is split along K."""
 import numpy as np
 import pytest
 import torch
@@ -30,6 +30,11 @@ CASES = {
     "E1_k1": I.mini("small_bf16", T=300, d=128, F=128, E=1, k=1),
     "k_eq_E": I.mini("small_bf16", T=257, d=128, F=64, E=4, k=4),
     "T1": I.mini("deepseek_v3", T=1, d=128, F=64, Fs=64),
+    # one expert, so the tile count is fixed: 4 x 66 = 264 gate/up tiles (just over one round of 256
+    # blocks), whose last round the GEMM splits along K into fp32 partial tiles ...
+    "split_last_round_up": I.mini("small_bf16", T=1000, d=512, F=8448, E=1, k=1),
+    # ... and 65 x 4 = 260 down-projection tiles
+    "split_last_round_down": I.mini("small_bf16", T=16640, d=1024, F=128, E=1, k=1),
 }
 
 
