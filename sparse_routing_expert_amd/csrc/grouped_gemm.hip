@@ -1257,26 +1257,30 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
 // Tail of gemm_bf16_persistent_kernel: sums the S fp32 partial tiles of each split tail tile in
 // slice order and applies the epilogue. One thread per group of 4 consecutive output features of
 // one token (gate and up together for SwiGLU); block b covers XCD b % 8, tail tile (b / 8) / CH and
-// chunk (b / 8) % CH of that tile's groups. Tile coordinates come from the header the GEMM wrote.
+// chunk (b / 8) % CH of that tile's groups (launch: 8 * nslots * CH blocks of 256 threads, nslots
+// the GEMM's blocks per XCD). Tile coordinates come from the header the GEMM wrote.
+template <int EPI>
+constexpr int tail_chunks() {
+    return 8 * 2 * (EPI == EPI_SWIGLU ? 2 : 4) * 4 * 64 / 256;  // (wave, i, j, v4, lane) groups / 256
+}
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_bf16_tail_kernel(const float* __restrict__ partials,
                                                              const uint16_t* __restrict__ bias,
-                                                             uint16_t* __restrict__ C, int n_out) {
+                                                             uint16_t* __restrict__ C, int n_out, int nslots) {
     constexpr bool GATED = EPI == EPI_SWIGLU;
     constexpr int TM = 2, TN = 4, TNO = GATED ? 2 : 4, WTNO = TNO * 32;
-    constexpr int NGROUPS = 8 * TM * TNO * 4 * 64;  // (wave, i, j, v4, lane) per tile
-    constexpr int CH = NGROUPS / 256;
+    constexpr int CH = tail_chunks<EPI>();
     const TailHeader* hdr = reinterpret_cast<const TailHeader*>(partials);
     const int xcd = blockIdx.x & 7;
     const int t = (blockIdx.x >> 3) / CH, ch = (blockIdx.x >> 3) % CH;
     const int S = hdr->S[xcd];
-    if (S < 2 || t >= hdr->rem[xcd]) return;
+    // the GEMM splits only when rem * S <= nslots, so every slot read below is one it wrote
+    if (S < 2 || t >= hdr->rem[xcd] || t >= nslots || (t + 1) * S > nslots) return;
     const TailTile tt = hdr->tile[xcd][t];
     const int gid = ch * 256 + threadIdx.x;  // group id: lane fastest, then v4, j, i, wave
     const int lane = gid & 63, v4 = (gid >> 6) & 3;
     const int j = (gid >> 8) % TNO, i = ((gid >> 8) / TNO) % TM, wave = (gid >> 8) / (TNO * TM);
     const int grp = wave >> 2, wig = wave & 3, wm = wig & 1, wn = wig >> 1;
-    const int nslots = gridDim.x / (8 * CH);
     floatx4 z = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
     for (int sidx = 0; sidx < S; ++sidx) {
         const floatx4* src = partial_at<TM, TN>(const_cast<float*>(partials), xcd * nslots + t * S + sidx, wave);
@@ -1341,10 +1345,9 @@ void launch_bf16_persistent(int epi, const void* A, const void* B, const void* b
     {                                                                                                     \
         gemm_bf16_persistent_kernel<EPI_, GM, D><<<grid, 512, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups, \
                                                                      dense_rows, n_out, K, partials);     \
-        if (partials) {                                                                                   \
-            constexpr int CH_ = 8 * 2 * (EPI_ == EPI_SWIGLU ? 2 : 4) * 4 * 64 / 256;                          \
-            gemm_bf16_tail_kernel<EPI_><<<grid * CH_, 256, 0, s>>>(partials, bi, c, n_out);               \
-        }                                                                                                 \
+        if (partials)                                                                                     \
+            gemm_bf16_tail_kernel<EPI_><<<grid * tail_chunks<EPI_>(), 256, 0, s>>>(partials, bi, c, n_out,  \
+                                                                                  (int)(grid / 8));       \
     }
     if (epi == EPI_SWIGLU) MOE_PERSIST(EPI_SWIGLU)
     else if (epi == EPI_GELU_BIAS) MOE_PERSIST(EPI_GELU_BIAS)
