@@ -178,3 +178,54 @@ def stats(x: Mat, w_r: Mat, idx: List[List[int]], score: str):
     f = [sum(row.count(e) for row in idx) / T for e in range(E)]
     aux = E * math.fsum(a * b for a, b in zip(f, P))
     return f, P, aux, ent
+
+
+def permutation_capacity(idx: List[List[int]], E: int, cap: int):
+    """(offsets, sorted_token, inv_pos) with at most `cap` rows per expert, by counting: an
+    assignment (t, j) to expert e is kept when fewer than `cap` assignments to e precede it in
+    t*k + j order; its row is the kept total of lower experts plus that number; a dropped one has
+    row -1."""
+    T = len(idx)
+    k = len(idx[0]) if T else 0
+    flat = [e for row in idx for e in row]
+    kept = [min(cap, sum(1 for v in flat if v == e)) for e in range(E)]
+    offsets = [sum(kept[:e]) for e in range(E + 1)]
+    inv_pos = [-1] * len(flat)
+    sorted_token = [0] * offsets[E]
+    for a, e in enumerate(flat):
+        n = sum(1 for b in range(a) if flat[b] == e)
+        if n < cap:
+            inv_pos[a] = offsets[e] + n
+            sorted_token[offsets[e] + n] = a // k
+    return offsets, sorted_token, inv_pos
+
+
+def layer_capacity(x: Mat, w_r: Mat, w_in, b_in, w_out, b_out, k: int, act: str, cap: int,
+                   score: str = "softmax", renorm: bool = True, sel_bias: Optional[Vec] = None,
+                   ws_in=None, ws_out=None):
+    """The dense masked ensemble with expert capacity: the gate of a dropped assignment (one with
+    `cap` or more earlier assignments, in token order, to the same expert) is multiplied by 0."""
+    E = len(w_r)
+    choices = []
+    for xt in x:
+        l = logits(xt, w_r)
+        choices.append((l, select(key_of(l, score, sel_bias), k)))
+    seen = [0] * E
+    ys = []
+    for xt, (l, chosen) in zip(x, choices):
+        g_all = masked_gates(l, chosen, score, renorm)
+        for e in chosen:  # slot order j = 0..k-1 within the token
+            if seen[e] >= cap:
+                g_all[e] = 0.0
+            seen[e] += 1
+        acc = [0.0] * len(xt)
+        for e in range(E):
+            out = expert(xt, w_in[e], None if b_in is None else b_in[e], w_out[e],
+                         None if b_out is None else b_out[e], act)
+            acc = [a + g_all[e] * o for a, o in zip(acc, out)]
+        if ws_in is not None:
+            sh = expert(xt, ws_in, None, ws_out, None, "swiglu")
+            acc = [a + v for a, v in zip(acc, sh)]
+        ys.append(acc)
+    return [c for _, c in choices], ys
+

@@ -42,7 +42,11 @@ reason in the design notes of the repository):
     probability (sigmoid: of s / sum s), aux = E * sum f_e P_e (the caller applies
     alpha), entropy = mean over tokens of -sum p ln p, in nats;
   * GELU is the exact erf form; SwiGLU is (SiLU(x Wg^T) * (x Wu^T)) Wd^T with no
-    biases; a shared expert has gate 1 and is added after the routed sum.
+    biases; a shared expert has gate 1 and is added after the routed sum;
+  * capacity: C = ceil(c * T * k / E) rows per expert; an expert keeps its first C
+    assignments in (t, j) order; a dropped assignment contributes nothing (it reaches
+    the next layer through the residual, outside this layer); kept gates unchanged;
+  * bias update: b_e <- b_e - gamma * sign(count_e - T*k/E), sign(0) = 0, in float32.
 """
 from __future__ import annotations
 
@@ -209,31 +213,57 @@ def route(x, w_r, k: int, score: str = "softmax", renorm: bool = True,
 # --------------------------------------------------------------------------------------
 
 
-def permute(idx: np.ndarray, E: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+def permute(idx: np.ndarray, E: int, capacity: int = 0) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Expert-contiguous order of the T*k assignments.
 
-    offsets[e] = sum of counts of experts below e (offsets[E] = T*k). Within
-    expert e, its assignments (t, j) appear in ascending t*k + j -- the order a
-    per-expert nonzero() over the [T, k] index matrix yields ([FS] loop over
-    experts) -- packed into one contiguous buffer ([RO] What Most Articles
-    Miss 2). Returns (offsets [E+1], sorted_token [T*k] (row -> token),
-    inv_pos [T*k] ((t, j) -> row)).
+    offsets[e] = sum of the row counts of experts below e. Within expert e, its
+    assignments (t, j) appear in ascending t*k + j -- the order a per-expert
+    nonzero() over the [T, k] index matrix yields ([FS] loop over experts) --
+    packed into one contiguous buffer ([RO] What Most Articles Miss 2).
+
+    capacity > 0 caps every expert at that many rows ([RO] Why It Matters 3 and
+    FAQ 6; [VI] capacity factor; [MT] The capacity factor formula): an expert
+    keeps the first `capacity` of its assignments in that order, and the rest
+    are dropped -- they pass the layer untouched through the residual, so they
+    get no row (inv_pos = -1). capacity = 0 keeps everything (dropless).
+
+    Returns (offsets [E+1], sorted_token [offsets[E]] (row -> token),
+    inv_pos [T*k] ((t, j) -> row, or -1 when dropped)).
     """
     T, k = idx.shape
     flat = idx.reshape(-1)
     offsets = np.zeros(E + 1, dtype=np.int64)
     sorted_token = np.empty(T * k, dtype=np.int64)
-    inv_pos = np.empty(T * k, dtype=np.int64)
+    inv_pos = np.full(T * k, -1, dtype=np.int64)
     row = 0
     for e in range(E):
         offsets[e] = row
-        for a in np.nonzero(flat == e)[0]:  # ascending assignment index a = t*k + j
+        for n, a in enumerate(np.nonzero(flat == e)[0]):  # ascending assignment index a = t*k + j
+            if capacity > 0 and n >= capacity:
+                break
             sorted_token[row] = a // k
             inv_pos[a] = row
             row += 1
     offsets[E] = row
-    assert row == T * k
-    return offsets, sorted_token, inv_pos
+    assert capacity > 0 or row == T * k
+    return offsets, sorted_token[:row], inv_pos
+
+
+def capacity_rows(T: int, k: int, E: int, factor: float) -> int:
+    """Expert capacity in rows: ceil(factor * T * k / E) ([RO] Why It Matters 3 and FAQ 6 state it
+    as (tokens * k / experts) * capacity factor; rounding up keeps factor 1 exactly balanced)."""
+    return int(math.ceil(factor * T * k / E))
+
+
+def update_bias(bias: np.ndarray, counts: np.ndarray, T: int, k: int, gamma: float) -> np.ndarray:
+    """Aux-loss-free balancing step ([RO] How It Works 2 and Fine-Tuning Strategies 1): an expert
+    above the uniform load T*k/E lowers its selection bias by gamma, one below raises it by gamma,
+    one exactly at it keeps it. The bias is stored in float32, so the step is one float32
+    subtraction; the comparison with T*k/E is exact (counts * E against T * k in integers)."""
+    counts = np.asarray(counts, dtype=np.int64)
+    E = counts.shape[0]
+    s = np.sign(counts * E - T * k).astype(np.float32)
+    return (np.asarray(bias, dtype=np.float32) - np.float32(gamma) * s).astype(np.float32)
 
 
 # --------------------------------------------------------------------------------------
@@ -319,8 +349,10 @@ def combine(y_perm: np.ndarray, inv_pos: np.ndarray, g: np.ndarray,
     [RO] MoE Layer Output; [FS] index_add of gate-scaled expert outputs)."""
     T, k = g.shape
     y = np.zeros((T, y_perm.shape[1]))
+    pos = inv_pos.reshape(T, k)
     for j in range(k):
-        y += g[:, j:j + 1] * y_perm[inv_pos.reshape(T, k)[:, j]]
+        kept = pos[:, j] >= 0  # a dropped assignment (capacity) contributes nothing
+        y[kept] += g[kept, j:j + 1] * y_perm[pos[kept, j]]
     if y_shared is not None:
         y = y + y_shared
     return y
@@ -340,12 +372,14 @@ class LayerResult:
 
 def layer_forward(x, w_r, get_expert: ExpertGetter, k: int, act: str, score: str = "softmax",
                   renorm: bool = True, sel_bias=None, ws_in=None, ws_out=None,
-                  forced_idx: Optional[np.ndarray] = None) -> LayerResult:
+                  forced_idx: Optional[np.ndarray] = None, capacity: int = 0) -> LayerResult:
     """The whole layer: y[t] = sum over the selected e of g_e(t) FFN_e(x[t]) (+ shared(x[t])).
 
     forced_idx replaces the oracle's own selection (used to re-run the expert and
     combine steps on another implementation's routing of ambiguous tokens); the
-    gates are then those of the forced selection.
+    gates are then those of the forced selection. capacity > 0 drops the
+    assignments beyond each expert's first `capacity` (see permute); the gates of
+    the kept ones are unchanged.
     """
     x = f64(x)
     E = w_r.shape[0]
@@ -354,7 +388,7 @@ def layer_forward(x, w_r, get_expert: ExpertGetter, k: int, act: str, score: str
         idx = np.asarray(forced_idx, dtype=np.int64)
         r = dataclasses.replace(r, idx=idx, gates=gates(r.logits, idx, score, renorm),
                                 counts=expert_counts(idx, E))
-    offsets, sorted_token, inv_pos = permute(r.idx, E)
+    offsets, sorted_token, inv_pos = permute(r.idx, E, capacity)
     x_perm = x[sorted_token]
     y_perm = experts_on_rows(x_perm, offsets, get_expert, act)
     ys = shared_ffn(x, f64(ws_in), f64(ws_out)) if ws_in is not None else None

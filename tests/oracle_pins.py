@@ -296,6 +296,88 @@ def check_ambiguity(ref):
     assert not ref.ambiguous_tokens(key, 4).any()
 
 
+# ------------------------------------------------------------------ capacity and bias update
+
+
+def check_capacity_brute(ref, seeds=range(30)):
+    """Capacity permutation and layer against counting / the masked dense ensemble."""
+    for s in seeds:
+        c = tiny_case(2000 + s, T=int(np.random.default_rng(s).integers(2, 9)))
+        for cap in (1, 2, 3):
+            r = run_ref(ref, c, capacity=cap)
+            b_idx, b_y = brute.layer_capacity(_L(c["x"]), _L(c["w_r"]), _L(c["w_in"]), _L(c["b_in"]),
+                                              _L(c["w_out"]), _L(c["b_out"]), c["k"], c["act"], cap, c["score"],
+                                              c["renorm"], _L(c["sel_bias"]), _L(c["ws_in"]), _L(c["ws_out"]))
+            assert r.route.idx.tolist() == b_idx, s
+            off, st, inv = brute.permutation_capacity(b_idx, c["E"], cap)
+            assert r.offsets.tolist() == off and r.sorted_token.tolist() == st and r.inv_pos.tolist() == inv, (s, cap)
+            _close(r.y, b_y, 1e-10, f"capacity y seed {s} cap {cap}")
+
+
+def check_capacity_limits(ref, seeds=range(10)):
+    """A capacity at or above every expert's load changes nothing; kept rows = min(count, C); the
+    output lost to capacity is exactly the gate-weighted expert output of the dropped assignments."""
+    for s in seeds:
+        c = tiny_case(3000 + s, T=8, E=3, k=2)
+        full = run_ref(ref, c)
+        big = run_ref(ref, c, capacity=int(full.route.counts.max()))
+        assert np.array_equal(big.inv_pos, full.inv_pos) and np.array_equal(big.offsets, full.offsets)
+        assert np.array_equal(big.y, full.y)
+        for cap in (1, 2, 4):
+            r = run_ref(ref, c, capacity=cap)
+            kept = np.diff(r.offsets)
+            assert kept.tolist() == np.minimum(full.route.counts, cap).tolist(), (s, cap)
+            assert int((r.inv_pos >= 0).sum()) == int(r.offsets[-1])
+            lost = np.zeros_like(full.y)
+            flat = full.route.idx.reshape(-1)
+            for a in np.nonzero(r.inv_pos < 0)[0]:
+                t, j = divmod(int(a), c["k"])
+                e = int(flat[a])
+                Y = ref.expert_ffn(c["x"][t:t + 1], c["w_in"][e], None if c["b_in"] is None else c["b_in"][e],
+                                   c["w_out"][e], None if c["b_out"] is None else c["b_out"][e], c["act"])
+                lost[t] += full.route.gates[t, j] * Y[0]
+            _close(full.y - r.y, lost, 1e-10, f"dropped contribution seed {s} cap {cap}")
+
+
+def check_capacity_formula(ref):
+    """ceil(c * T * k / E): a factor of 1 gives exactly the uniform load when it divides."""
+    assert ref.capacity_rows(4096, 2, 16, 1.0) == 512
+    assert ref.capacity_rows(4096, 2, 16, 1.25) == 640
+    assert ref.capacity_rows(8192, 2, 8, 1.0) == 2048
+    assert ref.capacity_rows(10, 1, 3, 1.0) == 4  # 10/3 rounded up
+    assert ref.capacity_rows(64, 8, 128, 1.5) == 6
+
+
+def check_bias_update(ref):
+    """Sign rule of the dynamic-bias router, against the pages' float formulation
+    (bias - rate * sign(counts - T*k/E), evaluated here with Python floats rounded to float32)."""
+    import struct
+
+    def f32(v):
+        return struct.unpack("f", struct.pack("f", v))[0]
+
+    gamma = 0.001
+    rng = np.random.default_rng(7)
+    for T, k, E in ((6, 2, 4), (10, 1, 3), (4096, 8, 256), (64, 2, 8)):
+        counts = rng.multinomial(T * k, np.ones(E) / E)
+        if T == 6:
+            counts = np.array([5, 3, 1, 3])  # target 3: one over, two at, one under
+        bias = (rng.integers(-50, 51, E) * gamma).astype(np.float32)
+        got = ref.update_bias(bias, counts, T, k, gamma)
+        for e in range(E):
+            err = float(counts[e]) - (T * k) / E
+            sgn = (err > 0) - (err < 0)
+            want = f32(float(bias[e]) - f32(gamma) * sgn)
+            assert got[e] == np.float32(want), (T, k, E, e, got[e], want)
+        if T == 6:
+            assert got[0] < bias[0] and got[1] == bias[1] and got[2] > bias[2] and got[3] == bias[3]
+    # repeated steps stay on the gamma grid (up to float32 rounding)
+    b = np.zeros(5, dtype=np.float32)
+    for it in range(40):  # T*k/E = 4: one expert over, two under, two exactly at the target
+        b = ref.update_bias(b, np.array([9, 1, 2, 4, 4]), 10, 2, gamma)
+    assert np.allclose(b, np.array([-40, 40, 40, 0, 0]) * gamma, atol=1e-6), b
+
+
 ALL_CHECKS = [
     ("brute", lambda ref, pv: check_against_brute(ref)),
     ("permute_brute", lambda ref, pv: check_permute_brute(ref)),
@@ -310,4 +392,8 @@ ALL_CHECKS = [
     ("relabel_token_order", lambda ref, pv: check_relabel_and_token_order(ref)),
     ("bias_split", lambda ref, pv: check_bias_split(ref)),
     ("ambiguity", lambda ref, pv: check_ambiguity(ref)),
+    ("capacity_brute", lambda ref, pv: check_capacity_brute(ref)),
+    ("capacity_limits", lambda ref, pv: check_capacity_limits(ref)),
+    ("capacity_formula", lambda ref, pv: check_capacity_formula(ref)),
+    ("bias_update", lambda ref, pv: check_bias_update(ref)),
 ]

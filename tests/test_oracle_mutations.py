@@ -81,16 +81,17 @@ def _gelu_tanh(z):
 def _mut_permute_descending(m):
     orig = m.permute
 
-    def permute(idx, E):
+    def permute(idx, E, capacity=0):
         T, k = idx.shape
-        offsets, st, inv = orig(idx, E)
+        offsets, st, inv = orig(idx, E, capacity)
         st2, inv2 = st.copy(), inv.copy()
         for e in range(E):
             r0, r1 = offsets[e], offsets[e + 1]
             st2[r0:r1] = st[r0:r1][::-1]
         for a in range(T * k):
             e = idx.reshape(-1)[a]
-            inv2[a] = offsets[e] + offsets[e + 1] - 1 - (inv[a] - offsets[e]) - offsets[e]
+            if inv[a] >= 0:
+                inv2[a] = offsets[e] + offsets[e + 1] - 1 - (inv[a] - offsets[e]) - offsets[e]
         return offsets, st2, inv2
     return permute
 
@@ -98,8 +99,8 @@ def _mut_permute_descending(m):
 def _mut_inclusive_offsets(m):
     orig = m.permute
 
-    def permute(idx, E):
-        offsets, st, inv = orig(idx, E)
+    def permute(idx, E, capacity=0):
+        offsets, st, inv = orig(idx, E, capacity)
         counts = np.bincount(idx.ravel(), minlength=E)
         off2 = offsets.copy()
         off2[:E] = offsets[:E] + counts  # inclusive instead of exclusive
@@ -162,6 +163,63 @@ def _mut_router_transposed_bias(m):
     return key
 
 
+def _mut_capacity_keeps_last(m):
+    """Keeps the last C assignments of an overloaded expert instead of the first C."""
+    def permute(idx, E, capacity=0):
+        if capacity <= 0:
+            return m.__dict__["_orig_permute"](idx, E, 0)
+        T, k = idx.shape
+        rev = idx[::-1, ::-1].copy()
+        off, st, inv = m.__dict__["_orig_permute"](rev, E, capacity)
+        inv2 = inv[::-1].copy()
+        # rows of each expert back in ascending token order
+        st2 = st.copy()
+        for e in range(E):
+            r0, r1 = off[e], off[e + 1]
+            st2[r0:r1] = (T - 1 - st[r0:r1])[::-1]
+        for a in range(T * k):
+            if inv2[a] >= 0:
+                e = idx.reshape(-1)[a]
+                inv2[a] = off[e] + off[e + 1] - 1 - (inv2[a] - off[e]) - off[e] + off[e]
+        return off, st2, inv2
+    return permute
+
+
+def _mut_capacity_off_by_one(m):
+    orig = m.permute
+    return lambda idx, E, capacity=0: orig(idx, E, capacity + 1 if capacity > 0 else 0)
+
+
+def _mut_capacity_renormalises(m):
+    """Renormalises the kept gates of a token whose assignment was dropped."""
+    orig = m.combine
+
+    def combine(y_perm, inv_pos, g, y_shared=None):
+        T, k = g.shape
+        pos = inv_pos.reshape(T, k)
+        g2 = np.where(pos >= 0, g, 0.0)
+        s = g2.sum(axis=1, keepdims=True)
+        g2 = np.where(s > 0, g2 / np.where(s > 0, s, 1.0) * g.sum(axis=1, keepdims=True), g2)
+        return orig(y_perm, inv_pos, g2, y_shared)
+    return combine
+
+
+def _mut_bias_sign_flipped(m):
+    orig = m.update_bias
+    return lambda bias, counts, T, k, gamma: orig(bias, counts, T, k, -gamma)
+
+
+def _mut_bias_target_per_token(m):
+    """Uniform load taken as T/E (tokens) instead of T*k/E (assignments)."""
+    orig = m.update_bias
+    return lambda bias, counts, T, k, gamma: orig(bias, counts, T, 1, gamma) if k > 1 else orig(bias, np.asarray(counts) + 1, T, k, gamma)
+
+
+def _install_keeps_last(m):
+    m._orig_permute = m.permute
+    m.permute = _mut_capacity_keeps_last(m)
+
+
 MUTANTS = {
     "ties_to_higher_index": lambda m: setattr(m, "topk", _ties_to_higher_index),
     "gates_full_softmax": lambda m: setattr(m, "gates", _mut_gates_full_softmax(m)),
@@ -181,6 +239,11 @@ MUTANTS = {
     "bias_inside_sigmoid": lambda m: setattr(m, "selection_key", _mut_router_transposed_bias(m)),
     "softmax_without_normalisation": lambda m: setattr(m, "softmax", lambda l: np.exp(l - l.max(axis=-1, keepdims=True))),
     "logits_sign_flipped": lambda m: setattr(m, "router_logits", lambda x, w: -(x @ w.T)),
+    "capacity_keeps_last": _install_keeps_last,
+    "capacity_off_by_one": lambda m: setattr(m, "permute", _mut_capacity_off_by_one(m)),
+    "capacity_renormalises_gates": lambda m: setattr(m, "combine", _mut_capacity_renormalises(m)),
+    "bias_update_sign_flipped": lambda m: setattr(m, "update_bias", _mut_bias_sign_flipped(m)),
+    "bias_target_per_token": lambda m: setattr(m, "update_bias", _mut_bias_target_per_token(m)),
 }
 
 
