@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--stage-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0: automatic)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="also time hipBLASLt (torch.mm) on the gate/up shape, dense and per expert, for context")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run two plain 1 GiB device copies (calibration for the HBM byte counters)")
     return ap.parse_args()
@@ -121,6 +123,7 @@ def main():
             b.record(stream)
             b.synchronize()
             times[name].append(a.elapsed_time(b))
+    next_rows = next_row_timings(cfg, L, flush, stream, args.stage_reps)
     del flush
     if args.copy_probe:  # a plain copy of known size: FETCH_SIZE and WRITE_SIZE should each read 1 GiB
         src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(3)
@@ -129,6 +132,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    vendor = vendor_gemm(cfg, L, stream) if args.vendor_gemm and cfg.dtype == "bf16" else None
     work = stage_bytes_flops(cfg)
     peak_tf = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_PEAK_TFLOPS
     stages = {}
@@ -180,9 +184,83 @@ def main():
         "route_GB/s": stages["route"]["GB/s"],
         "assignments_per_s": round(value * cfg.k, 1),
         "event_ms_per_step": round(ev_ms, 4),
+        "vendor_gemm": vendor,
+        "capacity_permute": next_rows["capacity_permute"],
+        "bias_update": next_rows["bias_update"],
         "input_gen_s": round(gen_s, 2),
     }
     print(json.dumps(out), flush=True)
+
+
+def next_row_timings(cfg, L, flush, stream, reps):
+    """Expert capacity (moe_permute with C = ceil(1.0 * T * k / E)) and the aux-loss-free bias step
+    (moe_update_bias) on the same layer, HIP events on the launch stream, caches flushed before each."""
+    import math
+
+    import numpy as np
+    import torch
+
+    from sparse_routing_expert_amd import _lib as LIB
+
+    T, k, E, d, b = cfg.T, cfg.k, cfg.E, cfg.d, cfg.elem_bytes
+    cap = int(math.ceil(1.0 * T * k / E))
+    shape_c = LIB.shape_of(cfg, T, cap)
+    ws = L.ws(LIB.MOE_STAGE_PERMUTE)
+    bias = L.t["sel_bias"].clone() if L.t["sel_bias"] is not None else torch.zeros(E, dtype=torch.float32,
+                                                                                  device=L.dev)
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps):
+            flush.fill_(1)
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            e.record(stream)
+            e.synchronize()
+            ts.append(a.elapsed_time(e))
+        return float(np.median(ts))
+
+    ms = timed(lambda: LIB.moe_permute(shape_c, L.topk_idx, L.t["x"], L.offsets, L.sorted_token, L.inv_pos,
+                                       L.x_perm, ws))
+    kept = int(L.offsets[-1].item())
+    A = T * k
+    nbytes = A * 4 + T * d * b + kept * d * b + 2 * A * 4 + (E + 1) * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    perm = {"capacity_rows": cap, "kept": kept, "dropped": A - kept, "ms": round(ms, 5), "bytes": nbytes,
+            "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    ms_b = timed(lambda: LIB.moe_update_bias(L.shape, L.counts, 1e-3, bias))
+    L.permute()  # back to the dropless permutation the other stages use
+    torch.cuda.synchronize()
+    return {"capacity_permute": perm,
+            "bias_update": {"ms": round(ms_b, 5), "bytes": E * 12, "note": "E-length, launch-bound"}}
+
+
+def vendor_gemm(cfg, L, stream):
+    """hipBLASLt through torch.mm on the gate/up product: all routed rows against one expert's
+    [2F, d] weights (a dense GEMM of the same total size), and one expert's share of the rows."""
+    import torch
+
+    A = L.x_perm
+    W = L.t["w_in"][0]
+    out = {}
+    for name, rows in (("dense_all_rows", A.shape[0]), ("one_expert_rows", A.shape[0] // cfg.E)):
+        a = A[:rows]
+        torch.mm(a, W.t())
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            torch.mm(a, W.t())
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[len(ts) // 2]
+        flops = 2.0 * rows * W.shape[0] * W.shape[1]
+        out[name] = {"m": rows, "n": W.shape[0], "k": W.shape[1], "ms": round(ms, 4),
+                     "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1)}
+    return out
 
 
 COPY_PROBE_BYTES = 1 << 30

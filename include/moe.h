@@ -89,7 +89,7 @@ enum {
     MOE_STAGE_EXPERT = 5 /* moe_expert_up / moe_expert_down */
 };
 
-/* Layer description (host memory). Limits: T >= 0; 1 <= E <= 1024; 1 <= k <= min(E, 32);
+/* Layer description (host memory). Limits: T >= 0; 1 <= E <= 1024; 1 <= k <= min(E, 32); capacity >= 0;
  * T*k <= 2^31-1; bf16: d_model, d_ff, d_ff_shared multiples of 64; f32: multiples of 4;
  * MOE_SIGMOID requires renorm = 1. Violations give MOE_ERR_INVALID_ARG or
  * MOE_ERR_UNSUPPORTED (multiples). */
@@ -104,6 +104,7 @@ typedef struct {
     int32_t score;       /* MOE_SOFTMAX | MOE_SIGMOID */
     int32_t renorm;      /* 1: gates renormalised over the selected k; 0: raw softmax probabilities */
     int32_t d_ff_shared; /* shared SwiGLU expert intermediate size; 0 = no shared expert */
+    int32_t capacity;    /* rows each expert may take (moe_permute); 0 = unlimited (dropless) */
 } moe_shape;
 
 typedef void* moe_stream_t; /* a hipStream_t */
@@ -150,13 +151,19 @@ int moe_route(const moe_shape* shape, const void* x, const float* w_router, cons
  *   topk_idx     [T, k]        int32  in: experts per token (each in [0, E); a token's k experts
  *                                     distinct, as moe_route produces; other values: undefined)
  *   x            [T, d_model]  dtype  in: token activations
- *   offsets      [E + 1]       int32  out: exclusive prefix sum of the expert histogram;
- *                                     offsets[E] = T*k
- *   sorted_token [T*k]         int32  out: row p of x_perm holds token sorted_token[p]
- *   inv_pos      [T*k]         int32  out: assignment (t, j) sits at row inv_pos[t*k + j]
- *   x_perm       [T*k, d_model] dtype out: x_perm[p] = x[sorted_token[p]]
- * Within an expert's segment rows are ordered by ascending t*k + j. Integer outputs are exact
- * and deterministic. Workspace: MOE_STAGE_PERMUTE. */
+ *   offsets      [E + 1]       int32  out: exclusive prefix sum of the rows each expert keeps;
+ *                                     offsets[E] = T*k when dropless
+ *   sorted_token [T*k]         int32  out: row p < offsets[E] of x_perm holds token sorted_token[p]
+ *   inv_pos      [T*k]         int32  out: assignment (t, j) sits at row inv_pos[t*k + j], or -1
+ *                                     when it was dropped
+ *   x_perm       [T*k, d_model] dtype out: x_perm[p] = x[sorted_token[p]] for p < offsets[E]
+ * Within an expert's segment rows are ordered by ascending t*k + j. Expert capacity
+ * (shape->capacity = C > 0; "Router Optimization Techniques", Why It Matters 3 and FAQ 6, with
+ * C = ceil(capacity factor * T * k / E); "Mixture of Experts" tutorial, The capacity factor
+ * formula): an expert keeps only the first C of its assignments in that order; the others get
+ * inv_pos = -1 and no row, and contribute nothing to the layer output (they reach the next layer
+ * through the residual connection, outside this layer). Rows p >= offsets[E] are untouched.
+ * Integer outputs are exact and deterministic. Workspace: MOE_STAGE_PERMUTE. */
 int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, int32_t* offsets,
                 int32_t* sorted_token, int32_t* inv_pos, void* x_perm, void* ws, size_t ws_bytes,
                 moe_stream_t stream);
@@ -229,7 +236,8 @@ int moe_shared_ffn(const moe_shape* shape, const void* x, const void* ws_in, con
  * index_add of gate-scaled expert outputs.
  *
  *   y_perm   [T*k, d_model] dtype        in
- *   inv_pos  [T*k]          int32        in: moe_permute's inverse permutation
+ *   inv_pos  [T*k]          int32        in: moe_permute's inverse permutation (-1: dropped by
+ *                                        capacity; that slot contributes nothing)
  *   topk_w   [T, k]         fp32         in: gates
  *   y_shared [T, d_model]   dtype or NULL in: shared-expert output, added with gate 1
  *   y        [T, d_model]   dtype        out: y[t] = sum_j topk_w[t,j] y_perm[inv_pos[t*k+j]]
@@ -238,6 +246,21 @@ int moe_shared_ffn(const moe_shape* shape, const void* x, const void* ws_in, con
  * Needs no workspace. */
 int moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* inv_pos, const float* topk_w,
                 const void* y_shared, void* y, moe_stream_t stream);
+
+/* moe_update_bias -- one step of auxiliary-loss-free load balancing on the selection bias.
+ *
+ * Defined by: "Router Optimization Techniques", How It Works 2 and Fine-Tuning Strategies 1 (the
+ * dynamic-bias router): the uniform load is T*k/E assignments per expert; an expert above it
+ * lowers its bias by gamma, one below raises it by gamma, one exactly at it keeps it:
+ *   sel_bias[e] <- sel_bias[e] - gamma * sign(counts[e] - T*k/E)
+ * The comparison is exact (counts[e] * E against T * k in 64-bit integers); the step is one fp32
+ * subtraction.
+ *   counts   [E]  int32  in: assignments per expert (moe_route's counts)
+ *   sel_bias [E]  fp32   in/out: the bias moe_route adds to the selection key
+ *   gamma         fp32   step (the pages use 0.001); must be finite
+ * Needs no workspace. */
+int moe_update_bias(const moe_shape* shape, const int32_t* counts, float gamma, float* sel_bias,
+                    moe_stream_t stream);
 
 /* moe_forward -- route, permute, grouped FFN, shared expert and combine on one stream.
  *

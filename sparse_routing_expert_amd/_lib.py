@@ -35,7 +35,8 @@ class MoeError(RuntimeError):
 class moe_shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("dtype", ctypes.c_int32), ("act", ctypes.c_int32),
-                ("score", ctypes.c_int32), ("renorm", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32)]
+                ("score", ctypes.c_int32), ("renorm", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32),
+                ("capacity", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -53,6 +54,7 @@ _SIGS = {
     "moe_combine": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P]),
     "moe_forward": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    _P, ctypes.c_size_t, _P]),
+    "moe_update_bias": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, ctypes.c_float, _P, _P]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
 }
 EXPORTED = tuple(_SIGS)
@@ -83,17 +85,18 @@ def status_name(status: int) -> str:
 
 
 def make_shape(T, d_model, d_ff, E, k, dtype="bf16", act="swiglu", score="softmax", renorm=True,
-               d_ff_shared=0) -> moe_shape:
+               d_ff_shared=0, capacity=0) -> moe_shape:
     return moe_shape(int(T), int(d_model), int(d_ff), int(E), int(k),
                      MOE_BF16 if dtype == "bf16" else MOE_F32,
                      MOE_SWIGLU if act == "swiglu" else MOE_GELU_MLP,
-                     MOE_SIGMOID if score == "sigmoid" else MOE_SOFTMAX, int(bool(renorm)), int(d_ff_shared))
+                     MOE_SIGMOID if score == "sigmoid" else MOE_SOFTMAX, int(bool(renorm)), int(d_ff_shared),
+                     int(capacity))
 
 
-def shape_of(cfg, T: Optional[int] = None) -> moe_shape:
-    """moe_shape of an inputs.LayerConfig (optionally with another token count)."""
+def shape_of(cfg, T: Optional[int] = None, capacity: int = 0) -> moe_shape:
+    """moe_shape of an inputs.LayerConfig (optionally with another token count or an expert capacity)."""
     return make_shape(cfg.T if T is None else T, cfg.d, cfg.F, cfg.E, cfg.k, cfg.dtype, cfg.act, cfg.score,
-                      cfg.renorm, cfg.Fs)
+                      cfg.renorm, cfg.Fs, capacity)
 
 
 def _ptr(t) -> Optional[int]:
@@ -177,3 +180,8 @@ def moe_forward(shape, x, w_router, sel_bias, w_in, b_in, w_out, b_out, ws_in, w
                                             _ptr(b_in), _ptr(w_out), _ptr(b_out), _ptr(ws_in), _ptr(ws_out), _ptr(y),
                                             _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(counts_out), _ptr(stats_out),
                                             _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_update_bias(shape, counts, gamma: float, sel_bias, stream=None) -> None:
+    _check("moe_update_bias", lib().moe_update_bias(ctypes.byref(shape), _ptr(counts), float(gamma), _ptr(sel_bias),
+                                                    _stream(stream)))

@@ -37,17 +37,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint8_t* __restrict_
             for (int i = 0; i < EPV; ++i) acc[u][i] = 0.f;
         u32x4 cur[U], nxt[U];
         {
-            const uint8_t* row = y_perm + (int64_t)__builtin_amdgcn_readlane(mypos, 0) * row_bytes;
+            const int p = __builtin_amdgcn_readlane(mypos, 0);
+            const uint8_t* row = y_perm + (int64_t)(p < 0 ? 0 : p) * row_bytes;
 #pragma unroll
-            for (int u = 0; u < U; ++u) cur[u] = c0 + 64 * u < nvec ? ld16(row + (int64_t)(c0 + 64 * u) * 16) : zero;
+            for (int u = 0; u < U; ++u)
+                cur[u] = p >= 0 && c0 + 64 * u < nvec ? ld16(row + (int64_t)(c0 + 64 * u) * 16) : zero;
         }
         for (int j = 0; j < k; ++j) {
             if (j + 1 < k) {
-                const uint8_t* row = y_perm + (int64_t)__builtin_amdgcn_readlane(mypos, j + 1) * row_bytes;
+                const int p = __builtin_amdgcn_readlane(mypos, j + 1);
+                const uint8_t* row = y_perm + (int64_t)(p < 0 ? 0 : p) * row_bytes;
 #pragma unroll
                 for (int u = 0; u < U; ++u)
-                    nxt[u] = c0 + 64 * u < nvec ? ld16(row + (int64_t)(c0 + 64 * u) * 16) : zero;
+                    nxt[u] = p >= 0 && c0 + 64 * u < nvec ? ld16(row + (int64_t)(c0 + 64 * u) * 16) : zero;
             }
+            // a slot dropped by expert capacity (row -1) adds nothing
+            const bool kept = __builtin_amdgcn_readlane(mypos, j) >= 0;
             const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(myg), j));
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -56,8 +61,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint8_t* __restrict_
                 else
 #pragma unroll
                     for (int i = 0; i < EPV; ++i) f[i] = __uint_as_float(cur[u][i]);
+                if (kept)
 #pragma unroll
-                for (int i = 0; i < EPV; ++i) acc[u][i] = fmaf(g, f[i], acc[u][i]);
+                    for (int i = 0; i < EPV; ++i) acc[u][i] = fmaf(g, f[i], acc[u][i]);
                 cur[u] = nxt[u];
             }
         }

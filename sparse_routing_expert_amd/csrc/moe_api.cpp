@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <cmath>
 #include <cstdint>
 
 #include "../../include/moe.h"
@@ -27,6 +28,7 @@ int check_shape(const moe_shape* s) {
     if (s->act != MOE_GELU_MLP && s->act != MOE_SWIGLU) return MOE_ERR_INVALID_ARG;
     if (s->score != MOE_SOFTMAX && s->score != MOE_SIGMOID) return MOE_ERR_INVALID_ARG;
     if (s->renorm != 0 && s->renorm != 1) return MOE_ERR_INVALID_ARG;
+    if (s->capacity < 0) return MOE_ERR_INVALID_ARG;
     if (s->T * (int64_t)s->k > (int64_t)INT32_MAX) return MOE_ERR_INVALID_ARG;
     if (s->score == MOE_SIGMOID && s->renorm != 1) return MOE_ERR_UNSUPPORTED;
     const int mult = s->dtype == MOE_BF16 ? 64 : 4;
@@ -171,9 +173,10 @@ void do_permute(const moe_shape* s, const int32_t* topk_idx, const void* x, int3
     const PermWs w = perm_ws(s);
     const int64_t A = s->T * s->k;
     moe::launch_perm_count(topk_idx, A, s->E, at<int32_t>(ws, w.tile_counts), st);
-    moe::launch_perm_scan(at<int32_t>(ws, w.tile_counts), w.ntiles, A, s->E, at<int32_t>(ws, w.tile_base), offsets,
-                          st);
-    moe::launch_perm_rank(topk_idx, at<int32_t>(ws, w.tile_base), A, s->E, s->k, inv_pos, sorted_token, st);
+    moe::launch_perm_scan(at<int32_t>(ws, w.tile_counts), w.ntiles, A, s->E, s->capacity, at<int32_t>(ws, w.tile_base),
+                          offsets, st);
+    moe::launch_perm_rank(topk_idx, at<int32_t>(ws, w.tile_base), offsets, A, s->E, s->k, s->capacity, inv_pos,
+                          sorted_token, st);
     moe::launch_perm_scatter(x, inv_pos, s->T, s->d_model, s->k, elem_bytes(s), x_perm, st);
 }
 
@@ -350,6 +353,17 @@ int moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* inv_p
     (void)hipGetLastError();
     moe::launch_combine(shape->dtype, y_perm, inv_pos, topk_w, y_shared, y, shape->T, shape->d_model, shape->k,
                         static_cast<hipStream_t>(stream));
+    return launched();
+}
+
+int moe_update_bias(const moe_shape* shape, const int32_t* counts, float gamma, float* sel_bias,
+                    moe_stream_t stream) {
+    const int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    MOE_REQUIRE(ok_ptr(counts) && ok_ptr(sel_bias) && std::isfinite(gamma));
+    (void)hipGetLastError();
+    moe::launch_route_bias_update(counts, shape->T, shape->E, shape->k, gamma, sel_bias,
+                                  static_cast<hipStream_t>(stream));
     return launched();
 }
 

@@ -25,14 +25,19 @@ void launch_route_finalize(const int32_t* blk_counts, const float* blk_P, const 
                            int E, int32_t* counts, double* fp_scratch, int32_t* ticket, float* stats,
                            hipStream_t s);
 
+// sel_bias[e] -= gamma * sign(counts[e] * E - T * k)
+void launch_route_bias_update(const int32_t* counts, int64_t T, int E, int k, float gamma, float* sel_bias,
+                              hipStream_t s);
+
 // ---- permute ----------------------------------------------------------------------------
 constexpr int kPermTile = 1024;  // assignments per histogram / rank tile
 
 void launch_perm_count(const int32_t* topk_idx, int64_t A, int E, int32_t* tile_counts, hipStream_t s);
-void launch_perm_scan(const int32_t* tile_counts, int ntiles, int64_t A, int E, int32_t* tile_base,
+// capacity: rows each expert keeps (0 = all); dropped assignments get inv_pos = -1
+void launch_perm_scan(const int32_t* tile_counts, int ntiles, int64_t A, int E, int capacity, int32_t* tile_base,
                       int32_t* offsets, hipStream_t s);
-void launch_perm_rank(const int32_t* topk_idx, const int32_t* tile_base, int64_t A, int E, int k,
-                      int32_t* inv_pos, int32_t* sorted_token, hipStream_t s);
+void launch_perm_rank(const int32_t* topk_idx, const int32_t* tile_base, const int32_t* offsets, int64_t A, int E,
+                      int k, int capacity, int32_t* inv_pos, int32_t* sorted_token, hipStream_t s);
 void launch_perm_scatter(const void* x, const int32_t* inv_pos, int64_t T, int d, int k, int elem_bytes,
                          void* x_perm, hipStream_t s);
 

@@ -5,9 +5,10 @@
 //
 // Assignments a = t*k + j are cut into tiles of kPermTile. perm_count builds one LDS-atomic
 // histogram per tile (integer atomics: exact and order-independent); perm_scan turns the
-// [tile][expert] counts into expert offsets and per-tile bases; perm_rank ranks every
-// assignment inside its tile with wave ballots (stable, no atomics); perm_scatter reads each token
-// row once and writes its k copies with 128-bit stores.
+// [tile][expert] counts into expert offsets and per-tile rank bases; perm_rank ranks every
+// assignment inside its tile with wave ballots (stable, no atomics) and, with an expert capacity,
+// drops the ones ranked at or past it ("Router Optimization Techniques", Why It Matters 3 and
+// FAQ 6); perm_scatter reads each token row once and writes its kept copies with 128-bit stores.
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -28,20 +29,23 @@ __global__ __launch_bounds__(256) void perm_count_kernel(const int32_t* __restri
     for (int e = threadIdx.x; e < E; e += 256) tile_counts[(int64_t)blockIdx.x * E + e] = h[e];
 }
 
-// One block of 1024 threads; thread e owns expert e (E <= 1024).
+// One block of 1024 threads; thread e owns expert e (E <= 1024). offsets = exclusive scan of the
+// rows each expert keeps (min(count, capacity) with a capacity); tile_base[tile][e] = how many
+// assignments to e the earlier tiles hold (the expert-local rank of the tile's first one).
 __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restrict__ tile_counts, int ntiles,
-                                                         int E, int32_t* __restrict__ tile_base,
+                                                         int E, int capacity, int32_t* __restrict__ tile_base,
                                                          int32_t* __restrict__ offsets) {
     __shared__ int s_wave[17];
     const int e = threadIdx.x;
     int tot = 0;
     if (e < E)
         for (int tile = 0; tile < ntiles; ++tile) tot += tile_counts[(int64_t)tile * E + e];
+    const int kept = capacity > 0 && tot > capacity ? capacity : tot;
     int total;
-    const int start = block1024_excl_scan(tot, s_wave, &total);
+    const int start = block1024_excl_scan(kept, s_wave, &total);
     if (e < E) {
         offsets[e] = start;
-        int run = start;
+        int run = 0;
         for (int tile = 0; tile < ntiles; ++tile) {
             tile_base[(int64_t)tile * E + e] = run;
             run += tile_counts[(int64_t)tile * E + e];
@@ -53,11 +57,14 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restri
 // Stable rank of each assignment within its tile. The tile is processed as 16 chunks of 64
 // consecutive assignments (chunk c = iteration * 4 + wave). Inside a chunk, lanes holding the
 // same expert are found by intersecting ballots over the bits of the expert id; the lane's rank
-// among them is the popcount below it. Chunk counts go to LDS, so
-// position = tile_base[e] + sum of counts of e in earlier chunks + rank.
+// among them is the popcount below it. Chunk counts go to LDS, so the expert-local rank is
+// tile_base[e] + sum of counts of e in earlier chunks + rank, and the row is offsets[e] + that
+// rank -- unless a capacity is set and the rank reaches it: then the assignment is dropped.
 __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restrict__ idx,
-                                                        const int32_t* __restrict__ tile_base, int64_t A,
-                                                        int E, int k, int nbits, int32_t* __restrict__ inv_pos,
+                                                        const int32_t* __restrict__ tile_base,
+                                                        const int32_t* __restrict__ offsets, int64_t A,
+                                                        int E, int k, int nbits, int capacity,
+                                                        int32_t* __restrict__ inv_pos,
                                                         int32_t* __restrict__ sorted_token) {
     constexpr int ITERS = kPermTile / 256;
     constexpr int CHUNKS = kPermTile / 64;
@@ -91,15 +98,21 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restric
         if (a >= A) continue;
         const int e = ev[it];
         const int c = it * 4 + wave;
-        int pos = tile_base[(int64_t)blockIdx.x * E + e] + rank[it];
-        for (int c2 = 0; c2 < c; ++c2) pos += cnt[c2 * E + e];
+        int r = tile_base[(int64_t)blockIdx.x * E + e] + rank[it];
+        for (int c2 = 0; c2 < c; ++c2) r += cnt[c2 * E + e];
+        if (capacity > 0 && r >= capacity) {
+            inv_pos[a] = -1;
+            continue;
+        }
+        const int pos = offsets[e] + r;
         inv_pos[a] = pos;
         sorted_token[pos] = (int32_t)(a / k);
     }
 }
 
 // One wave per token: read the row once, store it at its k destinations (16-byte vectors, up to
-// 8 per lane loaded before any store so a row is one memory round trip).
+// 8 per lane loaded before any store so a row is one memory round trip); dropped slots (-1) are
+// skipped.
 __global__ __launch_bounds__(256) void perm_scatter_kernel(const uint8_t* __restrict__ x,
                                                            const int32_t* __restrict__ inv_pos, int64_t T,
                                                            int row_bytes, int k, uint8_t* __restrict__ x_perm) {
@@ -116,7 +129,9 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const uint8_t* __rest
         for (int u = 0; u < U; ++u)
             if (c0 + 64 * u < nchunks) v[u] = ld16(src + (int64_t)(c0 + 64 * u) * 16);
         for (int j = 0; j < k; ++j) {
-            uint8_t* dst = x_perm + (int64_t)__builtin_amdgcn_readlane(mypos, j) * row_bytes;
+            const int p = __builtin_amdgcn_readlane(mypos, j);
+            if (p < 0) continue;
+            uint8_t* dst = x_perm + (int64_t)p * row_bytes;
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 if (c0 + 64 * u < nchunks) st16(dst + (int64_t)(c0 + 64 * u) * 16, v[u]);
@@ -129,19 +144,20 @@ void launch_perm_count(const int32_t* topk_idx, int64_t A, int E, int32_t* tile_
     perm_count_kernel<<<ntiles, 256, 0, s>>>(topk_idx, A, E, tile_counts);
 }
 
-void launch_perm_scan(const int32_t* tile_counts, int ntiles, int64_t A, int E, int32_t* tile_base,
+void launch_perm_scan(const int32_t* tile_counts, int ntiles, int64_t A, int E, int capacity, int32_t* tile_base,
                       int32_t* offsets, hipStream_t s) {
     (void)A;
-    perm_scan_kernel<<<1, 1024, 0, s>>>(tile_counts, ntiles, E, tile_base, offsets);
+    perm_scan_kernel<<<1, 1024, 0, s>>>(tile_counts, ntiles, E, capacity, tile_base, offsets);
 }
 
-void launch_perm_rank(const int32_t* topk_idx, const int32_t* tile_base, int64_t A, int E, int k,
-                      int32_t* inv_pos, int32_t* sorted_token, hipStream_t s) {
+void launch_perm_rank(const int32_t* topk_idx, const int32_t* tile_base, const int32_t* offsets, int64_t A, int E,
+                      int k, int capacity, int32_t* inv_pos, int32_t* sorted_token, hipStream_t s) {
     const unsigned ntiles = (unsigned)((A + kPermTile - 1) / kPermTile);
     int nbits = 0;
     while ((1 << nbits) <= E) ++nbits;  // ids 0..E (E = padding sentinel) fit in nbits bits
     const size_t lds = (size_t)(kPermTile / 64) * E * sizeof(int);
-    perm_rank_kernel<<<ntiles, 256, lds, s>>>(topk_idx, tile_base, A, E, k, nbits, inv_pos, sorted_token);
+    perm_rank_kernel<<<ntiles, 256, lds, s>>>(topk_idx, tile_base, offsets, A, E, k, nbits, capacity, inv_pos,
+                                              sorted_token);
 }
 
 void launch_perm_scatter(const void* x, const int32_t* inv_pos, int64_t T, int d, int k, int elem_bytes,

@@ -374,6 +374,24 @@ __global__ __launch_bounds__(256) void route_finalize_kernel(const int32_t* __re
     }
 }
 
+// Aux-loss-free balancing step ("Router Optimization Techniques", How It Works 2 and Fine-Tuning
+// Strategies 1): sel_bias[e] -= gamma * sign(counts[e] - T*k/E), the sign taken exactly in
+// integers and the step as one fp32 subtraction.
+__global__ __launch_bounds__(256) void route_bias_update_kernel(const int32_t* __restrict__ counts, int64_t T,
+                                                                int E, int k, float gamma,
+                                                                float* __restrict__ sel_bias) {
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= E) return;
+    const int64_t diff = (int64_t)counts[e] * E - T * k;
+    const float step = diff > 0 ? gamma : (diff < 0 ? -gamma : 0.0f);
+    sel_bias[e] = sel_bias[e] - step;
+}
+
+void launch_route_bias_update(const int32_t* counts, int64_t T, int E, int k, float gamma, float* sel_bias,
+                              hipStream_t s) {
+    route_bias_update_kernel<<<(unsigned)((E + 255) / 256), 256, 0, s>>>(counts, T, E, k, gamma, sel_bias);
+}
+
 void launch_route_prep(const float* w_router, int E, int Epad, int d, uint16_t* wsplit, int32_t* ticket,
                        hipStream_t s) {
     const int64_t n = wsplit ? (int64_t)Epad * d : 0;

@@ -16,10 +16,12 @@ from . import _lib as L
 class MoeLayer:
     """Holds a layer's weights (device tensors) and preallocated outputs/workspaces."""
 
-    def __init__(self, cfg, tensors: Dict[str, Optional[torch.Tensor]], device="cuda", T: Optional[int] = None):
+    def __init__(self, cfg, tensors: Dict[str, Optional[torch.Tensor]], device="cuda", T: Optional[int] = None,
+                 capacity: int = 0):
         self.cfg = cfg
         self.T = cfg.T if T is None else T
-        self.shape = L.shape_of(cfg, self.T)
+        self.capacity = capacity  # rows per expert kept by permute (0: dropless)
+        self.shape = L.shape_of(cfg, self.T, capacity)
         self.dev = torch.device(device)
         self.t = {k: (v.to(self.dev) if v is not None else None) for k, v in tensors.items()}
         T_, k, E, d = self.T, cfg.k, cfg.E, cfg.d
@@ -100,3 +102,7 @@ class MoeLayer:
                       self.counts if with_routing else None, self.stats if with_routing else None,
                       self.ws(L.MOE_STAGE_FORWARD))
         return self.y if out is None else out
+
+    def update_bias(self, gamma: float = 1e-3, counts=None):
+        """One aux-loss-free balancing step on the layer's selection bias (in place)."""
+        L.moe_update_bias(self.shape, self.counts if counts is None else counts, gamma, self.t["sel_bias"])

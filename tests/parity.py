@@ -86,13 +86,16 @@ def check_route(cfg, L, ref: "R.RouteResult", logits=True):
 
 
 def check_permute(cfg, L, x_host64):
-    """GPU permutation of the GPU's own selection vs the oracle's permutation of it (bit-exact)."""
+    """GPU permutation of the GPU's own selection vs the oracle's permutation of it (bit-exact),
+    with the layer's expert capacity (rows past offsets[E] are not compared)."""
     idx = L.topk_idx.cpu().numpy().astype(np.int64)
-    off, st, inv = R.permute(idx, cfg.E)
+    cap = getattr(L, "capacity", 0)
+    off, st, inv = R.permute(idx, cfg.E, cap)
+    n = int(off[-1])
     assert (L.offsets.cpu().numpy() == off).all(), "offsets"
-    assert (L.sorted_token.cpu().numpy() == st).all(), "sorted_token"
+    assert (L.sorted_token.cpu().numpy()[:n] == st).all(), "sorted_token"
     assert (L.inv_pos.cpu().numpy() == inv).all(), "inv_pos"
-    xp = L.x_perm.cpu()
+    xp = L.x_perm.cpu()[:n]
     want = L.t["x"].cpu()[torch.from_numpy(st)]
     assert torch.equal(xp.view(torch.int16) if xp.dtype == torch.bfloat16 else xp.view(torch.int32),
                        want.view(torch.int16) if want.dtype == torch.bfloat16 else want.view(torch.int32)), "x_perm"
@@ -106,7 +109,7 @@ def get_expert_fn(L):
 
 def check_ffn(cfg, L, off, x_perm64, e_range=None):
     y_ref = R.experts_on_rows(x_perm64, off, get_expert_fn(L), cfg.act, e_range)
-    y = np64(L.y_perm)
+    y = np64(L.y_perm)[:y_ref.shape[0]]  # with a capacity only the kept rows exist
     rows = ~np.isnan(y_ref[:, 0])
     if rows.any():
         err = R.rel_l2_per_row(y[rows], y_ref[rows])
@@ -121,7 +124,7 @@ def oracle_layer_on_gpu_routing(cfg, L):
     idx = L.topk_idx.cpu().numpy().astype(np.int64)
     return R.layer_forward(t["x"], np64(t["w_r"]), get_expert_fn(L), cfg.k, cfg.act, cfg.score, cfg.renorm,
                            None if t["sel_bias"] is None else np64(t["sel_bias"]), t["ws_in"], t["ws_out"],
-                           forced_idx=idx)
+                           forced_idx=idx, capacity=getattr(L, "capacity", 0))
 
 
 def check_layer(cfg, y_gpu, y_ref):

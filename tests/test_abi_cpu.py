@@ -103,6 +103,20 @@ def test_workspace_sizes_monotone(lib):
     assert rc == 0 and n == 0
 
 
+def test_capacity_and_bias_rejections(lib):
+    s = good_shape(capacity=-1)
+    assert ws_bytes(s, L.MOE_STAGE_PERMUTE)[0] == L.MOE_ERR_INVALID_ARG
+    ok = good_shape(capacity=64)
+    assert ws_bytes(ok, L.MOE_STAGE_PERMUTE)[0] == L.MOE_OK
+    ub = lib.moe_update_bias
+    assert ub(ctypes.byref(ok), None, 1e-3, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert ub(ctypes.byref(ok), FAKE, 1e-3, None, None) == L.MOE_ERR_INVALID_ARG
+    assert ub(ctypes.byref(ok), FAKE, 1e-3, MISALIGNED, None) == L.MOE_ERR_INVALID_ARG
+    assert ub(ctypes.byref(ok), FAKE, float("nan"), FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert ub(ctypes.byref(ok), FAKE, float("inf"), FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert ub(ctypes.byref(good_shape(capacity=-5)), FAKE, 1e-3, FAKE, None) == L.MOE_ERR_INVALID_ARG
+
+
 def test_route_rejections(lib):
     s = good_shape()
     r = lib.moe_route
