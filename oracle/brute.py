@@ -229,3 +229,21 @@ def layer_capacity(x: Mat, w_r: Mat, w_in, b_in, w_out, b_out, k: int, act: str,
         ys.append(acc)
     return [c for _, c in choices], ys
 
+
+def noisy_route(x: Mat, w_r: Mat, w_noise: Mat, noise: Mat, k: int, score: str = "softmax",
+                renorm: bool = True, sel_bias: Optional[Vec] = None):
+    """Noisy top-k by explicit sums: H_e = l_e + n_e * log(1 + exp(s_e)) with s = x . W_noise,
+    then the same exact-subset selection and masked gates as the plain router.
+    Returns (H [T][E], idx [T][k], gates [T][k])."""
+    Hs, idx, gts = [], [], []
+    for t, xt in enumerate(x):
+        l = logits(xt, w_r)
+        sn = logits(xt, w_noise)
+        H = [l[e] + noise[t][e] * math.log1p(math.exp(sn[e])) for e in range(len(l))]
+        chosen = select(key_of(H, score, sel_bias), k)
+        g_all = masked_gates(H, chosen, score, renorm)
+        Hs.append(H)
+        idx.append(chosen)
+        gts.append([g_all[e] for e in chosen])
+    return Hs, idx, gts
+

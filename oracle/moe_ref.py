@@ -46,7 +46,9 @@ reason in the design notes of the repository):
   * capacity: C = ceil(c * T * k / E) rows per expert; an expert keeps its first C
     assignments in (t, j) order; a dropped assignment contributes nothing (it reaches
     the next layer through the residual, outside this layer); kept gates unchanged;
-  * bias update: b_e <- b_e - gamma * sign(count_e - T*k/E), sign(0) = 0, in float32.
+  * bias update: b_e <- b_e - gamma * sign(count_e - T*k/E), sign(0) = 0, in float32;
+  * noisy top-k: H = x W_r^T + n * softplus(x W_noise^T) with caller-supplied noise n,
+    then H replaces the logits everywhere (key, gates, statistics).
 """
 from __future__ import annotations
 
@@ -191,15 +193,30 @@ class RouteResult:
     ambiguous: np.ndarray  # [T] bool
 
 
+def softplus(z: np.ndarray) -> np.ndarray:
+    """log(1 + e^z), evaluated as max(z, 0) + log1p(e^-|z|)."""
+    return np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+
+
+def noisy_logits(x: np.ndarray, w_r: np.ndarray, w_noise: np.ndarray, noise: np.ndarray) -> np.ndarray:
+    """Noisy top-k gating ([MT] Noisy top-k gating): the router logits plus Gaussian noise scaled
+    per token and expert by a second learned projection of x, H = x W_r^T + n * softplus(x W_noise^T).
+    The page names the recipe and its two parts but its formula was lost; the scale is kept
+    positive with softplus as in the published recipe. The noise n [T, E] is supplied by the
+    caller (it is the only randomness); every later step uses H as the logits."""
+    return router_logits(x, w_r) + f64(noise) * softplus(router_logits(x, f64(w_noise)))
+
+
 def route(x, w_r, k: int, score: str = "softmax", renorm: bool = True,
-          sel_bias: Optional[np.ndarray] = None) -> RouteResult:
-    """The routing stage: logits, key, top-k, gates, counts and load-balance statistics."""
+          sel_bias: Optional[np.ndarray] = None, w_noise=None, noise=None) -> RouteResult:
+    """The routing stage: logits, key, top-k, gates, counts and load-balance statistics. With
+    w_noise and noise, the logits are the noisy ones (noisy_logits)."""
     x, w_r = f64(x), f64(w_r)
     if sel_bias is not None:
         sel_bias = f64(sel_bias)
     assert np.all(np.isfinite(x)) and np.all(np.isfinite(w_r))
     E = w_r.shape[0]
-    l = router_logits(x, w_r)
+    l = router_logits(x, w_r) if w_noise is None else noisy_logits(x, w_r, w_noise, noise)
     key = selection_key(l, score, sel_bias)
     idx = topk(key, k)
     g = gates(l, idx, score, renorm)

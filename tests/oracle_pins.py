@@ -378,6 +378,42 @@ def check_bias_update(ref):
     assert np.allclose(b, np.array([-40, 40, 40, 0, 0]) * gamma, atol=1e-6), b
 
 
+# ------------------------------------------------------------------ noisy top-k
+
+
+def check_noisy_brute(ref, seeds=range(25)):
+    for s in seeds:
+        c = tiny_case(4000 + s)
+        rng = np.random.default_rng(4000 + s)
+        w_n = rng.standard_normal((c["E"], c["d"]))
+        n = rng.standard_normal((c["T"], c["E"]))
+        r = ref.route(c["x"], c["w_r"], c["k"], c["score"], c["renorm"], c["sel_bias"], w_n, n)
+        H, b_idx, b_g = brute.noisy_route(_L(c["x"]), _L(c["w_r"]), _L(w_n), _L(n), c["k"], c["score"], c["renorm"],
+                                          _L(c["sel_bias"]))
+        _close(r.logits, H, 1e-12, f"noisy logits seed {s}")
+        assert r.idx.tolist() == b_idx, s
+        _close(r.gates, b_g, 1e-12, f"noisy gates seed {s}")
+
+
+def check_noisy_limits(ref):
+    """Zero noise reduces to the plain router; softplus closed forms; noise can flip a choice."""
+    c = tiny_case(77, T=5, E=4, k=2, score="softmax")
+    rng = np.random.default_rng(77)
+    w_n = rng.standard_normal((4, c["d"]))
+    plain = ref.route(c["x"], c["w_r"], 2, "softmax", c["renorm"], c["sel_bias"])
+    quiet = ref.route(c["x"], c["w_r"], 2, "softmax", c["renorm"], c["sel_bias"], w_n, np.zeros((5, 4)))
+    assert np.array_equal(plain.logits, quiet.logits) and np.array_equal(plain.idx, quiet.idx)
+    assert abs(ref.softplus(np.array([0.0]))[0] - math.log(2.0)) < 1e-15
+    z = np.linspace(-30, 30, 61)
+    assert np.allclose(ref.softplus(z) - ref.softplus(-z), z, atol=1e-12, rtol=0)
+    # one token, two experts with equal logits; a positive draw on expert 1 must select it
+    x = np.array([[1.0, 0.0]])
+    w = np.array([[1.0, 0.0], [1.0, 0.0]])
+    wn = np.array([[0.0, 0.0], [0.0, 0.0]])  # softplus(0) = ln 2 scales both draws
+    r = ref.route(x, w, 1, "softmax", True, None, wn, np.array([[0.0, 0.5]]))
+    assert r.idx.tolist() == [[1]] and abs(r.logits[0, 1] - (1.0 + 0.5 * math.log(2.0))) < 1e-15
+
+
 ALL_CHECKS = [
     ("brute", lambda ref, pv: check_against_brute(ref)),
     ("permute_brute", lambda ref, pv: check_permute_brute(ref)),
@@ -396,4 +432,6 @@ ALL_CHECKS = [
     ("capacity_limits", lambda ref, pv: check_capacity_limits(ref)),
     ("capacity_formula", lambda ref, pv: check_capacity_formula(ref)),
     ("bias_update", lambda ref, pv: check_bias_update(ref)),
+    ("noisy_brute", lambda ref, pv: check_noisy_brute(ref)),
+    ("noisy_limits", lambda ref, pv: check_noisy_limits(ref)),
 ]

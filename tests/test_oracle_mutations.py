@@ -215,6 +215,15 @@ def _mut_bias_target_per_token(m):
     return lambda bias, counts, T, k, gamma: orig(bias, counts, T, 1, gamma) if k > 1 else orig(bias, np.asarray(counts) + 1, T, k, gamma)
 
 
+def _mut_noise_unscaled(m):
+    """Noise added without the learned softplus scale."""
+    return lambda x, w_r, w_noise, noise: m.router_logits(x, w_r) + m.f64(noise)
+
+
+def _mut_softplus_as_exp(m):
+    return lambda z: np.exp(z)
+
+
 def _install_keeps_last(m):
     m._orig_permute = m.permute
     m.permute = _mut_capacity_keeps_last(m)
@@ -244,6 +253,8 @@ MUTANTS = {
     "capacity_renormalises_gates": lambda m: setattr(m, "combine", _mut_capacity_renormalises(m)),
     "bias_update_sign_flipped": lambda m: setattr(m, "update_bias", _mut_bias_sign_flipped(m)),
     "bias_target_per_token": lambda m: setattr(m, "update_bias", _mut_bias_target_per_token(m)),
+    "noise_unscaled": lambda m: setattr(m, "noisy_logits", _mut_noise_unscaled(m)),
+    "softplus_as_exp": lambda m: setattr(m, "softplus", _mut_softplus_as_exp(m)),
 }
 
 
