@@ -187,6 +187,7 @@ def main():
         "vendor_gemm": vendor,
         "capacity_permute": next_rows["capacity_permute"],
         "bias_update": next_rows["bias_update"],
+        "noisy_route": next_rows["noisy_route"],
         "input_gen_s": round(gen_s, 2),
     }
     print(json.dumps(out), flush=True)
@@ -230,10 +231,18 @@ def next_row_timings(cfg, L, flush, stream, reps):
     perm = {"capacity_rows": cap, "kept": kept, "dropped": A - kept, "ms": round(ms, 5), "bytes": nbytes,
             "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
     ms_b = timed(lambda: LIB.moe_update_bias(L.shape, L.counts, 1e-3, bias))
-    L.permute()  # back to the dropless permutation the other stages use
+    # noisy top-k routing: x once, both fp32 projections, the noise, and the route outputs
+    from sparse_routing_expert_amd import inputs as I
+
+    w_n, noise = I.gen_noisy_router(cfg, device=L.dev)
+    ms_n = timed(lambda: L.route_noisy(w_n, noise, with_logits=False, with_stats=False))
+    nb = T * d * b + 2 * E * d * 4 + T * E * 4 + T * k * 8 + E * 4
+    L.route(with_logits=False)
+    L.permute()  # back to the plain routing and dropless permutation the other stages use
     torch.cuda.synchronize()
     return {"capacity_permute": perm,
-            "bias_update": {"ms": round(ms_b, 5), "bytes": E * 12, "note": "E-length, launch-bound"}}
+            "bias_update": {"ms": round(ms_b, 5), "bytes": E * 12, "note": "E-length, launch-bound"},
+            "noisy_route": {"ms": round(ms_n, 5), "bytes": nb, "GB/s": round(nb / (ms_n * 1e-3) / 1e9, 1)}}
 
 
 def vendor_gemm(cfg, L, stream):

@@ -86,7 +86,8 @@ enum {
     MOE_STAGE_FFN = 2,
     MOE_STAGE_SHARED = 3,
     MOE_STAGE_FORWARD = 4,
-    MOE_STAGE_EXPERT = 5 /* moe_expert_up / moe_expert_down */
+    MOE_STAGE_EXPERT = 5,      /* moe_expert_up / moe_expert_down */
+    MOE_STAGE_ROUTE_NOISY = 6  /* moe_route_noisy */
 };
 
 /* Layer description (host memory). Limits: T >= 0; 1 <= E <= 1024; 1 <= k <= min(E, 32); capacity >= 0;
@@ -141,6 +142,23 @@ int moe_workspace_bytes(const moe_shape* shape, int stage, size_t* bytes);
 int moe_route(const moe_shape* shape, const void* x, const float* w_router, const float* sel_bias,
               float* logits, int32_t* topk_idx, float* topk_w, int32_t* counts, float* stats,
               void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* moe_route_noisy -- moe_route with noisy top-k gating.
+ *
+ * Defined by: "Mixture of Experts" tutorial, Noisy top-k gating: Gaussian noise is added to the
+ * gating logits before the top-k, scaled per token by a second learned linear projection of x:
+ *   H = x W_router^T + noise * softplus(x W_noise^T)
+ * (the page's formula was lost; the scale is kept positive with softplus as in the published
+ * recipe). H then replaces the logits everywhere: key, top-k, gates and statistics, exactly as in
+ * moe_route. The noise is an input (the caller draws it), so the call is deterministic.
+ *   w_noise [E, d_model] fp32  in: noise-scale projection
+ *   noise   [T, E]       fp32  in: standard normal draws
+ *   logits  [T, E] fp32 or NULL out: H
+ * Other arguments as moe_route. Workspace: MOE_STAGE_ROUTE_NOISY. */
+int moe_route_noisy(const moe_shape* shape, const void* x, const float* w_router, const float* w_noise,
+                    const float* noise, const float* sel_bias, float* logits, int32_t* topk_idx,
+                    float* topk_w, int32_t* counts, float* stats, void* ws, size_t ws_bytes,
+                    moe_stream_t stream);
 
 /* moe_permute -- expert-contiguous, stable order of the T*k assignments.
  *

@@ -19,7 +19,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 MOE_GELU_MLP, MOE_SWIGLU = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
-MOE_STAGE_ROUTE, MOE_STAGE_PERMUTE, MOE_STAGE_FFN, MOE_STAGE_SHARED, MOE_STAGE_FORWARD, MOE_STAGE_EXPERT = range(6)
+(MOE_STAGE_ROUTE, MOE_STAGE_PERMUTE, MOE_STAGE_FFN, MOE_STAGE_SHARED, MOE_STAGE_FORWARD, MOE_STAGE_EXPERT,
+ MOE_STAGE_ROUTE_NOISY) = range(7)
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -55,6 +56,8 @@ _SIGS = {
     "moe_forward": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    _P, ctypes.c_size_t, _P]),
     "moe_update_bias": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, ctypes.c_float, _P, _P]),
+    "moe_route_noisy": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                       ctypes.c_size_t, _P]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
 }
 EXPORTED = tuple(_SIGS)
@@ -185,3 +188,12 @@ def moe_forward(shape, x, w_router, sel_bias, w_in, b_in, w_out, b_out, ws_in, w
 def moe_update_bias(shape, counts, gamma: float, sel_bias, stream=None) -> None:
     _check("moe_update_bias", lib().moe_update_bias(ctypes.byref(shape), _ptr(counts), float(gamma), _ptr(sel_bias),
                                                     _stream(stream)))
+
+
+def moe_route_noisy(shape, x, w_router, w_noise, noise, sel_bias, logits, topk_idx, topk_w, counts, stats, ws,
+                    stream=None) -> None:
+    _check("moe_route_noisy", lib().moe_route_noisy(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(w_noise),
+                                                    _ptr(noise), _ptr(sel_bias), _ptr(logits), _ptr(topk_idx),
+                                                    _ptr(topk_w), _ptr(counts), _ptr(stats), _ptr(ws), _nbytes(ws),
+                                                    _stream(stream)))
+

@@ -68,6 +68,22 @@ RouteWs route_ws(const moe_shape* s) {
     return w;
 }
 
+// noisy routing: the route workspace plus the noise projection's logits and split
+struct RouteNoisyWs {
+    RouteWs base;
+    size_t s_logits, wsplit_n, bytes;
+};
+RouteNoisyWs route_noisy_ws(const moe_shape* s) {
+    RouteNoisyWs w;
+    w.base = route_ws(s);
+    Carver c;
+    c.off = w.base.bytes;
+    w.s_logits = c.take((size_t)s->T * s->E * 4);
+    w.wsplit_n = c.take(s->dtype == MOE_BF16 ? (size_t)3 * w.base.Epad * s->d_model * 2 : 0);
+    w.bytes = c.off;
+    return w;
+}
+
 struct PermWs {
     size_t tile_counts, tile_base, bytes;
     int ntiles;
@@ -163,7 +179,31 @@ void do_route(const moe_shape* s, const void* x, const float* w_router, const fl
     moe::launch_route_prep(w_router, s->E, w.Epad, s->d_model, wsplit, ticket, st);
     moe::launch_route_logits(s->dtype, x, w_router, wsplit, w.Epad, lg, s->T, s->d_model, s->E, st);
     moe::launch_route_select(lg, sel_bias, s->T, s->E, s->k, s->score, s->renorm, topk_idx, topk_w, blk_counts, blk_P,
-                             blk_H, st);
+                             blk_H, nullptr, nullptr, nullptr, st);
+    moe::launch_route_finalize(blk_counts, blk_P, blk_H, w.nblk, s->T, s->E, counts, at<double>(ws, w.fp), ticket,
+                               stats, st);
+}
+
+void do_route_noisy(const moe_shape* s, const void* x, const float* w_router, const float* w_noise,
+                    const float* noise, const float* sel_bias, float* logits, int32_t* topk_idx, float* topk_w,
+                    int32_t* counts, float* stats, void* ws, hipStream_t st) {
+    const RouteNoisyWs wn = route_noisy_ws(s);
+    const RouteWs& w = wn.base;
+    float* lg = at<float>(ws, w.logits);
+    float* sl = at<float>(ws, wn.s_logits);
+    const bool bf = s->dtype == MOE_BF16;
+    uint16_t* wsplit = bf ? at<uint16_t>(ws, w.wsplit) : nullptr;
+    uint16_t* wsplit_n = bf ? at<uint16_t>(ws, wn.wsplit_n) : nullptr;
+    int32_t* ticket = at<int32_t>(ws, w.ticket);
+    int32_t* blk_counts = at<int32_t>(ws, w.blk_counts);
+    float* blk_P = stats ? at<float>(ws, w.blk_P) : nullptr;
+    float* blk_H = stats ? at<float>(ws, w.blk_H) : nullptr;
+    moe::launch_route_prep(w_router, s->E, w.Epad, s->d_model, wsplit, ticket, st);
+    moe::launch_route_logits(s->dtype, x, w_router, wsplit, w.Epad, lg, s->T, s->d_model, s->E, st);
+    moe::launch_route_prep(w_noise, s->E, w.Epad, s->d_model, wsplit_n, ticket, st);
+    moe::launch_route_logits(s->dtype, x, w_noise, wsplit_n, w.Epad, sl, s->T, s->d_model, s->E, st);
+    moe::launch_route_select(lg, sel_bias, s->T, s->E, s->k, s->score, s->renorm, topk_idx, topk_w, blk_counts, blk_P,
+                             blk_H, sl, noise, logits, st);
     moe::launch_route_finalize(blk_counts, blk_P, blk_H, w.nblk, s->T, s->E, counts, at<double>(ws, w.fp), ticket,
                                stats, st);
 }
@@ -247,6 +287,7 @@ int moe_workspace_bytes(const moe_shape* shape, int stage, size_t* bytes) {
         case MOE_STAGE_SHARED: *bytes = shared_ws(shape).bytes; break;
         case MOE_STAGE_FORWARD: *bytes = fwd_ws(shape).bytes; break;
         case MOE_STAGE_EXPERT: *bytes = expert_ws(shape).bytes; break;
+        case MOE_STAGE_ROUTE_NOISY: *bytes = route_noisy_ws(shape).bytes; break;
         default: return MOE_ERR_INVALID_ARG;
     }
     return MOE_OK;
@@ -353,6 +394,23 @@ int moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* inv_p
     (void)hipGetLastError();
     moe::launch_combine(shape->dtype, y_perm, inv_pos, topk_w, y_shared, y, shape->T, shape->d_model, shape->k,
                         static_cast<hipStream_t>(stream));
+    return launched();
+}
+
+int moe_route_noisy(const moe_shape* shape, const void* x, const float* w_router, const float* w_noise,
+                    const float* noise, const float* sel_bias, float* logits, int32_t* topk_idx, float* topk_w,
+                    int32_t* counts, float* stats, void* ws, size_t ws_bytes, moe_stream_t stream) {
+    const int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    MOE_REQUIRE(ok_ptr(x) && ok_ptr(w_router) && ok_ptr(w_noise) && ok_ptr(noise) && ok_ptr(topk_idx) &&
+                ok_ptr(topk_w) && ok_ptr(counts));
+    MOE_REQUIRE(ok_opt(sel_bias) && ok_opt(logits) && ok_opt(stats) && ok_opt(ws));
+    const size_t need = route_noisy_ws(shape).bytes;
+    if (ws_bytes < need || (ws == nullptr && need > 0)) return MOE_ERR_WORKSPACE;
+    if (shape->T == 0) return MOE_OK;
+    (void)hipGetLastError();
+    do_route_noisy(shape, x, w_router, w_noise, noise, sel_bias, logits, topk_idx, topk_w, counts, stats, ws,
+                   static_cast<hipStream_t>(stream));
     return launched();
 }
 

@@ -17,9 +17,11 @@ void launch_route_prep(const float* w_router, int E, int Epad, int d, uint16_t* 
                        hipStream_t s);
 void launch_route_logits(int dtype, const void* x, const float* w_router, const uint16_t* wsplit, int Epad,
                          float* logits, int64_t T, int d, int E, hipStream_t s);
+// s_logits / noise (both or neither): noisy top-k, logits replaced by logits + noise * softplus(s_logits),
+// written to h_out when given
 void launch_route_select(const float* logits, const float* sel_bias, int64_t T, int E, int k, int score,
                          int renorm, int32_t* topk_idx, float* topk_w, int32_t* blk_counts, float* blk_P,
-                         float* blk_H, hipStream_t s);
+                         float* blk_H, const float* s_logits, const float* noise, float* h_out, hipStream_t s);
 // counts[E] always; stats (f, P, aux, entropy) when stats != NULL
 void launch_route_finalize(const int32_t* blk_counts, const float* blk_P, const float* blk_H, int nblk, int64_t T,
                            int E, int32_t* counts, double* fp_scratch, int32_t* ticket, float* stats,

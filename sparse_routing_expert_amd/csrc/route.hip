@@ -24,6 +24,7 @@ __device__ __forceinline__ uint64_t pack_key(float v, int e) {
 __device__ __forceinline__ int key_index(uint64_t k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
 
 __device__ __forceinline__ float sigmoidf_(float l) { return 1.0f / (1.0f + expf(-l)); }
+__device__ __forceinline__ float softplusf_(float z) { return fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z))); }
 
 }  // namespace
 
@@ -185,7 +186,9 @@ __global__ __launch_bounds__(256) void route_logits_f32_kernel(const float* __re
 // Per token (one wave handles kSelTokensPerWave tokens, their logits loaded up front): scores,
 // balance-statistic partials, top-k by k rounds of a wave-wide max over packed keys, gates. Each
 // block writes its expert histogram, its per-expert probability sums and its entropy sum;
-// route_finalize reduces them.
+// route_finalize reduces them. Noisy top-k ("Mixture of Experts" tutorial, Noisy top-k gating):
+// with s_logits (= x W_noise^T) and noise given, the logits become H = l + noise * softplus(s)
+// before anything else, and H is written to h_out when that is given.
 constexpr int kSelTokensPerWave = kRouteTokensPerBlock / 4;
 template <int EPL>
 __global__ __launch_bounds__(256) void route_select_kernel(const float* __restrict__ logits,
@@ -194,7 +197,10 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
                                                            int32_t* __restrict__ topk_idx,
                                                            float* __restrict__ topk_w,
                                                            int32_t* __restrict__ blk_counts,
-                                                           float* __restrict__ blk_P, float* __restrict__ blk_H) {
+                                                           float* __restrict__ blk_P, float* __restrict__ blk_H,
+                                                           const float* __restrict__ s_logits,
+                                                           const float* __restrict__ noise,
+                                                           float* __restrict__ h_out) {
     __shared__ int s_cnt[1024];
     __shared__ float s_P[4][1024];
     __shared__ float s_H[4];
@@ -221,6 +227,19 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
             const int e = lane + 64 * i;
             lall[q][i] = (tb + q < T && e < E) ? logits[(tb + q) * E + e] : -INFINITY;
         }
+    if (s_logits != nullptr) {
+#pragma unroll
+        for (int q = 0; q < kSelTokensPerWave; ++q)
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const int e = lane + 64 * i;
+                if (tb + q < T && e < E) {
+                    const int64_t o = (tb + q) * E + e;
+                    lall[q][i] = lall[q][i] + noise[o] * softplusf_(s_logits[o]);
+                    if (h_out != nullptr) h_out[o] = lall[q][i];
+                }
+            }
+    }
 #pragma unroll
     for (int q = 0; q < kSelTokensPerWave; ++q) {
         const int64_t t = tb + q;
@@ -419,11 +438,11 @@ void launch_route_logits(int dtype, const void* x, const float* w_router, const 
 
 void launch_route_select(const float* logits, const float* sel_bias, int64_t T, int E, int k, int score,
                          int renorm, int32_t* topk_idx, float* topk_w, int32_t* blk_counts, float* blk_P,
-                         float* blk_H, hipStream_t s) {
+                         float* blk_H, const float* s_logits, const float* noise, float* h_out, hipStream_t s) {
     const unsigned nblk = (unsigned)((T + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock);
 #define MOE_SELECT(EPL)                                                                                  \
     route_select_kernel<EPL><<<nblk, 256, 0, s>>>(logits, sel_bias, T, E, k, score, renorm, topk_idx, topk_w, \
-                                                 blk_counts, blk_P, blk_H)
+                                                 blk_counts, blk_P, blk_H, s_logits, noise, h_out)
     if (E <= 64) MOE_SELECT(1);
     else if (E <= 128) MOE_SELECT(2);
     else if (E <= 256) MOE_SELECT(4);

@@ -102,7 +102,7 @@ CONFIGS: Dict[str, LayerConfig] = {
 }
 
 # Tensor ids of the seed streams.
-_X, _WR, _BIAS, _WIN, _BIN, _WOUT, _BOUT, _SIN, _SOUT, _PERM = range(10)
+_X, _WR, _BIAS, _WIN, _BIN, _WOUT, _BOUT, _SIN, _SOUT, _PERM, _WNOISE, _NOISE = range(12)
 X_CHUNK_ROWS = 64  # token rows drawn per seed (so prefixes of x are length-independent)
 
 ZIPF_S = 1.2  # popularity exponent of the Qwen3-shaped layer
@@ -265,6 +265,20 @@ def gen_router(cfg: LayerConfig, device="cpu", seed: int = 0):
                               generator=_gen("cpu", seed, cfg.layer_id, _BIAS))
         bias = (steps.to(torch.float64) * BIAS_STEP).to(torch.float32).to(device)
     return w, bias
+
+
+def gen_noisy_router(cfg: LayerConfig, device="cpu", seed: int = 0, T: Optional[int] = None):
+    """Noisy top-k inputs: the noise-scale projection W_noise [E, d] fp32 (same std as the router)
+    and standard normal draws [T, E] fp32 (64-token chunks, like x)."""
+    w = torch.empty((cfg.E, cfg.d), dtype=torch.float32, device=device)
+    for e in range(cfg.E):
+        w[e] = _normal((cfg.d,), cfg.router_std, device, torch.float32, seed, cfg.layer_id, _WNOISE, e)
+    T = cfg.T if T is None else T
+    n = torch.empty((T, cfg.E), dtype=torch.float32, device=device)
+    for c0 in range(0, T, 64):
+        c1 = min(T, c0 + 64)
+        n[c0:c1] = _normal((c1 - c0, cfg.E), 1.0, device, torch.float32, seed, cfg.layer_id, _NOISE, c0 // 64)
+    return w, n
 
 
 def gen_expert(cfg: LayerConfig, e: int, device="cpu", seed: int = 0):

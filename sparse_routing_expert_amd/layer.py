@@ -57,6 +57,13 @@ class MoeLayer:
                     self.logits if with_logits else None, self.topk_idx, self.topk_w, self.counts,
                     self.stats if with_stats else None, self.ws(L.MOE_STAGE_ROUTE))
 
+    def route_noisy(self, w_noise, noise, with_logits=True, with_stats=True):
+        """Noisy top-k routing; the logits buffer receives H = l + noise * softplus(x W_noise^T)."""
+        t = self.t
+        L.moe_route_noisy(self.shape, t["x"], t["w_r"], w_noise, noise, t["sel_bias"],
+                          self.logits if with_logits else None, self.topk_idx, self.topk_w, self.counts,
+                          self.stats if with_stats else None, self.ws(L.MOE_STAGE_ROUTE_NOISY))
+
     def permute(self, topk_idx=None, x=None):
         L.moe_permute(self.shape, self.topk_idx if topk_idx is None else topk_idx, self.t["x"] if x is None else x,
                       self.offsets, self.sorted_token, self.inv_pos, self.x_perm, self.ws(L.MOE_STAGE_PERMUTE))

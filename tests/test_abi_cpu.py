@@ -117,6 +117,27 @@ def test_capacity_and_bias_rejections(lib):
     assert ub(ctypes.byref(good_shape(capacity=-5)), FAKE, 1e-3, FAKE, None) == L.MOE_ERR_INVALID_ARG
 
 
+def test_route_noisy_rejections(lib):
+    s = good_shape()
+    rc, n = ws_bytes(s, L.MOE_STAGE_ROUTE_NOISY)
+    assert rc == 0 and n > ws_bytes(s, L.MOE_STAGE_ROUTE)[1]
+    f = lib.moe_route_noisy
+    good = [ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, FAKE, n, None]
+    for i in (1, 2, 3, 4, 7, 8, 9):  # required pointers
+        bad = list(good)
+        bad[i] = None
+        assert f(*bad) == L.MOE_ERR_INVALID_ARG, i
+    bad = list(good)
+    bad[4] = MISALIGNED
+    assert f(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(good)
+    bad[12] = n - 1
+    assert f(*bad) == L.MOE_ERR_WORKSPACE
+    z = list(good)
+    z[0] = ctypes.byref(good_shape(T=0))
+    assert f(*z) == L.MOE_OK
+
+
 def test_route_rejections(lib):
     s = good_shape()
     r = lib.moe_route
