@@ -16,7 +16,7 @@
  *                   (= moe_expert_up then moe_expert_down)
  *   moe_shared_ffn  the always-on shared SwiGLU expert (dense)
  *   moe_combine     gate-weighted sum back to token order (+ shared output)
- * and moe_forward, which chains them.
+ * and moe_forward, which chains them; moe_backward differentiates the layer.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -87,7 +87,8 @@ enum {
     MOE_STAGE_SHARED = 3,
     MOE_STAGE_FORWARD = 4,
     MOE_STAGE_EXPERT = 5,      /* moe_expert_up / moe_expert_down */
-    MOE_STAGE_ROUTE_NOISY = 6  /* moe_route_noisy */
+    MOE_STAGE_ROUTE_NOISY = 6, /* moe_route_noisy */
+    MOE_STAGE_BACKWARD = 7     /* moe_backward */
 };
 
 /* Layer description (host memory). Limits: T >= 0; 1 <= E <= 1024; 1 <= k <= min(E, 32); capacity >= 0;
@@ -292,6 +293,55 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router, co
                 const void* ws_in, const void* ws_out, void* y, int32_t* topk_idx_out,
                 float* topk_w_out, int32_t* counts_out, float* stats_out, void* ws, size_t ws_bytes,
                 moe_stream_t stream);
+
+/* moe_backward -- gradients of the layer for an output gradient dy (fine-tuning).
+ *
+ * Defined by: the chain rule through the forward above, for the fine-tuning the pages describe
+ * ("Fine-tuning and serving MoE models", Why MoE breaks naive fine-tuning: task loss plus the
+ * balancing loss, backpropagated; "Router Optimization Techniques", How It Works 1: L_aux puts
+ * gradients on the router weights). The routing
+ * choice is piecewise constant, so gradients reach the router only through the gates of the
+ * selected experts ("Mixture of Experts" tutorial, Noisy top-k gating: entries outside the top-k are
+ * -inf before the softmax); the selection bias gets none (it moves by moe_update_bias); assignments
+ * dropped by capacity get none. Per piece (row vectors, Linear [out, in] weights):
+ *   combine:  dg[t,j] = <dy[t], y_perm[row]>,  dY[row] = g[t,j] dy[t]
+ *   expert:   GELU   dh = dY W2, dz = dh gelu'(z), dW1 = dz^T X, db1 = sum dz, dX = dz W1,
+ *                    dW2 = dY^T h, db2 = sum dY;
+ *             SwiGLU dh = dY Wd, da = dh u silu'(a), du = dh silu(a), dWg = da^T X, dWu = du^T X,
+ *                    dX = da Wg + du Wu, dWd = dY^T h
+ *   gates:    softmax & renorm: dl_S = g (dg - <g, dg>); softmax & !renorm: dl = p (dp - <p, dp>)
+ *             with dp = dg on the selection; sigmoid: dl_S = (dg - <g, dg>) / sum_S s * s (1 - s)
+ *   balance:  + gradient of aux_coef * E * sum_e f_e P_e with f = counts / T held constant
+ *   router:   dW_router = dl^T x,  dx = sum of the kept slots' dX rows + shared dX + dl W_router
+ * The expert pre-activations and h are recomputed from x_perm (one grouped GEMM), not stored by the
+ * forward: the selective recomputation of the intra-expert activations that "Router Optimization
+ * Techniques", Lessons From Production Deployments, Lesson 3 describes.
+ *
+ * Inputs: the forward's arguments (shape, x, w_router, w_in, b_in, w_out, b_out, ws_in, ws_out) and
+ * its saved results:
+ *   logits   [T, E]        fp32   moe_route's logits (moe_route_noisy: H)
+ *   topk_idx [T, k], topk_w [T, k], counts [E] (NULL allowed when aux_coef == 0)   moe_route
+ *   offsets [E + 1], inv_pos [T*k], x_perm [T*k, d_model]                          moe_permute
+ *   y_perm   [T*k, d_model] dtype  moe_grouped_ffn's output
+ *   dy       [T, d_model]   dtype  gradient of the loss with respect to y
+ *   aux_coef                       weight of the balancing term (0: none); must be finite
+ * Outputs (fp32 except dx):
+ *   dx        [T, d_model]        dtype  one rounding of the fp32 sum
+ *   dw_router [E, d_model]
+ *   dw_in     [E, n_in, d_model], dw_out [E, d_model, d_ff]   zero for an expert without rows
+ *   db_in [E, d_ff], db_out [E, d_model]   exactly when b_in / b_out are given (else NULL)
+ *   dws_in [2 d_ff_shared, d_model], dws_out [d_model, d_ff_shared]   exactly when d_ff_shared > 0
+ *   dlogits   [T, E] or NULL      the router logit gradient dl
+ * Products accumulate in fp32 (bf16 layers: bf16 operands on the matrix cores; the recomputed
+ * pre-activation, h, dY and the activation gradient are rounded once to bf16 as operands); every sum
+ * runs in a fixed order, so results are deterministic. Gradients are written, not accumulated.
+ * Workspace: MOE_STAGE_BACKWARD. */
+int moe_backward(const moe_shape* shape, const void* x, const float* w_router, const void* w_in, const void* b_in,
+                 const void* w_out, const void* b_out, const void* ws_in, const void* ws_out, const float* logits,
+                 const int32_t* topk_idx, const float* topk_w, const int32_t* counts, const int32_t* offsets,
+                 const int32_t* inv_pos, const void* x_perm, const void* y_perm, const void* dy, float aux_coef,
+                 void* dx, float* dw_router, float* dw_in, float* db_in, float* dw_out, float* db_out,
+                 float* dws_in, float* dws_out, float* dlogits, void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* Human-readable name of a moe_status value (static string; never NULL). */
 const char* moe_status_str(int status);

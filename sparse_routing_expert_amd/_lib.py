@@ -20,7 +20,7 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_GELU_MLP, MOE_SWIGLU = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 (MOE_STAGE_ROUTE, MOE_STAGE_PERMUTE, MOE_STAGE_FFN, MOE_STAGE_SHARED, MOE_STAGE_FORWARD, MOE_STAGE_EXPERT,
- MOE_STAGE_ROUTE_NOISY) = range(7)
+ MOE_STAGE_ROUTE_NOISY, MOE_STAGE_BACKWARD) = range(8)
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -58,6 +58,8 @@ _SIGS = {
     "moe_update_bias": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, ctypes.c_float, _P, _P]),
     "moe_route_noisy": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        ctypes.c_size_t, _P]),
+    "moe_backward": (ctypes.c_int, [ctypes.POINTER(moe_shape)] + [_P] * 17 + [ctypes.c_float] + [_P] * 10
+                     + [ctypes.c_size_t, _P]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
 }
 EXPORTED = tuple(_SIGS)
@@ -197,3 +199,14 @@ def moe_route_noisy(shape, x, w_router, w_noise, noise, sel_bias, logits, topk_i
                                                     _ptr(topk_w), _ptr(counts), _ptr(stats), _ptr(ws), _nbytes(ws),
                                                     _stream(stream)))
 
+
+
+def moe_backward(shape, x, w_router, w_in, b_in, w_out, b_out, ws_in, ws_out, logits, topk_idx, topk_w, counts,
+                 offsets, inv_pos, x_perm, y_perm, dy, aux_coef: float, dx, dw_router, dw_in, db_in, dw_out, db_out,
+                 dws_in, dws_out, dlogits, ws, stream=None) -> None:
+    _check("moe_backward", lib().moe_backward(
+        ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(w_in), _ptr(b_in), _ptr(w_out), _ptr(b_out), _ptr(ws_in),
+        _ptr(ws_out), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(inv_pos),
+        _ptr(x_perm), _ptr(y_perm), _ptr(dy), float(aux_coef), _ptr(dx), _ptr(dw_router), _ptr(dw_in), _ptr(db_in),
+        _ptr(dw_out), _ptr(db_out), _ptr(dws_in), _ptr(dws_out), _ptr(dlogits), _ptr(ws), _nbytes(ws),
+        _stream(stream)))

@@ -1,0 +1,611 @@
+// moe_backward kernels: gradients of the MoE-FFN layer (the chain rule of the forward in
+// moe_route / moe_permute / moe_grouped_ffn / moe_combine; the fine-tuning setting of "Fine-Tuning
+// Mixture of Experts (MoE) Models: Router Optimization Techniques" and "Fine-tuning and serving MoE
+// models").
+//
+// Products with a transposed or token-indexed operand (dh = dY Wd, dX = dAU W_in, dWd = dY^T h,
+// dW_in = dAU^T X) all go through one strided grouped GEMM, C(m, n) = sum_k A(m, k) B(n, k) with
+// arbitrary element strides, so no operand is ever transposed in memory:
+//   rows:   groups are expert segments of a permuted buffer (rows offsets[g] .. offsets[g+1]),
+//           B and K per group (dgrad),
+//   ksplit: K runs over an expert's rows (k = offsets[g] .. offsets[g+1]), one C per group (wgrad),
+//   dense:  one group (the shared expert).
+// bf16 operands use v_mfma_f32_32x32x16_bf16 on 128 x 128 tiles with fp32 accumulation and fp32
+// output; a 16-byte load runs along whichever of the operand's two indices is contiguous, and the
+// LDS tile is always K-contiguous (64-byte rows, XOR-swizzled 16-byte chunks). fp32 operands
+// (fp32 layers) take a plain per-element kernel.
+#include "moe_common.h"
+#include "moe_kernels.h"
+#include "../../include/moe.h"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ float sigm(float z) { return 1.0f / (1.0f + expf(-z)); }
+__device__ __forceinline__ float silu_b(float z) { return z * sigm(z); }
+__device__ __forceinline__ float silu_grad_b(float z) {
+    const float s = sigm(z);
+    return s * (1.0f + z * (1.0f - s));
+}
+__device__ __forceinline__ float gelu_b(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+__device__ __forceinline__ float gelu_grad_b(float z) {
+    return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) + z * 0.39894228040143268f * expf(-0.5f * z * z);
+}
+__device__ __forceinline__ int swz_b(int r) { return (r >> 2) & 3; }
+
+template <bool BF16>
+__device__ __forceinline__ float ld_elem(const void* p, int64_t i) {
+    if (BF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+    return static_cast<const float*>(p)[i];
+}
+template <bool BF16>
+__device__ __forceinline__ void st_elem(void* p, int64_t i, float v) {
+    if (BF16) static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
+    else static_cast<float*>(p)[i] = v;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------------
+// Strided grouped GEMM
+// ------------------------------------------------------------------------------------------------
+
+// rows mode: the per-block tile schedule (prefix sums of 128-row tiles per group) in LDS.
+__device__ __forceinline__ void sg_schedule(const int32_t* __restrict__ offsets, int e_begin, int G, int* s_ts,
+                                            int* s_wave) {
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    int n[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int g = tid * 4 + i;
+        n[i] = 0;
+        if (g < G) n[i] = (offsets[e_begin + g + 1] - offsets[e_begin + g] + 127) / 128;
+        sum += n[i];
+    }
+    int inc = sum;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int v = __shfl_up(inc, o, kWave);
+        if (lane >= o) inc += v;
+    }
+    if (lane == kWave - 1) s_wave[wave] = inc;
+    __syncthreads();
+    int base = inc - sum;
+    for (int w = 0; w < wave; ++w) base += s_wave[w];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int g = tid * 4 + i;
+        if (g < G) s_ts[g] = base;
+        base += n[i];
+    }
+    if (tid == 255) s_ts[G] = base;
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void sg_gemm_bf16_kernel(SgArgs p) {
+    constexpr int BM = 128, BN = 128, BK = 32;
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[2][(BM + BN) * BK];
+    __shared__ int s_ts[1025];
+    __shared__ int s_wave[4];
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t tiles_n = (p.N + BN - 1) / BN;
+
+    // ---- tile -> (group, m0, n0), the group's M, K range and bases
+    int g = 0;
+    int64_t m0 = 0, n0 = 0, M = p.M, kb = 0, ke = p.K, row_base = 0;
+    if (p.mode == SG_ROWS) {
+        sg_schedule(p.offsets, p.e_begin, p.G, s_ts, s_wave);
+        const int64_t lin = blockIdx.x;
+        const int64_t total = (int64_t)s_ts[p.G] * tiles_n;
+        if (lin >= total) return;  // uniform per block
+        const int64_t key = lin / tiles_n;
+        int lo = 0, hi = p.G - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_ts[mid] <= key) lo = mid;
+            else hi = mid - 1;
+        }
+        g = lo;
+        m0 = (key - s_ts[g]) * BM;
+        n0 = (lin % tiles_n) * BN;
+        row_base = p.offsets[p.e_begin + g];
+        M = p.offsets[p.e_begin + g + 1] - row_base;
+    } else {
+        const int64_t tiles_m = (p.M + BM - 1) / BM;
+        const int64_t per_group = tiles_m * tiles_n;
+        g = (int)(blockIdx.x / per_group);
+        if (g >= p.G) return;
+        const int64_t t = blockIdx.x % per_group;
+        m0 = (t / tiles_n) * BM;
+        n0 = (t % tiles_n) * BN;
+        if (p.mode == SG_KSPLIT) {
+            kb = p.offsets[p.e_begin + g];
+            ke = p.offsets[p.e_begin + g + 1];
+        }
+    }
+    const uint16_t* A = p.A + (p.mode == SG_ROWS ? row_base * p.sam : 0);
+    const uint16_t* B = p.B + (int64_t)(p.mode == SG_ROWS ? g : 0) * p.b_group;
+    float* C = p.C + (p.mode == SG_ROWS ? row_base * p.scm : (int64_t)g * p.c_group);
+    const bool a_kc = p.sak == 1, b_kc = p.sbk == 1;
+    const int64_t nk = (ke - kb + BK - 1) / BK;
+
+    // ---- loads: 2 x 16 bytes of A and of B per thread and stage
+    u32x4 ra[2], rb[2];
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#define SG_LOAD(R, base, s_row, s_k, kc_layout, rows_valid, kt_)                                           \
+    _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                                        \
+        const int c = h * 256 + tid;                                                                       \
+        R[h] = zero;                                                                                       \
+        if (kc_layout) {                                                                                   \
+            const int r = c >> 2, kc = c & 3;                                                              \
+            const int64_t k = kb + (kt_) * BK + kc * 8;                                                    \
+            if (r < (rows_valid) && k < ke) R[h] = ld16(base + (int64_t)r * (s_row) + k);                  \
+        } else {                                                                                           \
+            const int kk = c >> 4, mc = c & 15;                                                            \
+            const int64_t k = kb + (kt_) * BK + kk;                                                        \
+            if (mc * 8 < (rows_valid) && k < ke) R[h] = ld16(base + (int64_t)mc * 8 + k * (s_k));          \
+        }                                                                                                  \
+    }
+#define SG_STORE(R, buf, row0, kc_layout)                                                                  \
+    _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                                        \
+        const int c = h * 256 + tid;                                                                       \
+        uint16_t* L = lds[buf];                                                                            \
+        if (kc_layout) {                                                                                   \
+            const int r = (row0) + (c >> 2), kc = c & 3;                                                   \
+            *reinterpret_cast<u32x4*>(L + r * BK + ((kc ^ swz_b(r)) << 3)) = R[h];                          \
+        } else {                                                                                           \
+            const int kk = c >> 4, mc = c & 15;                                                            \
+            const uint16_t* e8 = reinterpret_cast<const uint16_t*>(&R[h]);                                  \
+            _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                \
+                const int r = (row0) + mc * 8 + i;                                                         \
+                L[r * BK + (((kk >> 3) ^ swz_b(r)) << 3) + (kk & 7)] = e8[i];                              \
+            }                                                                                              \
+        }                                                                                                  \
+    }
+    // A(m, k) at Ab + m * sam + k * sak for m in the tile; B(n, k) likewise
+    const uint16_t* Ab = A + m0 * p.sam;
+    const uint16_t* Bb = B + n0 * p.sbn;
+    const int a_rows = (int)(M - m0 < BM ? M - m0 : BM);
+    const int b_rows = (int)(p.N - n0 < BN ? p.N - n0 : BN);
+    // for a K-contiguous operand the row stride is s_row; for a row-contiguous one the 8-element
+    // chunk runs along the rows and s_k steps k (m-chunks need rows_valid to be a multiple of 8)
+    const int wm = wave & 1, wn = wave >> 1;
+    const int khalf = lane >> 5;
+    floatx16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    if (nk > 0) {
+        SG_LOAD(ra, Ab, p.sam, p.sak, a_kc, a_rows, 0)
+        SG_LOAD(rb, Bb, p.sbn, p.sbk, b_kc, b_rows, 0)
+        SG_STORE(ra, 0, 0, a_kc)
+        SG_STORE(rb, 0, BM, b_kc)
+        __syncthreads();
+    }
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        const int buf = (int)(kt & 1);
+        if (kt + 1 < nk) {
+            SG_LOAD(ra, Ab, p.sam, p.sak, a_kc, a_rows, kt + 1)
+            SG_LOAD(rb, Bb, p.sbn, p.sbk, b_kc, b_rows, kt + 1)
+        }
+        const uint16_t* L = lds[buf];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int c = kk * 2 + khalf;
+            bf16x8 fa[2], fb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = wm * 64 + i * 32 + (lane & 31);
+                fa[i] = *reinterpret_cast<const bf16x8*>(L + r * BK + ((c ^ swz_b(r)) << 3));
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int r = BM + wn * 64 + j * 32 + (lane & 31);
+                fb[j] = *reinterpret_cast<const bf16x8*>(L + r * BK + ((c ^ swz_b(r)) << 3));
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < nk) {
+            SG_STORE(ra, buf ^ 1, 0, a_kc)
+            SG_STORE(rb, buf ^ 1, BM, b_kc)
+        }
+        __syncthreads();
+    }
+#undef SG_LOAD
+#undef SG_STORE
+    // C layout of the 32x32 tile: lane holds column lane%32, rows 8*(v/4) + 4*(lane/32) + v%4
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
+            if (n >= p.N) continue;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t m = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
+                if (m < M) C[m * p.scm + n] = acc[i][j][v];
+            }
+        }
+}
+
+// fp32 operands: one thread per output element, sequential fp32 FMA over K.
+__global__ __launch_bounds__(256) void sg_gemm_f32_kernel(SgArgsF p) {
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t m_rel = blockIdx.y;
+    const int g = blockIdx.z;
+    if (n >= p.N || g >= p.G) return;
+    int64_t M = p.M, kb = 0, ke = p.K, row_base = 0;
+    if (p.mode == SG_ROWS) {
+        row_base = p.offsets[p.e_begin + g];
+        M = p.offsets[p.e_begin + g + 1] - row_base;
+    } else if (p.mode == SG_KSPLIT) {
+        kb = p.offsets[p.e_begin + g];
+        ke = p.offsets[p.e_begin + g + 1];
+    }
+    const float* B = p.B + (int64_t)(p.mode == SG_ROWS ? g : 0) * p.b_group;
+    float* C = p.C + (p.mode == SG_ROWS ? row_base * p.scm : (int64_t)g * p.c_group);
+    for (int64_t m = m_rel; m < M; m += gridDim.y) {
+        const float* A = p.A + (row_base + m) * p.sam;
+        float acc = 0.f;
+        for (int64_t k = kb; k < ke; ++k) acc = fmaf(A[k * p.sak], B[n * p.sbn + k * p.sbk], acc);
+        C[m * p.scm + n] = acc;
+    }
+}
+
+void launch_sg_gemm_bf16(const SgArgs& a, int64_t max_rows, hipStream_t s) {
+    const int64_t tiles_n = (a.N + 127) / 128;
+    int64_t blocks;
+    if (a.mode == SG_ROWS) blocks = ((max_rows + 127) / 128 + a.G) * tiles_n;
+    else blocks = ((a.M + 127) / 128) * tiles_n * a.G;
+    if (blocks <= 0) return;
+    sg_gemm_bf16_kernel<<<(unsigned)blocks, 256, 0, s>>>(a);
+}
+
+void launch_sg_gemm_f32(const SgArgsF& a, int64_t max_rows, hipStream_t s) {
+    const int64_t ymax = a.mode == SG_ROWS ? max_rows : a.M;
+    const unsigned gy = (unsigned)(ymax < 1024 ? (ymax > 0 ? ymax : 1) : 1024);
+    dim3 grid((unsigned)((a.N + 255) / 256), gy, (unsigned)a.G);
+    sg_gemm_f32_kernel<<<grid, 256, 0, s>>>(a);
+}
+
+// ------------------------------------------------------------------------------------------------
+// Elementwise and reduction kernels
+// ------------------------------------------------------------------------------------------------
+
+// Per token (one wave): dg[t, j] = <dy[t], y_perm[row]> and dYp[row] = g[t, j] * dy[t] for each kept
+// slot (row = inv_pos[t*k + j] >= 0); dropped slots get dg = 0 and no row.
+template <bool BF16>
+__global__ __launch_bounds__(256) void bwd_combine_kernel(const void* __restrict__ dy, const void* __restrict__ y_perm,
+                                                          const int32_t* __restrict__ inv_pos,
+                                                          const float* __restrict__ topk_w, int64_t T, int d, int k,
+                                                          float* __restrict__ dg, void* __restrict__ dYp) {
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    for (int j = 0; j < k; ++j) {
+        const int p = inv_pos[t * k + j];
+        if (p < 0) {
+            if (lane == 0) dg[t * k + j] = 0.f;
+            continue;
+        }
+        const float gj = topk_w[t * k + j];
+        float dot = 0.f;
+        for (int i = lane; i < d; i += 64) {
+            const float v = ld_elem<BF16>(dy, t * d + i);
+            dot = fmaf(v, ld_elem<BF16>(y_perm, (int64_t)p * d + i), dot);
+            st_elem<BF16>(dYp, (int64_t)p * d + i, gj * v);
+        }
+        dot = wave_sum(dot);
+        if (lane == 0) dg[t * k + j] = dot;
+    }
+}
+
+// h = act(pre) on n_rows rows: SwiGLU pre = [a | u] (2F wide) -> silu(a) * u; GELU pre = z -> gelu(z).
+template <bool BF16>
+__global__ __launch_bounds__(256) void bwd_act_fwd_kernel(const void* __restrict__ pre, int64_t n_rows, int F, int act,
+                                                          void* __restrict__ h) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_rows * F) return;
+    const int64_t r = i / F;
+    const int f = (int)(i - r * F);
+    float v;
+    if (act == MOE_SWIGLU) v = silu_b(ld_elem<BF16>(pre, r * 2 * F + f)) * ld_elem<BF16>(pre, r * 2 * F + F + f);
+    else v = gelu_b(ld_elem<BF16>(pre, r * F + f));
+    st_elem<BF16>(h, i, v);
+}
+
+// dAU from dh (fp32) and the pre-activations: SwiGLU da = dh * u * silu'(a), du = dh * silu(a);
+// GELU dz = dh * gelu'(z).
+template <bool BF16>
+__global__ __launch_bounds__(256) void bwd_act_bwd_kernel(const float* __restrict__ dh, const void* __restrict__ pre,
+                                                          int64_t n_rows, int F, int act, void* __restrict__ dAU) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_rows * F) return;
+    const int64_t r = i / F;
+    const int f = (int)(i - r * F);
+    const float g = dh[i];
+    if (act == MOE_SWIGLU) {
+        const float a = ld_elem<BF16>(pre, r * 2 * F + f), u = ld_elem<BF16>(pre, r * 2 * F + F + f);
+        st_elem<BF16>(dAU, r * 2 * F + f, g * u * silu_grad_b(a));
+        st_elem<BF16>(dAU, r * 2 * F + F + f, g * silu_b(a));
+    } else {
+        st_elem<BF16>(dAU, i, g * gelu_grad_b(ld_elem<BF16>(pre, i)));
+    }
+}
+
+// dx32[t] = sum over kept slots of dXp[inv_pos[t*k + j]] (+ extra[t]), fp32, in slot order.
+__global__ __launch_bounds__(256) void bwd_unpermute_kernel(const float* __restrict__ dXp,
+                                                            const int32_t* __restrict__ inv_pos,
+                                                            const float* __restrict__ extra, int64_t T, int d, int k,
+                                                            float* __restrict__ dx32) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= T * d) return;
+    const int64_t t = i / d;
+    const int c = (int)(i - t * d);
+    float acc = 0.f;
+    for (int j = 0; j < k; ++j) {
+        const int p = inv_pos[t * k + j];
+        if (p >= 0) acc += dXp[(int64_t)p * d + c];
+    }
+    if (extra != nullptr) acc += extra[i];
+    dx32[i] = acc;
+}
+
+// Column sums per group: out[g][c] = sum over rows r in [offsets[g], offsets[g+1]) of src[r][c],
+// rows in ascending order (fixed order, so deterministic).
+template <bool BF16>
+__global__ __launch_bounds__(256) void bwd_colsum_kernel(const void* __restrict__ src, const int32_t* __restrict__ offsets,
+                                                         int e_begin, int ncols, float* __restrict__ out) {
+    const int g = blockIdx.y;
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= ncols) return;
+    const int r0 = offsets[e_begin + g], r1 = offsets[e_begin + g + 1];
+    float acc = 0.f;
+    for (int r = r0; r < r1; ++r) acc += ld_elem<BF16>(src, (int64_t)r * ncols + c);
+    out[(int64_t)g * ncols + c] = acc;
+}
+
+// Router logit gradient per token (one wave): the gate backward for the scoring in use, plus the
+// balancing term coef * E * sum f P with f = counts / T held constant.
+template <int EPL>
+__global__ __launch_bounds__(256) void bwd_gate_kernel(const float* __restrict__ logits,
+                                                       const int32_t* __restrict__ topk_idx,
+                                                       const float* __restrict__ dg, const int32_t* __restrict__ counts,
+                                                       float aux_coef, int64_t T, int E, int k, int score, int renorm,
+                                                       float* __restrict__ dl) {
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    const float* lt = logits + t * E;
+    float l[EPL], out[EPL];
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        l[i] = e < E ? lt[e] : -INFINITY;
+        out[i] = 0.f;
+        lmax = fmaxf(lmax, l[i]);
+    }
+    const bool softmax = score == MOE_SOFTMAX;
+    // lane j < k holds slot j: its expert, logit and gate gradient
+    const int ej = lane < k ? topk_idx[t * k + lane] : -1;
+    const float dgj = lane < k ? dg[t * k + lane] : 0.f;
+    float lj = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        // the logit of expert ej is held by lane ej % 64, register ej / 64
+        const int src = ej >= 0 ? (ej & 63) : 0;
+        const float v = __shfl(l[i], src, 64);
+        if (ej >= 0 && (ej >> 6) == i) lj = v;
+    }
+    if (softmax && !renorm) {
+        // dl = p * (dp - <p, dp>), dp = dg at the selected experts
+        const float m = wave_max(lmax);
+        float z = 0.f, p[EPL];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            p[i] = lane + 64 * i < E ? expf(l[i] - m) : 0.f;
+            z += p[i];
+        }
+        const float invZ = 1.0f / wave_sum(z);
+        float dpsum = 0.f;  // <p, dp> over the selection, formed on the slot lanes
+        const float pj = lane < k ? expf(lj - m) * invZ : 0.f;
+        dpsum = wave_sum(pj * dgj);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane + 64 * i;
+            float dp = 0.f;
+            for (int j = 0; j < k; ++j) {
+                const int ejj = __shfl(ej, j, 64);
+                const float dgg = __shfl(dgj, j, 64);
+                if (ejj == e) dp = dgg;
+            }
+            out[i] = p[i] * invZ * (dp - dpsum);
+        }
+    } else {
+        // selected slots only: softmax over the selected logits, or sigmoid normalised over them
+        float gsel, dsel;
+        if (softmax) {
+            const float ms = wave_max(lane < k ? lj : -INFINITY);
+            const float ex = lane < k ? expf(lj - ms) : 0.f;
+            gsel = ex / wave_sum(ex);
+            const float c = wave_sum(lane < k ? gsel * dgj : 0.f);
+            dsel = gsel * (dgj - c);
+        } else {
+            const float s = lane < k ? sigm(lj) : 0.f;
+            const float Z = wave_sum(s);
+            gsel = s / Z;
+            const float c = wave_sum(lane < k ? gsel * dgj : 0.f);
+            dsel = (dgj - c) / Z * s * (1.0f - s);
+        }
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane + 64 * i;
+            for (int j = 0; j < k; ++j) {
+                const int ejj = __shfl(ej, j, 64);
+                const float v = __shfl(dsel, j, 64);
+                if (ejj == e) out[i] = v;
+            }
+        }
+    }
+    if (aux_coef != 0.f) {
+        // p = balance distribution; dl += p' * (dp - <p, dp>) with dp_e = coef * E * f_e / T
+        const float m = wave_max(lmax);
+        float q[EPL], s[EPL], z = 0.f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane + 64 * i;
+            s[i] = e < E ? (softmax ? expf(l[i] - m) : sigm(l[i])) : 0.f;
+            z += s[i];
+        }
+        const float Z = wave_sum(z);
+        float pdp = 0.f, dpv[EPL];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane + 64 * i;
+            q[i] = s[i] / Z;
+            dpv[i] = e < E ? aux_coef * (float)E * ((float)counts[e] / (float)T) / (float)T : 0.f;
+            pdp += q[i] * dpv[i];
+        }
+        pdp = wave_sum(pdp);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const float c = dpv[i] - pdp;
+            out[i] += softmax ? q[i] * c : c / Z * s[i] * (1.0f - s[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E) dl[t * E + e] = out[i];
+    }
+}
+
+// dW_r[e][c] = sum_t dl[t][e] x[t][c]. Block (column block, 8 experts, token chunk z) sums its
+// kRouterChunk tokens in order into partials[z][e][c]; bwd_router_reduce adds the chunks in order.
+template <bool BF16>
+__global__ __launch_bounds__(256) void bwd_router_wgrad_kernel(const float* __restrict__ dl, const void* __restrict__ x,
+                                                               int64_t T, int E, int d, float* __restrict__ partials) {
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    const int e0 = blockIdx.y * 8;
+    const int64_t t0 = (int64_t)blockIdx.z * kRouterChunk;
+    if (c >= d) return;
+    const int64_t t1 = t0 + kRouterChunk < T ? t0 + kRouterChunk : T;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int64_t t = t0; t < t1; ++t) {
+        const float xv = ld_elem<BF16>(x, t * d + c);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (e0 + i < E) acc[i] = fmaf(dl[t * E + e0 + i], xv, acc[i]);
+    }
+    float* out = partials + (int64_t)blockIdx.z * E * d;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (e0 + i < E) out[(int64_t)(e0 + i) * d + c] = acc[i];
+}
+
+__global__ __launch_bounds__(256) void bwd_router_reduce_kernel(const float* __restrict__ partials, int nchunks,
+                                                                int64_t n, float* __restrict__ dw_r) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float acc = 0.f;
+    for (int z = 0; z < nchunks; ++z) acc += partials[(int64_t)z * n + i];
+    dw_r[i] = acc;
+}
+
+// dx[t][c] = dx32[t][c] + sum_e dl[t][e] W_r[e][c], written in the layer dtype (one rounding).
+template <bool BF16>
+__global__ __launch_bounds__(256) void bwd_router_dgrad_kernel(const float* __restrict__ dx32,
+                                                               const float* __restrict__ dl,
+                                                               const float* __restrict__ w_r, int64_t T, int E, int d,
+                                                               void* __restrict__ dx) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= T * d) return;
+    const int64_t t = i / d;
+    const int c = (int)(i - t * d);
+    float acc = dx32[i];
+    for (int e = 0; e < E; ++e) acc = fmaf(dl[t * E + e], w_r[(int64_t)e * d + c], acc);
+    st_elem<BF16>(dx, i, acc);
+}
+
+// ------------------------------------------------------------------------------------------------
+// launchers
+// ------------------------------------------------------------------------------------------------
+
+static unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
+
+void launch_bwd_combine(int dtype, const void* dy, const void* y_perm, const int32_t* inv_pos, const float* topk_w,
+                        int64_t T, int d, int k, float* dg, void* dYp, hipStream_t s) {
+    const unsigned nb = (unsigned)((T + 3) / 4);
+    if (dtype == MOE_BF16) bwd_combine_kernel<true><<<nb, 256, 0, s>>>(dy, y_perm, inv_pos, topk_w, T, d, k, dg, dYp);
+    else bwd_combine_kernel<false><<<nb, 256, 0, s>>>(dy, y_perm, inv_pos, topk_w, T, d, k, dg, dYp);
+}
+
+void launch_bwd_act_fwd(int dtype, const void* pre, int64_t n_rows, int F, int act, void* h, hipStream_t s) {
+    if (n_rows <= 0) return;
+    if (dtype == MOE_BF16) bwd_act_fwd_kernel<true><<<blocks_for(n_rows * F), 256, 0, s>>>(pre, n_rows, F, act, h);
+    else bwd_act_fwd_kernel<false><<<blocks_for(n_rows * F), 256, 0, s>>>(pre, n_rows, F, act, h);
+}
+
+void launch_bwd_act_bwd(int dtype, const float* dh, const void* pre, int64_t n_rows, int F, int act, void* dAU,
+                        hipStream_t s) {
+    if (n_rows <= 0) return;
+    if (dtype == MOE_BF16) bwd_act_bwd_kernel<true><<<blocks_for(n_rows * F), 256, 0, s>>>(dh, pre, n_rows, F, act, dAU);
+    else bwd_act_bwd_kernel<false><<<blocks_for(n_rows * F), 256, 0, s>>>(dh, pre, n_rows, F, act, dAU);
+}
+
+void launch_bwd_unpermute(const float* dXp, const int32_t* inv_pos, const float* extra, int64_t T, int d, int k,
+                          float* dx32, hipStream_t s) {
+    bwd_unpermute_kernel<<<blocks_for(T * d), 256, 0, s>>>(dXp, inv_pos, extra, T, d, k, dx32);
+}
+
+void launch_bwd_colsum(int dtype, const void* src, const int32_t* offsets, int e_begin, int G, int ncols, float* out,
+                       hipStream_t s) {
+    dim3 grid(blocks_for(ncols), (unsigned)G);
+    if (dtype == MOE_BF16) bwd_colsum_kernel<true><<<grid, 256, 0, s>>>(src, offsets, e_begin, ncols, out);
+    else bwd_colsum_kernel<false><<<grid, 256, 0, s>>>(src, offsets, e_begin, ncols, out);
+}
+
+void launch_bwd_gate(const float* logits, const int32_t* topk_idx, const float* dg, const int32_t* counts,
+                     float aux_coef, int64_t T, int E, int k, int score, int renorm, float* dl, hipStream_t s) {
+    const unsigned nb = (unsigned)((T + 3) / 4);
+#define MOE_GATE(EPL) bwd_gate_kernel<EPL><<<nb, 256, 0, s>>>(logits, topk_idx, dg, counts, aux_coef, T, E, k, score, renorm, dl)
+    if (E <= 64) MOE_GATE(1);
+    else if (E <= 128) MOE_GATE(2);
+    else if (E <= 256) MOE_GATE(4);
+    else if (E <= 512) MOE_GATE(8);
+    else MOE_GATE(16);
+#undef MOE_GATE
+}
+
+size_t bwd_router_partials_bytes(int64_t T, int E, int d) {
+    return (size_t)((T + kRouterChunk - 1) / kRouterChunk) * E * d * sizeof(float);
+}
+
+void launch_bwd_router(int dtype, const float* dl, const void* x, const float* w_r, const float* dx32, int64_t T,
+                       int E, int d, float* partials, float* dw_r, void* dx, hipStream_t s) {
+    const int nchunks = (int)((T + kRouterChunk - 1) / kRouterChunk);
+    dim3 gw(blocks_for(d), (unsigned)((E + 7) / 8), (unsigned)nchunks);
+    const int64_t n = (int64_t)E * d;
+    if (dtype == MOE_BF16) {
+        bwd_router_wgrad_kernel<true><<<gw, 256, 0, s>>>(dl, x, T, E, d, partials);
+        bwd_router_dgrad_kernel<true><<<blocks_for(T * d), 256, 0, s>>>(dx32, dl, w_r, T, E, d, dx);
+    } else {
+        bwd_router_wgrad_kernel<false><<<gw, 256, 0, s>>>(dl, x, T, E, d, partials);
+        bwd_router_dgrad_kernel<false><<<blocks_for(T * d), 256, 0, s>>>(dx32, dl, w_r, T, E, d, dx);
+    }
+    bwd_router_reduce_kernel<<<blocks_for(n), 256, 0, s>>>(partials, nchunks, n, dw_r);
+}
+
+}  // namespace moe

@@ -159,6 +159,35 @@ FwdWs fwd_ws(const moe_shape* s) {
     return w;
 }
 
+// backward: intermediates of the chain rule (rows = T*k bound of the permuted buffer)
+struct BwdWs {
+    size_t dg, dYp, pre, h, dh, dAU, dXp, dx32, dl, partials, rpart, pre_s, hs, dhs, dAUs, dXs, bytes;
+};
+BwdWs bwd_ws(const moe_shape* s) {
+    BwdWs w;
+    Carver c;
+    const size_t A = (size_t)s->T * s->k, eb = elem_bytes(s), T = (size_t)s->T;
+    const size_t d = s->d_model, F = s->d_ff, n_in = s->act == MOE_SWIGLU ? 2 * F : F, Fs = s->d_ff_shared;
+    w.dg = c.take(A * 4);
+    w.dYp = c.take(A * d * eb);
+    w.pre = c.take(A * n_in * eb);
+    w.h = c.take(A * F * eb);
+    w.dh = c.take(A * F * 4);
+    w.dAU = c.take(A * n_in * eb);
+    w.dXp = c.take(A * d * 4);
+    w.dx32 = c.take(T * d * 4);
+    w.dl = c.take(T * s->E * 4);
+    w.partials = c.take(moe::gemm_partials_bytes(s->dtype));
+    w.rpart = c.take(moe::bwd_router_partials_bytes(s->T, s->E, s->d_model));
+    w.pre_s = c.take(T * 2 * Fs * eb);
+    w.hs = c.take(T * Fs * eb);
+    w.dhs = c.take(T * Fs * 4);
+    w.dAUs = c.take(T * 2 * Fs * eb);
+    w.dXs = c.take(Fs ? T * d * 4 : 0);
+    w.bytes = c.off;
+    return w;
+}
+
 template <typename T>
 inline T* at(void* ws, size_t off) {
     return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
@@ -264,6 +293,103 @@ void do_shared(const moe_shape* s, const void* x, const void* ws_in, const void*
                              s->d_model, s->d_ff_shared, partials, st);
 }
 
+// C(m, n) = sum_k A(m, k) B(n, k) on layer-dtype operands (fp32 C), dispatched on the dtype.
+struct Sg {
+    const void* A;
+    int64_t sam, sak;
+    const void* B;
+    int64_t sbn, sbk, b_group;
+    float* C;
+    int64_t scm, c_group;
+    int64_t M, N, K;
+    const int32_t* offsets;
+    int G, mode;
+};
+void run_sg(const moe_shape* s, const Sg& g, int64_t max_rows, hipStream_t st) {
+    if (s->dtype == MOE_BF16) {
+        moe::SgArgs a{static_cast<const uint16_t*>(g.A), static_cast<const uint16_t*>(g.B), g.C, g.sam, g.sak, g.sbn,
+                      g.sbk, g.scm, g.b_group, g.c_group, g.M, g.N, g.K, g.offsets, 0, g.G, g.mode};
+        moe::launch_sg_gemm_bf16(a, max_rows, st);
+    } else {
+        moe::SgArgsF a{static_cast<const float*>(g.A), static_cast<const float*>(g.B), g.C, g.sam, g.sak, g.sbn,
+                       g.sbk, g.scm, g.b_group, g.c_group, g.M, g.N, g.K, g.offsets, 0, g.G, g.mode};
+        moe::launch_sg_gemm_f32(a, max_rows, st);
+    }
+}
+
+struct BwdIn {
+    const void *x, *w_in, *b_in, *w_out, *b_out, *ws_in, *ws_out, *x_perm, *y_perm, *dy;
+    const float *w_router, *logits, *topk_w;
+    const int32_t *topk_idx, *counts, *offsets, *inv_pos;
+    float aux_coef;
+};
+struct BwdOut {
+    void* dx;
+    float *dw_router, *dw_in, *db_in, *dw_out, *db_out, *dws_in, *dws_out, *dlogits;
+};
+
+void do_backward(const moe_shape* s, const BwdIn& in, const BwdOut& out, void* ws, hipStream_t st) {
+    const BwdWs w = bwd_ws(s);
+    const int64_t T = s->T, A = s->T * s->k, d = s->d_model, F = s->d_ff, E = s->E;
+    const int64_t n_in = s->act == MOE_SWIGLU ? 2 * F : F, Fs = s->d_ff_shared;
+    const int dt = s->dtype;
+    float* dg = at<float>(ws, w.dg);
+    void* dYp = at<void>(ws, w.dYp);
+    void* pre = at<void>(ws, w.pre);
+    void* h = at<void>(ws, w.h);
+    float* dh = at<float>(ws, w.dh);
+    void* dAU = at<void>(ws, w.dAU);
+    float* dXp = at<float>(ws, w.dXp);
+    float* dx32 = at<float>(ws, w.dx32);
+    float* dl = out.dlogits ? out.dlogits : at<float>(ws, w.dl);
+    float* partials = partials_of(ws, w.partials, s);
+    // combine: gate gradients and the gate-scaled output gradient per permuted row
+    moe::launch_bwd_combine(dt, in.dy, in.y_perm, in.inv_pos, in.topk_w, T, (int)d, s->k, dg, dYp, st);
+    // recompute the pre-activations and h of every expert
+    const moe::GemmPlan p = moe::plan_gemm(dt, A / E, (int)n_in, (int)d);
+    moe::launch_grouped_gemm(dt, moe::EPI_BIAS, p.bm, in.x_perm, in.w_in, in.b_in, pre, in.offsets, 0, (int)E, A, 0,
+                             (int)n_in, (int)d, partials, st);
+    moe::launch_bwd_act_fwd(dt, pre, A, (int)F, s->act, h, st);
+    // dh = dY W_out, then the activation backward
+    run_sg(s, Sg{dYp, d, 1, in.w_out, 1, F, d * F, dh, F, 0, 0, F, d, in.offsets, (int)E, moe::SG_ROWS}, A, st);
+    moe::launch_bwd_act_bwd(dt, dh, pre, A, (int)F, s->act, dAU, st);
+    // dX = dAU W_in
+    run_sg(s, Sg{dAU, n_in, 1, in.w_in, 1, d, n_in * d, dXp, d, 0, 0, d, n_in, in.offsets, (int)E, moe::SG_ROWS}, A,
+           st);
+    // weight gradients: K runs over each expert's rows
+    run_sg(s, Sg{dYp, 1, d, h, 1, F, 0, out.dw_out, F, d * F, d, F, 0, in.offsets, (int)E, moe::SG_KSPLIT}, A, st);
+    run_sg(s, Sg{dAU, 1, n_in, in.x_perm, 1, d, 0, out.dw_in, d, n_in * d, n_in, d, 0, in.offsets, (int)E,
+                 moe::SG_KSPLIT},
+           A, st);
+    if (out.db_out) moe::launch_bwd_colsum(dt, dYp, in.offsets, 0, (int)E, (int)d, out.db_out, st);
+    if (out.db_in) moe::launch_bwd_colsum(dt, dAU, in.offsets, 0, (int)E, (int)F, out.db_in, st);
+    // shared expert (gate 1, input x, output gradient dy)
+    float* dXs = nullptr;
+    if (Fs > 0) {
+        void* pre_s = at<void>(ws, w.pre_s);
+        void* hs = at<void>(ws, w.hs);
+        float* dhs = at<float>(ws, w.dhs);
+        void* dAUs = at<void>(ws, w.dAUs);
+        dXs = at<float>(ws, w.dXs);
+        const moe::GemmPlan ps = moe::plan_gemm(dt, T, (int)(2 * Fs), (int)d);
+        moe::launch_grouped_gemm(dt, moe::EPI_BIAS, ps.bm, in.x, in.ws_in, nullptr, pre_s, nullptr, 0, 1, T, T,
+                                 (int)(2 * Fs), (int)d, partials, st);
+        moe::launch_bwd_act_fwd(dt, pre_s, T, (int)Fs, MOE_SWIGLU, hs, st);
+        run_sg(s, Sg{in.dy, d, 1, in.ws_out, 1, Fs, 0, dhs, Fs, 0, T, Fs, d, nullptr, 1, moe::SG_DENSE}, T, st);
+        moe::launch_bwd_act_bwd(dt, dhs, pre_s, T, (int)Fs, MOE_SWIGLU, dAUs, st);
+        run_sg(s, Sg{dAUs, 2 * Fs, 1, in.ws_in, 1, d, 0, dXs, d, 0, T, d, 2 * Fs, nullptr, 1, moe::SG_DENSE}, T, st);
+        run_sg(s, Sg{in.dy, 1, d, hs, 1, Fs, 0, out.dws_out, Fs, 0, d, Fs, T, nullptr, 1, moe::SG_DENSE}, T, st);
+        run_sg(s, Sg{dAUs, 1, 2 * Fs, in.x, 1, d, 0, out.dws_in, d, 0, 2 * Fs, d, T, nullptr, 1, moe::SG_DENSE}, T,
+               st);
+    }
+    moe::launch_bwd_unpermute(dXp, in.inv_pos, dXs, T, (int)d, s->k, dx32, st);
+    // router: logit gradient through the gates (+ balancing term), then dW_r and dx
+    moe::launch_bwd_gate(in.logits, in.topk_idx, dg, in.counts, in.aux_coef, T, (int)E, s->k, s->score, s->renorm, dl,
+                         st);
+    moe::launch_bwd_router(dt, dl, in.x, in.w_router, dx32, T, (int)E, (int)d, at<float>(ws, w.rpart), out.dw_router,
+                           out.dx, st);
+}
+
 #define MOE_REQUIRE(cond)                       \
     do {                                        \
         if (!(cond)) return MOE_ERR_INVALID_ARG; \
@@ -288,6 +414,7 @@ int moe_workspace_bytes(const moe_shape* shape, int stage, size_t* bytes) {
         case MOE_STAGE_FORWARD: *bytes = fwd_ws(shape).bytes; break;
         case MOE_STAGE_EXPERT: *bytes = expert_ws(shape).bytes; break;
         case MOE_STAGE_ROUTE_NOISY: *bytes = route_noisy_ws(shape).bytes; break;
+        case MOE_STAGE_BACKWARD: *bytes = bwd_ws(shape).bytes; break;
         default: return MOE_ERR_INVALID_ARG;
     }
     return MOE_OK;
@@ -460,6 +587,37 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router, co
     }
     moe::launch_combine(shape->dtype, at<void>(ws, w.y_perm), inv_pos, gw, ys, y, shape->T, shape->d_model, shape->k,
                         st);
+    return launched();
+}
+
+int moe_backward(const moe_shape* shape, const void* x, const float* w_router, const void* w_in, const void* b_in,
+                 const void* w_out, const void* b_out, const void* ws_in, const void* ws_out, const float* logits,
+                 const int32_t* topk_idx, const float* topk_w, const int32_t* counts, const int32_t* offsets,
+                 const int32_t* inv_pos, const void* x_perm, const void* y_perm, const void* dy, float aux_coef,
+                 void* dx, float* dw_router, float* dw_in, float* db_in, float* dw_out, float* db_out,
+                 float* dws_in, float* dws_out, float* dlogits, void* ws, size_t ws_bytes, moe_stream_t stream) {
+    const int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    MOE_REQUIRE(ok_ptr(x) && ok_ptr(w_router) && ok_ptr(w_in) && ok_ptr(w_out) && ok_ptr(logits) && ok_ptr(topk_idx) &&
+                ok_ptr(topk_w) && ok_ptr(offsets) && ok_ptr(inv_pos) && ok_ptr(x_perm) && ok_ptr(y_perm) &&
+                ok_ptr(dy));
+    MOE_REQUIRE(ok_ptr(dx) && ok_ptr(dw_router) && ok_ptr(dw_in) && ok_ptr(dw_out) && ok_opt(dlogits) && ok_opt(ws));
+    MOE_REQUIRE(ok_opt(b_in) && ok_opt(b_out) && ok_opt(db_in) && ok_opt(db_out) && ok_opt(counts));
+    MOE_REQUIRE(std::isfinite(aux_coef));
+    if (aux_coef != 0.f) MOE_REQUIRE(counts != nullptr);
+    if (shape->act == MOE_SWIGLU && (b_in != nullptr || b_out != nullptr)) return MOE_ERR_INVALID_ARG;
+    // a bias gradient exactly when the bias exists
+    MOE_REQUIRE((b_in == nullptr) == (db_in == nullptr) && (b_out == nullptr) == (db_out == nullptr));
+    if (shape->d_ff_shared > 0) MOE_REQUIRE(ok_ptr(ws_in) && ok_ptr(ws_out) && ok_ptr(dws_in) && ok_ptr(dws_out));
+    else MOE_REQUIRE(ws_in == nullptr && ws_out == nullptr && dws_in == nullptr && dws_out == nullptr);
+    const BwdWs w = bwd_ws(shape);
+    if (ws_bytes < w.bytes || ws == nullptr) return MOE_ERR_WORKSPACE;
+    if (shape->T == 0) return MOE_OK;
+    (void)hipGetLastError();
+    const BwdIn in{x, w_in, b_in, w_out, b_out, ws_in, ws_out, x_perm, y_perm, dy, w_router, logits, topk_w,
+                   topk_idx, counts, offsets, inv_pos, aux_coef};
+    const BwdOut out{dx, dw_router, dw_in, db_in, dw_out, db_out, dws_in, dws_out, dlogits};
+    do_backward(shape, in, out, ws, static_cast<hipStream_t>(stream));
     return launched();
 }
 

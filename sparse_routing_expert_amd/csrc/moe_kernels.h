@@ -65,4 +65,59 @@ size_t gemm_partials_bytes(int dtype);
 void launch_combine(int dtype, const void* y_perm, const int32_t* inv_pos, const float* topk_w,
                     const void* y_shared, void* y, int64_t T, int d, int k, hipStream_t s);
 
+// ---- backward ---------------------------------------------------------------------------
+// Strided grouped GEMM C(m, n) = sum_k A(m, k) B(n, k); A(m, k) at A[m*sam + k*sak], B(n, k) at
+// B[n*sbn + k*sbk], C(m, n) at C[m*scm + n] (fp32). Each operand is contiguous along k (s?k == 1) or
+// along its row index (sam == 1 / sbn == 1).
+//   SG_ROWS:   group g = expert e_begin + g owns rows offsets[e_begin+g] .. offsets[e_begin+g+1] of
+//              A and C; B advances b_group elements per group; N, K fixed (M unused)
+//   SG_KSPLIT: group g sums k over offsets[e_begin+g] .. offsets[e_begin+g+1]; C advances c_group
+//              elements per group; M, N fixed
+//   SG_DENSE:  one group, M x N, k in [0, K)
+enum SgMode { SG_ROWS = 0, SG_KSPLIT = 1, SG_DENSE = 2 };
+struct SgArgs {
+    const uint16_t* A;
+    const uint16_t* B;
+    float* C;
+    int64_t sam, sak, sbn, sbk, scm, b_group, c_group;
+    int64_t M, N, K;
+    const int32_t* offsets;
+    int e_begin, G, mode;
+};
+struct SgArgsF {
+    const float* A;
+    const float* B;
+    float* C;
+    int64_t sam, sak, sbn, sbk, scm, b_group, c_group;
+    int64_t M, N, K;
+    const int32_t* offsets;
+    int e_begin, G, mode;
+};
+// max_rows: total rows of the grouped buffer (SG_ROWS grid bound)
+void launch_sg_gemm_bf16(const SgArgs& a, int64_t max_rows, hipStream_t s);
+void launch_sg_gemm_f32(const SgArgsF& a, int64_t max_rows, hipStream_t s);
+
+// dg[t, j] = <dy[t], y_perm[row]>, dYp[row] = topk_w[t, j] * dy[t] for kept slots (dg = 0 if dropped)
+void launch_bwd_combine(int dtype, const void* dy, const void* y_perm, const int32_t* inv_pos, const float* topk_w,
+                        int64_t T, int d, int k, float* dg, void* dYp, hipStream_t s);
+// h = act(pre): SwiGLU pre [rows, 2F] -> silu(a) * u; GELU pre [rows, F] -> gelu(z)
+void launch_bwd_act_fwd(int dtype, const void* pre, int64_t n_rows, int F, int act, void* h, hipStream_t s);
+// dAU [rows, n_in] from dh [rows, F] fp32 and pre
+void launch_bwd_act_bwd(int dtype, const float* dh, const void* pre, int64_t n_rows, int F, int act, void* dAU,
+                        hipStream_t s);
+// dx32[t] = sum over kept slots of dXp[inv_pos[t*k + j]] (+ extra[t])
+void launch_bwd_unpermute(const float* dXp, const int32_t* inv_pos, const float* extra, int64_t T, int d, int k,
+                          float* dx32, hipStream_t s);
+// out[g][c] = sum of src rows offsets[e_begin+g] .. offsets[e_begin+g+1], column c
+void launch_bwd_colsum(int dtype, const void* src, const int32_t* offsets, int e_begin, int G, int ncols, float* out,
+                       hipStream_t s);
+// router logit gradient [T, E] from the gate gradients (+ the balancing term when aux_coef != 0)
+void launch_bwd_gate(const float* logits, const int32_t* topk_idx, const float* dg, const int32_t* counts,
+                     float aux_coef, int64_t T, int E, int k, int score, int renorm, float* dl, hipStream_t s);
+// dw_r = dl^T x (token chunks of kRouterChunk summed in order through `partials`), dx = dx32 + dl W_r
+constexpr int kRouterChunk = 256;
+size_t bwd_router_partials_bytes(int64_t T, int E, int d);
+void launch_bwd_router(int dtype, const float* dl, const void* x, const float* w_r, const float* dx32, int64_t T,
+                       int E, int d, float* partials, float* dw_r, void* dx, hipStream_t s);
+
 }  // namespace moe

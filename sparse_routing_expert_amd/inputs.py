@@ -102,7 +102,7 @@ CONFIGS: Dict[str, LayerConfig] = {
 }
 
 # Tensor ids of the seed streams.
-_X, _WR, _BIAS, _WIN, _BIN, _WOUT, _BOUT, _SIN, _SOUT, _PERM, _WNOISE, _NOISE = range(12)
+_X, _WR, _BIAS, _WIN, _BIN, _WOUT, _BOUT, _SIN, _SOUT, _PERM, _WNOISE, _NOISE, _DY = range(13)
 X_CHUNK_ROWS = 64  # token rows drawn per seed (so prefixes of x are length-independent)
 
 ZIPF_S = 1.2  # popularity exponent of the Qwen3-shaped layer
@@ -279,6 +279,17 @@ def gen_noisy_router(cfg: LayerConfig, device="cpu", seed: int = 0, T: Optional[
         c1 = min(T, c0 + 64)
         n[c0:c1] = _normal((c1 - c0, cfg.E), 1.0, device, torch.float32, seed, cfg.layer_id, _NOISE, c0 // 64)
     return w, n
+
+
+def gen_dy(cfg: LayerConfig, device="cpu", seed: int = 0, T: Optional[int] = None) -> torch.Tensor:
+    """Output gradient dy ~ N(0,1) [T, d] in the layer dtype (64-token chunks, like x)."""
+    T = cfg.T if T is None else T
+    out = torch.empty((T, cfg.d), dtype=cfg.torch_dtype, device=device)
+    for c0 in range(0, T, X_CHUNK_ROWS):
+        c1 = min(T, c0 + X_CHUNK_ROWS)
+        out[c0:c1] = _normal((c1 - c0, cfg.d), 1.0, device, cfg.torch_dtype, seed, cfg.layer_id, _DY,
+                             c0 // X_CHUNK_ROWS)
+    return out
 
 
 def gen_expert(cfg: LayerConfig, e: int, device="cpu", seed: int = 0):

@@ -113,3 +113,33 @@ class MoeLayer:
     def update_bias(self, gamma: float = 1e-3, counts=None):
         """One aux-loss-free balancing step on the layer's selection bias (in place)."""
         L.moe_update_bias(self.shape, self.counts if counts is None else counts, gamma, self.t["sel_bias"])
+
+    def alloc_grads(self) -> Dict[str, Optional[torch.Tensor]]:
+        """fp32 gradient buffers of the layer's parameters, dx in the layer dtype."""
+        cfg, dev, f32 = self.cfg, self.dev, torch.float32
+        t = self.t
+        n_in = t["w_in"].shape[1]
+        g = {
+            "dx": torch.empty((self.T, cfg.d), dtype=cfg.torch_dtype, device=dev),
+            "dw_r": torch.empty((cfg.E, cfg.d), dtype=f32, device=dev),
+            "dw_in": torch.empty((cfg.E, n_in, cfg.d), dtype=f32, device=dev),
+            "db_in": torch.empty((cfg.E, cfg.F), dtype=f32, device=dev) if t["b_in"] is not None else None,
+            "dw_out": torch.empty((cfg.E, cfg.d, cfg.F), dtype=f32, device=dev),
+            "db_out": torch.empty((cfg.E, cfg.d), dtype=f32, device=dev) if t["b_out"] is not None else None,
+            "dws_in": torch.empty((2 * cfg.Fs, cfg.d), dtype=f32, device=dev) if cfg.Fs else None,
+            "dws_out": torch.empty((cfg.d, cfg.Fs), dtype=f32, device=dev) if cfg.Fs else None,
+            "dlogits": torch.empty((self.T, cfg.E), dtype=f32, device=dev),
+        }
+        return g
+
+    def backward(self, dy, grads=None, aux_coef: float = 0.0, with_dlogits=True):
+        """Gradients of the layer for output gradient dy, from the saved routing (self.logits, topk_idx,
+        topk_w, counts), permutation (offsets, inv_pos, x_perm) and expert outputs (y_perm)."""
+        t = self.t
+        g = self.alloc_grads() if grads is None else grads
+        L.moe_backward(self.shape, t["x"], t["w_r"], t["w_in"], t["b_in"], t["w_out"], t["b_out"], t["ws_in"],
+                       t["ws_out"], self.logits, self.topk_idx, self.topk_w, self.counts, self.offsets, self.inv_pos,
+                       self.x_perm, self.y_perm, dy, aux_coef, g["dx"], g["dw_r"], g["dw_in"], g["db_in"],
+                       g["dw_out"], g["db_out"], g["dws_in"], g["dws_out"], g["dlogits"] if with_dlogits else None,
+                       self.ws(L.MOE_STAGE_BACKWARD))
+        return g

@@ -11,6 +11,12 @@ the GPU's selection.
 FFN and layer: per-row relative L2 error, maximum over rows, <= 1e-4 (fp32 layers) or 2e-2
 (bf16 layers), with the oracle re-run on the GPU's selection (so ambiguous tokens compare like
 with like).
+Backward: each gradient is cut into blocks (a token's row of dx and dlogits, an expert's slice of
+the weight gradients); a block's L2 error must be <= the same tolerance times the larger of its own
+norm and the median block norm. The median floor covers blocks whose value is a small difference
+of large terms (a token whose two gate gradients nearly cancel): their error scales with the terms,
+not with the difference. Blocks the oracle makes exactly zero (an expert without rows) must be
+exactly zero.
 """
 from __future__ import annotations
 
@@ -130,4 +136,22 @@ def oracle_layer_on_gpu_routing(cfg, L):
 def check_layer(cfg, y_gpu, y_ref):
     err = R.rel_l2_per_row(np64(y_gpu), y_ref)
     assert err.max() <= tol_for(cfg), f"layer max per-token rel-L2 {err.max():.3g}"
+    return float(err.max())
+
+
+def grad_err(got, ref, blocks: int, what: str, tol: float) -> float:
+    """Block-wise gradient comparison (see the module notes); returns the largest block error."""
+    g = np64(got).reshape(blocks, -1)
+    r = np64(ref).reshape(blocks, -1)
+    assert np.isfinite(g).all(), f"{what}: non-finite values"
+    num = np.linalg.norm(g - r, axis=1)
+    den = np.linalg.norm(r, axis=1)
+    zero = den == 0.0
+    assert (num[zero] == 0.0).all(), f"{what}: blocks {np.nonzero(zero & (num > 0))[0][:8]} must be exactly zero"
+    if zero.all():
+        return 0.0
+    floor = float(np.median(den[~zero]))
+    err = num / np.maximum(den, floor)
+    worst = int(np.argmax(err))
+    assert err.max() <= tol, f"{what}: block {worst} rel err {err.max():.3g} (tol {tol})"
     return float(err.max())

@@ -240,6 +240,68 @@ def test_forward_rejections(lib):
               None, FAKE, n2, None) == L.MOE_ERR_INVALID_ARG  # shared weights without a shared expert
 
 
+def test_backward_rejections(lib):
+    s = good_shape()
+    rc, n = ws_bytes(s, L.MOE_STAGE_BACKWARD)
+    # at least dY, the recomputed pre-activation [T*k, 2F], h, dh (fp32) and dX (fp32)
+    A = 128 * 2
+    assert rc == 0 and n >= A * (256 * 2 + 256 * 2 + 128 * 2 + 128 * 4 + 256 * 4)
+    f = lib.moe_backward
+    # shape, x, w_r, w_in, b_in, w_out, b_out, ws_in, ws_out, logits, idx, topk_w, counts, offsets, inv_pos,
+    # x_perm, y_perm, dy, aux_coef, dx, dw_r, dw_in, db_in, dw_out, db_out, dws_in, dws_out, dlogits, ws, bytes, st
+    good = [ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, None, None, None, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+            FAKE, FAKE, FAKE, 0.0, FAKE, FAKE, FAKE, None, FAKE, None, None, None, None, FAKE, n, None]
+    for i in (1, 2, 3, 5, 9, 10, 11, 13, 14, 15, 16, 17, 19, 20, 21, 23):  # required pointers
+        bad = list(good)
+        bad[i] = None
+        assert f(*bad) == L.MOE_ERR_INVALID_ARG, i
+    for i in (1, 17, 27):
+        bad = list(good)
+        bad[i] = MISALIGNED
+        assert f(*bad) == L.MOE_ERR_INVALID_ARG, i
+    bad = list(good)
+    bad[18] = 0.01  # balancing term without counts
+    assert f(*bad) == L.MOE_ERR_INVALID_ARG
+    bad[18] = float("nan")
+    bad[12] = FAKE
+    assert f(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(good)
+    bad[4] = FAKE  # SwiGLU has no biases
+    bad[22] = FAKE
+    assert f(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(good)
+    bad[22] = FAKE  # a bias gradient without the bias
+    assert f(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(good)
+    bad[25] = FAKE  # shared gradients without a shared expert
+    assert f(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(good)
+    bad[29] = n - 1
+    assert f(*bad) == L.MOE_ERR_WORKSPACE
+    bad = list(good)
+    bad[28] = None
+    assert f(*bad) == L.MOE_ERR_WORKSPACE
+    # GELU layer: biases and their gradients go together
+    g = good_shape(act="gelu")
+    ng = ws_bytes(g, L.MOE_STAGE_BACKWARD)[1]
+    gg = list(good)
+    gg[0], gg[29] = ctypes.byref(g), ng
+    gg[4] = FAKE  # b_in without db_in
+    assert f(*gg) == L.MOE_ERR_INVALID_ARG
+    # shared expert: its weights and gradients are required
+    sh = good_shape(d_ff_shared=128)
+    nsh = ws_bytes(sh, L.MOE_STAGE_BACKWARD)[1]
+    assert nsh > n
+    gs = list(good)
+    gs[0], gs[29] = ctypes.byref(sh), nsh
+    gs[7], gs[8], gs[25] = FAKE, FAKE, FAKE  # dws_out missing
+    assert f(*gs) == L.MOE_ERR_INVALID_ARG
+    z = list(good)
+    z[0] = ctypes.byref(good_shape(T=0))
+    z[29] = ws_bytes(good_shape(T=0), L.MOE_STAGE_BACKWARD)[1]
+    assert f(*z) == L.MOE_OK
+
+
 def test_binding_raises_on_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "nope.so"))
     monkeypatch.setattr(L, "_lib", None)
