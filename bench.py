@@ -188,6 +188,7 @@ def main():
         "capacity_permute": next_rows["capacity_permute"],
         "bias_update": next_rows["bias_update"],
         "noisy_route": next_rows["noisy_route"],
+        "backward": next_rows["backward"],
         "input_gen_s": round(gen_s, 2),
     }
     print(json.dumps(out), flush=True)
@@ -237,12 +238,28 @@ def next_row_timings(cfg, L, flush, stream, reps):
     w_n, noise = I.gen_noisy_router(cfg, device=L.dev)
     ms_n = timed(lambda: L.route_noisy(w_n, noise, with_logits=False, with_stats=False))
     nb = T * d * b + 2 * E * d * 4 + T * E * 4 + T * k * 8 + E * 4
-    L.route(with_logits=False)
+    L.route(with_logits=True)
     L.permute()  # back to the plain routing and dropless permutation the other stages use
+    L.ffn()
+    if cfg.Fs:
+        L.shared()
     torch.cuda.synchronize()
+    # layer backward (dy ~ N(0,1), balancing coefficient 0.01): the recomputed up projection, two
+    # dgrad and two wgrad products per expert, plus the shared expert's five
+    dy = I.gen_dy(cfg, device=L.dev)
+    grads = L.alloc_grads()
+    L.backward(dy, grads, aux_coef=0.01)
+    torch.cuda.synchronize()
+    ms_bw = timed(lambda: L.backward(dy, grads, aux_coef=0.01))
+    rows = int(L.offsets[-1].item())
+    n_in = cfg.n_in
+    fl = 2.0 * rows * d * (3 * n_in + 2 * cfg.F) + 16.0 * T * d * cfg.Fs + 4.0 * T * E * d
+    del grads
     return {"capacity_permute": perm,
             "bias_update": {"ms": round(ms_b, 5), "bytes": E * 12, "note": "E-length, launch-bound"},
-            "noisy_route": {"ms": round(ms_n, 5), "bytes": nb, "GB/s": round(nb / (ms_n * 1e-3) / 1e9, 1)}}
+            "noisy_route": {"ms": round(ms_n, 5), "bytes": nb, "GB/s": round(nb / (ms_n * 1e-3) / 1e9, 1)},
+            "backward": {"ms": round(ms_bw, 4), "flops": fl, "TFLOP/s": round(fl / (ms_bw * 1e-3) / 1e12, 1),
+                         "frac_mfma_bf16": round(fl / (ms_bw * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}}
 
 
 def vendor_gemm(cfg, L, stream):

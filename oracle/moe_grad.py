@@ -194,3 +194,64 @@ def layer_backward(x, w_r, get_expert, k: int, act: str, score: str, renorm: boo
     dw_r = dl.T @ x
     dx = dx + dl @ w_r
     return BackwardResult(dx, dw_r, dw_in, db_in, dw_out, db_out, dws_in, dws_out, dl, dg, fwd.y)
+
+
+def tokens_backward(x_rows, w_r, idx_rows: np.ndarray, logits_rows: np.ndarray, get_expert, act: str, score: str,
+                    renorm: bool, ws_in, ws_out, dy_rows, dl_extra: Optional[np.ndarray] = None):
+    """dx and the router-logit gradient of a subset of tokens, given their selection and logits.
+
+    Without capacity and with the balancing term's f held constant, token t's gradients depend only
+    on its own x, dy and routing, so sampled tokens of a large layer are evaluated directly: for each
+    expert the sample uses, the FFN and its backward on the sampled rows routed to it (one expert
+    converted to float64 at a time). dl_extra [S, E] is added to the logit gradient before it
+    reaches dx (the balancing term's rows, which need the whole layer's counts)."""
+    x_rows, dy_rows, w_r = R.f64(x_rows), R.f64(dy_rows), R.f64(w_r)
+    S, k = idx_rows.shape
+    g = R.gates(logits_rows, idx_rows, score, renorm)
+    dg = np.zeros((S, k))
+    dx = np.zeros(x_rows.shape)
+    for e in np.unique(idx_rows):
+        rows, slots = np.nonzero(idx_rows == e)
+        wi, bi, wo, bo = get_expert(int(e))
+        Y = R.expert_ffn(x_rows[rows], wi, bi, wo, bo, act)
+        dg[rows, slots] = np.sum(dy_rows[rows] * Y, axis=1)
+        dX = expert_backward(x_rows[rows], wi, bi, wo, bo, act, g[rows, slots][:, None] * dy_rows[rows])[0]
+        np.add.at(dx, rows, dX)
+    if ws_in is not None:
+        dx = dx + expert_backward(x_rows, R.f64(ws_in), None, R.f64(ws_out), None, "swiglu", dy_rows)[0]
+    dl = gate_backward(logits_rows, idx_rows, score, renorm, dg)
+    if dl_extra is not None:
+        dl = dl + dl_extra
+    return dx + dl @ w_r, dl
+
+
+def expert_backward_features(X, w_in, b_in, w_out, b_out, act: str, dY, feats: np.ndarray):
+    """expert_backward's weight gradients restricted to the hidden features `feats`.
+
+    Hidden feature f enters the expert only through row f of W1 (rows f and F + f of [Wg; Wu]),
+    b1[f] and column f of W2, so the gradients of those entries need only that feature's
+    pre-activation over the expert's rows. Returns (dw_in rows: [len(feats), d] for GELU, gate rows
+    then up rows [2 len(feats), d] for SwiGLU; db_in[feats] or None; dw_out[:, feats])."""
+    X, dY = R.f64(X), R.f64(dY)
+    feats = np.asarray(feats)
+    if act == "gelu":
+        z = X @ w_in[feats].T
+        if b_in is not None:
+            z = z + b_in[feats][None, :]
+        h = R.gelu(z)
+        dz = (dY @ w_out[:, feats]) * gelu_grad(z)
+        dw_in = dz.T @ X
+        db_in = dz.sum(axis=0) if b_in is not None else None
+    elif act == "swiglu":
+        F = w_in.shape[0] // 2
+        a = X @ w_in[feats].T
+        u = X @ w_in[F + feats].T
+        h = R.silu(a) * u
+        dh = dY @ w_out[:, feats]
+        da = dh * u * silu_grad(a)
+        du = dh * R.silu(a)
+        dw_in = np.concatenate([da.T @ X, du.T @ X], axis=0)
+        db_in = None
+    else:
+        raise ValueError(act)
+    return dw_in, db_in, dY.T @ h

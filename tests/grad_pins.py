@@ -76,13 +76,17 @@ def check_finite_differences(G, cases=range(10), eps=1e-6, tol=2e-6):
                 assert abs(fd - grad[pos]) <= tol * (1.0 + abs(fd)), (i, name, pos, fd, grad[pos])
 
 
-def _torch_layer(c, idx, capacity, aux_coef, params):
-    """The layer forward in torch ops for a fixed selection idx [T, k]; returns the loss."""
+def _torch_layer(c, idx, capacity, aux_coef, params, keep=None):
+    """The layer forward in torch ops for a fixed selection idx [T, k]; returns the loss (keep, if
+    given, receives the logits with their gradient retained)."""
     x, w_r, w_in, w_out = params["x"], params["w_r"], params["w_in"], params["w_out"]
     b_in, b_out = params.get("b_in"), params.get("b_out")
     T, k = idx.shape
     E = w_r.shape[0]
     l = x @ w_r.T
+    if keep is not None:
+        l.retain_grad()
+        keep["l"] = l
     sel = torch.gather(l, 1, torch.as_tensor(idx))
     if c["score"] == "softmax" and c["renorm"]:
         gts = torch.softmax(sel, dim=1)
@@ -151,7 +155,48 @@ def check_autograd(G, cases=range(12)):
             assert err <= 1e-12 * (1.0 + np.max(np.abs(ref))), (i, n, err)
 
 
+def check_sampled_restrictions(G, cases=range(10)):
+    """tokens_backward on a subset of tokens and expert_backward_features on a subset of hidden
+    features against torch autograd of the whole (dropless) layer: the token rows of dx and of the
+    logit gradient, and the matching rows / columns of each expert's weight gradients."""
+    for i in cases:
+        c = _case(i, seed_base=7000)
+        r = R.route(c["x"], c["w_r"], c["k"], c["score"], c["renorm"], c["sel_bias"])
+        idx, logits = r.idx, r.logits
+        keys = ["x", "w_r", "w_in", "w_out"] + (["b_in", "b_out"] if c["b_in"] is not None else []) + \
+            (["ws_in", "ws_out"] if c["ws_in"] is not None else [])
+        params = {n: torch.tensor(c[n], dtype=torch.float64, requires_grad=True) for n in keys}
+        keep = {}
+        _torch_layer(c, idx, 0, 0.0, params, keep).backward()
+        S = np.array([i % 5, (i + 2) % 5, 4])
+        S = np.unique(S)
+        dx, dl = G.tokens_backward(c["x"][S], c["w_r"], idx[S], logits[S], _getter(c), c["act"], c["score"],
+                                   c["renorm"], c["ws_in"], c["ws_out"], c["dy"][S])
+        for what, mine, ref in (("dx", dx, params["x"].grad.numpy()[S]), ("dl", dl, keep["l"].grad.numpy()[S])):
+            err = np.max(np.abs(mine - ref))
+            assert err <= 1e-12 * (1.0 + np.max(np.abs(ref))), (i, what, err)
+        g = R.gates(logits, idx, c["score"], c["renorm"])
+        F = c["w_out"].shape[2]
+        feats = np.array([i % F])
+        for e in range(c["w_r"].shape[0]):
+            rows, slots = np.nonzero(idx == e)
+            if rows.size == 0:
+                continue
+            wi, bi, wo, bo = _getter(c)(e)
+            dwi, dbi, dwo = G.expert_backward_features(c["x"][rows], wi, bi, wo, bo, c["act"],
+                                                       g[rows, slots][:, None] * c["dy"][rows], feats)
+            gi = params["w_in"].grad.numpy()[e]
+            want_in = gi[feats] if c["act"] == "gelu" else np.concatenate([gi[feats], gi[F + feats]], axis=0)
+            pairs = [("dw_in", dwi, want_in), ("dw_out", dwo, params["w_out"].grad.numpy()[e][:, feats])]
+            if bi is not None:
+                pairs.append(("db_in", dbi, params["b_in"].grad.numpy()[e][feats]))
+            for what, mine, ref in pairs:
+                err = np.max(np.abs(mine - ref))
+                assert err <= 1e-12 * (1.0 + np.max(np.abs(ref))), (i, e, what, err)
+
+
 ALL_GRAD_CHECKS = [
     ("finite_differences", check_finite_differences),
     ("autograd", check_autograd),
+    ("sampled_restrictions", check_sampled_restrictions),
 ]

@@ -34,7 +34,30 @@ MUTANTS = {
     "gate_grad_without_centering": lambda m: setattr(m, "gate_backward", _no_centering(m)),
     "aux_grad_ignored": lambda m: setattr(m, "aux_backward", lambda l, idx, score, coef: np.zeros_like(l)),
     "expert_dw_out_from_pre_activation": lambda m: setattr(m, "expert_backward", _dw_out_wrong(m)),
+    "feature_gate_and_up_rows_swapped": lambda m: setattr(m, "expert_backward_features", _feats_swapped(m)),
+    "tokens_shared_expert_dropped": lambda m: setattr(m, "tokens_backward", _tokens_no_shared(m)),
 }
+
+
+def _feats_swapped(m):
+    orig = m.expert_backward_features
+
+    def f(X, w_in, b_in, w_out, b_out, act, dY, feats):
+        dwi, dbi, dwo = orig(X, w_in, b_in, w_out, b_out, act, dY, feats)
+        n = len(feats)
+        if act == "swiglu":
+            dwi = np.concatenate([dwi[n:], dwi[:n]], axis=0)
+        return dwi, dbi, dwo
+    return f
+
+
+def _tokens_no_shared(m):
+    orig = m.tokens_backward
+
+    def f(x_rows, w_r, idx_rows, logits_rows, get_expert, act, score, renorm, ws_in, ws_out, dy_rows,
+          dl_extra=None):
+        return orig(x_rows, w_r, idx_rows, logits_rows, get_expert, act, score, renorm, None, None, dy_rows, dl_extra)
+    return f
 
 
 def _no_centering(m):
