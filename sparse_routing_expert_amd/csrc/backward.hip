@@ -51,7 +51,8 @@ __device__ __forceinline__ void st_elem(void* p, int64_t i, float v) {
 // Strided grouped GEMM
 // ------------------------------------------------------------------------------------------------
 
-// rows mode: the per-block tile schedule (prefix sums of 128-row tiles per group) in LDS.
+// rows mode: the per-block tile schedule (prefix sums of BM-row tiles per group) in LDS.
+template <int BM>
 __device__ __forceinline__ void sg_schedule(const int32_t* __restrict__ offsets, int e_begin, int G, int* s_ts,
                                             int* s_wave) {
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -60,7 +61,7 @@ __device__ __forceinline__ void sg_schedule(const int32_t* __restrict__ offsets,
     for (int i = 0; i < 4; ++i) {
         const int g = tid * 4 + i;
         n[i] = 0;
-        if (g < G) n[i] = (offsets[e_begin + g + 1] - offsets[e_begin + g] + 127) / 128;
+        if (g < G) n[i] = (offsets[e_begin + g + 1] - offsets[e_begin + g] + BM - 1) / BM;
         sum += n[i];
     }
     int inc = sum;
@@ -83,20 +84,53 @@ __device__ __forceinline__ void sg_schedule(const int32_t* __restrict__ offsets,
     __syncthreads();
 }
 
-__global__ __launch_bounds__(256) void sg_gemm_bf16_kernel(SgArgs p) {
-    constexpr int BM = 128, BN = 128, BK = 32;
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[2][(BM + BN) * BK];
-    __shared__ int s_ts[1025];
-    __shared__ int s_wave[4];
+// LDS element offset of (row R, 16-byte chunk c) inside one stage of 64-byte rows. Rows are permuted
+// within each group of four by bits 3-4 of the row and chunks are XOR-swizzled by bits 2-3, so each
+// quarter-wave access below covers the 64 banks once: 16 lanes reading 16 consecutive rows at one
+// chunk (MFMA fragments), writing 4 consecutive rows x 4 chunks (K-contiguous operand), or writing
+// row 8*mg + i of 4 consecutive mg x 4 chunks (transposed operand).
+__device__ __forceinline__ int sg_lds(int R, int c) {
+    return (((R & ~3) | ((R ^ (R >> 3)) & 3)) << 5) + ((c ^ ((R >> 2) & 3)) << 3);
+}
+
+// Row q of the transpose of an 8 x 8 bf16 block held as 8 rows (k = 0..7) of 8 elements (m = 0..7):
+// the 8 values of k at m = q, packed as 4 dwords of (k = 2j, 2j + 1).
+// (q is a constant after the callers' loops unroll.)
+__device__ __forceinline__ u32x4 sg_tr_row(const u32x4* v, int q) {
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t x = v[2 * j][q >> 1], y = v[2 * j + 1][q >> 1];
+        o[j] = (q & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+    }
+    return o;
+}
+
+// Strided grouped GEMM, bf16 operands, fp32 C. 256 x 256 tiles, four waves of 128 x 128 (4 x 4
+// v_mfma_f32_32x32x16_bf16 tiles), BK = 32, two LDS stages and two register staging sets, loads
+// issued three stages ahead (the register-staged schedule of the forward GEMM). Waves 0-1 stage
+// operand A and waves 2-3 operand B, 8 x 16 bytes per thread and stage. A K-contiguous operand
+// (AK / BK_ true) loads 16 bytes along k of one row; a row-contiguous one loads an 8 x 8 block (8
+// rows of k, 8 consecutive m each) and writes its transpose. Buffer descriptors bound every load:
+// rows past the tile's valid range and k past the group's K read as zero.
+template <bool AK, bool BKC>
+__global__ __launch_bounds__(256, 1) void sg_gemm_bf16_kernel(SgArgs p) {
+    constexpr int BM = 256, BN = 256, BK = 32, TM = 4, TN = 4, NQ = 8;
+    constexpr int STAGE = (BM + BN) * BK;
+    constexpr int STEPS = 16, RNH = 4, RSP = 4;
+    static_assert(STEPS >= 2 * NQ && STEPS >= TM + TN && RSP * RNH == STEPS, "schedule slots");
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * STAGE];
+    int* s_ts = reinterpret_cast<int*>(lds);
+    int* s_wave = s_ts + 1025;
     const int tid = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t tiles_n = (p.N + BN - 1) / BN;
 
-    // ---- tile -> (group, m0, n0), the group's M, K range and bases
+    // ---- tile -> (group, m0, n0), the group's M and K range
     int g = 0;
     int64_t m0 = 0, n0 = 0, M = p.M, kb = 0, ke = p.K, row_base = 0;
     if (p.mode == SG_ROWS) {
-        sg_schedule(p.offsets, p.e_begin, p.G, s_ts, s_wave);
+        sg_schedule<BM>(p.offsets, p.e_begin, p.G, s_ts, s_wave);
         const int64_t lin = blockIdx.x;
         const int64_t total = (int64_t)s_ts[p.G] * tiles_n;
         if (lin >= total) return;  // uniform per block
@@ -112,126 +146,218 @@ __global__ __launch_bounds__(256) void sg_gemm_bf16_kernel(SgArgs p) {
         n0 = (lin % tiles_n) * BN;
         row_base = p.offsets[p.e_begin + g];
         M = p.offsets[p.e_begin + g + 1] - row_base;
+        __syncthreads();  // the schedule shares LDS with the stages
     } else {
         const int64_t tiles_m = (p.M + BM - 1) / BM;
         const int64_t per_group = tiles_m * tiles_n;
         g = (int)(blockIdx.x / per_group);
         if (g >= p.G) return;
-        const int64_t t = blockIdx.x % per_group;
-        m0 = (t / tiles_n) * BM;
-        n0 = (t % tiles_n) * BN;
+        const int64_t tt = blockIdx.x % per_group;
+        m0 = (tt / tiles_n) * BM;
+        n0 = (tt % tiles_n) * BN;
         if (p.mode == SG_KSPLIT) {
             kb = p.offsets[p.e_begin + g];
             ke = p.offsets[p.e_begin + g + 1];
         }
     }
-    const uint16_t* A = p.A + (p.mode == SG_ROWS ? row_base * p.sam : 0);
-    const uint16_t* B = p.B + (int64_t)(p.mode == SG_ROWS ? g : 0) * p.b_group;
+    const int64_t Kext = ke - kb;
+    const int nk = (int)((Kext + BK - 1) / BK);
+    const uint16_t* Ag = p.A + (p.mode == SG_ROWS ? row_base * p.sam : 0);
+    const uint16_t* Bg = p.B + (int64_t)(p.mode == SG_ROWS ? g : 0) * p.b_group;
     float* C = p.C + (p.mode == SG_ROWS ? row_base * p.scm : (int64_t)g * p.c_group);
-    const bool a_kc = p.sak == 1, b_kc = p.sbk == 1;
-    const int64_t nk = (ke - kb + BK - 1) / BK;
 
-    // ---- loads: 2 x 16 bytes of A and of B per thread and stage
-    u32x4 ra[2], rb[2];
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-#define SG_LOAD(R, base, s_row, s_k, kc_layout, rows_valid, kt_)                                           \
-    _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                                        \
-        const int c = h * 256 + tid;                                                                       \
-        R[h] = zero;                                                                                       \
-        if (kc_layout) {                                                                                   \
-            const int r = c >> 2, kc = c & 3;                                                              \
-            const int64_t k = kb + (kt_) * BK + kc * 8;                                                    \
-            if (r < (rows_valid) && k < ke) R[h] = ld16(base + (int64_t)r * (s_row) + k);                  \
-        } else {                                                                                           \
-            const int kk = c >> 4, mc = c & 15;                                                            \
-            const int64_t k = kb + (kt_) * BK + kk;                                                        \
-            if (mc * 8 < (rows_valid) && k < ke) R[h] = ld16(base + (int64_t)mc * 8 + k * (s_k));          \
-        }                                                                                                  \
+    // ---- this thread's operand: element (row r, k) at X0 + r * s_row + k * s_k, r < rows_valid
+    const bool isA = wave < 2;
+    const bool kcont = isA ? AK : BKC;
+    const int t = tid & 127;
+    const uint16_t* X0 = isA ? Ag + m0 * p.sam + kb * p.sak : Bg + n0 * p.sbn + kb * p.sbk;
+    const int64_t s_row = isA ? p.sam : p.sbn, s_k = isA ? p.sak : p.sbk;
+    const int64_t rv64 = isA ? M - m0 : p.N - n0;
+    const int rows_valid = (int)(rv64 < BM ? rv64 : BM);
+    const int lds_row0 = isA ? 0 : BM;
+    // K-contiguous: one descriptor for the tile (rows beyond rows_valid read 0), the stage as soffset.
+    // Row-contiguous: a descriptor per stage covering k in [k0, min(k0 + BK, Kext)).
+    // K-contiguous operands have K a multiple of BK (checked by the host), so only rows need a bound.
+    const __amdgpu_buffer_rsrc_t rs_tile = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)X0, (short)0, kcont && rows_valid > 0 ? (int)(((int64_t)rows_valid - 1) * s_row * 2 + Kext * 2) : 0,
+        0x00020000);
+    int voff[NQ];
+    int wofs[NQ];
+    const int mg = t >> 2, kg = t & 3;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        if (kcont) {
+            const int r = q * 32 + (t >> 2), c = t & 3;
+            voff[q] = (int)(r * s_row * 2) + c * 16;
+            wofs[q] = sg_lds(lds_row0 + r, c);
+        } else {
+            voff[q] = (int)((mg * 8 + (kg * 8 + q) * s_k) * 2);
+            wofs[q] = sg_lds(lds_row0 + mg * 8 + q, kg);
+        }
     }
-#define SG_STORE(R, buf, row0, kc_layout)                                                                  \
-    _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                                        \
-        const int c = h * 256 + tid;                                                                       \
-        uint16_t* L = lds[buf];                                                                            \
-        if (kc_layout) {                                                                                   \
-            const int r = (row0) + (c >> 2), kc = c & 3;                                                   \
-            *reinterpret_cast<u32x4*>(L + r * BK + ((kc ^ swz_b(r)) << 3)) = R[h];                          \
-        } else {                                                                                           \
-            const int kk = c >> 4, mc = c & 15;                                                            \
-            const uint16_t* e8 = reinterpret_cast<const uint16_t*>(&R[h]);                                  \
-            _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                \
-                const int r = (row0) + mc * 8 + i;                                                         \
-                L[r * BK + (((kk >> 3) ^ swz_b(r)) << 3) + (kk & 7)] = e8[i];                              \
-            }                                                                                              \
-        }                                                                                                  \
-    }
-    // A(m, k) at Ab + m * sam + k * sak for m in the tile; B(n, k) likewise
-    const uint16_t* Ab = A + m0 * p.sam;
-    const uint16_t* Bb = B + n0 * p.sbn;
-    const int a_rows = (int)(M - m0 < BM ? M - m0 : BM);
-    const int b_rows = (int)(p.N - n0 < BN ? p.N - n0 : BN);
-    // for a K-contiguous operand the row stride is s_row; for a row-contiguous one the 8-element
-    // chunk runs along the rows and s_k steps k (m-chunks need rows_valid to be a multiple of 8)
     const int wm = wave & 1, wn = wave >> 1;
+    int a_base[TM], a_sw[TM], b_base[TN], b_sw[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int r = wm * 128 + i * 32 + (lane & 31);
+        a_base[i] = sg_lds(r, 0) & ~31;
+        a_sw[i] = (r >> 2) & 3;
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int r = BM + wn * 128 + j * 32 + (lane & 31);
+        b_base[j] = sg_lds(r, 0) & ~31;
+        b_sw[j] = (r >> 2) & 3;
+    }
     const int khalf = lane >> 5;
-    floatx16 acc[2][2];
+    floatx16 acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    bf16x8 fa[2][TM], fb[2][TN];
+    u32x4 stg[2][NQ];
+
+#define SG_LOAD1(set, q, stage)                                                                           \
+    {                                                                                                     \
+        if (kcont) {                                                                                      \
+            stg[set][q] = __builtin_bit_cast(                                                             \
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_tile, voff[q], (stage) * BK * 2, 0));      \
+        } else {                                                                                          \
+            const int64_t k0_ = (int64_t)(stage) * BK;                                                    \
+            const int64_t kr_ = Kext - k0_ < BK ? Kext - k0_ : BK;                                        \
+            const __amdgpu_buffer_rsrc_t rs_ = __builtin_amdgcn_make_buffer_rsrc(                         \
+                (void*)(X0 + k0_ * s_k), (short)0,                                                        \
+                kr_ > 0 && rows_valid > 0 ? (int)(((kr_ - 1) * s_k + rows_valid) * 2) : 0, 0x00020000);   \
+            stg[set][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_, voff[q], 0, 0)); \
+        }                                                                                                 \
+    }
+#define SG_WRITE1(set, q, slot)                                                                           \
+    {                                                                                                     \
+        const u32x4 w_ = kcont ? stg[set][q] : sg_tr_row(stg[set], q);                                    \
+        *reinterpret_cast<u32x4*>(lds + (slot) * STAGE + wofs[q]) = w_;                                   \
+    }
+#define SG_READ(slot, kk, f)                                                                              \
+    {                                                                                                     \
+        const uint16_t* L_ = lds + (slot) * STAGE;                                                        \
+        const int c_ = (kk) * 2 + khalf;                                                                  \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i) fa[f][i] =                                          \
+            *reinterpret_cast<const bf16x8*>(L_ + a_base[i] + ((c_ ^ a_sw[i]) << 3));                     \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j) fb[f][j] =                                          \
+            *reinterpret_cast<const bf16x8*>(L_ + b_base[j] + ((c_ ^ b_sw[j]) << 3));                     \
+    }
+// Iteration kt: phase A = MFMAs on (kt, first K half), reads of (kt, second half), LDS writes of
+// stage kt+1 from staging set SET, then loads of the first half of stage kt+3 into SET (a transposed
+// row needs all eight staged registers, so every write of the set precedes its first reload);
+// barrier; phase B = MFMAs on (kt, second half), reads of (kt+1, first half), loads of the second
+// half of stage kt+3.
+#define SG_STEP(kt_, SET, DO_W, DO_L)                                                                     \
+    {                                                                                                     \
+        const int ktv = (kt_);                                                                            \
+        const uint16_t* L1 = lds + (ktv & 1) * STAGE;                                                     \
+        const int c1 = 2 + khalf;                                                                         \
+        const int wslot = (ktv + 1) & 1;                                                                  \
+        _Pragma("unroll") for (int st = 0; st < STEPS; ++st) {                                            \
+            acc[st / TN][st % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][st / TN], fb[0][st % TN], \
+                                                                            acc[st / TN][st % TN], 0, 0, 0); \
+            if (st < TM) fa[1][st] = *reinterpret_cast<const bf16x8*>(L1 + a_base[st] + ((c1 ^ a_sw[st]) << 3)); \
+            else if (st < TM + TN)                                                                        \
+                fb[1][st - TM] =                                                                          \
+                    *reinterpret_cast<const bf16x8*>(L1 + b_base[st - TM] + ((c1 ^ b_sw[st - TM]) << 3)); \
+            if (st < NQ) {                                                                                \
+                if (DO_W) SG_WRITE1(SET, st, wslot)                                                       \
+            }                                                                                             \
+            if (st >= NQ && st % 2 == 1) {                                                                \
+                if (DO_L) SG_LOAD1(SET, (st - NQ) / 2, ktv + 3)                                           \
+            }                                                                                             \
+            __builtin_amdgcn_sched_barrier(0);                                                            \
+        }                                                                                                 \
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                                 \
+        __builtin_amdgcn_sched_barrier(0);                                                                \
+        const uint16_t* L0 = lds + wslot * STAGE;                                                         \
+        const int c0 = khalf;                                                                             \
+        _Pragma("unroll") for (int st = 0; st < STEPS; ++st) {                                            \
+            acc[st / TN][st % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][st / TN], fb[1][st % TN], \
+                                                                            acc[st / TN][st % TN], 0, 0, 0); \
+            if (st < TM) {                                                                                \
+                if (DO_W) fa[0][st] = *reinterpret_cast<const bf16x8*>(L0 + a_base[st] + ((c0 ^ a_sw[st]) << 3)); \
+            } else if (st < TM + TN) {                                                                    \
+                if (DO_W)                                                                                 \
+                    fb[0][st - TM] =                                                                      \
+                        *reinterpret_cast<const bf16x8*>(L0 + b_base[st - TM] + ((c0 ^ b_sw[st - TM]) << 3)); \
+            }                                                                                             \
+            if (st % RSP == 1) {                                                                          \
+                if (DO_L) SG_LOAD1(SET, RNH + st / RSP, ktv + 3)                                          \
+            }                                                                                             \
+            __builtin_amdgcn_sched_barrier(0);                                                            \
+        }                                                                                                 \
+    }
+
     if (nk > 0) {
-        SG_LOAD(ra, Ab, p.sam, p.sak, a_kc, a_rows, 0)
-        SG_LOAD(rb, Bb, p.sbn, p.sbk, b_kc, b_rows, 0)
-        SG_STORE(ra, 0, 0, a_kc)
-        SG_STORE(rb, 0, BM, b_kc)
-        __syncthreads();
+        // prologue: stage 0 -> set 0 -> slot 0; stage 1 -> set 1; stage 2 -> set 0
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) SG_LOAD1(0, q, 0)
+        if (nk > 1) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) SG_LOAD1(1, q, 1)
+        }
+        SG_WRITE1(0, 0, 0) SG_WRITE1(0, 1, 0) SG_WRITE1(0, 2, 0) SG_WRITE1(0, 3, 0)
+        SG_WRITE1(0, 4, 0) SG_WRITE1(0, 5, 0) SG_WRITE1(0, 6, 0) SG_WRITE1(0, 7, 0)
+        if (nk > 2) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) SG_LOAD1(0, q, 2)
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        SG_READ(0, 0, 0)
+        int kt = 0;
+        for (; kt + 4 < nk; kt += 2) {
+            SG_STEP(kt, 1, true, true)
+            SG_STEP(kt + 1, 0, true, true)
+        }
+        // tail (kt even; at most four iterations): plain order, static staging sets
+#define SG_TAIL(j, SET)                                                                                   \
+    if (kt + (j) < nk) {                                                                                  \
+        const int ktv = kt + (j);                                                                         \
+        const bool w = ktv + 1 < nk, l = ktv + 3 < nk;                                                    \
+        SG_READ(ktv & 1, 1, 1)                                                                            \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i) _Pragma("unroll") for (int jj = 0; jj < TN; ++jj)  \
+            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][i], fb[0][jj], acc[i][jj], 0, 0, 0); \
+        if (w) {                                                                                          \
+            SG_WRITE1(SET, 0, (ktv + 1) & 1) SG_WRITE1(SET, 1, (ktv + 1) & 1)                             \
+            SG_WRITE1(SET, 2, (ktv + 1) & 1) SG_WRITE1(SET, 3, (ktv + 1) & 1)                             \
+            SG_WRITE1(SET, 4, (ktv + 1) & 1) SG_WRITE1(SET, 5, (ktv + 1) & 1)                             \
+            SG_WRITE1(SET, 6, (ktv + 1) & 1) SG_WRITE1(SET, 7, (ktv + 1) & 1)                             \
+        }                                                                                                 \
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                                 \
+        if (w) SG_READ((ktv + 1) & 1, 0, 0)                                                               \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i) _Pragma("unroll") for (int jj = 0; jj < TN; ++jj)  \
+            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][jj], acc[i][jj], 0, 0, 0); \
+        if (l) {                                                                                          \
+            _Pragma("unroll") for (int q = 0; q < NQ; ++q) SG_LOAD1(SET, q, ktv + 3)                      \
+        }                                                                                                 \
     }
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        const int buf = (int)(kt & 1);
-        if (kt + 1 < nk) {
-            SG_LOAD(ra, Ab, p.sam, p.sak, a_kc, a_rows, kt + 1)
-            SG_LOAD(rb, Bb, p.sbn, p.sbk, b_kc, b_rows, kt + 1)
-        }
-        const uint16_t* L = lds[buf];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int c = kk * 2 + khalf;
-            bf16x8 fa[2], fb[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int r = wm * 64 + i * 32 + (lane & 31);
-                fa[i] = *reinterpret_cast<const bf16x8*>(L + r * BK + ((c ^ swz_b(r)) << 3));
-            }
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int r = BM + wn * 64 + j * 32 + (lane & 31);
-                fb[j] = *reinterpret_cast<const bf16x8*>(L + r * BK + ((c ^ swz_b(r)) << 3));
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < nk) {
-            SG_STORE(ra, buf ^ 1, 0, a_kc)
-            SG_STORE(rb, buf ^ 1, BM, b_kc)
-        }
-        __syncthreads();
+        SG_TAIL(0, 1)
+        SG_TAIL(1, 0)
+        SG_TAIL(2, 1)
+        SG_TAIL(3, 0)
+#undef SG_TAIL
     }
-#undef SG_LOAD
-#undef SG_STORE
-    // C layout of the 32x32 tile: lane holds column lane%32, rows 8*(v/4) + 4*(lane/32) + v%4
+#undef SG_LOAD1
+#undef SG_WRITE1
+#undef SG_READ
+#undef SG_STEP
+    // C layout of a 32 x 32 tile: lane holds column lane % 32, rows 8 (v / 4) + 4 (lane / 32) + v % 4
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
+        for (int j = 0; j < TN; ++j) {
+            const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
             if (n >= p.N) continue;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int64_t m = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
+                const int64_t m = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
                 if (m < M) C[m * p.scm + n] = acc[i][j][v];
             }
         }
@@ -262,12 +388,16 @@ __global__ __launch_bounds__(256) void sg_gemm_f32_kernel(SgArgsF p) {
 }
 
 void launch_sg_gemm_bf16(const SgArgs& a, int64_t max_rows, hipStream_t s) {
-    const int64_t tiles_n = (a.N + 127) / 128;
+    const int64_t tiles_n = (a.N + 255) / 256;
     int64_t blocks;
-    if (a.mode == SG_ROWS) blocks = ((max_rows + 127) / 128 + a.G) * tiles_n;
-    else blocks = ((a.M + 127) / 128) * tiles_n * a.G;
+    if (a.mode == SG_ROWS) blocks = ((max_rows + 255) / 256 + a.G) * tiles_n;
+    else blocks = ((a.M + 255) / 256) * tiles_n * a.G;
     if (blocks <= 0) return;
-    sg_gemm_bf16_kernel<<<(unsigned)blocks, 256, 0, s>>>(a);
+    const bool ak = a.sak == 1, bk = a.sbk == 1;
+    if (ak && bk) sg_gemm_bf16_kernel<true, true><<<(unsigned)blocks, 256, 0, s>>>(a);
+    else if (ak) sg_gemm_bf16_kernel<true, false><<<(unsigned)blocks, 256, 0, s>>>(a);
+    else if (bk) sg_gemm_bf16_kernel<false, true><<<(unsigned)blocks, 256, 0, s>>>(a);
+    else sg_gemm_bf16_kernel<false, false><<<(unsigned)blocks, 256, 0, s>>>(a);
 }
 
 void launch_sg_gemm_f32(const SgArgsF& a, int64_t max_rows, hipStream_t s) {
