@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restric
 
 // One wave per token: read the row once, store it at its k destinations (16-byte vectors, up to
 // 8 per lane loaded before any store so a row is one memory round trip); dropped slots (-1) are
-// skipped.
+// skipped. Loads and stores are non-temporal: each byte is touched once here.
 __global__ __launch_bounds__(256) void perm_scatter_kernel(const uint8_t* __restrict__ x,
                                                            const int32_t* __restrict__ inv_pos, int64_t T,
                                                            int row_bytes, int k, uint8_t* __restrict__ x_perm) {
@@ -127,14 +127,15 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const uint8_t* __rest
         u32x4 v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (c0 + 64 * u < nchunks) v[u] = ld16(src + (int64_t)(c0 + 64 * u) * 16);
+            if (c0 + 64 * u < nchunks) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)(c0 + 64 * u) * 16));
         for (int j = 0; j < k; ++j) {
             const int p = __builtin_amdgcn_readlane(mypos, j);
             if (p < 0) continue;
             uint8_t* dst = x_perm + (int64_t)p * row_bytes;
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (c0 + 64 * u < nchunks) st16(dst + (int64_t)(c0 + 64 * u) * 16, v[u]);
+                if (c0 + 64 * u < nchunks)
+                    __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(dst + (int64_t)(c0 + 64 * u) * 16));
         }
     }
 }

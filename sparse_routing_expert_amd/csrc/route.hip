@@ -70,7 +70,8 @@ __global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict
 // in a fixed order. Any assignment of the reduced index k to lanes is valid as long as both
 // operands use the same one, so each lane reads 64 contiguous bytes of its token row and of its
 // expert row per 128-wide step; the next step's loads are issued before the current products.
-template <int TT>
+// NTX: x is read by one block only (E <= 16), so its loads are non-temporal.
+template <int TT, bool NTX>
 __global__ __launch_bounds__(256) void route_logits_bf16_kernel(const uint16_t* __restrict__ x,
                                                                 const uint16_t* __restrict__ wsplit, int Epad,
                                                                 float* __restrict__ logits, int64_t T, int d,
@@ -100,7 +101,9 @@ __global__ __launch_bounds__(256) void route_logits_bf16_kernel(const uint16_t* 
     {                                                                                                     \
         const int base = (kb_) + g * 32;                                                                  \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                   \
-            _Pragma("unroll") for (int tt = 0; tt < TT; ++tt) xv[b_][tt][i] = ld16(xr[tt] + base + i * 8); \
+            _Pragma("unroll") for (int tt = 0; tt < TT; ++tt) xv[b_][tt][i] = NTX ?                       \
+                __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr[tt] + base + i * 8)) :           \
+                ld16(xr[tt] + base + i * 8);                                                              \
             _Pragma("unroll") for (int p = 0; p < 3; ++p) wv[b_][p][i] =                                   \
                 w_ok ? ld16(wh + p * n + base + i * 8) : zero;                                            \
         }                                                                                                 \
@@ -422,12 +425,15 @@ void launch_route_logits(int dtype, const void* x, const float* w_router, const 
                          float* logits, int64_t T, int d, int E, hipStream_t s) {
     if (dtype == MOE_BF16) {
         const auto xb = static_cast<const uint16_t*>(x);
+        const bool nt = Epad == 16;
         if (T >= 32 * 256) {  // two token tiles per wave still leave a block per CU
             dim3 grid((unsigned)((T + 31) / 32), (unsigned)(Epad / 16));
-            route_logits_bf16_kernel<2><<<grid, 256, 0, s>>>(xb, wsplit, Epad, logits, T, d, E);
+            if (nt) route_logits_bf16_kernel<2, true><<<grid, 256, 0, s>>>(xb, wsplit, Epad, logits, T, d, E);
+            else route_logits_bf16_kernel<2, false><<<grid, 256, 0, s>>>(xb, wsplit, Epad, logits, T, d, E);
         } else {
             dim3 grid((unsigned)((T + 15) / 16), (unsigned)(Epad / 16));
-            route_logits_bf16_kernel<1><<<grid, 256, 0, s>>>(xb, wsplit, Epad, logits, T, d, E);
+            if (nt) route_logits_bf16_kernel<1, true><<<grid, 256, 0, s>>>(xb, wsplit, Epad, logits, T, d, E);
+            else route_logits_bf16_kernel<1, false><<<grid, 256, 0, s>>>(xb, wsplit, Epad, logits, T, d, E);
         }
     } else {
         const int64_t n = T * E;
