@@ -22,6 +22,11 @@ namespace moe {
 
 namespace {
 
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
+
 __device__ __forceinline__ float sigm(float z) { return 1.0f / (1.0f + expf(-z)); }
 __device__ __forceinline__ float silu_b(float z) { return z * sigm(z); }
 __device__ __forceinline__ float silu_grad_b(float z) {
@@ -168,7 +173,6 @@ __global__ __launch_bounds__(256, 1) void sg_gemm_bf16_kernel(SgArgs p) {
 
     // ---- this thread's operand: element (row r, k) at X0 + r * s_row + k * s_k, r < rows_valid
     const bool isA = wave < 2;
-    const bool kcont = isA ? AK : BKC;
     const int t = tid & 127;
     const uint16_t* X0 = isA ? Ag + m0 * p.sam + kb * p.sak : Bg + n0 * p.sbn + kb * p.sbk;
     const int64_t s_row = isA ? p.sam : p.sbn, s_k = isA ? p.sak : p.sbk;
@@ -178,6 +182,7 @@ __global__ __launch_bounds__(256, 1) void sg_gemm_bf16_kernel(SgArgs p) {
     // K-contiguous: one descriptor for the tile (rows beyond rows_valid read 0), the stage as soffset.
     // Row-contiguous: a descriptor per stage covering k in [k0, min(k0 + BK, Kext)).
     // K-contiguous operands have K a multiple of BK (checked by the host), so only rows need a bound.
+    const bool kcont = isA ? AK : BKC;
     const __amdgpu_buffer_rsrc_t rs_tile = __builtin_amdgcn_make_buffer_rsrc(
         (void*)X0, (short)0, kcont && rows_valid > 0 ? (int)(((int64_t)rows_valid - 1) * s_row * 2 + Kext * 2) : 0,
         0x00020000);
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(256, 1) void sg_gemm_bf16_kernel(SgArgs p) {
 
 #define SG_LOAD1(set, q, stage)                                                                           \
     {                                                                                                     \
-        if (kcont) {                                                                                      \
+        if (KC) {                                                                                         \
             stg[set][q] = __builtin_bit_cast(                                                             \
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_tile, voff[q], (stage) * BK * 2, 0));      \
         } else {                                                                                          \
@@ -236,7 +241,7 @@ __global__ __launch_bounds__(256, 1) void sg_gemm_bf16_kernel(SgArgs p) {
     }
 #define SG_WRITE1(set, q, slot)                                                                           \
     {                                                                                                     \
-        const u32x4 w_ = kcont ? stg[set][q] : sg_tr_row(stg[set], q);                                    \
+        const u32x4 w_ = KC ? stg[set][q] : sg_tr_row(stg[set], q);                                       \
         *reinterpret_cast<u32x4*>(lds + (slot) * STAGE + wofs[q]) = w_;                                   \
     }
 #define SG_READ(slot, kk, f)                                                                              \
@@ -295,7 +300,10 @@ __global__ __launch_bounds__(256, 1) void sg_gemm_bf16_kernel(SgArgs p) {
         }                                                                                                 \
     }
 
-    if (nk > 0) {
+    // The pipeline, instantiated once per staging role (waves 0-1: operand A's layout, waves 2-3:
+    // B's), so the pinned schedule has no layout branches. Both copies issue the same barriers.
+    auto pipeline = [&](auto kc_tag) {
+        constexpr bool KC = decltype(kc_tag)::value;
         // prologue: stage 0 -> set 0 -> slot 0; stage 1 -> set 1; stage 2 -> set 0
 #pragma unroll
         for (int q = 0; q < NQ; ++q) SG_LOAD1(0, q, 0)
@@ -343,6 +351,10 @@ __global__ __launch_bounds__(256, 1) void sg_gemm_bf16_kernel(SgArgs p) {
         SG_TAIL(2, 1)
         SG_TAIL(3, 0)
 #undef SG_TAIL
+    };
+    if (nk > 0) {
+        if (isA) pipeline(BoolTag<AK>{});
+        else pipeline(BoolTag<BKC>{});
     }
 #undef SG_LOAD1
 #undef SG_WRITE1
