@@ -983,6 +983,13 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[TM][TN], int64_
                         o[c] = EPI == EPI_GELU_BIAS ? gelu_f(z) : z;
                     }
                 }
+                if (EPI == EPI_F32) {
+                    if (row < row_end && f0 < n_out)
+                        *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(C) + row * n_out + f0) =
+                            floatx4{acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2],
+                                    acc[i][j][4 * q4 + 3]};
+                    continue;
+                }
                 if (row < row_end && f0 < n_out) {
                     uint2 pk;
                     pk.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
@@ -1290,6 +1297,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_tail_kernel(const float* __rest
     const int64_t row = tt.row0 + grp * 128 + wm * 64 + i * 32 + (lane & 31);
     const int f0 = tt.n0 + wn * WTNO + j * 32 + 8 * v4 + 4 * (lane >> 5);
     if (row >= tt.row_end || f0 >= n_out) return;
+    if (EPI == EPI_F32) {
+        *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(C) + row * n_out + f0) = z;
+        return;
+    }
     float o[4];
     if (GATED) {
 #pragma unroll
@@ -1332,9 +1343,11 @@ void launch_bf16_persistent(int epi, const void* A, const void* B, const void* b
     const int bno = epi == EPI_SWIGLU ? 128 : 256;
     const int64_t m_tiles = offsets ? (max_rows + 255) / 256 + n_groups : (dense_rows + 255) / 256;
     const int64_t tiles = m_tiles * ((n_out + bno - 1) / bno);
+    if (tiles <= 0) return;
     const int64_t cap = persistent_grid_cap();
     const int64_t want = ((tiles + 7) / 8) * 8;
-    const unsigned grid = (unsigned)(want < cap ? want : cap);
+    // a dense product with fewer tiles than CUs takes every CU anyway when it may split along K
+    const unsigned grid = (unsigned)(want < cap && (offsets || !partials) ? want : cap);
     // a dense product whose tiles fill whole rounds needs no tail pass
     if (!offsets && tiles % grid == 0) partials = nullptr;
     const auto a = static_cast<const uint16_t*>(A);
@@ -1351,6 +1364,7 @@ void launch_bf16_persistent(int epi, const void* A, const void* B, const void* b
     }
     if (epi == EPI_SWIGLU) MOE_PERSIST(EPI_SWIGLU)
     else if (epi == EPI_GELU_BIAS) MOE_PERSIST(EPI_GELU_BIAS)
+    else if (epi == EPI_F32) MOE_PERSIST(EPI_F32)
     else MOE_PERSIST(EPI_BIAS)
 #undef MOE_PERSIST
 }

@@ -49,21 +49,27 @@ struct Carver {
 };
 
 struct RouteWs {
-    size_t logits, wsplit, blk_counts, blk_P, blk_H, fp, ticket, bytes;
+    size_t logits, wsplit, blk_counts, blk_P, blk_H, fp, ticket, gpart, bytes;
     int nblk, Epad;
+    bool gemm;  // logits as a dense product of x and the split router through the grouped GEMM
+    int lg_ld, lg_split;
 };
 RouteWs route_ws(const moe_shape* s) {
     RouteWs w;
     Carver c;
     w.nblk = (int)cdiv(s->T, kRouteTokensPerBlock);
     w.Epad = (int)cdiv(s->E, 16) * 16;
-    w.logits = c.take((size_t)s->T * s->E * 4);
+    w.gemm = s->dtype == MOE_BF16 && w.Epad >= moe::kRouteGemmMinEpad;
+    w.lg_ld = w.gemm ? 3 * w.Epad : s->E;
+    w.lg_split = w.gemm ? w.Epad : 0;
+    w.logits = c.take((size_t)s->T * w.lg_ld * 4);
     w.wsplit = c.take(s->dtype == MOE_BF16 ? (size_t)3 * w.Epad * s->d_model * 2 : 0);
     w.blk_counts = c.take((size_t)w.nblk * s->E * 4);
     w.blk_P = c.take((size_t)w.nblk * s->E * 4);
     w.blk_H = c.take((size_t)w.nblk * 4);
     w.fp = c.take((size_t)s->E * 8);
     w.ticket = c.take(4);
+    w.gpart = c.take(w.gemm ? moe::gemm_partials_bytes(s->dtype) : 0);
     w.bytes = c.off;
     return w;
 }
@@ -78,7 +84,7 @@ RouteNoisyWs route_noisy_ws(const moe_shape* s) {
     w.base = route_ws(s);
     Carver c;
     c.off = w.base.bytes;
-    w.s_logits = c.take((size_t)s->T * s->E * 4);
+    w.s_logits = c.take((size_t)s->T * w.base.lg_ld * 4);
     w.wsplit_n = c.take(s->dtype == MOE_BF16 ? (size_t)3 * w.base.Epad * s->d_model * 2 : 0);
     w.bytes = c.off;
     return w;
@@ -196,19 +202,31 @@ inline T* at(void* ws, size_t off) {
 inline int launched() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // ---- stage bodies (arguments already validated) ------------------------------------------------
+// logits (fp32) of x and the router; bf16 layers split the router into hi/mid/lo first. With a wide
+// router (w.gemm) lg receives the three products side by side ([T, 3 Epad]).
+void route_logits(const moe_shape* s, const RouteWs& w, const void* x, const float* w_router, uint16_t* wsplit,
+                  int32_t* ticket, float* lg, void* ws, hipStream_t st) {
+    moe::launch_route_prep(w_router, s->E, w.Epad, s->d_model, wsplit, ticket, st);
+    if (w.gemm)
+        moe::launch_grouped_gemm(MOE_BF16, moe::EPI_F32, 0, x, wsplit, nullptr, lg, nullptr, 0, 1, 0, s->T, w.lg_ld,
+                                 s->d_model, at<float>(ws, w.gpart), st);
+    else
+        moe::launch_route_logits(s->dtype, x, w_router, wsplit, w.Epad, lg, s->T, s->d_model, s->E, st);
+}
+
 void do_route(const moe_shape* s, const void* x, const float* w_router, const float* sel_bias, float* logits,
               int32_t* topk_idx, float* topk_w, int32_t* counts, float* stats, void* ws, hipStream_t st) {
     const RouteWs w = route_ws(s);
-    float* lg = logits ? logits : at<float>(ws, w.logits);
+    float* lg = logits && !w.gemm ? logits : at<float>(ws, w.logits);
     uint16_t* wsplit = s->dtype == MOE_BF16 ? at<uint16_t>(ws, w.wsplit) : nullptr;
     int32_t* ticket = at<int32_t>(ws, w.ticket);
     int32_t* blk_counts = at<int32_t>(ws, w.blk_counts);
     float* blk_P = stats ? at<float>(ws, w.blk_P) : nullptr;
     float* blk_H = stats ? at<float>(ws, w.blk_H) : nullptr;
-    moe::launch_route_prep(w_router, s->E, w.Epad, s->d_model, wsplit, ticket, st);
-    moe::launch_route_logits(s->dtype, x, w_router, wsplit, w.Epad, lg, s->T, s->d_model, s->E, st);
-    moe::launch_route_select(lg, sel_bias, s->T, s->E, s->k, s->score, s->renorm, topk_idx, topk_w, blk_counts, blk_P,
-                             blk_H, nullptr, nullptr, nullptr, st);
+    route_logits(s, w, x, w_router, wsplit, ticket, lg, ws, st);
+    moe::launch_route_select(lg, w.lg_ld, w.lg_split, w.gemm ? logits : nullptr, sel_bias, s->T, s->E, s->k,
+                             s->score, s->renorm, topk_idx, topk_w, blk_counts, blk_P, blk_H, nullptr, nullptr,
+                             nullptr, st);
     moe::launch_route_finalize(blk_counts, blk_P, blk_H, w.nblk, s->T, s->E, counts, at<double>(ws, w.fp), ticket,
                                stats, st);
 }
@@ -227,12 +245,10 @@ void do_route_noisy(const moe_shape* s, const void* x, const float* w_router, co
     int32_t* blk_counts = at<int32_t>(ws, w.blk_counts);
     float* blk_P = stats ? at<float>(ws, w.blk_P) : nullptr;
     float* blk_H = stats ? at<float>(ws, w.blk_H) : nullptr;
-    moe::launch_route_prep(w_router, s->E, w.Epad, s->d_model, wsplit, ticket, st);
-    moe::launch_route_logits(s->dtype, x, w_router, wsplit, w.Epad, lg, s->T, s->d_model, s->E, st);
-    moe::launch_route_prep(w_noise, s->E, w.Epad, s->d_model, wsplit_n, ticket, st);
-    moe::launch_route_logits(s->dtype, x, w_noise, wsplit_n, w.Epad, sl, s->T, s->d_model, s->E, st);
-    moe::launch_route_select(lg, sel_bias, s->T, s->E, s->k, s->score, s->renorm, topk_idx, topk_w, blk_counts, blk_P,
-                             blk_H, sl, noise, logits, st);
+    route_logits(s, w, x, w_router, wsplit, ticket, lg, ws, st);
+    route_logits(s, w, x, w_noise, wsplit_n, ticket, sl, ws, st);
+    moe::launch_route_select(lg, w.lg_ld, w.lg_split, nullptr, sel_bias, s->T, s->E, s->k, s->score, s->renorm,
+                             topk_idx, topk_w, blk_counts, blk_P, blk_H, sl, noise, logits, st);
     moe::launch_route_finalize(blk_counts, blk_P, blk_H, w.nblk, s->T, s->E, counts, at<double>(ws, w.fp), ticket,
                                stats, st);
 }

@@ -41,26 +41,52 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
-// Wave-wide reductions (all 64 lanes participate; every lane receives the result).
+// Wave-wide reductions (all 64 lanes participate; every lane receives the same result). Inside each
+// 16-lane row, DPP moves combine lanes (quad xor 1, quad xor 2, row rotate 4, row rotate 8); lane 0
+// of every row then holds (Q0 + Q1) + (Q2 + Q3) of its row's quads, and the four row results are
+// read into scalars and combined as (R0 + R1) + (R2 + R3): a fixed order, so results are
+// deterministic, with no LDS round trip.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRor4 = 0x124, kDppRor8 = 0x128;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+__device__ __forceinline__ float lane_f32(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    v += dpp_f32<kDppXor1>(v);
+    v += dpp_f32<kDppXor2>(v);
+    v += dpp_f32<kDppRor4>(v);
+    v += dpp_f32<kDppRor8>(v);
+    return (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
+    v = fmaxf(v, dpp_f32<kDppXor1>(v));
+    v = fmaxf(v, dpp_f32<kDppXor2>(v));
+    v = fmaxf(v, dpp_f32<kDppRor4>(v));
+    v = fmaxf(v, dpp_f32<kDppRor8>(v));
+    return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
 }
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    return ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+}
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l) {
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), l) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        uint32_t lo = __shfl_xor((uint32_t)v, o, kWave);
-        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
-        uint64_t w = ((uint64_t)hi << 32) | lo;
-        v = w > v ? w : v;
-    }
-    return v;
+    v = max_u64(v, dpp_u64<kDppXor1>(v));
+    v = max_u64(v, dpp_u64<kDppXor2>(v));
+    v = max_u64(v, dpp_u64<kDppRor4>(v));
+    v = max_u64(v, dpp_u64<kDppRor8>(v));
+    return max_u64(max_u64(lane_u64(v, 0), lane_u64(v, 16)), max_u64(lane_u64(v, 32), lane_u64(v, 48)));
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }

@@ -17,11 +17,18 @@ void launch_route_prep(const float* w_router, int E, int Epad, int d, uint16_t* 
                        hipStream_t s);
 void launch_route_logits(int dtype, const void* x, const float* w_router, const uint16_t* wsplit, int Epad,
                          float* logits, int64_t T, int d, int E, hipStream_t s);
+// Logits (and s_logits) of token t, expert e at [t * lg_ld + e], or, with lg_split > 0, the sum of the
+// split-router products at columns e, lg_split + e, 2 * lg_split + e (written to logits_out when given).
 // s_logits / noise (both or neither): noisy top-k, logits replaced by logits + noise * softplus(s_logits),
 // written to h_out when given
-void launch_route_select(const float* logits, const float* sel_bias, int64_t T, int E, int k, int score,
-                         int renorm, int32_t* topk_idx, float* topk_w, int32_t* blk_counts, float* blk_P,
-                         float* blk_H, const float* s_logits, const float* noise, float* h_out, hipStream_t s);
+void launch_route_select(const float* logits, int lg_ld, int lg_split, float* logits_out, const float* sel_bias,
+                         int64_t T, int E, int k, int score, int renorm, int32_t* topk_idx, float* topk_w,
+                         int32_t* blk_counts, float* blk_P, float* blk_H, const float* s_logits, const float* noise,
+                         float* h_out, hipStream_t s);
+// Routers with at least this many (16-padded) experts take the logits as one dense MFMA product
+// x [T, d] . [hi; mid; lo]^T [3 Epad, d] through the grouped GEMM (fp32 output), split along K over
+// every CU; the select kernel sums the three products.
+constexpr int kRouteGemmMinEpad = 64;
 // counts[E] always; stats (f, P, aux, entropy) when stats != NULL
 void launch_route_finalize(const int32_t* blk_counts, const float* blk_P, const float* blk_H, int nblk, int64_t T,
                            int E, int32_t* counts, double* fp_scratch, int32_t* ticket, float* stats,
@@ -44,7 +51,8 @@ void launch_perm_scatter(const void* x, const int32_t* inv_pos, int64_t T, int d
                          void* x_perm, hipStream_t s);
 
 // ---- grouped FFN ------------------------------------------------------------------------
-enum Epilogue { EPI_SWIGLU = 0, EPI_GELU_BIAS = 1, EPI_BIAS = 2 };
+// EPI_F32 (dense bf16 products only): C is float, the fp32 accumulators stored as they are
+enum Epilogue { EPI_SWIGLU = 0, EPI_GELU_BIAS = 1, EPI_BIAS = 2, EPI_F32 = 3 };
 
 struct GemmPlan {
     int bm;  // rows per tile

@@ -65,18 +65,17 @@ __global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict
 }
 
 // logits[T, E] = x[T, d] (bf16) . w[E, d]^T with the split router (v_mfma_f32_16x16x32_bf16, three
-// products per K step). A block owns 16*TT tokens x 16 experts; its four waves take a quarter of d
-// each (TT token tiles per wave share each router load) and their partial tiles are summed in LDS
-// in a fixed order. Any assignment of the reduced index k to lanes is valid as long as both
-// operands use the same one, so each lane reads 64 contiguous bytes of its token row and of its
-// expert row per 128-wide step; the next step's loads are issued before the current products.
-// NTX: x is read by one block only (E <= 16), so its loads are non-temporal.
-template <int TT, bool NTX>
-__global__ __launch_bounds__(256) void route_logits_bf16_kernel(const uint16_t* __restrict__ x,
-                                                                const uint16_t* __restrict__ wsplit, int Epad,
-                                                                float* __restrict__ logits, int64_t T, int d,
-                                                                int E) {
-    __shared__ floatx4 s_part[4][TT][64];
+// products per K step). A block owns 16*TT tokens x 16 experts; its NW waves take 1/NW of d each
+// (TT token tiles per wave share each router load) and their partial tiles are summed in LDS in a
+// fixed order. Each 32-wide K chunk of a 128-wide step is one load instruction per operand, in
+// which the four lanes of a row read 64 contiguous bytes; the next step's loads are issued before
+// the current products. NTX: x is read by one block only (E <= 16), so its loads are non-temporal.
+template <int TT, bool NTX, int NW>
+__global__ __launch_bounds__(NW * 64) void route_logits_bf16_kernel(const uint16_t* __restrict__ x,
+                                                                    const uint16_t* __restrict__ wsplit, int Epad,
+                                                                    float* __restrict__ logits, int64_t T, int d,
+                                                                    int E) {
+    __shared__ floatx4 s_part[NW][TT][64];
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int64_t t0 = (int64_t)blockIdx.x * 16 * TT;
     const int e0 = blockIdx.y * 16;
@@ -90,8 +89,8 @@ __global__ __launch_bounds__(256) void route_logits_bf16_kernel(const uint16_t* 
     const bool w_ok = e0 + r < E;  // rows E..Epad-1 are zero: not loaded
     const int64_t n = (int64_t)Epad * d;
     const uint16_t* wh = wsplit + (int64_t)(e0 + r) * d;
-    const int nc = d / 32;  // 32-wide K chunks, split over the four waves
-    const int kb0 = (wave * nc / 4) * 32, kb1 = ((wave + 1) * nc / 4) * 32;
+    const int nc = d / 32;  // 32-wide K chunks, split over the waves
+    const int kb0 = (wave * nc / NW) * 32, kb1 = ((wave + 1) * nc / NW) * 32;
     floatx4 acc[TT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) acc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -99,13 +98,13 @@ __global__ __launch_bounds__(256) void route_logits_bf16_kernel(const uint16_t* 
     u32x4 xv[2][TT][4], wv[2][3][4];
 #define RL_LOAD(b_, kb_)                                                                                  \
     {                                                                                                     \
-        const int base = (kb_) + g * 32;                                                                  \
+        const int base = (kb_) + g * 8;                                                                   \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                   \
             _Pragma("unroll") for (int tt = 0; tt < TT; ++tt) xv[b_][tt][i] = NTX ?                       \
-                __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr[tt] + base + i * 8)) :           \
-                ld16(xr[tt] + base + i * 8);                                                              \
+                __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr[tt] + base + i * 32)) :      \
+                ld16(xr[tt] + base + i * 32);                                                             \
             _Pragma("unroll") for (int p = 0; p < 3; ++p) wv[b_][p][i] =                                   \
-                w_ok ? ld16(wh + p * n + base + i * 8) : zero;                                            \
+                w_ok ? ld16(wh + p * n + base + i * 32) : zero;                                           \
         }                                                                                                 \
     }
 #define RL_MMA(b_)                                                                                        \
@@ -153,12 +152,13 @@ __global__ __launch_bounds__(256) void route_logits_bf16_kernel(const uint16_t* 
     if (e < E) {
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
-            const floatx4 p0 = s_part[0][tt][lane], p1 = s_part[1][tt][lane], p2 = s_part[2][tt][lane],
-                          p3 = s_part[3][tt][lane];
+            floatx4 sum = s_part[0][tt][lane];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) sum += s_part[w][tt][lane];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int64_t tk = t0 + tt * 16 + 4 * g + v;
-                if (tk < T) logits[tk * E + e] = ((p0[v] + p1[v]) + p2[v]) + p3[v];
+                if (tk < T) logits[tk * E + e] = sum[v];
             }
         }
     }
@@ -186,15 +186,17 @@ __global__ __launch_bounds__(256) void route_logits_f32_kernel(const float* __re
     logits[i] = acc;
 }
 
-// Per token (one wave handles kSelTokensPerWave tokens, their logits loaded up front): scores,
+// Per token (one wave per token, sixteen waves per block): scores,
 // balance-statistic partials, top-k by k rounds of a wave-wide max over packed keys, gates. Each
 // block writes its expert histogram, its per-expert probability sums and its entropy sum;
 // route_finalize reduces them. Noisy top-k ("Mixture of Experts" tutorial, Noisy top-k gating):
 // with s_logits (= x W_noise^T) and noise given, the logits become H = l + noise * softplus(s)
 // before anything else, and H is written to h_out when that is given.
-constexpr int kSelTokensPerWave = kRouteTokensPerBlock / 4;
+constexpr int kSelTokensPerWave = 1;
+constexpr int kSelWaves = kRouteTokensPerBlock / kSelTokensPerWave;
 template <int EPL>
-__global__ __launch_bounds__(256) void route_select_kernel(const float* __restrict__ logits,
+__global__ __launch_bounds__(kSelWaves * 64) void route_select_kernel(const float* __restrict__ logits, int lg_ld,
+                                                           int lg_split, float* __restrict__ logits_out,
                                                            const float* __restrict__ sel_bias, int64_t T,
                                                            int E, int k, int score, int renorm,
                                                            int32_t* __restrict__ topk_idx,
@@ -204,11 +206,11 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
                                                            const float* __restrict__ s_logits,
                                                            const float* __restrict__ noise,
                                                            float* __restrict__ h_out) {
-    __shared__ int s_cnt[1024];
-    __shared__ float s_P[4][1024];
-    __shared__ float s_H[4];
+    __shared__ int s_cnt[64 * EPL];
+    __shared__ float s_P[kSelWaves][64 * EPL];
+    __shared__ float s_H[kSelWaves];
     const int lane = lane_id(), wave = threadIdx.x >> 6;
-    for (int e = threadIdx.x; e < E; e += 256) s_cnt[e] = 0;
+    for (int e = threadIdx.x; e < E; e += kSelWaves * 64) s_cnt[e] = 0;
     __syncthreads();
 
     const bool softmax = score == MOE_SOFTMAX;
@@ -222,13 +224,19 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
     float hacc = 0.f;
 
     const int64_t tb = (int64_t)blockIdx.x * kRouteTokensPerBlock + wave * kSelTokensPerWave;
+    // logits of token t, expert e: lg[t * lg_ld + e], or with lg_split > 0 the sum of the three
+    // split-router products (hi, mid, lo) at columns e, lg_split + e and 2 * lg_split + e
+    auto logit_at = [&](const float* lg, int64_t t, int e) {
+        const float* r = lg + t * lg_ld + e;
+        return lg_split > 0 ? (r[0] + r[lg_split]) + r[2 * lg_split] : r[0];
+    };
     float lall[kSelTokensPerWave][EPL];
 #pragma unroll
     for (int q = 0; q < kSelTokensPerWave; ++q)
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
             const int e = lane + 64 * i;
-            lall[q][i] = (tb + q < T && e < E) ? logits[(tb + q) * E + e] : -INFINITY;
+            lall[q][i] = (tb + q < T && e < E) ? logit_at(logits, tb + q, e) : -INFINITY;
         }
     if (s_logits != nullptr) {
 #pragma unroll
@@ -238,9 +246,17 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
                 const int e = lane + 64 * i;
                 if (tb + q < T && e < E) {
                     const int64_t o = (tb + q) * E + e;
-                    lall[q][i] = lall[q][i] + noise[o] * softplusf_(s_logits[o]);
+                    lall[q][i] = lall[q][i] + noise[o] * softplusf_(logit_at(s_logits, tb + q, e));
                     if (h_out != nullptr) h_out[o] = lall[q][i];
                 }
+            }
+    } else if (logits_out != nullptr) {
+#pragma unroll
+        for (int q = 0; q < kSelTokensPerWave; ++q)
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const int e = lane + 64 * i;
+                if (tb + q < T && e < E) logits_out[(tb + q) * E + e] = lall[q][i];
             }
     }
 #pragma unroll
@@ -328,17 +344,27 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
     const float hw = wave_sum(hacc);
     if (lane == 0) s_H[wave] = hw;
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += 256) {
+    for (int e = threadIdx.x; e < E; e += kSelWaves * 64) {
         blk_counts[(int64_t)blockIdx.x * E + e] = s_cnt[e];
-        if (blk_P != nullptr) blk_P[(int64_t)blockIdx.x * E + e] = ((s_P[0][e] + s_P[1][e]) + s_P[2][e]) + s_P[3][e];
+        if (blk_P != nullptr) {
+            float sp = s_P[0][e];
+#pragma unroll
+            for (int w = 1; w < kSelWaves; ++w) sp += s_P[w][e];
+            blk_P[(int64_t)blockIdx.x * E + e] = sp;
+        }
     }
-    if (threadIdx.x == 0 && blk_H != nullptr) blk_H[blockIdx.x] = ((s_H[0] + s_H[1]) + s_H[2]) + s_H[3];
+    if (threadIdx.x == 0 && blk_H != nullptr) {
+        float sh = s_H[0];
+#pragma unroll
+        for (int w = 1; w < kSelWaves; ++w) sh += s_H[w];
+        blk_H[blockIdx.x] = sh;
+    }
 }
 
 // Expert counts and balance statistics from the per-block partials, in fixed-order sums (float64
 // for the statistics): block e < E reduces expert e (count; with stats, f = counts/T and P = mean
 // p), block E the entropy; the last block to finish (ticket) forms aux = E * sum_e f_e P_e over the
-// per-expert products in expert order.
+// per-expert products in a fixed order.
 __global__ __launch_bounds__(256) void route_finalize_kernel(const int32_t* __restrict__ blk_counts,
                                                              const float* __restrict__ blk_P,
                                                              const float* __restrict__ blk_H, int nblk,
@@ -389,11 +415,16 @@ __global__ __launch_bounds__(256) void route_finalize_kernel(const int32_t* __re
     __syncthreads();
     if (!s_last) return;
     __threadfence();
-    if (tid == 0) {
-        double aux = 0.0;
-        for (int i = 0; i < E; ++i) aux += __builtin_nontemporal_load(fp_scratch + i);
-        stats[2 * E] = (float)((double)E * aux);
+    // sum_e f_e P_e: each thread sums experts tid, tid + 256, ... in order, then a fixed tree
+    double a = 0.0;
+    for (int i = tid; i < E; i += 256) a += __builtin_nontemporal_load(fp_scratch + i);
+    s_sum[tid] = a;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (tid < o) s_sum[tid] += s_sum[tid + o];
+        __syncthreads();
     }
+    if (tid == 0) stats[2 * E] = (float)((double)E * s_sum[0]);
 }
 
 // Aux-loss-free balancing step ("Router Optimization Techniques", How It Works 2 and Fine-Tuning
@@ -426,14 +457,19 @@ void launch_route_logits(int dtype, const void* x, const float* w_router, const 
     if (dtype == MOE_BF16) {
         const auto xb = static_cast<const uint16_t*>(x);
         const bool nt = Epad == 16;
-        if (T >= 32 * 256) {  // two token tiles per wave still leave a block per CU
+        // one 16-expert tile: eight waves split d, more loads in flight per token tile
+        if (nt && T >= 32 * 256) {
+            dim3 grid((unsigned)((T + 31) / 32), 1);
+            route_logits_bf16_kernel<2, true, 8><<<grid, 512, 0, s>>>(xb, wsplit, Epad, logits, T, d, E);
+        } else if (nt) {
+            dim3 grid((unsigned)((T + 15) / 16), 1);
+            route_logits_bf16_kernel<1, true, 8><<<grid, 512, 0, s>>>(xb, wsplit, Epad, logits, T, d, E);
+        } else if (T >= 32 * 256) {  // two token tiles per wave still leave a block per CU
             dim3 grid((unsigned)((T + 31) / 32), (unsigned)(Epad / 16));
-            if (nt) route_logits_bf16_kernel<2, true><<<grid, 256, 0, s>>>(xb, wsplit, Epad, logits, T, d, E);
-            else route_logits_bf16_kernel<2, false><<<grid, 256, 0, s>>>(xb, wsplit, Epad, logits, T, d, E);
+            route_logits_bf16_kernel<2, false, 4><<<grid, 256, 0, s>>>(xb, wsplit, Epad, logits, T, d, E);
         } else {
             dim3 grid((unsigned)((T + 15) / 16), (unsigned)(Epad / 16));
-            if (nt) route_logits_bf16_kernel<1, true><<<grid, 256, 0, s>>>(xb, wsplit, Epad, logits, T, d, E);
-            else route_logits_bf16_kernel<1, false><<<grid, 256, 0, s>>>(xb, wsplit, Epad, logits, T, d, E);
+            route_logits_bf16_kernel<1, false, 4><<<grid, 256, 0, s>>>(xb, wsplit, Epad, logits, T, d, E);
         }
     } else {
         const int64_t n = T * E;
@@ -442,13 +478,15 @@ void launch_route_logits(int dtype, const void* x, const float* w_router, const 
     }
 }
 
-void launch_route_select(const float* logits, const float* sel_bias, int64_t T, int E, int k, int score,
-                         int renorm, int32_t* topk_idx, float* topk_w, int32_t* blk_counts, float* blk_P,
-                         float* blk_H, const float* s_logits, const float* noise, float* h_out, hipStream_t s) {
+void launch_route_select(const float* logits, int lg_ld, int lg_split, float* logits_out, const float* sel_bias,
+                         int64_t T, int E, int k, int score, int renorm, int32_t* topk_idx, float* topk_w,
+                         int32_t* blk_counts, float* blk_P, float* blk_H, const float* s_logits, const float* noise,
+                         float* h_out, hipStream_t s) {
     const unsigned nblk = (unsigned)((T + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock);
 #define MOE_SELECT(EPL)                                                                                  \
-    route_select_kernel<EPL><<<nblk, 256, 0, s>>>(logits, sel_bias, T, E, k, score, renorm, topk_idx, topk_w, \
-                                                 blk_counts, blk_P, blk_H, s_logits, noise, h_out)
+    route_select_kernel<EPL><<<nblk, kSelWaves * 64, 0, s>>>(logits, lg_ld, lg_split, logits_out, sel_bias, T, E, k, score, \
+                                                 renorm, topk_idx, topk_w, blk_counts, blk_P, blk_H, s_logits, \
+                                                 noise, h_out)
     if (E <= 64) MOE_SELECT(1);
     else if (E <= 128) MOE_SELECT(2);
     else if (E <= 256) MOE_SELECT(4);
