@@ -186,8 +186,89 @@ __global__ __launch_bounds__(256) void route_logits_f32_kernel(const float* __re
     logits[i] = acc;
 }
 
-// Per token (one wave per token, sixteen waves per block): scores,
-// balance-statistic partials, top-k by k rounds of a wave-wide max over packed keys, gates. Each
+// One token's selection, with its logits held as l[i] = logit of expert lane + 64 i (-inf past E):
+// the scores' distribution (softmax or normalised sigmoid) is added to pacc and its entropy to
+// hacc; the top-k by k rounds of a wave-wide max over packed (key, index) pairs, key = logit
+// (softmax) or sigmoid score, plus the selection bias; the gates from the unbiased scores of the
+// selection; slot j is written by lane j, which also counts its expert in s_cnt.
+template <int EPL>
+__device__ __forceinline__ void select_token(const float (&l)[EPL], const float (&bias)[EPL], int64_t t, int E,
+                                             int k, bool softmax, int renorm, float (&pacc)[EPL], float& hacc,
+                                             int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                                             int* s_cnt) {
+    const int lane = lane_id();
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) lmax = fmaxf(lmax, l[i]);
+    const float m = wave_max(lmax);
+    // distribution whose mean is P_e and whose entropy is reported
+    float p[EPL];
+    float zpart = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        p[i] = e < E ? (softmax ? expf(l[i] - m) : sigmoidf_(l[i])) : 0.f;
+        zpart += p[i];
+    }
+    const float Z = wave_sum(zpart);
+    const float invZ = 1.0f / Z, lnZ = logf(Z);
+    uint64_t key[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        const float pi = p[i] * invZ;
+        pacc[i] += pi;
+        if (pi > 0.f) hacc -= pi * (softmax ? (l[i] - m) - lnZ : logf(pi));
+        float kv = softmax ? l[i] : p[i];  // p[i] holds the raw sigmoid score here
+        kv = kv + bias[i];
+        kv = kv + 0.0f;  // -0 -> +0: equal keys compare equal
+        key[i] = e < E ? pack_key(kv, e) : 0ull;
+    }
+    int sel_e = 0;
+    float sel_l = -INFINITY;
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = 0ull;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) best = key[i] > best ? key[i] : best;
+        best = wave_max_u64(best);
+        const int e = key_index(best);
+        float le = -INFINITY;  // unbiased logit of the winner, from the lane that holds it
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if (e == lane + 64 * i) {
+                key[i] = 0ull;
+                le = l[i];
+            }
+        le = wave_max(le);
+        if (lane == j) {
+            sel_e = e;
+            sel_l = le;
+        }
+    }
+    // gates from the unbiased logits of the selection (lane j holds slot j)
+    const float lv = lane < k ? sel_l : -INFINITY;
+    float gate;
+    if (softmax) {
+        if (renorm) {
+            const float ms = wave_max(lv);
+            const float ex = lane < k ? expf(lv - ms) : 0.f;
+            gate = ex / wave_sum(ex);
+        } else {
+            gate = expf(lv - m) * invZ;
+        }
+    } else {
+        const float sg = lane < k ? sigmoidf_(lv) : 0.f;
+        gate = sg / wave_sum(sg);
+    }
+    if (lane < k) {
+        topk_idx[t * k + lane] = sel_e;
+        topk_w[t * k + lane] = gate;
+        atomicAdd(&s_cnt[sel_e], 1);
+    }
+}
+
+// Per token (one wave per token, sixteen waves per block): scores, balance-statistic partials,
+// top-k by k rounds of a wave-wide max over packed keys, gates. Each
 // block writes its expert histogram, its per-expert probability sums and its entropy sum;
 // route_finalize reduces them. Noisy top-k ("Mixture of Experts" tutorial, Noisy top-k gating):
 // with s_logits (= x W_noise^T) and noise given, the logits become H = l + noise * softplus(s)
@@ -263,78 +344,7 @@ __global__ __launch_bounds__(kSelWaves * 64) void route_select_kernel(const floa
     for (int q = 0; q < kSelTokensPerWave; ++q) {
         const int64_t t = tb + q;
         if (t >= T) break;
-        float l[EPL];
-        float lmax = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            l[i] = lall[q][i];
-            lmax = fmaxf(lmax, l[i]);
-        }
-        const float m = wave_max(lmax);
-        // distribution whose mean is P_e and whose entropy is reported
-        float p[EPL];
-        float zpart = 0.f;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const int e = lane + 64 * i;
-            p[i] = e < E ? (softmax ? expf(l[i] - m) : sigmoidf_(l[i])) : 0.f;
-            zpart += p[i];
-        }
-        const float Z = wave_sum(zpart);
-        const float invZ = 1.0f / Z, lnZ = logf(Z);
-        uint64_t key[EPL];
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const int e = lane + 64 * i;
-            const float pi = p[i] * invZ;
-            pacc[i] += pi;
-            if (pi > 0.f) hacc -= pi * (softmax ? (l[i] - m) - lnZ : logf(pi));
-            float kv = softmax ? l[i] : p[i];  // p[i] holds the raw sigmoid score here
-            kv = kv + bias[i];
-            kv = kv + 0.0f;  // -0 -> +0: equal keys compare equal
-            key[i] = e < E ? pack_key(kv, e) : 0ull;
-        }
-        int sel_e = 0;
-        float sel_l = -INFINITY;
-        for (int j = 0; j < k; ++j) {
-            uint64_t best = 0ull;
-#pragma unroll
-            for (int i = 0; i < EPL; ++i) best = key[i] > best ? key[i] : best;
-            best = wave_max_u64(best);
-            const int e = key_index(best);
-            float le = -INFINITY;  // unbiased logit of the winner, from the lane that holds it
-#pragma unroll
-            for (int i = 0; i < EPL; ++i)
-                if (e == lane + 64 * i) {
-                    key[i] = 0ull;
-                    le = l[i];
-                }
-            le = wave_max(le);
-            if (lane == j) {
-                sel_e = e;
-                sel_l = le;
-            }
-        }
-        // gates from the unbiased logits of the selection (lane j holds slot j)
-        const float lv = lane < k ? sel_l : -INFINITY;
-        float gate;
-        if (softmax) {
-            if (renorm) {
-                const float ms = wave_max(lv);
-                const float ex = lane < k ? expf(lv - ms) : 0.f;
-                gate = ex / wave_sum(ex);
-            } else {
-                gate = expf(lv - m) * invZ;
-            }
-        } else {
-            const float sg = lane < k ? sigmoidf_(lv) : 0.f;
-            gate = sg / wave_sum(sg);
-        }
-        if (lane < k) {
-            topk_idx[t * k + lane] = sel_e;
-            topk_w[t * k + lane] = gate;
-            atomicAdd(&s_cnt[sel_e], 1);
-        }
+        select_token<EPL>(lall[q], bias, t, E, k, softmax, renorm, pacc, hacc, topk_idx, topk_w, s_cnt);
     }
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
@@ -359,6 +369,182 @@ __global__ __launch_bounds__(kSelWaves * 64) void route_select_kernel(const floa
         for (int w = 1; w < kSelWaves; ++w) sh += s_H[w];
         blk_H[blockIdx.x] = sh;
     }
+}
+
+// Small routers (E <= 16), bf16 activations: logits and selection in one launch. A block owns
+// 16 * TT tokens and the 16 (padded) experts; its waves split d as in route_logits_bf16_kernel,
+// but form the hi + mid + lo bf16 terms of the fp32 router in registers from fp32 loads (the same
+// roundings as route_prep_kernel, so the products and their order are the same). The wave partials
+// are summed in LDS in wave order, then each wave selects for its share of the block's tokens
+// (select_token, lane e holding expert e) and the block writes its partials for route_finalize.
+// Block 0 zeroes the ticket route_finalize counts its blocks with.
+constexpr int kFusedRouteWaves = 8;
+template <int TT>
+__global__ __launch_bounds__(kFusedRouteWaves * 64) void route_fused_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ w, const float* __restrict__ sel_bias, int64_t T, int d,
+    int E, int k, int score, int renorm, float* __restrict__ logits_out, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, int32_t* __restrict__ blk_counts, float* __restrict__ blk_P,
+    float* __restrict__ blk_H, int32_t* __restrict__ ticket) {
+    constexpr int NW = kFusedRouteWaves, TPB = 16 * TT, TPWV = TPB / NW;
+    __shared__ floatx4 s_part[NW][TT][64];
+    __shared__ int s_cnt[64];
+    __shared__ float s_P[NW][64];
+    __shared__ float s_H[NW];
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0;
+    if (threadIdx.x < 64) s_cnt[threadIdx.x] = 0;
+    const int64_t t0 = (int64_t)blockIdx.x * TPB;
+    const int r = lane & 15, g = lane >> 4;
+    const uint16_t* xr[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+        const int64_t t = t0 + tt * 16 + r;
+        xr[tt] = x + (t < T ? t : T - 1) * d;
+    }
+    const bool w_ok = r < E;  // padded expert rows are zero and not loaded
+    const float* wr = w + (int64_t)(w_ok ? r : 0) * d;
+    const int nc = d / 32;
+    const int kb0 = (wave * nc / NW) * 32, kb1 = ((wave + 1) * nc / NW) * 32;
+    floatx4 acc[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) acc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const floatx4 fzero = {0.f, 0.f, 0.f, 0.f};
+    u32x4 xv[2][TT][4];
+    floatx4 wf[2][4][2];
+    // hi / mid / lo bf16 terms of 8 fp32 weights
+    auto split8 = [](const floatx4 (&v)[2], bf16x8& h8, bf16x8& m8, bf16x8& l8) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float f = v[j >> 2][j & 3];
+            const __bf16 h = (__bf16)f;
+            const float r1 = f - (float)h;
+            const __bf16 m = (__bf16)r1;
+            const float r2 = r1 - (float)m;
+            h8[j] = h;
+            m8[j] = m;
+            l8[j] = (__bf16)r2;
+        }
+    };
+#define RF_LOAD(b_, kb_)                                                                                  \
+    {                                                                                                     \
+        const int base = (kb_) + g * 8;                                                                   \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                   \
+            _Pragma("unroll") for (int tt = 0; tt < TT; ++tt) xv[b_][tt][i] =                             \
+                __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr[tt] + base + i * 32));       \
+            wf[b_][i][0] = w_ok ? *reinterpret_cast<const floatx4*>(wr + base + i * 32) : fzero;          \
+            wf[b_][i][1] = w_ok ? *reinterpret_cast<const floatx4*>(wr + base + i * 32 + 4) : fzero;      \
+        }                                                                                                 \
+    }
+#define RF_MMA(b_)                                                                                        \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                       \
+        bf16x8 w3[3];                                                                                     \
+        split8(wf[b_][i], w3[0], w3[1], w3[2]);                                                           \
+        _Pragma("unroll") for (int tt = 0; tt < TT; ++tt) _Pragma("unroll") for (int p = 0; p < 3; ++p)   \
+            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[b_][tt][i]), w3[p], \
+                                                              acc[tt], 0, 0, 0);                          \
+    }
+    int kb = kb0;
+    const int nsteps = (kb1 - kb0) / 128;
+    if (nsteps > 0) {
+        RF_LOAD(0, kb)
+        int st = 0;
+        for (; st + 2 <= nsteps; st += 2) {
+            if (st + 1 < nsteps) RF_LOAD(1, kb + 128)
+            RF_MMA(0)
+            if (st + 2 < nsteps) RF_LOAD(0, kb + 256)
+            RF_MMA(1)
+            kb += 256;
+        }
+        if (st < nsteps) {
+            RF_MMA(0)
+            kb += 128;
+        }
+    }
+#undef RF_LOAD
+#undef RF_MMA
+    for (; kb < kb1; kb += 32) {  // 32-wide tail of the wave's range
+        const int base = kb + g * 8;
+        floatx4 w8[2] = {w_ok ? *reinterpret_cast<const floatx4*>(wr + base) : fzero,
+                         w_ok ? *reinterpret_cast<const floatx4*>(wr + base + 4) : fzero};
+        bf16x8 w3[3];
+        split8(w8, w3[0], w3[1], w3[2]);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(xr[tt] + base));
+#pragma unroll
+            for (int p = 0; p < 3; ++p) acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w3[p], acc[tt], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) s_part[wave][tt][lane] = acc[tt];
+    __syncthreads();
+    // 16x16 accumulator: lane holds column (expert) lane % 16 and rows (tokens) 4 (lane / 16) + v
+    const float* sp = reinterpret_cast<const float*>(&s_part[0][0][0]);
+    const bool softmax = score == MOE_SOFTMAX;
+    float bias[1] = {(sel_bias != nullptr && lane < E) ? sel_bias[lane] : 0.f};
+    float pacc[1] = {0.f}, hacc = 0.f;
+#pragma unroll
+    for (int q = 0; q < TPWV; ++q) {
+        const int lt = wave * TPWV + q, tt = lt >> 4, row = lt & 15;
+        const int64_t t = t0 + lt;
+        if (t >= T) break;
+        float l[1] = {-INFINITY};
+        if (lane < E) {
+            const int off = (tt * 64 + lane + 16 * (row >> 2)) * 4 + (row & 3);
+            float sum = sp[off];
+#pragma unroll
+            for (int wv = 1; wv < NW; ++wv) sum += sp[wv * TT * 256 + off];
+            l[0] = sum;
+            if (logits_out != nullptr) logits_out[t * E + lane] = sum;
+        }
+        select_token<1>(l, bias, t, E, k, softmax, renorm, pacc, hacc, topk_idx, topk_w, s_cnt);
+    }
+    if (lane < E) s_P[wave][lane] = pacc[0];
+    const float hw = wave_sum(hacc);
+    if (lane == 0) s_H[wave] = hw;
+    __syncthreads();
+    if (threadIdx.x < E) {
+        const int e = threadIdx.x;
+        blk_counts[(int64_t)blockIdx.x * E + e] = s_cnt[e];
+        if (blk_P != nullptr) {
+            float sp2 = s_P[0][e];
+#pragma unroll
+            for (int wv = 1; wv < NW; ++wv) sp2 += s_P[wv][e];
+            blk_P[(int64_t)blockIdx.x * E + e] = sp2;
+        }
+    }
+    if (threadIdx.x == 0 && blk_H != nullptr) {
+        float sh = s_H[0];
+#pragma unroll
+        for (int wv = 1; wv < NW; ++wv) sh += s_H[wv];
+        blk_H[blockIdx.x] = sh;
+    }
+}
+
+bool route_small_ok(int dtype, int E, int k, int d) {
+    (void)d;
+    return dtype == MOE_BF16 && E <= 16 && k <= E;
+}
+
+int route_small_tokens_per_block(int64_t T, int E) {
+    (void)E;
+    return T >= 32 * 256 ? 32 : 16;  // two token tiles per block still leave a block per CU
+}
+
+void launch_route_small(const void* x, const float* w_router, const float* sel_bias, int64_t T, int d, int E, int k,
+                        int score, int renorm, float* logits, int32_t* topk_idx, float* topk_w, int32_t* blk_counts,
+                        float* blk_P, float* blk_H, int32_t* ticket, hipStream_t s) {
+    const int tpb = route_small_tokens_per_block(T, E);
+    const unsigned nblk = (unsigned)((T + tpb - 1) / tpb);
+    const auto xb = static_cast<const uint16_t*>(x);
+    if (tpb == 32)
+        route_fused_kernel<2><<<nblk, kFusedRouteWaves * 64, 0, s>>>(xb, w_router, sel_bias, T, d, E, k, score, renorm,
+                                                                    logits, topk_idx, topk_w, blk_counts, blk_P,
+                                                                    blk_H, ticket);
+    else
+        route_fused_kernel<1><<<nblk, kFusedRouteWaves * 64, 0, s>>>(xb, w_router, sel_bias, T, d, E, k, score, renorm,
+                                                                    logits, topk_idx, topk_w, blk_counts, blk_P,
+                                                                    blk_H, ticket);
 }
 
 // Expert counts and balance statistics from the per-block partials, in fixed-order sums (float64
