@@ -29,29 +29,62 @@ __global__ __launch_bounds__(256) void perm_count_kernel(const int32_t* __restri
     for (int e = threadIdx.x; e < E; e += 256) tile_counts[(int64_t)blockIdx.x * E + e] = h[e];
 }
 
-// One block of 1024 threads; thread e owns expert e (E <= 1024). offsets = exclusive scan of the
-// rows each expert keeps (min(count, capacity) with a capacity); tile_base[tile][e] = how many
-// assignments to e the earlier tiles hold (the expert-local rank of the tile's first one).
+// One block of 1024 threads: J = 1024 / Ep threads per expert (Ep = E rounded up to a power of two),
+// thread (e, j) owning the contiguous tile range [j * C, (j + 1) * C), C = ceil(ntiles / J). Each
+// thread sums its range (loads issued 8 at a time), the J range sums of an expert are scanned in
+// LDS, and each thread then writes tile_base[tile][e] = assignments to e in earlier tiles over its
+// range. offsets = exclusive scan of the rows each expert keeps (min(count, capacity) with a
+// capacity).
 __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restrict__ tile_counts, int ntiles,
-                                                         int E, int capacity, int32_t* __restrict__ tile_base,
+                                                         int E, int Ep, int capacity, int32_t* __restrict__ tile_base,
                                                          int32_t* __restrict__ offsets) {
+    __shared__ int s_rng[1024];
     __shared__ int s_wave[17];
-    const int e = threadIdx.x;
+    const int J = 1024 / Ep;
+    const int e = threadIdx.x / J, j = threadIdx.x % J;
+    const int C = (ntiles + J - 1) / J;
+    const int tb = j * C, te = tb + C < ntiles ? tb + C : ntiles;
+    int sum = 0;
+    if (e < E) {
+        int tile = tb;
+        for (; tile + 8 <= te; tile += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = tile_counts[(int64_t)(tile + u) * E + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) sum += v[u];
+        }
+        for (; tile < te; ++tile) sum += tile_counts[(int64_t)tile * E + e];
+    }
+    s_rng[threadIdx.x] = sum;
+    __syncthreads();
+    // expert totals (thread e < Ep sums its expert's J ranges), scanned over experts
     int tot = 0;
-    if (e < E)
-        for (int tile = 0; tile < ntiles; ++tile) tot += tile_counts[(int64_t)tile * E + e];
-    const int kept = capacity > 0 && tot > capacity ? capacity : tot;
+    if (threadIdx.x < Ep)
+        for (int jj = 0; jj < J; ++jj) tot += s_rng[threadIdx.x * J + jj];
+    const int kept = threadIdx.x < E ? (capacity > 0 && tot > capacity ? capacity : tot) : 0;
     int total;
     const int start = block1024_excl_scan(kept, s_wave, &total);
-    if (e < E) {
-        offsets[e] = start;
-        int run = 0;
-        for (int tile = 0; tile < ntiles; ++tile) {
-            tile_base[(int64_t)tile * E + e] = run;
-            run += tile_counts[(int64_t)tile * E + e];
+    if (threadIdx.x < E) offsets[threadIdx.x] = start;
+    if (threadIdx.x == 0) offsets[E] = total;
+    if (e >= E) return;
+    int run = 0;
+    for (int jj = 0; jj < j; ++jj) run += s_rng[e * J + jj];
+    int tile = tb;
+    for (; tile + 8 <= te; tile += 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = tile_counts[(int64_t)(tile + u) * E + e];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            tile_base[(int64_t)(tile + u) * E + e] = run;
+            run += v[u];
         }
     }
-    if (e == 0) offsets[E] = total;
+    for (; tile < te; ++tile) {
+        tile_base[(int64_t)tile * E + e] = run;
+        run += tile_counts[(int64_t)tile * E + e];
+    }
 }
 
 // Stable rank of each assignment within its tile. The tile is processed as 16 chunks of 64
@@ -148,7 +181,9 @@ void launch_perm_count(const int32_t* topk_idx, int64_t A, int E, int32_t* tile_
 void launch_perm_scan(const int32_t* tile_counts, int ntiles, int64_t A, int E, int capacity, int32_t* tile_base,
                       int32_t* offsets, hipStream_t s) {
     (void)A;
-    perm_scan_kernel<<<1, 1024, 0, s>>>(tile_counts, ntiles, E, capacity, tile_base, offsets);
+    int Ep = 1;
+    while (Ep < E) Ep <<= 1;  // E <= 1024
+    perm_scan_kernel<<<1, 1024, 0, s>>>(tile_counts, ntiles, E, Ep, capacity, tile_base, offsets);
 }
 
 void launch_perm_rank(const int32_t* topk_idx, const int32_t* tile_base, const int32_t* offsets, int64_t A, int E,

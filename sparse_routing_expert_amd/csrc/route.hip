@@ -231,15 +231,14 @@ __device__ __forceinline__ void select_token(const float (&l)[EPL], const float 
 #pragma unroll
         for (int i = 0; i < EPL; ++i) best = key[i] > best ? key[i] : best;
         best = wave_max_u64(best);
-        const int e = key_index(best);
-        float le = -INFINITY;  // unbiased logit of the winner, from the lane that holds it
+        const int e = key_index(best);  // wave-uniform
+        // unbiased logit of the winner, read from the lane that holds it
+        float le = 0.f;
 #pragma unroll
-        for (int i = 0; i < EPL; ++i)
-            if (e == lane + 64 * i) {
-                key[i] = 0ull;
-                le = l[i];
-            }
-        le = wave_max(le);
+        for (int i = 0; i < EPL; ++i) {
+            if ((e >> 6) == i) le = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l[i]), e & 63));
+            if (e == lane + 64 * i) key[i] = 0ull;
+        }
         if (lane == j) {
             sel_e = e;
             sel_l = le;
