@@ -1442,11 +1442,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 }
 
 GemmPlan plan_gemm(int dtype, int64_t rows_per_group_hint, int n_out, int K) {
-    (void)rows_per_group_hint;
     (void)n_out;
     (void)K;
     GemmPlan p;
-    p.bm = dtype == MOE_BF16 ? 256 : 64;
+    // bf16: groups of a few dozen rows (decode batches) are bound by streaming their weights, which
+    // 64-row tiles with a deep operand ring do better than the 256-row persistent tiles
+    p.bm = dtype == MOE_BF16 ? (rows_per_group_hint <= kGemmSmallRowsMax ? 64 : 256) : 64;
     return p;
 }
 
@@ -1478,7 +1479,18 @@ void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* 
                          const int32_t* offsets, int e_begin, int n_groups, int64_t max_rows, int64_t dense_rows,
                          int n_out, int K, float* partials, hipStream_t s) {
     if (dtype == MOE_BF16) {
-        (void)bm;
+        if (bm == 64 && offsets != nullptr) {
+            // small segments: 64-row tiles, each block streaming its weight panel through an 8- or 9-stage
+            // LDS ring; 128-wide panels when 256-wide ones would leave most CUs without a tile
+            const int64_t est_tiles = (int64_t)n_groups * ((n_out + 127) / 128) / (epi == EPI_SWIGLU ? 1 : 2);
+            if (est_tiles >= 2 * device_cu_count())
+                launch_bf16_tiles<64, 256, 8, 8>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows,
+                                                 n_out, K, s);
+            else
+                launch_bf16_tiles<64, 128, 9, 8>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows,
+                                                 n_out, K, s);
+            return;
+        }
         launch_bf16_persistent<8, 3>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows, n_out, K,
                                      partials, s);
         return;

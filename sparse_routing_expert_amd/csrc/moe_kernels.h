@@ -64,6 +64,11 @@ enum Epilogue { EPI_SWIGLU = 0, EPI_GELU_BIAS = 1, EPI_BIAS = 2, EPI_F32 = 3 };
 struct GemmPlan {
     int bm;  // rows per tile
 };
+#ifndef MOE_GEMM_SMALL_ROWS_MAX
+#define MOE_GEMM_SMALL_ROWS_MAX 32
+#endif
+// bf16 grouped products whose groups average at most this many rows take 64-row tiles
+constexpr int64_t kGemmSmallRowsMax = MOE_GEMM_SMALL_ROWS_MAX;
 GemmPlan plan_gemm(int dtype, int64_t rows_per_group_hint, int n_out, int K);
 
 // C[rows, n_out] = epi(A[rows, K] * B_e^T) over groups e_begin.. (offsets != NULL; the kernel builds
