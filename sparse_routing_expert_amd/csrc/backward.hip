@@ -637,24 +637,42 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const float* __restrict__
 template <bool BF16>
 __global__ __launch_bounds__(256) void bwd_router_wgrad_kernel(const float* __restrict__ dl, const void* __restrict__ x,
                                                                int64_t T, int E, int d, float* __restrict__ partials) {
+    constexpr int EB = kRouterWgradExperts;
+    __shared__ float s_dl[kRouterChunk][EB];  // dl of the chunk's tokens for this block's experts
     const int c = blockIdx.x * 256 + threadIdx.x;
-    const int e0 = blockIdx.y * 8;
+    const int e0 = blockIdx.y * EB;
     const int64_t t0 = (int64_t)blockIdx.z * kRouterChunk;
-    if (c >= d) return;
     const int64_t t1 = t0 + kRouterChunk < T ? t0 + kRouterChunk : T;
-    float acc[8];
+    const int ne = E - e0 < EB ? E - e0 : EB;
+    for (int i = threadIdx.x; i < kRouterChunk * EB; i += 256) {
+        const int tt = i / EB, j = i % EB;
+        s_dl[tt][j] = (t0 + tt < t1 && j < ne) ? dl[(t0 + tt) * E + e0 + j] : 0.f;
+    }
+    __syncthreads();
+    if (c >= d) return;
+    float acc[EB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int64_t t = t0; t < t1; ++t) {
-        const float xv = ld_elem<BF16>(x, t * d + c);
+    for (int i = 0; i < EB; ++i) acc[i] = 0.f;
+    const int n = (int)(t1 - t0);
+    int tt = 0;
+    for (; tt + 4 <= n; tt += 4) {  // four token rows in flight
+        float xv[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if (e0 + i < E) acc[i] = fmaf(dl[t * E + e0 + i], xv, acc[i]);
+        for (int u = 0; u < 4; ++u) xv[u] = ld_elem<BF16>(x, (t0 + tt + u) * d + c);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < EB; ++i) acc[i] = fmaf(s_dl[tt + u][i], xv[u], acc[i]);
+    }
+    for (; tt < n; ++tt) {
+        const float xv = ld_elem<BF16>(x, (t0 + tt) * d + c);
+#pragma unroll
+        for (int i = 0; i < EB; ++i) acc[i] = fmaf(s_dl[tt][i], xv, acc[i]);
     }
     float* out = partials + (int64_t)blockIdx.z * E * d;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        if (e0 + i < E) out[(int64_t)(e0 + i) * d + c] = acc[i];
+    for (int i = 0; i < EB; ++i)
+        if (i < ne) out[(int64_t)(e0 + i) * d + c] = acc[i];
 }
 
 __global__ __launch_bounds__(256) void bwd_router_reduce_kernel(const float* __restrict__ partials, int nchunks,
@@ -672,13 +690,44 @@ __global__ __launch_bounds__(256) void bwd_router_dgrad_kernel(const float* __re
                                                                const float* __restrict__ dl,
                                                                const float* __restrict__ w_r, int64_t T, int E, int d,
                                                                void* __restrict__ dx) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= T * d) return;
-    const int64_t t = i / d;
-    const int c = (int)(i - t * d);
-    float acc = dx32[i];
-    for (int e = 0; e < E; ++e) acc = fmaf(dl[t * E + e], w_r[(int64_t)e * d + c], acc);
-    st_elem<BF16>(dx, i, acc);
+    constexpr int TB = kRouterDgradTokens, EC = 256;
+    __shared__ float s_dl[TB][EC];  // dl of the block's tokens, one chunk of experts at a time
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    const int64_t t0 = (int64_t)blockIdx.y * TB;
+    const int nt = T - t0 < TB ? (int)(T - t0) : TB;
+    const bool col = c < d;
+    float acc[TB];
+#pragma unroll
+    for (int q = 0; q < TB; ++q) acc[q] = (col && q < nt) ? dx32[(t0 + q) * d + c] : 0.f;
+    for (int e0 = 0; e0 < E; e0 += EC) {
+        const int ne = E - e0 < EC ? E - e0 : EC;
+        __syncthreads();
+        for (int i = threadIdx.x; i < TB * EC; i += 256) {
+            const int q = i / EC, j = i % EC;
+            s_dl[q][j] = (q < nt && j < ne) ? dl[(t0 + q) * E + e0 + j] : 0.f;
+        }
+        __syncthreads();
+        if (!col) continue;
+        int j = 0;
+        for (; j + 4 <= ne; j += 4) {  // four router rows in flight
+            float wv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) wv[u] = w_r[(int64_t)(e0 + j + u) * d + c];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int q = 0; q < TB; ++q) acc[q] = fmaf(s_dl[q][j + u], wv[u], acc[q]);
+        }
+        for (; j < ne; ++j) {
+            const float wv = w_r[(int64_t)(e0 + j) * d + c];
+#pragma unroll
+            for (int q = 0; q < TB; ++q) acc[q] = fmaf(s_dl[q][j], wv, acc[q]);
+        }
+    }
+    if (!col) return;
+#pragma unroll
+    for (int q = 0; q < TB; ++q)
+        if (q < nt) st_elem<BF16>(dx, (t0 + q) * d + c, acc[q]);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -738,14 +787,16 @@ size_t bwd_router_partials_bytes(int64_t T, int E, int d) {
 void launch_bwd_router(int dtype, const float* dl, const void* x, const float* w_r, const float* dx32, int64_t T,
                        int E, int d, float* partials, float* dw_r, void* dx, hipStream_t s) {
     const int nchunks = (int)((T + kRouterChunk - 1) / kRouterChunk);
-    dim3 gw(blocks_for(d), (unsigned)((E + 7) / 8), (unsigned)nchunks);
+    const unsigned cblk = (unsigned)((d + 255) / 256);
+    dim3 gw(cblk, (unsigned)((E + kRouterWgradExperts - 1) / kRouterWgradExperts), (unsigned)nchunks);
+    dim3 gd(cblk, (unsigned)((T + kRouterDgradTokens - 1) / kRouterDgradTokens));
     const int64_t n = (int64_t)E * d;
     if (dtype == MOE_BF16) {
         bwd_router_wgrad_kernel<true><<<gw, 256, 0, s>>>(dl, x, T, E, d, partials);
-        bwd_router_dgrad_kernel<true><<<blocks_for(T * d), 256, 0, s>>>(dx32, dl, w_r, T, E, d, dx);
+        bwd_router_dgrad_kernel<true><<<gd, 256, 0, s>>>(dx32, dl, w_r, T, E, d, dx);
     } else {
         bwd_router_wgrad_kernel<false><<<gw, 256, 0, s>>>(dl, x, T, E, d, partials);
-        bwd_router_dgrad_kernel<false><<<blocks_for(T * d), 256, 0, s>>>(dx32, dl, w_r, T, E, d, dx);
+        bwd_router_dgrad_kernel<false><<<gd, 256, 0, s>>>(dx32, dl, w_r, T, E, d, dx);
     }
     bwd_router_reduce_kernel<<<blocks_for(n), 256, 0, s>>>(partials, nchunks, n, dw_r);
 }

@@ -136,6 +136,8 @@ void launch_bwd_gate(const float* logits, const int32_t* topk_idx, const float* 
                      float aux_coef, int64_t T, int E, int k, int score, int renorm, float* dl, hipStream_t s);
 // dw_r = dl^T x (token chunks of kRouterChunk summed in order through `partials`), dx = dx32 + dl W_r
 constexpr int kRouterChunk = 256;
+constexpr int kRouterWgradExperts = 32;  // experts per dW_r block (x read once per 32 experts)
+constexpr int kRouterDgradTokens = 16;   // tokens per dx block (W_r read once per 16 tokens)
 size_t bwd_router_partials_bytes(int64_t T, int E, int d);
 void launch_bwd_router(int dtype, const float* dl, const void* x, const float* w_r, const float* dx32, int64_t T,
                        int E, int d, float* partials, float* dw_r, void* dx, hipStream_t s);
