@@ -425,29 +425,67 @@ void launch_sg_gemm_f32(const SgArgsF& a, int64_t max_rows, hipStream_t s) {
 
 // Per token (one wave): dg[t, j] = <dy[t], y_perm[row]> and dYp[row] = g[t, j] * dy[t] for each kept
 // slot (row = inv_pos[t*k + j] >= 0); dropped slots get dg = 0 and no row.
-template <bool BF16>
+template <bool BF16, int KMAX>
 __global__ __launch_bounds__(256) void bwd_combine_kernel(const void* __restrict__ dy, const void* __restrict__ y_perm,
                                                           const int32_t* __restrict__ inv_pos,
                                                           const float* __restrict__ topk_w, int64_t T, int d, int k,
                                                           float* __restrict__ dg, void* __restrict__ dYp) {
+    constexpr int EB = BF16 ? 2 : 4, EPV = 16 / EB;  // element bytes, elements per 16-byte vector
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int64_t t = (int64_t)blockIdx.x * 4 + wave;
     if (t >= T) return;
-    for (int j = 0; j < k; ++j) {
-        const int p = inv_pos[t * k + j];
-        if (p < 0) {
-            if (lane == 0) dg[t * k + j] = 0.f;
-            continue;
+    const int mypos = lane < k ? inv_pos[t * k + lane] : -1;
+    const float myg = lane < k ? topk_w[t * k + lane] : 0.f;
+    const int64_t row_bytes = (int64_t)d * EB;
+    const uint8_t* dyr = static_cast<const uint8_t*>(dy) + t * row_bytes;
+    const uint8_t* yp = static_cast<const uint8_t*>(y_perm);
+    uint8_t* dyp = static_cast<uint8_t*>(dYp);
+    float dot[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) dot[j] = 0.f;
+    const int nvec = d / EPV;
+    for (int c0 = lane; c0 < nvec; c0 += 64) {
+        float f[EPV];
+        const u32x4 dv = ld16(dyr + (int64_t)c0 * 16);
+        if (BF16) unpack8(dv, f);
+        else
+#pragma unroll
+            for (int i = 0; i < EPV; ++i) f[i] = __uint_as_float(dv[i]);
+        u32x4 yv[KMAX];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            const int p = j < k ? __builtin_amdgcn_readlane(mypos, j) : -1;
+            if (p >= 0) yv[j] = ld16(yp + (int64_t)p * row_bytes + (int64_t)c0 * 16);
         }
-        const float gj = topk_w[t * k + j];
-        float dot = 0.f;
-        for (int i = lane; i < d; i += 64) {
-            const float v = ld_elem<BF16>(dy, t * d + i);
-            dot = fmaf(v, ld_elem<BF16>(y_perm, (int64_t)p * d + i), dot);
-            st_elem<BF16>(dYp, (int64_t)p * d + i, gj * v);
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            const int p = j < k ? __builtin_amdgcn_readlane(mypos, j) : -1;
+            if (p < 0) continue;
+            const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(myg), j));
+            float yf[EPV], o[EPV];
+            if (BF16) unpack8(yv[j], yf);
+            else
+#pragma unroll
+                for (int i = 0; i < EPV; ++i) yf[i] = __uint_as_float(yv[j][i]);
+#pragma unroll
+            for (int i = 0; i < EPV; ++i) {
+                dot[j] = fmaf(f[i], yf[i], dot[j]);
+                o[i] = g * f[i];
+            }
+            u32x4 ov;
+            if (BF16) ov = pack8(o);
+            else
+#pragma unroll
+                for (int i = 0; i < EPV; ++i) ov[i] = __float_as_uint(o[i]);
+            st16(dyp + (int64_t)p * row_bytes + (int64_t)c0 * 16, ov);
         }
-        dot = wave_sum(dot);
-        if (lane == 0) dg[t * k + j] = dot;
+    }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        if (j >= k) break;
+        const int p = __builtin_amdgcn_readlane(mypos, j);
+        const float s = wave_sum(dot[j]);
+        if (lane == 0) dg[t * k + j] = p < 0 ? 0.f : s;
     }
 }
 
@@ -485,21 +523,38 @@ __global__ __launch_bounds__(256) void bwd_act_bwd_kernel(const float* __restric
 }
 
 // dx32[t] = sum over kept slots of dXp[inv_pos[t*k + j]] (+ extra[t]), fp32, in slot order.
+template <int KMAX>
 __global__ __launch_bounds__(256) void bwd_unpermute_kernel(const float* __restrict__ dXp,
                                                             const int32_t* __restrict__ inv_pos,
                                                             const float* __restrict__ extra, int64_t T, int d, int k,
                                                             float* __restrict__ dx32) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= T * d) return;
-    const int64_t t = i / d;
-    const int c = (int)(i - t * d);
-    float acc = 0.f;
-    for (int j = 0; j < k; ++j) {
-        const int p = inv_pos[t * k + j];
-        if (p >= 0) acc += dXp[(int64_t)p * d + c];
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    const int mypos = lane < k ? inv_pos[t * k + lane] : -1;
+    const int nvec = d / 4;
+    for (int c0 = lane; c0 < nvec; c0 += 64) {
+        floatx4 v[KMAX];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            const int p = j < k ? __builtin_amdgcn_readlane(mypos, j) : -1;
+            if (p >= 0) v[j] = *reinterpret_cast<const floatx4*>(dXp + (int64_t)p * d + (int64_t)c0 * 4);
+        }
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            const int p = j < k ? __builtin_amdgcn_readlane(mypos, j) : -1;
+            if (p < 0) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] += v[j][i];
+        }
+        if (extra != nullptr) {
+            const floatx4 xe = *reinterpret_cast<const floatx4*>(extra + t * d + (int64_t)c0 * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] += xe[i];
+        }
+        *reinterpret_cast<floatx4*>(dx32 + t * d + (int64_t)c0 * 4) = floatx4{acc[0], acc[1], acc[2], acc[3]};
     }
-    if (extra != nullptr) acc += extra[i];
-    dx32[i] = acc;
 }
 
 // Column sums per group: out[g][c] = sum over rows r in [offsets[g], offsets[g+1]) of src[r][c],
@@ -739,8 +794,21 @@ static unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 void launch_bwd_combine(int dtype, const void* dy, const void* y_perm, const int32_t* inv_pos, const float* topk_w,
                         int64_t T, int d, int k, float* dg, void* dYp, hipStream_t s) {
     const unsigned nb = (unsigned)((T + 3) / 4);
-    if (dtype == MOE_BF16) bwd_combine_kernel<true><<<nb, 256, 0, s>>>(dy, y_perm, inv_pos, topk_w, T, d, k, dg, dYp);
-    else bwd_combine_kernel<false><<<nb, 256, 0, s>>>(dy, y_perm, inv_pos, topk_w, T, d, k, dg, dYp);
+#define MOE_BWD_COMBINE(B_, K_) bwd_combine_kernel<B_, K_><<<nb, 256, 0, s>>>(dy, y_perm, inv_pos, topk_w, T, d, k, dg, dYp)
+    if (dtype == MOE_BF16) {
+        if (k <= 2) MOE_BWD_COMBINE(true, 2);
+        else if (k <= 4) MOE_BWD_COMBINE(true, 4);
+        else if (k <= 8) MOE_BWD_COMBINE(true, 8);
+        else if (k <= 16) MOE_BWD_COMBINE(true, 16);
+        else MOE_BWD_COMBINE(true, 32);
+    } else {
+        if (k <= 2) MOE_BWD_COMBINE(false, 2);
+        else if (k <= 4) MOE_BWD_COMBINE(false, 4);
+        else if (k <= 8) MOE_BWD_COMBINE(false, 8);
+        else if (k <= 16) MOE_BWD_COMBINE(false, 16);
+        else MOE_BWD_COMBINE(false, 32);
+    }
+#undef MOE_BWD_COMBINE
 }
 
 void launch_bwd_act_fwd(int dtype, const void* pre, int64_t n_rows, int F, int act, void* h, hipStream_t s) {
@@ -758,7 +826,12 @@ void launch_bwd_act_bwd(int dtype, const float* dh, const void* pre, int64_t n_r
 
 void launch_bwd_unpermute(const float* dXp, const int32_t* inv_pos, const float* extra, int64_t T, int d, int k,
                           float* dx32, hipStream_t s) {
-    bwd_unpermute_kernel<<<blocks_for(T * d), 256, 0, s>>>(dXp, inv_pos, extra, T, d, k, dx32);
+    const unsigned nb = (unsigned)((T + 3) / 4);
+    if (k <= 2) bwd_unpermute_kernel<2><<<nb, 256, 0, s>>>(dXp, inv_pos, extra, T, d, k, dx32);
+    else if (k <= 4) bwd_unpermute_kernel<4><<<nb, 256, 0, s>>>(dXp, inv_pos, extra, T, d, k, dx32);
+    else if (k <= 8) bwd_unpermute_kernel<8><<<nb, 256, 0, s>>>(dXp, inv_pos, extra, T, d, k, dx32);
+    else if (k <= 16) bwd_unpermute_kernel<16><<<nb, 256, 0, s>>>(dXp, inv_pos, extra, T, d, k, dx32);
+    else bwd_unpermute_kernel<32><<<nb, 256, 0, s>>>(dXp, inv_pos, extra, T, d, k, dx32);
 }
 
 void launch_bwd_colsum(int dtype, const void* src, const int32_t* offsets, int e_begin, int G, int ncols, float* out,
