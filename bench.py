@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0: automatic)")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="also time hipBLASLt (torch.mm) on the gate/up shape, dense and per expert, for context")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a HIP graph captured once (every kernel of the step runs "
+                         "on each replay; the output is checked bit for bit against the eager step)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run two plain 1 GiB device copies (calibration for the HBM byte counters)")
     return ap.parse_args()
@@ -102,6 +105,8 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     ev_ms = ev0.elapsed_time(ev1) / args.steps
     value = cfg.T / (ms_per_step / 1e3)
+
+    graph = graph_timing(L, args.steps) if args.graph else None
 
     # ---- per-stage timings (HIP events on the launch stream, caches flushed before each) ------
     flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
@@ -184,6 +189,7 @@ def main():
         "route_GB/s": stages["route"]["GB/s"],
         "assignments_per_s": round(value * cfg.k, 1),
         "event_ms_per_step": round(ev_ms, 4),
+        "graph_replay": graph,
         "vendor_gemm": vendor,
         "capacity_permute": next_rows["capacity_permute"],
         "bias_update": next_rows["bias_update"],
@@ -192,6 +198,32 @@ def main():
         "input_gen_s": round(gen_s, 2),
     }
     print(json.dumps(out), flush=True)
+
+
+def graph_timing(L, steps):
+    """The step captured once into a HIP graph (torch.cuda.CUDAGraph over the library's launches on
+    the capture stream) and replayed `steps` times; the replayed output must equal the eager one bit
+    for bit (the kernels are deterministic)."""
+    import torch
+
+    L.forward()
+    torch.cuda.synchronize()
+    ref = L.y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.forward()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(L.y.view(torch.int16) if L.y.dtype == torch.bfloat16 else L.y, ref.view(torch.int16)
+                            if ref.dtype == torch.bfloat16 else ref))
+    w0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - w0) * 1e3 / steps
+    del g
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(L.T / (ms / 1e3), 1), "matches_eager": same}
 
 
 def next_row_timings(cfg, L, flush, stream, reps):
