@@ -13,19 +13,20 @@
 // tiles sweep the column panels: the row tiles that share a weight panel run on the same XCD and
 // read it through that XCD's L2 once.
 //
-// bf16 path (one kernel per projection): 256 threads = 2 x 2 waves, a BM x BN output tile (SwiGLU:
-// BN/2 gate columns and the matching BN/2 up columns, so a lane holds gate and up of the same
-// output element), v_mfma_f32_32x32x16_bf16 with fp32 accumulators. Operands stream into an NS-
-// stage LDS ring (K slices of 32) with buffer_load ... lds (global -> LDS without registers),
-// issued NS-1 stages ahead; buffer descriptors bound each tile's rows, so rows past an expert's end
-// or columns past n_out read as zero and nothing is clamped. LDS rows are 64 bytes; their four
-// 16-byte chunks are XOR-swizzled by (row >> 2) & 3, which measured conflict-free for the 128-bit
-// operand reads on gfx950 (16 lanes per LDS cycle, 64 banks). The steady-state loop is straight-
-// line with its issue order pinned: MFMAs of one 16-wide K half interleaved with the LDS reads of
-// the next half and, evenly spaced (one every four MFMAs), half of a future stage's DMA. Each CU
-// moves about 64 bytes per clock from L1/L2, so a stage's operands need roughly half the MFMA time;
-// bunched loads would stall the waves' in-order issue, MFMAs included. Waits on the DMA are
-// explicit (vmcnt), because the compiler cannot see it.
+// bf16 kernels (one launch per projection, plus a short fixup launch when the last round of tiles is
+// split along K):
+//  - gemm_bf16_persistent_kernel, the main path: one block of eight waves per CU walks 256 x 256
+//    output tiles (SwiGLU: 128 gate and the matching 128 up columns, so a lane holds gate and up of
+//    the same output element) in an XCD-aware order; two groups of four waves alternate LDS
+//    fragment reads and MFMA clusters (ping-pong), and the LDS ring runs on across tiles.
+//  - gemm_bf16_kernel: four waves on one BM x BN tile with a deeper ring, for groups of a few dozen
+//    rows (decode batches), whose time is spent streaming the weight panels.
+// Both use v_mfma_f32_32x32x16_bf16 with fp32 accumulators. Operands stream into an LDS ring (K
+// slices of 32) with buffer_load ... lds (global -> LDS without registers); buffer descriptors bound
+// each tile's rows, so rows past an expert's end or columns past n_out read as zero and nothing is
+// clamped. LDS rows are 64 bytes; their four 16-byte chunks are XOR-swizzled by (row >> 2) & 3,
+// which measured conflict-free for the 128-bit operand reads on gfx950 (16 lanes per LDS cycle, 64
+// banks). Waits on the DMA are explicit (vmcnt), because the compiler cannot see it.
 #include "moe_common.h"
 #include "moe_kernels.h"
 #include "../../include/moe.h"
@@ -388,453 +389,6 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
         }
     }
 }
-
-// Register-staged variant of the same tile: operands come to
-// VGPRs with buffer loads two stages ahead (two staging sets) and each stage is written to a
-// 2-slot LDS ring with ds_write_b128. Needs less LDS than the DMA ring and leaves the waits to the
-// compiler. Same fragment layout, swizzle and epilogue as gemm_bf16_kernel; the pinned schedule
-// spreads a wave's 8 buffer loads and 8 LDS writes per stage evenly over the 32 MFMAs.
-template <int BM, int BN, int EPI, int GM>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_rs_kernel(const uint16_t* __restrict__ A,
-                                                              const uint16_t* __restrict__ B,
-                                                              const uint16_t* __restrict__ bias,
-                                                              uint16_t* __restrict__ C,
-                                                              const int32_t* __restrict__ offsets, int e_begin,
-                                                              int n_groups, int64_t dense_rows, int n_out, int K) {
-    constexpr int BK = 32, WM = 2, WN = 2, NSL = 2;
-    constexpr bool GATED = EPI == EPI_SWIGLU;
-    constexpr int WTM = BM / WM, TM = WTM / 32;
-    constexpr int BNO = GATED ? BN / 2 : BN, WTNO = BNO / WN, TNO = WTNO / 32, TN = GATED ? 2 * TNO : TNO;
-    constexpr int ROWS = BM + BN;
-    constexpr int STAGE_ELEMS = ROWS * BK;
-    constexpr int NQ = ROWS / 64;  // 16-byte chunks per thread per stage
-    static_assert(TM >= 1 && TNO >= 1 && BM % 64 == 0 && BN % 128 == 0, "tile shape");
-    constexpr int STEPS = TM * TN > 2 * NQ ? TM * TN : 2 * NQ;  // writes every other step of phase A
-    constexpr int RNH = NQ / 2;                                  // loads per phase (first half in A)
-    constexpr int RSP = STEPS / RNH;
-    static_assert(RSP >= 2 && 2 * (RNH - 1) <= RSP * (RNH - 1) + 1 && STEPS >= TM + TN, "RS slots");
-    static_assert(NSL * STAGE_ELEMS * 2 >= 1029 * 4, "schedule scratch");
-
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[NSL * STAGE_ELEMS];
-    int* s_ts = reinterpret_cast<int*>(lds);
-    int* s_wave = s_ts + 1025;
-    if (offsets) build_schedule<BM, 256>(offsets, e_begin, n_groups, s_ts, s_wave);
-    const TileCoord tc = decode_tile<BM, BNO, GM>(offsets, s_ts, e_begin, n_groups, dense_rows, n_out);
-    if (!tc.valid) return;
-    __syncthreads();
-
-    const int tid = threadIdx.x, lane = lane_id();
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave % WM, wn = wave / WM;
-    const int64_t n_b_rows = GATED ? 2 * (int64_t)n_out : n_out;
-    const uint16_t* Bg = B + (int64_t)tc.e * n_b_rows * K;
-    const int64_t a_rows = tc.row_end - tc.row0 < BM ? tc.row_end - tc.row0 : BM;
-    const int bn_part = GATED ? BN / 2 : BN;
-    const int bcols = n_out - tc.n0 < bn_part ? n_out - tc.n0 : bn_part;
-    const __amdgpu_buffer_rsrc_t ra =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(A + tc.row0 * K), (short)0, (int)(a_rows * K * 2), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rb0 = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(Bg + (int64_t)tc.n0 * K), (short)0, (int)((int64_t)bcols * K * 2), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rb1 = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(Bg + (int64_t)(GATED ? n_out + tc.n0 : tc.n0) * K), (short)0, (int)((int64_t)bcols * K * 2),
-        0x00020000);
-
-    // chunk q of this thread: LDS rows [(q * 4 + wave) * 16, +16), lane -> (row, 16-byte chunk)
-    int voff[NQ];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        const int R = (q * 4 + wave) * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ swz(R);
-        int row;
-        if (q < BM / 64) row = R;
-        else if (!GATED || q < (BM + BN / 2) / 64) row = R - BM;
-        else row = R - BM - BN / 2;
-        voff[q] = row * K * 2 + c * 16;
-    }
-    const int wofs = wave * 512 + lane * 8;  // element offset of this lane's 16 bytes in chunk q = 0
-    int a_off[TM], a_sw[TM], b_off[TN], b_sw[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int r = wm * WTM + i * 32 + (lane & 31);
-        a_off[i] = r * BK;
-        a_sw[i] = swz(r);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int jj = j < TNO ? j : j - TNO;
-        const int r = BM + (GATED && j >= TNO ? BN / 2 : 0) + wn * WTNO + jj * 32 + (lane & 31);
-        b_off[j] = r * BK;
-        b_sw[j] = swz(r);
-    }
-    const int khalf = lane >> 5;
-    floatx16 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-    bf16x8 fa[2][TM], fb[2][TN];
-    u32x4 stg[2][NQ];
-
-#define RS_RSRC(q) ((q) < BM / 64 ? ra : ((!GATED || (q) < (BM + BN / 2) / 64) ? rb0 : rb1))
-#define RS_LOAD1(set, q, stage)                                                                           \
-    stg[set][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(RS_RSRC(q), voff[q],    \
-                                                                                  (stage) * BK * 2, 0));
-#define RS_WRITE1(set, q, slot)                                                                           \
-    *reinterpret_cast<u32x4*>(lds + (slot) * STAGE_ELEMS + (q) * 2048 + wofs) = stg[set][q];
-#define RS_READ(slot, kk, f)                                                                              \
-    {                                                                                                     \
-        const uint16_t* L_ = lds + (slot) * STAGE_ELEMS;                                                  \
-        const int c_ = (kk) * 2 + khalf;                                                                  \
-        _Pragma("unroll") for (int i = 0; i < TM; ++i) fa[f][i] =                                          \
-            *reinterpret_cast<const bf16x8*>(L_ + a_off[i] + ((c_ ^ a_sw[i]) << 3));                      \
-        _Pragma("unroll") for (int j = 0; j < TN; ++j) fb[f][j] =                                          \
-            *reinterpret_cast<const bf16x8*>(L_ + b_off[j] + ((c_ ^ b_sw[j]) << 3));                      \
-    }
-    // One iteration kt: phase A = MFMAs on (kt, first K half), reads of (kt, second half), LDS write
-    // of stage kt+1 from staging set SET; barrier; phase B = MFMAs on (kt, second half), reads of
-    // (kt+1, first half), loads of stage kt+3 into SET. SET = (kt + 1) & 1 is a constant per copy.
-#define RS_STEP(kt_, SET, DO_W, DO_L)                                                                     \
-    {                                                                                                     \
-        const int ktv = (kt_);                                                                            \
-        const uint16_t* L1 = lds + (ktv & 1) * STAGE_ELEMS;                                               \
-        const int c1 = 2 + khalf;                                                                         \
-        const int wslot = (ktv + 1) & 1;                                                                  \
-        _Pragma("unroll") for (int t = 0; t < STEPS; ++t) {                                               \
-            if (t < TM * TN)                                                                              \
-                acc[t / TN][t % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][t / TN], fb[0][t % TN], \
-                                                                              acc[t / TN][t % TN], 0, 0, 0); \
-            if (t < TM) fa[1][t] = *reinterpret_cast<const bf16x8*>(L1 + a_off[t] + ((c1 ^ a_sw[t]) << 3)); \
-            else if (t < TM + TN)                                                                         \
-                fb[1][t - TM] = *reinterpret_cast<const bf16x8*>(L1 + b_off[t - TM] + ((c1 ^ b_sw[t - TM]) << 3)); \
-            if (t % 2 == 0 && t / 2 < NQ) {                                                               \
-                if (DO_W) { RS_WRITE1(SET, t / 2, wslot) }                                                \
-            }                                                                                             \
-            if (t % RSP == 1 && t / RSP < RNH) {                                                          \
-                if (DO_L) { RS_LOAD1(SET, t / RSP, ktv + 3) }                                             \
-            }                                                                                             \
-            __builtin_amdgcn_sched_barrier(0);                                                            \
-        }                                                                                                 \
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                                 \
-        __builtin_amdgcn_sched_barrier(0);                                                                \
-        const uint16_t* L0 = lds + wslot * STAGE_ELEMS;                                                   \
-        const int c0 = khalf;                                                                             \
-        const int nstage = ktv + 3;                                                                       \
-        _Pragma("unroll") for (int t = 0; t < STEPS; ++t) {                                               \
-            if (t < TM * TN)                                                                              \
-                acc[t / TN][t % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][t / TN], fb[1][t % TN], \
-                                                                              acc[t / TN][t % TN], 0, 0, 0); \
-            if (t < TM) {                                                                                 \
-                if (DO_W) fa[0][t] = *reinterpret_cast<const bf16x8*>(L0 + a_off[t] + ((c0 ^ a_sw[t]) << 3)); \
-            } else if (t < TM + TN) {                                                                     \
-                if (DO_W)                                                                                 \
-                    fb[0][t - TM] =                                                                       \
-                        *reinterpret_cast<const bf16x8*>(L0 + b_off[t - TM] + ((c0 ^ b_sw[t - TM]) << 3)); \
-            }                                                                                             \
-            if (t % RSP == 1 && RNH + t / RSP < NQ) {                                                     \
-                if (DO_L) { RS_LOAD1(SET, RNH + t / RSP, nstage) }                                        \
-            }                                                                                             \
-            __builtin_amdgcn_sched_barrier(0);                                                            \
-        }                                                                                                 \
-    }
-
-    const int nk = K / BK;
-    // prologue: stage 0 -> set 0 -> slot 0; stage 1 -> set 1; stage 2 -> set 0
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) RS_LOAD1(0, q, 0)
-    if (nk > 1) {
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) RS_LOAD1(1, q, 1)
-    }
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) RS_WRITE1(0, q, 0)
-    if (nk > 2) {
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) RS_LOAD1(0, q, 2)
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    RS_READ(0, 0, 0)
-    int kt = 0;
-    for (; kt + 4 < nk; kt += 2) {
-        RS_STEP(kt, 1, true, true)
-        RS_STEP(kt + 1, 0, true, true)
-    }
-    // tail (kt is even here; at most four iterations): plain order, static staging sets
-#define RS_TAIL(j, SET)                                                                                   \
-    if (kt + (j) < nk) {                                                                                  \
-        const int ktv = kt + (j);                                                                         \
-        const bool w = ktv + 1 < nk, l = ktv + 3 < nk;                                                    \
-        RS_READ(ktv & 1, 1, 1)                                                                            \
-        _Pragma("unroll") for (int i = 0; i < TM; ++i) _Pragma("unroll") for (int jj = 0; jj < TN; ++jj)  \
-            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][i], fb[0][jj], acc[i][jj], 0, 0, 0); \
-        if (w) {                                                                                          \
-            _Pragma("unroll") for (int q = 0; q < NQ; ++q) { RS_WRITE1(SET, q, (ktv + 1) & 1) }           \
-        }                                                                                                 \
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                                 \
-        if (w) RS_READ((ktv + 1) & 1, 0, 0)                                                               \
-        _Pragma("unroll") for (int i = 0; i < TM; ++i) _Pragma("unroll") for (int jj = 0; jj < TN; ++jj)  \
-            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][jj], acc[i][jj], 0, 0, 0); \
-        if (l) {                                                                                          \
-            _Pragma("unroll") for (int q = 0; q < NQ; ++q) { RS_LOAD1(SET, q, ktv + 3) }                  \
-        }                                                                                                 \
-    }
-    RS_TAIL(0, 1)
-    RS_TAIL(1, 0)
-    RS_TAIL(2, 1)
-    RS_TAIL(3, 0)
-#undef RS_TAIL
-#undef RS_RSRC
-#undef RS_LOAD1
-#undef RS_WRITE1
-#undef RS_READ
-#undef RS_STEP
-
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int j = 0; j < TNO; ++j) {
-            const int col = tc.n0 + wn * WTNO + j * 32 + (lane & 31);
-            if (col >= n_out) continue;
-            float bcol = 0.f;
-            if (EPI != EPI_SWIGLU && bias != nullptr) bcol = bf16_to_f32(bias[(int64_t)tc.e * n_out + col]);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t row = tc.row0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
-                if (row >= tc.row_end) continue;
-                float out;
-                if (EPI == EPI_SWIGLU) out = silu_f(acc[i][j][v]) * acc[i][j + TNO][v];
-                else if (EPI == EPI_GELU_BIAS) out = gelu_f(acc[i][j][v] + bcol);
-                else out = acc[i][j][v] + bcol;
-                C[row * n_out + col] = f32_to_bf16(out);
-            }
-        }
-    }
-}
-
-template <int BM, int BN, int GM>
-void launch_bf16_rs_tiles(int epi, const void* A, const void* B, const void* bias, void* C, const int32_t* offsets,
-                          int e_begin, int n_groups, int64_t max_rows, int64_t dense_rows, int n_out, int K,
-                          hipStream_t s) {
-    const int bno = epi == EPI_SWIGLU ? BN / 2 : BN;
-    const int64_t m_tiles = offsets ? (max_rows + BM - 1) / BM + n_groups : (dense_rows + BM - 1) / BM;
-    const int64_t tiles = m_tiles * ((n_out + bno - 1) / bno);
-    const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
-    const auto a = static_cast<const uint16_t*>(A);
-    const auto b = static_cast<const uint16_t*>(B);
-    const auto bi = static_cast<const uint16_t*>(bias);
-    auto c = static_cast<uint16_t*>(C);
-    if (epi == EPI_SWIGLU)
-        gemm_bf16_rs_kernel<BM, BN, EPI_SWIGLU, GM><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
-                                                                        dense_rows, n_out, K);
-    else if (epi == EPI_GELU_BIAS)
-        gemm_bf16_rs_kernel<BM, BN, EPI_GELU_BIAS, GM><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
-                                                                           dense_rows, n_out, K);
-    else
-        gemm_bf16_rs_kernel<BM, BN, EPI_BIAS, GM><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
-                                                                      dense_rows, n_out, K);
-}
-
-// Eight-wave ping-pong variant of the 256 x 256 tile (two waves per SIMD). Waves 0-3 (group 0) and
-// 4-7 (group 1) each own half of the output rows; a wave computes a 64 x 128 sub-tile (SwiGLU:
-// 64 gate + 64 up columns). Every wave alternates a memory cluster (the LDS fragment reads of one
-// 32-wide K stage, its group's half of the stage D ahead as buffer_load ... lds, and the waits) and
-// a compute cluster (16 MFMAs on those fragments), with a block barrier after each. Group 1 starts
-// one barrier late, so on every SIMD one wave issues MFMAs back to back while the other issues its
-// memory operations: a stalled load no longer holds up the matrix core. Group 0 loads the A rows of
-// each stage and group 1 the B rows. The ring has D + 1 stages; a slot is refilled only after both
-// groups' reads of it have returned (lgkmcnt(0) before every barrier that ends a memory cluster).
-// Per output element the K order is the same as gemm_bf16_kernel's, so results are bitwise equal.
-template <int EPI, int GM, int D>
-__global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(const uint16_t* __restrict__ A,
-                                                              const uint16_t* __restrict__ B,
-                                                              const uint16_t* __restrict__ bias,
-                                                              uint16_t* __restrict__ C,
-                                                              const int32_t* __restrict__ offsets, int e_begin,
-                                                              int n_groups, int64_t dense_rows, int n_out, int K) {
-    constexpr int BM = 256, BN = 256, BK = 32, NS = D + 1;
-    constexpr bool GATED = EPI == EPI_SWIGLU;
-    constexpr int TM = 2;  // 64 rows per wave
-    constexpr int BNO = GATED ? BN / 2 : BN, WTNO = BNO / 2, TNO = WTNO / 32, TN = GATED ? 2 * TNO : TNO;
-    constexpr int STAGE_ELEMS = (BM + BN) * BK;  // 512 rows of 64 bytes
-    constexpr int STAGE_BYTES = STAGE_ELEMS * 2;
-    constexpr int NQ = 4;  // DMA instructions per wave per stage (a group moves 256 rows = 16 KB)
-    static_assert(TN == 4 && D >= 2 && D <= 6, "tile shape");
-    static_assert(NS * STAGE_BYTES >= 1029 * 4 && NS * STAGE_BYTES <= 160 * 1024, "LDS budget");
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE_ELEMS];
-    int* s_ts = reinterpret_cast<int*>(lds);
-    int* s_wave = s_ts + 1025;
-
-    if (offsets) build_schedule<BM, 512>(offsets, e_begin, n_groups, s_ts, s_wave);
-    const TileCoord tc = decode_tile<BM, BNO, GM>(offsets, s_ts, e_begin, n_groups, dense_rows, n_out);
-    if (!tc.valid) return;  // uniform per block
-    __syncthreads();
-
-    const int tid = threadIdx.x, lane = lane_id();
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = wave >> 2, wig = wave & 3;
-    const int wm = wig & 1, wn = wig >> 1;
-    const int64_t n_b_rows = GATED ? 2 * (int64_t)n_out : n_out;
-    const uint16_t* Bg = B + (int64_t)tc.e * n_b_rows * K;
-    const int64_t a_rows = tc.row_end - tc.row0 < BM ? tc.row_end - tc.row0 : BM;
-    const int bn_part = GATED ? BN / 2 : BN;
-    const int bcols = n_out - tc.n0 < bn_part ? n_out - tc.n0 : bn_part;
-    const i32x4 ra = make_rsrc(A + tc.row0 * K, (uint32_t)(a_rows * K * 2));
-    const i32x4 rb0 = make_rsrc(Bg + (int64_t)tc.n0 * K, (uint32_t)((int64_t)bcols * K * 2));
-    const i32x4 rb1 = make_rsrc(Bg + (int64_t)(GATED ? n_out + tc.n0 : tc.n0) * K, (uint32_t)((int64_t)bcols * K * 2));
-    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)lds;
-
-    // DMA q of this wave: LDS rows grp * 256 + (q * 4 + wig) * 16 + [0, 16); lane -> (row, chunk)
-    int voff[NQ];
-    i32x4 rs[NQ];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        const int Rl = (q * 4 + wig) * 16 + (lane >> 2);  // row within the group's 256
-        const int R = grp * 256 + Rl;
-        const int c = (lane & 3) ^ swz(R);
-        int row;
-        if (grp == 0) {
-            row = Rl;
-            rs[q] = ra;
-        } else if (GATED && q >= 2) {
-            row = Rl - 128;
-            rs[q] = rb1;
-        } else {
-            row = Rl;
-            rs[q] = rb0;
-        }
-        voff[q] = row * K * 2 + c * 16;
-    }
-    int a_off[TM], a_sw[TM], b_off[TN], b_sw[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int r = grp * 128 + wm * 64 + i * 32 + (lane & 31);
-        a_off[i] = r * BK;
-        a_sw[i] = swz(r);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int jj = j < TNO ? j : j - TNO;
-        const int r = BM + (GATED && j >= TNO ? BN / 2 : 0) + wn * WTNO + jj * 32 + (lane & 31);
-        b_off[j] = r * BK;
-        b_sw[j] = swz(r);
-    }
-    const int khalf = lane >> 5;
-
-    floatx16 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-    bf16x8 fa[2][TM], fb[2][TN];
-
-#define PP_ISSUE(st_)                                                                                     \
-    {                                                                                                     \
-        const int st__ = (st_);                                                                           \
-        const uint32_t sbase = lds_base + (st__ % NS) * STAGE_BYTES + grp * 16384 + wig * 1024;           \
-        const int soff = __builtin_amdgcn_readfirstlane(st__ * BK * 2);                                   \
-        _Pragma("unroll") for (int q = 0; q < NQ; ++q) dma16(sbase + q * 4096, voff[q], rs[q], soff);     \
-    }
-#define PP_READ(st_)                                                                                      \
-    {                                                                                                     \
-        const uint16_t* L_ = lds + ((st_) % NS) * STAGE_ELEMS;                                            \
-        _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                                \
-            const int c_ = kk * 2 + khalf;                                                                \
-            _Pragma("unroll") for (int i = 0; i < TM; ++i) fa[kk][i] =                                     \
-                *reinterpret_cast<const bf16x8*>(L_ + a_off[i] + ((c_ ^ a_sw[i]) << 3));                  \
-            _Pragma("unroll") for (int j = 0; j < TN; ++j) fb[kk][j] =                                     \
-                *reinterpret_cast<const bf16x8*>(L_ + b_off[j] + ((c_ ^ b_sw[j]) << 3));                  \
-        }                                                                                                 \
-    }
-#define PP_MMA                                                                                            \
-    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) _Pragma("unroll") for (int i = 0; i < TM; ++i)       \
-        _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                    \
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
-#define PP_END_MEM                                                                                        \
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                                    \
-    lds_barrier();                                                                                        \
-    __builtin_amdgcn_sched_barrier(0);
-
-    const int nk = K / BK;
-    const int npro = nk < D ? nk : D;
-    for (int p = 0; p < npro; ++p) PP_ISSUE(p)
-    wait_stages<NQ>(npro - 1);  // stage 0 of this wave has landed
-    lds_barrier();
-    if (grp == 1) lds_barrier();  // group 1 runs one cluster behind group 0
-    __builtin_amdgcn_sched_barrier(0);
-    int st = 0;
-    for (; st + D < nk; ++st) {
-        PP_READ(st)
-        PP_ISSUE(st + D)
-        wait_vm<(D - 1) * NQ>();  // stage st + 1 of this wave has landed
-        PP_END_MEM
-        PP_MMA
-        __builtin_amdgcn_sched_barrier(0);
-        lds_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    for (; st < nk; ++st) {
-        PP_READ(st)
-        wait_stages<NQ>(nk - st - 2);
-        PP_END_MEM
-        PP_MMA
-        __builtin_amdgcn_sched_barrier(0);
-        lds_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    if (grp == 0) lds_barrier();
-#undef PP_ISSUE
-#undef PP_READ
-#undef PP_MMA
-#undef PP_END_MEM
-
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int j = 0; j < TNO; ++j) {
-            const int col = tc.n0 + wn * WTNO + j * 32 + (lane & 31);
-            if (col >= n_out) continue;
-            float bcol = 0.f;
-            if (EPI != EPI_SWIGLU && bias != nullptr) bcol = bf16_to_f32(bias[(int64_t)tc.e * n_out + col]);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t row = tc.row0 + grp * 128 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
-                if (row >= tc.row_end) continue;
-                float out;
-                if (EPI == EPI_SWIGLU) out = silu_f(acc[i][j][v]) * acc[i][j + TNO][v];
-                else if (EPI == EPI_GELU_BIAS) out = gelu_f(acc[i][j][v] + bcol);
-                else out = acc[i][j][v] + bcol;
-                C[row * n_out + col] = f32_to_bf16(out);
-            }
-        }
-    }
-}
-
-template <int GM, int D>
-void launch_bf16_pp_tiles(int epi, const void* A, const void* B, const void* bias, void* C, const int32_t* offsets,
-                          int e_begin, int n_groups, int64_t max_rows, int64_t dense_rows, int n_out, int K,
-                          hipStream_t s) {
-    const int bno = epi == EPI_SWIGLU ? 128 : 256;
-    const int64_t m_tiles = offsets ? (max_rows + 255) / 256 + n_groups : (dense_rows + 255) / 256;
-    const int64_t tiles = m_tiles * ((n_out + bno - 1) / bno);
-    const unsigned grid = (unsigned)(((tiles + 7) / 8) * 8);
-    const auto a = static_cast<const uint16_t*>(A);
-    const auto b = static_cast<const uint16_t*>(B);
-    const auto bi = static_cast<const uint16_t*>(bias);
-    auto c = static_cast<uint16_t*>(C);
-    if (epi == EPI_SWIGLU)
-        gemm_bf16_pp_kernel<EPI_SWIGLU, GM, D><<<grid, 512, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
-                                                                   dense_rows, n_out, K);
-    else if (epi == EPI_GELU_BIAS)
-        gemm_bf16_pp_kernel<EPI_GELU_BIAS, GM, D><<<grid, 512, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
-                                                                      dense_rows, n_out, K);
-    else
-        gemm_bf16_pp_kernel<EPI_BIAS, GM, D><<<grid, 512, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
-                                                                 dense_rows, n_out, K);
-}
-
 
 // Compute units of the current device (cached per device; 256 on MI355X).
 int device_cu_count() {
