@@ -46,23 +46,29 @@ def parse():
     return ap.parse_args()
 
 
-def stage_bytes_flops(cfg):
-    """Algorithmic bytes / flops per stage call (each input read once, each output written once)."""
+def stage_bytes_flops(cfg, used_experts=None):
+    """Algorithmic bytes / flops per stage call (each input read once, each output written once).
+    The expert projections carry both: their flops, and their bytes = weights (and biases) of the
+    experts that received rows (all E when used_experts is None) + the activations read + written."""
     T, d, F, E, k = cfg.T, cfg.d, cfg.F, cfg.E, cfg.k
     A, b = T * k, cfg.elem_bytes
     gemm1_n = 2 * F if cfg.act == "swiglu" else F
+    nu = E if used_experts is None else used_experts
+    bias = cfg.act != "swiglu"
     out = {
         # x, router weights, top-k indices + gates, counts (logits not requested in the forward)
         "route": dict(bytes=T * d * b + E * d * 4 + A * 8 + E * 4),
         # top-k indices, x once, x_perm, sorted_token + inv_pos, offsets
         "permute": dict(bytes=A * 4 + T * d * b + A * d * b + 2 * A * 4 + (E + 1) * 4),
-        "expert_up": dict(flops=2.0 * A * d * gemm1_n),
-        "expert_down": dict(flops=2.0 * A * F * d),
+        "expert_up": dict(flops=2.0 * A * d * gemm1_n,
+                          bytes=nu * (gemm1_n * d + (F if bias else 0)) * b + A * d * b + A * F * b),
+        "expert_down": dict(flops=2.0 * A * F * d, bytes=nu * (d * F + (d if bias else 0)) * b + A * F * b + A * d * b),
         # y_perm, gates + positions, y (+ shared output)
         "combine": dict(bytes=A * d * b + A * 8 + T * d * b + (T * d * b if cfg.Fs else 0)),
     }
     if cfg.Fs:
-        out["shared"] = dict(flops=2.0 * T * d * 2 * cfg.Fs + 2.0 * T * cfg.Fs * d)
+        out["shared"] = dict(flops=2.0 * T * d * 2 * cfg.Fs + 2.0 * T * cfg.Fs * d,
+                             bytes=3 * d * cfg.Fs * b + 2 * T * d * b)
     return out
 
 
@@ -138,7 +144,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     vendor = vendor_gemm(cfg, L, stream) if args.vendor_gemm and cfg.dtype == "bf16" else None
-    work = stage_bytes_flops(cfg)
+    used = int((L.counts > 0).sum().item())
+    work = stage_bytes_flops(cfg, used)
     peak_tf = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_PEAK_TFLOPS
     stages = {}
     for name, ts in times.items():
@@ -148,19 +155,32 @@ def main():
         if "bytes" in w:
             gbs = w["bytes"] / (ms * 1e-3) / 1e9
             ent.update({"GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": w["bytes"]})
-        else:
+        if "flops" in w:
             tf = w["flops"] / (ms * 1e-3) / 1e12
             ent.update({"TFLOP/s": round(tf, 1), "frac_mfma": round(tf / peak_tf, 4), "flops": w["flops"]})
+        if "bytes" in w and "flops" in w:  # the roofline that binds: the larger of the two floors
+            mfma_floor = w["flops"] / (peak_tf * 1e12)
+            hbm_floor = w["bytes"] / (HBM_PEAK_GBS * 1e9)
+            ent["bound"] = "mfma" if mfma_floor >= hbm_floor else "hbm"
+            ent["frac_roofline"] = round(max(mfma_floor, hbm_floor) / (ms * 1e-3), 4)
         stages[name] = ent
     up = stages["expert_up"]
     ffn_ms = stages["expert_up"]["ms"] + stages["expert_down"]["ms"]
     ffn_tf = (work["expert_up"]["flops"] + work["expert_down"]["flops"]) / (ffn_ms * 1e-3) / 1e12
-    roofline = {"kernel": "gemm_bf16_persistent_kernel (expert_up: gate/up grouped GEMM + SwiGLU)"
-                if cfg.dtype == "bf16" else "gemm_f32_kernel (expert_up)",
-                "bound": "mfma" if cfg.dtype == "bf16" else "alu", "achieved": up["TFLOP/s"], "peak": peak_tf,
-                "unit": "TFLOP/s", "frac": round(up["TFLOP/s"] / peak_tf, 4),
-                "traffic": measured_traffic(cfg.name) if cfg.dtype == "bf16" else None,
-                "algorithmic_flops_per_launch": work["expert_up"]["flops"], "avg_launch_ms": up["ms"]}
+    kernel = ("gemm_bf16_persistent_kernel (expert_up: gate/up grouped GEMM + SwiGLU)" if cfg.dtype == "bf16"
+              else "gemm_f32_kernel (expert_up)")
+    if cfg.dtype == "bf16" and up["bound"] == "hbm":
+        # weight streaming binds: groups of a few dozen rows take the four-wave 64-row kernel
+        if cfg.T * cfg.k / cfg.E <= 32:
+            kernel = "gemm_bf16_kernel (expert_up: gate/up grouped GEMM + SwiGLU, 64-row tiles)"
+        roofline = {"kernel": kernel, "bound": "hbm", "achieved": up["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": up["frac_hbm"], "traffic": measured_traffic(cfg.name),
+                    "algorithmic_bytes_per_launch": work["expert_up"]["bytes"], "avg_launch_ms": up["ms"]}
+    else:
+        roofline = {"kernel": kernel, "bound": "mfma" if cfg.dtype == "bf16" else "alu", "achieved": up["TFLOP/s"],
+                    "peak": peak_tf, "unit": "TFLOP/s", "frac": round(up["TFLOP/s"] / peak_tf, 4),
+                    "traffic": measured_traffic(cfg.name) if cfg.dtype == "bf16" else None,
+                    "algorithmic_flops_per_launch": work["expert_up"]["flops"], "avg_launch_ms": up["ms"]}
 
     # ---- CPU oracle on a bounded sample of the same workload ----------------------------------
     cpu = None
