@@ -28,6 +28,12 @@ CASES = {
     "qwen_mini": I.mini("qwen3_30b_a3b", T=2000, d=256, F=192),
     "deepseek_mini": I.mini("deepseek_v3", T=500, d=448, F=128, Fs=192),
     "E1_k1": I.mini("small_bf16", T=300, d=128, F=128, E=1, k=1),
+    # router widths on each route path: E <= 16 fused logits + selection (E not a power of two),
+    # 16 < E <= 48 split + logits kernel over three 16-expert tiles, E > 48 the router GEMM with
+    # zero padded rows (Epad = 80)
+    "router_E13_k3": I.mini("small_bf16", T=777, d=192, F=128, E=13, k=3),
+    "router_E40_k4": I.mini("small_bf16", T=555, d=256, F=128, E=40, k=4),
+    "router_E72_k6": I.mini("qwen3_30b_a3b", T=999, d=320, F=128, E=72, k=6),
     "k_eq_E": I.mini("small_bf16", T=257, d=128, F=64, E=4, k=4),
     "T1": I.mini("deepseek_v3", T=1, d=128, F=64, Fs=64),
     # one expert, so the tile count is fixed: 4 x 66 = 264 gate/up tiles (just over one round of 256
