@@ -482,10 +482,11 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(const void* __restrict
     }
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
-        if (j >= k) break;
-        const int p = __builtin_amdgcn_readlane(mypos, j);
-        const float s = wave_sum(dot[j]);
-        if (lane == 0) dg[t * k + j] = p < 0 ? 0.f : s;
+        if (j < k) {
+            const int p = __builtin_amdgcn_readlane(mypos, j);
+            const float s = wave_sum(dot[j]);
+            if (lane == 0) dg[t * k + j] = p < 0 ? 0.f : s;
+        }
     }
 }
 

@@ -770,9 +770,12 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         lds_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        // compute cluster
+        // compute cluster, at raised issue priority so the partner wave's memory cluster on the same
+        // SIMD does not delay an MFMA issue (measured: down projection about 2 % faster)
+        __builtin_amdgcn_s_setprio(1);
         PS_MMA
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
         r_slot = r_slot + 1 == NS ? 0 : r_slot + 1;
         if (++r_ks == r_ke) {  // last stage of a unit: store it
             if (cmp_u < (int)nw) {
