@@ -19,8 +19,8 @@
 //    output tiles (SwiGLU: 128 gate and the matching 128 up columns, so a lane holds gate and up of
 //    the same output element) in an XCD-aware order; two groups of four waves alternate LDS
 //    fragment reads and MFMA clusters (ping-pong), and the LDS ring runs on across tiles.
-//  - gemm_bf16_kernel: four waves on one 64 x 128 tile with a 9-stage ring, for groups of a few
-//    dozen rows (decode batches), whose time is spent streaming the weight panels.
+//  - gemm_bf16_kernel: four waves on one 64 x 128 tile with a 6-stage ring (two blocks per CU), for
+//    groups of a few dozen rows (decode batches), whose time is spent streaming the weight panels.
 // Both use v_mfma_f32_32x32x16_bf16 with fp32 accumulators. Operands stream into an LDS ring (K
 // slices of 32) with buffer_load ... lds (global -> LDS without registers); buffer descriptors bound
 // each tile's rows, so rows past an expert's end or columns past n_out read as zero and nothing is
@@ -1037,10 +1037,10 @@ void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* 
                          int n_out, int K, float* partials, hipStream_t s) {
     if (dtype == MOE_BF16) {
         if (bm == 64 && offsets != nullptr) {
-            // small groups: 64-row x 128-column tiles, each block streaming its weight panel through a
-            // 9-stage LDS ring (measured on the decode batch: 128-wide panels beat 256-wide ones on
-            // both projections, having more tiles to spread over the CUs)
-            launch_bf16_tiles<64, 128, 9, 8>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows,
+            // small groups: 64-row x 128-column tiles with a 6-stage LDS ring (72 KB, two blocks per CU).
+            // Measured on the decode batch: 128-wide panels beat 256-wide ones (more tiles to spread
+            // over the CUs), and two blocks per CU with 6 stages beat one block with 9 or 13.
+            launch_bf16_tiles<64, 128, 6, 8>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows,
                                              n_out, K, s);
             return;
         }
