@@ -818,6 +818,43 @@ void launch_bwd_act_fwd(int dtype, const void* pre, int64_t n_rows, int F, int a
     else bwd_act_fwd_kernel<false><<<blocks_for(n_rows * F), 256, 0, s>>>(pre, n_rows, F, act, h);
 }
 
+// Batched bf16 transpose: src [G][R][C] -> dst [G][C][R] (R, C multiples of 64), 64 x 64 tiles
+// through LDS: 16-byte loads along C, 16-byte stores along R.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src, int64_t R, int64_t C,
+                                                             uint16_t* __restrict__ dst) {
+    __shared__ uint16_t tile[64][64 + 2];
+    const int64_t g = blockIdx.z;
+    const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+    const uint16_t* sg = src + g * R * C;
+    uint16_t* dg = dst + g * R * C;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int v = it * 256 + threadIdx.x;  // 512 vectors of 8 elements
+        const int r = v >> 3, c = (v & 7) * 8;
+        const u32x4 q = ld16(sg + (r0 + r) * C + c0 + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            tile[r][c + 2 * i] = (uint16_t)(q[i] & 0xffffu);
+            tile[r][c + 2 * i + 1] = (uint16_t)(q[i] >> 16);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int v = it * 256 + threadIdx.x;
+        const int c = v >> 3, r = (v & 7) * 8;  // output row c (a source column), 8 source rows
+        u32x4 q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = (uint32_t)tile[r + 2 * i][c] | ((uint32_t)tile[r + 2 * i + 1][c] << 16);
+        st16(dg + (c0 + c) * R + r0 + r, q);
+    }
+}
+
+void launch_transpose_bf16(const void* src, int64_t G, int64_t R, int64_t C, void* dst, hipStream_t s) {
+    dim3 grid((unsigned)(C / 64), (unsigned)(R / 64), (unsigned)G);
+    transpose_bf16_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(src), R, C, static_cast<uint16_t*>(dst));
+}
+
 void launch_bwd_act_bwd(int dtype, const float* dh, const void* pre, int64_t n_rows, int F, int act, void* dAU,
                         hipStream_t s) {
     if (n_rows <= 0) return;

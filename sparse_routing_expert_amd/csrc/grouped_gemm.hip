@@ -1036,7 +1036,7 @@ void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* 
                          const int32_t* offsets, int e_begin, int n_groups, int64_t max_rows, int64_t dense_rows,
                          int n_out, int K, float* partials, hipStream_t s) {
     if (dtype == MOE_BF16) {
-        if (bm == 64 && offsets != nullptr) {
+        if (bm == 64 && offsets != nullptr && epi != EPI_F32) {
             // small groups: 64-row x 128-column tiles with a 6-stage LDS ring (72 KB, two blocks per CU).
             // Measured on the decode batch: 128-wide panels beat 256-wide ones (more tiles to spread
             // over the CUs), and two blocks per CU with 6 stages beat one block with 9 or 13.

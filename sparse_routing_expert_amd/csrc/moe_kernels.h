@@ -86,6 +86,8 @@ void launch_combine(int dtype, const void* y_perm, const int32_t* inv_pos, const
                     const void* y_shared, void* y, int64_t T, int d, int k, hipStream_t s);
 
 // ---- backward ---------------------------------------------------------------------------
+// bf16 [G][R][C] -> [G][C][R] (R, C multiples of 64)
+void launch_transpose_bf16(const void* src, int64_t G, int64_t R, int64_t C, void* dst, hipStream_t s);
 // Strided grouped GEMM C(m, n) = sum_k A(m, k) B(n, k); A(m, k) at A[m*sam + k*sak], B(n, k) at
 // B[n*sbn + k*sbk], C(m, n) at C[m*scm + n] (fp32). Each operand is contiguous along k (s?k == 1) or
 // along its row index (sam == 1 / sbn == 1).
