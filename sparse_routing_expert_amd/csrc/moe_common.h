@@ -89,6 +89,33 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return max_u64(max_u64(lane_u64(v, 0), lane_u64(v, 16)), max_u64(lane_u64(v, 32), lane_u64(v, 48)));
 }
 
+// Reductions over each 16-lane DPP row (xor 1, xor 2 inside quads, then the half-row and row
+// mirrors). Every step pairs each lane with a partner that holds the mirrored operand, so by the
+// commutativity of + and max every lane of a row ends with the same bits: ((q0 + q1) + (q2 + q3))
+// over the quad sums.
+constexpr int kDppHalfMirror = 0x141, kDppMirror = 0x140;
+__device__ __forceinline__ float row_sum(float v) {
+    v += dpp_f32<kDppXor1>(v);
+    v += dpp_f32<kDppXor2>(v);
+    v += dpp_f32<kDppHalfMirror>(v);
+    v += dpp_f32<kDppMirror>(v);
+    return v;
+}
+__device__ __forceinline__ float row_max(float v) {
+    v = fmaxf(v, dpp_f32<kDppXor1>(v));
+    v = fmaxf(v, dpp_f32<kDppXor2>(v));
+    v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f32<kDppMirror>(v));
+    return v;
+}
+__device__ __forceinline__ uint64_t row_max_u64(uint64_t v) {
+    v = max_u64(v, dpp_u64<kDppXor1>(v));
+    v = max_u64(v, dpp_u64<kDppXor2>(v));
+    v = max_u64(v, dpp_u64<kDppHalfMirror>(v));
+    v = max_u64(v, dpp_u64<kDppMirror>(v));
+    return v;
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 }  // namespace moe

@@ -477,39 +477,84 @@ __global__ __launch_bounds__(kFusedRouteWaves * 64) void route_fused_kernel(
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) s_part[wave][tt][lane] = acc[tt];
     __syncthreads();
-    // 16x16 accumulator: lane holds column (expert) lane % 16 and rows (tokens) 4 (lane / 16) + v
+    // Selection, one token per 16-lane DPP row: wave w takes tokens 4w + r (r = lane / 16) of the
+    // block, lane e = lane % 16 of a row holds expert e. The same steps as select_token, with the
+    // wave reductions replaced by row reductions, so a wave selects its tokens together.
     const float* sp = reinterpret_cast<const float*>(&s_part[0][0][0]);
     const bool softmax = score == MOE_SOFTMAX;
-    float bias[1] = {(sel_bias != nullptr && lane < E) ? sel_bias[lane] : 0.f};
-    float pacc[1] = {0.f}, hacc = 0.f;
+    const int row = lane >> 4, e = lane & 15;
+    const int lt = wave * TPWV + row;
+    const int64_t t = t0 + lt;
+    const bool valid = row < TPWV && t < T;
+    const bool live = valid && e < E;
+    // the 16x16 accumulator of token tile tt: lane c holds column (expert) c % 16 and rows (tokens)
+    // 4 (c / 16) + v; the eight wave partials are summed in wave order
+    float l = -INFINITY;
+    if (live) {
+        const int tt = lt >> 4, r16 = lt & 15;
+        const int off = (tt * 64 + e + 16 * (r16 >> 2)) * 4 + (r16 & 3);
+        float sum = sp[off];
 #pragma unroll
-    for (int q = 0; q < TPWV; ++q) {
-        const int lt = wave * TPWV + q, tt = lt >> 4, row = lt & 15;
-        const int64_t t = t0 + lt;
-        if (t >= T) break;
-        float l[1] = {-INFINITY};
-        if (lane < E) {
-            const int off = (tt * 64 + lane + 16 * (row >> 2)) * 4 + (row & 3);
-            float sum = sp[off];
-#pragma unroll
-            for (int wv = 1; wv < NW; ++wv) sum += sp[wv * TT * 256 + off];
-            l[0] = sum;
-            if (logits_out != nullptr) logits_out[t * E + lane] = sum;
-        }
-        select_token<1>(l, bias, t, E, k, softmax, renorm, pacc, hacc, topk_idx, topk_w, s_cnt);
+        for (int wv = 1; wv < NW; ++wv) sum += sp[wv * TT * 256 + off];
+        l = sum;
+        if (logits_out != nullptr) logits_out[t * E + e] = sum;
     }
-    if (lane < E) s_P[wave][lane] = pacc[0];
-    const float hw = wave_sum(hacc);
+    const float m = row_max(l);
+    const float p = live ? (softmax ? expf(l - m) : sigmoidf_(l)) : 0.f;
+    const float Z = row_sum(p);
+    const float invZ = 1.0f / Z, lnZ = logf(Z);
+    const float pn = live ? p * invZ : 0.f;
+    float hcur = 0.f;
+    if (pn > 0.f) hcur = -pn * (softmax ? (l - m) - lnZ : logf(pn));
+    float kv = softmax ? l : p;  // p holds the raw sigmoid score here
+    kv = kv + (live && sel_bias != nullptr ? sel_bias[e] : 0.f);
+    kv = kv + 0.0f;  // -0 -> +0: equal keys compare equal
+    uint64_t key = live ? pack_key(kv, e) : 0ull;
+    int sel_e = 0;
+    for (int j = 0; j < k; ++j) {
+        const uint64_t best = row_max_u64(key);
+        const int ej = key_index(best);  // uniform over the row
+        if (e == ej) key = 0ull;
+        if (e == j) sel_e = ej;
+    }
+    // unbiased logit of slot j's expert, fetched from that expert's lane of the row
+    const float sel_l = __shfl(l, (lane & 48) + sel_e);
+    const bool slot = valid && e < k;
+    const float lv = slot ? sel_l : -INFINITY;
+    float gate;
+    if (softmax) {
+        if (renorm) {
+            const float ms = row_max(lv);
+            const float ex = slot ? expf(lv - ms) : 0.f;
+            gate = ex / row_sum(ex);
+        } else {
+            gate = expf(lv - m) * invZ;
+        }
+    } else {
+        const float sg = slot ? sigmoidf_(lv) : 0.f;
+        gate = sg / row_sum(sg);
+    }
+    if (slot) {
+        topk_idx[t * k + e] = sel_e;
+        topk_w[t * k + e] = gate;
+        atomicAdd(&s_cnt[sel_e], 1);
+    }
+    // the wave's partials: per expert the sum over its tokens in row order; the entropy terms summed
+    // the same way, then over the row
+    const float p1 = __shfl(pn, lane + 16), p2 = __shfl(pn, lane + 32), p3 = __shfl(pn, lane + 48);
+    const float h1 = __shfl(hcur, lane + 16), h2 = __shfl(hcur, lane + 32), h3 = __shfl(hcur, lane + 48);
+    const float hw = row_sum(((hcur + h1) + h2) + h3);
+    if (lane < E) s_P[wave][lane] = ((pn + p1) + p2) + p3;
     if (lane == 0) s_H[wave] = hw;
     __syncthreads();
     if (threadIdx.x < E) {
-        const int e = threadIdx.x;
-        blk_counts[(int64_t)blockIdx.x * E + e] = s_cnt[e];
+        const int ex = threadIdx.x;
+        blk_counts[(int64_t)blockIdx.x * E + ex] = s_cnt[ex];
         if (blk_P != nullptr) {
-            float sp2 = s_P[0][e];
+            float sp2 = s_P[0][ex];
 #pragma unroll
-            for (int wv = 1; wv < NW; ++wv) sp2 += s_P[wv][e];
-            blk_P[(int64_t)blockIdx.x * E + e] = sp2;
+            for (int wv = 1; wv < NW; ++wv) sp2 += s_P[wv][ex];
+            blk_P[(int64_t)blockIdx.x * E + ex] = sp2;
         }
     }
     if (threadIdx.x == 0 && blk_H != nullptr) {
@@ -680,9 +725,73 @@ void launch_route_select(const float* logits, int lg_ld, int lg_split, float* lo
 #undef MOE_SELECT
 }
 
+// Single-block form for routers of at most kFinalizeSmallExperts experts: item i <= E (expert i, or
+// the entropy for i = E) goes to wave i % 16; lane j of that wave sums blocks j, j + 64, ... in
+// order and the wave adds its lanes in a fixed tree (float64 for the statistics). Thread 0 then
+// forms aux = E * sum_e f_e P_e in expert order. One launch and no cross-block ticket.
+constexpr int kFinalizeSmallExperts = 16;
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int lo = __shfl_xor(__double2loint(v), o), hi = __shfl_xor(__double2hiint(v), o);
+        const double u = __hiloint2double(hi, lo);
+        // the lane with the lower index keeps its own value on the left, so both lanes of a pair
+        // form the same sum
+        v = (lane_id() & o) ? u + v : v + u;
+    }
+    return v;
+}
+__global__ __launch_bounds__(1024) void route_finalize_small_kernel(const int32_t* __restrict__ blk_counts,
+                                                                    const float* __restrict__ blk_P,
+                                                                    const float* __restrict__ blk_H, int nblk,
+                                                                    int64_t T, int E, int32_t* __restrict__ counts,
+                                                                    float* __restrict__ stats) {
+    __shared__ double s_fp[kFinalizeSmallExperts];
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const double invT = 1.0 / (double)T;
+    for (int it = wave; it <= E; it += 16) {
+        if (it < E) {
+            int cnt = 0;
+            double acc = 0.0;
+            for (int b = lane; b < nblk; b += 64) {
+                cnt += blk_counts[(int64_t)b * E + it];
+                if (stats) acc += (double)blk_P[(int64_t)b * E + it];
+            }
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) cnt += __shfl_xor(cnt, o);
+            if (stats) acc = wave_sum_f64(acc);
+            if (lane == 0) {
+                counts[it] = cnt;
+                if (stats) {
+                    const double f = (double)cnt * invT, Pm = acc * invT;
+                    stats[it] = (float)f;
+                    stats[E + it] = (float)Pm;
+                    s_fp[it] = f * Pm;
+                }
+            }
+        } else if (stats) {
+            double acc = 0.0;
+            for (int b = lane; b < nblk; b += 64) acc += (double)blk_H[b];
+            acc = wave_sum_f64(acc);
+            if (lane == 0) stats[2 * E + 1] = (float)(acc * invT);
+        }
+    }
+    if (stats == nullptr) return;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double a = 0.0;
+        for (int e = 0; e < E; ++e) a += s_fp[e];
+        stats[2 * E] = (float)((double)E * a);
+    }
+}
+
 void launch_route_finalize(const int32_t* blk_counts, const float* blk_P, const float* blk_H, int nblk, int64_t T,
                            int E, int32_t* counts, double* fp_scratch, int32_t* ticket, float* stats,
                            hipStream_t s) {
+    if (E <= kFinalizeSmallExperts) {
+        route_finalize_small_kernel<<<1, 1024, 0, s>>>(blk_counts, blk_P, blk_H, nblk, T, E, counts, stats);
+        return;
+    }
     route_finalize_kernel<<<(unsigned)(stats ? E + 1 : E), 256, 0, s>>>(blk_counts, blk_P, blk_H, nblk, T, E,
                                                                          counts, fp_scratch, ticket, stats);
 }
