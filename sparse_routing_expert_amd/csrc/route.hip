@@ -389,6 +389,10 @@ __global__ __launch_bounds__(kFusedRouteWaves * 64) void route_fused_kernel(
     __shared__ int s_cnt[64];
     __shared__ float s_P[NW][64];
     __shared__ float s_H[NW];
+    // per wave: the block's 16 * TT token rows x 128 columns of x, 16 slots of 16 bytes per row, slot
+    // j of row R at position j ^ (R % 16)
+    constexpr int XI = TPB / 4;  // load instructions per 128-column step: 4 rows of 256 bytes each
+    __shared__ u32x4 s_x[NW][TPB * 16];
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0;
     if (threadIdx.x < 64) s_cnt[threadIdx.x] = 0;
@@ -400,6 +404,17 @@ __global__ __launch_bounds__(kFusedRouteWaves * 64) void route_fused_kernel(
         const int64_t t = t0 + tt * 16 + r;
         xr[tt] = x + (t < T ? t : T - 1) * d;
     }
+    // the 128-column steps read x as whole 256-byte row pieces: load q covers rows 4q + lane / 16,
+    // lane % 16 taking the row's 16-byte slot lane % 16
+    const uint16_t* xq[XI];
+    int xw[XI];
+#pragma unroll
+    for (int q = 0; q < XI; ++q) {
+        const int R = q * 4 + g;
+        const int64_t t = t0 + R;
+        xq[q] = x + (t < T ? t : T - 1) * d + r * 8;
+        xw[q] = R * 16 + (r ^ (R & 15));
+    }
     const bool w_ok = r < E;  // padded expert rows are zero and not loaded
     const float* wr = w + (int64_t)(w_ok ? r : 0) * d;
     const int nc = d / 32;
@@ -408,7 +423,7 @@ __global__ __launch_bounds__(kFusedRouteWaves * 64) void route_fused_kernel(
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) acc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
     const floatx4 fzero = {0.f, 0.f, 0.f, 0.f};
-    u32x4 xv[2][TT][4];
+    u32x4 xv[2][XI];
     floatx4 wf[2][4][2];
     // hi / mid / lo bf16 terms of 8 fp32 weights
     auto split8 = [](const floatx4 (&v)[2], bf16x8& h8, bf16x8& m8, bf16x8& l8) {
@@ -427,20 +442,27 @@ __global__ __launch_bounds__(kFusedRouteWaves * 64) void route_fused_kernel(
 #define RF_LOAD(b_, kb_)                                                                                  \
     {                                                                                                     \
         const int base = (kb_) + g * 8;                                                                   \
+        _Pragma("unroll") for (int q = 0; q < XI; ++q) xv[b_][q] =                                         \
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xq[q] + (kb_)));                    \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                   \
-            _Pragma("unroll") for (int tt = 0; tt < TT; ++tt) xv[b_][tt][i] =                             \
-                __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr[tt] + base + i * 32));       \
             wf[b_][i][0] = w_ok ? *reinterpret_cast<const floatx4*>(wr + base + i * 32) : fzero;          \
             wf[b_][i][1] = w_ok ? *reinterpret_cast<const floatx4*>(wr + base + i * 32 + 4) : fzero;      \
         }                                                                                                 \
     }
 #define RF_MMA(b_)                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                       \
-        bf16x8 w3[3];                                                                                     \
-        split8(wf[b_][i], w3[0], w3[1], w3[2]);                                                           \
-        _Pragma("unroll") for (int tt = 0; tt < TT; ++tt) _Pragma("unroll") for (int p = 0; p < 3; ++p)   \
-            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[b_][tt][i]), w3[p], \
-                                                              acc[tt], 0, 0, 0);                          \
+    {                                                                                                     \
+        __builtin_amdgcn_wave_barrier();                                                                  \
+        _Pragma("unroll") for (int q = 0; q < XI; ++q) s_x[wave][xw[q]] = xv[b_][q];                      \
+        __builtin_amdgcn_wave_barrier();                                                                  \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                   \
+            bf16x8 w3[3];                                                                                 \
+            split8(wf[b_][i], w3[0], w3[1], w3[2]);                                                       \
+            _Pragma("unroll") for (int tt = 0; tt < TT; ++tt) {                                           \
+                const bf16x8 a_ = __builtin_bit_cast(bf16x8, s_x[wave][(tt * 16 + r) * 16 + ((4 * i + g) ^ r)]); \
+                _Pragma("unroll") for (int p = 0; p < 3; ++p)                                             \
+                    acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_, w3[p], acc[tt], 0, 0, 0);       \
+            }                                                                                             \
+        }                                                                                                 \
     }
     int kb = kb0;
     const int nsteps = (kb1 - kb0) / 128;

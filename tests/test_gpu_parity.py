@@ -32,6 +32,10 @@ CASES = {
     # 16 < E <= 48 split + logits kernel over three 16-expert tiles, E > 48 the router GEMM with
     # zero padded rows (Epad = 80)
     "router_E13_k3": I.mini("small_bf16", T=777, d=192, F=128, E=13, k=3),
+    # E <= 16 with d wide enough for the fused route's 128-column steps (x staged through LDS) and a
+    # 32-column tail per wave: 16-token blocks with a ragged last block, and 32-token blocks
+    "route_steps_T777": I.mini("mixtral_prefill", T=777, d=1664, F=64),
+    "route_steps_T8200": I.mini("mixtral_prefill", T=8200, d=2112, F=64),
     "router_E40_k4": I.mini("small_bf16", T=555, d=256, F=128, E=40, k=4),
     "router_E72_k6": I.mini("qwen3_30b_a3b", T=999, d=320, F=128, E=72, k=6),
     "k_eq_E": I.mini("small_bf16", T=257, d=128, F=64, E=4, k=4),
