@@ -278,6 +278,11 @@ void do_permute(const moe_shape* s, const int32_t* topk_idx, const void* x, int3
                 int32_t* sorted_token, int32_t* inv_pos, void* x_perm, void* ws, hipStream_t st) {
     const PermWs w = perm_ws(s);
     const int64_t A = s->T * s->k;
+    if (moe::perm_index_small_ok(A, s->E)) {
+        moe::launch_perm_index_small(topk_idx, A, s->E, s->k, s->capacity, offsets, inv_pos, sorted_token, st);
+        moe::launch_perm_scatter(x, inv_pos, s->T, s->d_model, s->k, elem_bytes(s), x_perm, st);
+        return;
+    }
     moe::launch_perm_count(topk_idx, A, s->E, at<int32_t>(ws, w.tile_counts), st);
     moe::launch_perm_scan(at<int32_t>(ws, w.tile_counts), w.ntiles, A, s->E, s->capacity, at<int32_t>(ws, w.tile_base),
                           offsets, st);

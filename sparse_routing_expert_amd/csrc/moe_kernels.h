@@ -47,6 +47,14 @@ void launch_route_bias_update(const int32_t* counts, int64_t T, int E, int k, fl
 
 // ---- permute ----------------------------------------------------------------------------
 constexpr int kPermTile = 1024;  // assignments per histogram / rank tile
+// single-block index stage: per-chunk (64 assignments) expert counts held in LDS
+constexpr int kPermSmallCounts = 16384;
+// A <= 16 waves x 4 chunks x 64 = 4096. Measured beyond that, the one block is slower than the tiled
+// kernels (A = 16384: 62.9 against 56.4 us for the permute; A = 8192: even)
+constexpr int kPermSmallChunksPerWave = 4;
+bool perm_index_small_ok(int64_t A, int E);
+void launch_perm_index_small(const int32_t* topk_idx, int64_t A, int E, int k, int capacity, int32_t* offsets,
+                             int32_t* inv_pos, int32_t* sorted_token, hipStream_t s);
 
 void launch_perm_count(const int32_t* topk_idx, int64_t A, int E, int32_t* tile_counts, hipStream_t s);
 // capacity: rows each expert keeps (0 = all); dropped assignments get inv_pos = -1

@@ -173,6 +173,127 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const uint8_t* __rest
     }
 }
 
+// The whole index stage in one block of 1024 threads, for layers whose per-chunk expert counts fit
+// in LDS (chunks of 64 assignments, ceil(A / 64) * E <= kPermSmallCounts). The same positions as
+// the tiled kernels (stable in (t, j) order, dropped past the capacity), in one launch:
+//  1. wave w loads the expert ids of chunks w, w + 16, ... (at most kPermSmallChunksPerWave) at
+//     once, matches each chunk's assignments by ballots over the id bits and stores the chunk's
+//     count per expert (no atomics);
+//  2. per expert, J = min(64, 1024 / Ep) lanes of one wave each own a contiguous range of chunks;
+//     the range sums are scanned across those lanes by shuffles, and each lane rewrites its chunks'
+//     counts as exclusive bases (assignments to e in earlier chunks); the expert totals (capped at
+//     the capacity) are scanned over experts into offsets;
+//  3. the chunks are matched again from the held ids, and each assignment gets row
+//     offsets[e] + base + rank.
+__global__ __launch_bounds__(1024) void perm_index_small_kernel(const int32_t* __restrict__ idx, int64_t A, int E,
+                                                                int k, int nbits, int Ep, int capacity,
+                                                                int32_t* __restrict__ offsets,
+                                                                int32_t* __restrict__ inv_pos,
+                                                                int32_t* __restrict__ sorted_token) {
+    extern __shared__ int cnt[];  // [nch][E]
+    __shared__ int s_tot[1024];
+    __shared__ int s_off[1025];
+    __shared__ int s_wave[17];
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int nch = (int)((A + 63) / 64);
+    for (int i = threadIdx.x; i < nch * E; i += 1024) cnt[i] = 0;
+    __syncthreads();
+    const uint64_t below = (1ull << lane) - 1ull;
+    // every expert id of the wave's chunks, loaded at once (chunk wave + 16 i in ev[i]); E marks
+    // positions past A and never equals a real expert id
+    int ev[kPermSmallChunksPerWave];
+#pragma unroll
+    for (int i = 0; i < kPermSmallChunksPerWave; ++i) {
+        const int64_t a = (int64_t)(wave + 16 * i) * 64 + lane;
+        ev[i] = a < A ? idx[a] : E;
+    }
+    auto match = [&](int e, int& rk) -> uint64_t {
+        uint64_t m = ~0ull;
+        for (int b = 0; b < nbits; ++b) {
+            const int bit = (e >> b) & 1;
+            const uint64_t bb = __ballot(bit);
+            m &= bit ? bb : ~bb;
+        }
+        rk = __popcll(m & below);
+        return m;
+    };
+#pragma unroll
+    for (int i = 0; i < kPermSmallChunksPerWave; ++i) {
+        const int c = wave + 16 * i;
+        if (c >= nch) break;  // uniform per wave
+        int rk;
+        const uint64_t m = match(ev[i], rk);
+        if (ev[i] < E && rk == 0) cnt[c * E + ev[i]] = __popcll(m);
+    }
+    __syncthreads();
+    // per-expert exclusive bases over chunks
+    const int J = 1024 / Ep < 64 ? 1024 / Ep : 64;
+    const int e = threadIdx.x / J, j = threadIdx.x % J;
+    const int C = (nch + J - 1) / J;
+    const int cb = j * C < nch ? j * C : nch, ce = cb + C < nch ? cb + C : nch;
+    int sum = 0;
+    if (e < E)
+        for (int c = cb; c < ce; ++c) sum += cnt[c * E + e];
+    int inc = sum;  // inclusive scan over the J lanes of this expert (one segment of a wave)
+    for (int o = 1; o < J; o <<= 1) {
+        const int n = __shfl_up(inc, o, J);
+        if (j >= o) inc += n;
+    }
+    if (e < E) {
+        int run = inc - sum;
+        for (int c = cb; c < ce; ++c) {
+            const int v = cnt[c * E + e];
+            cnt[c * E + e] = run;
+            run += v;
+        }
+        if (j == J - 1) s_tot[e] = inc;
+    }
+    __syncthreads();
+    const int tot = threadIdx.x < E ? s_tot[threadIdx.x] : 0;
+    const int kept = capacity > 0 && tot > capacity ? capacity : tot;
+    int total;
+    const int start = block1024_excl_scan(kept, s_wave, &total);
+    if (threadIdx.x < E) {
+        offsets[threadIdx.x] = start;
+        s_off[threadIdx.x] = start;
+    }
+    if (threadIdx.x == 0) offsets[E] = total;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kPermSmallChunksPerWave; ++i) {
+        const int c = wave + 16 * i;
+        if (c >= nch) break;  // uniform per wave
+        const int64_t a = (int64_t)c * 64 + lane;
+        const int ea = ev[i];
+        int rk;
+        match(ea, rk);
+        if (a >= A) continue;
+        const int r = cnt[c * E + ea] + rk;
+        if (capacity > 0 && r >= capacity) {
+            inv_pos[a] = -1;
+            continue;
+        }
+        const int pos = s_off[ea] + r;
+        inv_pos[a] = pos;
+        sorted_token[pos] = (int32_t)(a / k);
+    }
+}
+
+bool perm_index_small_ok(int64_t A, int E) {
+    return A > 0 && A <= (int64_t)16 * 64 * kPermSmallChunksPerWave && (A + 63) / 64 * E <= kPermSmallCounts;
+}
+
+void launch_perm_index_small(const int32_t* topk_idx, int64_t A, int E, int k, int capacity, int32_t* offsets,
+                             int32_t* inv_pos, int32_t* sorted_token, hipStream_t s) {
+    int nbits = 0;
+    while ((1 << nbits) <= E) ++nbits;  // ids 0..E (E = padding sentinel) fit in nbits bits
+    int Ep = 1;
+    while (Ep < E) Ep <<= 1;  // E <= 1024
+    const size_t lds = (size_t)((A + 63) / 64) * E * sizeof(int);
+    perm_index_small_kernel<<<1, 1024, lds, s>>>(topk_idx, A, E, k, nbits, Ep, capacity, offsets, inv_pos,
+                                                 sorted_token);
+}
+
 void launch_perm_count(const int32_t* topk_idx, int64_t A, int E, int32_t* tile_counts, hipStream_t s) {
     const unsigned ntiles = (unsigned)((A + kPermTile - 1) / kPermTile);
     perm_count_kernel<<<ntiles, 256, 0, s>>>(topk_idx, A, E, tile_counts);
