@@ -187,7 +187,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
     constexpr int STAGE_ELEMS = ROWS * BK;  // bf16 elements per stage
     constexpr int STAGE_BYTES = STAGE_ELEMS * 2;
     constexpr int NQ = ROWS / 64;  // 1 KB DMA instructions per wave per stage
-    static_assert(TM >= 1 && TNO >= 1 && BM % 64 == 0 && BN % 128 == 0 && NS >= 4 && NS <= 9, "tile shape");
+    static_assert(TM >= 1 && TNO >= 1 && BM % 64 == 0 && BN % (GATED ? 128 : 64) == 0 && NS >= 4 && NS <= 9,
+                  "tile shape");
     // one phase = max(MFMAs, fragment reads) pinned steps; a wave's DMAs go out every SP steps
     constexpr int STEPS_A = TM * TN > TM + TN ? TM * TN : TM + TN;
     constexpr int STEPS_B = STEPS_A;
@@ -1021,10 +1022,14 @@ void launch_bf16_tiles(int epi, const void* A, const void* B, const void* bias, 
     const auto b = static_cast<const uint16_t*>(B);
     const auto bi = static_cast<const uint16_t*>(bias);
     auto c = static_cast<uint16_t*>(C);
-    if (epi == EPI_SWIGLU)
-        gemm_bf16_kernel<BM, BN, EPI_SWIGLU, NS, GM><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
-                                                                         dense_rows, n_out, K);
-    else if (epi == EPI_GELU_BIAS)
+    if constexpr (BN >= 128) {  // a gated tile holds gate and up halves of at least 64 columns each
+        if (epi == EPI_SWIGLU) {
+            gemm_bf16_kernel<BM, BN, EPI_SWIGLU, NS, GM><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin,
+                                                                             n_groups, dense_rows, n_out, K);
+            return;
+        }
+    }
+    if (epi == EPI_GELU_BIAS)
         gemm_bf16_kernel<BM, BN, EPI_GELU_BIAS, NS, GM><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin,
                                                                             n_groups, dense_rows, n_out, K);
     else
@@ -1039,7 +1044,15 @@ void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* 
         if (bm == 64 && offsets != nullptr && epi != EPI_F32) {
             // small groups: 64-row x 128-column tiles with a 6-stage LDS ring (72 KB, two blocks per CU).
             // Measured on the decode batch: 128-wide panels beat 256-wide ones (more tiles to spread
-            // over the CUs), and two blocks per CU with 6 stages beat one block with 9 or 13.
+            // over the CUs), and two blocks per CU with 6 stages beat one block with 9 or 13. A
+            // non-gated projection with fewer than 512 such tiles (the down projection of a decode
+            // batch: 8 experts x 32 panels) takes 64-wide panels with an 8-stage ring (64 KB), so each
+            // CU holds two blocks: 260 -> 253-257 us there.
+            if (epi != EPI_SWIGLU && (int64_t)n_groups * ((n_out + 127) / 128) < 512) {
+                launch_bf16_tiles<64, 64, 8, 8>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows,
+                                                n_out, K, s);
+                return;
+            }
             launch_bf16_tiles<64, 128, 6, 8>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows,
                                              n_out, K, s);
             return;
