@@ -167,7 +167,10 @@ def main():
     up = stages["expert_up"]
     ffn_ms = stages["expert_up"]["ms"] + stages["expert_down"]["ms"]
     ffn_tf = (work["expert_up"]["flops"] + work["expert_down"]["flops"]) / (ffn_ms * 1e-3) / 1e12
-    kernel = ("gemm_bf16_persistent_kernel (expert_up: gate/up grouped GEMM + SwiGLU)" if cfg.dtype == "bf16"
+    # the library's dispatch: expert groups averaging >= 2048 rows take the four-wave wide-K kernel
+    wide = cfg.T * cfg.k >= 2048 * cfg.E
+    kernel = ((("gemm_bf16_wide_kernel" if wide else "gemm_bf16_persistent_kernel")
+               + " (expert_up: gate/up grouped GEMM + SwiGLU)") if cfg.dtype == "bf16"
               else "gemm_f32_kernel (expert_up)")
     if cfg.dtype == "bf16" and up["bound"] == "hbm":
         # weight streaming binds: groups of a few dozen rows take the four-wave 64-row kernel

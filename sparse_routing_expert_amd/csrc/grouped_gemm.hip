@@ -15,18 +15,23 @@
 //
 // bf16 kernels (one launch per projection, plus a short fixup launch when the last round of tiles is
 // split along K):
-//  - gemm_bf16_persistent_kernel, the main path: one block of eight waves per CU walks 256 x 256
-//    output tiles (SwiGLU: 128 gate and the matching 128 up columns, so a lane holds gate and up of
-//    the same output element) in an XCD-aware order; two groups of four waves alternate LDS
-//    fragment reads and MFMA clusters (ping-pong), and the LDS ring runs on across tiles.
-//  - gemm_bf16_kernel: four waves on one 64 x 128 tile with a 6-stage ring (two blocks per CU), for
-//    groups of a few dozen rows (decode batches), whose time is spent streaming the weight panels.
-// Both use v_mfma_f32_32x32x16_bf16 with fp32 accumulators. Operands stream into an LDS ring (K
-// slices of 32) with buffer_load ... lds (global -> LDS without registers); buffer descriptors bound
-// each tile's rows, so rows past an expert's end or columns past n_out read as zero and nothing is
-// clamped. LDS rows are 64 bytes; their four 16-byte chunks are XOR-swizzled by (row >> 2) & 3,
-// which measured conflict-free for the 128-bit operand reads on gfx950 (16 lanes per LDS cycle, 64
-// banks). Waits on the DMA are explicit (vmcnt), because the compiler cannot see it.
+//  - gemm_bf16_persistent_kernel: one block of eight waves per CU walks 256 x 256 output tiles
+//    (SwiGLU: 128 gate and the matching 128 up columns, so a lane holds gate and up of the same
+//    output element) in an XCD-aware order; two groups of four waves alternate LDS fragment reads
+//    and MFMA clusters (ping-pong), and the LDS ring runs on across tiles.
+//  - gemm_bf16_wide_kernel, for expert groups averaging at least 2048 rows: the same tiles and
+//    order, four waves of 128 x 128 (accumulators in AGPRs) that place their memory instructions
+//    between their own MFMAs, and 64-wide K stages, so each DMA reads whole 128-byte row pieces.
+//  - gemm_bf16_kernel: four waves on one 64 x 128 (or 64 x 64) tile with a 6- (8-) stage ring, two
+//    blocks per CU, for groups of a few dozen rows (decode batches), whose time is spent streaming
+//    the weight panels.
+// All use v_mfma_f32_32x32x16_bf16 with fp32 accumulators. Operands stream into an LDS ring with
+// buffer_load ... lds (global -> LDS without registers); buffer descriptors bound each tile's rows,
+// so rows past an expert's end or columns past n_out read as zero and nothing is clamped. LDS rows of
+// 64 bytes have their four 16-byte chunks XOR-swizzled by (row >> 2) & 3, rows of 128 bytes their
+// eight chunks by (row >> 1) & 7, which keeps the 128-bit operand reads on gfx950 free of bank
+// conflicts (16 lanes per LDS cycle, 64 banks). Waits on the DMA are explicit (vmcnt), because the
+// compiler cannot see it.
 #include "moe_common.h"
 #include "moe_kernels.h"
 #include "../../include/moe.h"
@@ -475,14 +480,14 @@ __device__ __forceinline__ XcdPlan xcd_plan(uint32_t R, uint32_t xcd, uint32_t n
     return p;
 }
 
-// Build the schedule in LDS (512 threads) and fill a TileSched.
-template <int BM, int BNO, int GM>
+// Build the schedule in LDS (a block of NT threads) and fill a TileSched.
+template <int BM, int BNO, int GM, int NT = 512>
 __device__ __forceinline__ TileSched<BM, BNO, GM> setup_sched(const int32_t* __restrict__ offsets, int e_begin,
                                                               int n_groups, int64_t dense_rows, int n_out,
                                                               int* s_ts, int* s_off, int* s_wave) {
     if (offsets) {
-        for (int g = threadIdx.x; g <= n_groups; g += 512) s_off[g] = offsets[e_begin + g];
-        build_schedule<BM, 512>(offsets, e_begin, n_groups, s_ts, s_wave);  // ends with a barrier
+        for (int g = threadIdx.x; g <= n_groups; g += NT) s_off[g] = offsets[e_begin + g];
+        build_schedule<BM, NT>(offsets, e_begin, n_groups, s_ts, s_wave);  // ends with a barrier
     }
     TileSched<BM, BNO, GM> ts;
     ts.s_ts = s_ts;
@@ -498,62 +503,81 @@ __device__ __forceinline__ TileSched<BM, BNO, GM> setup_sched(const int32_t* __r
     return ts;
 }
 
-// Epilogue of one wave's block of a tile: acc[i][j] holds (feature x token) 32 x 32 blocks; a lane
-// owns token i*32 + lane%32 of the wave's 64 and, per group of 4 registers, 4 consecutive features.
+// Epilogue of one 32-token row block of a wave: a[j] holds a (feature x token) 32 x 32 block; a lane
+// owns token `row` and, per group of 4 registers, 4 consecutive features from fbase + j * 32. FENCE
+// keeps each group's reads of the accumulators next to its stores (for accumulators held in the
+// AGPR file, so the copies out of it do not pile up in VGPRs).
+// One accumulator value copied out of the AGPR file: the operand constraint keeps the accumulators
+// in AGPRs where the epilogue's arithmetic would otherwise pull them into VGPRs.
+__device__ __forceinline__ float from_agpr(float x) {
+    float y;
+    asm("v_accvgpr_read_b32 %0, %1" : "=v"(y) : "a"(x));
+    return y;
+}
+template <int EPI, int TN, bool FENCE = false>
+__device__ __forceinline__ void store_block(const floatx16 (&a)[TN], int64_t row, int64_t row_end, int e,
+                                            int fbase, int lane, uint16_t* __restrict__ C,
+                                            const uint16_t* __restrict__ bias, int n_out) {
+    constexpr bool GATED = EPI == EPI_SWIGLU;
+    constexpr int TNO = GATED ? TN / 2 : TN;
+    const int khalf = lane >> 5;
+    auto rd = [&](float x) { return FENCE ? from_agpr(x) : x; };
+#pragma unroll
+    for (int j = 0; j < TNO; ++j) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int f0 = fbase + j * 32 + 8 * q4 + 4 * khalf;
+            float o[4];
+            if (GATED) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float z = rd(a[j][4 * q4 + c]);
+                    o[c] = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) * rd(a[j + TNO][4 * q4 + c]);
+                }
+            } else {
+                float bc[4] = {0.f, 0.f, 0.f, 0.f};
+                if (bias != nullptr && f0 < n_out) {
+                    const uint2 bb = *reinterpret_cast<const uint2*>(bias + (int64_t)e * n_out + f0);
+                    bc[0] = __uint_as_float(bb.x << 16);
+                    bc[1] = __uint_as_float(bb.x & 0xffff0000u);
+                    bc[2] = __uint_as_float(bb.y << 16);
+                    bc[3] = __uint_as_float(bb.y & 0xffff0000u);
+                }
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float z = rd(a[j][4 * q4 + c]) + bc[c];
+                    o[c] = EPI == EPI_GELU_BIAS ? gelu_f(z) : z;
+                }
+            }
+            if (EPI == EPI_F32) {
+                if (row < row_end && f0 < n_out)
+                    *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(C) + row * n_out + f0) =
+                        floatx4{rd(a[j][4 * q4]), rd(a[j][4 * q4 + 1]), rd(a[j][4 * q4 + 2]), rd(a[j][4 * q4 + 3])};
+                continue;
+            }
+            if (row < row_end && f0 < n_out) {
+                uint2 pk;
+                pk.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+                    pk.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+                *reinterpret_cast<uint2*>(C + row * n_out + f0) = pk;
+            }
+            if (FENCE) __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// Epilogue of one wave's block of a tile (eight-wave layout): acc[i] is the row block of tokens
+// grp * 128 + wm * 64 + i * 32, features from n0 + wn * (TNO * 32).
 template <int EPI, int TM, int TN>
 __device__ __forceinline__ void store_tile(const floatx16 (&acc)[TM][TN], int64_t row0, int64_t row_end, int e,
                                            int n0, int grp, int wm, int wn, int lane,
                                            uint16_t* __restrict__ C, const uint16_t* __restrict__ bias,
                                            int n_out) {
-    constexpr bool GATED = EPI == EPI_SWIGLU;
-    constexpr int TNO = GATED ? TN / 2 : TN, WTNO = TNO * 32;
-    const int khalf = lane >> 5;
+    constexpr int TNO = EPI == EPI_SWIGLU ? TN / 2 : TN, WTNO = TNO * 32;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int64_t row = row0 + grp * 128 + wm * 64 + i * 32 + (lane & 31);
-#pragma unroll
-        for (int j = 0; j < TNO; ++j) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int f0 = n0 + wn * WTNO + j * 32 + 8 * q4 + 4 * khalf;
-                float o[4];
-                if (GATED) {
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const float z = acc[i][j][4 * q4 + c];
-                        o[c] = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) * acc[i][j + TNO][4 * q4 + c];
-                    }
-                } else {
-                    float bc[4] = {0.f, 0.f, 0.f, 0.f};
-                    if (bias != nullptr && f0 < n_out) {
-                        const uint2 bb = *reinterpret_cast<const uint2*>(bias + (int64_t)e * n_out + f0);
-                        bc[0] = __uint_as_float(bb.x << 16);
-                        bc[1] = __uint_as_float(bb.x & 0xffff0000u);
-                        bc[2] = __uint_as_float(bb.y << 16);
-                        bc[3] = __uint_as_float(bb.y & 0xffff0000u);
-                    }
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const float z = acc[i][j][4 * q4 + c] + bc[c];
-                        o[c] = EPI == EPI_GELU_BIAS ? gelu_f(z) : z;
-                    }
-                }
-                if (EPI == EPI_F32) {
-                    if (row < row_end && f0 < n_out)
-                        *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(C) + row * n_out + f0) =
-                            floatx4{acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2],
-                                    acc[i][j][4 * q4 + 3]};
-                    continue;
-                }
-                if (row < row_end && f0 < n_out) {
-                    uint2 pk;
-                    pk.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
-                    pk.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
-                    *reinterpret_cast<uint2*>(C + row * n_out + f0) = pk;
-                }
-            }
-        }
-    }
+    for (int i = 0; i < TM; ++i)
+        store_block<EPI, TN>(acc[i], row0 + grp * 128 + wm * 64 + i * 32 + (lane & 31), row_end, e, n0 + wn * WTNO,
+                             lane, C, bias, n_out);
 }
 
 // Partial buffer: a header, then the fp32 accumulators of each tile slice as
@@ -819,6 +843,246 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
 #undef PS_MMA
 }
 
+// Four-wave, wide-K form of the persistent GEMM, for large groups: the same 256 x 256 tiles, tile
+// sequence, XCD plan and K split, with each wave owning a 128 x 128 block of the tile (16 accumulators
+// of 32 x 32 in the AGPR file, one wave per SIMD) and the memory instructions placed between the
+// wave's own MFMAs instead of in a partner wave's cluster. Stages are 64 columns wide (128-byte LDS
+// rows, a two-slot ring), so each DMA instruction reads 8 whole 128-byte row pieces instead of 16
+// half lines. K-split slices store their partial tiles in the eight-wave layout that
+// gemm_bf16_tail_kernel reads. Chunk c of LDS
+// row r sits at position c ^ ((r / 2) % 8), which keeps the 16-lane groups of a fragment read on
+// distinct banks. A stage is four 16-wide K steps; the DMAs of the next stage all go out during the
+// first step, and the last step waits for them, passes the stage barrier and reads the next stage's
+// first fragments.
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+template <int EPI, int GM>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ C, const int32_t* __restrict__ offsets, int e_begin, int n_groups, int64_t dense_rows,
+    int n_out, int K, float* __restrict__ partials) {
+    constexpr int BM = 256, BN = 256, BK = 64, NS = 2;
+    constexpr bool GATED = EPI == EPI_SWIGLU;
+    constexpr int TM = 4;
+    constexpr int BNO = GATED ? BN / 2 : BN, WTNO = BNO / 2, TNO = WTNO / 32, TN = GATED ? 2 * TNO : TNO;
+    constexpr int STAGE_ELEMS = (BM + BN) * BK;  // 512 rows of 128 bytes
+    constexpr int STAGE_BYTES = STAGE_ELEMS * 2;
+    constexpr int NQ = 16;  // DMA instructions per wave per stage (8 rows each)
+    static_assert(TN == 4, "tile shape");
+    static_assert(NS * STAGE_BYTES + 2 * 1025 * 4 + 8 * 4 <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE_ELEMS];
+    __shared__ int s_ts[1025];
+    __shared__ int s_off[1025];
+    __shared__ int s_wave[8];
+
+    const int tid = threadIdx.x, lane = lane_id();
+    const TileSched<BM, BNO, GM> ts =
+        setup_sched<BM, BNO, GM, 256>(offsets, e_begin, n_groups, dense_rows, n_out, s_ts, s_off, s_wave);
+    const int nk = K / BK;
+    const uint32_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
+    const XcdPlan plan = xcd_plan(ts.R, xcd, nslots, nk, partials != nullptr);
+    const uint32_t nw = plan.nwhole + ((plan.S == 1 && slot < plan.rem) ? 1u : 0u);
+    const bool has_slice = plan.S >= 2 && slot < plan.rem * plan.S;
+    const uint32_t slice_lin = plan.chunk0 + plan.nwhole * nslots + (has_slice ? slot / plan.S : 0);
+    const int slice_part = has_slice ? (int)(slot % plan.S) : 0;
+    const int slice_kb = slice_part * nk / (int)plan.S, slice_ke = (slice_part + 1) * nk / (int)plan.S;
+    const int nunits = (int)nw + (has_slice ? 1 : 0);
+    if (partials != nullptr && tid == 0) {
+        TailHeader* hdr = reinterpret_cast<TailHeader*>(partials);
+        if (slot == 0) {
+            hdr->rem[xcd] = (int32_t)plan.rem;
+            hdr->S[xcd] = (int32_t)plan.S;
+        }
+        if (has_slice && slice_part == 0) {
+            TailTile tt;
+            ts.decode(slice_lin, tt.row0, tt.row_end, tt.e, tt.n0);
+            hdr->tile[xcd][slot / plan.S] = tt;
+        }
+    }
+    if (nunits == 0) return;  // uniform per block
+    auto unit_lin = [&](int u) { return u < (int)nw ? plan.chunk0 + slot + (uint32_t)u * nslots : slice_lin; };
+    auto unit_kb = [&](int u) { return u < (int)nw ? 0 : slice_kb; };
+    auto unit_ke = [&](int u) { return u < (int)nw ? nk : slice_ke; };
+
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+    const int64_t n_b_rows = GATED ? 2 * (int64_t)n_out : n_out;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)lds;
+
+    // DMA q of this wave: LDS rows (q * 4 + wave) * 8 + [0, 8); rows 0-255 token tile, 256-511 weights
+    int voff[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int R = (q * 4 + wave) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz8(R);
+        const int row = q < 8 ? R : ((GATED && q >= 12) ? R - 384 : R - 256);
+        voff[q] = row * K * 2 + c * 16;
+    }
+    i32x4 ra, rb0, rb1;
+    auto set_dma_tile = [&](uint32_t lin) {
+        int64_t row0, row_end;
+        int e, n0;
+        ts.decode(lin, row0, row_end, e, n0);
+        const int64_t a_rows = row_end - row0 < BM ? row_end - row0 : BM;
+        ra = make_rsrc(A + row0 * K, (uint32_t)(a_rows * K * 2));
+        const uint16_t* Bg = B + (int64_t)e * n_b_rows * K;
+        const int bn_part = GATED ? BN / 2 : BN;
+        const int bcols = n_out - n0 < bn_part ? n_out - n0 : bn_part;
+        rb0 = make_rsrc(Bg + (int64_t)n0 * K, (uint32_t)((int64_t)bcols * K * 2));
+        rb1 = make_rsrc(Bg + (int64_t)(GATED ? n_out + n0 : n0) * K, (uint32_t)((int64_t)bcols * K * 2));
+    };
+
+    int a_off[TM], a_sw[TM], b_off[TN], b_sw[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int r = wm * 128 + i * 32 + (lane & 31);
+        a_off[i] = r * BK;
+        a_sw[i] = swz8(r);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int jj = j < TNO ? j : j - TNO;
+        const int r = BM + (GATED && j >= TNO ? BN / 2 : 0) + wn * WTNO + jj * 32 + (lane & 31);
+        b_off[j] = r * BK;
+        b_sw[j] = swz8(r);
+    }
+    const int khalf = lane >> 5;
+
+    floatx16 acc[TM][TN];
+    bf16x8 fa[2][TM], fb[2][TN];
+
+#define PW_DMA(slot_, ks_, q_)                                                                            \
+    dma16(lds_base + (slot_) * STAGE_BYTES + ((q_) * 4 + wave) * 1024, voff[q_],                          \
+          (q_) < 8 ? ra : ((GATED && (q_) >= 12) ? rb1 : rb0), (ks_) * (BK * 2));
+    // fragment n (in MFMA use order: fa0, fb0..fb3, fa1..fa3) of 16-wide K step kk_ into buffer b_
+#define PW_READ(b_, kk_, slot_, n_)                                                                       \
+    {                                                                                                     \
+        const int m_ = (n_) == 0 ? 0 : ((n_) <= 4 ? (n_) + 3 : (n_) - 4);                                 \
+        const uint16_t* L_ = lds + (slot_) * STAGE_ELEMS;                                                 \
+        const int c_ = (kk_) * 2 + khalf;                                                                 \
+        if (m_ < 4)                                                                                       \
+            fa[b_][m_ & 3] = *reinterpret_cast<const bf16x8*>(L_ + a_off[m_ & 3] + ((c_ ^ a_sw[m_ & 3]) << 3)); \
+        else                                                                                              \
+            fb[b_][m_ & 3] = *reinterpret_cast<const bf16x8*>(L_ + b_off[m_ & 3] + ((c_ ^ b_sw[m_ & 3]) << 3)); \
+    }
+#define PW_MMA(b_, t_)                                                                                    \
+    acc[(t_) >> 2][(t_) & 3] =                                                                            \
+        __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[b_][(t_) & 3], fa[b_][(t_) >> 2], acc[(t_) >> 2][(t_) & 3], 0, 0, 0);
+
+    int dma_u = 0;
+    set_dma_tile(unit_lin(0));
+    int w_ks = unit_kb(0), w_ke = unit_ke(0);
+    // past the block's last stage the DMAs go on with zero-range descriptors into the free slot
+    auto dma_advance = [&]() {
+        if (++w_ks == w_ke) {
+            if (dma_u + 1 < nunits) {
+                ++dma_u;
+                set_dma_tile(unit_lin(dma_u));
+                w_ks = unit_kb(dma_u);
+                w_ke = unit_ke(dma_u);
+            } else {
+                ra = make_rsrc(A, 0);
+                rb0 = ra;
+                rb1 = ra;
+            }
+        }
+    };
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) PW_DMA(0, w_ks, q)
+    dma_advance();
+    wait_vm<0>();
+    lds_barrier();
+#pragma unroll
+    for (int n = 0; n < 8; ++n) PW_READ(0, 0, 0, n)
+    __builtin_amdgcn_sched_barrier(0);
+
+    int r_slot = 0;
+    // one stage: K step 0 with the next stage's 16 DMAs between its MFMAs (and step 1's fragment
+    // reads), steps 1 and 2 with the reads of the following step, step 3: four MFMAs, the wait for the
+    // next stage's DMAs and the stage barrier, the rest with the reads of the next stage's first step
+#define PW_STAGE                                                                                          \
+    {                                                                                                     \
+        const int n_slot = r_slot ^ 1;                                                                    \
+        _Pragma("unroll") for (int t = 0; t < 16; ++t) {                                                  \
+            PW_MMA(0, t)                                                                                  \
+            PW_DMA(n_slot, w_ks, t)                                                                       \
+            if ((t & 1) == 0) PW_READ(1, 1, r_slot, t >> 1)                                               \
+            __builtin_amdgcn_sched_barrier(0);                                                            \
+        }                                                                                                 \
+        dma_advance();                                                                                    \
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                                \
+        __builtin_amdgcn_sched_barrier(0);                                                                \
+        _Pragma("unroll") for (int t = 0; t < 16; ++t) {                                                  \
+            PW_MMA(1, t)                                                                                  \
+            if ((t & 1) == 0) PW_READ(0, 2, r_slot, t >> 1)                                               \
+            __builtin_amdgcn_sched_barrier(0);                                                            \
+        }                                                                                                 \
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                                \
+        __builtin_amdgcn_sched_barrier(0);                                                                \
+        _Pragma("unroll") for (int t = 0; t < 16; ++t) {                                                  \
+            PW_MMA(0, t)                                                                                  \
+            if ((t & 1) == 0) PW_READ(1, 3, r_slot, t >> 1)                                               \
+            __builtin_amdgcn_sched_barrier(0);                                                            \
+        }                                                                                                 \
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                                \
+        __builtin_amdgcn_sched_barrier(0);                                                                \
+        _Pragma("unroll") for (int t = 0; t < 4; ++t) PW_MMA(1, t)                                        \
+        __builtin_amdgcn_sched_barrier(0);                                                                \
+        wait_vm<0>();                                                                                     \
+        lds_barrier();                                                                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                                \
+        _Pragma("unroll") for (int t = 4; t < 16; ++t) {                                                  \
+            PW_MMA(1, t)                                                                                  \
+            if (t >= 4 && t < 12) PW_READ(0, 0, n_slot, t - 4)                                            \
+            __builtin_amdgcn_sched_barrier(0);                                                            \
+        }                                                                                                 \
+        r_slot = n_slot;                                                                                  \
+    }
+    for (int u = 0; u < nunits; ++u) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+        const int ns = unit_ke(u) - unit_kb(u);
+        for (int st = 0; st < ns; ++st) PW_STAGE
+        if (u < (int)nw) {
+            int64_t row0, row_end;
+            int e, n0;
+            ts.decode(unit_lin(u), row0, row_end, e, n0);
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                store_block<EPI, TN, true>(acc[i], row0 + wm * 128 + i * 32 + (ln & 31), row_end, e,
+                                           n0 + wn * WTNO, ln, C, bias, n_out);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            float* pb = partials;
+            int ln = lane;
+            asm volatile("" : "+s"(pb), "+v"(ln));
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                floatx4* dst = partial_at<2, TN>(pb, xcd * nslots + slot, wm * 4 + ((i >> 1) | (wn << 1)));
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int v4 = 0; v4 < 4; ++v4)
+                        dst[(((i & 1) * TN + j) * 4 + v4) * 64 + ln] =
+                            floatx4{from_agpr(acc[i][j][4 * v4]), from_agpr(acc[i][j][4 * v4 + 1]),
+                                    from_agpr(acc[i][j][4 * v4 + 2]), from_agpr(acc[i][j][4 * v4 + 3])};
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vm<0>();  // no DMA may land in LDS after the block has left the CU
+#undef PW_STAGE
+#undef PW_DMA
+#undef PW_READ
+#undef PW_MMA
+}
+
 // Tail of gemm_bf16_persistent_kernel: sums the S fp32 partial tiles of each split tail tile in
 // slice order and applies the epilogue. One thread per group of 4 consecutive output features of
 // one token (gate and up together for SwiGLU); block b covers XCD b % 8, tail tile (b / 8) / CH and
@@ -925,6 +1189,37 @@ void launch_bf16_persistent(int epi, const void* A, const void* B, const void* b
     else if (epi == EPI_F32) MOE_PERSIST(EPI_F32)
     else MOE_PERSIST(EPI_BIAS)
 #undef MOE_PERSIST
+}
+
+template <int GM>
+void launch_bf16_wide(int epi, const void* A, const void* B, const void* bias, void* C, const int32_t* offsets,
+                    int e_begin, int n_groups, int64_t max_rows, int64_t dense_rows, int n_out, int K, float* partials,
+                    hipStream_t s) {
+    const int bno = epi == EPI_SWIGLU ? 128 : 256;
+    const int64_t m_tiles = offsets ? (max_rows + 255) / 256 + n_groups : (dense_rows + 255) / 256;
+    const int64_t tiles = m_tiles * ((n_out + bno - 1) / bno);
+    if (tiles <= 0) return;
+    const int64_t cap = persistent_grid_cap();
+    const int64_t want = ((tiles + 7) / 8) * 8;
+    const unsigned grid = (unsigned)(want < cap && (offsets || !partials) ? want : cap);
+    if (!offsets && tiles % grid == 0) partials = nullptr;
+    const auto a = static_cast<const uint16_t*>(A);
+    const auto b = static_cast<const uint16_t*>(B);
+    const auto bi = static_cast<const uint16_t*>(bias);
+    auto c = static_cast<uint16_t*>(C);
+#define MOE_WIDE(EPI_)                                                                                      \
+    {                                                                                                     \
+        gemm_bf16_wide_kernel<EPI_, GM><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,      \
+                                                            dense_rows, n_out, K, partials);              \
+        if (partials)                                                                                     \
+            gemm_bf16_tail_kernel<EPI_><<<grid * tail_chunks<EPI_>(), 256, 0, s>>>(partials, bi, c, n_out,  \
+                                                                                  (int)(grid / 8));       \
+    }
+    if (epi == EPI_SWIGLU) MOE_WIDE(EPI_SWIGLU)
+    else if (epi == EPI_GELU_BIAS) MOE_WIDE(EPI_GELU_BIAS)
+    else if (epi == EPI_F32) MOE_WIDE(EPI_F32)
+    else MOE_WIDE(EPI_BIAS)
+#undef MOE_WIDE
 }
 
 // fp32 path (SIMT, 64 x 64 output tile, 4 x 4 per thread, sequential fp32 FMA over K).
@@ -1057,8 +1352,15 @@ void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* 
                                              n_out, K, s);
             return;
         }
-        launch_bf16_persistent<8, 3>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows, n_out, K,
-                                     partials, s);
+        // expert groups averaging at least kGemmWideRows rows take the four-wave wide-K kernel;
+        // smaller groups and dense products keep the eight-wave kernel, whose deeper ring streams
+        // weights better
+        if (offsets != nullptr && max_rows >= kGemmWideRows * (int64_t)(n_groups > 0 ? n_groups : 1))
+            launch_bf16_wide<8>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows, n_out, K,
+                                partials, s);
+        else
+            launch_bf16_persistent<8, 3>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows,
+                                         n_out, K, partials, s);
         return;
     }
     const int64_t m_tiles = offsets ? (max_rows + 63) / 64 + n_groups : (dense_rows + 63) / 64;

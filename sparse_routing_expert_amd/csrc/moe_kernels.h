@@ -146,6 +146,10 @@ void launch_bwd_gate(const float* logits, const int32_t* topk_idx, const float* 
                      float aux_coef, int64_t T, int E, int k, int score, int renorm, float* dl, hipStream_t s);
 // dw_r = dl^T x (token chunks of kRouterChunk summed in order through `partials`), dx = dx32 + dl W_r
 constexpr int kRouterChunk = 256;
+// bf16 grouped GEMM: expert groups averaging at least this many rows use the four-wave wide-K
+// persistent kernel (measured: Mixtral-shaped projections, 2048 rows per expert, 2-3 % faster; groups
+// of 128 to 1024 rows and a dense 4096-row product slower than on the eight-wave kernel)
+constexpr int64_t kGemmWideRows = 2048;
 constexpr int kRouterWgradExperts = 32;  // experts per dW_r block (x read once per 32 experts)
 constexpr int kRouterDgradTokens = 16;   // tokens per dx block (W_r read once per 16 tokens)
 size_t bwd_router_partials_bytes(int64_t T, int E, int d);
