@@ -848,13 +848,13 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
 // of 32 x 32 in the AGPR file, one wave per SIMD) and the memory instructions placed between the
 // wave's own MFMAs instead of in a partner wave's cluster. Stages are 64 columns wide (128-byte LDS
 // rows, a two-slot ring), so each DMA instruction reads 8 whole 128-byte row pieces instead of 16
-// half lines. K-split slices store their partial tiles in the eight-wave layout that
-// gemm_bf16_tail_kernel reads. Chunk c of LDS
-// row r sits at position c ^ ((r / 2) % 8), which keeps the 16-lane groups of a fragment read on
-// distinct banks. A stage is four 16-wide K steps; the DMAs of the next stage all go out during the
-// first step, and the last step waits for them, passes the stage barrier and reads the next stage's
-// first fragments.
+// half lines. Chunk c of LDS row r sits at position c ^ ((r / 2) % 8), which keeps the 16-lane groups
+// of a fragment read on distinct banks. A stage is four 16-wide K steps; the DMAs of the next stage go
+// out during the first two (one after every other MFMA), and the last step waits for them, passes the
+// stage barrier and reads the next stage's first fragments. K-split slices store their partial tiles
+// in the eight-wave layout that gemm_bf16_tail_kernel reads.
 __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+
 template <int EPI, int GM>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, const uint16_t* __restrict__ bias,
@@ -996,26 +996,28 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
     __builtin_amdgcn_sched_barrier(0);
 
     int r_slot = 0;
-    // one stage: K step 0 with the next stage's 16 DMAs between its MFMAs (and step 1's fragment
-    // reads), steps 1 and 2 with the reads of the following step, step 3: four MFMAs, the wait for the
-    // next stage's DMAs and the stage barrier, the rest with the reads of the next stage's first step
+    // one stage: K steps 0 and 1 with the next stage's 16 DMAs after their odd MFMAs and the following
+    // step's fragment reads after their even ones, step 2 with the reads of step 3, step 3: four MFMAs,
+    // the wait for the next stage's DMAs and the stage barrier, the rest with the reads of the next
+    // stage's first step
 #define PW_STAGE                                                                                          \
     {                                                                                                     \
         const int n_slot = r_slot ^ 1;                                                                    \
         _Pragma("unroll") for (int t = 0; t < 16; ++t) {                                                  \
             PW_MMA(0, t)                                                                                  \
-            PW_DMA(n_slot, w_ks, t)                                                                       \
+            if (t & 1) PW_DMA(n_slot, w_ks, t >> 1)                                                       \
             if ((t & 1) == 0) PW_READ(1, 1, r_slot, t >> 1)                                               \
             __builtin_amdgcn_sched_barrier(0);                                                            \
         }                                                                                                 \
-        dma_advance();                                                                                    \
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                                \
         __builtin_amdgcn_sched_barrier(0);                                                                \
         _Pragma("unroll") for (int t = 0; t < 16; ++t) {                                                  \
             PW_MMA(1, t)                                                                                  \
+            if (t & 1) PW_DMA(n_slot, w_ks, 8 + (t >> 1))                                                 \
             if ((t & 1) == 0) PW_READ(0, 2, r_slot, t >> 1)                                               \
             __builtin_amdgcn_sched_barrier(0);                                                            \
         }                                                                                                 \
+        dma_advance();                                                                                    \
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                                \
         __builtin_amdgcn_sched_barrier(0);                                                                \
         _Pragma("unroll") for (int t = 0; t < 16; ++t) {                                                  \
