@@ -21,6 +21,8 @@ CASES = {
     "f32_swiglu_sigmoid_shared": TINY.with_sizes(act="swiglu", score="sigmoid", router="biased", E=6, k=3, T=100,
                                                  Fs=64),
     "bf16_gelu_bias": TINY.with_sizes(dtype="bf16", T=300, d=128, F=192, E=6, k=2),
+    # GELU with biases on the four-wave wide-K GEMM (experts averaging >= 2048 rows)
+    "wide_gelu_bias": TINY.with_sizes(dtype="bf16", T=4200, d=192, F=320, E=2, k=1),
     "small_mini": I.mini("small_bf16", T=1000, d=256, F=320),
     "small_norenorm": I.mini("small_bf16", T=300, d=128, F=128, renorm=False),
     "mixtral_mini": I.mini("mixtral_prefill", T=700, d=512, F=448),
