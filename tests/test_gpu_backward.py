@@ -43,6 +43,9 @@ CASES = {
     # weights (SwiGLU, and GELU with biases, whose n_in = F)
     "rows1600_swiglu": (I.mini("small_bf16", T=1600, d=256, F=192, E=2, k=2), 0, 0.01),
     "rows1600_gelu_bias": (TINY.with_sizes(dtype="bf16", T=3200, d=128, F=192, E=2, k=1), 0, 0.0),
+    # at least 2048 rows per expert: every grouped product, the fp32 dgrad ones included, runs on the
+    # four-wave wide-K GEMM
+    "rows2100_swiglu": (I.mini("small_bf16", T=2100, d=256, F=192, E=2, k=2), 0, 0.01),
 }
 
 
