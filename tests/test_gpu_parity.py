@@ -27,6 +27,10 @@ CASES = {
     "small_norenorm": I.mini("small_bf16", T=300, d=128, F=128, renorm=False),
     "mixtral_mini": I.mini("mixtral_prefill", T=700, d=512, F=448),
     "mixtral_decode_mini": I.mini("mixtral_prefill", T=64, d=512, F=448),
+    # decode-sized groups with a long down-projection K (16384) on the small-group GEMM, SwiGLU and
+    # GELU with biases
+    "decode_split_down": I.mini("mixtral_prefill", T=64, d=256, F=16384),
+    "decode_split_gelu_bias": TINY.with_sizes(dtype="bf16", T=64, d=128, F=16384, E=4, k=2),
     "qwen_mini": I.mini("qwen3_30b_a3b", T=2000, d=256, F=192),
     "deepseek_mini": I.mini("deepseek_v3", T=500, d=448, F=128, Fs=192),
     "E1_k1": I.mini("small_bf16", T=300, d=128, F=128, E=1, k=1),
