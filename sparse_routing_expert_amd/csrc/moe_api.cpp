@@ -237,9 +237,9 @@ void do_route(const moe_shape* s, const void* x, const float* w_router, const fl
     float* blk_P = stats ? at<float>(ws, w.blk_P) : nullptr;
     float* blk_H = stats ? at<float>(ws, w.blk_H) : nullptr;
     if (moe::route_small_ok(s->dtype, s->E, s->k, s->d_model)) {  // logits and selection in one launch
-        const int nblk = (int)cdiv(s->T, moe::route_small_tokens_per_block(s->T, s->E));
-        moe::launch_route_small(x, w_router, sel_bias, s->T, s->d_model, s->E, s->k, s->score, s->renorm, logits,
-                                topk_idx, topk_w, blk_counts, blk_P, blk_H, ticket, st);
+        const int nblk = (int)cdiv(s->T, moe::route_small_tokens_per_block(s->T, s->E, false));
+        moe::launch_route_small(x, w_router, nullptr, nullptr, sel_bias, s->T, s->d_model, s->E, s->k, s->score,
+                                s->renorm, logits, topk_idx, topk_w, blk_counts, blk_P, blk_H, ticket, st);
         moe::launch_route_finalize(blk_counts, blk_P, blk_H, nblk, s->T, s->E, counts, at<double>(ws, w.fp), ticket,
                                    stats, st);
         return;
@@ -266,6 +266,14 @@ void do_route_noisy(const moe_shape* s, const void* x, const float* w_router, co
     int32_t* blk_counts = at<int32_t>(ws, w.blk_counts);
     float* blk_P = stats ? at<float>(ws, w.blk_P) : nullptr;
     float* blk_H = stats ? at<float>(ws, w.blk_H) : nullptr;
+    if (moe::route_small_ok(s->dtype, s->E, s->k, s->d_model)) {  // both projections and the selection fused
+        const int nblk = (int)cdiv(s->T, moe::route_small_tokens_per_block(s->T, s->E, true));
+        moe::launch_route_small(x, w_router, w_noise, noise, sel_bias, s->T, s->d_model, s->E, s->k, s->score,
+                                s->renorm, logits, topk_idx, topk_w, blk_counts, blk_P, blk_H, ticket, st);
+        moe::launch_route_finalize(blk_counts, blk_P, blk_H, nblk, s->T, s->E, counts, at<double>(ws, w.fp), ticket,
+                                   stats, st);
+        return;
+    }
     route_logits(s, w, x, w_router, wsplit, ticket, lg, ws, st);
     route_logits(s, w, x, w_noise, wsplit_n, ticket, sl, ws, st);
     moe::launch_route_select(lg, w.lg_ld, w.lg_split, nullptr, sel_bias, s->T, s->E, s->k, s->score, s->renorm,

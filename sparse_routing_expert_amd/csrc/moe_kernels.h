@@ -30,12 +30,13 @@ void launch_route_select(const float* logits, int lg_ld, int lg_split, float* lo
 // every CU; the select kernel sums the three products.
 constexpr int kRouteGemmMinEpad = 64;
 // Small routers (route_small_ok): logits (written to `logits` when given), selection and per-block
-// partials in one launch over blocks of route_small_tokens_per_block(T, E) tokens; zeroes *ticket.
+// partials in one launch over blocks of route_small_tokens_per_block(T, E, noisy) tokens; zeroes *ticket.
 bool route_small_ok(int dtype, int E, int k, int d);
-int route_small_tokens_per_block(int64_t T, int E);
-void launch_route_small(const void* x, const float* w_router, const float* sel_bias, int64_t T, int d, int E, int k,
-                        int score, int renorm, float* logits, int32_t* topk_idx, float* topk_w, int32_t* blk_counts,
-                        float* blk_P, float* blk_H, int32_t* ticket, hipStream_t s);
+int route_small_tokens_per_block(int64_t T, int E, bool noisy);
+void launch_route_small(const void* x, const float* w_router, const float* w_noise, const float* noise,
+                        const float* sel_bias, int64_t T, int d, int E, int k, int score, int renorm, float* logits,
+                        int32_t* topk_idx, float* topk_w, int32_t* blk_counts, float* blk_P, float* blk_H,
+                        int32_t* ticket, hipStream_t s);
 // counts[E] always; stats (f, P, aux, entropy) when stats != NULL
 void launch_route_finalize(const int32_t* blk_counts, const float* blk_P, const float* blk_H, int nblk, int64_t T,
                            int E, int32_t* counts, double* fp_scratch, int32_t* ticket, float* stats,

@@ -377,15 +377,19 @@ __global__ __launch_bounds__(kSelWaves * 64) void route_select_kernel(const floa
 // are summed in LDS in wave order, then each wave selects for its share of the block's tokens
 // (select_token, lane e holding expert e) and the block writes its partials for route_finalize.
 // Block 0 zeroes the ticket route_finalize counts its blocks with.
+// NOISY (noisy top-k gating, "Mixture of Experts" tutorial, Noisy top-k gating): the K loop runs a
+// second time with the noise-scale projection w_noise, and the selection uses
+// H = l + noise * softplus(x w_noise^T) in place of l (H is what logits_out receives).
 constexpr int kFusedRouteWaves = 8;
-template <int TT>
+template <int TT, bool NOISY>
 __global__ __launch_bounds__(kFusedRouteWaves * 64) void route_fused_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ w, const float* __restrict__ sel_bias, int64_t T, int d,
-    int E, int k, int score, int renorm, float* __restrict__ logits_out, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, int32_t* __restrict__ blk_counts, float* __restrict__ blk_P,
-    float* __restrict__ blk_H, int32_t* __restrict__ ticket) {
-    constexpr int NW = kFusedRouteWaves, TPB = 16 * TT, TPWV = TPB / NW;
-    __shared__ floatx4 s_part[NW][TT][64];
+    const uint16_t* __restrict__ x, const float* __restrict__ w, const float* __restrict__ w_noise,
+    const float* __restrict__ noise, const float* __restrict__ sel_bias, int64_t T, int d, int E, int k, int score,
+    int renorm, float* __restrict__ logits_out, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int32_t* __restrict__ blk_counts, float* __restrict__ blk_P, float* __restrict__ blk_H,
+    int32_t* __restrict__ ticket) {
+    constexpr int NW = kFusedRouteWaves, TPB = 16 * TT, TPWV = TPB / NW, NP = NOISY ? 2 : 1;
+    __shared__ floatx4 s_part[NP][NW][TT][64];
     __shared__ int s_cnt[64];
     __shared__ float s_P[NW][64];
     __shared__ float s_H[NW];
@@ -416,12 +420,8 @@ __global__ __launch_bounds__(kFusedRouteWaves * 64) void route_fused_kernel(
         xw[q] = R * 16 + (r ^ (R & 15));
     }
     const bool w_ok = r < E;  // padded expert rows are zero and not loaded
-    const float* wr = w + (int64_t)(w_ok ? r : 0) * d;
     const int nc = d / 32;
     const int kb0 = (wave * nc / NW) * 32, kb1 = ((wave + 1) * nc / NW) * 32;
-    floatx4 acc[TT];
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) acc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
     const floatx4 fzero = {0.f, 0.f, 0.f, 0.f};
     u32x4 xv[2][XI];
     floatx4 wf[2][4][2];
@@ -442,8 +442,7 @@ __global__ __launch_bounds__(kFusedRouteWaves * 64) void route_fused_kernel(
 #define RF_LOAD(b_, kb_)                                                                                  \
     {                                                                                                     \
         const int base = (kb_) + g * 8;                                                                   \
-        _Pragma("unroll") for (int q = 0; q < XI; ++q) xv[b_][q] =                                         \
-            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xq[q] + (kb_)));                    \
+        _Pragma("unroll") for (int q = 0; q < XI; ++q) xv[b_][q] = x_load(xq[q] + (kb_));                 \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                   \
             wf[b_][i][0] = w_ok ? *reinterpret_cast<const floatx4*>(wr + base + i * 32) : fzero;          \
             wf[b_][i][1] = w_ok ? *reinterpret_cast<const floatx4*>(wr + base + i * 32 + 4) : fzero;      \
@@ -464,6 +463,16 @@ __global__ __launch_bounds__(kFusedRouteWaves * 64) void route_fused_kernel(
             }                                                                                             \
         }                                                                                                 \
     }
+    // x is read once per pass; with a second pass it is loaded normally so that it stays in L2
+    auto x_load = [](const uint16_t* p_) {
+        return NOISY ? *reinterpret_cast<const u32x4*>(p_)
+                     : __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p_));
+    };
+    for (int pass = 0; pass < NP; ++pass) {
+    const float* wr = (pass == 0 ? w : w_noise) + (int64_t)(w_ok ? r : 0) * d;
+    floatx4 acc[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) acc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
     int kb = kb0;
     const int nsteps = (kb1 - kb0) / 128;
     if (nsteps > 0) {
@@ -497,12 +506,13 @@ __global__ __launch_bounds__(kFusedRouteWaves * 64) void route_fused_kernel(
         }
     }
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) s_part[wave][tt][lane] = acc[tt];
+    for (int tt = 0; tt < TT; ++tt) s_part[pass][wave][tt][lane] = acc[tt];
+    }  // pass
     __syncthreads();
     // Selection, one token per 16-lane DPP row: wave w takes tokens 4w + r (r = lane / 16) of the
     // block, lane e = lane % 16 of a row holds expert e. The same steps as select_token, with the
     // wave reductions replaced by row reductions, so a wave selects its tokens together.
-    const float* sp = reinterpret_cast<const float*>(&s_part[0][0][0]);
+    const float* sp = reinterpret_cast<const float*>(&s_part[0][0][0][0]);
     const bool softmax = score == MOE_SOFTMAX;
     const int row = lane >> 4, e = lane & 15;
     const int lt = wave * TPWV + row;
@@ -519,7 +529,14 @@ __global__ __launch_bounds__(kFusedRouteWaves * 64) void route_fused_kernel(
 #pragma unroll
         for (int wv = 1; wv < NW; ++wv) sum += sp[wv * TT * 256 + off];
         l = sum;
-        if (logits_out != nullptr) logits_out[t * E + e] = sum;
+        if (NOISY) {  // the noise-scale logit, summed the same way
+            const float* sq = sp + NW * TT * 256;
+            float sn = sq[off];
+#pragma unroll
+            for (int wv = 1; wv < NW; ++wv) sn += sq[wv * TT * 256 + off];
+            l = l + noise[t * E + e] * softplusf_(sn);
+        }
+        if (logits_out != nullptr) logits_out[t * E + e] = l;
     }
     const float m = row_max(l);
     const float p = live ? (softmax ? expf(l - m) : sigmoidf_(l)) : 0.f;
@@ -592,25 +609,29 @@ bool route_small_ok(int dtype, int E, int k, int d) {
     return dtype == MOE_BF16 && E <= 16 && k <= E;
 }
 
-int route_small_tokens_per_block(int64_t T, int E) {
+int route_small_tokens_per_block(int64_t T, int E, bool noisy) {
     (void)E;
-    return T >= 32 * 256 ? 32 : 16;  // two token tiles per block still leave a block per CU
+    // two token tiles per block still leave a block per CU; the noisy kernel keeps one tile (a second
+    // one would spill registers with both projections' loop state live)
+    return !noisy && T >= 32 * 256 ? 32 : 16;
 }
 
-void launch_route_small(const void* x, const float* w_router, const float* sel_bias, int64_t T, int d, int E, int k,
-                        int score, int renorm, float* logits, int32_t* topk_idx, float* topk_w, int32_t* blk_counts,
-                        float* blk_P, float* blk_H, int32_t* ticket, hipStream_t s) {
-    const int tpb = route_small_tokens_per_block(T, E);
+void launch_route_small(const void* x, const float* w_router, const float* w_noise, const float* noise,
+                        const float* sel_bias, int64_t T, int d, int E, int k, int score, int renorm, float* logits,
+                        int32_t* topk_idx, float* topk_w, int32_t* blk_counts, float* blk_P, float* blk_H,
+                        int32_t* ticket, hipStream_t s) {
+    const bool noisy = w_noise != nullptr;
+    const int tpb = route_small_tokens_per_block(T, E, noisy);
     const unsigned nblk = (unsigned)((T + tpb - 1) / tpb);
     const auto xb = static_cast<const uint16_t*>(x);
-    if (tpb == 32)
-        route_fused_kernel<2><<<nblk, kFusedRouteWaves * 64, 0, s>>>(xb, w_router, sel_bias, T, d, E, k, score, renorm,
-                                                                    logits, topk_idx, topk_w, blk_counts, blk_P,
-                                                                    blk_H, ticket);
-    else
-        route_fused_kernel<1><<<nblk, kFusedRouteWaves * 64, 0, s>>>(xb, w_router, sel_bias, T, d, E, k, score, renorm,
-                                                                    logits, topk_idx, topk_w, blk_counts, blk_P,
-                                                                    blk_H, ticket);
+#define MOE_ROUTE_FUSED(TT_, NOISY_)                                                                      \
+    route_fused_kernel<TT_, NOISY_><<<nblk, kFusedRouteWaves * 64, 0, s>>>(                               \
+        xb, w_router, w_noise, noise, sel_bias, T, d, E, k, score, renorm, logits, topk_idx, topk_w, blk_counts, \
+        blk_P, blk_H, ticket)
+    if (noisy) MOE_ROUTE_FUSED(1, true);
+    else if (tpb == 32) MOE_ROUTE_FUSED(2, false);
+    else MOE_ROUTE_FUSED(1, false);
+#undef MOE_ROUTE_FUSED
 }
 
 // Expert counts and balance statistics from the per-block partials, in fixed-order sums (float64
