@@ -75,8 +75,8 @@ def stage_bytes_flops(cfg, used_experts=None):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not part of "
-                                   "this build (see the sharding notes in DESIGN.md)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the library has no multi-GPU "
+                                   "path, so --gpus must be 1", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import numpy as np

@@ -60,7 +60,7 @@ extern "C" {
 typedef enum {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = -1, /* null required pointer, bad enum, inconsistent sizes, misalignment */
-    MOE_ERR_UNSUPPORTED = -2, /* valid request this build does not implement (e.g. d_model % 64) */
+    MOE_ERR_UNSUPPORTED = -2, /* valid request the library does not implement (e.g. d_model % 64) */
     MOE_ERR_WORKSPACE = -3,   /* ws_bytes below moe_workspace_bytes() for the call */
     MOE_ERR_HIP = -4          /* a kernel launch failed (hipGetLastError) */
 } moe_status;
