@@ -291,12 +291,15 @@ void do_permute(const moe_shape* s, const int32_t* topk_idx, const void* x, int3
         moe::launch_perm_scatter(x, inv_pos, s->T, s->d_model, s->k, elem_bytes(s), x_perm, st);
         return;
     }
-    moe::launch_perm_count(topk_idx, A, s->E, at<int32_t>(ws, w.tile_counts), st);
-    moe::launch_perm_scan(at<int32_t>(ws, w.tile_counts), w.ntiles, A, s->E, s->capacity, at<int32_t>(ws, w.tile_base),
-                          offsets, st);
-    moe::launch_perm_rank(topk_idx, at<int32_t>(ws, w.tile_base), offsets, A, s->E, s->k, s->capacity, inv_pos,
-                          sorted_token, st);
-    moe::launch_perm_scatter(x, inv_pos, s->T, s->d_model, s->k, elem_bytes(s), x_perm, st);
+    int32_t* tile_counts = at<int32_t>(ws, w.tile_counts);
+    moe::launch_perm_local(topk_idx, A, s->E, tile_counts, inv_pos, st);  // inv_pos holds in-tile ranks
+    int32_t* tile_base = nullptr;
+    if (!moe::perm_fold_ok(A, s->E, s->k)) {
+        tile_base = at<int32_t>(ws, w.tile_base);
+        moe::launch_perm_scan(tile_counts, w.ntiles, A, s->E, s->capacity, tile_base, offsets, st);
+    }
+    moe::launch_perm_place_scatter(x, topk_idx, tile_counts, tile_base, offsets, s->E, s->capacity, s->T,
+                                   s->d_model, s->k, elem_bytes(s), inv_pos, sorted_token, x_perm, st);
 }
 
 inline float* partials_of(void* ws, size_t off, const moe_shape* s) {

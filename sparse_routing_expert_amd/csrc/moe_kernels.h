@@ -48,21 +48,31 @@ void launch_route_bias_update(const int32_t* counts, int64_t T, int E, int k, fl
 
 // ---- permute ----------------------------------------------------------------------------
 constexpr int kPermTile = 1024;  // assignments per histogram / rank tile
+// the scatter forms the offsets and tile bases itself for at most this many experts and tiles
+constexpr int kPermFoldExperts = 64;
+constexpr int kPermFoldTiles = 64;
 // single-block index stage: per-chunk (64 assignments) expert counts held in LDS
 constexpr int kPermSmallCounts = 16384;
 // A <= 16 waves x 4 chunks x 64 = 4096. Measured beyond that, the one block is slower than the tiled
 // kernels (A = 16384: 62.9 against 56.4 us for the permute; A = 8192: even)
 constexpr int kPermSmallChunksPerWave = 4;
+// Tiled index path: perm_local (tile counts, in-tile ranks into inv_pos), then perm_scan unless
+// perm_fold_ok (tile_base == nullptr: the scatter forms offsets and bases itself), then the placing
+// scatter (inv_pos, sorted_token, x_perm; offsets when folded).
+void launch_perm_local(const int32_t* topk_idx, int64_t A, int E, int32_t* tile_counts, int32_t* local_rank,
+                       hipStream_t s);
+bool perm_fold_ok(int64_t A, int E, int k);
+void launch_perm_place_scatter(const void* x, const int32_t* topk_idx, const int32_t* tile_counts,
+                               const int32_t* tile_base, int32_t* offsets, int E, int capacity, int64_t T, int d,
+                               int k, int elem_bytes, int32_t* inv_pos, int32_t* sorted_token, void* x_perm,
+                               hipStream_t s);
 bool perm_index_small_ok(int64_t A, int E);
 void launch_perm_index_small(const int32_t* topk_idx, int64_t A, int E, int k, int capacity, int32_t* offsets,
                              int32_t* inv_pos, int32_t* sorted_token, hipStream_t s);
 
-void launch_perm_count(const int32_t* topk_idx, int64_t A, int E, int32_t* tile_counts, hipStream_t s);
 // capacity: rows each expert keeps (0 = all); dropped assignments get inv_pos = -1
 void launch_perm_scan(const int32_t* tile_counts, int ntiles, int64_t A, int E, int capacity, int32_t* tile_base,
                       int32_t* offsets, hipStream_t s);
-void launch_perm_rank(const int32_t* topk_idx, const int32_t* tile_base, const int32_t* offsets, int64_t A, int E,
-                      int k, int capacity, int32_t* inv_pos, int32_t* sorted_token, hipStream_t s);
 void launch_perm_scatter(const void* x, const int32_t* inv_pos, int64_t T, int d, int k, int elem_bytes,
                          void* x_perm, hipStream_t s);
 

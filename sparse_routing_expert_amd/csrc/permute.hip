@@ -3,31 +3,18 @@
 // What Most Articles Miss 2), each expert's rows in ascending token order -- the order of the
 // per-expert nonzero() in "Fine-tuning and serving MoE models", How an MoE layer actually works.
 //
-// Assignments a = t*k + j are cut into tiles of kPermTile. perm_count builds one LDS-atomic
-// histogram per tile (integer atomics: exact and order-independent); perm_scan turns the
-// [tile][expert] counts into expert offsets and per-tile rank bases; perm_rank ranks every
-// assignment inside its tile with wave ballots (stable, no atomics) and, with an expert capacity,
-// drops the ones ranked at or past it ("Router Optimization Techniques", Why It Matters 3 and
-// FAQ 6); perm_scatter reads each token row once and writes its kept copies with 128-bit stores.
+// Assignments a = t*k + j are cut into tiles of kPermTile. perm_local ranks every assignment inside
+// its tile with wave ballots (stable, no atomics) and writes the tile's per-expert counts;
+// perm_scan turns the [tile][expert] counts into expert offsets and per-tile rank bases (small
+// routers skip it: the scatter forms both from the counts); perm_place_scatter gives each
+// assignment its row, drops the ones ranked at or past an expert capacity ("Router Optimization
+// Techniques", Why It Matters 3 and FAQ 6), and reads each token row once to write its kept copies
+// with 128-bit stores. Batches of at most 4096 assignments take one block for the whole index stage
+// (perm_index_small) and the plain scatter.
 #include "moe_common.h"
 #include "moe_kernels.h"
 
 namespace moe {
-
-__global__ __launch_bounds__(256) void perm_count_kernel(const int32_t* __restrict__ idx, int64_t A, int E,
-                                                         int32_t* __restrict__ tile_counts) {
-    __shared__ int h[1024];
-    for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
-    __syncthreads();
-    const int64_t a0 = (int64_t)blockIdx.x * kPermTile;
-#pragma unroll
-    for (int it = 0; it < kPermTile / 256; ++it) {
-        const int64_t a = a0 + it * 256 + threadIdx.x;
-        if (a < A) atomicAdd(&h[idx[a]], 1);
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < E; e += 256) tile_counts[(int64_t)blockIdx.x * E + e] = h[e];
-}
 
 // One block of 1024 threads: J = 1024 / Ep threads per expert (Ep = E rounded up to a power of two),
 // thread (e, j) owning the contiguous tile range [j * C, (j + 1) * C), C = ceil(ntiles / J). Each
@@ -87,18 +74,45 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restri
     }
 }
 
-// Stable rank of each assignment within its tile. The tile is processed as 16 chunks of 64
-// consecutive assignments (chunk c = iteration * 4 + wave). Inside a chunk, lanes holding the
-// same expert are found by intersecting ballots over the bits of the expert id; the lane's rank
-// among them is the popcount below it. Chunk counts go to LDS, so the expert-local rank is
-// tile_base[e] + sum of counts of e in earlier chunks + rank, and the row is offsets[e] + that
-// rank -- unless a capacity is set and the rank reaches it: then the assignment is dropped.
-__global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restrict__ idx,
-                                                        const int32_t* __restrict__ tile_base,
-                                                        const int32_t* __restrict__ offsets, int64_t A,
-                                                        int E, int k, int nbits, int capacity,
-                                                        int32_t* __restrict__ inv_pos,
-                                                        int32_t* __restrict__ sorted_token) {
+// One wave per token: read the row once, store it at its k destinations (16-byte vectors, up to
+// 8 per lane loaded before any store so a row is one memory round trip); dropped slots (-1) are
+// skipped. Loads and stores are non-temporal: each byte is touched once here.
+__global__ __launch_bounds__(256) void perm_scatter_kernel(const uint8_t* __restrict__ x,
+                                                           const int32_t* __restrict__ inv_pos, int64_t T,
+                                                           int row_bytes, int k, uint8_t* __restrict__ x_perm) {
+    constexpr int U = 8;
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    const int mypos = lane < k ? inv_pos[t * k + lane] : 0;
+    const int nchunks = row_bytes / 16;
+    const uint8_t* src = x + t * row_bytes;
+    for (int c0 = lane; c0 < nchunks; c0 += 64 * U) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (c0 + 64 * u < nchunks) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)(c0 + 64 * u) * 16));
+        for (int j = 0; j < k; ++j) {
+            const int p = __builtin_amdgcn_readlane(mypos, j);
+            if (p < 0) continue;
+            uint8_t* dst = x_perm + (int64_t)p * row_bytes;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (c0 + 64 * u < nchunks)
+                    __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(dst + (int64_t)(c0 + 64 * u) * 16));
+        }
+    }
+}
+
+// Tile histogram and stable in-tile ranks in one pass. The tile is processed as 16 chunks of 64
+// consecutive assignments (chunk c = iteration * 4 + wave). Inside a chunk, lanes holding the same
+// expert are found by intersecting ballots over the bits of the expert id; the lane's rank among them
+// is the popcount below it, and the chunk's count per expert goes to LDS. An assignment's in-tile rank
+// (earlier assignments of the tile to the same expert) goes to local_rank[a], the tile's per-expert
+// totals to tile_counts. perm_place_scatter_kernel turns the rank into the row.
+__global__ __launch_bounds__(256) void perm_local_kernel(const int32_t* __restrict__ idx, int64_t A, int E,
+                                                         int nbits, int32_t* __restrict__ tile_counts,
+                                                         int32_t* __restrict__ local_rank) {
     constexpr int ITERS = kPermTile / 256;
     constexpr int CHUNKS = kPermTile / 64;
     extern __shared__ int cnt[];  // [CHUNKS][E]
@@ -111,8 +125,11 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restric
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
         const int64_t a = a0 + it * 256 + threadIdx.x;
-        const bool valid = a < A;
-        const int e = valid ? idx[a] : E;  // E never equals a real expert id
+        ev[it] = a < A ? idx[a] : E;  // E never equals a real expert id
+    }
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+        const int e = ev[it];
         uint64_t m = ~0ull;
         for (int b = 0; b < nbits; ++b) {
             const int bit = (e >> b) & 1;
@@ -120,9 +137,8 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restric
             m &= bit ? bb : ~bb;
         }
         const int rk = __popcll(m & below);
-        if (valid && rk == 0) cnt[(it * 4 + wave) * E + e] = __popcll(m);
+        if (e < E && rk == 0) cnt[(it * 4 + wave) * E + e] = __popcll(m);
         rank[it] = rk;
-        ev[it] = e;
     }
     __syncthreads();
 #pragma unroll
@@ -131,29 +147,80 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restric
         if (a >= A) continue;
         const int e = ev[it];
         const int c = it * 4 + wave;
-        int r = tile_base[(int64_t)blockIdx.x * E + e] + rank[it];
+        int r = rank[it];
         for (int c2 = 0; c2 < c; ++c2) r += cnt[c2 * E + e];
-        if (capacity > 0 && r >= capacity) {
-            inv_pos[a] = -1;
-            continue;
-        }
-        const int pos = offsets[e] + r;
-        inv_pos[a] = pos;
-        sorted_token[pos] = (int32_t)(a / k);
+        local_rank[a] = r;
+    }
+    for (int e = threadIdx.x; e < E; e += 256) {
+        int sum = 0;
+#pragma unroll
+        for (int c = 0; c < CHUNKS; ++c) sum += cnt[c * E + e];
+        tile_counts[(int64_t)blockIdx.x * E + e] = sum;
     }
 }
 
-// One wave per token: read the row once, store it at its k destinations (16-byte vectors, up to
-// 8 per lane loaded before any store so a row is one memory round trip); dropped slots (-1) are
-// skipped. Loads and stores are non-temporal: each byte is touched once here.
-__global__ __launch_bounds__(256) void perm_scatter_kernel(const uint8_t* __restrict__ x,
-                                                           const int32_t* __restrict__ inv_pos, int64_t T,
-                                                           int row_bytes, int k, uint8_t* __restrict__ x_perm) {
+// perm_scatter_kernel that first places its token's assignments: row = offsets[e] + (assignments to e
+// in earlier tiles) + in-tile rank, or dropped (-1) at or past the capacity; it writes inv_pos (over
+// the in-tile rank it held) and sorted_token, then copies the row. FOLD (E <= kPermFoldExperts and at
+// most kPermFoldTiles tiles): the block forms the expert offsets and its tiles' bases itself from the
+// tile counts, so no scan launch runs, and block 0 writes offsets. Otherwise perm_scan_kernel's
+// tile_base and offsets are read.
+template <bool FOLD>
+__global__ __launch_bounds__(256) void perm_place_scatter_kernel(
+    const uint8_t* __restrict__ x, const int32_t* __restrict__ idx, const int32_t* __restrict__ tile_counts,
+    const int32_t* __restrict__ tile_base, int32_t* __restrict__ offsets, int ntiles, int E, int capacity, int64_t T,
+    int row_bytes, int k, int32_t* __restrict__ inv_pos, int32_t* __restrict__ sorted_token,
+    uint8_t* __restrict__ x_perm) {
     constexpr int U = 8;
+    __shared__ int s_kept[FOLD ? kPermFoldExperts : 1];
+    __shared__ int s_off[FOLD ? kPermFoldExperts : 1];
+    __shared__ int s_pre[2][FOLD ? kPermFoldExperts : 1];
     const int lane = lane_id(), wave = threadIdx.x >> 6;
+    // the block's 4 k assignments span at most two tiles (4 k <= kPermTile)
+    const int64_t tile_lo = (int64_t)blockIdx.x * 4 * k / kPermTile;
+    if (FOLD) {
+        const int e = threadIdx.x;
+        if (e < E) {
+            int tot = 0, pre = 0, at_lo = 0;
+            for (int t0 = 0; t0 < ntiles; t0 += 8) {  // 8 loads in flight
+                int c[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) c[u] = t0 + u < ntiles ? tile_counts[(t0 + u) * E + e] : 0;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    pre += t0 + u < tile_lo ? c[u] : 0;
+                    at_lo = t0 + u == tile_lo ? c[u] : at_lo;
+                    tot += c[u];
+                }
+            }
+            s_pre[0][e] = pre;
+            s_pre[1][e] = pre + at_lo;
+            s_kept[e] = capacity > 0 && tot > capacity ? capacity : tot;
+        }
+        __syncthreads();
+        if (e < E) {
+            int o = 0;
+            for (int e2 = 0; e2 < e; ++e2) o += s_kept[e2];
+            s_off[e] = o;
+            if (blockIdx.x == 0) {
+                offsets[e] = o;
+                if (e == E - 1) offsets[E] = o + s_kept[e];
+            }
+        }
+        __syncthreads();
+    }
     const int64_t t = (int64_t)blockIdx.x * 4 + wave;
     if (t >= T) return;
-    const int mypos = lane < k ? inv_pos[t * k + lane] : 0;
+    int mypos = 0;
+    if (lane < k) {
+        const int64_t a = t * k + lane;
+        const int e = idx[a];
+        const int64_t tile = a / kPermTile;
+        const int r = (FOLD ? s_pre[tile - tile_lo][e] : tile_base[tile * E + e]) + inv_pos[a];
+        mypos = capacity > 0 && r >= capacity ? -1 : (FOLD ? s_off[e] : offsets[e]) + r;
+        inv_pos[a] = mypos;
+        if (mypos >= 0) sorted_token[mypos] = (int32_t)t;
+    }
     const int nchunks = row_bytes / 16;
     const uint8_t* src = x + t * row_bytes;
     for (int c0 = lane; c0 < nchunks; c0 += 64 * U) {
@@ -294,11 +361,6 @@ void launch_perm_index_small(const int32_t* topk_idx, int64_t A, int E, int k, i
                                                  sorted_token);
 }
 
-void launch_perm_count(const int32_t* topk_idx, int64_t A, int E, int32_t* tile_counts, hipStream_t s) {
-    const unsigned ntiles = (unsigned)((A + kPermTile - 1) / kPermTile);
-    perm_count_kernel<<<ntiles, 256, 0, s>>>(topk_idx, A, E, tile_counts);
-}
-
 void launch_perm_scan(const int32_t* tile_counts, int ntiles, int64_t A, int E, int capacity, int32_t* tile_base,
                       int32_t* offsets, hipStream_t s) {
     (void)A;
@@ -307,21 +369,41 @@ void launch_perm_scan(const int32_t* tile_counts, int ntiles, int64_t A, int E, 
     perm_scan_kernel<<<1, 1024, 0, s>>>(tile_counts, ntiles, E, Ep, capacity, tile_base, offsets);
 }
 
-void launch_perm_rank(const int32_t* topk_idx, const int32_t* tile_base, const int32_t* offsets, int64_t A, int E,
-                      int k, int capacity, int32_t* inv_pos, int32_t* sorted_token, hipStream_t s) {
-    const unsigned ntiles = (unsigned)((A + kPermTile - 1) / kPermTile);
-    int nbits = 0;
-    while ((1 << nbits) <= E) ++nbits;  // ids 0..E (E = padding sentinel) fit in nbits bits
-    const size_t lds = (size_t)(kPermTile / 64) * E * sizeof(int);
-    perm_rank_kernel<<<ntiles, 256, lds, s>>>(topk_idx, tile_base, offsets, A, E, k, nbits, capacity, inv_pos,
-                                              sorted_token);
-}
-
 void launch_perm_scatter(const void* x, const int32_t* inv_pos, int64_t T, int d, int k, int elem_bytes,
                          void* x_perm, hipStream_t s) {
     const unsigned nblk = (unsigned)((T + 3) / 4);
     perm_scatter_kernel<<<nblk, 256, 0, s>>>(static_cast<const uint8_t*>(x), inv_pos, T, d * elem_bytes, k,
                                              static_cast<uint8_t*>(x_perm));
+}
+
+void launch_perm_local(const int32_t* topk_idx, int64_t A, int E, int32_t* tile_counts, int32_t* local_rank,
+                       hipStream_t s) {
+    const unsigned ntiles = (unsigned)((A + kPermTile - 1) / kPermTile);
+    int nbits = 0;
+    while ((1 << nbits) <= E) ++nbits;  // ids 0..E (E = padding sentinel) fit in nbits bits
+    const size_t lds = (size_t)(kPermTile / 64) * E * sizeof(int);
+    perm_local_kernel<<<ntiles, 256, lds, s>>>(topk_idx, A, E, nbits, tile_counts, local_rank);
+}
+
+bool perm_fold_ok(int64_t A, int E, int k) {
+    return E <= kPermFoldExperts && (A + kPermTile - 1) / kPermTile <= kPermFoldTiles && 4 * k <= kPermTile;
+}
+
+void launch_perm_place_scatter(const void* x, const int32_t* topk_idx, const int32_t* tile_counts,
+                               const int32_t* tile_base, int32_t* offsets, int E, int capacity, int64_t T, int d,
+                               int k, int elem_bytes, int32_t* inv_pos, int32_t* sorted_token, void* x_perm,
+                               hipStream_t s) {
+    const unsigned nblk = (unsigned)((T + 3) / 4);
+    const int ntiles = (int)((T * k + kPermTile - 1) / kPermTile);
+    const auto xb = static_cast<const uint8_t*>(x);
+    const auto xp = static_cast<uint8_t*>(x_perm);
+    if (tile_base == nullptr)
+        perm_place_scatter_kernel<true><<<nblk, 256, 0, s>>>(xb, topk_idx, tile_counts, nullptr, offsets, ntiles, E,
+                                                             capacity, T, d * elem_bytes, k, inv_pos, sorted_token, xp);
+    else
+        perm_place_scatter_kernel<false><<<nblk, 256, 0, s>>>(xb, topk_idx, nullptr, tile_base, offsets, ntiles, E,
+                                                              capacity, T, d * elem_bytes, k, inv_pos, sorted_token,
+                                                              xp);
 }
 
 }  // namespace moe

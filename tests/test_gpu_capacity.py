@@ -26,6 +26,10 @@ CASES = {
     "deepseek_mini_c1.0": (I.mini("deepseek_v3", T=500, d=448, F=128, Fs=192), 1.0),
     "tiny_fp32_c0.5": (I.CONFIGS["tiny_fp32"], 0.5),
     "small_c8_keeps_all": (I.mini("small_bf16", T=1000, d=256, F=320), 8.0),
+    # more than 4096 assignments over at most 64 experts: the tiled ranks with the offsets and tile
+    # bases formed inside the scatter, over several tiles and a ragged last one
+    "mixtral_T5000_c1.0": (I.mini("mixtral_prefill", T=5000, d=256, F=128), 1.0),
+    "small_T3001_c0.75": (I.mini("small_bf16", T=3001, d=256, F=128), 0.75),
 }
 
 

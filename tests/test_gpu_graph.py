@@ -13,6 +13,7 @@ CASES = {
     "mixtral_decode_mini": I.mini("mixtral_prefill", T=64, d=512, F=448),
     "deepseek_mini": I.mini("deepseek_v3", T=500, d=448, F=128, Fs=192),
     "qwen_mini": I.mini("qwen3_30b_a3b", T=2000, d=256, F=192),
+    "mixtral_T5000": I.mini("mixtral_prefill", T=5000, d=256, F=128),
 }
 
 
