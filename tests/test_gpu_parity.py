@@ -51,6 +51,11 @@ CASES = {
     "split_last_round_up": I.mini("small_bf16", T=1000, d=512, F=8448, E=1, k=1),
     # ... and 65 x 4 = 260 down-projection tiles
     "split_last_round_down": I.mini("small_bf16", T=16640, d=1024, F=128, E=1, k=1),
+    # tiled permute: offsets formed inside the scatter up to 64 experts and 64 tiles of 1024
+    # assignments, a separate scan past either limit
+    "perm_fold_E64": I.mini("qwen3_30b_a3b", T=2600, d=128, F=64, E=64, k=2),
+    "perm_fold_64tiles": I.mini("small_bf16", T=32768, d=64, F=64, k=2),
+    "perm_scan_65tiles": I.mini("small_bf16", T=32769, d=64, F=64, k=2),
 }
 
 
