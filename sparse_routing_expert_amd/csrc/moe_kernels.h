@@ -54,7 +54,8 @@ constexpr int kPermFoldTiles = 64;
 // single-block index stage: per-chunk (64 assignments) expert counts held in LDS
 constexpr int kPermSmallCounts = 16384;
 // A <= 16 waves x 4 chunks x 64 = 4096. Measured beyond that, the one block is slower than the tiled
-// kernels (A = 16384: 62.9 against 56.4 us for the permute; A = 8192: even)
+// kernels (A = 16384: 62.9 us for the permute, against 56.4 us for the four-launch tiled path of the
+// time and 47 us for the two-launch one; A = 8192: even with the four-launch path)
 constexpr int kPermSmallChunksPerWave = 4;
 // Tiled index path: perm_local (tile counts, in-tile ranks into inv_pos), then perm_scan unless
 // perm_fold_ok (tile_base == nullptr: the scatter forms offsets and bases itself), then the placing
