@@ -57,6 +57,9 @@ constexpr int kPermSmallCounts = 16384;
 // kernels (A = 16384: 62.9 us for the permute, against 56.4 us for the four-launch tiled path of the
 // time and 47 us for the two-launch one; A = 8192: even with the four-launch path)
 constexpr int kPermSmallChunksPerWave = 4;
+// with at most kPermFoldExperts experts the single block is used up to this many assignments
+// (measured cold: A = 2048, 13.9 against 14.3 us for the tiled path; A = 4096, 19.8 against 17.8 us)
+constexpr int kPermSmallFoldMax = 2048;
 // Tiled index path: perm_local (tile counts, in-tile ranks into inv_pos), then perm_scan unless
 // perm_fold_ok (tile_base == nullptr: the scatter forms offsets and bases itself), then the placing
 // scatter (inv_pos, sorted_token, x_perm; offsets when folded).

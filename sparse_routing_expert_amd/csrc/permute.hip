@@ -347,7 +347,10 @@ __global__ __launch_bounds__(1024) void perm_index_small_kernel(const int32_t* _
 }
 
 bool perm_index_small_ok(int64_t A, int E) {
-    return A > 0 && A <= (int64_t)16 * 64 * kPermSmallChunksPerWave && (A + 63) / 64 * E <= kPermSmallCounts;
+    // where the tiled path folds its scan into the scatter (two launches, like this one) it is the
+    // faster of the two past 2048 assignments
+    const int64_t amax = E <= kPermFoldExperts ? kPermSmallFoldMax : (int64_t)16 * 64 * kPermSmallChunksPerWave;
+    return A > 0 && A <= amax && (A + 63) / 64 * E <= kPermSmallCounts;
 }
 
 void launch_perm_index_small(const int32_t* topk_idx, int64_t A, int E, int k, int capacity, int32_t* offsets,
