@@ -21,6 +21,7 @@ CASES = {
     # block, and a token count past the one where the plain router switches to two token tiles a block
     "small_mini": I.mini("small_bf16", T=1234, d=512, F=256),
     "mixtral_T9000": I.mini("mixtral_prefill", T=9000, d=256, F=128),
+    "qwen_T8192": I.mini("qwen3_30b_a3b", T=8192, d=128, F=64),
     "qwen_mini": I.mini("qwen3_30b_a3b", T=2000, d=256, F=192),
     "deepseek_mini": I.mini("deepseek_v3", T=500, d=448, F=128, Fs=192),
 }

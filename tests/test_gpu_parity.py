@@ -56,6 +56,11 @@ CASES = {
     "perm_fold_E64": I.mini("qwen3_30b_a3b", T=2600, d=128, F=64, E=64, k=2),
     "perm_fold_64tiles": I.mini("small_bf16", T=32768, d=64, F=64, k=2),
     "perm_scan_65tiles": I.mini("small_bf16", T=32769, d=64, F=64, k=2),
+    # routers wider than 16 experts select one token per 16-lane row from 8192 tokens on: the logits
+    # kernel path (40 experts, ragged last block), the router GEMM (128), sigmoid with a bias (256)
+    "rowsel_E40_T8200": I.mini("small_bf16", T=8200, d=128, F=64, E=40, k=4),
+    "rowsel_E128_T8192": I.mini("qwen3_30b_a3b", T=8192, d=128, F=64),
+    "rowsel_E256_T8192": I.mini("deepseek_v3", T=8192, d=128, F=64, Fs=64),
 }
 
 
