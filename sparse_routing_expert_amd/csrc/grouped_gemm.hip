@@ -1354,10 +1354,12 @@ void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* 
                                              n_out, K, s);
             return;
         }
-        // expert groups averaging at least kGemmWideRows rows take the four-wave wide-K kernel;
-        // smaller groups and dense products keep the eight-wave kernel, whose deeper ring streams
-        // weights better
-        if (offsets != nullptr && max_rows >= kGemmWideRows * (int64_t)(n_groups > 0 ? n_groups : 1))
+        // expert groups averaging at least kGemmWideRows rows (kGemmWideRowsLongK over a K of at least
+        // kGemmWideMinK) take the four-wave wide-K kernel; smaller groups and dense products keep the
+        // eight-wave kernel, whose deeper ring streams weights better
+        const int64_t ng = n_groups > 0 ? n_groups : 1;
+        if (offsets != nullptr &&
+            (max_rows >= kGemmWideRows * ng || (K >= kGemmWideMinK && max_rows >= kGemmWideRowsLongK * ng)))
             launch_bf16_wide<8>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows, n_out, K,
                                 partials, s);
         else

@@ -163,8 +163,13 @@ void launch_bwd_gate(const float* logits, const int32_t* topk_idx, const float* 
 constexpr int kRouterChunk = 256;
 // bf16 grouped GEMM: expert groups averaging at least this many rows use the four-wave wide-K
 // persistent kernel (measured: Mixtral-shaped projections, 2048 rows per expert, 2-3 % faster; groups
-// of 128 to 1024 rows and a dense 4096-row product slower than on the eight-wave kernel)
+// of 128 to 1024 rows and a dense 4096-row product slower than on the eight-wave kernel) ...
 constexpr int64_t kGemmWideRows = 2048;
+// ... and so do groups averaging at least kGemmWideRowsLongK rows over a K of at least kGemmWideMinK
+// (measured: Qwen3-shaped gate/up, 1024 rows per expert and K = 2048, 0.913 against 0.952 ms; its
+// down projection, K = 768, and the small layer's, K = 1024, are faster on the eight-wave kernel)
+constexpr int64_t kGemmWideRowsLongK = 1024;
+constexpr int kGemmWideMinK = 2048;
 constexpr int kRouterWgradExperts = 32;  // experts per dW_r block (x read once per 32 experts)
 constexpr int kRouterDgradTokens = 16;   // tokens per dx block (W_r read once per 16 tokens)
 size_t bwd_router_partials_bytes(int64_t T, int E, int d);
