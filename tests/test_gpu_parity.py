@@ -63,6 +63,8 @@ CASES = {
     "rowsel_E256_T8192": I.mini("deepseek_v3", T=8192, d=128, F=64, Fs=64),
     # groups averaging 1024 rows over K = 2048 take the wide-K kernel for gate/up (16 skewed experts)
     "wide_longK_E16": I.mini("qwen3_30b_a3b", T=2048, d=2048, F=64, E=16, k=8),
+    # the shared expert and the router GEMM as dense products over K = 2048 with a ragged last row tile
+    "dense_longK_shared": I.mini("deepseek_v3", T=1100, d=2048, F=64, Fs=128),
 }
 
 
