@@ -414,6 +414,64 @@ def check_noisy_limits(ref):
     assert r.idx.tolist() == [[1]] and abs(r.logits[0, 1] - (1.0 + 0.5 * math.log(2.0))) < 1e-15
 
 
+# ------------------------------------------------------------------ sampled-token layer and the error measure
+
+
+def check_tokens_forward(ref, seeds=range(16)):
+    """tokens_forward on a subset of rows (any order, repeats allowed) equals the brute-force layer's
+    rows when given the brute force's own selection and gates; with arbitrary gates it equals the
+    gate-weighted sum of the selected experts' outputs plus the shared expert, token by token
+    ([VI] Eq. (moe-output); [FS] How an MoE layer actually works)."""
+    for s in seeds:
+        rng = np.random.default_rng(900 + s)
+        c = tiny_case(900 + s, T=7, shared=bool(s % 2), renorm=bool(s % 3))
+        b_idx, b_g, _, b_y = run_brute(c)
+        rows = rng.choice(c["T"], size=5, replace=True)
+        get = ref.stacked_experts(c["w_in"], c["b_in"], c["w_out"], c["b_out"])
+        idx = np.array(b_idx, dtype=np.int64)
+        g = np.array(b_g, dtype=np.float64)
+        got = ref.tokens_forward(c["x"][rows], idx[rows], g[rows], get, c["act"], c["ws_in"], c["ws_out"])
+        _close(got, np.array(b_y)[rows], 1e-10, f"tokens_forward seed {s}")
+        # arbitrary gates (not a softmax of anything), so each slot's own gate must scale its own expert
+        g2 = rng.standard_normal(idx.shape)
+        got2 = ref.tokens_forward(c["x"][rows], idx[rows], g2[rows], get, c["act"], c["ws_in"], c["ws_out"])
+        want2 = []
+        for t in rows:
+            xt = c["x"][t].tolist()
+            acc = [0.0] * c["d"]
+            for j, e in enumerate(idx[t]):
+                out = brute.expert(xt, _L(c["w_in"][e]), None if c["b_in"] is None else _L(c["b_in"][e]),
+                                   _L(c["w_out"][e]), None if c["b_out"] is None else _L(c["b_out"][e]), c["act"])
+                acc = [a + g2[t, j] * o for a, o in zip(acc, out)]
+            if c["ws_in"] is not None:
+                sh = brute.expert(xt, _L(c["ws_in"]), None, _L(c["ws_out"]), None, "swiglu")
+                acc = [a + v for a, v in zip(acc, sh)]
+            want2.append(acc)
+        _close(got2, want2, 1e-10, f"tokens_forward arbitrary gates seed {s}")
+
+
+def check_rel_l2(ref):
+    """Per-row relative L2 with the floor 1e-6 x (rms row norm of the reference), on values worked
+    out by hand: reference rows of norms 0, 2, 2, 2*sqrt(2) (rms 2, so the floor is 2e-6)."""
+    r = np.array([[0.0, 0.0], [2.0, 0.0], [0.0, 2.0], [2.0, 2.0]])
+    a = np.array([[1e-6, 0.0], [2.0, 0.0], [0.0, 3.0], [2.3, 2.4]])
+    got = ref.rel_l2_per_row(a, r)
+    want = np.array([0.5, 0.0, 0.5, math.sqrt(2.0) / 8.0])  # 1e-6/2e-6, 0, 1/2, 0.5/(2 sqrt 2)
+    assert got.shape == (4,), got.shape
+    assert np.allclose(got, want, rtol=1e-12, atol=0), (got, want)
+    # scale-free: both sides times 1000 give the same errors
+    assert np.allclose(ref.rel_l2_per_row(1e3 * a, 1e3 * r), want, rtol=1e-12, atol=0)
+    # equal inputs give exactly zero, including an all-zero reference
+    assert (ref.rel_l2_per_row(r, r) == 0).all()
+    assert (ref.rel_l2_per_row(np.zeros((3, 5)), np.zeros((3, 5))) == 0).all()
+    # a wide row: one element off by 0.01 over a row of norm 1 is 1e-2
+    w = np.zeros((1, 64))
+    w[0, 7] = 1.0
+    w2 = w.copy()
+    w2[0, 40] = 0.01
+    assert abs(ref.rel_l2_per_row(w2, w)[0] - 1e-2) < 1e-15
+
+
 ALL_CHECKS = [
     ("brute", lambda ref, pv: check_against_brute(ref)),
     ("permute_brute", lambda ref, pv: check_permute_brute(ref)),
@@ -434,4 +492,6 @@ ALL_CHECKS = [
     ("bias_update", lambda ref, pv: check_bias_update(ref)),
     ("noisy_brute", lambda ref, pv: check_noisy_brute(ref)),
     ("noisy_limits", lambda ref, pv: check_noisy_limits(ref)),
+    ("tokens_forward", lambda ref, pv: check_tokens_forward(ref)),
+    ("rel_l2", lambda ref, pv: check_rel_l2(ref)),
 ]

@@ -224,6 +224,59 @@ def _mut_softplus_as_exp(m):
     return lambda z: np.exp(z)
 
 
+def _mut_tokens_gate_of_slot0(m):
+    """Every slot weighted by the gate of slot 0."""
+    orig = m.tokens_forward
+    return lambda x_rows, idx_rows, gates_rows, get_expert, act, ws_in=None, ws_out=None: orig(
+        x_rows, idx_rows, np.repeat(np.asarray(gates_rows)[:, :1], gates_rows.shape[1], axis=1), get_expert, act,
+        ws_in, ws_out)
+
+
+def _mut_tokens_gates_reversed(m):
+    """Slot j weighted by the gate of slot k-1-j."""
+    orig = m.tokens_forward
+    return lambda x_rows, idx_rows, gates_rows, get_expert, act, ws_in=None, ws_out=None: orig(
+        x_rows, idx_rows, np.asarray(gates_rows)[:, ::-1].copy(), get_expert, act, ws_in, ws_out)
+
+
+def _mut_tokens_shared_twice(m):
+    orig = m.tokens_forward
+
+    def tf(x_rows, idx_rows, gates_rows, get_expert, act, ws_in=None, ws_out=None):
+        y = orig(x_rows, idx_rows, gates_rows, get_expert, act, ws_in, ws_out)
+        if ws_in is not None:
+            y = y + m.shared_ffn(m.f64(x_rows), m.f64(ws_in), m.f64(ws_out))
+        return y
+    return tf
+
+
+def _mut_rel_l2_axis0(m):
+    def rel(a, ref):
+        a, ref = m.f64(a), m.f64(ref)
+        num = np.linalg.norm(a - ref, axis=0)
+        den = np.linalg.norm(ref, axis=0)
+        floor = 1e-6 * math.sqrt(float(np.mean(den ** 2))) if den.size else 0.0
+        return num / np.maximum(den, max(floor, 1e-300))
+    return rel
+
+
+def _mut_rel_l2_big_floor(m):
+    def rel(a, ref):
+        a, ref = m.f64(a), m.f64(ref)
+        num = np.linalg.norm(a - ref, axis=1)
+        den = np.linalg.norm(ref, axis=1)
+        floor = 1e-2 * math.sqrt(float(np.mean(den ** 2))) if den.size else 0.0
+        return num / np.maximum(den, max(floor, 1e-300))
+    return rel
+
+
+def _mut_rel_l2_over_result(m):
+    """Denominator taken from the compared values instead of the reference."""
+    orig = m.rel_l2_per_row
+    return lambda a, ref: orig(a, ref) * np.linalg.norm(m.f64(ref), axis=1) / np.maximum(
+        np.linalg.norm(m.f64(a), axis=1), 1e-300)
+
+
 def _install_keeps_last(m):
     m._orig_permute = m.permute
     m.permute = _mut_capacity_keeps_last(m)
@@ -255,6 +308,12 @@ MUTANTS = {
     "bias_target_per_token": lambda m: setattr(m, "update_bias", _mut_bias_target_per_token(m)),
     "noise_unscaled": lambda m: setattr(m, "noisy_logits", _mut_noise_unscaled(m)),
     "softplus_as_exp": lambda m: setattr(m, "softplus", _mut_softplus_as_exp(m)),
+    "tokens_gate_of_slot0": lambda m: setattr(m, "tokens_forward", _mut_tokens_gate_of_slot0(m)),
+    "tokens_gates_reversed": lambda m: setattr(m, "tokens_forward", _mut_tokens_gates_reversed(m)),
+    "tokens_shared_twice": lambda m: setattr(m, "tokens_forward", _mut_tokens_shared_twice(m)),
+    "rel_l2_wrong_axis": lambda m: setattr(m, "rel_l2_per_row", _mut_rel_l2_axis0(m)),
+    "rel_l2_floor_swamps": lambda m: setattr(m, "rel_l2_per_row", _mut_rel_l2_big_floor(m)),
+    "rel_l2_over_result": lambda m: setattr(m, "rel_l2_per_row", _mut_rel_l2_over_result(m)),
 }
 
 
