@@ -65,6 +65,20 @@ CASES = {
     "wide_longK_E16": I.mini("qwen3_30b_a3b", T=2048, d=2048, F=64, E=16, k=8),
     # the shared expert and the router GEMM as dense products over K = 2048 with a ragged last row tile
     "dense_longK_shared": I.mini("deepseek_v3", T=1100, d=2048, F=64, Fs=128),
+    # softmax scoring with a selection-only bias (key = logit + bias, gates from the raw logits): the
+    # fused E <= 16 route at the dynamic-bias router's example shape (2048 tokens, d = 4096, 8 experts,
+    # top-2), the logits kernel (40 experts), the router GEMM (128), and the row selection from 8192
+    # tokens on (40 and 128 experts)
+    "softmax_bias_E8_d4096": I.mini("mixtral_prefill", T=2048, d=4096, F=64, router="biased"),
+    "softmax_bias_E40": I.mini("small_bf16", T=555, d=256, F=128, E=40, k=4, router="biased"),
+    "softmax_bias_E128": I.mini("qwen3_30b_a3b", T=999, d=320, F=128, router="biased"),
+    "rowsel_softmax_bias_E40_T8200": I.mini("small_bf16", T=8200, d=128, F=64, E=40, k=4, router="biased"),
+    "rowsel_softmax_bias_E128_T8192": I.mini("qwen3_30b_a3b", T=8192, d=128, F=64, router="biased"),
+    # sigmoid scoring with a bias on the fused E <= 16 route (16 and 32-token blocks)
+    "sigmoid_bias_E8_fused": I.mini("mixtral_prefill", T=1000, d=1024, F=64, router="biased", score="sigmoid"),
+    "sigmoid_bias_E16_fused_T8200": I.mini("small_bf16", T=8200, d=512, F=64, router="biased", score="sigmoid"),
+    # no renormalisation with a bias: gates are the raw full-softmax probabilities of the chosen experts
+    "softmax_bias_norenorm_E16": I.mini("small_bf16", T=700, d=256, F=64, router="biased", renorm=False),
 }
 
 
