@@ -24,7 +24,8 @@
  *            HIP device (except `shape`, which is host memory). The library never
  *            allocates, frees or synchronises and keeps no state between calls;
  *            scratch comes only from the caller's workspace `ws` of `ws_bytes`
- *            bytes, sized by moe_workspace_bytes().
+ *            bytes, sized by moe_workspace_bytes(). The one exception is
+ *            moe_permute_noalloc, whose scratch is a fixed array inside the library.
  * Layout:    row-major everywhere. Weights use the Linear [out, in] layout, so
  *            both operands of every product are contiguous along the reduced
  *            dimension. Expert weights are stacked along a leading expert axis.
@@ -186,6 +187,22 @@ int moe_route_noisy(const moe_shape* shape, const void* x, const float* w_router
 int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, int32_t* offsets,
                 int32_t* sorted_token, int32_t* inv_pos, void* x_perm, void* ws, size_t ws_bytes,
                 moe_stream_t stream);
+
+/* moe_permute_noalloc -- moe_permute with no workspace argument and no allocation.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Same arguments, outputs and errors as moe_permute,
+ * without ws / ws_bytes; the outputs are bit-identical to moe_permute's.
+ * Scratch: a fixed device array of MOE_NOALLOC_SCRATCH_BYTES (4 MiB) inside the library, one per
+ * device, held until the process ends (its device address is looked up on the first call on each
+ * device). A shape whose MOE_STAGE_PERMUTE workspace exceeds it returns MOE_ERR_WORKSPACE, before
+ * any HIP call (the permute needs 8 * E * ceil(T*k / 1024) bytes, rounded up to 256 per region).
+ * Every call on one device shares that array: calls that overlap on one device (other streams,
+ * other host threads) race and must be serialised by the caller. Allocates nothing (no hipMalloc,
+ * hipFree or allocating library call). */
+#define MOE_NOALLOC_SCRATCH_BYTES (4u << 20)
+int moe_permute_noalloc(const moe_shape* shape, const int32_t* topk_idx, const void* x, int32_t* offsets,
+                        int32_t* sorted_token, int32_t* inv_pos, void* x_perm, moe_stream_t stream);
 
 /* moe_grouped_ffn -- every expert's FFN on its contiguous rows, as one grouped GEMM pair.
  *

@@ -19,6 +19,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 MOE_GELU_MLP, MOE_SWIGLU = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
+MOE_NOALLOC_SCRATCH_BYTES = 4 << 20
 (MOE_STAGE_ROUTE, MOE_STAGE_PERMUTE, MOE_STAGE_FFN, MOE_STAGE_SHARED, MOE_STAGE_FORWARD, MOE_STAGE_EXPERT,
  MOE_STAGE_ROUTE_NOISY, MOE_STAGE_BACKWARD) = range(8)
 
@@ -45,6 +46,7 @@ _SIGS = {
     "moe_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(moe_shape), ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
     "moe_route": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_permute": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_permute_noalloc": (ctypes.c_int, [ctypes.POINTER(moe_shape), _P, _P, _P, _P, _P, _P, _P]),
     "moe_grouped_ffn": (ctypes.c_int, [ctypes.POINTER(moe_shape), ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P,
                                        _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_expert_up": (ctypes.c_int, [ctypes.POINTER(moe_shape), ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P,
@@ -151,6 +153,12 @@ def moe_permute(shape, topk_idx, x, offsets, sorted_token, inv_pos, x_perm, ws, 
                                             _stream(stream)))
 
 
+def moe_permute_noalloc(shape, topk_idx, x, offsets, sorted_token, inv_pos, x_perm, stream=None) -> None:
+    _check("moe_permute_noalloc", lib().moe_permute_noalloc(ctypes.byref(shape), _ptr(topk_idx), _ptr(x),
+                                                            _ptr(offsets), _ptr(sorted_token), _ptr(inv_pos),
+                                                            _ptr(x_perm), _stream(stream)))
+
+
 def moe_grouped_ffn(shape, e_begin, e_end, x_perm, offsets, w_in, b_in, w_out, b_out, y_perm, ws, stream=None) -> None:
     _check("moe_grouped_ffn", lib().moe_grouped_ffn(ctypes.byref(shape), int(e_begin), int(e_end), _ptr(x_perm),
                                                     _ptr(offsets), _ptr(w_in), _ptr(b_in), _ptr(w_out), _ptr(b_out),
@@ -210,3 +218,4 @@ def moe_backward(shape, x, w_router, w_in, b_in, w_out, b_out, ws_in, ws_out, lo
         _ptr(x_perm), _ptr(y_perm), _ptr(dy), float(aux_coef), _ptr(dx), _ptr(dw_router), _ptr(dw_in), _ptr(db_in),
         _ptr(dw_out), _ptr(db_out), _ptr(dws_in), _ptr(dws_out), _ptr(dlogits), _ptr(ws), _nbytes(ws),
         _stream(stream)))
+

@@ -178,6 +178,33 @@ def test_permute_combine_rejections(lib):
     assert c(ctypes.byref(good_shape(T=0)), FAKE, FAKE, FAKE, None, FAKE, None) == L.MOE_OK
 
 
+def test_permute_noalloc_rejections(lib):
+    """The no-allocation permute checks everything on the host before any HIP call: pointers, the
+    shape, and that the permute's scratch fits the library's fixed array."""
+    s = good_shape()
+    p = lib.moe_permute_noalloc
+    good = [ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    for i in range(1, 7):
+        bad = list(good)
+        bad[i] = None
+        assert p(*bad) == L.MOE_ERR_INVALID_ARG
+        bad[i] = MISALIGNED
+        assert p(*bad) == L.MOE_ERR_INVALID_ARG
+    assert p(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert p(ctypes.byref(good_shape(k=0)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    # T = 0 is a no-op that touches nothing (so it succeeds here, without a GPU)
+    assert p(ctypes.byref(good_shape(T=0)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.MOE_OK
+    # the largest permute workspace the fixed array holds, and one tile more
+    E, k = 1024, 1
+    per_tile = 2 * E * 4
+    ntiles = L.MOE_NOALLOC_SCRATCH_BYTES // per_tile
+    fits = good_shape(T=ntiles * 1024, E=E, k=k)
+    assert ws_bytes(fits, L.MOE_STAGE_PERMUTE)[1] <= L.MOE_NOALLOC_SCRATCH_BYTES
+    over = good_shape(T=ntiles * 1024 + 1, E=E, k=k)
+    assert ws_bytes(over, L.MOE_STAGE_PERMUTE)[1] > L.MOE_NOALLOC_SCRATCH_BYTES
+    assert p(ctypes.byref(over), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.MOE_ERR_WORKSPACE
+
+
 def test_ffn_rejections(lib):
     s = good_shape()
     n = ws_bytes(s, L.MOE_STAGE_FFN)[1]
