@@ -111,6 +111,7 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     ev_ms = ev0.elapsed_time(ev1) / args.steps
     value = cfg.T / (ms_per_step / 1e3)
+    step_stats = per_step_timings(L, stream, args.steps)
 
     graph = graph_timing(L, args.steps) if args.graph else None
 
@@ -144,6 +145,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     vendor = vendor_gemm(cfg, L, stream) if args.vendor_gemm and cfg.dtype == "bf16" else None
+    probes = peak_probes(dev, stream)
     used = int((L.counts > 0).sum().item())
     work = stage_bytes_flops(cfg, used)
     peak_tf = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_PEAK_TFLOPS
@@ -178,12 +180,15 @@ def main():
             kernel = "gemm_bf16_kernel (expert_up: gate/up grouped GEMM + SwiGLU, 64-row tiles)"
         roofline = {"kernel": kernel, "bound": "hbm", "achieved": up["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": up["frac_hbm"], "traffic": measured_traffic(cfg.name),
-                    "algorithmic_bytes_per_launch": work["expert_up"]["bytes"], "avg_launch_ms": up["ms"]}
+                    "algorithmic_bytes_per_launch": work["expert_up"]["bytes"], "avg_launch_ms": up["ms"],
+                    "frac_of_measured_copy": round(up["GB/s"] / probes["copy"]["GB/s"], 4)}
     else:
         roofline = {"kernel": kernel, "bound": "mfma" if cfg.dtype == "bf16" else "alu", "achieved": up["TFLOP/s"],
                     "peak": peak_tf, "unit": "TFLOP/s", "frac": round(up["TFLOP/s"] / peak_tf, 4),
                     "traffic": measured_traffic(cfg.name) if cfg.dtype == "bf16" else None,
                     "algorithmic_flops_per_launch": work["expert_up"]["flops"], "avg_launch_ms": up["ms"]}
+        if cfg.dtype == "bf16":
+            roofline["frac_of_measured_mfma_loop"] = round(up["TFLOP/s"] / probes["mfma_loop"]["TFLOP/s"], 4)
 
     # ---- CPU oracle on a bounded sample of the same workload ----------------------------------
     cpu = None
@@ -212,6 +217,8 @@ def main():
         "route_GB/s": stages["route"]["GB/s"],
         "assignments_per_s": round(value * cfg.k, 1),
         "event_ms_per_step": round(ev_ms, 4),
+        "step_timing": step_stats,
+        "peaks_measured": probes,
         "graph_replay": graph,
         "vendor_gemm": vendor,
         "capacity_permute": next_rows["capacity_permute"],
@@ -221,6 +228,75 @@ def main():
         "input_gen_s": round(gen_s, 2),
     }
     print(json.dumps(out), flush=True)
+
+
+def per_step_timings(L, stream, steps):
+    """The forward step timed one by one with HIP events on its stream: warm (back to back, as in the
+    headline) and cold (a 1 GiB fill before each step evicts the 256 MiB last-level cache and the L2s,
+    so weights and activations come from HBM); median and minimum of each."""
+    import numpy as np
+    import torch
+
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=L.dev)
+
+    def run(cold):
+        ts = []
+        for _ in range(steps):
+            if cold:
+                flush.fill_(7)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            L.forward()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return {"median_ms": round(float(np.median(ts)), 4), "min_ms": round(float(np.min(ts)), 4),
+                "tokens_per_s_median": round(L.T / (float(np.median(ts)) * 1e-3), 1)}
+
+    out = {"warm": run(False), "cold": run(True), "steps": steps, "flush_bytes": 1 << 30}
+    del flush
+    return out
+
+
+def peak_probes(dev, stream):
+    """What this card reaches right now on a streaming copy (read + write) and on bf16 matrix
+    instructions alone (register operands), next to the published 8 TB/s and 2.5 PFLOP/s."""
+    import numpy as np
+    import torch
+
+    from sparse_routing_expert_amd import _lib as LIB
+
+    def timed(fn, reps=5):
+        fn()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(3)
+    dst = torch.empty_like(src)
+    ms_c = timed(lambda: LIB.moe_probe_copy(src, dst, n, 2048))
+    ms_t = timed(lambda: dst.copy_(src))
+    del src, dst
+    blocks, iters = 1024, 4000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    flops = LIB.moe_probe_mfma(blocks, iters, out)
+    ms_m = timed(lambda: LIB.moe_probe_mfma(blocks, iters, out))
+    del out
+    copy_gbs = 2 * n / (ms_c * 1e-3) / 1e9
+    mfma_tf = flops / (ms_m * 1e-3) / 1e12
+    return {"copy": {"kernel": "moe_probe_copy (64 KB chunks per block, 16 loads then 16 stores per lane, non-temporal)", "bytes_moved": 2 * n,
+                     "ms": round(ms_c, 4), "GB/s": round(copy_gbs, 1), "frac_of_published": round(copy_gbs / HBM_PEAK_GBS, 4),
+                     "torch_copy_GB/s": round(2 * n / (ms_t * 1e-3) / 1e9, 1)},
+            "mfma_loop": {"kernel": "moe_probe_mfma (v_mfma_f32_32x32x16_bf16 on registers)", "flops": flops,
+                          "ms": round(ms_m, 4), "TFLOP/s": round(mfma_tf, 1),
+                          "frac_of_published": round(mfma_tf / BF16_PEAK_TFLOPS, 4)}}
 
 
 def graph_timing(L, steps):
@@ -381,9 +457,18 @@ def cpu_baseline(cfg, L, n_tokens: int):
     try:
         from threadpoolctl import threadpool_info
 
-        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
-        cores = 1
+        threads = 1
+    allowed = len(os.sched_getaffinity(0))
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     if n_tokens <= 0:  # about 10-30 s of CPU work on a many-core host
         per_tok = 6.0 * cfg.k * cfg.d * cfg.F + 2.0 * cfg.E * cfg.d + (6.0 * cfg.d * cfg.Fs if cfg.Fs else 0)
         n_tokens = int(max(16, min(cfg.T, 1e13 / per_tok)))
@@ -396,7 +481,8 @@ def cpu_baseline(cfg, L, n_tokens: int):
                           t["ws_out"])
     dt = time.perf_counter() - t0
     assert np.isfinite(res.y).all()
-    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": min(threads, allowed), "kind": "oracle",
+            "blas_threads": threads, "cpus_allowed": allowed, "cpu_model": model,
             "sample": f"first {n_tokens} of {cfg.T} tokens of the same layer, full oracle forward (route, permute, "
                       f"per-expert fp64 loop incl. converting each used expert's bf16 weights, combine)",
             "seconds": round(dt, 2)}

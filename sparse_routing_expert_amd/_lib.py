@@ -65,6 +65,13 @@ _SIGS = {
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
 }
 EXPORTED = tuple(_SIGS)
+# measurement probes (include/moe_probe.h), not part of the layer
+_PROBE_SIGS = {
+    "moe_probe_copy": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int, _P]),
+    "moe_probe_mfma": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _P, _P]),
+    "moe_probe_mfma_flops": (ctypes.c_double, [ctypes.c_int, ctypes.c_int]),
+}
+PROBES = tuple(_PROBE_SIGS)
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -76,7 +83,7 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise MoeLibraryMissing(f"{LIB_PATH} not found: build it with `python -m sparse_routing_expert_amd.build`")
         h = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in _SIGS.items():
+        for name, (res, args) in {**_SIGS, **_PROBE_SIGS}.items():
             fn = getattr(h, name)
             fn.restype = res
             fn.argtypes = args
@@ -219,3 +226,12 @@ def moe_backward(shape, x, w_router, w_in, b_in, w_out, b_out, ws_in, ws_out, lo
         _ptr(dw_out), _ptr(db_out), _ptr(dws_in), _ptr(dws_out), _ptr(dlogits), _ptr(ws), _nbytes(ws),
         _stream(stream)))
 
+
+def moe_probe_copy(src, dst, nbytes: int, blocks: int, stream=None) -> None:
+    _check("moe_probe_copy", lib().moe_probe_copy(_ptr(src), _ptr(dst), int(nbytes), int(blocks), _stream(stream)))
+
+
+def moe_probe_mfma(blocks: int, iters: int, out, stream=None) -> float:
+    """Enqueues the MFMA-only loop; returns its floating-point work."""
+    _check("moe_probe_mfma", lib().moe_probe_mfma(int(blocks), int(iters), _ptr(out), _stream(stream)))
+    return float(lib().moe_probe_mfma_flops(int(blocks), int(iters)))

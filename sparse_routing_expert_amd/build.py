@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libmoe.so")
-SOURCES = ["route.hip", "permute.hip", "grouped_gemm.hip", "combine.hip", "backward.hip", "noalloc.hip", "moe_api.cpp"]
+SOURCES = ["route.hip", "permute.hip", "grouped_gemm.hip", "combine.hip", "backward.hip", "noalloc.hip", "probes.hip", "moe_api.cpp"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -34,6 +34,19 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
+def test_exports_probes(lib):
+    src = open(os.path.join(ROOT, "include", "moe_probe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    declared = sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    assert declared == sorted(L.PROBES)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.moe_probe_copy(None, FAKE, 16, 1, None) == -1
+    assert lib.moe_probe_copy(FAKE, FAKE, 17, 1, None) == -1
+    assert lib.moe_probe_mfma(0, 1, FAKE, None) == -1
+    assert lib.moe_probe_mfma_flops(2, 3) == 2 * 4 * 3 * 8 * 32 * 32 * 16 * 2
+
+
 def test_status_strings(lib):
     assert L.status_name(0) == "MOE_OK"
     assert L.status_name(-3) == "MOE_ERR_WORKSPACE"
