@@ -22,10 +22,15 @@
  * ---------------------------------------
  * Memory:    every pointer argument is caller-owned DEVICE memory of the current
  *            HIP device (except `shape`, which is host memory). The library never
- *            allocates, frees or synchronises and keeps no state between calls;
- *            scratch comes only from the caller's workspace `ws` of `ws_bytes`
+ *            allocates, frees or synchronises and keeps no state of its own between
+ *            calls; scratch comes only from the caller's workspace `ws` of `ws_bytes`
  *            bytes, sized by moe_workspace_bytes(). The one exception is
  *            moe_permute_noalloc, whose scratch is a fixed array inside the library.
+ * Workspace: the workspaces of moe_route, moe_route_noisy and moe_forward carry a
+ *            completion counter between calls: zero each such workspace once after
+ *            allocating it (hipMemset, torch.zeros); every call leaves the counter at
+ *            zero again. Between two calls that share one, write nothing else into it.
+ *            The other stages' workspaces need no initialisation.
  * Layout:    row-major everywhere. Weights use the Linear [out, in] layout, so
  *            both operands of every product are contiguous along the reduced
  *            dimension. Expert weights are stacked along a leading expert axis.
@@ -61,7 +66,8 @@ extern "C" {
 typedef enum {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = -1, /* null required pointer, bad enum, inconsistent sizes, misalignment */
-    MOE_ERR_UNSUPPORTED = -2, /* valid request the library does not implement (e.g. d_model % 64) */
+    MOE_ERR_UNSUPPORTED = -2, /* valid request the library does not implement (e.g. a bf16 backward
+                                 with d_model % 64 != 0) */
     MOE_ERR_WORKSPACE = -3,   /* ws_bytes below moe_workspace_bytes() for the call */
     MOE_ERR_HIP = -4          /* a kernel launch failed (hipGetLastError) */
 } moe_status;
@@ -93,9 +99,10 @@ enum {
 };
 
 /* Layer description (host memory). Limits: T >= 0; 1 <= E <= 1024; 1 <= k <= min(E, 32); capacity >= 0;
- * T*k <= 2^31-1; bf16: d_model, d_ff, d_ff_shared multiples of 64; f32: multiples of 4;
- * MOE_SIGMOID requires renorm = 1. Violations give MOE_ERR_INVALID_ARG or
- * MOE_ERR_UNSUPPORTED (multiples). */
+ * T*k <= 2^31-1; d_model, d_ff and d_ff_shared multiples of 8 (bf16) or 4 (f32), so every row is
+ * whole 16-byte vectors (MOE_ERR_INVALID_ARG otherwise); MOE_SIGMOID requires renorm = 1
+ * (MOE_ERR_UNSUPPORTED). moe_backward on bf16 layers further needs multiples of 64
+ * (MOE_ERR_UNSUPPORTED). */
 typedef struct {
     int64_t T;           /* tokens */
     int32_t d_model;     /* hidden size d */
@@ -112,8 +119,11 @@ typedef struct {
 
 typedef void* moe_stream_t; /* a hipStream_t */
 
-/* Scratch bytes a call needs. stage: MOE_STAGE_*. Writes the size to *bytes.
- * Returns MOE_ERR_INVALID_ARG for an invalid shape or stage, else MOE_OK. */
+/* Scratch bytes a call needs. stage: MOE_STAGE_*. Writes the size to *bytes (a status and an
+ * out-parameter rather than a bare size_t, so an invalid shape or stage is reported, not sized).
+ * Returns MOE_ERR_INVALID_ARG for an invalid shape or stage, else MOE_OK. The MOE_STAGE_ROUTE,
+ * MOE_STAGE_ROUTE_NOISY and MOE_STAGE_FORWARD workspaces must be zeroed once before first use
+ * (see Workspace above). */
 int moe_workspace_bytes(const moe_shape* shape, int stage, size_t* bytes);
 
 /* moe_route -- the router: logits, scores, per-token top-k, gates, counts, statistics.

@@ -174,16 +174,25 @@ __device__ __forceinline__ void wait_stages(int n) {
     else wait_vm<6 * NQ>();
 }
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+// Byte offset of 16-byte chunk c of row R of a gathered tile (rows row0 + R of the group are tokens
+// gather[row0 + R] of A). Rows past the group's end read its last row, which the epilogue never
+// stores; the descriptor spans A, so every offset stays in range.
+__device__ __forceinline__ int gathered_voff(const int32_t* __restrict__ gather, int64_t row0, int64_t row_end, int R,
+                                             int K, int c) {
+    const int64_t p = row0 + R < row_end ? row0 + R : row_end - 1;
+    return (int)((uint32_t)gather[p] * (uint32_t)(K * 2) + (uint32_t)(c * 16));
+}
 
 }  // namespace
 
-template <int BM, int BN, int EPI, int NS, int GM>
+template <int BM, int BN, int EPI, int NS, int GM, bool KT>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                            const uint16_t* __restrict__ B,
                                                            const uint16_t* __restrict__ bias,
                                                            uint16_t* __restrict__ C,
                                                            const int32_t* __restrict__ offsets, int e_begin,
-                                                           int n_groups, int64_t dense_rows, int n_out, int K) {
+                                                           int n_groups, int64_t dense_rows, int n_out, int K,
+                                                           const int32_t* __restrict__ gather, uint32_t a_bytes) {
     constexpr int BK = 32, WM = 2, WN = 2;
     constexpr bool GATED = EPI == EPI_SWIGLU;
     constexpr int WTM = BM / WM, TM = WTM / 32;
@@ -221,7 +230,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
     const int64_t a_rows = tc.row_end - tc.row0 < BM ? tc.row_end - tc.row0 : BM;
     const int bn_part = GATED ? BN / 2 : BN;
     const int bcols = n_out - tc.n0 < bn_part ? n_out - tc.n0 : bn_part;
-    const i32x4 ra = make_rsrc(A + tc.row0 * K, (uint32_t)(a_rows * K * 2));
+    // gathered rows: A holds the tokens and row p of the group is A[gather[p]]; the descriptor covers
+    // all of A and each lane addresses its own row
+    const i32x4 ra = gather ? make_rsrc(A, a_bytes) : make_rsrc(A + tc.row0 * K, (uint32_t)(a_rows * K * 2));
     const i32x4 rb0 = make_rsrc(Bg + (int64_t)tc.n0 * K, (uint32_t)((int64_t)bcols * K * 2));
     const i32x4 rb1 = make_rsrc(Bg + (int64_t)(GATED ? n_out + tc.n0 : tc.n0) * K, (uint32_t)((int64_t)bcols * K * 2));
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)lds;
@@ -237,6 +248,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
         else if (!GATED || q < (BM + BN / 2) / 64) row = R - BM;
         else row = R - BM - BN / 2;
         voff[q] = row * K * 2 + c * 16;
+        if (q < BM / 64 && gather) voff[q] = gathered_voff(gather, tc.row0, tc.row_end, R, K, c);
+    }
+    // K not a multiple of BK (KT): the last stage's weight chunks past K read as zeros (the lane's
+    // offset is pushed past the descriptor's range), so the token rows' bytes past K, which belong to
+    // the next row, are multiplied by zero
+    const int nk = KT ? (K + BK - 1) / BK : K / BK;
+    int tor[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int R = (q * 4 + wave) * 16 + (lane >> 2);
+        tor[q] = KT && q >= BM / 64 && ((lane & 3) ^ swz(R)) * 8 >= K - (nk - 1) * BK ? (int)0x80000000 : 0;
     }
     // operand rows of this lane
     int a_off[TM], a_sw[TM], b_off[TN], b_sw[TN];
@@ -265,13 +287,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
     bf16x8 fa[2][TM], fb[2][TN];
 
 #define MOE_RSRC(q) ((q) < BM / 64 ? ra : ((!GATED || (q) < (BM + BN / 2) / 64) ? rb0 : rb1))
+#define MOE_VOFF(q, kd_) (KT && (kd_) == nk - 1 ? (voff[q] | tor[q]) : voff[q])
 #define MOE_ISSUE(kt_, q0, q1)                                                                            \
     {                                                                                                     \
         const int kt__ = (kt_);                                                                           \
         const uint32_t sbase = lds_base + (kt__ % NS) * STAGE_BYTES + wave * 1024;                        \
         const int soff = __builtin_amdgcn_readfirstlane(kt__ * BK * 2);                                   \
         _Pragma("unroll") for (int q = 0; q < NQ; ++q) if (q >= (q0) && q < (q1))                          \
-            dma16(sbase + q * 4096, voff[q], MOE_RSRC(q), soff);                                          \
+            dma16(sbase + q * 4096, MOE_VOFF(q, kt__), MOE_RSRC(q), soff);                                \
     }
 #define MOE_FREAD(slot_, kk, f)                                                                           \
     {                                                                                                     \
@@ -286,7 +309,6 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
     _Pragma("unroll") for (int i = 0; i < TM; ++i) _Pragma("unroll") for (int j = 0; j < TN; ++j)         \
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][i], fb[f][j], acc[i][j], 0, 0, 0);
 
-    const int nk = K / BK;
     // DMA schedule: a stage's first NH instructions go out in phase B of one iteration and the rest in
     // phase A of the next, one every two MFMAs, so no wave bursts the vector-memory queue.
     constexpr int NH = NQ / 2;
@@ -324,7 +346,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
                 }
                 if (t % SP == SP0 && NH + t / SP < NQ) {
                     const int q = NH + t / SP;
-                    dma16(sbase + q * 4096, voff[q], MOE_RSRC(q), soff);
+                    dma16(sbase + q * 4096, MOE_VOFF(q, kd), MOE_RSRC(q), soff);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -353,7 +375,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
                 }
                 if (t % SP == SP0 && t / SP < NH) {
                     const int q = t / SP;
-                    dma16(sbase + q * 4096, voff[q], MOE_RSRC(q), soff);
+                    dma16(sbase + q * 4096, MOE_VOFF(q, kd), MOE_RSRC(q), soff);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -369,6 +391,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
         MOE_MMA(1);
     }
 #undef MOE_ISSUE
+#undef MOE_VOFF
 #undef MOE_RSRC
 #undef MOE_FREAD
 #undef MOE_MMA
@@ -615,11 +638,11 @@ __device__ __forceinline__ floatx4* partial_at(float* partials, uint32_t pslot, 
 // consecutive output features, written with one 8-byte store. Stores and LDS-DMA loads share the
 // vector-memory counter and may complete out of order, so the memory cluster after a tile's stores
 // waits for the counter to drain before it issues new loads.
-template <int EPI, int GM, int D>
+template <int EPI, int GM, int D, bool KT>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ C, const int32_t* __restrict__ offsets, int e_begin, int n_groups, int64_t dense_rows,
-    int n_out, int K, float* __restrict__ partials) {
+    int n_out, int K, float* __restrict__ partials, const int32_t* __restrict__ gather, uint32_t a_bytes) {
     constexpr int BM = 256, BN = 256, BK = 32, NS = D + 1;
     constexpr bool GATED = EPI == EPI_SWIGLU;
     constexpr int TM = 2;  // 64 tokens per wave
@@ -637,7 +660,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
     const int tid = threadIdx.x, lane = lane_id();
     const TileSched<BM, BNO, GM> ts =
         setup_sched<BM, BNO, GM>(offsets, e_begin, n_groups, dense_rows, n_out, s_ts, s_off, s_wave);
-    const int nk = K / BK;
+    const int nk = KT ? (K + BK - 1) / BK : K / BK;
     const uint32_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
     const XcdPlan plan = xcd_plan(ts.R, xcd, nslots, nk, partials != nullptr);
     // this block's units: nw whole tiles, then at most one K slice of a tail tile
@@ -680,6 +703,14 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
         const int row = (grp == 1 && GATED && q >= 2) ? Rl - 128 : Rl;
         voff[q] = row * K * 2 + c * 16;
     }
+    // K not a multiple of BK (KT): the weight chunks of the last stage past K read as zeros
+    int tor[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int Rl = (q * 4 + wig) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ swz(grp * 256 + Rl);
+        tor[q] = KT && grp == 1 && c * 8 >= K - (nk - 1) * BK ? (int)0x80000000 : 0;
+    }
     // buffer descriptors of the tile whose stages are being loaded
     i32x4 rs[NQ];
     auto set_dma_tile = [&](uint32_t lin) {
@@ -688,9 +719,16 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
         ts.decode(lin, row0, row_end, e, n0);
         if (grp == 0) {
             const int64_t a_rows = row_end - row0 < BM ? row_end - row0 : BM;
-            const i32x4 ra = make_rsrc(A + row0 * K, (uint32_t)(a_rows * K * 2));
+            const i32x4 ra = gather ? make_rsrc(A, a_bytes) : make_rsrc(A + row0 * K, (uint32_t)(a_rows * K * 2));
 #pragma unroll
             for (int q = 0; q < NQ; ++q) rs[q] = ra;
+            if (gather) {  // gathered token rows: this tile's row offsets
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    const int Rl = (q * 4 + wig) * 16 + (lane >> 2);
+                    voff[q] = gathered_voff(gather, row0, row_end, Rl, K, (lane & 3) ^ swz(Rl));
+                }
+            }
         } else {
             const uint16_t* Bg = B + (int64_t)e * n_b_rows * K;
             const int bn_part = GATED ? BN / 2 : BN;
@@ -734,7 +772,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
     {                                                                                                     \
         const uint32_t sbase = lds_base + (slot_) * STAGE_BYTES + grp * 16384 + wig * 1024;               \
         const int soff = (ks_) * (BK * 2);                                                                \
-        _Pragma("unroll") for (int q = 0; q < NQ; ++q) dma16(sbase + q * 4096, voff[q], rs[q], soff);     \
+        const bool tail_ = KT && (ks_) == nk - 1;                                                         \
+        _Pragma("unroll") for (int q = 0; q < NQ; ++q)                                                    \
+            dma16(sbase + q * 4096, tail_ ? (voff[q] | tor[q]) : voff[q], rs[q], soff);                   \
     }
 #define PS_READ(slot_)                                                                                    \
     {                                                                                                     \
@@ -855,11 +895,11 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
 // in the eight-wave layout that gemm_bf16_tail_kernel reads.
 __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 
-template <int EPI, int GM>
+template <int EPI, int GM, bool KT>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ C, const int32_t* __restrict__ offsets, int e_begin, int n_groups, int64_t dense_rows,
-    int n_out, int K, float* __restrict__ partials) {
+    int n_out, int K, float* __restrict__ partials, const int32_t* __restrict__ gather, uint32_t a_bytes) {
     constexpr int BM = 256, BN = 256, BK = 64, NS = 2;
     constexpr bool GATED = EPI == EPI_SWIGLU;
     constexpr int TM = 4;
@@ -877,7 +917,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
     const int tid = threadIdx.x, lane = lane_id();
     const TileSched<BM, BNO, GM> ts =
         setup_sched<BM, BNO, GM, 256>(offsets, e_begin, n_groups, dense_rows, n_out, s_ts, s_off, s_wave);
-    const int nk = K / BK;
+    const int nk = KT ? (K + BK - 1) / BK : K / BK;
     const uint32_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
     const XcdPlan plan = xcd_plan(ts.R, xcd, nslots, nk, partials != nullptr);
     const uint32_t nw = plan.nwhole + ((plan.S == 1 && slot < plan.rem) ? 1u : 0u);
@@ -917,13 +957,29 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
         const int row = q < 8 ? R : ((GATED && q >= 12) ? R - 384 : R - 256);
         voff[q] = row * K * 2 + c * 16;
     }
+    // K not a multiple of BK (KT): the weight chunks of the last stage past K read as zeros
+    int tor[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int R = ((q + 8) * 4 + wave) * 8 + (lane >> 3);
+        tor[q] = KT && ((lane & 7) ^ swz8(R)) * 8 >= K - (nk - 1) * BK ? (int)0x80000000 : 0;
+    }
     i32x4 ra, rb0, rb1;
     auto set_dma_tile = [&](uint32_t lin) {
         int64_t row0, row_end;
         int e, n0;
         ts.decode(lin, row0, row_end, e, n0);
         const int64_t a_rows = row_end - row0 < BM ? row_end - row0 : BM;
-        ra = make_rsrc(A + row0 * K, (uint32_t)(a_rows * K * 2));
+        if (gather) {  // gathered token rows: the descriptor spans A, the row offsets follow the tile
+            ra = make_rsrc(A, a_bytes);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int R = (q * 4 + wave) * 8 + (lane >> 3);
+                voff[q] = gathered_voff(gather, row0, row_end, R, K, (lane & 7) ^ swz8(R));
+            }
+        } else {
+            ra = make_rsrc(A + row0 * K, (uint32_t)(a_rows * K * 2));
+        }
         const uint16_t* Bg = B + (int64_t)e * n_b_rows * K;
         const int bn_part = GATED ? BN / 2 : BN;
         const int bcols = n_out - n0 < bn_part ? n_out - n0 : bn_part;
@@ -951,7 +1007,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
     bf16x8 fa[2][TM], fb[2][TN];
 
 #define PW_DMA(slot_, ks_, q_)                                                                            \
-    dma16(lds_base + (slot_) * STAGE_BYTES + ((q_) * 4 + wave) * 1024, voff[q_],                          \
+    dma16(lds_base + (slot_) * STAGE_BYTES + ((q_) * 4 + wave) * 1024,                                    \
+          (KT && (q_) >= 8 && (ks_) == nk - 1) ? (voff[q_] | tor[((q_) + 8) & 7]) : voff[q_],             \
           (q_) < 8 ? ra : ((GATED && (q_) >= 12) ? rb1 : rb0), (ks_) * (BK * 2));
     // fragment n (in MFMA use order: fa0, fb0..fb3, fa1..fa3) of 16-wide K step kk_ into buffer b_
 #define PW_READ(b_, kk_, slot_, n_)                                                                       \
@@ -1163,7 +1220,8 @@ size_t gemm_partials_bytes(int dtype) {
 template <int GM, int D>
 void launch_bf16_persistent(int epi, const void* A, const void* B, const void* bias, void* C,
                             const int32_t* offsets, int e_begin, int n_groups, int64_t max_rows, int64_t dense_rows,
-                            int n_out, int K, float* partials, hipStream_t s) {
+                            int n_out, int K, float* partials, hipStream_t s, const int32_t* gather,
+                            uint32_t a_bytes) {
     const int bno = epi == EPI_SWIGLU ? 128 : 256;
     const int64_t m_tiles = offsets ? (max_rows + 255) / 256 + n_groups : (dense_rows + 255) / 256;
     const int64_t tiles = m_tiles * ((n_out + bno - 1) / bno);
@@ -1180,8 +1238,12 @@ void launch_bf16_persistent(int epi, const void* A, const void* B, const void* b
     auto c = static_cast<uint16_t*>(C);
 #define MOE_PERSIST(EPI_)                                                                                 \
     {                                                                                                     \
-        gemm_bf16_persistent_kernel<EPI_, GM, D><<<grid, 512, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups, \
-                                                                     dense_rows, n_out, K, partials);     \
+        if (K % 32)                                                                                       \
+            gemm_bf16_persistent_kernel<EPI_, GM, D, true><<<grid, 512, 0, s>>>(                          \
+                a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out, K, partials, gather, a_bytes);  \
+        else                                                                                              \
+            gemm_bf16_persistent_kernel<EPI_, GM, D, false><<<grid, 512, 0, s>>>(                         \
+                a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out, K, partials, gather, a_bytes);  \
         if (partials)                                                                                     \
             gemm_bf16_tail_kernel<EPI_><<<grid * tail_chunks<EPI_>(), 256, 0, s>>>(partials, bi, c, n_out,  \
                                                                                   (int)(grid / 8));       \
@@ -1196,7 +1258,7 @@ void launch_bf16_persistent(int epi, const void* A, const void* B, const void* b
 template <int GM>
 void launch_bf16_wide(int epi, const void* A, const void* B, const void* bias, void* C, const int32_t* offsets,
                     int e_begin, int n_groups, int64_t max_rows, int64_t dense_rows, int n_out, int K, float* partials,
-                    hipStream_t s) {
+                    hipStream_t s, const int32_t* gather, uint32_t a_bytes) {
     const int bno = epi == EPI_SWIGLU ? 128 : 256;
     const int64_t m_tiles = offsets ? (max_rows + 255) / 256 + n_groups : (dense_rows + 255) / 256;
     const int64_t tiles = m_tiles * ((n_out + bno - 1) / bno);
@@ -1211,8 +1273,12 @@ void launch_bf16_wide(int epi, const void* A, const void* B, const void* bias, v
     auto c = static_cast<uint16_t*>(C);
 #define MOE_WIDE(EPI_)                                                                                      \
     {                                                                                                     \
-        gemm_bf16_wide_kernel<EPI_, GM><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,      \
-                                                            dense_rows, n_out, K, partials);              \
+        if (K % 64)                                                                                       \
+            gemm_bf16_wide_kernel<EPI_, GM, true><<<grid, 256, 0, s>>>(                                   \
+                a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out, K, partials, gather, a_bytes);  \
+        else                                                                                              \
+            gemm_bf16_wide_kernel<EPI_, GM, false><<<grid, 256, 0, s>>>(                                  \
+                a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out, K, partials, gather, a_bytes);  \
         if (partials)                                                                                     \
             gemm_bf16_tail_kernel<EPI_><<<grid * tail_chunks<EPI_>(), 256, 0, s>>>(partials, bi, c, n_out,  \
                                                                                   (int)(grid / 8));       \
@@ -1309,7 +1375,7 @@ GemmPlan plan_gemm(int dtype, int64_t rows_per_group_hint, int n_out, int K) {
 template <int BM, int BN, int NS, int GM>
 void launch_bf16_tiles(int epi, const void* A, const void* B, const void* bias, void* C, const int32_t* offsets,
                        int e_begin, int n_groups, int64_t max_rows, int64_t dense_rows, int n_out, int K,
-                       hipStream_t s) {
+                       hipStream_t s, const int32_t* gather, uint32_t a_bytes) {
     const int bno = epi == EPI_SWIGLU ? BN / 2 : BN;
     const int64_t m_tiles = offsets ? (max_rows + BM - 1) / BM + n_groups : (dense_rows + BM - 1) / BM;
     const int64_t n_tiles = (n_out + bno - 1) / bno;
@@ -1319,24 +1385,30 @@ void launch_bf16_tiles(int epi, const void* A, const void* B, const void* bias, 
     const auto b = static_cast<const uint16_t*>(B);
     const auto bi = static_cast<const uint16_t*>(bias);
     auto c = static_cast<uint16_t*>(C);
+#define MOE_TILES(EPI_)                                                                                   \
+    {                                                                                                     \
+        if (K % 32)                                                                                       \
+            gemm_bf16_kernel<BM, BN, EPI_, NS, GM, true><<<grid, 256, 0, s>>>(                            \
+                a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out, K, gather, a_bytes);            \
+        else                                                                                              \
+            gemm_bf16_kernel<BM, BN, EPI_, NS, GM, false><<<grid, 256, 0, s>>>(                           \
+                a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out, K, gather, a_bytes);            \
+    }
     if constexpr (BN >= 128) {  // a gated tile holds gate and up halves of at least 64 columns each
         if (epi == EPI_SWIGLU) {
-            gemm_bf16_kernel<BM, BN, EPI_SWIGLU, NS, GM><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin,
-                                                                             n_groups, dense_rows, n_out, K);
+            MOE_TILES(EPI_SWIGLU)
             return;
         }
     }
-    if (epi == EPI_GELU_BIAS)
-        gemm_bf16_kernel<BM, BN, EPI_GELU_BIAS, NS, GM><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin,
-                                                                            n_groups, dense_rows, n_out, K);
-    else
-        gemm_bf16_kernel<BM, BN, EPI_BIAS, NS, GM><<<grid, 256, 0, s>>>(a, b, bi, c, offsets, e_begin, n_groups,
-                                                                       dense_rows, n_out, K);
+    if (epi == EPI_GELU_BIAS) MOE_TILES(EPI_GELU_BIAS)
+    else MOE_TILES(EPI_BIAS)
+#undef MOE_TILES
 }
 
 void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* B, const void* bias, void* C,
                          const int32_t* offsets, int e_begin, int n_groups, int64_t max_rows, int64_t dense_rows,
-                         int n_out, int K, float* partials, hipStream_t s) {
+                         int n_out, int K, float* partials, hipStream_t s, const int32_t* gather, int64_t a_rows) {
+    const uint32_t a_bytes = gather ? (uint32_t)(a_rows * K * 2) : 0u;
     if (dtype == MOE_BF16) {
         if (bm == 64 && offsets != nullptr && epi != EPI_F32) {
             // small groups: 64-row x 128-column tiles with a 6-stage LDS ring (72 KB, two blocks per CU).
@@ -1347,11 +1419,11 @@ void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* 
             // CU holds two blocks: 260 -> 253-257 us there.
             if (epi != EPI_SWIGLU && (int64_t)n_groups * ((n_out + 127) / 128) < 512) {
                 launch_bf16_tiles<64, 64, 8, 8>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows,
-                                                n_out, K, s);
+                                                n_out, K, s, gather, a_bytes);
                 return;
             }
             launch_bf16_tiles<64, 128, 6, 8>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows,
-                                             n_out, K, s);
+                                             n_out, K, s, gather, a_bytes);
             return;
         }
         // expert groups averaging at least kGemmWideRows rows (kGemmWideRowsLongK over a K of at least
@@ -1361,10 +1433,10 @@ void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* 
         if (offsets != nullptr &&
             (max_rows >= kGemmWideRows * ng || (K >= kGemmWideMinK && max_rows >= kGemmWideRowsLongK * ng)))
             launch_bf16_wide<8>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows, n_out, K,
-                                partials, s);
+                                partials, s, gather, a_bytes);
         else
             launch_bf16_persistent<8, 3>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows,
-                                         n_out, K, partials, s);
+                                         n_out, K, partials, s, gather, a_bytes);
         return;
     }
     const int64_t m_tiles = offsets ? (max_rows + 63) / 64 + n_groups : (dense_rows + 63) / 64;

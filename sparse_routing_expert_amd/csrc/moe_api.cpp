@@ -31,8 +31,9 @@ int check_shape(const moe_shape* s) {
     if (s->capacity < 0) return MOE_ERR_INVALID_ARG;
     if (s->T * (int64_t)s->k > (int64_t)INT32_MAX) return MOE_ERR_INVALID_ARG;
     if (s->score == MOE_SIGMOID && s->renorm != 1) return MOE_ERR_UNSUPPORTED;
-    const int mult = s->dtype == MOE_BF16 ? 64 : 4;
-    if (s->d_model % mult || s->d_ff % mult || s->d_ff_shared % mult) return MOE_ERR_UNSUPPORTED;
+    // 16-byte vectors of bf16 (8 elements) or fp32 (4 elements) along every row
+    const int mult = s->dtype == MOE_BF16 ? 8 : 4;
+    if (s->d_model % mult || s->d_ff % mult || s->d_ff_shared % mult) return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
 
@@ -59,7 +60,9 @@ RouteWs route_ws(const moe_shape* s) {
     Carver c;
     w.nblk = (int)cdiv(s->T, kRouteTokensPerBlock);
     w.Epad = (int)cdiv(s->E, 16) * 16;
-    w.gemm = s->dtype == MOE_BF16 && w.Epad >= moe::kRouteGemmMinEpad;
+    // the MFMA logits kernels step d in 32-column chunks; other widths take the router product on the
+    // grouped GEMM, whose last K stage is masked
+    w.gemm = s->dtype == MOE_BF16 && (w.Epad >= moe::kRouteGemmMinEpad || s->d_model % 32 != 0);
     w.lg_ld = w.gemm ? 3 * w.Epad : s->E;
     w.lg_split = w.gemm ? w.Epad : 0;
     w.logits = c.take((size_t)s->T * w.lg_ld * 4);
@@ -140,20 +143,27 @@ SharedWs shared_ws(const moe_shape* s) {
     return w;
 }
 
+// bf16 forward: the up projection reads token rows through sorted_token (no x_perm copy) while x
+// fits one buffer descriptor's 32-bit byte range
+bool fwd_gathers(const moe_shape* s) {
+    return s->dtype == MOE_BF16 && s->T * (int64_t)s->d_model * 2 <= (int64_t)UINT32_MAX;
+}
+
 struct FwdWs {
-    size_t topk_idx, topk_w, counts, offsets, sorted_token, inv_pos, x_perm, y_perm, ys, scratch, bytes;
+    size_t ticket, topk_idx, topk_w, counts, offsets, sorted_token, inv_pos, x_perm, y_perm, ys, scratch, bytes;
 };
 FwdWs fwd_ws(const moe_shape* s) {
     FwdWs w;
     Carver c;
     const size_t A = (size_t)s->T * s->k, eb = elem_bytes(s);
+    w.ticket = c.take(4);  // the route's completion ticket, apart from the scratch the later stages reuse
     w.topk_idx = c.take(A * 4);
     w.topk_w = c.take(A * 4);
     w.counts = c.take((size_t)s->E * 4);
     w.offsets = c.take((size_t)(s->E + 1) * 4);
     w.sorted_token = c.take(A * 4);
     w.inv_pos = c.take(A * 4);
-    w.x_perm = c.take(A * s->d_model * eb);
+    w.x_perm = c.take(fwd_gathers(s) ? 0 : A * s->d_model * eb);
     w.y_perm = c.take(A * s->d_model * eb);
     w.ys = c.take(s->d_ff_shared ? (size_t)s->T * s->d_model * eb : 0);
     size_t scratch = route_ws(s).bytes;  // the stages run one after another on one stream
@@ -227,21 +237,21 @@ void route_logits(const moe_shape* s, const RouteWs& w, const void* x, const flo
         moe::launch_route_logits(s->dtype, x, w_router, wsplit, w.Epad, lg, s->T, s->d_model, s->E, st);
 }
 
+// ticket_at: where the completion ticket lives (NULL: in ws). It is zero before and after every call.
 void do_route(const moe_shape* s, const void* x, const float* w_router, const float* sel_bias, float* logits,
-              int32_t* topk_idx, float* topk_w, int32_t* counts, float* stats, void* ws, hipStream_t st) {
+              int32_t* topk_idx, float* topk_w, int32_t* counts, float* stats, void* ws, hipStream_t st,
+              int32_t* ticket_at = nullptr) {
     const RouteWs w = route_ws(s);
     float* lg = logits && !w.gemm ? logits : at<float>(ws, w.logits);
     uint16_t* wsplit = s->dtype == MOE_BF16 ? at<uint16_t>(ws, w.wsplit) : nullptr;
-    int32_t* ticket = at<int32_t>(ws, w.ticket);
+    int32_t* ticket = ticket_at ? ticket_at : at<int32_t>(ws, w.ticket);
     int32_t* blk_counts = at<int32_t>(ws, w.blk_counts);
     float* blk_P = stats ? at<float>(ws, w.blk_P) : nullptr;
     float* blk_H = stats ? at<float>(ws, w.blk_H) : nullptr;
-    if (moe::route_small_ok(s->dtype, s->E, s->k, s->d_model)) {  // logits and selection in one launch
-        const int nblk = (int)cdiv(s->T, moe::route_small_tokens_per_block(s->T, s->E, false));
+    if (moe::route_small_ok(s->dtype, s->E, s->k, s->d_model)) {  // logits, selection and counts in one launch
         moe::launch_route_small(x, w_router, nullptr, nullptr, sel_bias, s->T, s->d_model, s->E, s->k, s->score,
-                                s->renorm, logits, topk_idx, topk_w, blk_counts, blk_P, blk_H, ticket, st);
-        moe::launch_route_finalize(blk_counts, blk_P, blk_H, nblk, s->T, s->E, counts, at<double>(ws, w.fp), ticket,
-                                   stats, st);
+                                s->renorm, logits, topk_idx, topk_w, blk_counts, blk_P, blk_H, ticket, counts, stats,
+                                st);
         return;
     }
     route_logits(s, w, x, w_router, wsplit, ticket, lg, ws, st);
@@ -266,12 +276,10 @@ void do_route_noisy(const moe_shape* s, const void* x, const float* w_router, co
     int32_t* blk_counts = at<int32_t>(ws, w.blk_counts);
     float* blk_P = stats ? at<float>(ws, w.blk_P) : nullptr;
     float* blk_H = stats ? at<float>(ws, w.blk_H) : nullptr;
-    if (moe::route_small_ok(s->dtype, s->E, s->k, s->d_model)) {  // both projections and the selection fused
-        const int nblk = (int)cdiv(s->T, moe::route_small_tokens_per_block(s->T, s->E, true));
+    if (moe::route_small_ok(s->dtype, s->E, s->k, s->d_model)) {  // both projections, selection, counts fused
         moe::launch_route_small(x, w_router, w_noise, noise, sel_bias, s->T, s->d_model, s->E, s->k, s->score,
-                                s->renorm, logits, topk_idx, topk_w, blk_counts, blk_P, blk_H, ticket, st);
-        moe::launch_route_finalize(blk_counts, blk_P, blk_H, nblk, s->T, s->E, counts, at<double>(ws, w.fp), ticket,
-                                   stats, st);
+                                s->renorm, logits, topk_idx, topk_w, blk_counts, blk_P, blk_H, ticket, counts, stats,
+                                st);
         return;
     }
     route_logits(s, w, x, w_router, wsplit, ticket, lg, ws, st);
@@ -282,13 +290,15 @@ void do_route_noisy(const moe_shape* s, const void* x, const float* w_router, co
                                stats, st);
 }
 
+// x_perm == NULL: positions only (offsets, sorted_token, inv_pos), no row copy; the forward's up
+// projection then reads the token rows through sorted_token itself
 void do_permute(const moe_shape* s, const int32_t* topk_idx, const void* x, int32_t* offsets,
                 int32_t* sorted_token, int32_t* inv_pos, void* x_perm, void* ws, hipStream_t st) {
     const PermWs w = perm_ws(s);
     const int64_t A = s->T * s->k;
     if (moe::perm_index_small_ok(A, s->E)) {
         moe::launch_perm_index_small(topk_idx, A, s->E, s->k, s->capacity, offsets, inv_pos, sorted_token, st);
-        moe::launch_perm_scatter(x, inv_pos, s->T, s->d_model, s->k, elem_bytes(s), x_perm, st);
+        if (x_perm != nullptr) moe::launch_perm_scatter(x, inv_pos, s->T, s->d_model, s->k, elem_bytes(s), x_perm, st);
         return;
     }
     int32_t* tile_counts = at<int32_t>(ws, w.tile_counts);
@@ -299,20 +309,23 @@ void do_permute(const moe_shape* s, const int32_t* topk_idx, const void* x, int3
         moe::launch_perm_scan(tile_counts, w.ntiles, A, s->E, s->capacity, tile_base, offsets, st);
     }
     moe::launch_perm_place_scatter(x, topk_idx, tile_counts, tile_base, offsets, s->E, s->capacity, s->T,
-                                   s->d_model, s->k, elem_bytes(s), inv_pos, sorted_token, x_perm, st);
+                                   s->d_model, s->k, x_perm != nullptr ? elem_bytes(s) : 0, inv_pos, sorted_token,
+                                   x_perm, st);
 }
 
 inline float* partials_of(void* ws, size_t off, const moe_shape* s) {
     return s->dtype == MOE_BF16 ? at<float>(ws, off) : nullptr;
 }
 
+// gather != NULL: x_perm is the token matrix x and row p of the product reads x[gather[p]]
 void do_up(const moe_shape* s, int e_begin, int e_end, const void* x_perm, const int32_t* offsets,
-           const void* w_in, const void* b_in, void* h, float* partials, hipStream_t st) {
+           const void* w_in, const void* b_in, void* h, float* partials, hipStream_t st,
+           const int32_t* gather = nullptr) {
     const int64_t A = s->T * s->k;
     const moe::GemmPlan p = moe::plan_gemm(s->dtype, A / s->E, s->d_ff, s->d_model);
     moe::launch_grouped_gemm(s->dtype, s->act == MOE_SWIGLU ? moe::EPI_SWIGLU : moe::EPI_GELU_BIAS, p.bm, x_perm,
                              w_in, b_in, h, offsets, e_begin, e_end - e_begin, A, 0, s->d_ff, s->d_model, partials,
-                             st);
+                             st, gather, s->T);
 }
 
 void do_down(const moe_shape* s, int e_begin, int e_end, const void* h, const int32_t* offsets, const void* w_out,
@@ -339,14 +352,14 @@ int ffn_experts_per_chunk(const moe_shape* s, int n_experts) {
 
 void do_ffn(const moe_shape* s, int e_begin, int e_end, const void* x_perm, const int32_t* offsets,
             const void* w_in, const void* b_in, const void* w_out, const void* b_out, void* y_perm, void* ws,
-            hipStream_t st) {
+            hipStream_t st, const int32_t* gather = nullptr) {
     const FfnWs w = ffn_ws(s);
     void* h = at<void>(ws, w.h);
     float* partials = partials_of(ws, w.partials, s);
     const int per = ffn_experts_per_chunk(s, e_end - e_begin);
     for (int e0 = e_begin; e0 < e_end; e0 += per) {
         const int e1 = e_end - e0 > per ? e0 + per : e_end;
-        do_up(s, e0, e1, x_perm, offsets, w_in, b_in, h, partials, st);
+        do_up(s, e0, e1, x_perm, offsets, w_in, b_in, h, partials, st, gather);
         do_down(s, e0, e1, h, offsets, w_out, b_out, y_perm, partials, st);
     }
 }
@@ -660,11 +673,17 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router, co
     void* scratch = at<void>(ws, w.scratch);
     int32_t* offsets = at<int32_t>(ws, w.offsets);
     int32_t* inv_pos = at<int32_t>(ws, w.inv_pos);
-    do_route(shape, x, w_router, sel_bias, nullptr, idx, gw, cnt, stats_out, scratch, st);
-    do_permute(shape, idx, x, offsets, at<int32_t>(ws, w.sorted_token), inv_pos, at<void>(ws, w.x_perm), scratch,
-               st);
-    do_ffn(shape, 0, shape->E, at<void>(ws, w.x_perm), offsets, w_in, b_in, w_out, b_out, at<void>(ws, w.y_perm),
-           scratch, st);
+    do_route(shape, x, w_router, sel_bias, nullptr, idx, gw, cnt, stats_out, scratch, st, at<int32_t>(ws, w.ticket));
+    int32_t* sorted_token = at<int32_t>(ws, w.sorted_token);
+    if (fwd_gathers(shape)) {  // positions only; the up projection gathers the token rows itself
+        do_permute(shape, idx, x, offsets, sorted_token, inv_pos, nullptr, scratch, st);
+        do_ffn(shape, 0, shape->E, x, offsets, w_in, b_in, w_out, b_out, at<void>(ws, w.y_perm), scratch, st,
+               sorted_token);
+    } else {
+        do_permute(shape, idx, x, offsets, sorted_token, inv_pos, at<void>(ws, w.x_perm), scratch, st);
+        do_ffn(shape, 0, shape->E, at<void>(ws, w.x_perm), offsets, w_in, b_in, w_out, b_out, at<void>(ws, w.y_perm),
+               scratch, st);
+    }
     void* ys = nullptr;
     if (shape->d_ff_shared > 0) {
         ys = at<void>(ws, w.ys);
@@ -683,6 +702,9 @@ int moe_backward(const moe_shape* shape, const void* x, const float* w_router, c
                  float* dws_in, float* dws_out, float* dlogits, void* ws, size_t ws_bytes, moe_stream_t stream) {
     const int rc = check_shape(shape);
     if (rc != MOE_OK) return rc;
+    // the backward's bf16 products and transposes tile d_model and the hidden sizes by 64
+    if (shape->dtype == MOE_BF16 && (shape->d_model % 64 || shape->d_ff % 64 || shape->d_ff_shared % 64))
+        return MOE_ERR_UNSUPPORTED;
     MOE_REQUIRE(ok_ptr(x) && ok_ptr(w_router) && ok_ptr(w_in) && ok_ptr(w_out) && ok_ptr(logits) && ok_ptr(topk_idx) &&
                 ok_ptr(topk_w) && ok_ptr(offsets) && ok_ptr(inv_pos) && ok_ptr(x_perm) && ok_ptr(y_perm) &&
                 ok_ptr(dy));

@@ -73,9 +73,15 @@ def ws_bytes(shape, stage):
     (dict(k=9), L.MOE_ERR_INVALID_ARG),  # k > E
     (dict(E=64, k=33), L.MOE_ERR_INVALID_ARG),
     (dict(d_model=0), L.MOE_ERR_INVALID_ARG),
-    (dict(d_model=96), L.MOE_ERR_UNSUPPORTED),  # bf16 needs multiples of 64
-    (dict(d_ff=100), L.MOE_ERR_UNSUPPORTED),
-    (dict(dtype="f32", d_model=6), L.MOE_ERR_UNSUPPORTED),
+    # bf16 rows are 16-byte vectors of 8 elements, fp32 ones of 4
+    (dict(d_model=72), L.MOE_OK),
+    (dict(d_ff=200), L.MOE_OK),
+    (dict(d_model=72, d_ff=200, d_ff_shared=40), L.MOE_OK),
+    (dict(d_model=100), L.MOE_ERR_INVALID_ARG),
+    (dict(d_ff=100), L.MOE_ERR_INVALID_ARG),
+    (dict(d_ff_shared=12), L.MOE_ERR_INVALID_ARG),
+    (dict(dtype="f32", d_model=6), L.MOE_ERR_INVALID_ARG),
+    (dict(dtype="f32", d_model=12, d_ff=20), L.MOE_OK),
     (dict(score="sigmoid", renorm=False), L.MOE_ERR_UNSUPPORTED),
     (dict(T=2**31, k=2), L.MOE_ERR_INVALID_ARG),  # T*k overflows int32
 ])
@@ -291,6 +297,12 @@ def test_backward_rejections(lib):
     # x_perm, y_perm, dy, aux_coef, dx, dw_r, dw_in, db_in, dw_out, db_out, dws_in, dws_out, dlogits, ws, bytes, st
     good = [ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, None, None, None, FAKE, FAKE, FAKE, None, FAKE, FAKE,
             FAKE, FAKE, FAKE, 0.0, FAKE, FAKE, FAKE, None, FAKE, None, None, None, None, FAKE, n, None]
+    # bf16 widths that are not multiples of 64: the forward takes them, the backward does not
+    rag = good_shape(d_model=72)
+    bad = list(good)
+    bad[0] = ctypes.byref(rag)
+    bad[-2] = ws_bytes(rag, L.MOE_STAGE_BACKWARD)[1]
+    assert f(*bad) == L.MOE_ERR_UNSUPPORTED
     for i in (1, 2, 3, 5, 9, 10, 11, 13, 14, 15, 16, 17, 19, 20, 21, 23):  # required pointers
         bad = list(good)
         bad[i] = None

@@ -24,6 +24,9 @@ CASES = {
     "qwen_T8192": I.mini("qwen3_30b_a3b", T=8192, d=128, F=64),
     "qwen_mini": I.mini("qwen3_30b_a3b", T=2000, d=256, F=192),
     "deepseek_mini": I.mini("deepseek_v3", T=500, d=448, F=128, Fs=192),
+    # d = 200 (a multiple of 8, not of 32): both projections through the router GEMM with a masked last
+    # K stage, then the noisy selection
+    "ragged_E8_d200": I.mini("mixtral_prefill", T=700, d=200, F=136),
 }
 
 

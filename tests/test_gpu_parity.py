@@ -79,6 +79,22 @@ CASES = {
     "sigmoid_bias_E16_fused_T8200": I.mini("small_bf16", T=8200, d=512, F=64, router="biased", score="sigmoid"),
     # no renormalisation with a bias: gates are the raw full-softmax probabilities of the chosen experts
     "softmax_bias_norenorm_E16": I.mini("small_bf16", T=700, d=256, F=64, router="biased", renorm=False),
+    # bf16 widths that are multiples of 8 but not of the kernels' K stages (the last stage's weight
+    # chunks past K read as zeros); widths not a multiple of 32 route through the router GEMM.
+    # Wide-K kernel (groups of about 2100 rows): K = 136 and 200 (both 8 past a 64-wide stage)
+    "ragged_wide_swiglu": I.mini("mixtral_prefill", T=8400, d=136, F=200),
+    # ... and K = 96 / 160 (32 past a 64-wide stage) with the fused E <= 16 route (d a multiple of 32)
+    "ragged_wide_k32": I.mini("mixtral_prefill", T=8400, d=96, F=160),
+    # eight-wave persistent kernel (groups of about 125 rows), 32-wide stages: K = 264 and 328
+    "ragged_persistent": I.mini("small_bf16", T=1000, d=264, F=328),
+    # GELU with biases, 6 experts, d = 72 and F = 200
+    "ragged_gelu_bias": TINY.with_sizes(dtype="bf16", T=300, d=72, F=200, E=6, k=2),
+    # decode-sized groups on the 64-row kernel: K = 200 and 456
+    "ragged_decode": I.mini("mixtral_prefill", T=64, d=200, F=456),
+    # 40 experts (the router GEMM instead of the logits kernel) with d = 136
+    "ragged_router_E40": I.mini("small_bf16", T=555, d=136, F=128, E=40, k=4),
+    # sigmoid + bias over 256 experts with a shared expert: router and shared K = 200, shared down K = 72
+    "ragged_deepseek_shared": I.mini("deepseek_v3", T=500, d=200, F=136, Fs=72),
 }
 
 
