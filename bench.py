@@ -60,6 +60,8 @@ def stage_bytes_flops(cfg, used_experts=None):
         "route": dict(bytes=T * d * b + E * d * 4 + A * 8 + E * 4),
         # top-k indices, x once, x_perm, sorted_token + inv_pos, offsets
         "permute": dict(bytes=A * 4 + T * d * b + A * d * b + 2 * A * 4 + (E + 1) * 4),
+        # the forward's form: top-k indices, sorted_token + inv_pos, offsets (no row copy)
+        "permute_positions": dict(bytes=A * 4 + 2 * A * 4 + (E + 1) * 4),
         "expert_up": dict(flops=2.0 * A * d * gemm1_n,
                           bytes=nu * (gemm1_n * d + (F if bias else 0)) * b + A * d * b + A * F * b),
         "expert_down": dict(flops=2.0 * A * F * d, bytes=nu * (d * F + (d if bias else 0)) * b + A * F * b + A * d * b),
@@ -120,8 +122,14 @@ def main():
     L.route()
     L.permute()
     torch.cuda.synchronize()
-    stage_calls = [("route", lambda: L.route(with_logits=False)), ("permute", L.permute), ("expert_up", L.up),
-                   ("expert_down", L.down)]
+    from sparse_routing_expert_amd import _lib as LIB
+
+    def permute_positions():  # the forward's permute: positions only, the up projection gathers x's rows
+        LIB.moe_permute(L.shape, L.topk_idx, L.t["x"], L.offsets, L.sorted_token, L.inv_pos, None,
+                        L.ws(LIB.MOE_STAGE_PERMUTE))
+
+    stage_calls = [("route", lambda: L.route(with_logits=False)), ("permute", L.permute),
+                   ("permute_positions", permute_positions), ("expert_up", L.up), ("expert_down", L.down)]
     if cfg.Fs:
         stage_calls.append(("shared", L.shared))
     stage_calls.append(("combine", L.combine))

@@ -186,7 +186,10 @@ int moe_route_noisy(const moe_shape* shape, const void* x, const float* w_router
  *   sorted_token [T*k]         int32  out: row p < offsets[E] of x_perm holds token sorted_token[p]
  *   inv_pos      [T*k]         int32  out: assignment (t, j) sits at row inv_pos[t*k + j], or -1
  *                                     when it was dropped
- *   x_perm       [T*k, d_model] dtype out: x_perm[p] = x[sorted_token[p]] for p < offsets[E]
+ *   x_perm       [T*k, d_model] dtype out: x_perm[p] = x[sorted_token[p]] for p < offsets[E];
+ *                                     or NULL: positions only (offsets, sorted_token, inv_pos), the
+ *                                     form moe_forward uses, whose up projection reads x's rows
+ *                                     through sorted_token itself
  * Within an expert's segment rows are ordered by ascending t*k + j. Expert capacity
  * (shape->capacity = C > 0; "Router Optimization Techniques", Why It Matters 3 and FAQ 6, with
  * C = ceil(capacity factor * T * k / E); "Mixture of Experts" tutorial, The capacity factor

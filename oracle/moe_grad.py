@@ -197,19 +197,25 @@ def layer_backward(x, w_r, get_expert, k: int, act: str, score: str, renorm: boo
 
 
 def tokens_backward(x_rows, w_r, idx_rows: np.ndarray, logits_rows: np.ndarray, get_expert, act: str, score: str,
-                    renorm: bool, ws_in, ws_out, dy_rows, dl_extra: Optional[np.ndarray] = None):
+                    renorm: bool, ws_in, ws_out, dy_rows, dl_extra: Optional[np.ndarray] = None,
+                    return_term_ssq: bool = False):
     """dx and the router-logit gradient of a subset of tokens, given their selection and logits.
 
     Without capacity and with the balancing term's f held constant, token t's gradients depend only
     on its own x, dy and routing, so sampled tokens of a large layer are evaluated directly: for each
     expert the sample uses, the FFN and its backward on the sampled rows routed to it (one expert
     converted to float64 at a time). dl_extra [S, E] is added to the logit gradient before it
-    reaches dx (the balancing term's rows, which need the whole layer's counts)."""
+    reaches dx (the balancing term's rows, which need the whole layer's counts).
+
+    return_term_ssq: also return, per token, the sum of the squared norms of the terms dx adds up
+    (one per selected expert, the shared expert's, the router's) -- the scale of a sum whose terms
+    may cancel. The gradients themselves are the same either way."""
     x_rows, dy_rows, w_r = R.f64(x_rows), R.f64(dy_rows), R.f64(w_r)
     S, k = idx_rows.shape
     g = R.gates(logits_rows, idx_rows, score, renorm)
     dg = np.zeros((S, k))
     dx = np.zeros(x_rows.shape)
+    ssq = np.zeros(S)
     for e in np.unique(idx_rows):
         rows, slots = np.nonzero(idx_rows == e)
         wi, bi, wo, bo = get_expert(int(e))
@@ -217,12 +223,18 @@ def tokens_backward(x_rows, w_r, idx_rows: np.ndarray, logits_rows: np.ndarray, 
         dg[rows, slots] = np.sum(dy_rows[rows] * Y, axis=1)
         dX = expert_backward(x_rows[rows], wi, bi, wo, bo, act, g[rows, slots][:, None] * dy_rows[rows])[0]
         np.add.at(dx, rows, dX)
+        np.add.at(ssq, rows, np.sum(dX * dX, axis=1))
     if ws_in is not None:
-        dx = dx + expert_backward(x_rows, R.f64(ws_in), None, R.f64(ws_out), None, "swiglu", dy_rows)[0]
+        dXs = expert_backward(x_rows, R.f64(ws_in), None, R.f64(ws_out), None, "swiglu", dy_rows)[0]
+        dx = dx + dXs
+        ssq = ssq + np.sum(dXs * dXs, axis=1)
     dl = gate_backward(logits_rows, idx_rows, score, renorm, dg)
     if dl_extra is not None:
         dl = dl + dl_extra
-    return dx + dl @ w_r, dl
+    dr = dl @ w_r
+    if return_term_ssq:
+        return dx + dr, dl, ssq + np.sum(dr * dr, axis=1)
+    return dx + dr, dl
 
 
 def expert_backward_features(X, w_in, b_in, w_out, b_out, act: str, dY, feats: np.ndarray):

@@ -539,7 +539,7 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const void* x, 
     const int rc = check_shape(shape);
     if (rc != MOE_OK) return rc;
     MOE_REQUIRE(ok_ptr(topk_idx) && ok_ptr(x) && ok_ptr(offsets) && ok_ptr(sorted_token) && ok_ptr(inv_pos) &&
-                ok_ptr(x_perm) && ok_opt(ws));
+                ok_opt(x_perm) && ok_opt(ws));
     if (ws_bytes < perm_ws(shape).bytes || (ws == nullptr && perm_ws(shape).bytes > 0)) return MOE_ERR_WORKSPACE;
     if (shape->T == 0) return MOE_OK;
     (void)hipGetLastError();

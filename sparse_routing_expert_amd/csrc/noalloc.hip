@@ -60,7 +60,7 @@ extern "C" int moe_permute_noalloc(const moe_shape* shape, const int32_t* topk_i
     const int rc = moe_workspace_bytes(shape, MOE_STAGE_PERMUTE, &need);
     if (rc != MOE_OK) return rc;
     if (!(ok_ptr(topk_idx) && ok_ptr(x) && ok_ptr(offsets) && ok_ptr(sorted_token) && ok_ptr(inv_pos) &&
-          ok_ptr(x_perm)))
+          (x_perm == nullptr || ok_ptr(x_perm))))
         return MOE_ERR_INVALID_ARG;
     if (need > kScratchBytes) return MOE_ERR_WORKSPACE;
     if (shape->T == 0) return MOE_OK;

@@ -195,8 +195,35 @@ def check_sampled_restrictions(G, cases=range(10)):
                 assert err <= 1e-12 * (1.0 + np.max(np.abs(ref))), (i, e, what, err)
 
 
+def check_term_ssq(G, cases=range(8)):
+    """tokens_backward's optional per-token sum of squared term norms: asking for it leaves dx and
+    the logit gradient unchanged; with one expert, k = 1 and no shared expert the gate is constantly 1,
+    so the logit gradient is zero and dx is the single expert term (ssq = ||dx||^2 exactly); and in
+    general the Cauchy-Schwarz bound ||dx||^2 <= (terms) * ssq holds (k experts, shared, router)."""
+    for i in cases:
+        c = _case(i, seed_base=9000)
+        r = R.route(c["x"], c["w_r"], c["k"], c["score"], c["renorm"], c["sel_bias"])
+        args = (c["x"], c["w_r"], r.idx, r.logits, _getter(c), c["act"], c["score"], c["renorm"], c["ws_in"],
+                c["ws_out"], c["dy"])
+        dx0, dl0 = G.tokens_backward(*args)
+        dx, dl, ssq = G.tokens_backward(*args, return_term_ssq=True)
+        assert np.array_equal(dx, dx0) and np.array_equal(dl, dl0), i
+        n_terms = c["k"] + 1 + (1 if c["ws_in"] is not None else 0)
+        assert (np.sum(dx * dx, axis=1) <= n_terms * ssq * (1 + 1e-12)).all(), i
+        assert (ssq >= 0).all()
+    for act in ("gelu", "swiglu"):
+        c = tiny_case(9100, T=6, d=4, F=3, E=1, k=1, act=act, score="softmax", renorm=True, bias=False, shared=False)
+        dy = np.random.default_rng(9101).standard_normal((6, 4))
+        r = R.route(c["x"], c["w_r"], 1, "softmax", True)
+        dx, dl, ssq = G.tokens_backward(c["x"], c["w_r"], r.idx, r.logits, _getter(c), act, "softmax", True, None,
+                                        None, dy, return_term_ssq=True)
+        assert np.abs(dl).max() == 0.0
+        assert np.allclose(ssq, np.sum(dx * dx, axis=1), rtol=1e-14, atol=0), act
+
+
 ALL_GRAD_CHECKS = [
     ("finite_differences", check_finite_differences),
     ("autograd", check_autograd),
     ("sampled_restrictions", check_sampled_restrictions),
+    ("term_ssq", check_term_ssq),
 ]

@@ -139,6 +139,16 @@ def check_layer(cfg, y_gpu, y_ref):
     return float(err.max())
 
 
+def sum_rel_l2(got, ref, term_ssq) -> np.ndarray:
+    """Per-row ||got - ref|| / max(||ref||, sqrt(term_ssq)): the relative error of a row that is a
+    sum of terms, measured against the larger of the sum and the root-sum-square of its terms."""
+    g, r = np64(got), np64(ref)
+    assert np.isfinite(g).all(), "non-finite values"
+    num = np.linalg.norm(g - r, axis=1)
+    den = np.maximum(np.linalg.norm(r, axis=1), np.sqrt(np.asarray(term_ssq, dtype=np.float64)))
+    return num / np.maximum(den, 1e-300)
+
+
 def grad_err(got, ref, blocks: int, what: str, tol: float) -> float:
     """Block-wise gradient comparison (see the module notes); returns the largest block error."""
     g = np64(got).reshape(blocks, -1)

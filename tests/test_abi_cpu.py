@@ -184,10 +184,13 @@ def test_permute_combine_rejections(lib):
     n = ws_bytes(s, L.MOE_STAGE_PERMUTE)[1]
     p = lib.moe_permute
     good = [ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n, None]
-    for i in range(1, 7):
+    for i in range(1, 6):
         bad = list(good)
         bad[i] = None
         assert p(*bad) == L.MOE_ERR_INVALID_ARG
+    bad = list(good)
+    bad[6] = MISALIGNED  # x_perm may be NULL (positions only) but not misaligned
+    assert p(*bad) == L.MOE_ERR_INVALID_ARG
     bad = list(good)
     bad[8] = 0
     assert p(*bad) == L.MOE_ERR_WORKSPACE
@@ -205,8 +208,9 @@ def test_permute_noalloc_rejections(lib):
     good = [ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None]
     for i in range(1, 7):
         bad = list(good)
-        bad[i] = None
-        assert p(*bad) == L.MOE_ERR_INVALID_ARG
+        if i < 6:  # x_perm (6) may be NULL: positions only
+            bad[i] = None
+            assert p(*bad) == L.MOE_ERR_INVALID_ARG
         bad[i] = MISALIGNED
         assert p(*bad) == L.MOE_ERR_INVALID_ARG
     assert p(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG

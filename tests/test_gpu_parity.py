@@ -223,3 +223,33 @@ def test_up_down_equal_grouped_ffn():
     L.down()
     torch.cuda.synchronize()
     assert torch.equal(L.y_perm.view(torch.int16), y1.view(torch.int16))
+
+
+@pytest.mark.parametrize("name,cfg", [
+    ("small_index_path", I.mini("mixtral_prefill", T=700, d=256, F=64)),
+    ("tiled_folded", I.mini("mixtral_prefill", T=9000, d=128, F=64)),
+    ("tiled_scan", I.mini("qwen3_30b_a3b", T=3000, d=128, F=64)),
+    ("capacity", I.mini("qwen3_30b_a3b", T=2500, d=128, F=64)),
+])
+def test_permute_positions_only(name, cfg):
+    """moe_permute with x_perm = NULL (the forward's form) writes the same offsets, sorted_token and
+    inv_pos, bit for bit, as with the row copy, and touches no x_perm row."""
+    from sparse_routing_expert_amd import _lib as LIB
+
+    cap = R.capacity_rows(cfg.T, cfg.k, cfg.E, 1.0) if name == "capacity" else 0
+    L = MoeLayer(cfg, I.gen_layer(cfg, device="cuda"), capacity=cap)
+    poison(L)
+    L.route()
+    L.permute()
+    torch.cuda.synchronize()
+    ref = {n: getattr(L, n).clone() for n in ("offsets", "sorted_token", "inv_pos")}
+    for n in ref:
+        getattr(L, n).fill_(-7)
+    L.x_perm.fill_(float("nan"))
+    LIB.moe_permute(L.shape, L.topk_idx, L.t["x"], L.offsets, L.sorted_token, L.inv_pos, None,
+                    L.ws(LIB.MOE_STAGE_PERMUTE))
+    torch.cuda.synchronize()
+    for n, v in ref.items():
+        assert torch.equal(getattr(L, n), v), n
+    assert torch.isnan(L.x_perm.float()).all()
+    print(f"[permute positions] {name}: ok rows={int(ref['offsets'][-1].item())}", flush=True)
