@@ -22,15 +22,11 @@
  * ---------------------------------------
  * Memory:    every pointer argument is caller-owned DEVICE memory of the current
  *            HIP device (except `shape`, which is host memory). The library never
- *            allocates, frees or synchronises and keeps no state of its own between
- *            calls; scratch comes only from the caller's workspace `ws` of `ws_bytes`
- *            bytes, sized by moe_workspace_bytes(). The one exception is
- *            moe_permute_noalloc, whose scratch is a fixed array inside the library.
- * Workspace: the workspaces of moe_route, moe_route_noisy and moe_forward carry a
- *            completion counter between calls: zero each such workspace once after
- *            allocating it (hipMemset, torch.zeros); every call leaves the counter at
- *            zero again. Between two calls that share one, write nothing else into it.
- *            The other stages' workspaces need no initialisation.
+ *            allocates, frees or synchronises and keeps no state between calls;
+ *            scratch comes only from the caller's workspace `ws` of `ws_bytes`
+ *            bytes, sized by moe_workspace_bytes(), which needs no initialisation.
+ *            The one exception is moe_permute_noalloc, whose scratch is a fixed
+ *            array inside the library.
  * Layout:    row-major everywhere. Weights use the Linear [out, in] layout, so
  *            both operands of every product are contiguous along the reduced
  *            dimension. Expert weights are stacked along a leading expert axis.
@@ -121,9 +117,7 @@ typedef void* moe_stream_t; /* a hipStream_t */
 
 /* Scratch bytes a call needs. stage: MOE_STAGE_*. Writes the size to *bytes (a status and an
  * out-parameter rather than a bare size_t, so an invalid shape or stage is reported, not sized).
- * Returns MOE_ERR_INVALID_ARG for an invalid shape or stage, else MOE_OK. The MOE_STAGE_ROUTE,
- * MOE_STAGE_ROUTE_NOISY and MOE_STAGE_FORWARD workspaces must be zeroed once before first use
- * (see Workspace above). */
+ * Returns MOE_ERR_INVALID_ARG for an invalid shape or stage, else MOE_OK. */
 int moe_workspace_bytes(const moe_shape* shape, int stage, size_t* bytes);
 
 /* moe_route -- the router: logits, scores, per-token top-k, gates, counts, statistics.

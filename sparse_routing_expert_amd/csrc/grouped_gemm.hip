@@ -537,6 +537,12 @@ __device__ __forceinline__ float from_agpr(float x) {
     asm("v_accvgpr_read_b32 %0, %1" : "=v"(y) : "a"(x));
     return y;
 }
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, v);
+}
 template <int EPI, int TN, bool FENCE = false>
 __device__ __forceinline__ void store_block(const floatx16 (&a)[TN], int64_t row, int64_t row_end, int e,
                                             int fbase, int lane, uint16_t* __restrict__ C,
@@ -545,44 +551,62 @@ __device__ __forceinline__ void store_block(const floatx16 (&a)[TN], int64_t row
     constexpr int TNO = GATED ? TN / 2 : TN;
     const int khalf = lane >> 5;
     auto rd = [&](float x) { return FENCE ? from_agpr(x) : x; };
+    auto group = [&](int j, int q4, float (&o)[4]) {
+        const int f0 = fbase + j * 32 + 8 * q4 + 4 * khalf;
+        if (GATED) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float z = rd(a[j][4 * q4 + c]);
+                o[c] = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) * rd(a[j + TNO][4 * q4 + c]);
+            }
+        } else {
+            float bc[4] = {0.f, 0.f, 0.f, 0.f};
+            if (bias != nullptr && f0 < n_out) {
+                const uint2 bb = *reinterpret_cast<const uint2*>(bias + (int64_t)e * n_out + f0);
+                bc[0] = __uint_as_float(bb.x << 16);
+                bc[1] = __uint_as_float(bb.x & 0xffff0000u);
+                bc[2] = __uint_as_float(bb.y << 16);
+                bc[3] = __uint_as_float(bb.y & 0xffff0000u);
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float z = rd(a[j][4 * q4 + c]) + bc[c];
+                o[c] = EPI == EPI_GELU_BIAS ? gelu_f(z) : z;
+            }
+        }
+    };
 #pragma unroll
     for (int j = 0; j < TNO; ++j) {
+        if (EPI == EPI_F32) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const int f0 = fbase + j * 32 + 8 * q4 + 4 * khalf;
-            float o[4];
-            if (GATED) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const float z = rd(a[j][4 * q4 + c]);
-                    o[c] = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) * rd(a[j + TNO][4 * q4 + c]);
-                }
-            } else {
-                float bc[4] = {0.f, 0.f, 0.f, 0.f};
-                if (bias != nullptr && f0 < n_out) {
-                    const uint2 bb = *reinterpret_cast<const uint2*>(bias + (int64_t)e * n_out + f0);
-                    bc[0] = __uint_as_float(bb.x << 16);
-                    bc[1] = __uint_as_float(bb.x & 0xffff0000u);
-                    bc[2] = __uint_as_float(bb.y << 16);
-                    bc[3] = __uint_as_float(bb.y & 0xffff0000u);
-                }
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const float z = rd(a[j][4 * q4 + c]) + bc[c];
-                    o[c] = EPI == EPI_GELU_BIAS ? gelu_f(z) : z;
-                }
-            }
-            if (EPI == EPI_F32) {
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int f0 = fbase + j * 32 + 8 * q4 + 4 * khalf;
                 if (row < row_end && f0 < n_out)
                     *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(C) + row * n_out + f0) =
                         floatx4{rd(a[j][4 * q4]), rd(a[j][4 * q4 + 1]), rd(a[j][4 * q4 + 2]), rd(a[j][4 * q4 + 3])};
-                continue;
             }
-            if (row < row_end && f0 < n_out) {
-                uint2 pk;
-                pk.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
-                    pk.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
-                *reinterpret_cast<uint2*>(C + row * n_out + f0) = pk;
+            continue;
+        }
+        // groups q4 = 2 qp and 2 qp + 1: a lane holds features 16 qp + 8 q + 4 khalf + [0, 4) of each; one
+        // swap between the wave's halves leaves lane l < 32 with features 16 qp + [0, 8) and lane l + 32
+        // with 16 qp + [8, 16) of the same token, so each lane writes 16 contiguous bytes
+#pragma unroll
+        for (int qp = 0; qp < 2; ++qp) {
+            float oP[4], oQ[4];
+            group(j, 2 * qp, oP);
+            group(j, 2 * qp + 1, oQ);
+            const auto s0 = __builtin_amdgcn_permlane32_swap(pack2_bf16(oP[0], oP[1]), pack2_bf16(oQ[0], oQ[1]),
+                                                             false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(pack2_bf16(oP[2], oP[3]), pack2_bf16(oQ[2], oQ[3]),
+                                                             false, false);
+            const int f = fbase + j * 32 + 16 * qp + 8 * khalf;
+            if (row < row_end && f < n_out) {
+                uint4 pk;
+                pk.x = s0[0];
+                pk.y = s1[0];
+                pk.z = s0[1];
+                pk.w = s1[1];
+                *reinterpret_cast<uint4*>(C + row * n_out + f) = pk;
             }
             if (FENCE) __builtin_amdgcn_sched_barrier(0);
         }

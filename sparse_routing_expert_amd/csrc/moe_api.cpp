@@ -150,13 +150,12 @@ bool fwd_gathers(const moe_shape* s) {
 }
 
 struct FwdWs {
-    size_t ticket, topk_idx, topk_w, counts, offsets, sorted_token, inv_pos, x_perm, y_perm, ys, scratch, bytes;
+    size_t topk_idx, topk_w, counts, offsets, sorted_token, inv_pos, x_perm, y_perm, ys, scratch, bytes;
 };
 FwdWs fwd_ws(const moe_shape* s) {
     FwdWs w;
     Carver c;
     const size_t A = (size_t)s->T * s->k, eb = elem_bytes(s);
-    w.ticket = c.take(4);  // the route's completion ticket, apart from the scratch the later stages reuse
     w.topk_idx = c.take(A * 4);
     w.topk_w = c.take(A * 4);
     w.counts = c.take((size_t)s->E * 4);
@@ -237,21 +236,21 @@ void route_logits(const moe_shape* s, const RouteWs& w, const void* x, const flo
         moe::launch_route_logits(s->dtype, x, w_router, wsplit, w.Epad, lg, s->T, s->d_model, s->E, st);
 }
 
-// ticket_at: where the completion ticket lives (NULL: in ws). It is zero before and after every call.
 void do_route(const moe_shape* s, const void* x, const float* w_router, const float* sel_bias, float* logits,
-              int32_t* topk_idx, float* topk_w, int32_t* counts, float* stats, void* ws, hipStream_t st,
-              int32_t* ticket_at = nullptr) {
+              int32_t* topk_idx, float* topk_w, int32_t* counts, float* stats, void* ws, hipStream_t st) {
     const RouteWs w = route_ws(s);
     float* lg = logits && !w.gemm ? logits : at<float>(ws, w.logits);
     uint16_t* wsplit = s->dtype == MOE_BF16 ? at<uint16_t>(ws, w.wsplit) : nullptr;
-    int32_t* ticket = ticket_at ? ticket_at : at<int32_t>(ws, w.ticket);
+    int32_t* ticket = at<int32_t>(ws, w.ticket);
     int32_t* blk_counts = at<int32_t>(ws, w.blk_counts);
     float* blk_P = stats ? at<float>(ws, w.blk_P) : nullptr;
     float* blk_H = stats ? at<float>(ws, w.blk_H) : nullptr;
-    if (moe::route_small_ok(s->dtype, s->E, s->k, s->d_model)) {  // logits, selection and counts in one launch
+    if (moe::route_small_ok(s->dtype, s->E, s->k, s->d_model)) {  // logits and selection in one launch
+        const int nblk = (int)cdiv(s->T, moe::route_small_tokens_per_block(s->T, s->E, false));
         moe::launch_route_small(x, w_router, nullptr, nullptr, sel_bias, s->T, s->d_model, s->E, s->k, s->score,
-                                s->renorm, logits, topk_idx, topk_w, blk_counts, blk_P, blk_H, ticket, counts, stats,
-                                st);
+                                s->renorm, logits, topk_idx, topk_w, blk_counts, blk_P, blk_H, ticket, st);
+        moe::launch_route_finalize(blk_counts, blk_P, blk_H, nblk, s->T, s->E, counts, at<double>(ws, w.fp), ticket,
+                                   stats, st);
         return;
     }
     route_logits(s, w, x, w_router, wsplit, ticket, lg, ws, st);
@@ -276,10 +275,12 @@ void do_route_noisy(const moe_shape* s, const void* x, const float* w_router, co
     int32_t* blk_counts = at<int32_t>(ws, w.blk_counts);
     float* blk_P = stats ? at<float>(ws, w.blk_P) : nullptr;
     float* blk_H = stats ? at<float>(ws, w.blk_H) : nullptr;
-    if (moe::route_small_ok(s->dtype, s->E, s->k, s->d_model)) {  // both projections, selection, counts fused
+    if (moe::route_small_ok(s->dtype, s->E, s->k, s->d_model)) {  // both projections and the selection fused
+        const int nblk = (int)cdiv(s->T, moe::route_small_tokens_per_block(s->T, s->E, true));
         moe::launch_route_small(x, w_router, w_noise, noise, sel_bias, s->T, s->d_model, s->E, s->k, s->score,
-                                s->renorm, logits, topk_idx, topk_w, blk_counts, blk_P, blk_H, ticket, counts, stats,
-                                st);
+                                s->renorm, logits, topk_idx, topk_w, blk_counts, blk_P, blk_H, ticket, st);
+        moe::launch_route_finalize(blk_counts, blk_P, blk_H, nblk, s->T, s->E, counts, at<double>(ws, w.fp), ticket,
+                                   stats, st);
         return;
     }
     route_logits(s, w, x, w_router, wsplit, ticket, lg, ws, st);
@@ -673,7 +674,7 @@ int moe_forward(const moe_shape* shape, const void* x, const float* w_router, co
     void* scratch = at<void>(ws, w.scratch);
     int32_t* offsets = at<int32_t>(ws, w.offsets);
     int32_t* inv_pos = at<int32_t>(ws, w.inv_pos);
-    do_route(shape, x, w_router, sel_bias, nullptr, idx, gw, cnt, stats_out, scratch, st, at<int32_t>(ws, w.ticket));
+    do_route(shape, x, w_router, sel_bias, nullptr, idx, gw, cnt, stats_out, scratch, st);
     int32_t* sorted_token = at<int32_t>(ws, w.sorted_token);
     if (fwd_gathers(shape)) {  // positions only; the up projection gathers the token rows itself
         do_permute(shape, idx, x, offsets, sorted_token, inv_pos, nullptr, scratch, st);

@@ -29,16 +29,14 @@ void launch_route_select(const float* logits, int lg_ld, int lg_split, float* lo
 // x [T, d] . [hi; mid; lo]^T [3 Epad, d] through the grouped GEMM (fp32 output), split along K over
 // every CU; the select kernel sums the three products.
 constexpr int kRouteGemmMinEpad = 64;
-// Small routers (route_small_ok): logits (written to `logits` when given), selection, per-block
-// partials, and the counts and statistics (by the last block to finish) in one launch over blocks of
-// route_small_tokens_per_block(T, E, noisy) tokens. *ticket must be zero at launch and is zero again
-// when the launch ends.
+// Small routers (route_small_ok): logits (written to `logits` when given), selection and per-block
+// partials in one launch over blocks of route_small_tokens_per_block(T, E, noisy) tokens; zeroes *ticket.
 bool route_small_ok(int dtype, int E, int k, int d);
 int route_small_tokens_per_block(int64_t T, int E, bool noisy);
 void launch_route_small(const void* x, const float* w_router, const float* w_noise, const float* noise,
                         const float* sel_bias, int64_t T, int d, int E, int k, int score, int renorm, float* logits,
                         int32_t* topk_idx, float* topk_w, int32_t* blk_counts, float* blk_P, float* blk_H,
-                        int32_t* ticket, int32_t* counts, float* stats, hipStream_t s);
+                        int32_t* ticket, hipStream_t s);
 // counts[E] always; stats (f, P, aux, entropy) when stats != NULL
 void launch_route_finalize(const int32_t* blk_counts, const float* blk_P, const float* blk_H, int nblk, int64_t T,
                            int E, int32_t* counts, double* fp_scratch, int32_t* ticket, float* stats,

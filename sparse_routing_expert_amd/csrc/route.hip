@@ -370,11 +370,10 @@ __global__ __launch_bounds__(kSelWaves * 64) void route_select_kernel(const floa
     }
 }
 
-// Counts and statistics from the per-block partials, by one block of NWV waves (the standalone
-// single-block finalize, or the last block of the fused route): item i <= E (expert i, or the
-// entropy for i = E) goes to wave i % NWV; lane j of that wave sums blocks j, j + 64, ... in order
-// and the wave adds its lanes in a fixed tree (float64 for the statistics), so the result does not
-// depend on the wave count. Thread 0 then forms aux = E * sum_e f_e P_e in expert order.
+// Single-block form for routers of at most kFinalizeSmallExperts experts: item i <= E (expert i, or
+// the entropy for i = E) goes to wave i % NWV; lane j of that wave sums blocks j, j + 64, ... in
+// order and the wave adds its lanes in a fixed tree (float64 for the statistics). Thread 0 then forms
+// aux = E * sum_e f_e P_e in expert order. One launch and no cross-block ticket.
 constexpr int kFinalizeSmallExperts = 16;
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
@@ -399,8 +398,8 @@ __device__ __forceinline__ void finalize_small_block(const int32_t* __restrict__
             int cnt = 0;
             double acc = 0.0;
             for (int b = lane; b < nblk; b += 64) {
-                cnt += __builtin_nontemporal_load(blk_counts + (int64_t)b * E + it);
-                if (stats) acc += (double)__builtin_nontemporal_load(blk_P + (int64_t)b * E + it);
+                cnt += blk_counts[(int64_t)b * E + it];
+                if (stats) acc += (double)blk_P[(int64_t)b * E + it];
             }
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) cnt += __shfl_xor(cnt, o);
@@ -416,7 +415,7 @@ __device__ __forceinline__ void finalize_small_block(const int32_t* __restrict__
             }
         } else if (stats) {
             double acc = 0.0;
-            for (int b = lane; b < nblk; b += 64) acc += (double)__builtin_nontemporal_load(blk_H + b);
+            for (int b = lane; b < nblk; b += 64) acc += (double)blk_H[b];
             acc = wave_sum_f64(acc);
             if (lane == 0) stats[2 * E + 1] = (float)(acc * invT);
         }
@@ -443,10 +442,7 @@ __global__ __launch_bounds__(1024) void route_finalize_small_kernel(const int32_
 // but form the hi + mid + lo bf16 terms of the fp32 router in registers from fp32 loads (the same
 // roundings as route_prep_kernel, so the products and their order are the same). The wave partials
 // are summed in LDS in wave order, then each wave selects for its share of the block's tokens
-// (select_token, lane e holding expert e) and the block writes its partials. The last block to
-// finish (a ticket counter, zero at launch) then forms the counts and statistics from every block's
-// partials in a fixed order (finalize_small_block, so the result does not depend on which block is
-// last) and sets the ticket back to zero for the next call.
+// (select_token, lane e holding expert e) and the block writes its partials for route_finalize.
 // NOISY (noisy top-k gating, "Mixture of Experts" tutorial, Noisy top-k gating): the K loop runs a
 // second time with the noise-scale projection w_noise, and the selection uses
 // H = l + noise * softplus(x w_noise^T) in place of l (H is what logits_out receives).
@@ -457,7 +453,7 @@ __global__ __launch_bounds__(kFusedRouteWaves * 64) void route_fused_kernel(
     const float* __restrict__ noise, const float* __restrict__ sel_bias, int64_t T, int d, int E, int k, int score,
     int renorm, float* __restrict__ logits_out, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* __restrict__ blk_counts, float* __restrict__ blk_P, float* __restrict__ blk_H,
-    int32_t* __restrict__ ticket, int32_t* __restrict__ counts, float* __restrict__ stats) {
+    int32_t* __restrict__ ticket) {
     constexpr int NW = kFusedRouteWaves, TPB = 16 * TT, TPWV = TPB / NW, NP = NOISY ? 2 : 1;
     __shared__ floatx4 s_part[NP][NW][TT][64];
     __shared__ int s_cnt[64];
@@ -468,6 +464,7 @@ __global__ __launch_bounds__(kFusedRouteWaves * 64) void route_fused_kernel(
     constexpr int XI = TPB / 4;  // load instructions per 128-column step: 4 rows of 256 bytes each
     __shared__ u32x4 s_x[NW][TPB * 16];
     const int lane = lane_id(), wave = threadIdx.x >> 6;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0;  // for a route_finalize_kernel that follows
     if (threadIdx.x < 64) s_cnt[threadIdx.x] = 0;
     const int64_t t0 = (int64_t)blockIdx.x * TPB;
     const int r = lane & 15, g = lane >> 4;
@@ -671,19 +668,6 @@ __global__ __launch_bounds__(kFusedRouteWaves * 64) void route_fused_kernel(
         for (int wv = 1; wv < NW; ++wv) sh += s_H[wv];
         blk_H[blockIdx.x] = sh;
     }
-    // the last block to finish forms the counts and statistics
-    __shared__ bool s_last;
-    __shared__ double s_fp[kFinalizeSmallExperts];
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();  // this block's partials are visible device-wide before its ticket
-        s_last = atomicAdd(ticket, 1) == (int)gridDim.x - 1;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    finalize_small_block<NW>(blk_counts, blk_P, blk_H, (int)gridDim.x, T, E, counts, stats, s_fp);
-    if (threadIdx.x == 0) *ticket = 0;  // every other block has taken its ticket
 }
 
 bool route_small_ok(int dtype, int E, int k, int d) {
@@ -700,7 +684,7 @@ int route_small_tokens_per_block(int64_t T, int E, bool noisy) {
 void launch_route_small(const void* x, const float* w_router, const float* w_noise, const float* noise,
                         const float* sel_bias, int64_t T, int d, int E, int k, int score, int renorm, float* logits,
                         int32_t* topk_idx, float* topk_w, int32_t* blk_counts, float* blk_P, float* blk_H,
-                        int32_t* ticket, int32_t* counts, float* stats, hipStream_t s) {
+                        int32_t* ticket, hipStream_t s) {
     const bool noisy = w_noise != nullptr;
     const int tpb = route_small_tokens_per_block(T, E, noisy);
     const unsigned nblk = (unsigned)((T + tpb - 1) / tpb);
@@ -708,7 +692,7 @@ void launch_route_small(const void* x, const float* w_router, const float* w_noi
 #define MOE_ROUTE_FUSED(TT_, NOISY_)                                                                      \
     route_fused_kernel<TT_, NOISY_><<<nblk, kFusedRouteWaves * 64, 0, s>>>(                               \
         xb, w_router, w_noise, noise, sel_bias, T, d, E, k, score, renorm, logits, topk_idx, topk_w, blk_counts, \
-        blk_P, blk_H, ticket, counts, stats)
+        blk_P, blk_H, ticket)
     if (noisy) MOE_ROUTE_FUSED(1, true);
     else if (tpb == 32) MOE_ROUTE_FUSED(2, false);
     else MOE_ROUTE_FUSED(1, false);

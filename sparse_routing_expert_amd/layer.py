@@ -45,11 +45,9 @@ class MoeLayer:
         self._ws = {}
 
     def ws(self, stage: int) -> torch.Tensor:
-        """The stage's workspace, allocated once and zeroed (the route and forward workspaces carry a
-        completion counter that must be zero before their first use; the library leaves it zero)."""
         if stage not in self._ws:
             n = L.moe_workspace_bytes(self.shape, stage)
-            self._ws[stage] = torch.zeros((max(n, 1),), dtype=torch.uint8, device=self.dev)
+            self._ws[stage] = torch.empty((max(n, 1),), dtype=torch.uint8, device=self.dev)
         return self._ws[stage]
 
     # ---- stages -------------------------------------------------------------------------------
