@@ -175,12 +175,15 @@ __device__ __forceinline__ void wait_stages(int n) {
 }
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 // Byte offset of 16-byte chunk c of row R of a gathered tile (rows row0 + R of the group are tokens
-// gather[row0 + R] of A). Rows past the group's end read its last row, which the epilogue never
-// stores; the descriptor spans A, so every offset stays in range.
+// gather[row0 + R] of A). The descriptor spans A, which the host keeps below 2 GB; rows past the
+// group's end get an offset of 2 GB, out of the descriptor's range at every K stage, so they read as
+// zeros without a memory request (reading the group's last row instead cost a small group's tile as
+// many L2 requests again as its own rows: 128-row groups in 256-row tiles).
+constexpr uint32_t kGatherPastEnd = 0x80000000u;
 __device__ __forceinline__ int gathered_voff(const int32_t* __restrict__ gather, int64_t row0, int64_t row_end, int R,
                                              int K, int c) {
-    const int64_t p = row0 + R < row_end ? row0 + R : row_end - 1;
-    return (int)((uint32_t)gather[p] * (uint32_t)(K * 2) + (uint32_t)(c * 16));
+    if (row0 + R >= row_end) return (int)kGatherPastEnd;
+    return (int)((uint32_t)gather[row0 + R] * (uint32_t)(K * 2) + (uint32_t)(c * 16));
 }
 
 }  // namespace

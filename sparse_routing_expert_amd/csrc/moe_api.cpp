@@ -144,9 +144,9 @@ SharedWs shared_ws(const moe_shape* s) {
 }
 
 // bf16 forward: the up projection reads token rows through sorted_token (no x_perm copy) while x
-// fits one buffer descriptor's 32-bit byte range
+// stays below 2 GB, so that the offset the kernels give rows past a group's end lies out of range
 bool fwd_gathers(const moe_shape* s) {
-    return s->dtype == MOE_BF16 && s->T * (int64_t)s->d_model * 2 <= (int64_t)UINT32_MAX;
+    return s->dtype == MOE_BF16 && s->T * (int64_t)s->d_model * 2 < ((int64_t)1 << 31);
 }
 
 struct FwdWs {
