@@ -174,6 +174,7 @@ __device__ __forceinline__ void wait_stages(int n) {
     else wait_vm<6 * NQ>();
 }
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }  // 128-byte rows (wide kernel)
 // Byte offset of 16-byte chunk c of row R of a gathered tile (rows row0 + R of the group are tokens
 // gather[row0 + R] of A). The descriptor spans A, which the host keeps below 2 GB; rows past the
 // group's end get an offset of 2 GB, out of the descriptor's range at every K stage, so they read as
@@ -184,6 +185,45 @@ __device__ __forceinline__ int gathered_voff(const int32_t* __restrict__ gather,
                                              int K, int c) {
     if (row0 + R >= row_end) return (int)kGatherPastEnd;
     return (int)((uint32_t)gather[row0 + R] * (uint32_t)(K * 2) + (uint32_t)(c * 16));
+}
+// The same for the RPD rows r0 + [0, RPD) of one DMA instruction (64 / RPD lanes per row, r0 and the
+// tile wave-uniform; chunk c of row R at position c ^ swz(R) for 64-byte rows, c ^ swz8(R) for
+// 128-byte rows), read with scalar loads: the persistent kernels call this while their own LDS-DMA
+// loads are in flight, and a vector load here would make the wave wait for all of those before it
+// could use the index. The gather buffer holds at least 256 entries past its last row, so the RPD
+// reads stay inside it when the group ends within them. The lane id is recomputed here rather than
+// kept from the kernel's start, so the per-DMA chunk offsets need no registers (or spill slots)
+// across the main loop.
+__device__ __forceinline__ int lane_here() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+template <int RPD>
+__device__ __forceinline__ int gathered_voff_uniform(const int32_t* __restrict__ gather, int64_t row0,
+                                                     int64_t row_end, int r0, int K) {
+    constexpr int LPR = 64 / RPD;  // lanes per row
+    const int lane = lane_here();
+    const int R = r0 + lane / LPR;
+    const int c = (lane & (LPR - 1)) ^ (RPD == 16 ? swz(R) : swz8(R));
+    const int64_t base = ((int64_t)__builtin_amdgcn_readfirstlane((int)(row0 >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)row0);
+    // constant address space + readfirstlane: uniform loads the compiler must not fold into one
+    // per-lane vector load
+    typedef const __attribute__((address_space(4))) int32_t* cptr;
+    const cptr g = (cptr)(gather + base + __builtin_amdgcn_readfirstlane(r0));
+    const int i = lane / LPR;
+    int v = __builtin_amdgcn_readfirstlane(g[0]);
+#pragma unroll
+    for (int t = 1; t < RPD; ++t) {
+        const int gt = __builtin_amdgcn_readfirstlane(g[t]);
+        v = i == t ? gt : v;
+    }
+    // rows left in the group from the tile start, in 32 bits (a tile spans at most 256 rows)
+    const int64_t left64 = row_end - row0;
+    const int left = __builtin_amdgcn_readfirstlane(left64 > 4096 ? 4096 : (int)left64);
+    if (r0 + i >= left) return (int)kGatherPastEnd;
+    return (int)((uint32_t)v * (uint32_t)(K * 2) + (uint32_t)(c * 16));
 }
 
 }  // namespace
@@ -616,9 +656,18 @@ __device__ __forceinline__ void store_block(const floatx16 (&a)[TN], int64_t row
     }
 }
 
-// Epilogue of one wave's block of a tile (eight-wave layout): acc[i] is the row block of tokens
-// grp * 128 + wm * 64 + i * 32, features from n0 + wn * (TNO * 32).
-template <int EPI, int TM, int TN>
+// Eight-wave tile layouts. A wave (group grp, wm, wn) owns 64 tokens x TNO * 32 features (and, for
+// SwiGLU, the matching up features). 256-row tiles: the groups take tokens [0, 128) and [128, 256)
+// of the same features. 128-row tiles (R128): both groups take all 128 tokens, each its own half of
+// the tile's features.
+template <bool R128>
+__device__ __forceinline__ int wave_row_base(int grp, int wm) { return (R128 ? 0 : grp * 128) + wm * 64; }
+template <bool R128, int WTNO>
+__device__ __forceinline__ int wave_feat_base(int grp, int wn) { return (R128 ? grp * 2 * WTNO : 0) + wn * WTNO; }
+
+// Epilogue of one wave's block of a tile (eight-wave layouts): acc[i] is the row block of tokens
+// wave_row_base + i * 32, features from n0 + wave_feat_base.
+template <int EPI, int TM, int TN, bool R128>
 __device__ __forceinline__ void store_tile(const floatx16 (&acc)[TM][TN], int64_t row0, int64_t row_end, int e,
                                            int n0, int grp, int wm, int wn, int lane,
                                            uint16_t* __restrict__ C, const uint16_t* __restrict__ bias,
@@ -626,14 +675,14 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[TM][TN], int64_
     constexpr int TNO = EPI == EPI_SWIGLU ? TN / 2 : TN, WTNO = TNO * 32;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
-        store_block<EPI, TN>(acc[i], row0 + grp * 128 + wm * 64 + i * 32 + (lane & 31), row_end, e, n0 + wn * WTNO,
-                             lane, C, bias, n_out);
+        store_block<EPI, TN>(acc[i], row0 + wave_row_base<R128>(grp, wm) + i * 32 + (lane & 31), row_end, e,
+                             n0 + wave_feat_base<R128, WTNO>(grp, wn), lane, C, bias, n_out);
 }
 
 // Partial buffer: a header, then the fp32 accumulators of each tile slice as
 // [slot][wave][i][j][v / 4][lane] float4 (each store and load moves 1 KB per wave instruction).
 // Header: per XCD {rem, S} of its split last round, and per tail tile {row0, row_end, e, n0}.
-constexpr int kPartialFloats = 256 * 256;  // one 256 x 256 tile
+constexpr int kPartialFloats = 256 * 256;  // one 256 x 256 (or 128 x 512) tile
 constexpr int kMaxSlotsPerXcd = 64;        // nslots <= 64 (512 blocks)
 struct TailTile {
     int64_t row0, row_end;
@@ -665,18 +714,28 @@ __device__ __forceinline__ floatx4* partial_at(float* partials, uint32_t pslot, 
 // consecutive output features, written with one 8-byte store. Stores and LDS-DMA loads share the
 // vector-memory counter and may complete out of order, so the memory cluster after a tile's stores
 // waits for the counter to drain before it issues new loads.
-template <int EPI, int GM, int D, bool KT>
+//
+// R128: 128-token x 512-weight-row tiles for small expert groups (a few hundred rows or less, where
+// 256-row tiles are mostly padding): both groups multiply the same 128 tokens, each against its own
+// 256 weight rows, so a wave's block and the MFMA work per stage are those of the 256-row tile. A
+// stage is then 640 rows (40 KB), five DMA instructions per wave, and the ring holds D + 1 = 3
+// stages.
+template <int EPI, int GM, int D, bool KT, bool R128>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ C, const int32_t* __restrict__ offsets, int e_begin, int n_groups, int64_t dense_rows,
     int n_out, int K, float* __restrict__ partials, const int32_t* __restrict__ gather, uint32_t a_bytes) {
-    constexpr int BM = 256, BN = 256, BK = 32, NS = D + 1;
+    constexpr int BM = R128 ? 128 : 256, BN = R128 ? 512 : 256, BK = 32, NS = D + 1;
     constexpr bool GATED = EPI == EPI_SWIGLU;
     constexpr int TM = 2;  // 64 tokens per wave
-    constexpr int BNO = GATED ? BN / 2 : BN, WTNO = BNO / 2, TNO = WTNO / 32, TN = GATED ? 2 * TNO : TNO;
-    constexpr int STAGE_ELEMS = (BM + BN) * BK;  // 512 rows of 64 bytes
+    constexpr int BNO = GATED ? BN / 2 : BN, WTNO = R128 ? BNO / 4 : BNO / 2, TNO = WTNO / 32;
+    constexpr int TN = GATED ? 2 * TNO : TNO;
+    constexpr int STAGE_ELEMS = (BM + BN) * BK;  // 512 (R128: 640) rows of 64 bytes
     constexpr int STAGE_BYTES = STAGE_ELEMS * 2;
-    constexpr int NQ = 4;  // DMA instructions per wave per stage (a group moves 256 rows = 16 KB)
+    // DMA instructions per wave per stage, 16 rows each. 256-row tiles: group 0 moves the 256 token
+    // rows, group 1 the 256 weight rows. R128: instruction q of wave w moves stage rows
+    // (q * 8 + w) * 16 + [0, 16), so q = 0 covers the 128 token rows and q >= 1 the weight rows.
+    constexpr int NQ = R128 ? 5 : 4;
     static_assert(TN == 4 && D >= 2 && D <= 5, "tile shape");
     static_assert(NS * STAGE_BYTES + 2 * 1025 * 4 + 8 * 4 <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE_ELEMS];
@@ -720,65 +779,66 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
     const int64_t n_b_rows = GATED ? 2 * (int64_t)n_out : n_out;
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)lds;
 
-    // DMA q of this wave: LDS rows grp * 256 + (q * 4 + wig) * 16 + [0, 16); lane -> (row, chunk).
-    // Row offsets are relative to the tile's buffer descriptors, so they hold for every tile.
+    // DMA q of this wave: 16 stage rows (see NQ); lane -> (row, chunk). Row offsets are relative to
+    // the tile's buffer descriptors, so they hold for every tile.
+    // stage row of DMA q, this lane; whether it is a weight row; its row in its descriptor
+    auto dma_row0 = [&](int q) { return R128 ? (q * 8 + wave) * 16 : grp * 256 + (q * 4 + wig) * 16; };  // uniform
+    auto dma_row = [&](int q) { return dma_row0(q) + (lane >> 2); };
+    auto dma_is_b = [&](int q) { return R128 ? q >= 1 : grp == 1; };
+    auto dma_desc_row = [&](int q) {
+        const int R = dma_row(q);
+        if (!dma_is_b(q)) return R;
+        const int b = R - BM;  // weight row of the tile: gate rows, then (SwiGLU) the matching up rows
+        return GATED && b >= BNO ? b - BNO : b;
+    };
     int voff[NQ];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        const int Rl = (q * 4 + wig) * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ swz(grp * 256 + Rl);
-        const int row = (grp == 1 && GATED && q >= 2) ? Rl - 128 : Rl;
-        voff[q] = row * K * 2 + c * 16;
-    }
+    for (int q = 0; q < NQ; ++q) voff[q] = dma_desc_row(q) * K * 2 + ((lane & 3) ^ swz(dma_row(q))) * 16;
     // K not a multiple of BK (KT): the weight chunks of the last stage past K read as zeros
     int tor[NQ];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        const int Rl = (q * 4 + wig) * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ swz(grp * 256 + Rl);
-        tor[q] = KT && grp == 1 && c * 8 >= K - (nk - 1) * BK ? (int)0x80000000 : 0;
-    }
+    for (int q = 0; q < NQ; ++q)
+        tor[q] = KT && dma_is_b(q) && ((lane & 3) ^ swz(dma_row(q))) * 8 >= K - (nk - 1) * BK ? (int)0x80000000 : 0;
     // buffer descriptors of the tile whose stages are being loaded
     i32x4 rs[NQ];
     auto set_dma_tile = [&](uint32_t lin) {
         int64_t row0, row_end;
         int e, n0;
         ts.decode(lin, row0, row_end, e, n0);
-        if (grp == 0) {
+        if (R128 || grp == 0) {
             const int64_t a_rows = row_end - row0 < BM ? row_end - row0 : BM;
             const i32x4 ra = gather ? make_rsrc(A, a_bytes) : make_rsrc(A + row0 * K, (uint32_t)(a_rows * K * 2));
 #pragma unroll
-            for (int q = 0; q < NQ; ++q) rs[q] = ra;
-            if (gather) {  // gathered token rows: this tile's row offsets
-#pragma unroll
-                for (int q = 0; q < NQ; ++q) {
-                    const int Rl = (q * 4 + wig) * 16 + (lane >> 2);
-                    voff[q] = gathered_voff(gather, row0, row_end, Rl, K, (lane & 3) ^ swz(Rl));
+            for (int q = 0; q < NQ; ++q)
+                if (!dma_is_b(q)) {
+                    rs[q] = ra;
+                    if (gather)  // gathered token rows: this tile's row offsets
+                        voff[q] = gathered_voff_uniform<16>(gather, row0, row_end, dma_row0(q), K);
                 }
-            }
-        } else {
+        }
+        if (R128 || grp == 1) {
             const uint16_t* Bg = B + (int64_t)e * n_b_rows * K;
-            const int bn_part = GATED ? BN / 2 : BN;
-            const int bcols = n_out - n0 < bn_part ? n_out - n0 : bn_part;
+            const int bcols = n_out - n0 < BNO ? n_out - n0 : BNO;
             const i32x4 rb0 = make_rsrc(Bg + (int64_t)n0 * K, (uint32_t)((int64_t)bcols * K * 2));
             const i32x4 rb1 =
                 make_rsrc(Bg + (int64_t)(GATED ? n_out + n0 : n0) * K, (uint32_t)((int64_t)bcols * K * 2));
 #pragma unroll
-            for (int q = 0; q < NQ; ++q) rs[q] = (GATED && q >= 2) ? rb1 : rb0;
+            for (int q = 0; q < NQ; ++q)
+                if (dma_is_b(q)) rs[q] = (GATED && dma_row0(q) - BM >= BNO) ? rb1 : rb0;
         }
     };
 
     int a_off[TM], a_sw[TM], b_off[TN], b_sw[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-        const int r = grp * 128 + wm * 64 + i * 32 + (lane & 31);
+        const int r = wave_row_base<R128>(grp, wm) + i * 32 + (lane & 31);
         a_off[i] = r * BK;
         a_sw[i] = swz(r);
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         const int jj = j < TNO ? j : j - TNO;
-        const int r = BM + (GATED && j >= TNO ? BN / 2 : 0) + wn * WTNO + jj * 32 + (lane & 31);
+        const int r = BM + (GATED && j >= TNO ? BNO : 0) + wave_feat_base<R128, WTNO>(grp, wn) + jj * 32 + (lane & 31);
         b_off[j] = r * BK;
         b_sw[j] = swz(r);
     }
@@ -797,11 +857,11 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
     // in the unit
 #define PS_ISSUE(slot_, ks_)                                                                              \
     {                                                                                                     \
-        const uint32_t sbase = lds_base + (slot_) * STAGE_BYTES + grp * 16384 + wig * 1024;               \
+        const uint32_t sbase = lds_base + (slot_) * STAGE_BYTES + (R128 ? wave : grp * 16 + wig) * 1024;  \
         const int soff = (ks_) * (BK * 2);                                                                \
         const bool tail_ = KT && (ks_) == nk - 1;                                                         \
         _Pragma("unroll") for (int q = 0; q < NQ; ++q)                                                    \
-            dma16(sbase + q * 4096, tail_ ? (voff[q] | tor[q]) : voff[q], rs[q], soff);                   \
+            dma16(sbase + q * (R128 ? 8192 : 4096), tail_ ? (voff[q] | tor[q]) : voff[q], rs[q], soff);   \
     }
 #define PS_READ(slot_)                                                                                    \
     {                                                                                                     \
@@ -874,7 +934,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
                 int64_t row0, row_end;
                 int e, n0;
                 ts.decode(unit_lin(cmp_u), row0, row_end, e, n0);
-                store_tile<EPI, TM, TN>(acc, row0, row_end, e, n0, grp, wm, wn, lane, C, bias, n_out);
+                store_tile<EPI, TM, TN, R128>(acc, row0, row_end, e, n0, grp, wm, wn, lane, C, bias, n_out);
             } else {
                 floatx4* dst = partial_at<TM, TN>(partials, xcd * nslots + slot, wave);
 #pragma unroll
@@ -920,7 +980,6 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
 // out during the first two (one after every other MFMA), and the last step waits for them, passes the
 // stage barrier and reads the next stage's first fragments. K-split slices store their partial tiles
 // in the eight-wave layout that gemm_bf16_tail_kernel reads.
-__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 
 template <int EPI, int GM, bool KT>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
@@ -1001,8 +1060,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
             ra = make_rsrc(A, a_bytes);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                const int R = (q * 4 + wave) * 8 + (lane >> 3);
-                voff[q] = gathered_voff(gather, row0, row_end, R, K, (lane & 7) ^ swz8(R));
+                voff[q] = gathered_voff_uniform<8>(gather, row0, row_end, (q * 4 + wave) * 8, K);
             }
         } else {
             ra = make_rsrc(A + row0 * K, (uint32_t)(a_rows * K * 2));
@@ -1173,12 +1231,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
 // slice order and applies the epilogue. One thread per group of 4 consecutive output features of
 // one token (gate and up together for SwiGLU); block b covers XCD b % 8, tail tile (b / 8) / CH and
 // chunk (b / 8) % CH of that tile's groups (launch: 8 * nslots * CH blocks of 256 threads, nslots
-// the GEMM's blocks per XCD). Tile coordinates come from the header the GEMM wrote.
+// the GEMM's blocks per XCD). Tile coordinates come from the header the GEMM wrote; R128 is the
+// GEMM's tile layout.
 template <int EPI>
 constexpr int tail_chunks() {
     return 8 * 2 * (EPI == EPI_SWIGLU ? 2 : 4) * 4 * 64 / 256;  // (wave, i, j, v4, lane) groups / 256
 }
-template <int EPI>
+template <int EPI, bool R128>
 __global__ __launch_bounds__(256) void gemm_bf16_tail_kernel(const float* __restrict__ partials,
                                                              const uint16_t* __restrict__ bias,
                                                              uint16_t* __restrict__ C, int n_out, int nslots) {
@@ -1202,8 +1261,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_tail_kernel(const float* __rest
         z += src[((i * TN + j) * 4 + v4) * 64 + lane];
         if (GATED) u += src[((i * TN + j + TNO) * 4 + v4) * 64 + lane];
     }
-    const int64_t row = tt.row0 + grp * 128 + wm * 64 + i * 32 + (lane & 31);
-    const int f0 = tt.n0 + wn * WTNO + j * 32 + 8 * v4 + 4 * (lane >> 5);
+    const int64_t row = tt.row0 + wave_row_base<R128>(grp, wm) + i * 32 + (lane & 31);
+    const int f0 = tt.n0 + wave_feat_base<R128, WTNO>(grp, wn) + j * 32 + 8 * v4 + 4 * (lane >> 5);
     if (row >= tt.row_end || f0 >= n_out) return;
     if (EPI == EPI_F32) {
         *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(C) + row * n_out + f0) = z;
@@ -1244,13 +1303,14 @@ size_t gemm_partials_bytes(int dtype) {
     return kTailHeaderBytes + (size_t)persistent_grid_cap() * kPartialFloats * sizeof(float);
 }
 
-template <int GM, int D>
+template <int GM, int D, bool R128>
 void launch_bf16_persistent(int epi, const void* A, const void* B, const void* bias, void* C,
                             const int32_t* offsets, int e_begin, int n_groups, int64_t max_rows, int64_t dense_rows,
                             int n_out, int K, float* partials, hipStream_t s, const int32_t* gather,
                             uint32_t a_bytes) {
-    const int bno = epi == EPI_SWIGLU ? 128 : 256;
-    const int64_t m_tiles = offsets ? (max_rows + 255) / 256 + n_groups : (dense_rows + 255) / 256;
+    constexpr int bm = R128 ? 128 : 256;
+    const int bno = (epi == EPI_SWIGLU ? 128 : 256) * (R128 ? 2 : 1);
+    const int64_t m_tiles = offsets ? (max_rows + bm - 1) / bm + n_groups : (dense_rows + bm - 1) / bm;
     const int64_t tiles = m_tiles * ((n_out + bno - 1) / bno);
     if (tiles <= 0) return;
     const int64_t cap = persistent_grid_cap();
@@ -1266,14 +1326,14 @@ void launch_bf16_persistent(int epi, const void* A, const void* B, const void* b
 #define MOE_PERSIST(EPI_)                                                                                 \
     {                                                                                                     \
         if (K % 32)                                                                                       \
-            gemm_bf16_persistent_kernel<EPI_, GM, D, true><<<grid, 512, 0, s>>>(                          \
+            gemm_bf16_persistent_kernel<EPI_, GM, D, true, R128><<<grid, 512, 0, s>>>(                    \
                 a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out, K, partials, gather, a_bytes);  \
         else                                                                                              \
-            gemm_bf16_persistent_kernel<EPI_, GM, D, false><<<grid, 512, 0, s>>>(                         \
+            gemm_bf16_persistent_kernel<EPI_, GM, D, false, R128><<<grid, 512, 0, s>>>(                   \
                 a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out, K, partials, gather, a_bytes);  \
         if (partials)                                                                                     \
-            gemm_bf16_tail_kernel<EPI_><<<grid * tail_chunks<EPI_>(), 256, 0, s>>>(partials, bi, c, n_out,  \
-                                                                                  (int)(grid / 8));       \
+            gemm_bf16_tail_kernel<EPI_, R128><<<grid * tail_chunks<EPI_>(), 256, 0, s>>>(partials, bi, c,   \
+                                                                                        n_out, (int)(grid / 8)); \
     }
     if (epi == EPI_SWIGLU) MOE_PERSIST(EPI_SWIGLU)
     else if (epi == EPI_GELU_BIAS) MOE_PERSIST(EPI_GELU_BIAS)
@@ -1307,8 +1367,8 @@ void launch_bf16_wide(int epi, const void* A, const void* B, const void* bias, v
             gemm_bf16_wide_kernel<EPI_, GM, false><<<grid, 256, 0, s>>>(                                  \
                 a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out, K, partials, gather, a_bytes);  \
         if (partials)                                                                                     \
-            gemm_bf16_tail_kernel<EPI_><<<grid * tail_chunks<EPI_>(), 256, 0, s>>>(partials, bi, c, n_out,  \
-                                                                                  (int)(grid / 8));       \
+            gemm_bf16_tail_kernel<EPI_, false><<<grid * tail_chunks<EPI_>(), 256, 0, s>>>(partials, bi, c,  \
+                                                                                         n_out, (int)(grid / 8)); \
     }
     if (epi == EPI_SWIGLU) MOE_WIDE(EPI_SWIGLU)
     else if (epi == EPI_GELU_BIAS) MOE_WIDE(EPI_GELU_BIAS)
@@ -1461,9 +1521,12 @@ void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* 
             (max_rows >= kGemmWideRows * ng || (K >= kGemmWideMinK && max_rows >= kGemmWideRowsLongK * ng)))
             launch_bf16_wide<8>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows, n_out, K,
                                 partials, s, gather, a_bytes);
+        else if (offsets != nullptr && max_rows <= kGemmR128Rows * ng)
+            launch_bf16_persistent<8, 2, true>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows,
+                                               dense_rows, n_out, K, partials, s, gather, a_bytes);
         else
-            launch_bf16_persistent<8, 3>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows,
-                                         n_out, K, partials, s, gather, a_bytes);
+            launch_bf16_persistent<8, 3, false>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows,
+                                                dense_rows, n_out, K, partials, s, gather, a_bytes);
         return;
     }
     const int64_t m_tiles = offsets ? (max_rows + 63) / 64 + n_groups : (dense_rows + 63) / 64;

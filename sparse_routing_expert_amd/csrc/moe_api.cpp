@@ -160,7 +160,9 @@ FwdWs fwd_ws(const moe_shape* s) {
     w.topk_w = c.take(A * 4);
     w.counts = c.take((size_t)s->E * 4);
     w.offsets = c.take((size_t)(s->E + 1) * 4);
-    w.sorted_token = c.take(A * 4);
+    // the gathering GEMM reads sorted_token 16 rows at a time from a group's tile start, up to 255
+    // entries past the last row
+    w.sorted_token = c.take((A + 256) * 4);
     w.inv_pos = c.take(A * 4);
     w.x_perm = c.take(fwd_gathers(s) ? 0 : A * s->d_model * eb);
     w.y_perm = c.take(A * s->d_model * eb);

@@ -95,6 +95,15 @@ CASES = {
     "ragged_router_E40": I.mini("small_bf16", T=555, d=136, F=128, E=40, k=4),
     # sigmoid + bias over 256 experts with a shared expert: router and shared K = 200, shared down K = 72
     "ragged_deepseek_shared": I.mini("deepseek_v3", T=500, d=200, F=136, Fs=72),
+    # groups averaging more than 256 rows (and under the wide kernel's thresholds) keep the eight-wave
+    # kernel's 256-row tiles: SwiGLU, GELU with biases, and ragged K
+    "tiles256_swiglu": I.mini("small_bf16", T=1300, d=256, F=320, E=4, k=2),
+    "tiles256_gelu_bias": TINY.with_sizes(dtype="bf16", T=1400, d=192, F=320, E=2, k=1),
+    "tiles256_ragged": I.mini("small_bf16", T=1300, d=264, F=328, E=4, k=2),
+    # groups averaging 33 to 256 rows take 128-row tiles: Zipf-skewed groups (some far larger than
+    # 256 rows, several empty) with a long K, and GELU with biases
+    "tiles128_skewed_longK": I.mini("qwen3_30b_a3b", T=700, d=1536, F=96, E=32, k=4),
+    "tiles128_gelu_bias": TINY.with_sizes(dtype="bf16", T=700, d=192, F=320, E=6, k=2),
 }
 
 
