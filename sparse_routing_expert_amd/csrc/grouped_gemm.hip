@@ -720,7 +720,7 @@ __device__ __forceinline__ floatx4* partial_at(float* partials, uint32_t pslot, 
 // 256 weight rows, so a wave's block and the MFMA work per stage are those of the 256-row tile. A
 // stage is then 640 rows (40 KB), five DMA instructions per wave, and the ring holds D + 1 = 3
 // stages.
-template <int EPI, int GM, int D, bool KT, bool R128>
+template <int EPI, int GM, int D, bool KT, bool R128, bool GA>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ C, const int32_t* __restrict__ offsets, int e_begin, int n_groups, int64_t dense_rows,
@@ -807,12 +807,12 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
         ts.decode(lin, row0, row_end, e, n0);
         if (R128 || grp == 0) {
             const int64_t a_rows = row_end - row0 < BM ? row_end - row0 : BM;
-            const i32x4 ra = gather ? make_rsrc(A, a_bytes) : make_rsrc(A + row0 * K, (uint32_t)(a_rows * K * 2));
+            const i32x4 ra = GA ? make_rsrc(A, a_bytes) : make_rsrc(A + row0 * K, (uint32_t)(a_rows * K * 2));
 #pragma unroll
             for (int q = 0; q < NQ; ++q)
                 if (!dma_is_b(q)) {
                     rs[q] = ra;
-                    if (gather)  // gathered token rows: this tile's row offsets
+                    if (GA)  // gathered token rows: this tile's row offsets
                         voff[q] = gathered_voff_uniform<16>(gather, row0, row_end, dma_row0(q), K);
                 }
         }
@@ -981,7 +981,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
 // stage barrier and reads the next stage's first fragments. K-split slices store their partial tiles
 // in the eight-wave layout that gemm_bf16_tail_kernel reads.
 
-template <int EPI, int GM, bool KT>
+template <int EPI, int GM, bool KT, bool GA>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ C, const int32_t* __restrict__ offsets, int e_begin, int n_groups, int64_t dense_rows,
@@ -1056,7 +1056,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
         int e, n0;
         ts.decode(lin, row0, row_end, e, n0);
         const int64_t a_rows = row_end - row0 < BM ? row_end - row0 : BM;
-        if (gather) {  // gathered token rows: the descriptor spans A, the row offsets follow the tile
+        if (GA) {  // gathered token rows: the descriptor spans A, the row offsets follow the tile
             ra = make_rsrc(A, a_bytes);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
@@ -1323,14 +1323,25 @@ void launch_bf16_persistent(int epi, const void* A, const void* B, const void* b
     const auto b = static_cast<const uint16_t*>(B);
     const auto bi = static_cast<const uint16_t*>(bias);
     auto c = static_cast<uint16_t*>(C);
-#define MOE_PERSIST(EPI_)                                                                                 \
+#define MOE_PERSIST_GA(EPI_, GA_)                                                                          \
     {                                                                                                     \
         if (K % 32)                                                                                       \
-            gemm_bf16_persistent_kernel<EPI_, GM, D, true, R128><<<grid, 512, 0, s>>>(                    \
+            gemm_bf16_persistent_kernel<EPI_, GM, D, true, R128, GA_><<<grid, 512, 0, s>>>(               \
                 a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out, K, partials, gather, a_bytes);  \
         else                                                                                              \
-            gemm_bf16_persistent_kernel<EPI_, GM, D, false, R128><<<grid, 512, 0, s>>>(                   \
+            gemm_bf16_persistent_kernel<EPI_, GM, D, false, R128, GA_><<<grid, 512, 0, s>>>(              \
                 a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out, K, partials, gather, a_bytes);  \
+    }
+    // gathered rows only on the up projections (gated or GELU epilogues); the others build without
+    // the gather path
+#define MOE_PERSIST(EPI_)                                                                                 \
+    {                                                                                                     \
+        if constexpr (EPI_ == EPI_SWIGLU || EPI_ == EPI_GELU_BIAS) {                                      \
+            if (gather) MOE_PERSIST_GA(EPI_, true)                                                        \
+            else MOE_PERSIST_GA(EPI_, false)                                                              \
+        } else {                                                                                          \
+            MOE_PERSIST_GA(EPI_, false)                                                                   \
+        }                                                                                                 \
         if (partials)                                                                                     \
             gemm_bf16_tail_kernel<EPI_, R128><<<grid * tail_chunks<EPI_>(), 256, 0, s>>>(partials, bi, c,   \
                                                                                         n_out, (int)(grid / 8)); \
@@ -1340,6 +1351,7 @@ void launch_bf16_persistent(int epi, const void* A, const void* B, const void* b
     else if (epi == EPI_F32) MOE_PERSIST(EPI_F32)
     else MOE_PERSIST(EPI_BIAS)
 #undef MOE_PERSIST
+#undef MOE_PERSIST_GA
 }
 
 template <int GM>
@@ -1358,14 +1370,23 @@ void launch_bf16_wide(int epi, const void* A, const void* B, const void* bias, v
     const auto b = static_cast<const uint16_t*>(B);
     const auto bi = static_cast<const uint16_t*>(bias);
     auto c = static_cast<uint16_t*>(C);
-#define MOE_WIDE(EPI_)                                                                                      \
+#define MOE_WIDE_GA(EPI_, GA_)                                                                             \
     {                                                                                                     \
         if (K % 64)                                                                                       \
-            gemm_bf16_wide_kernel<EPI_, GM, true><<<grid, 256, 0, s>>>(                                   \
+            gemm_bf16_wide_kernel<EPI_, GM, true, GA_><<<grid, 256, 0, s>>>(                              \
                 a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out, K, partials, gather, a_bytes);  \
         else                                                                                              \
-            gemm_bf16_wide_kernel<EPI_, GM, false><<<grid, 256, 0, s>>>(                                  \
+            gemm_bf16_wide_kernel<EPI_, GM, false, GA_><<<grid, 256, 0, s>>>(                             \
                 a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out, K, partials, gather, a_bytes);  \
+    }
+#define MOE_WIDE(EPI_)                                                                                      \
+    {                                                                                                     \
+        if constexpr (EPI_ == EPI_SWIGLU || EPI_ == EPI_GELU_BIAS) {                                      \
+            if (gather) MOE_WIDE_GA(EPI_, true)                                                           \
+            else MOE_WIDE_GA(EPI_, false)                                                                 \
+        } else {                                                                                          \
+            MOE_WIDE_GA(EPI_, false)                                                                      \
+        }                                                                                                 \
         if (partials)                                                                                     \
             gemm_bf16_tail_kernel<EPI_, false><<<grid * tail_chunks<EPI_>(), 256, 0, s>>>(partials, bi, c,  \
                                                                                          n_out, (int)(grid / 8)); \
@@ -1375,6 +1396,7 @@ void launch_bf16_wide(int epi, const void* A, const void* B, const void* bias, v
     else if (epi == EPI_F32) MOE_WIDE(EPI_F32)
     else MOE_WIDE(EPI_BIAS)
 #undef MOE_WIDE
+#undef MOE_WIDE_GA
 }
 
 // fp32 path (SIMT, 64 x 64 output tile, 4 x 4 per thread, sequential fp32 FMA over K).

@@ -99,9 +99,10 @@ GemmPlan plan_gemm(int dtype, int64_t rows_per_group_hint, int n_out, int K);
 // (offsets == NULL). B is [E][n_b_rows][K] (n_b_rows = 2*n_out for SwiGLU). One kernel launch.
 // partials: fp32 scratch of gemm_partials_bytes(dtype) bytes (or NULL) in which the bf16 kernel
 // splits the last, incomplete round of tiles along K; summed in a fixed order by a second launch.
-// gather (bf16 only; NULL = A's rows in order): A is then a [a_rows, K] token matrix and row p of the
-// product's input is A[gather[p]] (a_rows * K * 2 < 2^31 bytes), read straight into the GEMM's LDS
-// ring, so no permuted copy of A is written.
+// gather (bf16 only, with EPI_SWIGLU or EPI_GELU_BIAS; NULL = A's rows in order): A is then a
+// [a_rows, K] token matrix and row p of the product's input is A[gather[p]] (a_rows * K * 2 < 2^31
+// bytes), read straight into the GEMM's LDS ring, so no permuted copy of A is written. The gather
+// buffer must hold 256 readable entries past the last row.
 void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* B, const void* bias,
                          void* C, const int32_t* offsets, int e_begin, int n_groups, int64_t max_rows,
                          int64_t dense_rows, int n_out, int K, float* partials, hipStream_t s,
