@@ -505,27 +505,29 @@ __global__ __launch_bounds__(kFusedRouteWaves * 64) void route_fused_kernel(
             l8[j] = (__bf16)r2;
         }
     };
+    // a step's router loads go out before its x loads, so (loads complete in order) the split of the
+    // router into bf16 terms runs while x is still arriving
 #define RF_LOAD(b_, kb_)                                                                                  \
     {                                                                                                     \
         const int base = (kb_) + g * 8;                                                                   \
-        _Pragma("unroll") for (int q = 0; q < XI; ++q) xv[b_][q] = x_load(xq[q] + (kb_));                 \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                   \
             wf[b_][i][0] = w_ok ? *reinterpret_cast<const floatx4*>(wr + base + i * 32) : fzero;          \
             wf[b_][i][1] = w_ok ? *reinterpret_cast<const floatx4*>(wr + base + i * 32 + 4) : fzero;      \
         }                                                                                                 \
+        _Pragma("unroll") for (int q = 0; q < XI; ++q) xv[b_][q] = x_load(xq[q] + (kb_));                 \
     }
 #define RF_MMA(b_)                                                                                        \
     {                                                                                                     \
+        bf16x8 w3[4][3];                                                                                  \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) split8(wf[b_][i], w3[i][0], w3[i][1], w3[i][2]);    \
         __builtin_amdgcn_wave_barrier();                                                                  \
         _Pragma("unroll") for (int q = 0; q < XI; ++q) s_x[wave][xw[q]] = xv[b_][q];                      \
         __builtin_amdgcn_wave_barrier();                                                                  \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                   \
-            bf16x8 w3[3];                                                                                 \
-            split8(wf[b_][i], w3[0], w3[1], w3[2]);                                                       \
             _Pragma("unroll") for (int tt = 0; tt < TT; ++tt) {                                           \
                 const bf16x8 a_ = __builtin_bit_cast(bf16x8, s_x[wave][(tt * 16 + r) * 16 + ((4 * i + g) ^ r)]); \
                 _Pragma("unroll") for (int p = 0; p < 3; ++p)                                             \
-                    acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_, w3[p], acc[tt], 0, 0, 0);       \
+                    acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_, w3[i][p], acc[tt], 0, 0, 0);    \
             }                                                                                             \
         }                                                                                                 \
     }
