@@ -1245,49 +1245,62 @@ __global__ __launch_bounds__(256) void gemm_bf16_tail_kernel(const float* __rest
     constexpr int TM = 2, TN = 4, TNO = GATED ? 2 : 4, WTNO = TNO * 32;
     constexpr int CH = tail_chunks<EPI>();
     const TailHeader* hdr = reinterpret_cast<const TailHeader*>(partials);
-    const int xcd = blockIdx.x & 7;
-    const int t = (blockIdx.x >> 3) / CH, ch = (blockIdx.x >> 3) % CH;
-    const int S = hdr->S[xcd];
-    // the GEMM splits only when rem * S <= nslots, so every slot read below is one it wrote
-    if (S < 2 || t >= hdr->rem[xcd] || t >= nslots || (t + 1) * S > nslots) return;
-    const TailTile tt = hdr->tile[xcd][t];
-    const int gid = ch * 256 + threadIdx.x;  // group id: lane fastest, then v4, j, i, wave
-    const int lane = gid & 63, v4 = (gid >> 6) & 3;
-    const int j = (gid >> 8) % TNO, i = ((gid >> 8) / TNO) % TM, wave = (gid >> 8) / (TNO * TM);
-    const int grp = wave >> 2, wig = wave & 3, wm = wig & 1, wn = wig >> 1;
-    floatx4 z = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
-    for (int sidx = 0; sidx < S; ++sidx) {
-        const floatx4* src = partial_at<TM, TN>(const_cast<float*>(partials), xcd * nslots + t * S + sidx, wave);
-        z += src[((i * TN + j) * 4 + v4) * 64 + lane];
-        if (GATED) u += src[((i * TN + j + TNO) * 4 + v4) * 64 + lane];
-    }
-    const int64_t row = tt.row0 + wave_row_base<R128>(grp, wm) + i * 32 + (lane & 31);
-    const int f0 = tt.n0 + wave_feat_base<R128, WTNO>(grp, wn) + j * 32 + 8 * v4 + 4 * (lane >> 5);
-    if (row >= tt.row_end || f0 >= n_out) return;
-    if (EPI == EPI_F32) {
-        *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(C) + row * n_out + f0) = z;
-        return;
-    }
-    float o[4];
-    if (GATED) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) o[c] = z[c] * __builtin_amdgcn_rcpf(1.0f + __expf(-z[c])) * u[c];
-    } else {
-        float bc[4] = {0.f, 0.f, 0.f, 0.f};
-        if (bias != nullptr) {
-            const uint2 bb = *reinterpret_cast<const uint2*>(bias + (int64_t)tt.e * n_out + f0);
-            bc[0] = __uint_as_float(bb.x << 16);
-            bc[1] = __uint_as_float(bb.x & 0xffff0000u);
-            bc[2] = __uint_as_float(bb.y << 16);
-            bc[3] = __uint_as_float(bb.y & 0xffff0000u);
+    // work item b = (t * CH + ch) * 8 + xcd over every slot the GEMM could have split; the few that
+    // hold a tail tile are the low ones, and a grid-stride loop over them launches far fewer blocks
+    // than one block per item
+    for (int b = blockIdx.x; b < 8 * nslots * CH; b += gridDim.x) {
+        const int xcd = b & 7;
+        const int t = (b >> 3) / CH, ch = (b >> 3) % CH;
+        const int S = hdr->S[xcd];
+        // the GEMM splits only when rem * S <= nslots, so every slot read below is one it wrote
+        if (S < 2 || t >= hdr->rem[xcd] || t >= nslots || (t + 1) * S > nslots) continue;
+        const TailTile tt = hdr->tile[xcd][t];
+        const int gid = ch * 256 + threadIdx.x;  // group id: lane fastest, then v4, j, i, wave
+        const int lane = gid & 63, v4 = (gid >> 6) & 3;
+        const int j = (gid >> 8) % TNO, i = ((gid >> 8) / TNO) % TM, wave = (gid >> 8) / (TNO * TM);
+        const int grp = wave >> 2, wig = wave & 3, wm = wig & 1, wn = wig >> 1;
+        floatx4 z = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+        for (int sidx = 0; sidx < S; ++sidx) {
+            const floatx4* src =
+                partial_at<TM, TN>(const_cast<float*>(partials), xcd * nslots + t * S + sidx, wave);
+            z += src[((i * TN + j) * 4 + v4) * 64 + lane];
+            if (GATED) u += src[((i * TN + j + TNO) * 4 + v4) * 64 + lane];
         }
+        const int64_t row = tt.row0 + wave_row_base<R128>(grp, wm) + i * 32 + (lane & 31);
+        const int f0 = tt.n0 + wave_feat_base<R128, WTNO>(grp, wn) + j * 32 + 8 * v4 + 4 * (lane >> 5);
+        if (row >= tt.row_end || f0 >= n_out) continue;
+        if (EPI == EPI_F32) {
+            *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(C) + row * n_out + f0) = z;
+            continue;
+        }
+        float o[4];
+        if (GATED) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) o[c] = EPI == EPI_GELU_BIAS ? gelu_f(z[c] + bc[c]) : z[c] + bc[c];
+            for (int c = 0; c < 4; ++c) o[c] = z[c] * __builtin_amdgcn_rcpf(1.0f + __expf(-z[c])) * u[c];
+        } else {
+            float bc[4] = {0.f, 0.f, 0.f, 0.f};
+            if (bias != nullptr) {
+                const uint2 bb = *reinterpret_cast<const uint2*>(bias + (int64_t)tt.e * n_out + f0);
+                bc[0] = __uint_as_float(bb.x << 16);
+                bc[1] = __uint_as_float(bb.x & 0xffff0000u);
+                bc[2] = __uint_as_float(bb.y << 16);
+                bc[3] = __uint_as_float(bb.y & 0xffff0000u);
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) o[c] = EPI == EPI_GELU_BIAS ? gelu_f(z[c] + bc[c]) : z[c] + bc[c];
+        }
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+        pk.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+        *reinterpret_cast<uint2*>(C + row * n_out + f0) = pk;
     }
-    uint2 pk;
-    pk.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
-    pk.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
-    *reinterpret_cast<uint2*>(C + row * n_out + f0) = pk;
+}
+
+// Blocks of the tail pass: one per possible work item (8 XCDs x slots x chunks), at most 2048; the
+// kernel loops over the rest.
+unsigned tail_grid(unsigned gemm_grid, int chunks) {
+    const unsigned items = gemm_grid * (unsigned)chunks;
+    return items < 2048u ? items : 2048u;
 }
 
 // Blocks of the persistent GEMM: the CU count in whole XCD rounds, at most 8 * kMaxSlotsPerXcd.
@@ -1343,8 +1356,8 @@ void launch_bf16_persistent(int epi, const void* A, const void* B, const void* b
             MOE_PERSIST_GA(EPI_, false)                                                                   \
         }                                                                                                 \
         if (partials)                                                                                     \
-            gemm_bf16_tail_kernel<EPI_, R128><<<grid * tail_chunks<EPI_>(), 256, 0, s>>>(partials, bi, c,   \
-                                                                                        n_out, (int)(grid / 8)); \
+            gemm_bf16_tail_kernel<EPI_, R128><<<tail_grid(grid, tail_chunks<EPI_>()), 256, 0, s>>>(        \
+                partials, bi, c, n_out, (int)(grid / 8));                                                 \
     }
     if (epi == EPI_SWIGLU) MOE_PERSIST(EPI_SWIGLU)
     else if (epi == EPI_GELU_BIAS) MOE_PERSIST(EPI_GELU_BIAS)
@@ -1388,8 +1401,8 @@ void launch_bf16_wide(int epi, const void* A, const void* B, const void* bias, v
             MOE_WIDE_GA(EPI_, false)                                                                      \
         }                                                                                                 \
         if (partials)                                                                                     \
-            gemm_bf16_tail_kernel<EPI_, false><<<grid * tail_chunks<EPI_>(), 256, 0, s>>>(partials, bi, c,  \
-                                                                                         n_out, (int)(grid / 8)); \
+            gemm_bf16_tail_kernel<EPI_, false><<<tail_grid(grid, tail_chunks<EPI_>()), 256, 0, s>>>(       \
+                partials, bi, c, n_out, (int)(grid / 8));                                                 \
     }
     if (epi == EPI_SWIGLU) MOE_WIDE(EPI_SWIGLU)
     else if (epi == EPI_GELU_BIAS) MOE_WIDE(EPI_GELU_BIAS)
