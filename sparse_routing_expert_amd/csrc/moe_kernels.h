@@ -143,7 +143,8 @@ struct SgArgsF {
     const int32_t* offsets;
     int e_begin, G, mode;
 };
-// max_rows: total rows of the grouped buffer (SG_ROWS grid bound)
+// max_rows: total rows of the grouped buffer (SG_ROWS grid bound). bf16: N and scm multiples of 4 and
+// C 16-byte aligned (each lane stores 4 consecutive columns).
 void launch_sg_gemm_bf16(const SgArgs& a, int64_t max_rows, hipStream_t s);
 void launch_sg_gemm_f32(const SgArgsF& a, int64_t max_rows, hipStream_t s);
 
