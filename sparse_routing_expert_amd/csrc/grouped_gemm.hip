@@ -580,6 +580,12 @@ __device__ __forceinline__ float from_agpr(float x) {
     asm("v_accvgpr_read_b32 %0, %1" : "=v"(y) : "a"(x));
     return y;
 }
+// Global-memory views of the epilogue's destinations. The stores must be global, not flat: a flat
+// store also counts on the LDS counter, so a later wait for fragment reads would wait for the stores
+// as well. (A pointer passed through an empty asm loses its address space: the wide kernel's K-split
+// partial stores compiled to flat stores before this cast.)
+typedef __attribute__((address_space(1))) floatx4 global_floatx4;
+__device__ __forceinline__ global_floatx4* as_global(floatx4* p) { return (global_floatx4*)p; }
 __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -625,7 +631,7 @@ __device__ __forceinline__ void store_block(const floatx16 (&a)[TN], int64_t row
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int f0 = fbase + j * 32 + 8 * q4 + 4 * khalf;
                 if (row < row_end && f0 < n_out)
-                    *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(C) + row * n_out + f0) =
+                    *as_global(reinterpret_cast<floatx4*>(reinterpret_cast<float*>(C) + row * n_out + f0)) =
                         floatx4{rd(a[j][4 * q4]), rd(a[j][4 * q4 + 1]), rd(a[j][4 * q4 + 2]), rd(a[j][4 * q4 + 3])};
             }
             continue;
@@ -1213,7 +1219,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
                 for (int j = 0; j < TN; ++j)
 #pragma unroll
                     for (int v4 = 0; v4 < 4; ++v4)
-                        dst[(((i & 1) * TN + j) * 4 + v4) * 64 + ln] =
+                        *as_global(dst + (((i & 1) * TN + j) * 4 + v4) * 64 + ln) =
                             floatx4{from_agpr(acc[i][j][4 * v4]), from_agpr(acc[i][j][4 * v4 + 1]),
                                     from_agpr(acc[i][j][4 * v4 + 2]), from_agpr(acc[i][j][4 * v4 + 3])};
             }
