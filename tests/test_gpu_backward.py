@@ -39,6 +39,9 @@ CASES = {
     "deepseek_mini_aux_c1.0": (I.mini("deepseek_v3", T=500, d=448, F=128, Fs=192), 1.0, 0.001),
     "E1_k1": (I.mini("small_bf16", T=300, d=128, F=128, E=1, k=1), 0, 0.0),
     "T1": (I.mini("deepseek_v3", T=1, d=128, F=64, Fs=64), 0, 0.0),
+    # the ABI's maximum router width and top-k
+    "max_E1024_k32": (I.mini("small_bf16", T=300, d=128, F=64, E=1024, k=32), 0, 0.01),
+    "max_E1024_k32_sigmoid_shared": (I.mini("deepseek_v3", T=400, d=128, F=64, Fs=64, E=1024, k=32), 0, 0.0),
     # at least 1536 rows per expert: the dgrad products run on the persistent GEMM against transposed
     # weights (SwiGLU, and GELU with biases, whose n_in = F)
     "rows1600_swiglu": (I.mini("small_bf16", T=1600, d=256, F=192, E=2, k=2), 0, 0.01),

@@ -104,6 +104,15 @@ CASES = {
     # 256 rows, several empty) with a long K, and GELU with biases
     "tiles128_skewed_longK": I.mini("qwen3_30b_a3b", T=700, d=1536, F=96, E=32, k=4),
     "tiles128_gelu_bias": TINY.with_sizes(dtype="bf16", T=700, d=192, F=320, E=6, k=2),
+    # the ABI's maximum router width and top-k (E = 1024, k = 32): the router GEMM over 3 x 1024
+    # columns, per-token selection, the permute's scan path, the 64-row kernel with 1024 groups and
+    # the combine's 32-slot form; with more rows per expert the 128-row tiles over 1024 groups (the
+    # tile schedule's LDS arrays full); sigmoid with a selection bias and a shared expert; and
+    # k = 16 over 8192 tokens
+    "max_E1024_k32": I.mini("small_bf16", T=300, d=128, F=64, E=1024, k=32),
+    "max_E1024_k32_rows": I.mini("small_bf16", T=2100, d=128, F=64, E=1024, k=32),
+    "max_E1024_k32_sigmoid_shared": I.mini("deepseek_v3", T=400, d=128, F=64, Fs=64, E=1024, k=32),
+    "max_E1024_k16_T8192": I.mini("small_bf16", T=8192, d=64, F=64, E=1024, k=16),
 }
 
 
