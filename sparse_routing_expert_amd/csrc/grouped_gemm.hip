@@ -452,6 +452,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
             for (int v = 0; v < 16; ++v) {
                 const int64_t row = tc.row0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
                 if (row >= tc.row_end) continue;
+                if (EPI == EPI_F32) {  // fp32 output (dense products only)
+                    reinterpret_cast<float*>(C)[row * n_out + col] = acc[i][j][v];
+                    continue;
+                }
                 float out;
                 if (EPI == EPI_SWIGLU) out = silu_f(acc[i][j][v]) * acc[i][j + TNO][v];
                 else if (EPI == EPI_GELU_BIAS) out = gelu_f(acc[i][j][v] + bcol);
@@ -1529,6 +1533,7 @@ void launch_bf16_tiles(int epi, const void* A, const void* B, const void* bias, 
         }
     }
     if (epi == EPI_GELU_BIAS) MOE_TILES(EPI_GELU_BIAS)
+    else if (epi == EPI_F32) MOE_TILES(EPI_F32)
     else MOE_TILES(EPI_BIAS)
 #undef MOE_TILES
 }
@@ -1538,6 +1543,18 @@ void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* 
                          int n_out, int K, float* partials, hipStream_t s, const int32_t* gather, int64_t a_rows) {
     const uint32_t a_bytes = gather ? (uint32_t)(a_rows * K * 2) : 0u;
     if (dtype == MOE_BF16) {
+        if (bm == 128 && offsets == nullptr && epi == EPI_F32 &&
+            ((dense_rows + 127) / 128) * ((n_out + 127) / 128) >= device_cu_count()) {
+            // dense fp32-output products with a short output (the wide routers' logits, x [T, d] x
+            // [3 Epad, d]) whose 128 x 128 tiles fill the CUs: one tile per block, two blocks per CU,
+            // no K split, so no fp32 partial tiles are written and summed. Measured on the routes:
+            // Qwen3-shaped (384 tiles, K = 2048) 86.4 -> 72.4 us; the DeepSeek-shaped one (192 tiles,
+            // K = 7168) was slower this way (94.5 against 125.4 us) and keeps the persistent kernel's
+            // K split.
+            launch_bf16_tiles<128, 128, 4, 8>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows,
+                                              n_out, K, s, gather, a_bytes);
+            return;
+        }
         if (bm == 64 && offsets != nullptr && epi != EPI_F32) {
             // small groups: 64-row x 128-column tiles with a 6-stage LDS ring (72 KB, two blocks per CU).
             // Measured on the decode batch: 128-wide panels beat 256-wide ones (more tiles to spread

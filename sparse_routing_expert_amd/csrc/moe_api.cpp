@@ -232,7 +232,7 @@ void route_logits(const moe_shape* s, const RouteWs& w, const void* x, const flo
                   int32_t* ticket, float* lg, void* ws, hipStream_t st) {
     moe::launch_route_prep(w_router, s->E, w.Epad, s->d_model, wsplit, ticket, st);
     if (w.gemm)
-        moe::launch_grouped_gemm(MOE_BF16, moe::EPI_F32, 0, x, wsplit, nullptr, lg, nullptr, 0, 1, 0, s->T, w.lg_ld,
+        moe::launch_grouped_gemm(MOE_BF16, moe::EPI_F32, 128, x, wsplit, nullptr, lg, nullptr, 0, 1, 0, s->T, w.lg_ld,
                                  s->d_model, at<float>(ws, w.gpart), st);
     else
         moe::launch_route_logits(s->dtype, x, w_router, wsplit, w.Epad, lg, s->T, s->d_model, s->E, st);

@@ -113,6 +113,8 @@ CASES = {
     "max_E1024_k32_rows": I.mini("small_bf16", T=2100, d=128, F=64, E=1024, k=32),
     "max_E1024_k32_sigmoid_shared": I.mini("deepseek_v3", T=400, d=128, F=64, Fs=64, E=1024, k=32),
     "max_E1024_k16_T8192": I.mini("small_bf16", T=8192, d=64, F=64, E=1024, k=16),
+    # a router GEMM whose 128 x 128 tiles fill the CUs (94 x 3 = 282) runs without a K split
+    "router_tiles128_E128": I.mini("qwen3_30b_a3b", T=12000, d=1024, F=64),
 }
 
 
