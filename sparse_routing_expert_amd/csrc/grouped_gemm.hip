@@ -19,9 +19,10 @@
 //    (SwiGLU: 128 gate and the matching 128 up columns, so a lane holds gate and up of the same
 //    output element) in an XCD-aware order; two groups of four waves alternate LDS fragment reads
 //    and MFMA clusters (ping-pong), and the LDS ring runs on across tiles.
-//  - gemm_bf16_wide_kernel, for expert groups averaging at least 2048 rows: the same tiles and
-//    order, four waves of 128 x 128 (accumulators in AGPRs) that place their memory instructions
-//    between their own MFMAs, and 64-wide K stages, so each DMA reads whole 128-byte row pieces.
+//  - gemm_bf16_wide_kernel, for expert groups averaging at least 2048 rows: 256 x 384 tiles (SwiGLU:
+//    192 gate and the matching 192 up columns), or 256 x 256 past 63 groups, in the same order;
+//    four waves that place their memory instructions between their own MFMAs, and 64-wide K
+//    stages, so each DMA reads whole 128-byte row pieces.
 //  - gemm_bf16_kernel: four waves on one 64 x 128 (or 64 x 64) tile with a 6- (8-) stage ring, two
 //    blocks per CU, for groups of a few dozen rows (decode batches), whose time is spent streaming
 //    the weight panels.
@@ -573,6 +574,81 @@ __device__ __forceinline__ TileSched<BM, BNO, GM> setup_sched(const int32_t* __r
     return ts;
 }
 
+// The same schedule held in registers instead of LDS, for kernels whose LDS ring takes all of it: at
+// most kRegSchedGroups groups, lane g of every wave holds s_ts[g] and offsets[e_begin + g] (g <=
+// n_groups). Each wave forms it on its own (a wave-wide scan), and decode finds the group with a
+// ballot, so it must be called by whole waves.
+constexpr int kRegSchedGroups = 63;
+template <int BM, int BNO, int GM>
+struct TileSchedR {
+    int ts_l, off_l;
+    bool grouped;
+    int e_begin, n_groups;
+    int64_t dense_rows;
+    uint32_t n_tiles_n, m_tiles, R;
+
+    __device__ __forceinline__ void decode(uint32_t lin, int64_t& row0, int64_t& row_end, int& e, int& n0) const {
+        int g = 0;
+        uint32_t g_mt = m_tiles, local = lin;
+        if (grouped) {
+            const uint32_t key = lin / n_tiles_n;
+            // s_ts is non-decreasing: the last group whose first row tile is at or before key
+            const uint64_t m = __ballot(lane_id() < n_groups && (uint32_t)ts_l <= key);
+            g = __builtin_amdgcn_readfirstlane(__popcll(m) - 1);
+            const uint32_t t0 = (uint32_t)__builtin_amdgcn_readlane(ts_l, g);
+            g_mt = (uint32_t)__builtin_amdgcn_readlane(ts_l, g + 1) - t0;
+            local = lin - t0 * n_tiles_n;
+        }
+        const uint32_t grp_ = local / (GM * n_tiles_n);
+        const uint32_t first_m = grp_ * GM;
+        const uint32_t gsz = g_mt - first_m < GM ? g_mt - first_m : GM;
+        const uint32_t rem = local - grp_ * GM * n_tiles_n;
+        const uint32_t col = rem / gsz;
+        const uint32_t mt = first_m + (rem - col * gsz);
+        n0 = (int)col * BNO;
+        if (grouped) {
+            e = e_begin + g;
+            row0 = __builtin_amdgcn_readlane(off_l, g) + (int64_t)mt * BM;
+            row_end = __builtin_amdgcn_readlane(off_l, g + 1);
+        } else {
+            e = 0;
+            row0 = (int64_t)mt * BM;
+            row_end = dense_rows;
+        }
+    }
+};
+template <int BM, int BNO, int GM>
+__device__ __forceinline__ TileSchedR<BM, BNO, GM> setup_sched_regs(const int32_t* __restrict__ offsets,
+                                                                    int e_begin, int n_groups, int64_t dense_rows,
+                                                                    int n_out) {
+    TileSchedR<BM, BNO, GM> ts;
+    const int lane = lane_id();
+    ts.ts_l = 0;
+    ts.off_l = 0;
+    ts.m_tiles = (uint32_t)((dense_rows + BM - 1) / BM);
+    if (offsets) {
+        const int o = lane <= n_groups ? offsets[e_begin + lane] : 0;
+        const int o1 = lane < n_groups ? offsets[e_begin + lane + 1] : o;
+        const int n = (o1 - o + BM - 1) / BM;
+        int inc = n;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int v = __shfl_up(inc, d, kWave);
+            if (lane >= d) inc += v;
+        }
+        ts.ts_l = inc - n;  // exclusive: lane n_groups holds the total
+        ts.off_l = o;
+        ts.m_tiles = (uint32_t)__builtin_amdgcn_readlane(ts.ts_l, n_groups);
+    }
+    ts.grouped = offsets != nullptr;
+    ts.e_begin = e_begin;
+    ts.n_groups = n_groups;
+    ts.dense_rows = dense_rows;
+    ts.n_tiles_n = (uint32_t)((n_out + BNO - 1) / BNO);
+    ts.R = ts.m_tiles * ts.n_tiles_n;
+    return ts;
+}
+
 // Epilogue of one 32-token row block of a wave: a[j] holds a (feature x token) 32 x 32 block; a lane
 // owns token `row` and, per group of 4 registers, 4 consecutive features from fbase + j * 32. FENCE
 // keeps each group's reads of the accumulators next to its stores (for accumulators held in the
@@ -583,6 +659,17 @@ __device__ __forceinline__ float from_agpr(float x) {
     float y;
     asm("v_accvgpr_read_b32 %0, %1" : "=v"(y) : "a"(x));
     return y;
+}
+// The same for accumulators held in VGPRs (where the AGPR file cannot hold them all).
+__device__ __forceinline__ float from_vgpr(float x) {
+    float y;
+    asm("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
+    return y;
+}
+// Accumulator j of a row block: the first NAG in AGPRs, the rest in VGPRs.
+template <int NAG>
+__device__ __forceinline__ float acc_read(int j, float x) {
+    return j < NAG ? from_agpr(x) : from_vgpr(x);
 }
 // Global-memory views of the epilogue's destinations. The stores must be global, not flat: a flat
 // store also counts on the LDS counter, so a later wait for fragment reads would wait for the stores
@@ -596,21 +683,21 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
     const bf16x2_t v = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
     return __builtin_bit_cast(uint32_t, v);
 }
-template <int EPI, int TN, bool FENCE = false>
+template <int EPI, int TN, bool FENCE = false, int NAG = TN>
 __device__ __forceinline__ void store_block(const floatx16 (&a)[TN], int64_t row, int64_t row_end, int e,
                                             int fbase, int lane, uint16_t* __restrict__ C,
                                             const uint16_t* __restrict__ bias, int n_out) {
     constexpr bool GATED = EPI == EPI_SWIGLU;
     constexpr int TNO = GATED ? TN / 2 : TN;
     const int khalf = lane >> 5;
-    auto rd = [&](float x) { return FENCE ? from_agpr(x) : x; };
+    auto rd = [&](int jj, float x) { return FENCE ? acc_read<NAG>(jj, x) : x; };
     auto group = [&](int j, int q4, float (&o)[4]) {
         const int f0 = fbase + j * 32 + 8 * q4 + 4 * khalf;
         if (GATED) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const float z = rd(a[j][4 * q4 + c]);
-                o[c] = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) * rd(a[j + TNO][4 * q4 + c]);
+                const float z = rd(j, a[j][4 * q4 + c]);
+                o[c] = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) * rd(j + TNO, a[j + TNO][4 * q4 + c]);
             }
         } else {
             float bc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -623,7 +710,7 @@ __device__ __forceinline__ void store_block(const floatx16 (&a)[TN], int64_t row
             }
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const float z = rd(a[j][4 * q4 + c]) + bc[c];
+                const float z = rd(j, a[j][4 * q4 + c]) + bc[c];
                 o[c] = EPI == EPI_GELU_BIAS ? gelu_f(z) : z;
             }
         }
@@ -636,7 +723,8 @@ __device__ __forceinline__ void store_block(const floatx16 (&a)[TN], int64_t row
                 const int f0 = fbase + j * 32 + 8 * q4 + 4 * khalf;
                 if (row < row_end && f0 < n_out)
                     *as_global(reinterpret_cast<floatx4*>(reinterpret_cast<float*>(C) + row * n_out + f0)) =
-                        floatx4{rd(a[j][4 * q4]), rd(a[j][4 * q4 + 1]), rd(a[j][4 * q4 + 2]), rd(a[j][4 * q4 + 3])};
+                        floatx4{rd(j, a[j][4 * q4]), rd(j, a[j][4 * q4 + 1]), rd(j, a[j][4 * q4 + 2]),
+                                rd(j, a[j][4 * q4 + 3])};
             }
             continue;
         }
@@ -692,7 +780,7 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[TM][TN], int64_
 // Partial buffer: a header, then the fp32 accumulators of each tile slice as
 // [slot][wave][i][j][v / 4][lane] float4 (each store and load moves 1 KB per wave instruction).
 // Header: per XCD {rem, S} of its split last round, and per tail tile {row0, row_end, e, n0}.
-constexpr int kPartialFloats = 256 * 256;  // one 256 x 256 (or 128 x 512) tile
+constexpr int kPartialFloats = 256 * (kGemmWideBN > 256 ? kGemmWideBN : 256);  // one output tile
 constexpr int kMaxSlotsPerXcd = 64;        // nslots <= 64 (512 blocks)
 struct TailTile {
     int64_t row0, row_end;
@@ -980,39 +1068,59 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
 #undef PS_MMA
 }
 
-// Four-wave, wide-K form of the persistent GEMM, for large groups: the same 256 x 256 tiles, tile
-// sequence, XCD plan and K split, with each wave owning a 128 x 128 block of the tile (16 accumulators
-// of 32 x 32 in the AGPR file, one wave per SIMD) and the memory instructions placed between the
-// wave's own MFMAs instead of in a partner wave's cluster. Stages are 64 columns wide (128-byte LDS
-// rows, a two-slot ring), so each DMA instruction reads 8 whole 128-byte row pieces instead of 16
-// half lines. Chunk c of LDS row r sits at position c ^ ((r / 2) % 8), which keeps the 16-lane groups
-// of a fragment read on distinct banks. A stage is four 16-wide K steps; the DMAs of the next stage go
-// out during the first two (one after every other MFMA), and the last step waits for them, passes the
-// stage barrier and reads the next stage's first fragments. K-split slices store their partial tiles
-// in the eight-wave layout that gemm_bf16_tail_kernel reads.
+// Four-wave, wide-K form of the persistent GEMM, for large groups: the tile sequence, XCD plan and K
+// split of the eight-wave kernel, with each wave owning a 128-token x BN / 2-weight-row block of the
+// tile (one wave per SIMD) and the memory instructions placed between the wave's own MFMAs instead of
+// in a partner wave's cluster. Stages are 64 columns wide (128-byte LDS rows, a two-slot ring), so each
+// DMA instruction reads 8 whole 128-byte row pieces instead of 16 half lines. Chunk c of LDS row r
+// sits at position c ^ ((r / 2) % 8), which keeps the 16-lane groups of a fragment read on distinct
+// banks. A stage is four 16-wide K steps; the DMAs of the next stage go out during the first two (one
+// after every other MFMA), and the last step waits for them, passes the stage barrier and reads the
+// next stage's first fragments. K-split slices store their partial tiles in the eight-wave layout
+// (with BN / 64 column blocks per wave) that gemm_bf16_tail_kernel reads.
+//
+// BN = 384 weight rows: 24 accumulators of 32 x 32 per wave, 384 registers, more than the 256 of the
+// AGPR file, so acc[i][4..5] live in VGPRs (fragments and addresses take the other 120 or so). A
+// stage is 80 KB, the two slots take all 160 KB of LDS, and the tile schedule lives in registers
+// (TileSchedR, at most 63 groups). Per MFMA, a stage moves 17 % fewer operand bytes than with
+// BN = 256, and each stage is half as long again, which covers more of the next stage's DMA latency.
 
-template <int EPI, int GM, bool KT, bool GA>
+template <int EPI, int GM, bool KT, bool GA, int BN>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ C, const int32_t* __restrict__ offsets, int e_begin, int n_groups, int64_t dense_rows,
     int n_out, int K, float* __restrict__ partials, const int32_t* __restrict__ gather, uint32_t a_bytes) {
-    constexpr int BM = 256, BN = 256, BK = 64, NS = 2;
+    constexpr int BM = 256, BK = 64, NS = 2;
     constexpr bool GATED = EPI == EPI_SWIGLU;
     constexpr int TM = 4;
     constexpr int BNO = GATED ? BN / 2 : BN, WTNO = BNO / 2, TNO = WTNO / 32, TN = GATED ? 2 * TNO : TNO;
-    constexpr int STAGE_ELEMS = (BM + BN) * BK;  // 512 rows of 128 bytes
+    constexpr int STAGE_ELEMS = (BM + BN) * BK;  // BM + BN rows of 128 bytes
     constexpr int STAGE_BYTES = STAGE_ELEMS * 2;
-    constexpr int NQ = 16;  // DMA instructions per wave per stage (8 rows each)
-    static_assert(TN == 4, "tile shape");
-    static_assert(NS * STAGE_BYTES + 2 * 1025 * 4 + 8 * 4 <= 160 * 1024, "LDS budget");
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE_ELEMS];
-    __shared__ int s_ts[1025];
-    __shared__ int s_off[1025];
-    __shared__ int s_wave[8];
+    constexpr int NQ = (BM + BN) / 32;  // DMA instructions per wave per stage (8 rows each)
+    constexpr int NQB = NQ - BM / 32;   // of them on the weight rows
+    constexpr int QUP = BM / 32 + BN / 64;  // first DMA on the up rows (SwiGLU)
+    constexpr int NF = TM + TN;             // fragment reads per 16-wide K step
+    constexpr int NT = TM * TN;             // MFMAs per 16-wide K step
+    // accumulators: 16 blocks of 32 x 32 fill the AGPR file; with 384 weight rows acc[i][4..5] are in VGPRs
+    constexpr int NAG = 16 / TM;
+    // 384-row weight tiles fill the LDS with the ring; their tile schedule is held in registers
+    constexpr bool RS = BN > 256;
+    constexpr int SCHED_ELEMS = RS ? 0 : (2 * 1025 + 8) * 2;
+    static_assert(TN == BN / 64 && BN % 128 == 0 && NF <= NT / 2 && NQ - NQ / 2 <= NT / 2 && NF <= NT - TN,
+                  "tile shape");
+    static_assert(NS * STAGE_BYTES + SCHED_ELEMS * 2 <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE_ELEMS + SCHED_ELEMS];
 
     const int tid = threadIdx.x, lane = lane_id();
-    const TileSched<BM, BNO, GM> ts =
-        setup_sched<BM, BNO, GM, 256>(offsets, e_begin, n_groups, dense_rows, n_out, s_ts, s_off, s_wave);
+    using Sched = typename std::conditional<RS, TileSchedR<BM, BNO, GM>, TileSched<BM, BNO, GM>>::type;
+    Sched ts;
+    if constexpr (RS) {
+        ts = setup_sched_regs<BM, BNO, GM>(offsets, e_begin, n_groups, dense_rows, n_out);
+    } else {
+        int* s_ts = reinterpret_cast<int*>(lds + NS * STAGE_ELEMS);
+        ts = setup_sched<BM, BNO, GM, 256>(offsets, e_begin, n_groups, dense_rows, n_out, s_ts, s_ts + 1025,
+                                           s_ts + 2050);
+    }
     const int nk = KT ? (K + BK - 1) / BK : K / BK;
     const uint32_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslots = gridDim.x >> 3;
     const XcdPlan plan = xcd_plan(ts.R, xcd, nslots, nk, partials != nullptr);
@@ -1022,16 +1130,16 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
     const int slice_part = has_slice ? (int)(slot % plan.S) : 0;
     const int slice_kb = slice_part * nk / (int)plan.S, slice_ke = (slice_part + 1) * nk / (int)plan.S;
     const int nunits = (int)nw + (has_slice ? 1 : 0);
-    if (partials != nullptr && tid == 0) {
+    if (partials != nullptr) {
         TailHeader* hdr = reinterpret_cast<TailHeader*>(partials);
-        if (slot == 0) {
+        if (slot == 0 && tid == 0) {
             hdr->rem[xcd] = (int32_t)plan.rem;
             hdr->S[xcd] = (int32_t)plan.S;
         }
-        if (has_slice && slice_part == 0) {
+        if (has_slice && slice_part == 0 && tid < 64) {  // decode by a whole wave
             TailTile tt;
             ts.decode(slice_lin, tt.row0, tt.row_end, tt.e, tt.n0);
-            hdr->tile[xcd][slot / plan.S] = tt;
+            if (tid == 0) hdr->tile[xcd][slot / plan.S] = tt;
         }
     }
     if (nunits == 0) return;  // uniform per block
@@ -1044,20 +1152,21 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
     const int64_t n_b_rows = GATED ? 2 * (int64_t)n_out : n_out;
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)lds;
 
-    // DMA q of this wave: LDS rows (q * 4 + wave) * 8 + [0, 8); rows 0-255 token tile, 256-511 weights
+    // DMA q of this wave: LDS rows (q * 4 + wave) * 8 + [0, 8); rows 0-255 token tile, then the weights
+    // (SwiGLU: BN / 2 gate rows, then the matching up rows)
     int voff[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         const int R = (q * 4 + wave) * 8 + (lane >> 3);
         const int c = (lane & 7) ^ swz8(R);
-        const int row = q < 8 ? R : ((GATED && q >= 12) ? R - 384 : R - 256);
+        const int row = q < BM / 32 ? R : ((GATED && q >= QUP) ? R - BM - BN / 2 : R - BM);
         voff[q] = row * K * 2 + c * 16;
     }
     // K not a multiple of BK (KT): the weight chunks of the last stage past K read as zeros
-    int tor[8];
+    int tor[NQB];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int R = ((q + 8) * 4 + wave) * 8 + (lane >> 3);
+    for (int q = 0; q < NQB; ++q) {
+        const int R = ((q + BM / 32) * 4 + wave) * 8 + (lane >> 3);
         tor[q] = KT && ((lane & 7) ^ swz8(R)) * 8 >= K - (nk - 1) * BK ? (int)0x80000000 : 0;
     }
     i32x4 ra, rb0, rb1;
@@ -1103,22 +1212,31 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
 
 #define PW_DMA(slot_, ks_, q_)                                                                            \
     dma16(lds_base + (slot_) * STAGE_BYTES + ((q_) * 4 + wave) * 1024,                                    \
-          (KT && (q_) >= 8 && (ks_) == nk - 1) ? (voff[q_] | tor[((q_) + 8) & 7]) : voff[q_],             \
-          (q_) < 8 ? ra : ((GATED && (q_) >= 12) ? rb1 : rb0), (ks_) * (BK * 2));
-    // fragment n (in MFMA use order: fa0, fb0..fb3, fa1..fa3) of 16-wide K step kk_ into buffer b_
+          (KT && (q_) >= BM / 32 && (ks_) == nk - 1) ? (voff[q_] | tor[((q_) - BM / 32) % NQB]) : voff[q_], \
+          (q_) < BM / 32 ? ra : ((GATED && (q_) >= QUP) ? rb1 : rb0), (ks_) * (BK * 2));
+    // fragment n (in MFMA use order: fa0, fb0..fb[TN-1], fa1..fa3) of 16-wide K step kk_ into buffer b_
 #define PW_READ(b_, kk_, slot_, n_)                                                                       \
     {                                                                                                     \
-        const int m_ = (n_) == 0 ? 0 : ((n_) <= 4 ? (n_) + 3 : (n_) - 4);                                 \
         const uint16_t* L_ = lds + (slot_) * STAGE_ELEMS;                                                 \
         const int c_ = (kk_) * 2 + khalf;                                                                 \
-        if (m_ < 4)                                                                                       \
-            fa[b_][m_ & 3] = *reinterpret_cast<const bf16x8*>(L_ + a_off[m_ & 3] + ((c_ ^ a_sw[m_ & 3]) << 3)); \
-        else                                                                                              \
-            fb[b_][m_ & 3] = *reinterpret_cast<const bf16x8*>(L_ + b_off[m_ & 3] + ((c_ ^ b_sw[m_ & 3]) << 3)); \
+        if ((n_) == 0 || (n_) > TN) {                                                                     \
+            const int i_ = (n_) == 0 ? 0 : (n_) - TN;                                                     \
+            fa[b_][i_] = *reinterpret_cast<const bf16x8*>(L_ + a_off[i_] + ((c_ ^ a_sw[i_]) << 3));       \
+        } else {                                                                                          \
+            const int j_ = (n_) - 1;                                                                      \
+            fb[b_][j_] = *reinterpret_cast<const bf16x8*>(L_ + b_off[j_] + ((c_ ^ b_sw[j_]) << 3));       \
+        }                                                                                                 \
     }
+    // the compiler selects one register file for every MFMA accumulator of a kernel, so the ones kept in
+    // VGPRs are multiplied through inline asm (their hazards are covered where they are zeroed and read)
 #define PW_MMA(b_, t_)                                                                                    \
-    acc[(t_) >> 2][(t_) & 3] =                                                                            \
-        __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[b_][(t_) & 3], fa[b_][(t_) >> 2], acc[(t_) >> 2][(t_) & 3], 0, 0, 0);
+    if ((t_) % TN < NAG)                                                                                  \
+        acc[(t_) / TN][(t_) % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                              \
+            fb[b_][(t_) % TN], fa[b_][(t_) / TN], acc[(t_) / TN][(t_) % TN], 0, 0, 0);                    \
+    else                                                                                                  \
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"                                            \
+                     : "+v"(acc[(t_) / TN][(t_) % TN])                                                    \
+                     : "v"(fb[b_][(t_) % TN]), "v"(fa[b_][(t_) / TN]));
 
     int dma_u = 0;
     set_dma_tile(unit_lin(0));
@@ -1144,49 +1262,49 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
     wait_vm<0>();
     lds_barrier();
 #pragma unroll
-    for (int n = 0; n < 8; ++n) PW_READ(0, 0, 0, n)
+    for (int n = 0; n < NF; ++n) PW_READ(0, 0, 0, n)
     __builtin_amdgcn_sched_barrier(0);
 
     int r_slot = 0;
-    // one stage: K steps 0 and 1 with the next stage's 16 DMAs after their odd MFMAs and the following
-    // step's fragment reads after their even ones, step 2 with the reads of step 3, step 3: four MFMAs,
+    // one stage: K steps 0 and 1 with the next stage's NQ DMAs after their odd MFMAs and the following
+    // step's fragment reads after their even ones, step 2 with the reads of step 3, step 3: TN MFMAs,
     // the wait for the next stage's DMAs and the stage barrier, the rest with the reads of the next
     // stage's first step
 #define PW_STAGE                                                                                          \
     {                                                                                                     \
         const int n_slot = r_slot ^ 1;                                                                    \
-        _Pragma("unroll") for (int t = 0; t < 16; ++t) {                                                  \
+        _Pragma("unroll") for (int t = 0; t < NT; ++t) {                                                  \
             PW_MMA(0, t)                                                                                  \
-            if (t & 1) PW_DMA(n_slot, w_ks, t >> 1)                                                       \
-            if ((t & 1) == 0) PW_READ(1, 1, r_slot, t >> 1)                                               \
+            if ((t & 1) && (t >> 1) < NQ / 2) PW_DMA(n_slot, w_ks, t >> 1)                                \
+            if ((t & 1) == 0 && (t >> 1) < NF) PW_READ(1, 1, r_slot, t >> 1)                              \
             __builtin_amdgcn_sched_barrier(0);                                                            \
         }                                                                                                 \
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                                \
         __builtin_amdgcn_sched_barrier(0);                                                                \
-        _Pragma("unroll") for (int t = 0; t < 16; ++t) {                                                  \
+        _Pragma("unroll") for (int t = 0; t < NT; ++t) {                                                  \
             PW_MMA(1, t)                                                                                  \
-            if (t & 1) PW_DMA(n_slot, w_ks, 8 + (t >> 1))                                                 \
-            if ((t & 1) == 0) PW_READ(0, 2, r_slot, t >> 1)                                               \
+            if ((t & 1) && (t >> 1) < NQ - NQ / 2) PW_DMA(n_slot, w_ks, NQ / 2 + (t >> 1))                \
+            if ((t & 1) == 0 && (t >> 1) < NF) PW_READ(0, 2, r_slot, t >> 1)                              \
             __builtin_amdgcn_sched_barrier(0);                                                            \
         }                                                                                                 \
         dma_advance();                                                                                    \
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                                \
         __builtin_amdgcn_sched_barrier(0);                                                                \
-        _Pragma("unroll") for (int t = 0; t < 16; ++t) {                                                  \
+        _Pragma("unroll") for (int t = 0; t < NT; ++t) {                                                  \
             PW_MMA(0, t)                                                                                  \
-            if ((t & 1) == 0) PW_READ(1, 3, r_slot, t >> 1)                                               \
+            if ((t & 1) == 0 && (t >> 1) < NF) PW_READ(1, 3, r_slot, t >> 1)                              \
             __builtin_amdgcn_sched_barrier(0);                                                            \
         }                                                                                                 \
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                                \
         __builtin_amdgcn_sched_barrier(0);                                                                \
-        _Pragma("unroll") for (int t = 0; t < 4; ++t) PW_MMA(1, t)                                        \
+        _Pragma("unroll") for (int t = 0; t < TN; ++t) PW_MMA(1, t)                                       \
         __builtin_amdgcn_sched_barrier(0);                                                                \
         wait_vm<0>();                                                                                     \
         lds_barrier();                                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                                \
-        _Pragma("unroll") for (int t = 4; t < 16; ++t) {                                                  \
+        _Pragma("unroll") for (int t = TN; t < NT; ++t) {                                                 \
             PW_MMA(1, t)                                                                                  \
-            if (t >= 4 && t < 12) PW_READ(0, 0, n_slot, t - 4)                                            \
+            if (t - TN < NF) PW_READ(0, 0, n_slot, t - TN)                                                \
             __builtin_amdgcn_sched_barrier(0);                                                            \
         }                                                                                                 \
         r_slot = n_slot;                                                                                  \
@@ -1198,8 +1316,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+        if constexpr (NAG < TN) asm volatile("s_nop 4" ::: "memory");  // VALU writes before MFMA reads
         const int ns = unit_ke(u) - unit_kb(u);
         for (int st = 0; st < ns; ++st) PW_STAGE
+        // an MFMA's result is read by VALU instructions only some cycles after it issues
+        if constexpr (NAG < TN) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
         if (u < (int)nw) {
             int64_t row0, row_end;
             int e, n0;
@@ -1208,7 +1329,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
             asm volatile("" : "+v"(ln));
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
-                store_block<EPI, TN, true>(acc[i], row0 + wm * 128 + i * 32 + (ln & 31), row_end, e,
+                store_block<EPI, TN, true, NAG>(acc[i], row0 + wm * 128 + i * 32 + (ln & 31), row_end, e,
                                            n0 + wn * WTNO, ln, C, bias, n_out);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -1224,8 +1345,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
 #pragma unroll
                     for (int v4 = 0; v4 < 4; ++v4)
                         *as_global(dst + (((i & 1) * TN + j) * 4 + v4) * 64 + ln) =
-                            floatx4{from_agpr(acc[i][j][4 * v4]), from_agpr(acc[i][j][4 * v4 + 1]),
-                                    from_agpr(acc[i][j][4 * v4 + 2]), from_agpr(acc[i][j][4 * v4 + 3])};
+                            floatx4{acc_read<NAG>(j, acc[i][j][4 * v4]), acc_read<NAG>(j, acc[i][j][4 * v4 + 1]),
+                                    acc_read<NAG>(j, acc[i][j][4 * v4 + 2]), acc_read<NAG>(j, acc[i][j][4 * v4 + 3])};
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -1243,17 +1364,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
 // chunk (b / 8) % CH of that tile's groups (launch: 8 * nslots * CH blocks of 256 threads, nslots
 // the GEMM's blocks per XCD). Tile coordinates come from the header the GEMM wrote; R128 is the
 // GEMM's tile layout.
-template <int EPI>
+template <int EPI, int TN = 4>
 constexpr int tail_chunks() {
-    return 8 * 2 * (EPI == EPI_SWIGLU ? 2 : 4) * 4 * 64 / 256;  // (wave, i, j, v4, lane) groups / 256
+    return 8 * 2 * (EPI == EPI_SWIGLU ? TN / 2 : TN) * 4 * 64 / 256;  // (wave, i, j, v4, lane) groups / 256
 }
-template <int EPI, bool R128>
+template <int EPI, bool R128, int TN = 4>
 __global__ __launch_bounds__(256) void gemm_bf16_tail_kernel(const float* __restrict__ partials,
                                                              const uint16_t* __restrict__ bias,
                                                              uint16_t* __restrict__ C, int n_out, int nslots) {
     constexpr bool GATED = EPI == EPI_SWIGLU;
-    constexpr int TM = 2, TN = 4, TNO = GATED ? 2 : 4, WTNO = TNO * 32;
-    constexpr int CH = tail_chunks<EPI>();
+    constexpr int TM = 2, TNO = GATED ? TN / 2 : TN, WTNO = TNO * 32;
+    constexpr int CH = tail_chunks<EPI, TN>();
     const TailHeader* hdr = reinterpret_cast<const TailHeader*>(partials);
     // work item b = (t * CH + ch) * 8 + xcd over every slot the GEMM could have split; the few that
     // hold a tail tile are the low ones, and a grid-stride loop over them launches far fewer blocks
@@ -1377,11 +1498,11 @@ void launch_bf16_persistent(int epi, const void* A, const void* B, const void* b
 #undef MOE_PERSIST_GA
 }
 
-template <int GM>
+template <int GM, int BN>
 void launch_bf16_wide(int epi, const void* A, const void* B, const void* bias, void* C, const int32_t* offsets,
                     int e_begin, int n_groups, int64_t max_rows, int64_t dense_rows, int n_out, int K, float* partials,
                     hipStream_t s, const int32_t* gather, uint32_t a_bytes) {
-    const int bno = epi == EPI_SWIGLU ? 128 : 256;
+    const int bno = epi == EPI_SWIGLU ? BN / 2 : BN;
     const int64_t m_tiles = offsets ? (max_rows + 255) / 256 + n_groups : (dense_rows + 255) / 256;
     const int64_t tiles = m_tiles * ((n_out + bno - 1) / bno);
     if (tiles <= 0) return;
@@ -1396,10 +1517,10 @@ void launch_bf16_wide(int epi, const void* A, const void* B, const void* bias, v
 #define MOE_WIDE_GA(EPI_, GA_)                                                                             \
     {                                                                                                     \
         if (K % 64)                                                                                       \
-            gemm_bf16_wide_kernel<EPI_, GM, true, GA_><<<grid, 256, 0, s>>>(                              \
+            gemm_bf16_wide_kernel<EPI_, GM, true, GA_, BN><<<grid, 256, 0, s>>>(                          \
                 a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out, K, partials, gather, a_bytes);  \
         else                                                                                              \
-            gemm_bf16_wide_kernel<EPI_, GM, false, GA_><<<grid, 256, 0, s>>>(                             \
+            gemm_bf16_wide_kernel<EPI_, GM, false, GA_, BN><<<grid, 256, 0, s>>>(                         \
                 a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out, K, partials, gather, a_bytes);  \
     }
 #define MOE_WIDE(EPI_)                                                                                      \
@@ -1411,8 +1532,9 @@ void launch_bf16_wide(int epi, const void* A, const void* B, const void* bias, v
             MOE_WIDE_GA(EPI_, false)                                                                      \
         }                                                                                                 \
         if (partials)                                                                                     \
-            gemm_bf16_tail_kernel<EPI_, false><<<tail_grid(grid, tail_chunks<EPI_>()), 256, 0, s>>>(       \
-                partials, bi, c, n_out, (int)(grid / 8));                                                 \
+            gemm_bf16_tail_kernel<EPI_, false, BN / 64>                                                   \
+                <<<tail_grid(grid, tail_chunks<EPI_, BN / 64>()), 256, 0, s>>>(partials, bi, c, n_out,    \
+                                                                               (int)(grid / 8));          \
     }
     if (epi == EPI_SWIGLU) MOE_WIDE(EPI_SWIGLU)
     else if (epi == EPI_GELU_BIAS) MOE_WIDE(EPI_GELU_BIAS)
@@ -1577,8 +1699,14 @@ void launch_grouped_gemm(int dtype, int epi, int bm, const void* A, const void* 
         const int64_t ng = n_groups > 0 ? n_groups : 1;
         if (offsets != nullptr &&
             (max_rows >= kGemmWideRows * ng || (K >= kGemmWideMinK && max_rows >= kGemmWideRowsLongK * ng)))
-            launch_bf16_wide<8>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows, n_out, K,
-                                partials, s, gather, a_bytes);
+        {
+            if (kGemmWideBN > 256 && n_groups <= kRegSchedGroups)
+                launch_bf16_wide<8, kGemmWideBN>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows,
+                                                 dense_rows, n_out, K, partials, s, gather, a_bytes);
+            else
+                launch_bf16_wide<8, 256>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows, dense_rows,
+                                         n_out, K, partials, s, gather, a_bytes);
+        }
         else if (offsets != nullptr && max_rows <= kGemmR128Rows * ng)
             launch_bf16_persistent<8, 2, true>(epi, A, B, bias, C, offsets, e_begin, n_groups, max_rows,
                                                dense_rows, n_out, K, partials, s, gather, a_bytes);

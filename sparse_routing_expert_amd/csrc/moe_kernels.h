@@ -183,6 +183,12 @@ constexpr int kGemmWideMinK = 2048;
 #define MOE_GEMM_R128_ROWS 256
 #endif
 constexpr int64_t kGemmR128Rows = MOE_GEMM_R128_ROWS;
+// Weight rows per tile of the wide-K kernel: 256, or 384 (the tile schedule then moves from LDS into
+// registers, for launches of at most 63 expert groups)
+#ifndef MOE_GEMM_WIDE_BN
+#define MOE_GEMM_WIDE_BN 384
+#endif
+constexpr int kGemmWideBN = MOE_GEMM_WIDE_BN;
 constexpr int kRouterWgradExperts = 32;  // experts per dW_r block (x read once per 32 experts)
 constexpr int kRouterDgradTokens = 16;   // tokens per dx block (W_r read once per 16 tokens)
 size_t bwd_router_partials_bytes(int64_t T, int E, int d);
