@@ -20,7 +20,7 @@
 //    output element) in an XCD-aware order; two groups of four waves alternate LDS fragment reads
 //    and MFMA clusters (ping-pong), and the LDS ring runs on across tiles.
 //  - gemm_bf16_wide_kernel, for expert groups averaging at least 2048 rows: 256 x 384 tiles (SwiGLU:
-//    192 gate and the matching 192 up columns), or 256 x 256 past 63 groups, in the same order;
+//    192 gate and the matching 192 up columns), or 256 x 256 past 128 groups, in the same order;
 //    four waves that place their memory instructions between their own MFMAs, and 64-wide K
 //    stages, so each DMA reads whole 128-byte row pieces.
 //  - gemm_bf16_kernel: four waves on one 64 x 128 (or 64 x 64) tile with a 6- (8-) stage ring, two
@@ -575,28 +575,37 @@ __device__ __forceinline__ TileSched<BM, BNO, GM> setup_sched(const int32_t* __r
 }
 
 // The same schedule held in registers instead of LDS, for kernels whose LDS ring takes all of it: at
-// most kRegSchedGroups groups, lane g of every wave holds s_ts[g] and offsets[e_begin + g] (g <=
-// n_groups). Each wave forms it on its own (a wave-wide scan), and decode finds the group with a
-// ballot, so it must be called by whole waves.
-constexpr int kRegSchedGroups = 63;
+// most kRegSchedGroups groups; entry g < n_groups of s_ts and of offsets[e_begin ..] sits in lane
+// g % 64 of register g / 64 of every wave, entry n_groups (the totals) in scalars. Each wave forms it
+// on its own (a wave-wide scan), and decode finds the group with ballots, so it must be called by
+// whole waves.
+constexpr int kRegSchedGroups = 128;
 template <int BM, int BNO, int GM>
 struct TileSchedR {
-    int ts_l, off_l;
+    int ts_l[2], off_l[2];
+    int off_end;  // offsets[e_begin + n_groups]
     bool grouped;
     int e_begin, n_groups;
     int64_t dense_rows;
     uint32_t n_tiles_n, m_tiles, R;
 
+    // entry g (uniform, g <= n_groups); entry n_groups is `last`
+    __device__ __forceinline__ int at(const int (&v)[2], int g, int last) const {
+        if (g >= n_groups) return last;
+        return g < kWave ? __builtin_amdgcn_readlane(v[0], g) : __builtin_amdgcn_readlane(v[1], g - kWave);
+    }
     __device__ __forceinline__ void decode(uint32_t lin, int64_t& row0, int64_t& row_end, int& e, int& n0) const {
         int g = 0;
         uint32_t g_mt = m_tiles, local = lin;
         if (grouped) {
             const uint32_t key = lin / n_tiles_n;
             // s_ts is non-decreasing: the last group whose first row tile is at or before key
-            const uint64_t m = __ballot(lane_id() < n_groups && (uint32_t)ts_l <= key);
-            g = __builtin_amdgcn_readfirstlane(__popcll(m) - 1);
-            const uint32_t t0 = (uint32_t)__builtin_amdgcn_readlane(ts_l, g);
-            g_mt = (uint32_t)__builtin_amdgcn_readlane(ts_l, g + 1) - t0;
+            const int lane = lane_id();
+            const uint64_t m0 = __ballot(lane < n_groups && (uint32_t)ts_l[0] <= key);
+            const uint64_t m1 = __ballot(lane + kWave < n_groups && (uint32_t)ts_l[1] <= key);
+            g = __builtin_amdgcn_readfirstlane(__popcll(m0) + __popcll(m1) - 1);
+            const uint32_t t0 = (uint32_t)at(ts_l, g, (int)m_tiles);
+            g_mt = (uint32_t)at(ts_l, g + 1, (int)m_tiles) - t0;
             local = lin - t0 * n_tiles_n;
         }
         const uint32_t grp_ = local / (GM * n_tiles_n);
@@ -608,8 +617,8 @@ struct TileSchedR {
         n0 = (int)col * BNO;
         if (grouped) {
             e = e_begin + g;
-            row0 = __builtin_amdgcn_readlane(off_l, g) + (int64_t)mt * BM;
-            row_end = __builtin_amdgcn_readlane(off_l, g + 1);
+            row0 = at(off_l, g, off_end) + (int64_t)mt * BM;
+            row_end = at(off_l, g + 1, off_end);
         } else {
             e = 0;
             row0 = (int64_t)mt * BM;
@@ -623,12 +632,18 @@ __device__ __forceinline__ TileSchedR<BM, BNO, GM> setup_sched_regs(const int32_
                                                                     int n_out) {
     TileSchedR<BM, BNO, GM> ts;
     const int lane = lane_id();
-    ts.ts_l = 0;
-    ts.off_l = 0;
     ts.m_tiles = (uint32_t)((dense_rows + BM - 1) / BM);
-    if (offsets) {
-        const int o = lane <= n_groups ? offsets[e_begin + lane] : 0;
-        const int o1 = lane < n_groups ? offsets[e_begin + lane + 1] : o;
+    ts.n_groups = n_groups;
+    ts.off_end = 0;
+    int carry = 0;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        ts.ts_l[r] = 0;
+        ts.off_l[r] = 0;
+        if (!offsets) continue;
+        const int g = r * kWave + lane;
+        const int o = g < n_groups ? offsets[e_begin + g] : 0;
+        const int o1 = g < n_groups ? offsets[e_begin + g + 1] : o;
         const int n = (o1 - o + BM - 1) / BM;
         int inc = n;
 #pragma unroll
@@ -636,13 +651,16 @@ __device__ __forceinline__ TileSchedR<BM, BNO, GM> setup_sched_regs(const int32_
             const int v = __shfl_up(inc, d, kWave);
             if (lane >= d) inc += v;
         }
-        ts.ts_l = inc - n;  // exclusive: lane n_groups holds the total
-        ts.off_l = o;
-        ts.m_tiles = (uint32_t)__builtin_amdgcn_readlane(ts.ts_l, n_groups);
+        ts.ts_l[r] = carry + inc - n;  // exclusive prefix
+        ts.off_l[r] = o;
+        carry += __builtin_amdgcn_readlane(inc, kWave - 1);
+    }
+    if (offsets) {
+        ts.m_tiles = (uint32_t)carry;
+        ts.off_end = offsets[e_begin + n_groups];
     }
     ts.grouped = offsets != nullptr;
     ts.e_begin = e_begin;
-    ts.n_groups = n_groups;
     ts.dense_rows = dense_rows;
     ts.n_tiles_n = (uint32_t)((n_out + BNO - 1) / BNO);
     ts.R = ts.m_tiles * ts.n_tiles_n;
@@ -1082,7 +1100,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
 // BN = 384 weight rows: 24 accumulators of 32 x 32 per wave, 384 registers, more than the 256 of the
 // AGPR file, so acc[i][4..5] live in VGPRs (fragments and addresses take the other 120 or so). A
 // stage is 80 KB, the two slots take all 160 KB of LDS, and the tile schedule lives in registers
-// (TileSchedR, at most 63 groups). Per MFMA, a stage moves 17 % fewer operand bytes than with
+// (TileSchedR, at most 128 groups). Per MFMA, a stage moves 17 % fewer operand bytes than with
 // BN = 256, and each stage is half as long again, which covers more of the next stage's DMA latency.
 
 template <int EPI, int GM, bool KT, bool GA, int BN>
@@ -1162,13 +1180,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
         const int row = q < BM / 32 ? R : ((GATED && q >= QUP) ? R - BM - BN / 2 : R - BM);
         voff[q] = row * K * 2 + c * 16;
     }
-    // K not a multiple of BK (KT): the weight chunks of the last stage past K read as zeros
-    int tor[NQB];
-#pragma unroll
-    for (int q = 0; q < NQB; ++q) {
-        const int R = ((q + BM / 32) * 4 + wave) * 8 + (lane >> 3);
-        tor[q] = KT && ((lane & 7) ^ swz8(R)) * 8 >= K - (nk - 1) * BK ? (int)0x80000000 : 0;
-    }
+    // K not a multiple of BK (KT): the weight chunks of the last stage past K read as zeros. A lane's
+    // chunk is the same in every DMA (swz8 of rows 32 q + 8 wave + lane / 8 does not depend on q).
+    const int tor = KT && ((lane & 7) ^ swz8(wave * 8 + (lane >> 3))) * 8 >= K - (nk - 1) * BK ? (int)0x80000000 : 0;
     i32x4 ra, rb0, rb1;
     auto set_dma_tile = [&](uint32_t lin) {
         int64_t row0, row_end;
@@ -1191,20 +1205,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
         rb1 = make_rsrc(Bg + (int64_t)(GATED ? n_out + n0 : n0) * K, (uint32_t)((int64_t)bcols * K * 2));
     };
 
-    int a_off[TM], a_sw[TM], b_off[TN], b_sw[TN];
+    // fragment rows: row block base + lane % 32, whose swizzle is that of lane % 32 (the bases are
+    // multiples of 32)
+    int a_off[TM], b_off[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int r = wm * 128 + i * 32 + (lane & 31);
-        a_off[i] = r * BK;
-        a_sw[i] = swz8(r);
-    }
+    for (int i = 0; i < TM; ++i) a_off[i] = (wm * 128 + i * 32 + (lane & 31)) * BK;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         const int jj = j < TNO ? j : j - TNO;
-        const int r = BM + (GATED && j >= TNO ? BN / 2 : 0) + wn * WTNO + jj * 32 + (lane & 31);
-        b_off[j] = r * BK;
-        b_sw[j] = swz8(r);
+        b_off[j] = (BM + (GATED && j >= TNO ? BN / 2 : 0) + wn * WTNO + jj * 32 + (lane & 31)) * BK;
     }
+    const int fsw = swz8(lane & 31);
     const int khalf = lane >> 5;
 
     floatx16 acc[TM][TN];
@@ -1212,7 +1223,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
 
 #define PW_DMA(slot_, ks_, q_)                                                                            \
     dma16(lds_base + (slot_) * STAGE_BYTES + ((q_) * 4 + wave) * 1024,                                    \
-          (KT && (q_) >= BM / 32 && (ks_) == nk - 1) ? (voff[q_] | tor[((q_) - BM / 32) % NQB]) : voff[q_], \
+          (KT && (q_) >= BM / 32 && (ks_) == nk - 1) ? (voff[q_] | tor) : voff[q_],                       \
           (q_) < BM / 32 ? ra : ((GATED && (q_) >= QUP) ? rb1 : rb0), (ks_) * (BK * 2));
     // fragment n (in MFMA use order: fa0, fb0..fb[TN-1], fa1..fa3) of 16-wide K step kk_ into buffer b_
 #define PW_READ(b_, kk_, slot_, n_)                                                                       \
@@ -1221,10 +1232,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
         const int c_ = (kk_) * 2 + khalf;                                                                 \
         if ((n_) == 0 || (n_) > TN) {                                                                     \
             const int i_ = (n_) == 0 ? 0 : (n_) - TN;                                                     \
-            fa[b_][i_] = *reinterpret_cast<const bf16x8*>(L_ + a_off[i_] + ((c_ ^ a_sw[i_]) << 3));       \
+            fa[b_][i_] = *reinterpret_cast<const bf16x8*>(L_ + a_off[i_] + ((c_ ^ fsw) << 3));            \
         } else {                                                                                          \
             const int j_ = (n_) - 1;                                                                      \
-            fb[b_][j_] = *reinterpret_cast<const bf16x8*>(L_ + b_off[j_] + ((c_ ^ b_sw[j_]) << 3));       \
+            fb[b_][j_] = *reinterpret_cast<const bf16x8*>(L_ + b_off[j_] + ((c_ ^ fsw) << 3));            \
         }                                                                                                 \
     }
     // the compiler selects one register file for every MFMA accumulator of a kernel, so the ones kept in

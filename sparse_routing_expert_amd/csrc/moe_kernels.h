@@ -184,7 +184,7 @@ constexpr int kGemmWideMinK = 2048;
 #endif
 constexpr int64_t kGemmR128Rows = MOE_GEMM_R128_ROWS;
 // Weight rows per tile of the wide-K kernel: 256, or 384 (the tile schedule then moves from LDS into
-// registers, for launches of at most 63 expert groups)
+// registers, for launches of at most 128 expert groups)
 #ifndef MOE_GEMM_WIDE_BN
 #define MOE_GEMM_WIDE_BN 384
 #endif

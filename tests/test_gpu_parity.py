@@ -63,6 +63,10 @@ CASES = {
     "rowsel_E256_T8192": I.mini("deepseek_v3", T=8192, d=128, F=64, Fs=64),
     # groups averaging 1024 rows over K = 2048 take the wide-K kernel for gate/up (16 skewed experts)
     "wide_longK_E16": I.mini("qwen3_30b_a3b", T=2048, d=2048, F=64, E=16, k=8),
+    # ... with 100 and 128 experts: the wide kernel's 384-row tiles keep their tile schedule in two
+    # registers per lane (groups 64 and up in the second) and its last entries in scalars
+    "wide_longK_E100": I.mini("qwen3_30b_a3b", T=12800, d=2048, F=64, E=100, k=8),
+    "wide_longK_E128": I.mini("qwen3_30b_a3b", T=16384, d=2048, F=64, E=128, k=8),
     # the shared expert and the router GEMM as dense products over K = 2048 with a ragged last row tile
     "dense_longK_shared": I.mini("deepseek_v3", T=1100, d=2048, F=64, Fs=128),
     # softmax scoring with a selection-only bias (key = logit + bias, gates from the raw logits): the
