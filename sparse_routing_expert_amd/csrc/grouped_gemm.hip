@@ -1121,10 +1121,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
     constexpr int NT = TM * TN;             // MFMAs per 16-wide K step
     // accumulators: 16 blocks of 32 x 32 fill the AGPR file; with 384 weight rows acc[i][4..5] are in VGPRs
     constexpr int NAG = 16 / TM;
+    // MFMAs of the last K step before the wait for the next stage's DMAs: with 24 per step, the latest
+    // point that leaves one MFMA per fragment read of the next stage's first step (measured on the
+    // Mixtral-shaped layer against 6, 10 and 12: step 4.75, 4.71, 4.66 and 4.62 ms for 14)
+    constexpr int WB = BN > 256 ? NT - NF : TN;
     // 384-row weight tiles fill the LDS with the ring; their tile schedule is held in registers
     constexpr bool RS = BN > 256;
     constexpr int SCHED_ELEMS = RS ? 0 : (2 * 1025 + 8) * 2;
-    static_assert(TN == BN / 64 && BN % 128 == 0 && NF <= NT / 2 && NQ - NQ / 2 <= NT / 2 && NF <= NT - TN,
+    static_assert(TN == BN / 64 && BN % 128 == 0 && NF <= NT / 2 && NQ - NQ / 2 <= NT / 2 && NF <= NT - WB,
                   "tile shape");
     static_assert(NS * STAGE_BYTES + SCHED_ELEMS * 2 <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE_ELEMS + SCHED_ELEMS];
@@ -1278,7 +1282,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
 
     int r_slot = 0;
     // one stage: K steps 0 and 1 with the next stage's NQ DMAs after their odd MFMAs and the following
-    // step's fragment reads after their even ones, step 2 with the reads of step 3, step 3: TN MFMAs,
+    // step's fragment reads after their even ones, step 2 with the reads of step 3, step 3: WB MFMAs,
     // the wait for the next stage's DMAs and the stage barrier, the rest with the reads of the next
     // stage's first step
 #define PW_STAGE                                                                                          \
@@ -1308,14 +1312,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
         }                                                                                                 \
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                                \
         __builtin_amdgcn_sched_barrier(0);                                                                \
-        _Pragma("unroll") for (int t = 0; t < TN; ++t) PW_MMA(1, t)                                       \
+        _Pragma("unroll") for (int t = 0; t < WB; ++t) PW_MMA(1, t)                                       \
         __builtin_amdgcn_sched_barrier(0);                                                                \
         wait_vm<0>();                                                                                     \
         lds_barrier();                                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                                \
-        _Pragma("unroll") for (int t = TN; t < NT; ++t) {                                                 \
+        _Pragma("unroll") for (int t = WB; t < NT; ++t) {                                                 \
             PW_MMA(1, t)                                                                                  \
-            if (t - TN < NF) PW_READ(0, 0, n_slot, t - TN)                                                \
+            if (t - WB < NF) PW_READ(0, 0, n_slot, t - WB)                                                \
             __builtin_amdgcn_sched_barrier(0);                                                            \
         }                                                                                                 \
         r_slot = n_slot;                                                                                  \
