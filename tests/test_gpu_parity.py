@@ -67,6 +67,8 @@ CASES = {
     # registers per lane (groups 64 and up in the second) and its last entries in scalars
     "wide_longK_E100": I.mini("qwen3_30b_a3b", T=12800, d=2048, F=64, E=100, k=8),
     "wide_longK_E128": I.mini("qwen3_30b_a3b", T=16384, d=2048, F=64, E=128, k=8),
+    # ... and past 128 groups (160 experts) the wide kernel's 256 x 256 tiles, schedule in LDS
+    "wide_longK_E160": I.mini("qwen3_30b_a3b", T=20480, d=2048, F=64, E=160, k=8),
     # the shared expert and the router GEMM as dense products over K = 2048 with a ragged last row tile
     "dense_longK_shared": I.mini("deepseek_v3", T=1100, d=2048, F=64, Fs=128),
     # softmax scoring with a selection-only bias (key = logit + bias, gates from the raw logits): the
