@@ -854,6 +854,90 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
     }
 }
 
+// Weight gradients on the wide GEMM's K-grouped mode: expert e's rows of a permuted buffer become
+// columns [poff[e], poff[e] + rows_e) of a transposed copy, zero-padded to the next multiple of 64
+// (64 columns for an expert without rows, so every expert has at least one stage). poff[E] is the
+// padded total; blk[j] is the expert owning 64-column block j, or -1 past it (j < nblk).
+__global__ __launch_bounds__(256) void wgrad_pad_offsets_kernel(const int32_t* __restrict__ offsets, int E, int nblk,
+                                                               int32_t* __restrict__ poff, int32_t* __restrict__ blk) {
+    __shared__ int s_poff[1025];
+    if (threadIdx.x == 0) {  // E <= 1024 additions in expert order
+        int acc = 0;
+        for (int e = 0; e < E; ++e) {
+            s_poff[e] = acc;
+            const int rows = offsets[e + 1] - offsets[e];
+            acc += rows > 0 ? (rows + 63) / 64 * 64 : 64;
+        }
+        s_poff[E] = acc;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e <= E; e += 256) poff[e] = s_poff[e];
+    for (int j = threadIdx.x; j < nblk; j += 256) {
+        const int c = j * 64;
+        int owner = -1;
+        if (c < s_poff[E]) {  // the last expert whose range starts at or before c
+            int lo = 0, hi = E - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_poff[mid] <= c) lo = mid;
+                else hi = mid - 1;
+            }
+            owner = lo;
+        }
+        blk[j] = owner;
+    }
+}
+
+// dst[c][poff[e] + i] = src[offsets[e] + i][c] for the rows i of expert e, zero in the padding: 64 x 64
+// tiles through LDS, block (x, y) covering source columns 64 x and destination columns 64 y (one
+// expert's, as every padded range is a multiple of 64). C is a multiple of 64; dst rows are ld long.
+__global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __restrict__ src, int64_t C,
+                                                            const int32_t* __restrict__ offsets,
+                                                            const int32_t* __restrict__ poff,
+                                                            const int32_t* __restrict__ blk, int64_t ld,
+                                                            uint16_t* __restrict__ dst) {
+    __shared__ uint16_t tile[64][64 + 2];
+    const int e = blk[blockIdx.y];
+    if (e < 0) return;  // uniform per block
+    const int64_t c0 = (int64_t)blockIdx.x * 64;
+    const int j0 = (int)blockIdx.y * 64;
+    const int i0 = j0 - poff[e], rows = offsets[e + 1] - offsets[e];
+    const int64_t r0 = (int64_t)offsets[e] + i0;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int v = it * 256 + threadIdx.x;  // 512 vectors of 8 elements
+        const int r = v >> 3, c = (v & 7) * 8;
+        u32x4 q = {0u, 0u, 0u, 0u};
+        if (i0 + r < rows) q = ld16(src + (r0 + r) * C + c0 + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            tile[r][c + 2 * i] = (uint16_t)(q[i] & 0xffffu);
+            tile[r][c + 2 * i + 1] = (uint16_t)(q[i] >> 16);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int v = it * 256 + threadIdx.x;
+        const int c = v >> 3, r = (v & 7) * 8;  // destination row c0 + c, 8 destination columns
+        u32x4 q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = (uint32_t)tile[r + 2 * i][c] | ((uint32_t)tile[r + 2 * i + 1][c] << 16);
+        st16(dst + (c0 + c) * ld + j0 + r, q);
+    }
+}
+
+void launch_wgrad_pad_offsets(const int32_t* offsets, int E, int nblk, int32_t* poff, int32_t* blk, hipStream_t s) {
+    wgrad_pad_offsets_kernel<<<1, 256, 0, s>>>(offsets, E, nblk, poff, blk);
+}
+
+void launch_transpose_pad(const void* src, int64_t C, const int32_t* offsets, const int32_t* poff,
+                          const int32_t* blk, int nblk, int64_t ld, void* dst, hipStream_t s) {
+    dim3 grid((unsigned)(C / 64), (unsigned)nblk);
+    transpose_pad_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(src), C, offsets, poff, blk, ld,
+                                              static_cast<uint16_t*>(dst));
+}
+
 void launch_transpose_bf16(const void* src, int64_t G, int64_t R, int64_t C, void* dst, hipStream_t s) {
     dim3 grid((unsigned)(C / 64), (unsigned)(R / 64), (unsigned)G);
     transpose_bf16_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(src), R, C, static_cast<uint16_t*>(dst));

@@ -1086,6 +1086,16 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
 #undef PS_MMA
 }
 
+// K-grouped products (the weight gradients): one dense product per expert, C_e = A_e B_e^T, whose K
+// range is the expert's column range [poff[e], poff[e + 1]) of A and B (both [rows][ld], K
+// contiguous; each range a multiple of 64, zero-padded). The experts' output rows are stacked (row
+// e * m_per_e + m of C), m_per_e a multiple of 256, so a tile never spans two experts.
+struct KgArgs {
+    const int32_t* poff;
+    int64_t ld;
+    int m_per_e;
+};
+
 // Four-wave, wide-K form of the persistent GEMM, for large groups: the tile sequence, XCD plan and K
 // split of the eight-wave kernel, with each wave owning a 128-token x BN / 2-weight-row block of the
 // tile (one wave per SIMD) and the memory instructions placed between the wave's own MFMAs instead of
@@ -1103,11 +1113,12 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(
 // (TileSchedR, at most 128 groups). Per MFMA, a stage moves 17 % fewer operand bytes than with
 // BN = 256, and each stage is half as long again, which covers more of the next stage's DMA latency.
 
-template <int EPI, int GM, bool KT, bool GA, int BN>
+template <int EPI, int GM, bool KT, bool GA, int BN, bool KG>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ C, const int32_t* __restrict__ offsets, int e_begin, int n_groups, int64_t dense_rows,
-    int n_out, int K, float* __restrict__ partials, const int32_t* __restrict__ gather, uint32_t a_bytes) {
+    int n_out, int K, float* __restrict__ partials, const int32_t* __restrict__ gather, uint32_t a_bytes,
+    KgArgs kg) {
     constexpr int BM = 256, BK = 64, NS = 2;
     constexpr bool GATED = EPI == EPI_SWIGLU;
     constexpr int TM = 4;
@@ -1131,6 +1142,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
     static_assert(TN == BN / 64 && BN % 128 == 0 && NF <= NT / 2 && NQ - NQ / 2 <= NT / 2 && NF <= NT - WB,
                   "tile shape");
     static_assert(NS * STAGE_BYTES + SCHED_ELEMS * 2 <= 160 * 1024, "LDS budget");
+    static_assert(!KG || (EPI == EPI_F32 && !KT && !GA), "K-grouped products: fp32 output, K in whole stages");
     __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE_ELEMS + SCHED_ELEMS];
 
     const int tid = threadIdx.x, lane = lane_id();
@@ -1167,7 +1179,23 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
     if (nunits == 0) return;  // uniform per block
     auto unit_lin = [&](int u) { return u < (int)nw ? plan.chunk0 + slot + (uint32_t)u * nslots : slice_lin; };
     auto unit_kb = [&](int u) { return u < (int)nw ? 0 : slice_kb; };
-    auto unit_ke = [&](int u) { return u < (int)nw ? nk : slice_ke; };
+    // K-grouped: the expert of a tile and its column range, read with scalar loads (a vector load
+    // would be followed by a wait that also drains the DMAs in flight)
+    const __attribute__((address_space(4))) int32_t* kg_poff = (const __attribute__((address_space(4))) int32_t*)kg.poff;
+    auto kg_expert = [&](uint32_t lin) {
+        int64_t row0, row_end;
+        int e, n0;
+        ts.decode(lin, row0, row_end, e, n0);
+        return (int)(row0 / kg.m_per_e);
+    };
+    auto unit_ke = [&](int u) {
+        if constexpr (KG) {
+            const int ex = kg_expert(unit_lin(u));
+            return (kg_poff[ex + 1] - kg_poff[ex]) / BK;
+        } else {
+            return u < (int)nw ? nk : slice_ke;
+        }
+    };
 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
@@ -1182,7 +1210,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
         const int R = (q * 4 + wave) * 8 + (lane >> 3);
         const int c = (lane & 7) ^ swz8(R);
         const int row = q < BM / 32 ? R : ((GATED && q >= QUP) ? R - BM - BN / 2 : R - BM);
-        voff[q] = row * K * 2 + c * 16;
+        voff[q] = row * (KG ? (int)kg.ld : K) * 2 + c * 16;
     }
     // K not a multiple of BK (KT): the weight chunks of the last stage past K read as zeros. A lane's
     // chunk is the same in every DMA (swz8 of rows 32 q + 8 wave + lane / 8 does not depend on q).
@@ -1193,6 +1221,16 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
         int e, n0;
         ts.decode(lin, row0, row_end, e, n0);
         const int64_t a_rows = row_end - row0 < BM ? row_end - row0 : BM;
+        if constexpr (KG) {  // rows m0 .. m0 + 255 of the expert, columns from its K offset
+            const int ex = (int)(row0 / kg.m_per_e);
+            const int64_t m0 = row0 - (int64_t)ex * kg.m_per_e;
+            const int k0 = kg_poff[ex], kn = kg_poff[ex + 1] - k0;
+            const int bcols = n_out - n0 < BN ? n_out - n0 : BN;
+            ra = make_rsrc(A + m0 * kg.ld + k0, (uint32_t)(((int64_t)(BM - 1) * kg.ld + kn) * 2));
+            rb0 = make_rsrc(B + (int64_t)n0 * kg.ld + k0, (uint32_t)(((int64_t)(bcols - 1) * kg.ld + kn) * 2));
+            rb1 = rb0;
+            return;
+        }
         if (GA) {  // gathered token rows: the descriptor spans A, the row offsets follow the tile
             ra = make_rsrc(A, a_bytes);
 #pragma unroll
@@ -1532,11 +1570,13 @@ void launch_bf16_wide(int epi, const void* A, const void* B, const void* bias, v
 #define MOE_WIDE_GA(EPI_, GA_)                                                                             \
     {                                                                                                     \
         if (K % 64)                                                                                       \
-            gemm_bf16_wide_kernel<EPI_, GM, true, GA_, BN><<<grid, 256, 0, s>>>(                          \
-                a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out, K, partials, gather, a_bytes);  \
+            gemm_bf16_wide_kernel<EPI_, GM, true, GA_, BN, false><<<grid, 256, 0, s>>>(                   \
+                a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out, K, partials, gather, a_bytes,   \
+                KgArgs{nullptr, 0, 0});                                                                   \
         else                                                                                              \
-            gemm_bf16_wide_kernel<EPI_, GM, false, GA_, BN><<<grid, 256, 0, s>>>(                         \
-                a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out, K, partials, gather, a_bytes);  \
+            gemm_bf16_wide_kernel<EPI_, GM, false, GA_, BN, false><<<grid, 256, 0, s>>>(                  \
+                a, b, bi, c, offsets, e_begin, n_groups, dense_rows, n_out, K, partials, gather, a_bytes,   \
+                KgArgs{nullptr, 0, 0});                                                                   \
     }
 #define MOE_WIDE(EPI_)                                                                                      \
     {                                                                                                     \
@@ -1557,6 +1597,19 @@ void launch_bf16_wide(int epi, const void* A, const void* B, const void* bias, v
     else MOE_WIDE(EPI_BIAS)
 #undef MOE_WIDE
 #undef MOE_WIDE_GA
+}
+
+void launch_wgrad_kgrouped(const void* AT, const void* BT, float* C, const int32_t* poff, int E, int m_per_e,
+                           int n_out, int64_t ld, hipStream_t s) {
+    const int64_t rows = (int64_t)E * m_per_e;
+    const int64_t tiles = (rows / 256) * ((n_out + 383) / 384);
+    if (tiles <= 0) return;
+    const int64_t cap = persistent_grid_cap();
+    const int64_t want = ((tiles + 7) / 8) * 8;
+    const unsigned grid = (unsigned)(want < cap ? want : cap);
+    gemm_bf16_wide_kernel<EPI_F32, 8, false, false, 384, true><<<grid, 256, 0, s>>>(
+        static_cast<const uint16_t*>(AT), static_cast<const uint16_t*>(BT), nullptr, reinterpret_cast<uint16_t*>(C),
+        nullptr, 0, 0, rows, n_out, 64, nullptr, nullptr, 0u, KgArgs{poff, ld, m_per_e});
 }
 
 // fp32 path (SIMT, 64 x 64 output tile, 4 x 4 per thread, sequential fp32 FMA over K).

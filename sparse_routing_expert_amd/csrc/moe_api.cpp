@@ -186,9 +186,19 @@ constexpr int64_t kBwdTransposedMinRows = 1536;
 bool bwd_dgrad_transposed(const moe_shape* s) {
     return s->dtype == MOE_BF16 && s->T * s->k >= kBwdTransposedMinRows * s->E;
 }
+// The same layers run the two weight gradients on the wide GEMM's K-grouped mode, from transposed,
+// per-expert zero-padded copies of the permuted buffers (their output rows d and n_in must be
+// multiples of 256, the transposed widths multiples of 64); the strided GEMM otherwise.
+bool bwd_wgrad_kgrouped(const moe_shape* s) {
+    const int64_t n_in = s->act == MOE_SWIGLU ? 2 * (int64_t)s->d_ff : s->d_ff;
+    return bwd_dgrad_transposed(s) && s->d_model % 256 == 0 && n_in % 256 == 0 && s->d_ff % 64 == 0;
+}
+// columns of the transposed copies: every expert's rows padded to a multiple of 64, at least 64
+int64_t bwd_wgrad_ld(const moe_shape* s) { return (s->T * s->k + 63) / 64 * 64 + 64 * (int64_t)s->E; }
 
 struct BwdWs {
-    size_t dg, dYp, pre, h, dh, dAU, dXp, dx32, dl, partials, rpart, pre_s, hs, dhs, dAUs, dXs, w_inT, w_outT, bytes;
+    size_t dg, dYp, pre, h, dh, dAU, dXp, dx32, dl, partials, rpart, pre_s, hs, dhs, dAUs, dXs, w_inT, w_outT, wT1,
+        wT2, poff, pblk, bytes;
 };
 BwdWs bwd_ws(const moe_shape* s) {
     BwdWs w;
@@ -214,6 +224,12 @@ BwdWs bwd_ws(const moe_shape* s) {
     const bool tr = bwd_dgrad_transposed(s);
     w.w_inT = c.take(tr ? (size_t)s->E * n_in * d * 2 : 0);
     w.w_outT = c.take(tr ? (size_t)s->E * d * F * 2 : 0);
+    const bool kg = bwd_wgrad_kgrouped(s);
+    const size_t ld = kg ? (size_t)bwd_wgrad_ld(s) : 0;
+    w.wT1 = c.take(kg ? (d > n_in ? d : n_in) * ld * 2 : 0);  // dY^T, then dAU^T
+    w.wT2 = c.take(kg ? (F > d ? F : d) * ld * 2 : 0);        // h^T, then x_perm^T
+    w.poff = c.take(kg ? ((size_t)s->E + 1) * 4 : 0);
+    w.pblk = c.take(kg ? ld / 64 * 4 : 0);
     w.bytes = c.off;
     return w;
 }
@@ -458,10 +474,29 @@ void do_backward(const moe_shape* s, const BwdIn& in, const BwdOut& out, void* w
                A, st);
     }
     // weight gradients: K runs over each expert's rows
-    run_sg(s, Sg{dYp, 1, d, h, 1, F, 0, out.dw_out, F, d * F, d, F, 0, in.offsets, (int)E, moe::SG_KSPLIT}, A, st);
-    run_sg(s, Sg{dAU, 1, n_in, in.x_perm, 1, d, 0, out.dw_in, d, n_in * d, n_in, d, 0, in.offsets, (int)E,
-                 moe::SG_KSPLIT},
-           A, st);
+    if (bwd_wgrad_kgrouped(s)) {
+        // transposed copies, each expert's rows a zero-padded column range; then one K-grouped product
+        // per weight: dW_out[e] = dY_e^T h_e, dW_in[e] = dAU_e^T X_e
+        const int64_t ld = bwd_wgrad_ld(s);
+        const int nblk = (int)(ld / 64);
+        int32_t* poff = at<int32_t>(ws, w.poff);
+        int32_t* pblk = at<int32_t>(ws, w.pblk);
+        void* wT1 = at<void>(ws, w.wT1);
+        void* wT2 = at<void>(ws, w.wT2);
+        moe::launch_wgrad_pad_offsets(in.offsets, (int)E, nblk, poff, pblk, st);
+        moe::launch_transpose_pad(dYp, d, in.offsets, poff, pblk, nblk, ld, wT1, st);
+        moe::launch_transpose_pad(h, F, in.offsets, poff, pblk, nblk, ld, wT2, st);
+        moe::launch_wgrad_kgrouped(wT1, wT2, out.dw_out, poff, (int)E, (int)d, (int)F, ld, st);
+        moe::launch_transpose_pad(dAU, n_in, in.offsets, poff, pblk, nblk, ld, wT1, st);
+        moe::launch_transpose_pad(in.x_perm, d, in.offsets, poff, pblk, nblk, ld, wT2, st);
+        moe::launch_wgrad_kgrouped(wT1, wT2, out.dw_in, poff, (int)E, (int)n_in, (int)d, ld, st);
+    } else {
+        run_sg(s, Sg{dYp, 1, d, h, 1, F, 0, out.dw_out, F, d * F, d, F, 0, in.offsets, (int)E, moe::SG_KSPLIT}, A,
+               st);
+        run_sg(s, Sg{dAU, 1, n_in, in.x_perm, 1, d, 0, out.dw_in, d, n_in * d, n_in, d, 0, in.offsets, (int)E,
+                     moe::SG_KSPLIT},
+               A, st);
+    }
     if (out.db_out) moe::launch_bwd_colsum(dt, dYp, in.offsets, 0, (int)E, (int)d, out.db_out, st);
     if (out.db_in) moe::launch_bwd_colsum(dt, dAU, in.offsets, 0, (int)E, (int)F, out.db_in, st);
     // shared expert (gate 1, input x, output gradient dy)

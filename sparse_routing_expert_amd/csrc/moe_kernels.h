@@ -116,6 +116,15 @@ void launch_combine(int dtype, const void* y_perm, const int32_t* inv_pos, const
 // ---- backward ---------------------------------------------------------------------------
 // bf16 [G][R][C] -> [G][C][R] (R, C multiples of 64)
 void launch_transpose_bf16(const void* src, int64_t G, int64_t R, int64_t C, void* dst, hipStream_t s);
+// weight gradients on the wide GEMM: per-expert K offsets of the transposed copies, padded to 64
+// (poff [E + 1], blk [nblk] = owning expert of each 64-column block or -1), the padded transposes
+// ([A][C] -> [C][ld], C a multiple of 64), and the K-grouped product dW[e] = A_T[e] B_T[e]^T
+// (fp32 [E * m_per_e][n_out], m_per_e a multiple of 256)
+void launch_wgrad_pad_offsets(const int32_t* offsets, int E, int nblk, int32_t* poff, int32_t* blk, hipStream_t s);
+void launch_transpose_pad(const void* src, int64_t C, const int32_t* offsets, const int32_t* poff,
+                          const int32_t* blk, int nblk, int64_t ld, void* dst, hipStream_t s);
+void launch_wgrad_kgrouped(const void* AT, const void* BT, float* C, const int32_t* poff, int E, int m_per_e,
+                           int n_out, int64_t ld, hipStream_t s);
 // Strided grouped GEMM C(m, n) = sum_k A(m, k) B(n, k); A(m, k) at A[m*sam + k*sak], B(n, k) at
 // B[n*sbn + k*sbk], C(m, n) at C[m*scm + n] (fp32). Each operand is contiguous along k (s?k == 1) or
 // along its row index (sam == 1 / sbn == 1).

@@ -49,6 +49,11 @@ CASES = {
     # at least 2048 rows per expert: every grouped product, the fp32 dgrad ones included, runs on the
     # four-wave wide-K GEMM
     "rows2100_swiglu": (I.mini("small_bf16", T=2100, d=256, F=192, E=2, k=2), 0, 0.01),
+    # ... and with d_model and the up projection's width multiples of 256, the weight gradients run on
+    # the wide GEMM's K-grouped mode from zero-padded transposed copies (experts of 1700 rows: ragged
+    # against the 64-row padding)
+    "kgrouped_swiglu": (I.mini("small_bf16", T=1700, d=256, F=256, E=2, k=2), 0, 0.01),
+    "kgrouped_gelu_bias": (TINY.with_sizes(dtype="bf16", T=3400, d=256, F=256, E=2, k=1), 0, 0.0),
 }
 
 
@@ -105,6 +110,25 @@ def check_backward(name, cfg, L, dy, aux):
             assert torch.equal(v.view(torch.uint8), g2[key].view(torch.uint8)), f"{key} not deterministic"
     print(f"[backward] {name}: ok " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
     return g, ref
+
+
+def test_backward_kgrouped_empty_expert():
+    """K-grouped weight gradients with an expert that receives no rows (a selection bias of -10 keeps
+    expert 2 out of every top-1): its padded range is one block of zero columns, and its dW_in and
+    dW_out must be exactly zero while the other experts' match the oracle."""
+    cfg = I.mini("deepseek_v3", T=6400, d=256, F=128, Fs=0, E=4, k=1)
+    torch.manual_seed(0)
+    t = I.gen_layer(cfg, device="cuda")
+    assert t["sel_bias"] is not None
+    t["sel_bias"][2] = -10.0
+    L = MoeLayer(cfg, t)
+    poison(L)
+    run_forward(L)
+    counts = L.counts.cpu().numpy()
+    assert counts[2] == 0 and (counts[[0, 1, 3]] >= 1536).all(), counts
+    dy = I.gen_dy(cfg, device="cuda")
+    g, _ = check_backward("kgrouped_empty_expert", cfg, L, dy, 0.0)
+    assert (g["dw_in"][2] == 0).all() and (g["dw_out"][2] == 0).all()
 
 
 @pytest.mark.parametrize("name", sorted(CASES))
