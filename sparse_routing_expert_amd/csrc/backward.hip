@@ -37,7 +37,6 @@ __device__ __forceinline__ float gelu_b(float z) { return 0.5f * z * (1.0f + erf
 __device__ __forceinline__ float gelu_grad_b(float z) {
     return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) + z * 0.39894228040143268f * expf(-0.5f * z * z);
 }
-__device__ __forceinline__ int swz_b(int r) { return (r >> 2) & 3; }
 
 template <bool BF16>
 __device__ __forceinline__ float ld_elem(const void* p, int64_t i) {
