@@ -22,7 +22,8 @@
 //  - gemm_bf16_wide_kernel, for expert groups averaging at least 2048 rows: 256 x 384 tiles (SwiGLU:
 //    192 gate and the matching 192 up columns), or 256 x 256 past 128 groups, in the same order;
 //    four waves that place their memory instructions between their own MFMAs, and 64-wide K
-//    stages, so each DMA reads whole 128-byte row pieces.
+//    stages, so each DMA reads whole 128-byte row pieces. Its K-grouped mode (KgArgs) computes the
+//    backward's weight gradients, one product per expert over that expert's range of K.
 //  - gemm_bf16_kernel: four waves on one 64 x 128 (or 64 x 64) tile with a 6- (8-) stage ring, two
 //    blocks per CU, for groups of a few dozen rows (decode batches), whose time is spent streaming
 //    the weight panels.
@@ -1126,7 +1127,6 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_wide_kernel(
     constexpr int STAGE_ELEMS = (BM + BN) * BK;  // BM + BN rows of 128 bytes
     constexpr int STAGE_BYTES = STAGE_ELEMS * 2;
     constexpr int NQ = (BM + BN) / 32;  // DMA instructions per wave per stage (8 rows each)
-    constexpr int NQB = NQ - BM / 32;   // of them on the weight rows
     constexpr int QUP = BM / 32 + BN / 64;  // first DMA on the up rows (SwiGLU)
     constexpr int NF = TM + TN;             // fragment reads per 16-wide K step
     constexpr int NT = TM * TN;             // MFMAs per 16-wide K step
