@@ -23,7 +23,9 @@ from tests.test_gpu_parity import poison
 pytestmark = pytest.mark.gpu
 
 TINY = I.CONFIGS["tiny_fp32"]
-# name: (layer, capacity factor or 0 for dropless, balancing coefficient)
+# name: (layer, capacity factor or 0 for dropless, balancing coefficient); the logit gradient of
+# the names in DLOGITS_OWN follows the full-size protocol (dlogits_own_check)
+DLOGITS_OWN = {"qwen_kgrouped_E64"}
 CASES = {
     "tiny_fp32": (TINY, 0, 0.0),
     "tiny_fp32_aux": (TINY.with_sizes(T=37), 0, 0.01),
@@ -54,6 +56,9 @@ CASES = {
     # against the 64-row padding)
     "kgrouped_swiglu": (I.mini("small_bf16", T=1700, d=256, F=256, E=2, k=2), 0, 0.01),
     "kgrouped_gelu_bias": (TINY.with_sizes(dtype="bf16", T=3400, d=256, F=256, E=2, k=1), 0, 0.0),
+    # 64 skewed experts (8 of them empty, the largest 5659 rows): many padded ranges, 64-column zero
+    # blocks for the empty ones, whose gradients must be exactly zero
+    "qwen_kgrouped_E64": (I.mini("qwen3_30b_a3b", T=12288, d=256, F=128, E=64, k=8), 0, 0.01),
 }
 
 
@@ -73,7 +78,36 @@ def poison_grads(g):
             v.fill_(float("nan"))
 
 
-def check_backward(name, cfg, L, dy, aux):
+def dlogits_own_check(cfg, L, g, dy, aux, ref_dl, tol):
+    """The logit gradient by the full-size protocol, for layers with many top-8 tokens: y_perm's bf16
+    rounding, amplified where a token's gate gradients nearly cancel, can lift one token of thousands
+    past the block bound. The GPU's logit gradient must equal the oracle's gate backward of
+    dg = <dy, y_perm> formed in float64 from the GPU's own y_perm, to 1e-4 of its pre-cancellation
+    scale; against the all-float64 oracle the median block error is held to the layer tolerance."""
+    t = L.t
+    idx = L.topk_idx.cpu().numpy().astype(np.int64)
+    rt = R.route(t["x"], t["w_r"], cfg.k, cfg.score, cfg.renorm, t["sel_bias"])
+    aux_dl = G.aux_backward(rt.logits, idx, cfg.score, aux)
+    inv = L.inv_pos.cpu().numpy().astype(np.int64).reshape(L.T, cfg.k)
+    dg_own = np.einsum("tkd,td->tk", P.np64(L.y_perm)[inv], P.np64(dy))
+    dl_own = G.gate_backward(rt.logits, idx, cfg.score, cfg.renorm, dg_own) + aux_dl
+    gts = R.gates(rt.logits, idx, cfg.score, cfg.renorm)
+    scale = np.linalg.norm(gts, axis=1) * np.abs(dg_own).max(axis=1) + np.linalg.norm(aux_dl, axis=1)
+    dl_gpu = P.np64(g["dlogits"])
+    e_own = np.linalg.norm(dl_gpu - dl_own, axis=1) / np.maximum(np.maximum(np.linalg.norm(dl_own, axis=1), scale),
+                                                                 1e-300)
+    assert e_own.max() <= 1e-4, f"dlogits vs its own y_perm's gate backward: token {int(np.argmax(e_own))} " \
+                                f"rel err {e_own.max():.3g}"
+    num = np.linalg.norm(dl_gpu - ref_dl, axis=1)
+    den = np.linalg.norm(ref_dl, axis=1)
+    blk = num / np.maximum(den, float(np.median(den[den > 0])))
+    assert np.median(blk) <= tol, f"dlogits: median block error {np.median(blk):.3g}"
+    print(f"[backward] dlogits: own-y_perm max {e_own.max():.2e}; float64 oracle blocks median "
+          f"{np.median(blk):.2e} max {blk.max():.2e} (token {int(np.argmax(blk))})", flush=True)
+    return float(np.median(blk))
+
+
+def check_backward(name, cfg, L, dy, aux, dl_own=False):
     tol = P.tol_for(cfg)
     print(f"[backward] {name}: T={L.T} d={cfg.d} F={cfg.F} E={cfg.E} k={cfg.k} {cfg.dtype} {cfg.act} {cfg.score} "
           f"C={L.capacity} aux={aux}", flush=True)
@@ -89,7 +123,8 @@ def check_backward(name, cfg, L, dy, aux):
     E, T = cfg.E, L.T
     errs = {
         "dx": P.grad_err(g["dx"], ref.dx, T, "dx", tol),
-        "dlogits": P.grad_err(g["dlogits"], ref.dl, T, "dlogits", tol),
+        "dlogits": (dlogits_own_check(cfg, L, g, dy, aux, ref.dl, tol) if dl_own
+                    else P.grad_err(g["dlogits"], ref.dl, T, "dlogits", tol)),
         "dw_r": P.grad_err(g["dw_r"], ref.dw_r, E, "dw_router", tol),
         "dw_in": P.grad_err(g["dw_in"], ref.dw_in, E, "dw_in", tol),
         "dw_out": P.grad_err(g["dw_out"], ref.dw_out, E, "dw_out", tol),
@@ -140,7 +175,7 @@ def test_backward_parity(name):
     poison(L)
     run_forward(L)
     dy = I.gen_dy(cfg, device="cuda")
-    g, ref = check_backward(name, cfg, L, dy, aux)
+    g, ref = check_backward(name, cfg, L, dy, aux, dl_own=name in DLOGITS_OWN)
     if cap:
         assert int((L.inv_pos.cpu().numpy() < 0).sum()) > 0, "capacity case drops nothing"
     if name.startswith("qwen"):
