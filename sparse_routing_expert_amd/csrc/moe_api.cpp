@@ -355,32 +355,17 @@ void do_down(const moe_shape* s, int e_begin, int e_end, const void* h, const in
                              e_end - e_begin, A, 0, s->d_model, s->d_ff, partials, st);
 }
 
-// Experts per up/down pass of the grouped FFN. The hidden activations h of all experts are written
-// by the up projection and read back by the down projection; when they outgrow the 256 MiB
-// last-level cache (MALL), the down projection streams them from HBM. Running the experts in chunks
-// whose h fits (up then down per chunk, expected rows per expert = T*k/E) keeps the down
-// projection's A operand cache-resident; below that size one pass does all experts.
-constexpr int64_t kFfnChunkBytes = 256ll << 20;
-int ffn_experts_per_chunk(const moe_shape* s, int n_experts) {
-    if (s->dtype != MOE_BF16 || n_experts <= 1) return n_experts > 0 ? n_experts : 1;
-    const int64_t h_per_expert = s->T * s->k / s->E * s->d_ff * 2;
-    if (h_per_expert * n_experts <= kFfnChunkBytes) return n_experts;
-    const int64_t per = h_per_expert > 0 ? kFfnChunkBytes / h_per_expert : n_experts;
-    return per < 1 ? 1 : (int)per;
-}
-
 void do_ffn(const moe_shape* s, int e_begin, int e_end, const void* x_perm, const int32_t* offsets,
             const void* w_in, const void* b_in, const void* w_out, const void* b_out, void* y_perm, void* ws,
             hipStream_t st, const int32_t* gather = nullptr) {
     const FfnWs w = ffn_ws(s);
     void* h = at<void>(ws, w.h);
     float* partials = partials_of(ws, w.partials, s);
-    const int per = ffn_experts_per_chunk(s, e_end - e_begin);
-    for (int e0 = e_begin; e0 < e_end; e0 += per) {
-        const int e1 = e_end - e0 > per ? e0 + per : e_end;
-        do_up(s, e0, e1, x_perm, offsets, w_in, b_in, h, partials, st, gather);
-        do_down(s, e0, e1, h, offsets, w_out, b_out, y_perm, partials, st);
-    }
+    // one up and one down launch over all experts: running them in chunks whose h fits the 256 MiB
+    // last-level cache made the Mixtral-shaped step slower with the 256 x 384 tiles (4.79 against
+    // 4.73 ms), so the down projection streams h from HBM
+    do_up(s, e_begin, e_end, x_perm, offsets, w_in, b_in, h, partials, st, gather);
+    do_down(s, e_begin, e_end, h, offsets, w_out, b_out, y_perm, partials, st);
 }
 
 void do_shared(const moe_shape* s, const void* x, const void* ws_in, const void* ws_out, void* y_shared, void* ws,
