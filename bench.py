@@ -456,11 +456,34 @@ def measured_traffic(workload: str):
     return int(fields["hbm_bytes_per_launch"])
 
 
+def oracle_stages(cfg, t, x):
+    """The oracle's layer on the tokens x, stage by stage: the calls of oracle.moe_ref.layer_forward in
+    its order (route, permute with the row gather, the per-expert FFN loop, the shared expert, combine),
+    each timed. Returns the layer output and the seconds of each stage."""
+    from oracle import moe_ref as R
+
+    sec = {}
+    t0 = time.perf_counter()
+    xf = R.f64(x)
+    r = R.route(xf, t["w_r"], cfg.k, cfg.score, cfg.renorm, t["sel_bias"])
+    t1 = time.perf_counter()
+    offsets, sorted_token, inv_pos = R.permute(r.idx, cfg.E)
+    x_perm = xf[sorted_token]
+    t2 = time.perf_counter()
+    get = R.stacked_experts(t["w_in"], t["b_in"], t["w_out"], t["b_out"])
+    y_perm = R.experts_on_rows(x_perm, offsets, get, cfg.act)
+    t3 = time.perf_counter()
+    ys = R.shared_ffn(xf, R.f64(t["ws_in"]), R.f64(t["ws_out"])) if t["ws_in"] is not None else None
+    t4 = time.perf_counter()
+    y = R.combine(y_perm, inv_pos, r.gates, ys)
+    t5 = time.perf_counter()
+    sec = {"route": t1 - t0, "permute": t2 - t1, "expert_ffn": t3 - t2, "shared": t4 - t3, "combine": t5 - t4}
+    return y, sec
+
+
 def cpu_baseline(cfg, L, n_tokens: int):
     """The float64 oracle, as it stands, on the first n tokens of the same layer (host cores)."""
     import numpy as np
-
-    from oracle import moe_ref as R
 
     try:
         from threadpoolctl import threadpool_info
@@ -481,19 +504,14 @@ def cpu_baseline(cfg, L, n_tokens: int):
         per_tok = 6.0 * cfg.k * cfg.d * cfg.F + 2.0 * cfg.E * cfg.d + (6.0 * cfg.d * cfg.Fs if cfg.Fs else 0)
         n_tokens = int(max(16, min(cfg.T, 1e13 / per_tok)))
     n_tokens = min(n_tokens, cfg.T)
-    t = L.t
-    x = t["x"][:n_tokens]
-    get = R.stacked_experts(t["w_in"], t["b_in"], t["w_out"], t["b_out"])
-    t0 = time.perf_counter()
-    res = R.layer_forward(x, t["w_r"], get, cfg.k, cfg.act, cfg.score, cfg.renorm, t["sel_bias"], t["ws_in"],
-                          t["ws_out"])
-    dt = time.perf_counter() - t0
-    assert np.isfinite(res.y).all()
+    y, sec = oracle_stages(cfg, L.t, L.t["x"][:n_tokens])
+    dt = sum(sec.values())
+    assert np.isfinite(y).all()
     return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": min(threads, allowed), "kind": "oracle",
             "blas_threads": threads, "cpus_allowed": allowed, "cpu_model": model,
             "sample": f"first {n_tokens} of {cfg.T} tokens of the same layer, full oracle forward (route, permute, "
                       f"per-expert fp64 loop incl. converting each used expert's bf16 weights, combine)",
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2), "stage_seconds": {k: round(v, 3) for k, v in sec.items()}}
 
 
 if __name__ == "__main__":
