@@ -96,9 +96,11 @@ enum {
 
 /* Layer description (host memory). Limits: T >= 0; 1 <= E <= 1024; 1 <= k <= min(E, 32); capacity >= 0;
  * T*k <= 2^31-1; d_model, d_ff and d_ff_shared multiples of 8 (bf16) or 4 (f32), so every row is
- * whole 16-byte vectors (MOE_ERR_INVALID_ARG otherwise); MOE_SIGMOID requires renorm = 1
- * (MOE_ERR_UNSUPPORTED). moe_backward on bf16 layers further needs multiples of 64
- * (MOE_ERR_UNSUPPORTED). */
+ * whole 16-byte vectors (MOE_ERR_INVALID_ARG otherwise); d_model, d_ff and d_ff_shared at most
+ * MOE_MAX_WIDTH (MOE_ERR_UNSUPPORTED otherwise: the matrix kernels address a tile's operand rows
+ * with 32-bit byte offsets); MOE_SIGMOID requires renorm = 1 (MOE_ERR_UNSUPPORTED). moe_backward on
+ * bf16 layers further needs multiples of 64 (MOE_ERR_UNSUPPORTED). */
+#define MOE_MAX_WIDTH (1 << 18)
 typedef struct {
     int64_t T;           /* tokens */
     int32_t d_model;     /* hidden size d */

@@ -34,6 +34,10 @@ int check_shape(const moe_shape* s) {
     // 16-byte vectors of bf16 (8 elements) or fp32 (4 elements) along every row
     const int mult = s->dtype == MOE_BF16 ? 8 : 4;
     if (s->d_model % mult || s->d_ff % mult || s->d_ff_shared % mult) return MOE_ERR_INVALID_ARG;
+    // the GEMM kernels' DMA offsets are 32-bit: at most 640 operand rows of K bf16 elements per tile,
+    // with K up to 2 * d_ff (the backward's products against the transposed gate/up weights)
+    if (s->d_model > MOE_MAX_WIDTH || s->d_ff > MOE_MAX_WIDTH || s->d_ff_shared > MOE_MAX_WIDTH)
+        return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -189,12 +193,16 @@ bool bwd_dgrad_transposed(const moe_shape* s) {
 // The same layers run the two weight gradients on the wide GEMM's K-grouped mode, from transposed,
 // per-expert zero-padded copies of the permuted buffers (their output rows d and n_in must be
 // multiples of 256, the transposed widths multiples of 64); the strided GEMM otherwise.
-bool bwd_wgrad_kgrouped(const moe_shape* s) {
-    const int64_t n_in = s->act == MOE_SWIGLU ? 2 * (int64_t)s->d_ff : s->d_ff;
-    return bwd_dgrad_transposed(s) && s->d_model % 256 == 0 && n_in % 256 == 0 && s->d_ff % 64 == 0;
-}
 // columns of the transposed copies: every expert's rows padded to a multiple of 64, at least 64
 int64_t bwd_wgrad_ld(const moe_shape* s) { return (s->T * s->k + 63) / 64 * 64 + 64 * (int64_t)s->E; }
+// The K-grouped product's DMA offsets are 32-bit: a tile's 256 + 384 operand rows of ld bf16
+// elements must stay below 2^31 bytes. Longer token batches take the strided GEMM (64-bit addresses).
+constexpr int64_t kKgMaxLd = (((int64_t)1 << 31) - 1) / ((256 + 384) * 2);
+bool bwd_wgrad_kgrouped(const moe_shape* s) {
+    const int64_t n_in = s->act == MOE_SWIGLU ? 2 * (int64_t)s->d_ff : s->d_ff;
+    return bwd_dgrad_transposed(s) && s->d_model % 256 == 0 && n_in % 256 == 0 && s->d_ff % 64 == 0 &&
+           bwd_wgrad_ld(s) <= kKgMaxLd;
+}
 
 struct BwdWs {
     size_t dg, dYp, pre, h, dh, dAU, dXp, dx32, dl, partials, rpart, pre_s, hs, dhs, dAUs, dXs, w_inT, w_outT, wT1,

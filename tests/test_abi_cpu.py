@@ -84,6 +84,11 @@ def ws_bytes(shape, stage):
     (dict(dtype="f32", d_model=12, d_ff=20), L.MOE_OK),
     (dict(score="sigmoid", renorm=False), L.MOE_ERR_UNSUPPORTED),
     (dict(T=2**31, k=2), L.MOE_ERR_INVALID_ARG),  # T*k overflows int32
+    # widths up to MOE_MAX_WIDTH = 2^18 (32-bit DMA offsets in the matrix kernels)
+    (dict(T=16, d_ff=2**18), L.MOE_OK),
+    (dict(T=16, d_ff=2**18 + 8), L.MOE_ERR_UNSUPPORTED),
+    (dict(T=16, d_model=2**18 + 8), L.MOE_ERR_UNSUPPORTED),
+    (dict(T=16, d_ff_shared=2**18 + 8), L.MOE_ERR_UNSUPPORTED),
 ])
 def test_shape_validation(lib, kw, want):
     rc, _ = ws_bytes(good_shape(**kw), L.MOE_STAGE_FORWARD)
