@@ -121,6 +121,16 @@ CASES = {
     "max_E1024_k16_T8192": I.mini("small_bf16", T=8192, d=64, F=64, E=1024, k=16),
     # a router GEMM whose 128 x 128 tiles fill the CUs (94 x 3 = 282) runs without a K split
     "router_tiles128_E128": I.mini("qwen3_30b_a3b", T=12000, d=1024, F=64),
+    # widths at MOE_MAX_WIDTH = 2^18, where the matrix kernels' 32-bit DMA offsets are largest: the
+    # up projection over 2^19 gate/up rows and the down projection over K = 2^18 (128-row tiles);
+    # the fused router, the permute's rows and the 64-row kernel over d = 2^18 (router std 0.02 / 8, so
+    # the logits keep the spread they have at d = 4096, std 1.3: at std 10 an fp32 sum of 2^18 terms
+    # alone carries more rounding than the 5e-5 logit tolerance); the fp32 path over K = 2^18; a
+    # shared expert of width 2^18
+    "max_width_dff": I.mini("small_bf16", T=64, d=64, F=2**18, E=2, k=2),
+    "max_width_d": I.mini("small_bf16", T=48, d=2**18, F=64, E=2, k=1, router_std=0.0025),
+    "max_width_dff_f32": I.mini("tiny_fp32", T=32, d=64, F=2**18, E=2, k=2),
+    "max_width_shared": I.mini("deepseek_v3", T=40, d=64, F=64, Fs=2**18, E=8, k=2),
 }
 
 
