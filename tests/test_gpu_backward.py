@@ -166,6 +166,46 @@ def test_backward_kgrouped_empty_expert():
     assert (g["dw_in"][2] == 0).all() and (g["dw_out"][2] == 0).all()
 
 
+def test_backward_wgrad_past_kgrouped_bound():
+    """A layer whose padded token rows exceed the K-grouped product's 32-bit offset bound
+    ((2^31 - 1) / 1280 = 1677721 columns): moe_backward computes its weight gradients on the strided
+    GEMM there. One expert, top-1, 1.7 M tokens, so x_perm = x and dy reaches the expert unscaled
+    (a renormalised gate over one expert is 1, and its logit gradient is 0): the input and output
+    weight gradients of sampled hidden features over all 1.7 M rows, and dx of sampled tokens,
+    against the oracle."""
+    cfg = I.mini("small_bf16", T=1_700_000, d=256, F=256, E=1, k=1)
+    ld = (cfg.T * cfg.k + 63) // 64 * 64 + 64 * cfg.E
+    assert ld > ((1 << 31) - 1) // 1280
+    print(f"[backward] wgrad_past_kgrouped_bound: T={cfg.T} d={cfg.d} F={cfg.F} padded rows {ld}", flush=True)
+    torch.manual_seed(0)
+    L = MoeLayer(cfg, I.gen_layer(cfg, device="cuda"))
+    run_forward(L)
+    dy = I.gen_dy(cfg, device="cuda")
+    g = L.alloc_grads()
+    poison_grads(g)
+    L.backward(dy, g, aux_coef=0.0)
+    torch.cuda.synchronize()
+    for key in ("dx", "dw_in", "dw_out", "dw_r", "dlogits"):
+        assert torch.isfinite(g[key]).all(), key
+    t = L.t
+    F, tol = cfg.F, P.tol_for(cfg)
+    w_in, w_out = P.np64(t["w_in"][0]), P.np64(t["w_out"][0])
+    X, dY = P.np64(t["x"]), P.np64(dy)
+    feats = np.array([0, 97, 255])
+    dw_in_ref, _, dw_out_ref = G.expert_backward_features(X, w_in, None, w_out, None, cfg.act, dY, feats)
+    dw_in = P.np64(g["dw_in"][0])
+    got_in = np.concatenate([dw_in[feats], dw_in[F + feats]], axis=0)
+    e_in = R.rel_l2_per_row(got_in, dw_in_ref).max()
+    e_out = R.rel_l2_per_row(P.np64(g["dw_out"][0])[:, feats].T, dw_out_ref.T).max()
+    assert e_in <= tol and e_out <= tol, (e_in, e_out)
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 62, replace=False)]))
+    dx_ref = G.expert_backward(X[rows], w_in, None, w_out, None, cfg.act, dY[rows])[0]
+    e_dx = R.rel_l2_per_row(P.np64(g["dx"])[rows], dx_ref).max()
+    assert e_dx <= tol, e_dx
+    print(f"[backward] wgrad_past_kgrouped_bound: ok dw_in={e_in:.2e} dw_out={e_out:.2e} dx={e_dx:.2e}", flush=True)
+
+
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_backward_parity(name):
     cfg, factor, aux = CASES[name]
