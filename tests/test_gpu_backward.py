@@ -206,6 +206,42 @@ def test_backward_wgrad_past_kgrouped_bound():
     print(f"[backward] wgrad_past_kgrouped_bound: ok dw_in={e_in:.2e} dw_out={e_out:.2e} dx={e_dx:.2e}", flush=True)
 
 
+def test_backward_max_width():
+    """moe_backward at the ABI's maximum width, d_ff = MOE_MAX_WIDTH = 2^18: with 1536 rows per expert
+    the dgrad products run against the transposed expert weights, and dX = dAU W_in reduces over
+    K = 2 d_ff = 2^19, the longest K any of the matrix kernels takes. One expert, top-1: sampled
+    hidden features' input and output weight gradients over every row, and dx of 16 tokens, against
+    the oracle."""
+    cfg = I.mini("small_bf16", T=1536, d=64, F=2**18, E=1, k=1)
+    print(f"[backward] max_width: T={cfg.T} d={cfg.d} F={cfg.F}", flush=True)
+    torch.manual_seed(0)
+    L = MoeLayer(cfg, I.gen_layer(cfg, device="cuda"))
+    run_forward(L)
+    dy = I.gen_dy(cfg, device="cuda")
+    g = L.alloc_grads()
+    poison_grads(g)
+    L.backward(dy, g, aux_coef=0.0)
+    torch.cuda.synchronize()
+    for key in ("dx", "dw_in", "dw_out", "dw_r", "dlogits"):
+        assert torch.isfinite(g[key]).all(), key
+    t = L.t
+    F, tol = cfg.F, P.tol_for(cfg)
+    w_in, w_out = P.np64(t["w_in"][0]), P.np64(t["w_out"][0])
+    X, dY = P.np64(t["x"]), P.np64(dy)
+    feats = np.array([0, 12345, F - 1])
+    dw_in_ref, _, dw_out_ref = G.expert_backward_features(X, w_in, None, w_out, None, cfg.act, dY, feats)
+    dw_in = g["dw_in"][0]
+    got_in = np.concatenate([P.np64(dw_in[feats]), P.np64(dw_in[F + feats])], axis=0)
+    e_in = R.rel_l2_per_row(got_in, dw_in_ref).max()
+    e_out = R.rel_l2_per_row(P.np64(g["dw_out"][0][:, feats]).T, dw_out_ref.T).max()
+    assert e_in <= tol and e_out <= tol, (e_in, e_out)
+    rows = np.array([0, 1, 2, 100, 511, 512, 777, 1000, 1023, 1024, 1300, 1500, 1533, 1534, 1535, 64])
+    dx_ref = G.expert_backward(X[rows], w_in, None, w_out, None, cfg.act, dY[rows])[0]
+    e_dx = R.rel_l2_per_row(P.np64(g["dx"])[rows], dx_ref).max()
+    assert e_dx <= tol, e_dx
+    print(f"[backward] max_width: ok dw_in={e_in:.2e} dw_out={e_out:.2e} dx={e_dx:.2e}", flush=True)
+
+
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_backward_parity(name):
     cfg, factor, aux = CASES[name]
